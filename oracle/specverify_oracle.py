@@ -1,0 +1,367 @@
+"""Plain fp64 oracle of the verification step (chain, token tree, debug probs).
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.  Float64 throughout;
+bf16 inputs are widened exactly, fp32 uniforms and temperatures are promoted
+exactly.  No blocking, fusion or reordering: each function follows the
+algorithm as the pages state it.
+
+Readings of points the pages leave open (each applied where noted below):
+
+R1  accept test boundary: accept iff u <= tau (the close-reading notes,
+    section 4, use "r_i <= min(1, p/q)"; one course page's listing uses a
+    strict "<"; the two differ on a set of measure zero).
+R2  tau: 1 when q(x) <= p(x), otherwise p(x)/q(x) (lecture 17 notes, section
+    2.3, steps 2-3).  This equals min(1, p/q) whenever q > 0 and defines the
+    q = 0 case as "accept".
+R3  uniforms: u[b, i] for i < gamma is r_{i+1} of the accept test at draft
+    position i; u[b, gamma] feeds the single final draw, residual or bonus.
+R4  inverse CDF: C = cumsum(w) in vocabulary order, W = C[V-1]; the draw is
+    the smallest k with C[k] > u*W, so zero-weight tokens are never drawn.  If
+    rounding leaves no such k, the last index with w > 0 is returned.
+R5  empty residual (W == 0 after a rejection; only reachable through
+    rounding when p and q coincide): draw from p of that position instead.
+R6  greedy (T == 0): argmax with the lowest index among equal maxima; at the
+    first mismatch emit argmax p_i, if all match emit argmax p_{gamma+1}
+    (close-reading notes, section 10).  Draft logits are not read.
+R7  one temperature per request for both p and q (close-reading notes,
+    section 3: the same decoding strategy on both sides).
+R8  accepted count n in [0, gamma]; n + 1 tokens are emitted; the caller
+    drops gamma - n cached positions.
+R9  token tree: node 0 is the root (the last verified token), parents[0] =
+    -1, 0 <= parents[i] < i (depth-first linearisation, ancestors first,
+    lecture 17 notes section 4.3); children are visited in index order and
+    the lowest-index child carrying the chosen token is taken.
+R10 tree uniforms: u[b, n] is used for the draw at node n when n is visited.
+R11 bad input makes a whole request invalid (count -1, tokens -1): a draft
+    token or tree node token outside [0, V), a temperature that is negative
+    or not finite, a sampling request with a uniform outside [0, 1), a
+    malformed parent array, or a tree deeper than max_depth.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# inputs
+# ---------------------------------------------------------------------------
+def logits_to_f64(stored: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening: bf16 bit patterns (uint16) or float32 -> float64."""
+    if dtype == "bf16":
+        as_u32 = stored.astype(np.uint32) << np.uint32(16)
+        return as_u32.view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.asarray(stored, dtype=np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _temperature_ok(t: float) -> bool:
+    return bool(np.isfinite(t)) and t >= 0.0
+
+
+# ---------------------------------------------------------------------------
+# the distributions: p = softmax(l / T), q = softmax(d / T)
+# ---------------------------------------------------------------------------
+def softmax_t(logits_row: np.ndarray, T: float) -> np.ndarray:
+    """Temperature softmax in fp64 (R7: the same T for target and draft)."""
+    z = np.asarray(logits_row, dtype=np.float64) / np.float64(T)
+    m = np.max(z)
+    e = np.exp(z - m)
+    return e / np.sum(e)
+
+
+def log_sum_exp_t(logits_row: np.ndarray, T: float) -> float:
+    """log sum_k exp(l_k / T) in fp64."""
+    z = np.asarray(logits_row, dtype=np.float64) / np.float64(T)
+    m = np.max(z)
+    return float(m + np.log(np.sum(np.exp(z - m))))
+
+
+# ---------------------------------------------------------------------------
+# the two elementary steps
+# ---------------------------------------------------------------------------
+def accept_threshold(p_x: float, q_x: float) -> float:
+    """tau = acceptance probability of a draft token x (R2).
+
+    Lecture 17 notes section 2.3: accept outright when q(x) <= p(x), otherwise
+    accept with probability p(x)/q(x)."""
+    if q_x <= p_x:
+        return 1.0
+    return p_x / q_x
+
+
+def residual_weights(p: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Unnormalised residual max(0, p - q) (lecture 17 notes section 2.3 step 4;
+    close-reading notes section 5.1)."""
+    return np.maximum(0.0, p - q)
+
+
+def inverse_cdf_draw(w: np.ndarray, u: float):
+    """Draw a token from weights w with the uniform u (R4).
+
+    Returns (k, margin) where margin = distance of u from the nearer of the two
+    CDF values bracketing k: min(|u - F[k-1]|, |u - F[k]|), F = C / W."""
+    C = np.cumsum(np.asarray(w, dtype=np.float64))
+    W = C[-1]
+    t = np.float64(u) * W
+    k = int(np.searchsorted(C, t, side="right"))
+    if k >= len(C):
+        k = int(np.flatnonzero(np.asarray(w) > 0)[-1])
+    lo = 0.0 if k == 0 else C[k - 1] / W
+    hi = C[k] / W
+    margin = float(min(abs(u - lo), abs(u - hi)))
+    return k, margin
+
+
+# ---------------------------------------------------------------------------
+# chain verification (Algorithm 1)
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class Decision:
+    """One decision taken by the oracle, kept for parity accounting."""
+    kind: str           # "accept" | "draw" | "greedy"
+    position: int       # draft position i (accept), row of the draw, or -1
+    u: float            # the uniform used (nan for greedy)
+    threshold: float    # tau for accept tests, nan otherwise
+    outcome: int        # 1/0 for accept tests, token for draws / greedy
+    margin: float       # |u - tau| or the draw's CDF margin; inf for greedy
+
+
+@dataclasses.dataclass
+class ChainResult:
+    out_tokens: np.ndarray        # [B, gamma+1] int32, -1 padded
+    num_accepted: np.ndarray      # [B] int32, -1 => invalid request
+    decisions: List[List[Decision]]
+
+
+def chain_distributions(target_f64: np.ndarray, draft_f64: Optional[np.ndarray], T: float):
+    """p_1..p_{gamma+1} and q_1..q_gamma of one sampling request (T > 0)."""
+    P = [softmax_t(target_f64[i], T) for i in range(target_f64.shape[0])]
+    Q = [softmax_t(draft_f64[i], T) for i in range(draft_f64.shape[0])]
+    return P, Q
+
+
+def _request_invalid(tokens: np.ndarray, u: np.ndarray, T: float, V: int) -> bool:
+    if not _temperature_ok(T):
+        return True
+    if np.any(tokens < 0) or np.any(tokens >= V):
+        return True
+    if T > 0.0:
+        uu = np.asarray(u, dtype=np.float64)
+        if not np.all(np.isfinite(uu)) or np.any(uu < 0.0) or np.any(uu >= 1.0):
+            return True
+    return False
+
+
+def chain_decide_request(P, Q, target_f64, tokens, u, T):
+    """Accept/reject loop of one request (close-reading notes section 4,
+    acceptance stage; lecture 17 notes section 2.4 steps 3-4).
+
+    P, Q  : lists of fp64 probability rows (sampling) -- unused when T == 0
+    target_f64 : [gamma+1, V] fp64 logits (used for the greedy argmax)
+    Returns (emitted tokens, n, decisions)."""
+    gamma = len(tokens)
+    decisions: List[Decision] = []
+    emitted: List[int] = []
+    if T == 0.0:
+        # R6: greedy verification reduces to argmax equality
+        for i in range(gamma):
+            a = int(np.argmax(target_f64[i]))
+            decisions.append(Decision("greedy", i, float("nan"), float("nan"), a, float("inf")))
+            if int(tokens[i]) != a:
+                return emitted + [a], i, decisions
+            emitted.append(int(tokens[i]))
+        a = int(np.argmax(target_f64[gamma]))
+        decisions.append(Decision("greedy", gamma, float("nan"), float("nan"), a, float("inf")))
+        return emitted + [a], gamma, decisions
+
+    for i in range(gamma):
+        x = int(tokens[i])
+        tau = accept_threshold(P[i][x], Q[i][x])
+        ui = float(u[i])
+        ok = ui <= tau                                     # R1
+        decisions.append(Decision("accept", i, ui, tau, int(ok), abs(ui - tau)))
+        if ok:
+            emitted.append(x)
+            continue
+        w = residual_weights(P[i], Q[i])
+        if not np.sum(w) > 0.0:                            # R5
+            w = P[i]
+        k, margin = inverse_cdf_draw(w, float(u[gamma]))   # R3
+        decisions.append(Decision("draw", i, float(u[gamma]), float("nan"), k, margin))
+        return emitted + [k], i, decisions
+    # every draft accepted: bonus token from p_{gamma+1}
+    k, margin = inverse_cdf_draw(P[gamma], float(u[gamma]))
+    decisions.append(Decision("draw", gamma, float(u[gamma]), float("nan"), k, margin))
+    return emitted + [k], gamma, decisions
+
+
+def verify_chain(target: np.ndarray, draft: Optional[np.ndarray], draft_tokens: np.ndarray,
+                 uniforms: np.ndarray, temperature: np.ndarray, dtype: str,
+                 requests=None) -> ChainResult:
+    """Chain verification of a batch.
+
+    target [B, gamma+1, V], draft [B, gamma, V] (bf16 bits or float32),
+    draft_tokens [B, gamma] int, uniforms [B, gamma+1] float32,
+    temperature [B] float32.  `requests` optionally restricts the work to a
+    subset of request indices (the others are left at -1)."""
+    B, G1, V = target.shape
+    gamma = G1 - 1
+    out = np.full((B, gamma + 1), -1, dtype=np.int32)
+    nacc = np.full(B, -1, dtype=np.int32)
+    decisions: List[List[Decision]] = [[] for _ in range(B)]
+    todo = range(B) if requests is None else requests
+    for b in todo:
+        T = float(np.float32(temperature[b]))
+        toks = np.asarray(draft_tokens[b], dtype=np.int64)
+        u = np.asarray(uniforms[b], dtype=np.float32)
+        if _request_invalid(toks, u, T, V):
+            continue
+        tgt = logits_to_f64(target[b], dtype)
+        if T > 0.0:
+            drf = logits_to_f64(draft[b], dtype)
+            P, Q = chain_distributions(tgt, drf, T)
+        else:
+            P, Q = None, None
+        emitted, n, dec = chain_decide_request(P, Q, tgt, toks, u, T)
+        out[b, :len(emitted)] = emitted
+        nacc[b] = n
+        decisions[b] = dec
+    return ChainResult(out, nacc, decisions)
+
+
+# ---------------------------------------------------------------------------
+# token tree verification
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class TreeResult:
+    out_tokens: np.ndarray      # [B, max_depth+1] int32, -1 padded
+    out_path: np.ndarray        # [B, max_depth+1] int32 accepted node ids, -1 padded
+    num_accepted: np.ndarray    # [B] int32, -1 => invalid request
+    decisions: List[List[Decision]]
+
+
+def tree_node_depths(parents: np.ndarray) -> Optional[np.ndarray]:
+    """Depth of every node, or None when the parent array is malformed (R9)."""
+    N = len(parents)
+    if N < 1 or int(parents[0]) != -1:
+        return None
+    depth = np.zeros(N, dtype=np.int64)
+    for i in range(1, N):
+        p = int(parents[i])
+        if p < 0 or p >= i:
+            return None
+        depth[i] = depth[p] + 1
+    return depth
+
+
+def verify_tree(logits: np.ndarray, node_tokens: np.ndarray, parents: np.ndarray,
+                uniforms: np.ndarray, temperature: np.ndarray, dtype: str,
+                max_depth: int, requests=None) -> TreeResult:
+    """Tree verification of a batch (lecture 17 notes section 4.4 VerifyGreedy
+    for T == 0, section 4.5 naive sampling for T > 0).
+
+    Starting at the root: choose c = argmax p_n (greedy) or draw c from p_n
+    with u[b, n] (naive sampling); if a child of n carries c, accept that
+    child and continue from it, otherwise emit c and stop.  At a leaf the
+    chosen token is the extra token."""
+    B, N, V = logits.shape
+    L1 = max_depth + 1
+    out = np.full((B, L1), -1, dtype=np.int32)
+    path_out = np.full((B, L1), -1, dtype=np.int32)
+    nacc = np.full(B, -1, dtype=np.int32)
+    decisions: List[List[Decision]] = [[] for _ in range(B)]
+    todo = range(B) if requests is None else requests
+    for b in todo:
+        T = float(np.float32(temperature[b]))
+        par = np.asarray(parents[b], dtype=np.int64)
+        tok = np.asarray(node_tokens[b], dtype=np.int64)
+        u = np.asarray(uniforms[b], dtype=np.float32)
+        depth = tree_node_depths(par)
+        if depth is None or not _temperature_ok(T):
+            continue
+        if np.any(depth > max_depth):
+            continue
+        if N > 1 and (np.any(tok[1:] < 0) or np.any(tok[1:] >= V)):
+            continue
+        if T > 0.0:
+            uu = u.astype(np.float64)
+            if not np.all(np.isfinite(uu)) or np.any(uu < 0.0) or np.any(uu >= 1.0):
+                continue
+        node = 0
+        path: List[int] = []
+        dec: List[Decision] = []
+        while True:
+            row = logits_to_f64(logits[b, node], dtype)
+            if T == 0.0:
+                c = int(np.argmax(row))
+                dec.append(Decision("greedy", node, float("nan"), float("nan"), c, float("inf")))
+            else:
+                c, margin = inverse_cdf_draw(softmax_t(row, T), float(u[node]))
+                dec.append(Decision("draw", node, float(u[node]), float("nan"), c, margin))
+            nxt = -1
+            for j in range(node + 1, N):           # children in index order (R9)
+                if int(par[j]) == node and int(tok[j]) == c:
+                    nxt = j
+                    break
+            if nxt < 0:
+                break
+            path.append(nxt)
+            node = nxt
+        emitted = [int(tok[j]) for j in path] + [c]
+        out[b, :len(emitted)] = emitted
+        path_out[b, :len(path)] = path
+        nacc[b] = len(path)
+        decisions[b] = dec
+    return TreeResult(out, path_out, nacc, decisions)
+
+
+# ---------------------------------------------------------------------------
+# debug probabilities
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class ProbsResult:
+    p_at_draft: np.ndarray      # [B, gamma]
+    q_at_draft: np.ndarray      # [B, gamma]
+    residual_mass: np.ndarray   # [B, gamma] = sum_k max(0, p_i(k) - q_i(k))
+    target_lse: np.ndarray      # [B, gamma+1] log sum_k exp(l_k / T)
+    draft_lse: np.ndarray       # [B, gamma]
+
+
+def probs_debug(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray,
+                temperature: np.ndarray, dtype: str, requests=None) -> ProbsResult:
+    """For every draft position i < gamma regardless of where verification
+    stops: p_i(x~_i), q_i(x~_i), the residual mass sum_k max(0, p_i - q_i)
+    (= 1 - sum_k min(p_i, q_i), close-reading notes section 5.1) and the
+    log-normalisers.  Requests with T == 0 (or invalid T) are NaN; a token
+    outside [0, V) gives NaN p/q at that position."""
+    B, G1, V = target.shape
+    gamma = G1 - 1
+    nan = np.float64("nan")
+    pa = np.full((B, gamma), nan)
+    qa = np.full((B, gamma), nan)
+    rm = np.full((B, gamma), nan)
+    lt = np.full((B, gamma + 1), nan)
+    ld = np.full((B, gamma), nan)
+    todo = range(B) if requests is None else requests
+    for b in todo:
+        T = float(np.float32(temperature[b]))
+        if not (_temperature_ok(T) and T > 0.0):
+            continue
+        tgt = logits_to_f64(target[b], dtype)
+        drf = logits_to_f64(draft[b], dtype)
+        for i in range(gamma + 1):
+            lt[b, i] = log_sum_exp_t(tgt[i], T)
+        for i in range(gamma):
+            P = softmax_t(tgt[i], T)
+            Q = softmax_t(drf[i], T)
+            ld[b, i] = log_sum_exp_t(drf[i], T)
+            rm[b, i] = float(np.sum(residual_weights(P, Q)))
+            x = int(draft_tokens[b, i])
+            if 0 <= x < V:
+                pa[b, i] = P[x]
+                qa[b, i] = Q[x]
+    return ProbsResult(pa, qa, rm, lt, ld)
