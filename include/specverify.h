@@ -1,0 +1,196 @@
+/*
+ * libspecverify -- the verification step of speculative decoding on MI355X
+ * (gfx950).  C ABI: plain pointers and sizes, no framework types.
+ *
+ * The operation (chain form) is the acceptance stage of one speculative
+ * decoding round: Leviathan et al.'s Algorithm 1 as restated in "LLM
+ * speculative decoding close-reading notes 02", section 4 (the full
+ * algorithm with uniforms r_i), and in the CMU 15-779 lecture 17 notes,
+ * sections 2.3-2.4.  For each request b, with p_i = softmax(target_i / T)
+ * and q_i = softmax(draft_i / T) (one temperature for both, close-reading
+ * notes section 3):
+ *   for i = 0 .. gamma-1: accept draft token x_i iff u[b][i] <= tau_i,
+ *       tau_i = 1 if q_i(x_i) <= p_i(x_i) else p_i(x_i) / q_i(x_i);
+ *       at the first rejection emit a token drawn from the residual
+ *       max(0, p_i - q_i) (normalised) with u[b][gamma], and stop;
+ *   if all gamma drafts are accepted, emit a bonus token drawn from
+ *       p_gamma with u[b][gamma].
+ * Greedy requests (T == 0) accept iff x_i == argmax p_i and emit the argmax
+ * at the first mismatch, or argmax p_gamma after gamma matches
+ * (close-reading notes section 10).
+ *
+ * Conventions shared by every entry point:
+ *  - All array arguments are DEVICE pointers (HIP device memory), row-major
+ *    and contiguous, owned by the caller.  The library never allocates or
+ *    frees memory on a call.
+ *  - Calls are asynchronous on `hip_stream` (a hipStream_t, NULL = the
+ *    default stream).  The return code reports only what the host can see
+ *    before launching: NULL pointers, unsupported shapes, dtype, workspace
+ *    size/alignment, misaligned pointers and launch failures.  Outputs are
+ *    valid once the stream has been synchronised.
+ *  - Bad data inside an otherwise valid call (a draft or node token outside
+ *    [0, V), a temperature that is negative, NaN, infinite or positive but
+ *    below the smallest normal float (1.17549435e-38), a sampling
+ *    request whose uniforms are not all in [0, 1), a malformed parent array,
+ *    a tree deeper than max_depth, draft_logits == NULL for a sampling
+ *    request) marks that request invalid: its accepted count is -1 and all
+ *    its output tokens are -1.  Other requests are unaffected.
+ *  - Logits must be finite or -inf (masked); each row needs at least one
+ *    finite entry.  NaN / +inf logits give unspecified tokens.
+ *  - Inverse-CDF draws: with weights w_k in vocabulary order, C_k their
+ *    running sum and W = C_{V-1}, the token is the smallest k with
+ *    C_k > u * W (zero-weight tokens are never drawn).  Argmax ties go to
+ *    the lowest index.
+ *  - Workspace: a device buffer of at least the size returned by the
+ *    matching *_workspace_bytes query, 256-byte aligned.  It must be
+ *    zero-filled before its first use (e.g. allocate it zeroed, or call
+ *    sv_workspace_clear); every call that completes leaves it zero-filled
+ *    again.  One workspace serves one call at a time: calls that may overlap
+ *    (different streams) need different workspaces.
+ *  - The library is stateless and reentrant; it draws no random numbers.
+ *    All randomness is the caller's uniforms (close-reading notes section
+ *    11.3: deterministic, per-request random streams).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SV_API __attribute__((visibility("default")))
+#else
+#define SV_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_NULL = 1,        /* a required pointer is NULL */
+  SV_ERR_SHAPE = 2,       /* B, gamma, V, N or max_depth outside the limits below */
+  SV_ERR_DTYPE = 3,       /* dtype is not one of sv_dtype */
+  SV_ERR_WORKSPACE = 4,   /* workspace too small or not 256-byte aligned */
+  SV_ERR_ALIGN = 5,       /* a logit pointer is not aligned to its element size */
+  SV_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed */
+} sv_status;
+
+typedef enum {
+  SV_BF16 = 0,            /* logits are bfloat16 (raw 16-bit patterns) */
+  SV_F32 = 1              /* logits are IEEE float32 */
+} sv_dtype;
+
+/* Limits checked on the host (SV_ERR_SHAPE otherwise). */
+#define SV_MAX_GAMMA 32
+#define SV_MAX_VOCAB (1 << 24)
+#define SV_MAX_TREE_NODES 1024
+#define SV_MAX_TREE_DEPTH 64
+
+/* Text for a status code (static storage; never NULL). */
+SV_API const char* sv_status_string(int status);
+
+/* Library version as "major.minor.patch" (static storage). */
+SV_API const char* sv_version(void);
+
+/*
+ * Zero-fill `bytes` of a workspace on `hip_stream` with a fill kernel (safe
+ * under stream capture).  Only needed after an aborted call or for a new
+ * buffer that was not allocated zeroed.
+ */
+SV_API int sv_workspace_clear(void* workspace, size_t bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Chain verification.
+ *
+ * target_logits    [B][gamma+1][V]  dtype   target rows p_1 .. p_{gamma+1}
+ * draft_logits     [B][gamma][V]    dtype   draft rows q_1 .. q_gamma; may be
+ *                                           NULL if every request is greedy
+ * draft_tokens     [B][gamma]       int32   x_1 .. x_gamma (may be NULL if gamma == 0)
+ * uniforms         [B][gamma+1]     float   u[b][i], i < gamma: accept test of
+ *                                           draft i; u[b][gamma]: the final
+ *                                           draw (residual or bonus).  Read
+ *                                           only for sampling requests.
+ * temperature      [B]              float   T > 0 sampling, T == 0 greedy
+ * out_tokens       [B][gamma+1]     int32   emitted tokens x_1..x_n, then the
+ *                                           resampled/bonus/argmax token; the
+ *                                           rest is -1
+ * out_num_accepted [B]              int32   n in [0, gamma] (n + 1 tokens are
+ *                                           emitted; the caller rolls back
+ *                                           gamma - n cached positions), or -1
+ * Limits: B >= 0 (B == 0 is a no-op), 0 <= gamma <= SV_MAX_GAMMA,
+ *         1 <= V <= SV_MAX_VOCAB.
+ * Returns an sv_status.
+ * ---------------------------------------------------------------------- */
+SV_API size_t sv_chain_workspace_bytes(int B, int gamma, int V, int dtype);
+
+SV_API int spec_verify_chain(const void* target_logits, const void* draft_logits,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      const float* temperature, int B, int gamma, int V, int dtype,
+                      int32_t* out_tokens, int32_t* out_num_accepted,
+                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Token-tree verification (CMU 15-779 lecture 17 notes, section 4.4
+ * VerifyGreedy for T == 0 and section 4.5 naive sampling for T > 0).
+ *
+ * Each request holds a token tree of N nodes linearised depth-first
+ * (ancestors first, section 4.3); node 0 is the root, the last verified
+ * token.  From the root: pick c = argmax p_n (greedy) or draw c from p_n with
+ * u[b][n] (naive sampling); if a child of n carries c (children in index
+ * order, the lowest index wins on duplicate tokens) accept that child and
+ * continue from it, otherwise emit c and stop.  At a leaf c is the extra
+ * token.
+ *
+ * target_logits  [B][N][V]  dtype  one target row per node
+ * node_tokens    [B][N]     int32  token of each node (entry 0 ignored)
+ * parents        [B][N]     int32  parents[b][0] == -1, 0 <= parents[b][i] < i
+ * uniforms       [B][N]     float  u[b][n] for the draw at node n (sampling only)
+ * temperature    [B]        float  0 greedy descent, > 0 naive sampling
+ * max_depth                        every node's depth must be <= max_depth
+ * out_tokens     [B][max_depth+1] int32  accepted node tokens, then the extra
+ *                                        token; -1 padded
+ * out_path_nodes [B][max_depth+1] int32  accepted node ids (their positions in
+ *                                        the linearised KV cache); -1 padded
+ * out_num_accepted [B]            int32  number of accepted nodes, or -1
+ * Limits: B >= 0, 1 <= N <= SV_MAX_TREE_NODES, 1 <= V <= SV_MAX_VOCAB,
+ *         0 <= max_depth <= SV_MAX_TREE_DEPTH.
+ * ---------------------------------------------------------------------- */
+SV_API size_t sv_tree_workspace_bytes(int B, int N, int V, int dtype);
+
+SV_API int spec_verify_tree(const void* target_logits, const int32_t* node_tokens,
+                     const int32_t* parents, const float* uniforms,
+                     const float* temperature, int B, int N, int V, int max_depth,
+                     int dtype, int32_t* out_tokens, int32_t* out_path_nodes,
+                     int32_t* out_num_accepted, void* workspace,
+                     size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Debug probabilities for every draft position i < gamma, whether or not
+ * verification would reach it:
+ *   p_at_draft[b][i]    = p_i(x_i)
+ *   q_at_draft[b][i]    = q_i(x_i)
+ *   residual_mass[b][i] = sum_k max(0, p_i(k) - q_i(k)) = 1 - sum_k min(p_i, q_i)
+ *                         (close-reading notes section 5.1; lecture 17 notes
+ *                         section 2.3, acceptance rate = 1 - this)
+ *   target_lse[b][i]    = log sum_k exp(target_i(k) / T), i <= gamma (optional, may be NULL)
+ *   draft_lse[b][i]     = log sum_k exp(draft_i(k) / T), i < gamma  (optional, may be NULL)
+ * Requests with T == 0 or an invalid T produce NaN; a token outside [0, V)
+ * gives NaN p/q at that position.  Arrays are float32, [B][gamma] unless
+ * stated.  Limits as for spec_verify_chain.
+ * ---------------------------------------------------------------------- */
+SV_API size_t sv_probs_workspace_bytes(int B, int gamma, int V, int dtype);
+
+SV_API int spec_probs_debug(const void* target_logits, const void* draft_logits,
+                     const int32_t* draft_tokens, const float* temperature,
+                     int B, int gamma, int V, int dtype,
+                     float* p_at_draft, float* q_at_draft, float* residual_mass,
+                     float* target_lse, float* draft_lse,
+                     void* workspace, size_t workspace_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

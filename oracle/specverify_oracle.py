@@ -33,8 +33,8 @@ R9  token tree: node 0 is the root (the last verified token), parents[0] =
     the lowest-index child carrying the chosen token is taken.
 R10 tree uniforms: u[b, n] is used for the draw at node n when n is visited.
 R11 bad input makes a whole request invalid (count -1, tokens -1): a draft
-    token or tree node token outside [0, V), a temperature that is negative
-    or not finite, a sampling request with a uniform outside [0, 1), a
+    token or tree node token outside [0, V), a temperature that is negative,
+    not finite, or positive but below the smallest normal float32, a sampling request with a uniform outside [0, 1), a
     malformed parent array, or a tree deeper than max_depth.
 """
 from __future__ import annotations
@@ -58,8 +58,12 @@ def logits_to_f64(stored: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+FLT_MIN = 1.1754943508222875e-38   # smallest normal float32
+
+
 def _temperature_ok(t: float) -> bool:
-    return bool(np.isfinite(t)) and t >= 0.0
+    """R11: T must be 0 (greedy) or a finite positive normal float32."""
+    return bool(np.isfinite(t)) and (t == 0.0 or t >= FLT_MIN)
 
 
 # ---------------------------------------------------------------------------

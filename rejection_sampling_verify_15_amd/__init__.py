@@ -1,0 +1,14 @@
+"""libspecverify: the verification step of speculative decoding on MI355X.
+
+The compute lives in hand-written HIP kernels behind a C ABI
+(include/specverify.h, libspecverify.so built in this directory); this
+package is a thin argument-marshalling binding over it.
+"""
+from . import build  # noqa: F401
+from .binding import (  # noqa: F401
+    SVError, lib, library_path, probs_debug, verify_chain, verify_tree, workspace,
+    SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_ALIGN, SV_ERR_HIP,
+    SV_BF16, SV_F32,
+)
+
+__all__ = ["verify_chain", "verify_tree", "probs_debug", "lib", "SVError", "workspace"]

@@ -1,0 +1,228 @@
+"""Thin ctypes binding of libspecverify (argument marshalling only).
+
+Every computation happens in the HIP library; this module only checks
+shapes, allocates outputs and a workspace with torch, and passes raw device
+pointers plus the current HIP stream through the C ABI declared in
+include/specverify.h.  If the library has not been built, loading fails
+loudly: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+
+SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_ALIGN, SV_ERR_HIP = range(7)
+SV_BF16, SV_F32 = 0, 1
+SV_MAX_GAMMA = 32
+
+EXPORTS = {
+    # name: (restype, argtypes)
+    "sv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "sv_version": (ctypes.c_char_p, []),
+    "sv_workspace_clear": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "sv_chain_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "spec_verify_chain": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 +
+                          [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "sv_tree_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "spec_verify_tree": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 +
+                         [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "sv_probs_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "spec_probs_debug": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 4 +
+                         [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]),
+}
+
+_LIB = None
+_LOCK = threading.Lock()
+
+
+class SVError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().sv_status_string(status).decode() if _LIB is not None else str(status)
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libspecverify.so (built in-tree by build.build())."""
+    global _LIB
+    with _LOCK:
+        if _LIB is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise RuntimeError(
+                    f"{path} is missing: build it with "
+                    "`python -m rejection_sampling_verify_15_amd.build` (no CPU fallback exists)")
+            handle = ctypes.CDLL(path)
+            for name, (res, args) in EXPORTS.items():
+                fn = getattr(handle, name)
+                fn.restype = res
+                fn.argtypes = args
+            _LIB = handle
+    return _LIB
+
+
+def _check(status: int, where: str):
+    if status != SV_OK:
+        raise SVError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need_cuda(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# workspaces: zero-filled at allocation, cached per (device, stream)
+# ---------------------------------------------------------------------------
+_WORKSPACES = {}
+
+
+def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    """A zero-initialised device workspace of at least nbytes for the current
+    stream.  The library leaves a workspace zero-filled after every call, so
+    it is reused as is; calls on one stream never overlap."""
+    stream = torch.cuda.current_stream(device).cuda_stream
+    key = (device.index, stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        size = max(int(nbytes), 256)
+        if ws is not None:
+            size = max(size, 2 * ws.numel())
+        ws = torch.zeros(size, dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: torch.Tensor,
+                 uniforms: torch.Tensor, temperature: torch.Tensor,
+                 out_tokens: Optional[torch.Tensor] = None,
+                 out_num_accepted: Optional[torch.Tensor] = None,
+                 ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """spec_verify_chain over device tensors.
+
+    target [B, gamma+1, V] and draft [B, gamma, V] (bf16 or fp32, same dtype),
+    draft_tokens [B, gamma] int32, uniforms [B, gamma+1] fp32,
+    temperature [B] fp32.  Returns (out_tokens [B, gamma+1] int32,
+    out_num_accepted [B] int32)."""
+    _need_cuda(target, "target")
+    if target.dim() != 3:
+        raise ValueError("target must be [B, gamma+1, V]")
+    B, G1, V = target.shape
+    gamma = G1 - 1
+    dev = target.device
+    dt = _dtype_code(target)
+    if draft is not None:
+        _need_cuda(draft, "draft")
+        if draft.dtype != target.dtype or tuple(draft.shape) != (B, gamma, V):
+            raise ValueError("draft must match target's dtype with shape [B, gamma, V]")
+    for name, t, shape, dtype in (("draft_tokens", draft_tokens, (B, gamma), torch.int32),
+                                  ("uniforms", uniforms, (B, gamma + 1), torch.float32),
+                                  ("temperature", temperature, (B,), torch.float32)):
+        _need_cuda(t, name)
+        if tuple(t.shape) != shape or t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype} with shape {shape}")
+    if out_tokens is None:
+        out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    L = lib()
+    nbytes = L.sv_chain_workspace_bytes(B, gamma, V, dt)
+    if ws is None:
+        ws = workspace(nbytes, dev)
+    st = L.spec_verify_chain(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
+                             _ptr(temperature), B, gamma, V, dt, _ptr(out_tokens),
+                             _ptr(out_num_accepted), _ptr(ws), ws.numel(), _stream_handle(dev))
+    _check(st, "spec_verify_chain")
+    return out_tokens, out_num_accepted
+
+
+def verify_tree(logits: torch.Tensor, node_tokens: torch.Tensor, parents: torch.Tensor,
+                uniforms: torch.Tensor, temperature: torch.Tensor, max_depth: int,
+                ws: Optional[torch.Tensor] = None):
+    """spec_verify_tree over device tensors.  Returns (out_tokens, out_path_nodes,
+    out_num_accepted) with shapes [B, max_depth+1], [B, max_depth+1], [B]."""
+    _need_cuda(logits, "logits")
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, N, V]")
+    B, N, V = logits.shape
+    dev = logits.device
+    dt = _dtype_code(logits)
+    for name, t, shape, dtype in (("node_tokens", node_tokens, (B, N), torch.int32),
+                                  ("parents", parents, (B, N), torch.int32),
+                                  ("uniforms", uniforms, (B, N), torch.float32),
+                                  ("temperature", temperature, (B,), torch.float32)):
+        _need_cuda(t, name)
+        if tuple(t.shape) != shape or t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype} with shape {shape}")
+    out_tokens = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    out_path = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    out_n = torch.empty((B,), dtype=torch.int32, device=dev)
+    L = lib()
+    nbytes = L.sv_tree_workspace_bytes(B, N, V, dt)
+    if ws is None:
+        ws = workspace(nbytes, dev)
+    st = L.spec_verify_tree(_ptr(logits), _ptr(node_tokens), _ptr(parents), _ptr(uniforms),
+                            _ptr(temperature), B, N, V, int(max_depth), dt, _ptr(out_tokens),
+                            _ptr(out_path), _ptr(out_n), _ptr(ws), ws.numel(), _stream_handle(dev))
+    _check(st, "spec_verify_tree")
+    return out_tokens, out_path, out_n
+
+
+def probs_debug(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                temperature: torch.Tensor, ws: Optional[torch.Tensor] = None):
+    """spec_probs_debug over device tensors.  Returns a dict of float32 tensors:
+    p_at_draft, q_at_draft, residual_mass [B, gamma], target_lse [B, gamma+1],
+    draft_lse [B, gamma]."""
+    _need_cuda(target, "target")
+    B, G1, V = target.shape
+    gamma = G1 - 1
+    dev = target.device
+    dt = _dtype_code(target)
+    _need_cuda(draft, "draft")
+    if draft.dtype != target.dtype or tuple(draft.shape) != (B, gamma, V):
+        raise ValueError("draft must match target's dtype with shape [B, gamma, V]")
+    _need_cuda(draft_tokens, "draft_tokens")
+    _need_cuda(temperature, "temperature")
+    out = {k: torch.empty((B, gamma), dtype=torch.float32, device=dev)
+           for k in ("p_at_draft", "q_at_draft", "residual_mass", "draft_lse")}
+    out["target_lse"] = torch.empty((B, gamma + 1), dtype=torch.float32, device=dev)
+    L = lib()
+    nbytes = L.sv_probs_workspace_bytes(B, gamma, V, dt)
+    if ws is None:
+        ws = workspace(nbytes, dev)
+    st = L.spec_probs_debug(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(temperature),
+                            B, gamma, V, dt, _ptr(out["p_at_draft"]), _ptr(out["q_at_draft"]),
+                            _ptr(out["residual_mass"]), _ptr(out["target_lse"]),
+                            _ptr(out["draft_lse"]), _ptr(ws), ws.numel(), _stream_handle(dev))
+    _check(st, "spec_probs_debug")
+    return out

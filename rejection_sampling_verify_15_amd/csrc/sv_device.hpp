@@ -1,0 +1,224 @@
+// Device building blocks shared by the libspecverify kernels (gfx950, wave64).
+//
+// Row streaming: a (row, chunk) work item covers kChunk consecutive logits of
+// one vocabulary row.  A 256-thread workgroup reads it with 16-byte loads
+// (8 bf16 or 4 fp32 per lane); load j of the workgroup covers one contiguous
+// span of kThreads * kVec elements, so every wave reads 1 KiB contiguous per
+// instruction.  Rows that are not 16-byte aligned, or whose length is not a
+// multiple of the vector width, take the scalar variant of the same loops.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kThreads = 256;
+constexpr int kWave = 64;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kChunk = 8192;  // logits per (row, chunk) work item
+
+__host__ __device__ inline int num_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+
+// ---------------------------------------------------------------------------
+// element access
+// ---------------------------------------------------------------------------
+template <int DT> struct Elem;
+
+template <> struct Elem<0> {  // bf16 stored as raw 16-bit patterns
+  static constexpr int kVec = 8;
+  __device__ static inline float at(const void* row, int k) {
+    const uint16_t b = static_cast<const uint16_t*>(row)[k];
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+  }
+  __device__ static inline void vec(const void* row, int k, float (&x)[kVec]) {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + k);
+    const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(q[i] << 16);
+      x[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+    }
+  }
+};
+
+template <> struct Elem<1> {  // float32
+  static constexpr int kVec = 4;
+  __device__ static inline float at(const void* row, int k) {
+    return static_cast<const float*>(row)[k];
+  }
+  __device__ static inline void vec(const void* row, int k, float (&x)[kVec]) {
+    const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(row) + k);
+    x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
+  }
+};
+
+// Per-thread slice of one chunk: kItems groups of kPer consecutive elements.
+// Group j of thread t starts at element c0 + (j * kThreads + t) * kPer.
+template <int DT, bool VEC> struct Slice {
+  static constexpr int kPer = VEC ? Elem<DT>::kVec : 1;
+  static constexpr int kItems = kChunk / (kThreads * kPer);
+  static constexpr int kN = kItems * kPer;
+  float x[kItems][kPer];
+
+  __device__ static inline int index(int c0, int j, int e) {
+    return c0 + (j * kThreads + static_cast<int>(threadIdx.x)) * kPer + e;
+  }
+
+  // Loads [c0, c1) of `row`; out-of-range slots get -inf.
+  __device__ inline void load(const void* row, int c0, int c1) {
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+      const int k0 = index(c0, j, 0);
+      if constexpr (VEC) {
+        if (k0 < c1) {
+          Elem<DT>::vec(row, k0, x[j]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) x[j][e] = -INFINITY;
+        }
+      } else {
+        x[j][0] = (k0 < c1) ? Elem<DT>::at(row, k0) : -INFINITY;
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// reductions
+// ---------------------------------------------------------------------------
+// (value, index) argmax with the lowest index among equal values.
+struct ArgMax {
+  float v;
+  int i;
+};
+
+__device__ inline ArgMax argmax_combine(ArgMax a, ArgMax b) {
+  return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
+}
+
+// Running (max, sum of exp2((x - max) * s)) pair of a softmax normaliser.
+struct MaxSum {
+  float m;
+  float z;
+};
+
+__device__ inline float scale_to(float m_from, float m_to, float s) {
+  return (m_from == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_from - m_to) * s);
+}
+
+__device__ inline MaxSum maxsum_combine(MaxSum a, MaxSum b, float s) {
+  const float m = fmaxf(a.m, b.m);
+  if (m == -INFINITY) return {m, 0.0f};
+  return {m, a.z * scale_to(a.m, m, s) + b.z * scale_to(b.m, m, s)};
+}
+
+template <typename T> __device__ inline T wave_sum(T v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ inline ArgMax wave_argmax(ArgMax a) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    ArgMax b{__shfl_xor(a.v, o, kWave), __shfl_xor(a.i, o, kWave)};
+    a = argmax_combine(a, b);
+  }
+  return a;
+}
+
+__device__ inline MaxSum wave_maxsum(MaxSum a, float s) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    MaxSum b{__shfl_xor(a.m, o, kWave), __shfl_xor(a.z, o, kWave)};
+    a = maxsum_combine(a, b, s);
+  }
+  return a;
+}
+
+// Workgroup reductions through LDS; every thread receives the result.
+__device__ inline ArgMax block_argmax(ArgMax a) {
+  __shared__ float sv[kWaves];
+  __shared__ int si[kWaves];
+  a = wave_argmax(a);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x % kWave) == 0) { sv[w] = a.v; si[w] = a.i; }
+  __syncthreads();
+  ArgMax r{sv[0], si[0]};
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = argmax_combine(r, ArgMax{sv[i], si[i]});
+  __syncthreads();
+  return r;
+}
+
+__device__ inline MaxSum block_maxsum(MaxSum a, float s) {
+  __shared__ float sm[kWaves];
+  __shared__ float sz[kWaves];
+  a = wave_maxsum(a, s);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x % kWave) == 0) { sm[w] = a.m; sz[w] = a.z; }
+  __syncthreads();
+  MaxSum r{sm[0], sz[0]};
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = maxsum_combine(r, MaxSum{sm[i], sz[i]}, s);
+  __syncthreads();
+  return r;
+}
+
+template <int NV>
+__device__ inline void block_sum_doubles(double (&v)[NV]) {
+  __shared__ double sd[NV][kWaves];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) v[k] = wave_sum(v[k]);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x % kWave) == 0) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) sd[k][w] = v[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) t += sd[k][i];
+    v[k] = t;
+  }
+  __syncthreads();
+}
+
+// Exclusive prefix sum over the workgroup of one double per thread (lanes in
+// thread order); returns this thread's exclusive prefix and writes the total
+// to *total.
+__device__ inline double block_exclusive_scan(double v, double* total) {
+  __shared__ double sw[kWaves];
+  const int lane = threadIdx.x % kWave;
+  const int w = threadIdx.x / kWave;
+  double inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double t = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += t;
+  }
+  double exc = __shfl_up(inc, 1, kWave);
+  if (lane == 0) exc = 0.0;
+  if (lane == kWave - 1) sw[w] = inc;
+  __syncthreads();
+  double before = 0.0, all = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < w) before += sw[i];
+    all += sw[i];
+  }
+  __syncthreads();
+  *total = all;
+  return before + exc;
+}
+
+}  // namespace sv

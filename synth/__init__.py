@@ -23,7 +23,8 @@ and always in [0, 1).
 from __future__ import annotations
 
 import dataclasses
-import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Optional
 
 import numpy as np
@@ -44,9 +45,23 @@ TREE = dict(B=32, N=64, V=128256, max_depth=8)
 # --------------------------------------------------------------------------
 def bf16_round_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit pattern (uint16), round to nearest, ties to even."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
-    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    src = x.reshape(-1).view(np.uint32)
+    dst = out.reshape(-1)
+    step = 1 << 20
+    n = src.size
+
+    def work(i):
+        u = src[i * step:(i + 1) * step]
+        t = u >> np.uint32(16)
+        t &= np.uint32(1)
+        t += np.uint32(0x7FFF)
+        t += u
+        t >>= np.uint32(16)
+        dst[i * step:(i + 1) * step] = t
+    _run_blocks(work, (n + step - 1) // step)
+    return out
 
 
 def bf16_bits_as_float32(bits: np.ndarray) -> np.ndarray:
@@ -70,19 +85,67 @@ def _streams(seed: int, n: int):
     return [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(n)]
 
 
+# Bulk generation runs on fixed blocks of rows, each with its own generator
+# spawned from the stream's seed, so results do not depend on the number of
+# worker threads.
+ROWS_PER_BLOCK = 16
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _block_rngs(rng: np.random.Generator, rows: int):
+    nblk = (rows + ROWS_PER_BLOCK - 1) // ROWS_PER_BLOCK
+    seeds = rng.integers(0, 2 ** 63 - 1, size=nblk, dtype=np.int64)
+    return [np.random.default_rng(int(x)) for x in seeds]
+
+
+def _run_blocks(fn, nblk: int):
+    if nblk <= 1 or _THREADS == 1:
+        for i in range(nblk):
+            fn(i)
+        return
+    with ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(fn, range(nblk)))
+
+
+def normal_rows(rng: np.random.Generator, rows: int, V: int, std: float = 1.0) -> np.ndarray:
+    """float32 [rows, V] of N(0, std^2), generated block-parallel."""
+    out = np.empty((rows, V), dtype=np.float32)
+    gens = _block_rngs(rng, rows)
+
+    def work(i):
+        sl = out[i * ROWS_PER_BLOCK:(i + 1) * ROWS_PER_BLOCK]
+        gens[i].standard_normal(out=sl, dtype=np.float32)
+        if std != 1.0:
+            sl *= np.float32(std)
+    _run_blocks(work, len(gens))
+    return out
+
+
+def shuffle_rows(rng: np.random.Generator, x: np.ndarray) -> np.ndarray:
+    """Independent uniform random permutation of every row of x (in place)."""
+    gens = _block_rngs(rng, x.shape[0])
+
+    def work(i):
+        sl = x[i * ROWS_PER_BLOCK:(i + 1) * ROWS_PER_BLOCK]
+        for r in range(sl.shape[0]):
+            gens[i].shuffle(sl[r])
+    _run_blocks(work, len(gens))
+    return x
+
+
 # --------------------------------------------------------------------------
 # logit families
 # --------------------------------------------------------------------------
 def gaussian_logits(rng, rows: int, V: int, std: float = 1.0) -> np.ndarray:
     """i.i.d. N(0, std^2) logits, float32 [rows, V]."""
-    return rng.standard_normal((rows, V), dtype=np.float32) * np.float32(std)
+    return normal_rows(rng, rows, V, std)
 
 
 def peaked_logits(rng, rows: int, V: int, std: float = 2.0, boost: float = 8.0,
                   frac: float = 0.01) -> np.ndarray:
     """N(0, std^2) logits with round(frac*V) distinct entries per row raised by
     `boost` (a confident head over a long tail)."""
-    x = rng.standard_normal((rows, V), dtype=np.float32) * np.float32(std)
+    x = normal_rows(rng, rows, V, std)
     k = int(round(frac * V))
     if k > 0:
         for r in range(rows):
@@ -95,8 +158,9 @@ def zipf_logits(rng, rows: int, V: int, slope: float = 1.1,
                 noise: float = 0.5) -> np.ndarray:
     """-slope*ln(rank) + N(0, noise^2), ranks permuted independently per row."""
     base = (-slope * np.log(np.arange(1, V + 1, dtype=np.float64))).astype(np.float32)
-    x = base[None, :] + rng.standard_normal((rows, V), dtype=np.float32) * np.float32(noise)
-    return rng.permuted(x, axis=1)
+    x = normal_rows(rng, rows, V, noise)
+    x += base[None, :]
+    return shuffle_rows(rng, x)
 
 
 FAMILIES = {"gauss": gaussian_logits, "peaked": peaked_logits, "zipf": zipf_logits}
@@ -150,14 +214,17 @@ def sample_draft_tokens(rng, draft_stored: np.ndarray, dtype: str,
     draft logits; argmax of the draft logits for greedy (T == 0) requests."""
     B, G, V = draft_stored.shape
     out = np.empty((B, G), dtype=np.int32)
-    for b in range(B):
+    seeds = rng.integers(0, 2 ** 63 - 1, size=B, dtype=np.int64)
+
+    def work(b):
         d = _widen(draft_stored[b], dtype).astype(np.float32)
         t = float(temperature[b])
         if t > 0.0:
-            keys = d / np.float32(t) + gumbel(rng, d.shape)
+            keys = d / np.float32(t) + gumbel(np.random.default_rng(int(seeds[b])), d.shape)
             out[b] = np.argmax(keys, axis=1)
         else:
             out[b] = np.argmax(d, axis=1)
+    _run_blocks(work, B)
     return out
 
 
@@ -179,9 +246,9 @@ def chain_inputs(seed: int, B: int, gamma: int, V: int, dtype: str = "bf16",
         sig = r_mode.uniform(draft_sigma[0], draft_sigma[1], size=B).astype(np.float32)
     else:
         sig = np.full(B, draft_sigma, dtype=np.float32)
-    noise = r_noise.standard_normal((B, gamma, V), dtype=np.float32) * sig[:, None, None]
-    drf = tgt[:, :gamma, :] + noise
-    del noise
+    drf = normal_rows(r_noise, B * gamma, V).reshape(B, gamma, V)
+    drf *= sig[:, None, None]
+    drf += tgt[:, :gamma, :]
     T = np.full(B, temperature, dtype=np.float32)
     if greedy_odd:
         T[1::2] = 0.0

@@ -1,0 +1,175 @@
+"""GPU-vs-oracle comparison helpers (test infrastructure).
+
+Parity bar (from the workload statement): emitted tokens and accepted counts
+are bit-exact, except at decision-boundary cases where the uniform lies
+within 1e-5 of the decision's threshold (|u - tau| for an accept test, the
+distance to the nearer CDF step for a draw).  A GPU != oracle decision
+outside that window is a hard failure; inside it, such mismatches must stay
+below 0.01% of all decisions.  Once a request diverges, its later decisions
+are not compared.  Greedy decisions are always exact.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+WINDOW = 1e-5
+MAX_MISMATCH_RATE = 1e-4
+
+
+@dataclasses.dataclass
+class Tally:
+    decisions: int = 0
+    in_window: int = 0
+    mismatches: int = 0          # inside the window
+    hard: list = dataclasses.field(default_factory=list)
+
+    def add(self, other: "Tally"):
+        self.decisions += other.decisions
+        self.in_window += other.in_window
+        self.mismatches += other.mismatches
+        self.hard.extend(other.hard)
+
+    def check(self, label=""):
+        assert not self.hard, f"{label}: decisions differ outside the 1e-5 window: {self.hard[:5]}"
+        if self.decisions:
+            rate = self.mismatches / self.decisions
+            assert rate < MAX_MISMATCH_RATE, (
+                f"{label}: boundary mismatches {self.mismatches}/{self.decisions} = {rate:.2e}")
+
+    def __str__(self):
+        return (f"decisions={self.decisions} in_window={self.in_window} "
+                f"boundary_mismatches={self.mismatches} hard={len(self.hard)}")
+
+
+def compare_chain_request(b, gamma, dec, emitted_or, n_or, tok_gpu, n_gpu) -> Tally:
+    """Walk the oracle's decisions of request b against the GPU's outputs."""
+    t = Tally()
+    if n_or < 0:
+        if n_gpu != -1 or (tok_gpu != -1).any():
+            t.hard.append((b, "invalid request not flagged", n_gpu))
+        return t
+    for d in dec:
+        t.decisions += 1
+        if d.margin < WINDOW:
+            t.in_window += 1
+        if d.kind == "accept":
+            gpu_acc = int(n_gpu > d.position)
+            same = gpu_acc == d.outcome
+        elif d.kind == "draw":
+            same = (n_gpu == n_or) and int(tok_gpu[n_or]) == d.outcome
+        else:  # greedy
+            if d.position < n_or:
+                same = n_gpu > d.position
+            else:
+                same = (n_gpu == n_or) and int(tok_gpu[n_or]) == d.outcome
+        if not same:
+            if d.margin < WINDOW:
+                t.mismatches += 1
+            else:
+                t.hard.append((b, d.kind, d.position, d.margin, n_or, n_gpu))
+            return t
+    # every decision agreed: the outputs must agree exactly
+    exp = np.full(gamma + 1, -1, dtype=np.int64)
+    exp[:len(emitted_or)] = emitted_or
+    if n_gpu != n_or or not np.array_equal(tok_gpu.astype(np.int64), exp):
+        t.hard.append((b, "outputs differ although decisions agree", n_or, n_gpu))
+    return t
+
+
+def compare_chain(res, tok_gpu, n_gpu, requests=None) -> Tally:
+    tally = Tally()
+    B, G1 = res.out_tokens.shape
+    todo = range(B) if requests is None else requests
+    for b in todo:
+        n_or = int(res.num_accepted[b])
+        emitted = [int(x) for x in res.out_tokens[b] if x >= 0] if n_or >= 0 else []
+        tally.add(compare_chain_request(b, G1 - 1, res.decisions[b], emitted, n_or,
+                                        tok_gpu[b], int(n_gpu[b])))
+    return tally
+
+
+def compare_tree(res, tok_gpu, path_gpu, n_gpu, requests=None) -> Tally:
+    tally = Tally()
+    B = res.out_tokens.shape[0]
+    todo = range(B) if requests is None else requests
+    for b in todo:
+        t = Tally()
+        n_or = int(res.num_accepted[b])
+        if n_or < 0:
+            if int(n_gpu[b]) != -1:
+                t.hard.append((b, "invalid tree not flagged"))
+            tally.add(t)
+            continue
+        for step, d in enumerate(res.decisions[b]):
+            t.decisions += 1
+            if d.margin < WINDOW:
+                t.in_window += 1
+            # the GPU took the same decision at this step iff its output token
+            # at slot `step` equals the oracle's choice
+            if int(tok_gpu[b, step]) != d.outcome:
+                if d.margin < WINDOW:
+                    t.mismatches += 1
+                else:
+                    t.hard.append((b, step, d.kind, d.margin))
+                break
+        else:
+            if (int(n_gpu[b]) != n_or or not np.array_equal(tok_gpu[b], res.out_tokens[b])
+                    or not np.array_equal(path_gpu[b], res.out_path[b])):
+                t.hard.append((b, "tree outputs differ although decisions agree"))
+        tally.add(t)
+    return tally
+
+
+# ---------------------------------------------------------------------------
+# device transfer
+# ---------------------------------------------------------------------------
+def to_device_logits(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def to_device(arr: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+
+
+# ---------------------------------------------------------------------------
+# the oracle over many uniform sets (request-major, distributions reused)
+# ---------------------------------------------------------------------------
+def oracle_chain_many(ci, u_sets, requests=None):
+    """Oracle chain results for each uniform set in u_sets, computing every
+    request's distributions once.  Returns a list of oracle ChainResult."""
+    import oracle
+    from oracle import specverify_oracle as so
+
+    B, G = ci.B, ci.gamma
+    todo = list(range(B)) if requests is None else list(requests)
+    base = oracle.verify_chain(ci.target, ci.draft, ci.draft_tokens, u_sets[0], ci.temperature,
+                               ci.dtype, requests=[])
+    results = []
+    for _ in u_sets:
+        results.append(so.ChainResult(np.full((B, G + 1), -1, dtype=np.int32),
+                                      np.full(B, -1, dtype=np.int32), [[] for _ in range(B)]))
+    del base
+    for b in todo:
+        T = float(np.float32(ci.temperature[b]))
+        toks = np.asarray(ci.draft_tokens[b], dtype=np.int64)
+        # validity (uniform sets are generated inside [0, 1))
+        if so._request_invalid(toks, u_sets[0][b], T, ci.V):
+            continue
+        tgt = so.logits_to_f64(ci.target[b], ci.dtype)
+        if T > 0.0:
+            P, Q = oracle.chain_distributions(tgt, so.logits_to_f64(ci.draft[b], ci.dtype), T)
+        else:
+            P = Q = None
+        for s, u in enumerate(u_sets):
+            emitted, n, dec = oracle.chain_decide_request(P, Q, tgt, toks,
+                                                         np.asarray(u[b], dtype=np.float32), T)
+            r = results[s]
+            r.out_tokens[b, :len(emitted)] = emitted
+            r.num_accepted[b] = n
+            r.decisions[b] = dec
+    return results

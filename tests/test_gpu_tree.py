@@ -1,0 +1,100 @@
+"""GPU parity of spec_verify_tree against the fp64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import rejection_sampling_verify_15_amd as sv
+from parity import Tally, compare_tree, to_device, to_device_logits
+
+pytestmark = pytest.mark.gpu
+
+
+def run_tree(ti, u_sets):
+    lg = to_device_logits(ti.logits, ti.dtype)
+    tok = to_device(ti.node_tokens.astype(np.int32))
+    par = to_device(ti.parents.astype(np.int32))
+    T = to_device(ti.temperature.astype(np.float32))
+    outs = []
+    for u in u_sets:
+        outs.append(sv.verify_tree(lg, tok, par, to_device(np.asarray(u, np.float32)), T, ti.max_depth))
+    torch.cuda.synchronize()
+    return [tuple(x.cpu().numpy() for x in o) for o in outs]
+
+
+def tree_parity(ti, n_sets, label, seed=3):
+    rng = np.random.default_rng(seed)
+    u_sets = [ti.uniforms] + [synth.uniforms(rng, (ti.B, ti.N)) for _ in range(n_sets - 1)]
+    gpu = run_tree(ti, u_sets)
+    tally = Tally()
+    for (ot, op, on), u in zip(gpu, u_sets):
+        ref = oracle.verify_tree(ti.logits, ti.node_tokens, ti.parents, u, ti.temperature,
+                                 ti.dtype, ti.max_depth)
+        tally.add(compare_tree(ref, ot, op, on))
+    print(f"[{label}] {tally}", flush=True)
+    tally.check(label)
+    return tally, gpu
+
+
+def test_tree_config_greedy():
+    ti = synth.tree_inputs(temperature=0.0)
+    tree_parity(ti, 1, "tree greedy")
+
+
+def test_tree_config_naive_sampling():
+    ti = synth.tree_inputs(temperature=1.0)
+    tree_parity(ti, 6, "tree sampling")
+
+
+def test_small_trees_many_rounds():
+    for T in (0.0, 0.8):
+        ti = synth.tree_inputs(seed=301, B=24, N=40, V=3000, max_depth=6, temperature=T,
+                               draft_sigma=0.3)
+        t, gpu = tree_parity(ti, 40, f"small trees T={T}")
+        assert max(int(on.max()) for _, _, on in gpu) >= 2     # some deep accepts happen
+
+
+def test_tree_f32_scalar_path_and_mixed_modes():
+    ti = synth.tree_inputs(seed=302, B=16, N=30, V=4001, max_depth=8, temperature=1.0,
+                           dtype="f32", family="gauss", draft_sigma=0.2)
+    ti.temperature[1::2] = 0.0
+    tree_parity(ti, 20, "f32 mixed")
+
+
+def test_root_only_and_chains():
+    V = 500
+    rng = np.random.default_rng(9)
+    B, N = 4, 1
+    logits = synth.bf16_round_bits(rng.standard_normal((B, N, V)).astype(np.float32))
+    ti = synth.TreeInputs(logits, np.zeros((B, N), np.int32), -np.ones((B, N), np.int32),
+                          synth.uniforms(rng, (B, N)), np.array([0, 1, 0.5, 2], np.float32),
+                          "bf16", B, N, V, 0)
+    _, gpu = tree_parity(ti, 5, "root only")
+    assert (gpu[0][2] == 0).all()
+
+
+def test_invalid_trees_are_flagged():
+    ti = synth.tree_inputs(seed=303, B=8, N=16, V=1000, max_depth=8, temperature=1.0)
+    ti.parents[0, 5] = 7          # parent after the child
+    ti.parents[1, 0] = 0          # root with a parent
+    ti.node_tokens[2, 3] = 1000   # token out of range
+    ti.uniforms[3, 9] = 1.0       # uniform outside [0, 1)
+    ti.temperature[4] = np.nan
+    gpu = run_tree(ti, [ti.uniforms])
+    ref = oracle.verify_tree(ti.logits, ti.node_tokens, ti.parents, ti.uniforms, ti.temperature,
+                             ti.dtype, ti.max_depth)
+    for b in range(5):
+        assert ref.num_accepted[b] == -1 and gpu[0][2][b] == -1, b
+        assert (gpu[0][0][b] == -1).all() and (gpu[0][1][b] == -1).all()
+    compare_tree(ref, *gpu[0]).check("invalid trees")
+
+
+def test_depth_cap_enforced():
+    ti = synth.tree_inputs(seed=304, B=4, N=20, V=800, max_depth=8, temperature=0.0)
+    ti.max_depth = 2           # the generated trees are deeper than 2
+    gpu = run_tree(ti, [ti.uniforms])
+    ref = oracle.verify_tree(ti.logits, ti.node_tokens, ti.parents, ti.uniforms, ti.temperature,
+                             ti.dtype, 2)
+    compare_tree(ref, *gpu[0]).check("depth cap")
+    assert (ref.num_accepted == gpu[0][2]).all()
