@@ -27,12 +27,15 @@ template <int DT> struct Elem;
 
 template <> struct Elem<0> {  // bf16 stored as raw 16-bit patterns
   static constexpr int kVec = 8;
+  static constexpr int kBytes = 2;
   __device__ static inline float at(const void* row, int k) {
     const uint16_t b = static_cast<const uint16_t*>(row)[k];
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
   }
-  __device__ static inline void vec(const void* row, int k, float (&x)[kVec]) {
-    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + k);
+  __device__ static inline uint4 raw(const void* row, int k) {
+    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + k);
+  }
+  __device__ static inline void unpack(const uint4 w, float (&x)[kVec]) {
     const uint32_t q[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -44,41 +47,71 @@ template <> struct Elem<0> {  // bf16 stored as raw 16-bit patterns
 
 template <> struct Elem<1> {  // float32
   static constexpr int kVec = 4;
+  static constexpr int kBytes = 4;
   __device__ static inline float at(const void* row, int k) {
     return static_cast<const float*>(row)[k];
   }
-  __device__ static inline void vec(const void* row, int k, float (&x)[kVec]) {
-    const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(row) + k);
-    x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
+  __device__ static inline uint4 raw(const void* row, int k) {
+    return *reinterpret_cast<const uint4*>(static_cast<const float*>(row) + k);
+  }
+  __device__ static inline void unpack(const uint4 w, float (&x)[kVec]) {
+    x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
+    x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
   }
 };
 
-// Per-thread slice of one chunk: kItems groups of kPer consecutive elements.
-// Group j of thread t starts at element c0 + (j * kThreads + t) * kPer.
-template <int DT, bool VEC> struct Slice {
+// Per-thread slice of one span of kThreads * kPer * ITEMS elements: ITEMS
+// groups of kPer consecutive elements; group j of thread t starts at element
+// c0 + (j * kThreads + t) * kPer.  A full span issues all its loads before any
+// use (no branches between them, so they are in flight together); a partial
+// span loads from a clamped, in-range address and masks the excess to -inf.
+template <int DT, bool VEC, int ITEMS = kChunk / (kThreads * (VEC ? Elem<DT>::kVec : 1))>
+struct Slice {
   static constexpr int kPer = VEC ? Elem<DT>::kVec : 1;
-  static constexpr int kItems = kChunk / (kThreads * kPer);
-  static constexpr int kN = kItems * kPer;
+  static constexpr int kItems = ITEMS;
+  static constexpr int kSpan = kThreads * kPer * ITEMS;
   float x[kItems][kPer];
 
   __device__ static inline int index(int c0, int j, int e) {
     return c0 + (j * kThreads + static_cast<int>(threadIdx.x)) * kPer + e;
   }
 
-  // Loads [c0, c1) of `row`; out-of-range slots get -inf.
+  // Loads [c0, c1) of `row` (c1 - c0 <= kSpan).
   __device__ inline void load(const void* row, int c0, int c1) {
-#pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-      const int k0 = index(c0, j, 0);
+    if (c1 - c0 == kSpan) {
       if constexpr (VEC) {
-        if (k0 < c1) {
-          Elem<DT>::vec(row, k0, x[j]);
-        } else {
+        uint4 w[kItems];
 #pragma unroll
-          for (int e = 0; e < kPer; ++e) x[j][e] = -INFINITY;
+        for (int j = 0; j < kItems; ++j) w[j] = Elem<DT>::raw(row, index(c0, j, 0));
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) Elem<DT>::unpack(w[j], x[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) x[j][0] = Elem<DT>::at(row, index(c0, j, 0));
+      }
+    } else {
+      if constexpr (VEC) {
+        uint4 w[kItems];
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+          const int k0 = index(c0, j, 0);
+          w[j] = Elem<DT>::raw(row, k0 < c1 ? k0 : c0);
+        }
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+          Elem<DT>::unpack(w[j], x[j]);
+          if (index(c0, j, 0) >= c1) {
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) x[j][e] = -INFINITY;
+          }
         }
       } else {
-        x[j][0] = (k0 < c1) ? Elem<DT>::at(row, k0) : -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+          const int k0 = index(c0, j, 0);
+          const float v = Elem<DT>::at(row, k0 < c1 ? k0 : c0);
+          x[j][0] = k0 < c1 ? v : -INFINITY;
+        }
       }
     }
   }

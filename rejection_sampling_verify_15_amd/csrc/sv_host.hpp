@@ -4,7 +4,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/specverify.h"
+#include "specverify.h"
 
 namespace sv {
 

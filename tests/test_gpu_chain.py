@@ -172,3 +172,25 @@ def test_repeat_calls_are_deterministic(batched):
     gpu = run_gpu(batched, u)
     for ot, on in gpu[1:]:
         assert np.array_equal(ot, gpu[0][0]) and np.array_equal(on, gpu[0][1])
+
+
+def test_workspace_is_left_zeroed_across_shapes():
+    """One workspace serves calls of different shapes in a row: every completed
+    call returns it to all-zero, and each call stays correct."""
+    dev = torch.device("cuda")
+    L = sv.lib()
+    shapes = [(16, 4, 20000, "bf16"), (12, 3, 20001, "bf16"), (40, 2, 3000, "f32"),
+              (3, 6, 50000, "bf16"), (16, 4, 20000, "bf16")]
+    need = max(L.sv_chain_workspace_bytes(B, g, V, 0) for B, g, V, _ in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    for i, (B, g, V, dt) in enumerate(shapes):
+        ci = synth.chain_inputs(400 + i, B=B, gamma=g, V=V, dtype=dt, family="peaked",
+                                draft_sigma=(0.3, 2.0), temperature=0.9, greedy_odd=True)
+        ot, on = sv.verify_chain(to_device_logits(ci.target, dt), to_device_logits(ci.draft, dt),
+                                 to_device(ci.draft_tokens.astype(np.int32)),
+                                 to_device(ci.uniforms), to_device(ci.temperature), ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0, f"workspace not zero after call {i}"
+        ref = oracle.verify_chain(ci.target, ci.draft, ci.draft_tokens, ci.uniforms,
+                                  ci.temperature, dt)
+        compare_chain(ref, ot.cpu().numpy(), on.cpu().numpy()).check(f"shape {i}")
