@@ -84,6 +84,7 @@ typedef enum {
 
 /* Limits checked on the host (SV_ERR_SHAPE otherwise). */
 #define SV_MAX_GAMMA 32
+#define SV_MAX_BATCH 16384   /* requests per chain call */
 #define SV_MAX_VOCAB (1 << 24)
 #define SV_MAX_TREE_NODES 1024
 #define SV_MAX_TREE_DEPTH 64
@@ -119,7 +120,7 @@ SV_API int sv_workspace_clear(void* workspace, size_t bytes, void* hip_stream);
  * out_num_accepted [B]              int32   n in [0, gamma] (n + 1 tokens are
  *                                           emitted; the caller rolls back
  *                                           gamma - n cached positions), or -1
- * Limits: B >= 0 (B == 0 is a no-op), 0 <= gamma <= SV_MAX_GAMMA,
+ * Limits: 0 <= B <= SV_MAX_BATCH (B == 0 is a no-op), 0 <= gamma <= SV_MAX_GAMMA,
  *         1 <= V <= SV_MAX_VOCAB.
  * Returns an sv_status.
  * ---------------------------------------------------------------------- */

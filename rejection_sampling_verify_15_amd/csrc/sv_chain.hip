@@ -3,96 +3,56 @@
 // close-reading notes 02, section 4, and CMU 15-779 lecture 17 notes, sections
 // 2.2-2.4).  See include/specverify.h for the contract.
 //
-// One cooperative launch of a persistent kernel.  Every workgroup walks the
-// row items (request, row, chunk) grid-stride; the workgroup whose item
-// completes a request's rows takes that request's decision and raises the
-// request's flag.  The final draw of a sampling request is split into draw
-// units; unit q (request q / nunit) belongs to workgroup q mod grid, which
-// runs it as soon as the request's flag is up -- between its own row items,
-// or after them.  The workgroup completing a request's last unit locates and
-// emits the drawn token.  Workgroups only ever wait on per-request flags,
-// never on a shared counter, so no memory line is polled by the whole grid.
+// Three launches on the caller's stream; every dependency between workgroups
+// is a launch boundary, so all reads are plain loads:
 //
-//  row item   kChunk logits of one needed row: the chunk max and, for sampling
-//             rows, sum exp2((x - max) * log2e / T) in fp32; for greedy rows
-//             the argmax (lowest index).  Draft rows of greedy requests and
-//             all rows of requests with an invalid temperature are not read.
-//  decision   fp64 merge of the chunk partials; the gamma-step accept test
-//             (u <= tau, tau = 1 if q <= p else p / q, p and q from the
-//             gathered logits); greedy: argmax equality.  Writes the accepted
-//             tokens and count, and for greedy requests the final token.
-//  draw unit  kThreads * kPer logits of the final draw's row(s): fp64 sums of
-//             exp((x - max) / T) for the target and draft rows (all, and where
-//             p > q), also per 64-lane sub-span.
-//  finalise   fp64 normalisers from the units; cumulative residual (or bonus)
-//             weight per unit and sub-span; an fp64 scan of the crossing
-//             sub-span: the smallest k with C_k > u * W.
+//  1. chain_row_stats  one workgroup per needed (row, chunk) of kChunk logits:
+//                      the chunk max and, for sampling rows, the fp32 sum of
+//                      exp2((x - max) * log2e / T); for greedy rows the argmax
+//                      (lowest index).  The workgroup whose chunk holds a
+//                      row's draft token also records that logit.  Draft rows
+//                      of greedy requests are not read.
+//  2. chain_units      one workgroup per (request, draw unit) of kThreads*kPer
+//                      logits.  Each re-derives its request's decision from the
+//                      row partials in one round of loads (fp64 merge; the
+//                      gamma-step test u <= tau, tau = 1 if q <= p else p / q;
+//                      greedy: argmax equality); unit 0 writes the accepted
+//                      tokens and count.  For a sampling request each unit then
+//                      sums, in fp64, exp((x - max) / T) of the final draw's
+//                      target and draft rows over its span (all, and where
+//                      p > q), also per 64-lane sub-span.
+//  3. chain_finalize   one workgroup per request: fp64 normalisers from the
+//                      unit sums, the residual (or bonus) weight of every unit
+//                      and sub-span, an fp64 scan of the crossing sub-span -- the
+//                      smallest k with C_k > u * W -- and returns every
+//                      workspace word the request used to zero.
 //
-// Cross-workgroup data (partials, decisions, the draw queue) is written with
-// agent-scope coherent stores, drained with s_waitcnt before the arrival
-// atomic, and read with agent-scope coherent loads, so no L2 write-back or
-// invalidate is issued.  Every wait is bounded.  Every word of the workspace
-// is returned to zero by the workgroup that consumes it, so a completed call
-// leaves the whole workspace zeroed whatever the next call's shape.
+// Precision: the accept test needs p(x)/q(x) to ~1e-6 and uses the fp32 row
+// normalisers; the final draw uses fp64 exponentials and fp64 normalisers
+// summed in launch 2, so the inverse CDF matches an fp64 reference except
+// where u lies within a few ulps of a CDF step.
 #include "sv_device.hpp"
 #include "sv_host.hpp"
-
-#include <algorithm>
-#include <mutex>
-#include <utility>
-#include <vector>
 
 namespace sv {
 
 // ---------------------------------------------------------------------------
-// coherent accesses between workgroups (agent scope)
-// ---------------------------------------------------------------------------
-template <typename T> __device__ inline void cstore(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T> __device__ inline T cload(const T* p) {
-  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline int cadd(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline bool ccas(int* p, int expected, int desired) {
-  return __hip_atomic_compare_exchange_strong(p, &expected, desired, __ATOMIC_RELAXED,
-                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Every earlier store of this wave has completed (reached the coherence point).
-__device__ inline void drain_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-constexpr int kSpinLimit = 1 << 22;  // bound of every wait (~0.2 s with s_sleep)
-constexpr int kLine = 32;            // ints per padded counter (128 bytes)
-
-// ---------------------------------------------------------------------------
 // workspace records
 // ---------------------------------------------------------------------------
-struct RowPartial {  // one (row, chunk)
+struct RowPartial {  // one (row, chunk), packed in one 64-bit word
   float m;           // chunk max
   int32_t v;         // float bits of the exp-sum (sampling) or the argmax (greedy)
 };
 
-enum : int32_t { kModeResidual = 1, kModeBonus = 2 };
-
-struct DecisionRec {  // per sampling request, read by its draw units
-  int32_t mode, n;
-  float mt, md;       // maxima of the final draw's target / draft rows
-  double zt, zd;      // pass-1 normalisers of those rows (fp64 merge)
-  float u, t;
-};
-
-struct UnitRec {      // per (request, draw unit), fp64
+struct UnitRec {     // per (request, draw unit), fp64
   double st_all, sd_all, st_pos, sd_pos;
   double w_pos_t[kWaves], w_pos_d[kWaves], w_all_t[kWaves];
 };
 
-static_assert(sizeof(RowPartial) == 8, "row partials are cleared as one 64-bit word");
-static_assert(sizeof(DecisionRec) % 8 == 0 && sizeof(UnitRec) % 8 == 0,
-              "records are cleared in 64-bit words");
+static_assert(sizeof(RowPartial) == 8, "row partials are one 64-bit word");
+static_assert(sizeof(UnitRec) % 8 == 0, "unit records are cleared in 64-bit words");
 
-enum : int { kFlagNone = 0, kFlagDraw = 1, kFlagDone = 2 };  // per-request flag values
+enum : int32_t { kModeResidual = 1, kModeBonus = 2 };
 
 struct ChainArgs {
   const void* target;
@@ -100,15 +60,12 @@ struct ChainArgs {
   const int32_t* tokens;
   const float* uniforms;
   const float* temperature;
-  int B, gamma, V, nchunk, nunit, nslots;
+  int B, gamma, V, nchunk, nunit;
   int32_t* out_tokens;
   int32_t* out_n;
-  RowPartial* partials;    // [B][2*gamma+1][nchunk]
-  int* cnt_rows;           // [B][kLine]
-  int* cnt_units;          // [B][kLine]
-  int* flag;               // [B][kLine] kFlagNone / kFlagDraw / kFlagDone
-  DecisionRec* decisions;  // [B]
-  UnitRec* units;          // [B][nunit]
+  RowPartial* partials;  // [B][2*gamma+1][nchunk]
+  float* gathers;        // [B][2*gamma+1] logit of the draft token in each row
+  UnitRec* units;        // [B][nunit]
 };
 
 // T must be 0 (greedy) or a finite positive normal float.
@@ -123,180 +80,69 @@ __device__ inline double exp_scaled(float x, float m, double inv_t) {
   return exp(static_cast<double>(x - m) * inv_t);
 }
 
-// Returns the chunk partials of one row to zero once they have been consumed.
-__device__ inline void clear_row_partials(RowPartial* p, int nchunk) {
-  for (int c = 0; c < nchunk; ++c) cstore(reinterpret_cast<unsigned long long*>(p + c), 0ull);
+// Request classes: 0 samples with its draft rows (it has a final draw), 1 is
+// greedy or cannot sample (target rows only), 2 has an invalid temperature.
+__device__ inline int request_class(const ChainArgs& a, float T) {
+  if (!temp_ok(T)) return 2;
+  if (T > 0.0f && (a.draft != nullptr || a.gamma == 0)) return 0;
+  return 1;
 }
 
-// Rows of request b that are read: target rows, plus draft rows when sampling.
+// Rows of a request that are read: target rows, plus draft rows when sampling.
 __device__ inline int needed_rows(const ChainArgs& a, float T) {
   return (T > 0.0f && a.draft != nullptr) ? 2 * a.gamma + 1 : a.gamma + 1;
 }
 
 // ---------------------------------------------------------------------------
-// decision of request b (whole workgroup)
+// launch 1: row statistics
 // ---------------------------------------------------------------------------
-template <int DT>
-__device__ void decide(const ChainArgs& a, int b) {
-  constexpr int kMaxRows = 2 * SV_MAX_GAMMA + 1;
-  __shared__ float s_m[kMaxRows];
-  __shared__ double s_z[kMaxRows];
-  __shared__ int32_t s_arg[kMaxRows];
-  __shared__ float s_xt[SV_MAX_GAMMA], s_xd[SV_MAX_GAMMA];
-  __shared__ int32_t s_ok[SV_MAX_GAMMA];
-  const int tid = threadIdx.x;
+// Workgroups [0, B*(gamma+1)*nchunk) cover the target rows and the rest the
+// draft rows, so the workgroups that skip (draft rows of greedy requests)
+// come last.
+template <int DT, bool VEC>
+__device__ void row_stats_item(const ChainArgs& a, long long item) {
+  __shared__ float s_wm[kWaves];
   const int G = a.gamma;
   const int R = 2 * G + 1;
+  const long long ntgt = static_cast<long long>(a.B) * (G + 1) * a.nchunk;
+  int b, k, c;
+  if (item < ntgt) {
+    b = static_cast<int>(item / ((G + 1) * a.nchunk));
+    const int rem = static_cast<int>(item % ((G + 1) * a.nchunk));
+    k = rem / a.nchunk;
+    c = rem % a.nchunk;
+  } else {
+    const long long i2 = item - ntgt;
+    b = static_cast<int>(i2 / (G * a.nchunk));
+    const int rem = static_cast<int>(i2 % (G * a.nchunk));
+    k = G + 1 + rem / a.nchunk;
+    c = rem % a.nchunk;
+  }
   const float T = a.temperature[b];
+  if (!temp_ok(T)) return;
   const bool sampling = T > 0.0f;
-  // validity of tokens and uniforms; gather the draft tokens' logits
-  int bad = 0;
-  if (tid < G) {
-    const int32_t x = a.tokens[static_cast<size_t>(b) * G + tid];
-    bad |= (x < 0 || x >= a.V);
-    if (!bad && sampling && a.draft != nullptr) {
-      s_xt[tid] = Elem<DT>::at(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + tid, a.V), x);
-      s_xd[tid] = Elem<DT>::at(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + tid, a.V), x);
-    }
-  }
-  if (sampling && tid <= G) {
-    const float u = a.uniforms[static_cast<size_t>(b) * (G + 1) + tid];
-    bad |= !(u >= 0.0f && u < 1.0f);
-  }
-  if (sampling && G > 0 && a.draft == nullptr) bad = 1;
-  bad = __syncthreads_or(bad);
-  int32_t* out = a.out_tokens + static_cast<size_t>(b) * (G + 1);
-  if (bad) {
-    for (int i = tid; i <= G; i += kThreads) out[i] = -1;
-    if (tid < needed_rows(a, T))
-      clear_row_partials(a.partials + (static_cast<size_t>(b) * R + tid) * a.nchunk, a.nchunk);
-    if (tid == 0) {
-      a.out_n[b] = -1;
-      drain_stores();
-      cstore(&a.flag[b * kLine], int(kFlagDone));
-    }
-    return;
-  }
-  // merge the chunk partials of every needed row (one thread per row, eight
-  // coherent loads in flight at a time)
-  const double inv_t = sampling ? 1.0 / static_cast<double>(T) : 0.0;
-  const int nrows = needed_rows(a, T);
-  if (tid < nrows) {
-    const RowPartial* p = a.partials + (static_cast<size_t>(b) * R + tid) * a.nchunk;
-    if (!sampling) {
-      ArgMax best{-INFINITY, 0x7fffffff};
-      for (int c0 = 0; c0 < a.nchunk; c0 += 8) {
-        float pm[8];
-        int32_t pv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int c = min(c0 + i, a.nchunk - 1);
-          pm[i] = cload(&p[c].m);
-          pv[i] = cload(&p[c].v);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (c0 + i < a.nchunk) best = argmax_combine(best, ArgMax{pm[i], pv[i]});
-      }
-      s_m[tid] = best.v;
-      s_arg[tid] = best.i;
-      clear_row_partials(const_cast<RowPartial*>(p), a.nchunk);
-    } else {
-      float m = -INFINITY;
-      double z = 0.0;
-      for (int c0 = 0; c0 < a.nchunk; c0 += 8) {
-        float pm[8], pz[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int c = min(c0 + i, a.nchunk - 1);
-          pm[i] = cload(&p[c].m);
-          pz[i] = __int_as_float(cload(&p[c].v));
-        }
-        float mm = m;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (c0 + i < a.nchunk) mm = fmaxf(mm, pm[i]);
-        if (mm != m && m != -INFINITY) z *= exp(static_cast<double>(m - mm) * inv_t);
-        m = mm;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (c0 + i < a.nchunk && pm[i] != -INFINITY)
-            z += static_cast<double>(pz[i]) * exp_scaled(pm[i], m, inv_t);
-      }
-      s_m[tid] = m;
-      s_z[tid] = z;
-      clear_row_partials(const_cast<RowPartial*>(p), a.nchunk);
-    }
-  }
-  __syncthreads();
-  if (tid < G) {
-    const int32_t x = a.tokens[static_cast<size_t>(b) * G + tid];
-    int ok;
-    if (!sampling) {
-      ok = (x == s_arg[tid]);
-    } else {
-      const double p = exp_scaled(s_xt[tid], s_m[tid], inv_t) / s_z[tid];
-      const double q = exp_scaled(s_xd[tid], s_m[G + 1 + tid], inv_t) / s_z[G + 1 + tid];
-      const double tau = (q <= p) ? 1.0 : p / q;
-      const double u = static_cast<double>(a.uniforms[static_cast<size_t>(b) * (G + 1) + tid]);
-      ok = (u <= tau);
-    }
-    s_ok[tid] = ok;
-  }
-  __syncthreads();
-  int n = 0;
-  while (n < G && s_ok[n]) ++n;
-  // slot n of a sampling request belongs to the workgroup that finalises its
-  // draw (one writer per output word)
-  for (int i = tid; i <= G; i += kThreads) {
-    if (sampling && i == n) continue;
-    int32_t v = -1;
-    if (i < n) v = a.tokens[static_cast<size_t>(b) * G + i];
-    else if (i == n) v = s_arg[n];
-    out[i] = v;
-  }
-  if (tid == 0) {
-    a.out_n[b] = n;
-    if (sampling) {
-      DecisionRec* d = a.decisions + b;
-      cstore(&d->mode, n < G ? int32_t(kModeResidual) : int32_t(kModeBonus));
-      cstore(&d->n, int32_t(n));
-      cstore(&d->mt, s_m[n]);
-      cstore(&d->zt, s_z[n]);
-      if (n < G) {
-        cstore(&d->md, s_m[G + 1 + n]);
-        cstore(&d->zd, s_z[G + 1 + n]);
-      }
-      cstore(&d->u, a.uniforms[static_cast<size_t>(b) * (G + 1) + G]);
-      cstore(&d->t, T);
-    }
-    // the decision record is complete before the flag rises
-    drain_stores();
-    cstore(&a.flag[b * kLine], sampling ? int(kFlagDraw) : int(kFlagDone));
-  }
-}
-
-// ---------------------------------------------------------------------------
-// one row item
-// ---------------------------------------------------------------------------
-template <int DT, bool VEC>
-__device__ void row_item(const ChainArgs& a, int b, int k, int c, float T) {
-  __shared__ int s_last;
-  __shared__ float s_wm[kWaves];
-  const bool sampling = T > 0.0f;
-  const void* row = (k <= a.gamma)
-      ? row_ptr<DT>(a.target, static_cast<size_t>(b) * (a.gamma + 1) + k, a.V)
-      : row_ptr<DT>(a.draft, static_cast<size_t>(b) * a.gamma + (k - a.gamma - 1), a.V);
+  if (k > G && !(sampling && a.draft != nullptr)) return;  // draft rows are read only when sampling
+  const int pos = k <= G ? k : k - G - 1;                    // draft position of this row
+  const void* row = (k <= G) ? row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + k, a.V)
+                             : row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + pos, a.V);
   const int c0 = c * kChunk;
   const int c1 = min(a.V, c0 + kChunk);
+  const int32_t tok = (sampling && pos < G) ? a.tokens[static_cast<size_t>(b) * G + pos] : -1;
   Slice<DT, VEC> s;
   s.load(row, c0, c1);
+  if (tok >= c0 && tok < c1) {
+#pragma unroll
+    for (int j = 0; j < s.kItems; ++j)
+#pragma unroll
+      for (int e = 0; e < s.kPer; ++e)
+        if (s.index(c0, j, e) == tok) a.gathers[static_cast<size_t>(b) * R + k] = s.x[j][e];
+  }
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < s.kItems; ++j)
 #pragma unroll
     for (int e = 0; e < s.kPer; ++e) m = fmaxf(m, s.x[j][e]);
-  RowPartial out{};
+  RowPartial out;
   if (!sampling) {
     // chunk max first; only threads holding it look for its lowest index
     const float wm = wave_max(m);
@@ -332,66 +178,210 @@ __device__ void row_item(const ChainArgs& a, int b, int k, int c, float T) {
     out.m = ms.m;
     out.v = __float_as_int(ms.z);
   }
-  if (threadIdx.x == 0) {
-    RowPartial* dst = a.partials + (static_cast<size_t>(b) * (2 * a.gamma + 1) + k) * a.nchunk + c;
-    cstore(&dst->m, out.m);
-    cstore(&dst->v, out.v);
-    drain_stores();
-    const int need = needed_rows(a, T) * a.nchunk;
-    const int old = cadd(&a.cnt_rows[b * kLine], 1);
-    s_last = (old == need - 1);
-    if (old == need - 1) cstore(&a.cnt_rows[b * kLine], 0);
-  }
-  __syncthreads();
-  const int last = s_last;
-  __syncthreads();
-  if (last) decide<DT>(a, b);
+  if (threadIdx.x == 0) a.partials[(static_cast<size_t>(b) * R + k) * a.nchunk + c] = out;
+  __syncthreads();  // s_wm is reused by the next item
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void chain_row_stats(ChainArgs a) {
+  const long long items = static_cast<long long>(a.B) * (2 * a.gamma + 1) * a.nchunk;
+  for (long long item = blockIdx.x; item < items; item += gridDim.x) row_stats_item<DT, VEC>(a, item);
 }
 
 // ---------------------------------------------------------------------------
-// draw units
+// the decision of request b, derived by a whole workgroup from the partials
 // ---------------------------------------------------------------------------
-template <int DT, bool VEC>
-__device__ void finalize(const ChainArgs& a, int b, const DecisionRec& d);
+struct Decision {
+  int32_t bad;        // invalid token / uniform / missing draft logits
+  int32_t n;          // accepted drafts
+  int32_t mode;       // kModeResidual / kModeBonus (sampling)
+  int32_t final_tok;  // greedy: the emitted argmax
+  float mt, md;       // maxima of the final draw's target / draft rows
+  double zt, zd;      // their fp64-merged pass-1 normalisers
+  float u, t;         // u[b][gamma], temperature
+};
 
-// Draw unit `unit` of request b, whose flag was seen as `f`: kFlagDone units
-// only arrive; kFlagDraw units accumulate their weights first.  The last unit
-// to arrive finalises the draw (kFlagDraw) and returns the request's counters
-// and flag to zero.
-template <int DT, bool VEC>
-__device__ void draw_unit(const ChainArgs& a, int b, int unit, int f) {
-  using S = Slice<DT, VEC, 1>;
-  __shared__ int s_last;
-  __shared__ DecisionRec s_d;
-  __shared__ double s_w[4][kWaves];
+template <int DT>
+__device__ Decision decide(const ChainArgs& a, int b) {
+  constexpr int kMaxRows = 2 * SV_MAX_GAMMA + 1;
+  __shared__ float s_gm[kThreads];
+  __shared__ double s_gz[kThreads];
+  __shared__ int32_t s_garg[kThreads];
+  __shared__ float s_m[kMaxRows];
+  __shared__ double s_z[kMaxRows];
+  __shared__ int32_t s_arg[kMaxRows];
+  __shared__ float s_xt[SV_MAX_GAMMA], s_xd[SV_MAX_GAMMA];
+  __shared__ int32_t s_ok[SV_MAX_GAMMA];
+  __shared__ Decision s_dec;
+  const int tid = threadIdx.x;
   const int G = a.gamma;
-  if (f != kFlagDraw) {
-    if (threadIdx.x == 0) {
-      const int old = cadd(&a.cnt_units[b * kLine], 1);
-      if (old == a.nunit - 1) {
-        cstore(&a.cnt_units[b * kLine], 0);
-        cstore(&a.flag[b * kLine], int(kFlagNone));
+  const int R = 2 * G + 1;
+  const float T = a.temperature[b];
+  const bool sampling = T > 0.0f;
+  const double inv_t = sampling ? 1.0 / static_cast<double>(T) : 0.0;
+  const int nrows = needed_rows(a, T);
+  // one round of loads: the chunk partials (in groups of chunks, one group per
+  // thread), the draft tokens, their gathered logits and the uniforms
+  const int gpr = max(1, min((a.nchunk + 7) / 8, kThreads / nrows));  // groups per row
+  const int gs = (a.nchunk + gpr - 1) / gpr;                           // chunks per group
+  int bad = 0;
+  if (tid < G) {
+    const int32_t x = a.tokens[static_cast<size_t>(b) * G + tid];
+    bad |= (x < 0 || x >= a.V);
+    if (sampling && a.draft != nullptr) {
+      s_xt[tid] = a.gathers[static_cast<size_t>(b) * R + tid];
+      s_xd[tid] = a.gathers[static_cast<size_t>(b) * R + G + 1 + tid];
+    }
+  }
+  if (sampling && tid <= G) {
+    const float u = a.uniforms[static_cast<size_t>(b) * (G + 1) + tid];
+    bad |= !(u >= 0.0f && u < 1.0f);
+  }
+  if (sampling && G > 0 && a.draft == nullptr) bad = 1;
+  if (tid < nrows * gpr) {
+    const int r = tid / gpr;
+    const int g = tid % gpr;
+    const RowPartial* p = a.partials + (static_cast<size_t>(b) * R + r) * a.nchunk;
+    const int cb = g * gs;
+    const int ce = min(a.nchunk, cb + gs);
+    float m = -INFINITY;
+    double z = 0.0;
+    ArgMax best{-INFINITY, 0x7fffffff};
+    for (int c0 = cb; c0 < ce; c0 += 8) {
+      RowPartial w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = p[min(c0 + i, ce - 1)];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (c0 + i >= ce) continue;
+        if (!sampling) {
+          best = argmax_combine(best, ArgMax{w[i].m, w[i].v});
+        } else if (w[i].m != -INFINITY) {
+          if (w[i].m > m) {
+            if (m != -INFINITY) z *= exp(static_cast<double>(m - w[i].m) * inv_t);
+            m = w[i].m;
+          }
+          z += static_cast<double>(__int_as_float(w[i].v)) * exp_scaled(w[i].m, m, inv_t);
+        }
+      }
+    }
+    if (sampling) {
+      s_gm[tid] = m;
+      s_gz[tid] = z;
+    } else {
+      s_gm[tid] = best.v;
+      s_garg[tid] = best.i;
+    }
+  }
+  bad = __syncthreads_or(bad);
+  if (!bad) {
+    // combine the groups of each row
+    if (tid < nrows) {
+      if (!sampling) {
+        ArgMax best{-INFINITY, 0x7fffffff};
+        for (int g = 0; g < gpr; ++g)
+          best = argmax_combine(best, ArgMax{s_gm[tid * gpr + g], s_garg[tid * gpr + g]});
+        s_m[tid] = best.v;
+        s_arg[tid] = best.i;
+      } else {
+        float m = -INFINITY;
+        for (int g = 0; g < gpr; ++g) m = fmaxf(m, s_gm[tid * gpr + g]);
+        double z = 0.0;
+        for (int g = 0; g < gpr; ++g) {
+          const float gm = s_gm[tid * gpr + g];
+          if (gm != -INFINITY) z += s_gz[tid * gpr + g] * exp_scaled(gm, m, inv_t);
+        }
+        s_m[tid] = m;
+        s_z[tid] = z;
       }
     }
     __syncthreads();
-    return;
+    if (tid < G) {
+      const int32_t x = a.tokens[static_cast<size_t>(b) * G + tid];
+      int ok;
+      if (!sampling) {
+        ok = (x == s_arg[tid]);
+      } else {
+        const double p = exp_scaled(s_xt[tid], s_m[tid], inv_t) / s_z[tid];
+        const double q = exp_scaled(s_xd[tid], s_m[G + 1 + tid], inv_t) / s_z[G + 1 + tid];
+        const double tau = (q <= p) ? 1.0 : p / q;
+        const double u = static_cast<double>(a.uniforms[static_cast<size_t>(b) * (G + 1) + tid]);
+        ok = (u <= tau);
+      }
+      s_ok[tid] = ok;
+    }
+    __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    const DecisionRec* dr = a.decisions + b;
-    s_d.mode = cload(&dr->mode);
-    s_d.n = cload(&dr->n);
-    s_d.mt = cload(&dr->mt);
-    s_d.md = cload(&dr->md);
-    s_d.zt = cload(&dr->zt);
-    s_d.zd = cload(&dr->zd);
-    s_d.u = cload(&dr->u);
-    s_d.t = cload(&dr->t);
+  if (tid == 0) {
+    Decision d{};
+    d.bad = bad;
+    if (!bad) {
+      int n = 0;
+      while (n < G && s_ok[n]) ++n;
+      d.n = n;
+      d.t = T;
+      if (!sampling) {
+        d.final_tok = s_arg[n];
+      } else {
+        d.mode = n < G ? kModeResidual : kModeBonus;
+        d.mt = s_m[n];
+        d.zt = s_z[n];
+        if (n < G) {
+          d.md = s_m[G + 1 + n];
+          d.zd = s_z[G + 1 + n];
+        }
+        d.u = a.uniforms[static_cast<size_t>(b) * (G + 1) + G];
+      }
+    }
+    s_dec = d;
   }
   __syncthreads();
-  DecisionRec d = s_d;
-  // keep every row index in range whatever the record holds
-  if (d.n < 0 || d.n > G) d.n = G;
-  if (d.n == G) d.mode = kModeBonus;
+  const Decision d = s_dec;
+  __syncthreads();
+  return d;
+}
+
+// Accepted tokens, count, and for greedy requests the final token; slot n of
+// a sampling request is left to the launch that draws it.
+__device__ void write_outputs(const ChainArgs& a, int b, const Decision& d, bool sampling) {
+  const int G = a.gamma;
+  int32_t* out = a.out_tokens + static_cast<size_t>(b) * (G + 1);
+  for (int i = threadIdx.x; i <= G; i += kThreads) {
+    int32_t v = -1;
+    if (!d.bad) {
+      if (sampling && i == d.n) continue;
+      if (i < d.n) v = a.tokens[static_cast<size_t>(b) * G + i];
+      else if (i == d.n) v = d.final_tok;
+    }
+    out[i] = v;
+  }
+  if (threadIdx.x == 0) a.out_n[b] = d.bad ? -1 : d.n;
+}
+
+// ---------------------------------------------------------------------------
+// launch 2: decisions and draw-unit sums
+// ---------------------------------------------------------------------------
+template <int DT, bool VEC>
+__device__ void unit_item(const ChainArgs& a, long long item) {
+  using S = Slice<DT, VEC, 1>;
+  __shared__ double s_w[4][kWaves];
+  const int b = static_cast<int>(item / a.nunit);
+  const int unit = static_cast<int>(item % a.nunit);
+  const int G = a.gamma;
+  const float T = a.temperature[b];
+  const int cls = request_class(a, T);
+  if (cls == 2) {  // nothing was read for this request
+    if (unit == 0) {
+      for (int i = threadIdx.x; i <= G; i += kThreads) a.out_tokens[static_cast<size_t>(b) * (G + 1) + i] = -1;
+      if (threadIdx.x == 0) a.out_n[b] = -1;
+    }
+    return;
+  }
+  if (cls == 1 && unit != 0) return;
+  const Decision d = decide<DT>(a, b);
+  if (unit == 0) write_outputs(a, b, d, cls == 0);
+  if (cls != 0 || d.bad) return;
+  // this unit's share of the final draw
   const double inv_t = 1.0 / static_cast<double>(d.t);
   const int c0 = unit * S::kSpan;
   const int c1 = min(a.V, c0 + S::kSpan);
@@ -431,37 +421,31 @@ __device__ void draw_unit(const ChainArgs& a, int b, int unit, int f) {
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    UnitRec* ur = a.units + static_cast<size_t>(b) * a.nunit + unit;
-    double u_all_t = 0, u_all_d = 0, u_pos_t = 0, u_pos_d = 0;
+    UnitRec r;
+    r.st_pos = r.sd_pos = r.st_all = r.sd_all = 0.0;
     for (int i = 0; i < kWaves; ++i) {
-      u_pos_t += s_w[0][i];
-      u_pos_d += s_w[1][i];
-      u_all_t += s_w[2][i];
-      u_all_d += s_w[3][i];
-      cstore(&ur->w_pos_t[i], s_w[0][i]);
-      cstore(&ur->w_pos_d[i], s_w[1][i]);
-      cstore(&ur->w_all_t[i], s_w[2][i]);
+      r.w_pos_t[i] = s_w[0][i];
+      r.w_pos_d[i] = s_w[1][i];
+      r.w_all_t[i] = s_w[2][i];
+      r.st_pos += s_w[0][i];
+      r.sd_pos += s_w[1][i];
+      r.st_all += s_w[2][i];
+      r.sd_all += s_w[3][i];
     }
-    cstore(&ur->st_all, u_all_t);
-    cstore(&ur->sd_all, u_all_d);
-    cstore(&ur->st_pos, u_pos_t);
-    cstore(&ur->sd_pos, u_pos_d);
-    drain_stores();
-    const int old = cadd(&a.cnt_units[b * kLine], 1);
-    s_last = (old == a.nunit - 1);
+    a.units[static_cast<size_t>(b) * a.nunit + unit] = r;
   }
-  __syncthreads();
-  const int last = s_last;
-  __syncthreads();
-  if (last) {
-    finalize<DT, VEC>(a, b, d);
-    if (threadIdx.x == 0) {
-      cstore(&a.cnt_units[b * kLine], 0);
-      cstore(&a.flag[b * kLine], int(kFlagNone));
-    }
-  }
+  __syncthreads();  // s_w is reused by the next item
 }
 
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void chain_units(ChainArgs a) {
+  const long long items = static_cast<long long>(a.B) * a.nunit;
+  for (long long item = blockIdx.x; item < items; item += gridDim.x) unit_item<DT, VEC>(a, item);
+}
+
+// ---------------------------------------------------------------------------
+// launch 3: the final draw, and the workspace back to zero
+// ---------------------------------------------------------------------------
 // Weight of a unit (or of one of its sub-spans) in the final draw.
 __device__ inline double unit_weight(double pos_t, double pos_d, double all_t, bool residual,
                                      double zt, double zd) {
@@ -469,89 +453,84 @@ __device__ inline double unit_weight(double pos_t, double pos_d, double all_t, b
 }
 
 template <int DT, bool VEC>
-__device__ void finalize(const ChainArgs& a, int b, const DecisionRec& d) {
+__device__ void draw_token(const ChainArgs& a, int b, const Decision& d) {
   using S = Slice<DT, VEC, 1>;
-  __shared__ int s_unit, s_sub, s_found;
+  __shared__ int s_unit, s_sub, s_first, s_lastpos;
   __shared__ double s_before;
   const int G = a.gamma;
+  const int tid = threadIdx.x;
   const UnitRec* ur = a.units + static_cast<size_t>(b) * a.nunit;
-  // fp64 normalisers of the two rows
+  // 1) normalisers: fp64 sums of exp((x - max) / T) over every unit.  With at
+  //    most kThreads units (the usual case) each thread keeps its unit's sums
+  //    in registers for the scan below.
+  const bool one_batch = a.nunit <= kThreads;
+  double my_all_t = 0.0, my_pos_t = 0.0, my_pos_d = 0.0;
   double tot[2] = {0.0, 0.0};
-  for (int i = threadIdx.x; i < a.nunit; i += kThreads) {
-    tot[0] += cload(&ur[i].st_all);
-    tot[1] += cload(&ur[i].sd_all);
+  for (int i = tid; i < a.nunit; i += kThreads) {
+    const double at = ur[i].st_all, ad = ur[i].sd_all;
+    tot[0] += at;
+    tot[1] += ad;
+    if (one_batch) { my_all_t = at; my_pos_t = ur[i].st_pos; my_pos_d = ur[i].sd_pos; }
   }
   block_sum_doubles<2>(tot);
   const double zt = tot[0], zd = tot[1];
+  auto weight_of = [&](int i, bool resid) -> double {
+    if (one_batch) return unit_weight(my_pos_t, my_pos_d, my_all_t, resid, zt, zd);
+    return unit_weight(ur[i].st_pos, ur[i].sd_pos, ur[i].st_all, resid, zt, zd);
+  };
+  // 2) an empty residual (p and q equal up to rounding) draws from p of that
+  //    position instead
   bool residual = d.mode == kModeResidual;
-  // total weight; an empty residual (p and q equal up to rounding) draws from
-  // p of that position instead
+  if (residual) {
+    double ws[1] = {0.0};
+    for (int i = tid; i < a.nunit; i += kThreads) ws[0] += weight_of(i, true);
+    block_sum_doubles<1>(ws);
+    if (!(ws[0] > 0.0)) residual = false;
+  }
   double W;
   {
     double ws[1] = {0.0};
-    for (int i = threadIdx.x; i < a.nunit; i += kThreads)
-      ws[0] += unit_weight(cload(&ur[i].st_pos), cload(&ur[i].sd_pos), cload(&ur[i].st_all),
-                           residual, zt, zd);
+    for (int i = tid; i < a.nunit; i += kThreads) ws[0] += weight_of(i, residual);
     block_sum_doubles<1>(ws);
     W = ws[0];
-    if (residual && !(W > 0.0)) {
-      residual = false;
-      W = zt;
-    }
   }
   const double target = static_cast<double>(d.u) * W;
-  // crossing unit: block scan over units in batches of kThreads
-  if (threadIdx.x == 0) { s_found = 0; s_unit = -1; }
+  // 3) crossing unit: block scan of the unit weights in unit order
+  if (tid == 0) { s_unit = -1; s_lastpos = -1; }
   __syncthreads();
   double carry = 0.0;
-  int last_pos_unit = -1;
   for (int base = 0; base < a.nunit; base += kThreads) {
-    const int i = base + static_cast<int>(threadIdx.x);
-    double wu = 0.0;
-    if (i < a.nunit)
-      wu = unit_weight(cload(&ur[i].st_pos), cload(&ur[i].sd_pos), cload(&ur[i].st_all), residual, zt, zd);
+    const int i = base + tid;
+    const double wu = i < a.nunit ? weight_of(i, residual) : 0.0;
     double total;
     const double before = carry + block_exclusive_scan(wu, &total);
-    if (i < a.nunit && wu > 0.0) last_pos_unit = i;
-    const bool hit = i < a.nunit && before + wu > target;
-    // the first hitting thread wins
-    __shared__ int s_first;
-    if (threadIdx.x == 0) s_first = 0x7fffffff;
+    if (tid == 0) s_first = 0x7fffffff;
     __syncthreads();
-    if (hit && !s_found) atomicMin(&s_first, i);
+    if (i < a.nunit && wu > 0.0) atomicMax(&s_lastpos, i);
+    if (i < a.nunit && before + wu > target) atomicMin(&s_first, i);
     __syncthreads();
-    if (!s_found && s_first != 0x7fffffff && i == s_first) {
+    if (s_first != 0x7fffffff && i == s_first) {
       s_unit = i;
       s_before = before;
     }
     __syncthreads();
-    if (threadIdx.x == 0 && s_unit >= 0) s_found = 1;
-    __syncthreads();
     carry += total;
-    if (s_found) break;
+    if (s_unit >= 0) break;
   }
-  if (!s_found) {  // rounding left u * W at the very top: take the last positive unit
-    __shared__ int s_lp;
-    if (threadIdx.x == 0) s_lp = -1;
-    __syncthreads();
-    if (last_pos_unit >= 0) atomicMax(&s_lp, last_pos_unit);
-    __syncthreads();
-    const int lp = s_lp < 0 ? 0 : s_lp;
+  if (s_unit < 0) {  // rounding left u * W at the very top: take the last positive unit
+    const int lp = s_lastpos < 0 ? 0 : s_lastpos;
     double bsum[1] = {0.0};
-    for (int i = threadIdx.x; i < lp; i += kThreads)
-      bsum[0] += unit_weight(cload(&ur[i].st_pos), cload(&ur[i].sd_pos), cload(&ur[i].st_all), residual, zt, zd);
+    for (int i = tid; i < lp; i += kThreads) bsum[0] += weight_of(i, residual);
     block_sum_doubles<1>(bsum);
-    if (threadIdx.x == 0) { s_unit = lp; s_before = bsum[0]; }
+    if (tid == 0) { s_unit = lp; s_before = bsum[0]; }
     __syncthreads();
   }
-  // crossing sub-span inside the unit
-  if (threadIdx.x == 0) {
-    const UnitRec* u = ur + s_unit;
+  // 4) crossing sub-span inside the unit
+  if (tid == 0) {
+    const UnitRec& u = ur[s_unit];
     double ws[kWaves];
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i)
-      ws[i] = unit_weight(cload(&u->w_pos_t[i]), cload(&u->w_pos_d[i]), cload(&u->w_all_t[i]),
-                          residual, zt, zd);
+    for (int i = 0; i < kWaves; ++i) ws[i] = unit_weight(u.w_pos_t[i], u.w_pos_d[i], u.w_all_t[i], residual, zt, zd);
     double run = s_before;
     int sub = -1, lastsub = -1;
     double before_sub = run;
@@ -569,9 +548,9 @@ __device__ void finalize(const ChainArgs& a, int b, const DecisionRec& d) {
     s_before = before_sub;
   }
   __syncthreads();
-  // fp64 scan of the crossing sub-span by one wave; lane l owns kPer elements
-  if (static_cast<int>(threadIdx.x) < kWave) {
-    const int lane = threadIdx.x;
+  // 5) fp64 scan of the crossing sub-span by one wave; lane l owns kPer logits
+  if (tid < kWave) {
+    const int lane = tid;
     const int k0 = s_unit * S::kSpan + (s_sub * kWave + lane) * S::kPer;
     const double inv_t = 1.0 / static_cast<double>(d.t);
     const int trow = d.mode == kModeResidual ? d.n : G;
@@ -612,94 +591,40 @@ __device__ void finalize(const ChainArgs& a, int b, const DecisionRec& d) {
       hit = min(hit, __shfl_xor(hit, o, kWave));
       last_pos = max(last_pos, __shfl_xor(last_pos, o, kWave));
     }
-    if (lane == 0) {
-      const int tok = (hit != 0x7fffffff) ? hit : last_pos;
-      a.out_tokens[static_cast<size_t>(b) * (G + 1) + d.n] = tok;
-    }
+    if (lane == 0) a.out_tokens[static_cast<size_t>(b) * (G + 1) + d.n] = (hit != 0x7fffffff) ? hit : last_pos;
   }
   __syncthreads();
-  // every unit of this request has arrived and read the decision: return the
-  // request's unit records and decision record to zero
-  {
-    unsigned long long* w = reinterpret_cast<unsigned long long*>(a.units + static_cast<size_t>(b) * a.nunit);
-    const int nw = a.nunit * static_cast<int>(sizeof(UnitRec) / 8);
-    for (int i = threadIdx.x; i < nw; i += kThreads) cstore(w + i, 0ull);
-    unsigned long long* dw = reinterpret_cast<unsigned long long*>(a.decisions + b);
-    if (static_cast<int>(threadIdx.x) < static_cast<int>(sizeof(DecisionRec) / 8)) cstore(dw + threadIdx.x, 0ull);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// the kernel
-// ---------------------------------------------------------------------------
-// Flag of request b as seen by thread 0, broadcast to the workgroup.
-__device__ inline int read_flag(const ChainArgs& a, int b) {
-  __shared__ int s_f;
-  if (threadIdx.x == 0) s_f = cload(&a.flag[b * kLine]);
-  __syncthreads();
-  const int f = s_f;
-  __syncthreads();
-  return f;
 }
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void chain_fused(ChainArgs a) {
-  const int R = 2 * a.gamma + 1;
-  const int per_req = R * a.nchunk;
-  const int nunits = a.B * a.nunit;
-  int q = blockIdx.x;  // this workgroup's next draw unit
-  // phase 1: row items, grid-stride; after each, run this workgroup's next
-  // draw unit if its request is already decided
-  for (int it = blockIdx.x; it < a.nslots; it += gridDim.x) {
-    const int b = it / per_req;
-    const int rem = it % per_req;
-    const int k = rem / a.nchunk;
-    const int c = rem % a.nchunk;
-    const float T = a.temperature[b];
-    if (!temp_ok(T)) {
-      if (k == 0 && c == 0) {  // the whole request is invalid
-        for (int i = threadIdx.x; i <= a.gamma; i += kThreads)
-          a.out_tokens[static_cast<size_t>(b) * (a.gamma + 1) + i] = -1;
-        if (threadIdx.x == 0) {
-          a.out_n[b] = -1;
-          cstore(&a.flag[b * kLine], int(kFlagDone));
-        }
-      }
-      continue;
-    }
-    if (k >= needed_rows(a, T)) continue;  // draft rows are not read for this request
-    row_item<DT, VEC>(a, b, k, c, T);
-    if (q < nunits) {
-      const int qb = q / a.nunit;
-      const int f = read_flag(a, qb);
-      if (f != kFlagNone) {
-        draw_unit<DT, VEC>(a, qb, q % a.nunit, f);
-        q += gridDim.x;
-      }
+__global__ __launch_bounds__(kThreads) void chain_finalize(ChainArgs a) {
+  const int b = blockIdx.x;
+  const int G = a.gamma;
+  const int R = 2 * G + 1;
+  const float T = a.temperature[b];
+  const int cls = request_class(a, T);
+  if (cls == 2) return;  // nothing of this request is in the workspace
+  if (cls == 0) {
+    const Decision d = decide<DT>(a, b);
+    if (!d.bad) {
+      draw_token<DT, VEC>(a, b, d);
+      unsigned long long* w = reinterpret_cast<unsigned long long*>(a.units + static_cast<size_t>(b) * a.nunit);
+      const int nw = a.nunit * static_cast<int>(sizeof(UnitRec) / 8);
+      for (int i = threadIdx.x; i < nw; i += kThreads) w[i] = 0ull;
     }
   }
-  // phase 2: the remaining draw units, each as soon as its request is decided
-  for (; q < nunits; q += gridDim.x) {
-    const int qb = q / a.nunit;
-    int f = read_flag(a, qb);
-    for (int spins = 0, nap = 1; f == kFlagNone && spins < kSpinLimit; ++spins) {
-      if (nap < 16) {
-        __builtin_amdgcn_s_sleep(1);
-        nap <<= 1;
-      } else {
-        __builtin_amdgcn_s_sleep(16);
-      }
-      f = read_flag(a, qb);
-    }
-    draw_unit<DT, VEC>(a, qb, q % a.nunit, f == kFlagNone ? int(kFlagDone) : f);
-  }
+  // the request's row partials and gathered logits back to zero
+  const int nrows = needed_rows(a, T);
+  unsigned long long* p = reinterpret_cast<unsigned long long*>(a.partials + static_cast<size_t>(b) * R * a.nchunk);
+  for (int i = threadIdx.x; i < nrows * a.nchunk; i += kThreads) p[i] = 0ull;
+  if (static_cast<int>(threadIdx.x) < R) a.gathers[static_cast<size_t>(b) * R + threadIdx.x] = 0.0f;
 }
 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct ChainLayout {
-  size_t partials, cnt_rows, cnt_units, flag, decisions, units, total;
+  size_t partials, gathers, units, total;
 };
 
 static int units_for(int V, int kper) {
@@ -714,50 +639,28 @@ static ChainLayout chain_layout(int B, int gamma, int V) {
   const size_t R = 2 * static_cast<size_t>(gamma) + 1;
   const size_t nunit = static_cast<size_t>(units_for(V, 1));
   size_t off = 0;
-  L.partials = off;  off = align_up(off + static_cast<size_t>(B) * R * nchunk * sizeof(RowPartial));
-  L.cnt_rows = off;  off = align_up(off + static_cast<size_t>(B) * kLine * sizeof(int));
-  L.cnt_units = off; off = align_up(off + static_cast<size_t>(B) * kLine * sizeof(int));
-  L.flag = off;      off = align_up(off + static_cast<size_t>(B) * kLine * sizeof(int));
-  L.decisions = off; off = align_up(off + static_cast<size_t>(B) * sizeof(DecisionRec));
-  L.units = off;     off = align_up(off + static_cast<size_t>(B) * nunit * sizeof(UnitRec));
+  L.partials = off; off = align_up(off + static_cast<size_t>(B) * R * nchunk * sizeof(RowPartial));
+  L.gathers = off;  off = align_up(off + static_cast<size_t>(B) * R * sizeof(float));
+  L.units = off;    off = align_up(off + static_cast<size_t>(B) * nunit * sizeof(UnitRec));
   L.total = off;
   return L;
 }
 
-// Co-resident workgroups of one kernel on the current device (cached per device).
-template <int DT, bool VEC>
-static int coresident_blocks() {
-  static std::mutex mu;
-  static std::vector<std::pair<int, int>> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  std::lock_guard<std::mutex> lock(mu);
-  for (const auto& e : cache)
-    if (e.first == dev) return e.second;
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_fused<DT, VEC>, kThreads, 0) != hipSuccess)
-    return -1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  const int n = per_cu * cus;
-  cache.emplace_back(dev, n);
-  return n;
-}
+// Grids of the two streaming launches are capped; their workgroups stride over
+// the remaining items.
+constexpr long long kMaxGrid = 1 << 20;
 
 template <int DT, bool VEC>
 static int launch_chain(ChainArgs a, hipStream_t stream) {
-  const int cap = coresident_blocks<DT, VEC>();
-  if (cap <= 0) return SV_ERR_HIP;
-  const long long slots = static_cast<long long>(a.B) * (2 * a.gamma + 1) * a.nchunk;
-  if (slots > 0x7fffffffLL) return SV_ERR_SHAPE;
-  a.nslots = static_cast<int>(slots);
+  const long long items = static_cast<long long>(a.B) * (2 * a.gamma + 1) * a.nchunk;
   a.nunit = units_for(a.V, Slice<DT, VEC, 1>::kPer);
-  if (static_cast<long long>(a.B) * a.nunit > 0x7fffffffLL) return SV_ERR_SHAPE;
-  const int grid = static_cast<int>(std::min<long long>(cap, std::max<long long>(1, slots)));
-  void* args[] = {&a};
-  if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&chain_fused<DT, VEC>), dim3(grid),
-                                 dim3(kThreads), args, 0, stream) != hipSuccess)
-    return SV_ERR_HIP;
-  return SV_OK;
+  const long long units = static_cast<long long>(a.B) * a.nunit;
+  hipLaunchKernelGGL((chain_row_stats<DT, VEC>), dim3(static_cast<unsigned>(items < kMaxGrid ? items : kMaxGrid)),
+                     dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((chain_units<DT, VEC>), dim3(static_cast<unsigned>(units < kMaxGrid ? units : kMaxGrid)),
+                     dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((chain_finalize<DT, VEC>), dim3(static_cast<unsigned>(a.B)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
 }  // namespace sv
@@ -766,7 +669,8 @@ using namespace sv;
 
 extern "C" size_t sv_chain_workspace_bytes(int B, int gamma, int V, int dtype) {
   (void)dtype;
-  if (B < 0 || gamma < 0 || gamma > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB) return 0;
+  if (B < 0 || B > SV_MAX_BATCH || gamma < 0 || gamma > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB)
+    return 0;
   return chain_layout(B, gamma, V).total;
 }
 
@@ -776,7 +680,8 @@ extern "C" int spec_verify_chain(const void* target_logits, const void* draft_lo
                                  int32_t* out_tokens, int32_t* out_num_accepted,
                                  void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (dtype != SV_BF16 && dtype != SV_F32) return SV_ERR_DTYPE;
-  if (B < 0 || gamma < 0 || gamma > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB) return SV_ERR_SHAPE;
+  if (B < 0 || B > SV_MAX_BATCH || gamma < 0 || gamma > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB)
+    return SV_ERR_SHAPE;
   if (B == 0) return SV_OK;
   if (!target_logits || !temperature || !uniforms || !out_tokens || !out_num_accepted || !workspace)
     return SV_ERR_NULL;
@@ -799,10 +704,7 @@ extern "C" int spec_verify_chain(const void* target_logits, const void* draft_lo
   a.out_tokens = out_tokens;
   a.out_n = out_num_accepted;
   a.partials = reinterpret_cast<RowPartial*>(ws + L.partials);
-  a.cnt_rows = reinterpret_cast<int*>(ws + L.cnt_rows);
-  a.cnt_units = reinterpret_cast<int*>(ws + L.cnt_units);
-  a.flag = reinterpret_cast<int*>(ws + L.flag);
-  a.decisions = reinterpret_cast<DecisionRec*>(ws + L.decisions);
+  a.gathers = reinterpret_cast<float*>(ws + L.gathers);
   a.units = reinterpret_cast<UnitRec*>(ws + L.units);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const int kv = dtype == SV_BF16 ? Elem<0>::kVec : Elem<1>::kVec;

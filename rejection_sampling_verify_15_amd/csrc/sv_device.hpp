@@ -255,3 +255,32 @@ __device__ inline double block_exclusive_scan(double v, double* total) {
 }
 
 }  // namespace sv
+
+namespace sv {
+
+// Exclusive prefix sum over the workgroup of one int per thread (thread
+// order); returns this thread's prefix and writes the total to *total.
+__device__ inline int block_exclusive_scan_int(int v, int* total) {
+  __shared__ int sw[kWaves];
+  const int lane = threadIdx.x % kWave;
+  const int w = threadIdx.x / kWave;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += t;
+  }
+  if (lane == kWave - 1) sw[w] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < w) before += sw[i];
+    all += sw[i];
+  }
+  __syncthreads();
+  *total = all;
+  return before + inc - v;
+}
+
+}  // namespace sv
