@@ -190,6 +190,45 @@ SV_API int spec_probs_debug(const void* target_logits, const void* draft_logits,
                      float* target_lse, float* draft_lse,
                      void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* ------------------------------------------------------------------------
+ * Kernel timing, for benchmarks.  While a timing session is open, every
+ * kernel the library launches carries a pair of HIP events attached to its
+ * dispatch (hipExtLaunchKernel), so the recorded time is the kernel's own
+ * execution with no extra packets on the stream.
+ *
+ * sv_timing_begin(capacity)  creates `capacity` event pairs and opens a
+ *     session (host call; not while the stream is being captured).  Launches
+ *     beyond the capacity run untimed.  SV_ERR_SHAPE if capacity is not in
+ *     [1, 1 << 20], SV_ERR_HIP if event creation fails.
+ * sv_timing_end(total_ms, launches, n)  waits for every recorded launch,
+ *     ADDS each kernel's summed milliseconds and launch count into
+ *     total_ms[k] / launches[k] for k < n (indexed by sv_kernel; either
+ *     array may be NULL), destroys the events and closes the session.
+ *     Returns SV_ERR_HIP if an event could not be read.
+ * One session at a time per process; calls from several host threads during
+ * a session are recorded in launch order.
+ * ---------------------------------------------------------------------- */
+typedef enum {
+  SV_K_CHAIN_ROW_STATS = 0,   /* chain: per-(row, chunk) max / exp-sum / argmax */
+  SV_K_CHAIN_UNITS = 1,       /* chain: decisions and per-unit sums of the final draw */
+  SV_K_CHAIN_FINALIZE = 2,    /* chain: the final inverse-CDF draw per request */
+  SV_K_TREE_INIT = 3,
+  SV_K_TREE_NODE_PASS = 4,
+  SV_K_TREE_CHOOSE = 5,
+  SV_K_PROBS_ROW_STATS = 6,
+  SV_K_PROBS_RESIDUAL = 7,
+  SV_K_PROBS_FINALIZE = 8,
+  SV_K_WORKSPACE_CLEAR = 9,
+  SV_K_COUNT = 10
+} sv_kernel;
+
+/* Name of a kernel id (static storage; "unknown" outside [0, SV_K_COUNT)). */
+SV_API const char* sv_kernel_name(int kernel);
+
+SV_API int sv_timing_begin(int capacity);
+
+SV_API int sv_timing_end(double* total_ms, int* launches, int n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,7 +34,12 @@ EXPORTS = {
     "sv_probs_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "spec_probs_debug": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 4 +
                          [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "sv_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
+    "sv_timing_begin": (ctypes.c_int, [ctypes.c_int]),
+    "sv_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
+                                     ctypes.c_int]),
 }
+SV_K_COUNT = 10
 
 _LIB = None
 _LOCK = threading.Lock()
@@ -226,3 +231,39 @@ def probs_debug(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.T
                             _ptr(out["draft_lse"]), _ptr(ws), ws.numel(), _stream_handle(dev))
     _check(st, "spec_probs_debug")
     return out
+
+
+# ---------------------------------------------------------------------------
+# kernel timing sessions
+# ---------------------------------------------------------------------------
+class KernelTimer:
+    """Context manager around sv_timing_begin / sv_timing_end: every kernel the
+    library launches inside the block is timed by events attached to its
+    dispatch.  After the block, .ms[name] and .launches[name] hold the summed
+    milliseconds and launch counts per kernel."""
+
+    def __init__(self, capacity: int):
+        self.capacity = int(capacity)
+        self.ms = {}
+        self.launches = {}
+
+    def __enter__(self):
+        _check(lib().sv_timing_begin(self.capacity), "sv_timing_begin")
+        return self
+
+    def __exit__(self, *exc):
+        L = lib()
+        tot = (ctypes.c_double * SV_K_COUNT)()
+        cnt = (ctypes.c_int * SV_K_COUNT)()
+        st = L.sv_timing_end(tot, cnt, SV_K_COUNT)
+        for k in range(SV_K_COUNT):
+            if cnt[k]:
+                name = L.sv_kernel_name(k).decode()
+                self.ms[name] = float(tot[k])
+                self.launches[name] = int(cnt[k])
+        if exc[0] is None:
+            _check(st, "sv_timing_end")
+        return False
+
+    def mean_us(self, name: str) -> float:
+        return 1e3 * self.ms[name] / self.launches[name]

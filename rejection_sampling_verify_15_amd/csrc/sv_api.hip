@@ -1,5 +1,10 @@
-// Library-wide C-ABI entry points: status strings, version, workspace clear.
+// Library-wide C-ABI entry points: status strings, version, workspace clear,
+// kernel timing.
 #include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <mutex>
+#include <vector>
 
 #include "sv_host.hpp"
 
@@ -13,7 +18,84 @@ __global__ void fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t ntai
     for (size_t i = threadIdx.x; i < ntail; i += blockDim.x) tail[i] = 0;
 }
 
+// ---------------------------------------------------------------------------
+// kernel timing sessions
+// ---------------------------------------------------------------------------
+namespace {
+struct TimedLaunch {
+  int kernel;
+  hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+std::atomic<bool> g_timing_on{false};
+std::vector<TimedLaunch> g_timed;  // the session's event pairs
+size_t g_timed_used = 0;
+
+void destroy_events() {
+  for (TimedLaunch& t : g_timed) {
+    if (t.start) (void)hipEventDestroy(t.start);
+    if (t.stop) (void)hipEventDestroy(t.stop);
+  }
+  g_timed.clear();
+  g_timed_used = 0;
+}
+}  // namespace
+
+void timing_slot(int kernel, hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
+  if (!g_timing_on.load(std::memory_order_acquire)) return;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (!g_timing_on.load(std::memory_order_relaxed) || g_timed_used >= g_timed.size()) return;
+  TimedLaunch& t = g_timed[g_timed_used++];
+  t.kernel = kernel;
+  *start = t.start;
+  *stop = t.stop;
+}
+
 }  // namespace sv
+
+extern "C" const char* sv_kernel_name(int kernel) {
+  static const char* const names[SV_K_COUNT] = {
+      "chain_row_stats", "chain_units", "chain_finalize", "tree_init", "tree_node_pass",
+      "tree_choose", "probs_row_stats", "probs_residual", "probs_finalize", "fill_zero"};
+  return (kernel >= 0 && kernel < SV_K_COUNT) ? names[kernel] : "unknown";
+}
+
+extern "C" int sv_timing_begin(int capacity) {
+  if (capacity < 1 || capacity > (1 << 20)) return SV_ERR_SHAPE;
+  std::lock_guard<std::mutex> lk(sv::g_timing_mu);
+  sv::g_timing_on.store(false, std::memory_order_release);
+  sv::destroy_events();
+  sv::g_timed.resize(static_cast<size_t>(capacity), sv::TimedLaunch{-1, nullptr, nullptr});
+  for (sv::TimedLaunch& t : sv::g_timed) {
+    if (hipEventCreate(&t.start) != hipSuccess || hipEventCreate(&t.stop) != hipSuccess) {
+      sv::destroy_events();
+      return SV_ERR_HIP;
+    }
+  }
+  sv::g_timing_on.store(true, std::memory_order_release);
+  return SV_OK;
+}
+
+extern "C" int sv_timing_end(double* total_ms, int* launches, int n) {
+  std::lock_guard<std::mutex> lk(sv::g_timing_mu);
+  sv::g_timing_on.store(false, std::memory_order_release);
+  int status = SV_OK;
+  for (size_t i = 0; i < sv::g_timed_used; ++i) {
+    const sv::TimedLaunch& t = sv::g_timed[i];
+    float ms = 0.0f;
+    if (hipEventSynchronize(t.stop) != hipSuccess || hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess) {
+      status = SV_ERR_HIP;
+      continue;
+    }
+    if (t.kernel >= 0 && t.kernel < n) {
+      if (total_ms) total_ms[t.kernel] += ms;
+      if (launches) launches[t.kernel] += 1;
+    }
+  }
+  sv::destroy_events();
+  return status;
+}
 
 extern "C" const char* sv_status_string(int status) {
   switch (status) {
@@ -40,8 +122,7 @@ extern "C" int sv_workspace_clear(void* workspace, size_t bytes, void* hip_strea
   size_t blocks = (n16 + 255) / 256;
   if (blocks < 1) blocks = 1;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(sv::fill_zero, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     static_cast<hipStream_t>(hip_stream), static_cast<uint4*>(workspace), n16,
-                     tail, ntail);
+  sv::launch(SV_K_WORKSPACE_CLEAR, sv::fill_zero, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+             static_cast<hipStream_t>(hip_stream), static_cast<uint4*>(workspace), n16, tail, ntail);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }

@@ -655,11 +655,11 @@ static int launch_chain(ChainArgs a, hipStream_t stream) {
   const long long items = static_cast<long long>(a.B) * (2 * a.gamma + 1) * a.nchunk;
   a.nunit = units_for(a.V, Slice<DT, VEC, 1>::kPer);
   const long long units = static_cast<long long>(a.B) * a.nunit;
-  hipLaunchKernelGGL((chain_row_stats<DT, VEC>), dim3(static_cast<unsigned>(items < kMaxGrid ? items : kMaxGrid)),
-                     dim3(kThreads), 0, stream, a);
-  hipLaunchKernelGGL((chain_units<DT, VEC>), dim3(static_cast<unsigned>(units < kMaxGrid ? units : kMaxGrid)),
-                     dim3(kThreads), 0, stream, a);
-  hipLaunchKernelGGL((chain_finalize<DT, VEC>), dim3(static_cast<unsigned>(a.B)), dim3(kThreads), 0, stream, a);
+  launch(SV_K_CHAIN_ROW_STATS, chain_row_stats<DT, VEC>, dim3(static_cast<unsigned>(items < kMaxGrid ? items : kMaxGrid)),
+         dim3(kThreads), 0, stream, a);
+  launch(SV_K_CHAIN_UNITS, chain_units<DT, VEC>, dim3(static_cast<unsigned>(units < kMaxGrid ? units : kMaxGrid)),
+         dim3(kThreads), 0, stream, a);
+  launch(SV_K_CHAIN_FINALIZE, chain_finalize<DT, VEC>, dim3(static_cast<unsigned>(a.B)), dim3(kThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

@@ -4,6 +4,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+
 #include "specverify.h"
 
 namespace sv {
@@ -12,6 +15,20 @@ inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
 inline bool aligned(const void* p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+// Hands out the event pair of the next timed launch while a timing session is
+// open (sv_timing_begin); leaves both NULL otherwise.
+void timing_slot(int kernel, hipEvent_t* start, hipEvent_t* stop);
+
+// Every kernel launch of the library goes through here: a plain dispatch, with
+// events attached to it during a timing session.
+template <typename F, typename... Args>
+inline void launch(int kernel, F fn, dim3 grid, dim3 block, uint32_t shmem, hipStream_t stream,
+                   Args... args) {
+  hipEvent_t start = nullptr, stop = nullptr;
+  timing_slot(kernel, &start, &stop);
+  hipExtLaunchKernelGGL(fn, grid, block, shmem, stream, start, stop, 0u, args...);
 }
 
 }  // namespace sv

@@ -185,10 +185,10 @@ static int launch_probs(const ProbsArgs& a, hipStream_t stream) {
   const long long n1 = static_cast<long long>(a.B) * (2 * a.gamma + 1) * a.nchunk;
   const long long n2 = static_cast<long long>(a.B) * a.gamma * a.nchunk;
   if (n1 > 0x7fffffffLL || n2 > 0x7fffffffLL) return SV_ERR_SHAPE;
-  hipLaunchKernelGGL((probs_row_stats<DT, VEC>), dim3(static_cast<unsigned>(n1)), dim3(kThreads), 0, stream, a);
+  launch(SV_K_PROBS_ROW_STATS, probs_row_stats<DT, VEC>, dim3(static_cast<unsigned>(n1)), dim3(kThreads), 0, stream, a);
   if (n2 > 0)
-    hipLaunchKernelGGL((probs_residual<DT, VEC>), dim3(static_cast<unsigned>(n2)), dim3(kThreads), 0, stream, a);
-  hipLaunchKernelGGL((probs_finalize<DT>), dim3(static_cast<unsigned>(a.B)), dim3(kThreads), 0, stream, a);
+    launch(SV_K_PROBS_RESIDUAL, probs_residual<DT, VEC>, dim3(static_cast<unsigned>(n2)), dim3(kThreads), 0, stream, a);
+  launch(SV_K_PROBS_FINALIZE, probs_finalize<DT>, dim3(static_cast<unsigned>(a.B)), dim3(kThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

@@ -276,10 +276,10 @@ template <int DT, bool VEC>
 static int launch_tree(const TreeArgs& a, hipStream_t stream) {
   const long long n = static_cast<long long>(a.B) * a.nchunk;
   if (n > 0x7fffffffLL) return SV_ERR_SHAPE;
-  hipLaunchKernelGGL(tree_init, dim3(a.B), dim3(kThreads), a.N * sizeof(int32_t), stream, a);
+  launch(SV_K_TREE_INIT, tree_init, dim3(a.B), dim3(kThreads), a.N * sizeof(int32_t), stream, a);
   for (int step = 0; step <= a.max_depth; ++step) {
-    hipLaunchKernelGGL((tree_node_pass<DT, VEC>), dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL((tree_choose<DT>), dim3(a.B), dim3(kThreads), 0, stream, a);
+    launch(SV_K_TREE_NODE_PASS, tree_node_pass<DT, VEC>, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, stream, a);
+    launch(SV_K_TREE_CHOOSE, tree_choose<DT>, dim3(a.B), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }

@@ -49,6 +49,19 @@ def test_status_strings(lib):
     assert lib.sv_version().count(b".") == 2
 
 
+def test_kernel_names_and_timing_validation(lib):
+    names = [lib.sv_kernel_name(k).decode() for k in range(binding.SV_K_COUNT)]
+    assert names[0] == "chain_row_stats" and len(set(names)) == binding.SV_K_COUNT
+    assert lib.sv_kernel_name(-1) == b"unknown" and lib.sv_kernel_name(binding.SV_K_COUNT) == b"unknown"
+    assert lib.sv_timing_begin(0) == sv.SV_ERR_SHAPE
+    assert lib.sv_timing_begin((1 << 20) + 1) == sv.SV_ERR_SHAPE
+    # no session open: nothing to wait for, nothing added
+    tot = (ctypes.c_double * binding.SV_K_COUNT)()
+    cnt = (ctypes.c_int * binding.SV_K_COUNT)()
+    assert lib.sv_timing_end(tot, cnt, binding.SV_K_COUNT) == sv.SV_OK
+    assert sum(cnt) == 0 and sum(tot) == 0.0
+
+
 def test_workspace_queries(lib):
     assert lib.sv_chain_workspace_bytes(64, 4, 128256, 0) > 0
     assert lib.sv_chain_workspace_bytes(64, 33, 128256, 0) == 0   # gamma above the cap
