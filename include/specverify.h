@@ -209,17 +209,16 @@ SV_API int spec_probs_debug(const void* target_logits, const void* draft_logits,
  * a session are recorded in launch order.
  * ---------------------------------------------------------------------- */
 typedef enum {
-  SV_K_CHAIN_ROW_STATS = 0,   /* chain: per-(row, chunk) max / exp-sum / argmax */
-  SV_K_CHAIN_UNITS = 1,       /* chain: decisions and per-unit sums of the final draw */
-  SV_K_CHAIN_FINALIZE = 2,    /* chain: the final inverse-CDF draw per request */
-  SV_K_TREE_INIT = 3,
-  SV_K_TREE_NODE_PASS = 4,
-  SV_K_TREE_CHOOSE = 5,
-  SV_K_PROBS_ROW_STATS = 6,
-  SV_K_PROBS_RESIDUAL = 7,
-  SV_K_PROBS_FINALIZE = 8,
-  SV_K_WORKSPACE_CLEAR = 9,
-  SV_K_COUNT = 10
+  SV_K_CHAIN_ROW_STATS = 0,   /* chain: per-(row, chunk) max / exp-sum / argmax, and the accept tests */
+  SV_K_CHAIN_UNITS = 1,       /* chain: per-unit sums and the final inverse-CDF draw */
+  SV_K_TREE_INIT = 2,
+  SV_K_TREE_NODE_PASS = 3,
+  SV_K_TREE_CHOOSE = 4,
+  SV_K_PROBS_ROW_STATS = 5,
+  SV_K_PROBS_RESIDUAL = 6,
+  SV_K_PROBS_FINALIZE = 7,
+  SV_K_WORKSPACE_CLEAR = 8,
+  SV_K_COUNT = 9
 } sv_kernel;
 
 /* Name of a kernel id (static storage; "unknown" outside [0, SV_K_COUNT)). */

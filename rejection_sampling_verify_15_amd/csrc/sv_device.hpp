@@ -16,7 +16,7 @@ namespace sv {
 constexpr int kThreads = 256;
 constexpr int kWave = 64;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kChunk = 8192;  // logits per (row, chunk) work item
+constexpr int kChunk = 16384;  // logits per (row, chunk) work item
 
 __host__ __device__ inline int num_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
@@ -118,6 +118,41 @@ struct Slice {
 };
 
 // ---------------------------------------------------------------------------
+// fp64 exponential of a non-positive argument
+// ---------------------------------------------------------------------------
+constexpr double kLog2e = 0x1.71547652b82fep+0;
+
+// 2^t for t <= 0 (t = -inf gives 0), relative error about 3e-13 for results
+// above 2^-1022 (below, the denormal result is rounded by the final scaling).
+// t = n + f with n an integer (rounded by adding and subtracting 1.5 * 2^52)
+// and |f| <= 1/2; 2^f = e^(f ln 2) by its Taylor series to degree 10
+// (truncation below 3.1e-13); then the result is scaled by 2^n.
+__host__ __device__ inline double exp2_nonpos(double t_in) {
+  constexpr double kShift = 0x1.8p52;
+  const double t = __builtin_fmax(t_in, -1100.0);  // -inf -> 2^-1100 -> 0
+  const double sh = t + kShift;
+  const double n = sh - kShift;
+  const double f = t - n;
+  double p = 0x1.e4cf5158b8ecap-28;          // ln2^10 / 10!
+  p = __builtin_fma(p, f, 0x1.b5253d395e7c4p-24);
+  p = __builtin_fma(p, f, 0x1.62c0223a5c824p-20);
+  p = __builtin_fma(p, f, 0x1.ffcbfc588b0c7p-17);
+  p = __builtin_fma(p, f, 0x1.430912f86c787p-13);
+  p = __builtin_fma(p, f, 0x1.5d87fe78a6731p-10);
+  p = __builtin_fma(p, f, 0x1.3b2ab6fba4e77p-7);
+  p = __builtin_fma(p, f, 0x1.c6b08d704a0c0p-5);
+  p = __builtin_fma(p, f, 0x1.ebfbdff82c58fp-3);
+  p = __builtin_fma(p, f, 0x1.62e42fefa39efp-1);  // ln2
+  p = __builtin_fma(p, f, 1.0);
+  struct Words { uint32_t lo, hi; };
+  const int ni = static_cast<int>(__builtin_bit_cast(Words, sh).lo);  // n, two's complement
+  return __builtin_ldexp(p, ni);
+}
+
+// e^y for y <= 0.
+__host__ __device__ inline double exp_nonpos(double y) { return exp2_nonpos(y * kLog2e); }
+
+// ---------------------------------------------------------------------------
 // reductions
 // ---------------------------------------------------------------------------
 // (value, index) argmax with the lowest index among equal values.
@@ -149,6 +184,18 @@ __device__ inline MaxSum maxsum_combine(MaxSum a, MaxSum b, float s) {
 template <typename T> __device__ inline T wave_sum(T v) {
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ inline int wave_min(int v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ inline int wave_max_int(int v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
   return v;
 }
 
@@ -254,9 +301,48 @@ __device__ inline double block_exclusive_scan(double v, double* total) {
   return before + exc;
 }
 
-}  // namespace sv
+// ---------------------------------------------------------------------------
+// hand-off between workgroups of one launch
+// ---------------------------------------------------------------------------
+// Data that one workgroup produces and another consumes within the same
+// launch travels through agent-scope (whole-device) atomic accesses: the
+// stores write through to the device-coherent level and the loads read from
+// it, so neither depends on which XCD's L2 holds a copy.  A producer makes its
+// stores visible by waiting for their completion before it counts itself in;
+// the consumer that sees the final count issues its loads after that atomic
+// returns.
+__device__ inline void store_coherent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void store_coherent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t load_coherent(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint32_t load_coherent(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline double load_coherent_f64(const double* p) {
+  return __longlong_as_double(static_cast<long long>(load_coherent(reinterpret_cast<const uint64_t*>(p))));
+}
+__device__ inline void store_coherent_f64(double* p, double v) {
+  store_coherent(reinterpret_cast<uint64_t*>(p), static_cast<uint64_t>(__double_as_longlong(v)));
+}
 
-namespace sv {
+// Waits until every memory access this wave has issued is complete (on gfx9
+// the vector-memory counter covers stores as well as loads); also a compiler
+// barrier.
+__device__ inline void wait_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Counts the calling thread in on `counter` once its wave's coherent stores
+// are complete; returns the count before this arrival.
+__device__ inline uint32_t arrive(uint32_t* counter) {
+  wait_memory();
+  const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("" ::: "memory");
+  return old;
+}
 
 // Exclusive prefix sum over the workgroup of one int per thread (thread
 // order); returns this thread's prefix and writes the total to *total.

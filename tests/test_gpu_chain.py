@@ -197,8 +197,8 @@ def test_workspace_is_left_zeroed_across_shapes():
 
 
 def test_kernel_timer_counts_every_launch(batched):
-    """Events attached to the dispatches time each of the three chain kernels,
-    and timing does not change the results."""
+    """Events attached to the dispatches time each of the chain kernels, and
+    timing does not change the results."""
     tgt = to_device_logits(batched.target, batched.dtype)
     drf = to_device_logits(batched.draft, batched.dtype)
     tok = to_device(batched.draft_tokens.astype(np.int32))
@@ -208,7 +208,7 @@ def test_kernel_timer_counts_every_launch(batched):
     with sv.KernelTimer(64) as timer:
         for _ in range(4):
             timed = sv.verify_chain(tgt, drf, tok, u, T)
-    for name in ("chain_row_stats", "chain_units", "chain_finalize"):
+    for name in ("chain_row_stats", "chain_units"):
         assert timer.launches[name] == 4
         assert 0.0 < timer.mean_us(name) < 1e5
     assert torch.equal(plain[0], timed[0].cpu()) and torch.equal(plain[1], timed[1].cpu())
