@@ -476,8 +476,12 @@ __device__ void draw_token(const ChainArgs& a, int b, const Pending& d) {
     const double before = carry + block_exclusive_scan(wu, &total);
     if (tid == 0) s_first = 0x7fffffff;
     __syncthreads();
-    if (i < a.nunit && wu > 0.0) atomicMax(&s_lastpos, i);
-    if (i < a.nunit && before + wu > target) atomicMin(&s_first, i);
+    const int lp = wave_max_int((i < a.nunit && wu > 0.0) ? i : -1);
+    const int fi = wave_min((i < a.nunit && before + wu > target) ? i : 0x7fffffff);
+    if ((tid % kWave) == 0) {
+      atomicMax(&s_lastpos, lp);
+      atomicMin(&s_first, fi);
+    }
     __syncthreads();
     if (s_first != 0x7fffffff && i == s_first) {
       s_unit = i;

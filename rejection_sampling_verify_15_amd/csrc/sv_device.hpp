@@ -181,46 +181,117 @@ __device__ inline MaxSum maxsum_combine(MaxSum a, MaxSum b, float s) {
   return {m, a.z * scale_to(a.m, m, s) + b.z * scale_to(b.m, m, s)};
 }
 
+// ---------------------------------------------------------------------------
+// cross-lane moves within a wave (DPP: register to register, no LDS round
+// trip).  Controls use the gfx9 DPP encoding; lanes whose source is outside
+// the pattern, or that a row mask leaves out, receive 0.
+// ---------------------------------------------------------------------------
+enum : int {
+  kDppQuadSwap1 = 0xB1,       // quad_perm [1,0,3,2]: lane ^ 1
+  kDppQuadSwap2 = 0x4E,       // quad_perm [2,3,0,1]: lane ^ 2
+  kDppRowMirror = 0x140,      // lane i <- 15 - i within each row of 16
+  kDppRowHalfMirror = 0x141,  // lane i <- 7 - i within each half row
+  kDppRowShr1 = 0x111,        // lane i <- i - 1 within the row
+  kDppRowShr2 = 0x112,
+  kDppRowShr4 = 0x114,
+  kDppRowShr8 = 0x118,
+  kDppRowBcast15 = 0x142,     // lane 15 of each row to the whole next row
+  kDppRowBcast31 = 0x143,     // lane 31 to rows 2 and 3
+  kDppWaveShr1 = 0x138,       // lane i <- i - 1 across the wave
+};
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ inline int lane_move(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, true);
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ inline float lane_move(float v) {
+  return __int_as_float(lane_move<CTRL, ROW_MASK>(__float_as_int(v)));
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ inline double lane_move(double v) {
+  struct Words { int lo, hi; };
+  Words w = __builtin_bit_cast(Words, v);
+  w.lo = lane_move<CTRL, ROW_MASK>(w.lo);
+  w.hi = lane_move<CTRL, ROW_MASK>(w.hi);
+  return __builtin_bit_cast(double, w);
+}
+
+__device__ inline int read_lane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ inline float read_lane(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ inline double read_lane(double v, int lane) {
+  struct Words { int lo, hi; };
+  Words w = __builtin_bit_cast(Words, v);
+  w.lo = __builtin_amdgcn_readlane(w.lo, lane);
+  w.hi = __builtin_amdgcn_readlane(w.hi, lane);
+  return __builtin_bit_cast(double, w);
+}
+
+// Reduction of one value per lane over the whole wave with an associative,
+// commutative op; every lane receives the result.  Within each row of 16 the
+// butterfly xor 1, xor 2, half mirror, mirror leaves the row's result in all
+// its lanes; the four rows are then combined from lanes 0, 16, 32, 48.
+template <typename T, typename Op>
+__device__ inline T wave_allreduce(T v, Op op) {
+  v = op(v, lane_move<kDppQuadSwap1>(v));
+  v = op(v, lane_move<kDppQuadSwap2>(v));
+  v = op(v, lane_move<kDppRowHalfMirror>(v));
+  v = op(v, lane_move<kDppRowMirror>(v));
+  return op(op(read_lane(v, 0), read_lane(v, 16)), op(read_lane(v, 32), read_lane(v, 48)));
+}
+
 template <typename T> __device__ inline T wave_sum(T v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_allreduce(v, [](T a, T b) { return a + b; });
 }
 
 __device__ inline int wave_min(int v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_allreduce(v, [](int a, int b) { return min(a, b); });
 }
 
 __device__ inline int wave_max_int(int v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_allreduce(v, [](int a, int b) { return max(a, b); });
 }
 
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_allreduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 __device__ inline ArgMax wave_argmax(ArgMax a) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    ArgMax b{__shfl_xor(a.v, o, kWave), __shfl_xor(a.i, o, kWave)};
-    a = argmax_combine(a, b);
-  }
-  return a;
+  // the pair travels as two lanes' worth of moves per step
+  auto step = [](ArgMax x, ArgMax y) { return argmax_combine(x, y); };
+  a = step(a, ArgMax{lane_move<kDppQuadSwap1>(a.v), lane_move<kDppQuadSwap1>(a.i)});
+  a = step(a, ArgMax{lane_move<kDppQuadSwap2>(a.v), lane_move<kDppQuadSwap2>(a.i)});
+  a = step(a, ArgMax{lane_move<kDppRowHalfMirror>(a.v), lane_move<kDppRowHalfMirror>(a.i)});
+  a = step(a, ArgMax{lane_move<kDppRowMirror>(a.v), lane_move<kDppRowMirror>(a.i)});
+  const ArgMax r0{read_lane(a.v, 0), read_lane(a.i, 0)}, r1{read_lane(a.v, 16), read_lane(a.i, 16)};
+  const ArgMax r2{read_lane(a.v, 32), read_lane(a.i, 32)}, r3{read_lane(a.v, 48), read_lane(a.i, 48)};
+  return step(step(r0, r1), step(r2, r3));
 }
 
 __device__ inline MaxSum wave_maxsum(MaxSum a, float s) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    MaxSum b{__shfl_xor(a.m, o, kWave), __shfl_xor(a.z, o, kWave)};
-    a = maxsum_combine(a, b, s);
-  }
-  return a;
+  auto step = [s](MaxSum x, MaxSum y) { return maxsum_combine(x, y, s); };
+  a = step(a, MaxSum{lane_move<kDppQuadSwap1>(a.m), lane_move<kDppQuadSwap1>(a.z)});
+  a = step(a, MaxSum{lane_move<kDppQuadSwap2>(a.m), lane_move<kDppQuadSwap2>(a.z)});
+  a = step(a, MaxSum{lane_move<kDppRowHalfMirror>(a.m), lane_move<kDppRowHalfMirror>(a.z)});
+  a = step(a, MaxSum{lane_move<kDppRowMirror>(a.m), lane_move<kDppRowMirror>(a.z)});
+  const MaxSum r0{read_lane(a.m, 0), read_lane(a.z, 0)}, r1{read_lane(a.m, 16), read_lane(a.z, 16)};
+  const MaxSum r2{read_lane(a.m, 32), read_lane(a.z, 32)}, r3{read_lane(a.m, 48), read_lane(a.z, 48)};
+  return step(step(r0, r1), step(r2, r3));
+}
+
+// Inclusive prefix sum over the wave (lane order): a Hillis-Steele scan in
+// each row (shifts 1, 2, 4, 8), then row 0's total into row 1 and row 2's
+// into row 3, then the total of rows 0-1 into rows 2 and 3.
+__device__ inline double wave_inclusive_sum(double v) {
+  v += lane_move<kDppRowShr1>(v);
+  v += lane_move<kDppRowShr2>(v);
+  v += lane_move<kDppRowShr4>(v);
+  v += lane_move<kDppRowShr8>(v);
+  v += lane_move<kDppRowBcast15, 0xa>(v);
+  v += lane_move<kDppRowBcast31, 0xc>(v);
+  return v;
 }
 
 // Workgroup reductions through LDS; every thread receives the result.
@@ -278,17 +349,10 @@ __device__ inline void block_sum_doubles(double (&v)[NV]) {
 // to *total.
 __device__ inline double block_exclusive_scan(double v, double* total) {
   __shared__ double sw[kWaves];
-  const int lane = threadIdx.x % kWave;
   const int w = threadIdx.x / kWave;
-  double inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double t = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += t;
-  }
-  double exc = __shfl_up(inc, 1, kWave);
-  if (lane == 0) exc = 0.0;
-  if (lane == kWave - 1) sw[w] = inc;
+  const double inc = wave_inclusive_sum(v);
+  const double exc = lane_move<kDppWaveShr1>(inc);  // lane 0 receives 0
+  if ((threadIdx.x % kWave) == kWave - 1) sw[w] = inc;
   __syncthreads();
   double before = 0.0, all = 0.0;
 #pragma unroll
@@ -342,31 +406,6 @@ __device__ inline uint32_t arrive(uint32_t* counter) {
   const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   asm volatile("" ::: "memory");
   return old;
-}
-
-// Exclusive prefix sum over the workgroup of one int per thread (thread
-// order); returns this thread's prefix and writes the total to *total.
-__device__ inline int block_exclusive_scan_int(int v, int* total) {
-  __shared__ int sw[kWaves];
-  const int lane = threadIdx.x % kWave;
-  const int w = threadIdx.x / kWave;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += t;
-  }
-  if (lane == kWave - 1) sw[w] = inc;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    if (i < w) before += sw[i];
-    all += sw[i];
-  }
-  __syncthreads();
-  *total = all;
-  return before + inc - v;
 }
 
 }  // namespace sv

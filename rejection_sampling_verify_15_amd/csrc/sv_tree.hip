@@ -233,8 +233,12 @@ __global__ __launch_bounds__(kThreads) void tree_choose(TreeArgs a) {
       run += w[i];
       if (hit == 0x7fffffff && w[i] > 0.0 && run > s_target) hit = k0 + i;
     }
-    if (hit != 0x7fffffff) atomicMin(&s_hit, hit);
-    if (last_pos >= 0) atomicMax(&s_last, last_pos);
+    hit = wave_min(hit);
+    last_pos = wave_max_int(last_pos);
+    if ((threadIdx.x % kWave) == 0) {
+      atomicMin(&s_hit, hit);
+      atomicMax(&s_last, last_pos);
+    }
     __syncthreads();
     if (threadIdx.x == 0) s_token = (s_hit != 0x7fffffff) ? s_hit : s_last;
     __syncthreads();
