@@ -209,16 +209,18 @@ SV_API int spec_probs_debug(const void* target_logits, const void* draft_logits,
  * a session are recorded in launch order.
  * ---------------------------------------------------------------------- */
 typedef enum {
-  SV_K_CHAIN_ROW_STATS = 0,   /* chain: per-(row, chunk) max / exp-sum / argmax, and the accept tests */
-  SV_K_CHAIN_UNITS = 1,       /* chain: per-unit sums and the final inverse-CDF draw */
-  SV_K_TREE_INIT = 2,
-  SV_K_TREE_NODE_PASS = 3,
-  SV_K_TREE_CHOOSE = 4,
-  SV_K_PROBS_ROW_STATS = 5,
-  SV_K_PROBS_RESIDUAL = 6,
-  SV_K_PROBS_FINALIZE = 7,
-  SV_K_WORKSPACE_CLEAR = 8,
-  SV_K_COUNT = 9
+  SV_K_CHAIN_STREAM = 0,      /* chain: per-(row, chunk) max / exp-sum / argmax over the logits */
+  SV_K_CHAIN_DRAW = 1,        /* chain: accept tests, per-unit draw sums and inverse-CDF draws */
+  SV_K_CHAIN_DECIDE = 2,      /* chain, very large shapes: accept tests in a launch of their own */
+  SV_K_CHAIN_UNITS = 3,       /* chain, very large shapes: draw sums and draws in a launch of their own */
+  SV_K_TREE_INIT = 4,
+  SV_K_TREE_NODE_PASS = 5,
+  SV_K_TREE_CHOOSE = 6,
+  SV_K_PROBS_ROW_STATS = 7,
+  SV_K_PROBS_RESIDUAL = 8,
+  SV_K_PROBS_FINALIZE = 9,
+  SV_K_WORKSPACE_CLEAR = 10,
+  SV_K_COUNT = 11
 } sv_kernel;
 
 /* Name of a kernel id (static storage; "unknown" outside [0, SV_K_COUNT)). */

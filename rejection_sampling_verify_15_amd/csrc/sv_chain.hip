@@ -32,6 +32,8 @@
 // sums merged in fp64; the final draw uses fp64 exponentials and fp64
 // normalisers summed in launch 2, so the inverse CDF matches an fp64
 // reference except where u lies within a few ulps of a CDF step.
+#include <stdlib.h>
+
 #include "sv_device.hpp"
 #include "sv_host.hpp"
 
@@ -64,14 +66,24 @@ struct Pending {
   double zt, zd;  // their fp64-merged pass-1 normalisers
 };
 
+// A drawing request's Pending record travels to its units as kWireWords
+// 64-bit words, each holding one 32-bit word of the record and, above it, the
+// record's `valid` value.  The decider stores all words at once with
+// device-coherent stores, in no particular order; a unit takes the record once
+// every word it reads carries a nonzero mark.
+constexpr int kWireWords = sizeof(Pending) / 4;
+struct PendingWire {
+  uint64_t w[kWireWords];
+};
+
 static_assert(sizeof(RowPartial) == 8, "row partials are one 64-bit word");
 static_assert(sizeof(UnitRec) % 8 == 0 && sizeof(Pending) % 8 == 0, "records are cleared in 64-bit words");
 
 enum : int32_t { kModeResidual = 1, kModeBonus = 2 };
+enum : int32_t { kPendingDraw = 1, kPendingNone = 2 };  // Pending::valid once published
 
 constexpr int kCounterStride = 32;  // uint32 words per request: one 128-byte line
-constexpr int kRowCounter = 0;      // row-statistics workgroups arrived (launch 1)
-constexpr int kUnitCounter = 16;    // draw units arrived (launch 2)
+constexpr int kUnitCounter = 0;     // draw units of the request that have counted in
 
 struct ChainArgs {
   const void* target;
@@ -84,7 +96,7 @@ struct ChainArgs {
   int32_t* out_n;
   RowPartial* partials;  // [B][2*gamma+1][nchunk]
   float* gathers;        // [B][2*gamma+1] logit of the draft token in each row
-  Pending* pending;      // [B]
+  PendingWire* pending;  // [B]
   UnitRec* units;        // [B][nunit]
   uint32_t* counters;    // [B][kCounterStride]
 };
@@ -103,6 +115,11 @@ __device__ inline double exp_scaled(float x, float m, double l2t) {
   return exp2_nonpos((static_cast<double>(x) - static_cast<double>(m)) * l2t);
 }
 
+// The same with the LDS table of the calling workgroup.
+__device__ inline double exp_scaled(float x, float m, double l2t, const Exp2Table& tab) {
+  return exp2_tab((static_cast<double>(x) - static_cast<double>(m)) * l2t, tab);
+}
+
 // Request classes: 0 samples with its draft rows or has gamma == 0 (it has a
 // final draw), 1 is greedy or cannot sample (target rows only), 2 has an
 // invalid temperature.
@@ -117,13 +134,58 @@ __device__ inline int needed_rows(const ChainArgs& a, float T) {
   return (T > 0.0f && a.draft != nullptr) ? 2 * a.gamma + 1 : a.gamma + 1;
 }
 
-__device__ inline uint64_t pack_partial(float m, int32_t v) {
-  return static_cast<uint64_t>(__float_as_uint(m)) | (static_cast<uint64_t>(static_cast<uint32_t>(v)) << 32);
+
+// Thread t < kWireWords of the calling workgroup stores word t.
+__device__ inline void publish_pending(PendingWire* wire, const Pending& d) {
+  const int t = threadIdx.x;
+  if (t < kWireWords) {
+    struct Dwords { uint32_t v[kWireWords]; };
+    const Dwords src = __builtin_bit_cast(Dwords, d);
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < kWireWords; ++i)
+      if (t == i) v = src.v[i];  // constant indices keep the record in registers
+    const uint64_t mark = static_cast<uint64_t>(static_cast<uint32_t>(d.valid)) << 32;
+    store_coherent(&wire->w[t], mark | v);
+  }
 }
 
-__device__ inline RowPartial load_partial(const RowPartial* p) {
-  const uint64_t w = load_coherent(reinterpret_cast<const uint64_t*>(p));
-  return RowPartial{__uint_as_float(static_cast<uint32_t>(w)), static_cast<int32_t>(w >> 32)};
+// Upper bound on the polls of a unit waiting for its request's decision
+// (about 2 s); the decision is always made by workgroups dispatched before the
+// waiting one, so the bound only guards against a broken dispatch order.
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+// Waits (thread 0 polls, the workgroup then reads the copy in LDS) until the
+// decision of request b is published and returns it; valid = 0 means the
+// wait gave up.
+__device__ Pending wait_pending(const ChainArgs& a, int b) {
+  __shared__ Pending s_p;
+  if (threadIdx.x == 0) {
+    const PendingWire* wire = a.pending + b;
+    struct Dwords { uint32_t v[kWireWords]; };
+    Dwords got{};
+    bool whole = false;
+    for (uint32_t spin = 0; !whole && spin < kSpinLimit; ++spin) {
+      if ((load_coherent(&wire->w[0]) >> 32) != 0) {
+        asm volatile("" ::: "memory");
+        whole = true;
+#pragma unroll
+        for (int i = 0; i < kWireWords; ++i) {
+          const uint64_t w = load_coherent(&wire->w[i]);
+          whole = whole && (w >> 32) != 0;
+          got.v[i] = static_cast<uint32_t>(w);
+        }
+      }
+      if (!whole) __builtin_amdgcn_s_sleep(8);
+    }
+    Pending d = __builtin_bit_cast(Pending, got);
+    if (!whole) d.valid = 0;
+    s_p = d;
+  }
+  __syncthreads();
+  const Pending d = s_p;
+  __syncthreads();
+  return d;
 }
 
 __device__ void write_invalid(const ChainArgs& a, int b) {
@@ -133,18 +195,18 @@ __device__ void write_invalid(const ChainArgs& a, int b) {
 }
 
 // ---------------------------------------------------------------------------
-// the decision of request b, made by the last row-statistics workgroup
+// the decision of request b
 // ---------------------------------------------------------------------------
-// Merges the request's chunk partials (fp64, online rescaling), tests the
-// drafts in order, writes tokens [0, n] (all but a sampling request's slot
-// n) and the count, records a sampling request's pending draw, and zeroes the
-// partials, gathered logits and counter.
+// Merges the request's chunk partials in fp64: one thread per group of chunks
+// of a row takes the group max, then rescales every chunk sum to it (all
+// exponentials independent of each other); one thread per row combines the
+// groups the same way.  Then the drafts are tested in order; tokens [0, n]
+// (all but a sampling request's slot n) and the count are written, a
+// drawing request's outcome is published to its units, and the partials and
+// gathered logits return to zero.
 template <int DT>
-__device__ void decide_and_publish(const ChainArgs& a, int b) {
+__device__ void decide_and_publish(const ChainArgs& a, int b, const Exp2Table& tab) {
   constexpr int kMaxRows = 2 * SV_MAX_GAMMA + 1;
-  // one workgroup per request does this while others stream: let its waves
-  // issue first on their SIMDs
-  __builtin_amdgcn_s_setprio(3);
   __shared__ float s_gm[kThreads];
   __shared__ double s_gz[kThreads];
   __shared__ int32_t s_garg[kThreads];
@@ -154,6 +216,7 @@ __device__ void decide_and_publish(const ChainArgs& a, int b) {
   __shared__ float s_xt[SV_MAX_GAMMA], s_xd[SV_MAX_GAMMA];
   __shared__ int32_t s_ok[SV_MAX_GAMMA];
   __shared__ int32_t s_n;
+  __shared__ Pending s_pend;
   const int tid = threadIdx.x;
   const int G = a.gamma;
   const int R = 2 * G + 1;
@@ -161,7 +224,6 @@ __device__ void decide_and_publish(const ChainArgs& a, int b) {
   const bool sampling = T > 0.0f;
   const double l2t = sampling ? kLog2e / static_cast<double>(T) : 0.0;
   const int nrows = needed_rows(a, T);
-  const uint32_t* gathers = reinterpret_cast<const uint32_t*>(a.gathers) + static_cast<size_t>(b) * R;
   // one round of loads: the chunk partials (in groups of chunks, one group per
   // thread), the draft tokens, their gathered logits and the uniforms
   const int gpr = max(1, min((a.nchunk + 3) / 4, kThreads / nrows));  // groups per row
@@ -171,8 +233,8 @@ __device__ void decide_and_publish(const ChainArgs& a, int b) {
     const int32_t x = a.tokens[static_cast<size_t>(b) * G + tid];
     bad |= (x < 0 || x >= a.V);
     if (sampling && a.draft != nullptr) {
-      s_xt[tid] = __uint_as_float(load_coherent(gathers + tid));
-      s_xd[tid] = __uint_as_float(load_coherent(gathers + G + 1 + tid));
+      s_xt[tid] = a.gathers[static_cast<size_t>(b) * R + tid];
+      s_xd[tid] = a.gathers[static_cast<size_t>(b) * R + G + 1 + tid];
     }
   }
   if (sampling && tid <= G) {
@@ -192,18 +254,24 @@ __device__ void decide_and_publish(const ChainArgs& a, int b) {
     for (int c0 = cb; c0 < ce; c0 += 4) {
       RowPartial w[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = load_partial(p + min(c0 + i, ce - 1));
+      for (int i = 0; i < 4; ++i) w[i] = p[min(c0 + i, ce - 1)];
+      if (!sampling) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (c0 + i >= ce) continue;
-        if (!sampling) {
-          best = argmax_combine(best, ArgMax{w[i].m, w[i].v});
-        } else if (w[i].m != -INFINITY) {
-          if (w[i].m > m) {
-            if (m != -INFINITY) z *= exp_scaled(m, w[i].m, l2t);
-            m = w[i].m;
-          }
-          z += static_cast<double>(__int_as_float(w[i].v)) * exp_scaled(w[i].m, m, l2t);
+        for (int i = 0; i < 4; ++i)
+          if (c0 + i < ce) best = argmax_combine(best, ArgMax{w[i].m, w[i].v});
+      } else {
+        float m4 = m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (c0 + i < ce) m4 = fmaxf(m4, w[i].m);
+        if (m4 != -INFINITY) {
+          double z4 = (m != -INFINITY) ? z * exp_scaled(m, m4, l2t, tab) : 0.0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (c0 + i < ce && w[i].m != -INFINITY)
+              z4 += static_cast<double>(__int_as_float(w[i].v)) * exp_scaled(w[i].m, m4, l2t, tab);
+          m = m4;
+          z = z4;
         }
       }
     }
@@ -231,7 +299,7 @@ __device__ void decide_and_publish(const ChainArgs& a, int b) {
         double z = 0.0;
         for (int g = 0; g < gpr; ++g) {
           const float gm = s_gm[tid * gpr + g];
-          if (gm != -INFINITY) z += s_gz[tid * gpr + g] * exp_scaled(gm, m, l2t);
+          if (gm != -INFINITY) z += s_gz[tid * gpr + g] * exp_scaled(gm, m, l2t, tab);
         }
         s_m[tid] = m;
         s_z[tid] = z;
@@ -244,8 +312,8 @@ __device__ void decide_and_publish(const ChainArgs& a, int b) {
       if (!sampling) {
         ok = (x == s_arg[tid]);
       } else {
-        const double p = exp_scaled(s_xt[tid], s_m[tid], l2t) / s_z[tid];
-        const double q = exp_scaled(s_xd[tid], s_m[G + 1 + tid], l2t) / s_z[G + 1 + tid];
+        const double p = exp_scaled(s_xt[tid], s_m[tid], l2t, tab) / s_z[tid];
+        const double q = exp_scaled(s_xd[tid], s_m[G + 1 + tid], l2t, tab) / s_z[G + 1 + tid];
         const double tau = (q <= p) ? 1.0 : p / q;
         const double u = static_cast<double>(a.uniforms[static_cast<size_t>(b) * (G + 1) + tid]);
         ok = (u <= tau);
@@ -259,7 +327,7 @@ __device__ void decide_and_publish(const ChainArgs& a, int b) {
       s_n = n;
       if (sampling) {
         Pending d{};
-        d.valid = 1;
+        d.valid = kPendingDraw;
         d.n = n;
         d.mode = n < G ? kModeResidual : kModeBonus;
         d.u = a.uniforms[static_cast<size_t>(b) * (G + 1) + G];
@@ -270,11 +338,19 @@ __device__ void decide_and_publish(const ChainArgs& a, int b) {
           d.md = s_m[G + 1 + n];
           d.zd = s_z[G + 1 + n];
         }
-        a.pending[b] = d;
+        s_pend = d;
       }
     }
-    __syncthreads();
   }
+  if (tid == 0 && bad) {
+    Pending d{};
+    d.valid = kPendingNone;
+    s_pend = d;
+  }
+  __syncthreads();
+  // a request with draw units hears the outcome in every case: the draw, or
+  // that there is none
+  if (request_class(a, T) == 0) publish_pending(a.pending + b, s_pend);
   // outputs: tokens [0, n), greedy: the argmax at slot n, the rest -1; slot n
   // of a sampling request is filled by its draw
   int32_t* out = a.out_tokens + static_cast<size_t>(b) * (G + 1);
@@ -293,123 +369,259 @@ __device__ void decide_and_publish(const ChainArgs& a, int b) {
   unsigned long long* pz = reinterpret_cast<unsigned long long*>(a.partials + static_cast<size_t>(b) * R * a.nchunk);
   for (int i = tid; i < nrows * a.nchunk; i += kThreads) pz[i] = 0ull;
   if (tid < R) a.gathers[static_cast<size_t>(b) * R + tid] = 0.0f;
-  if (tid == 0) store_coherent(a.counters + static_cast<size_t>(b) * kCounterStride + kRowCounter, 0u);
-  __builtin_amdgcn_s_setprio(0);
 }
 
 // ---------------------------------------------------------------------------
-// launch 1: row statistics
+// launch 1: streaming row statistics
 // ---------------------------------------------------------------------------
-template <int DT, bool VEC>
-__device__ void row_stats_item(const ChainArgs& a, long long item) {
-  __shared__ float s_wm[kWaves];
-  __shared__ float s_gather;
-  __shared__ int s_last;
-  const int G = a.gamma;
-  const int R = 2 * G + 1;
-  const int per_req = R * a.nchunk;
-  const int b = static_cast<int>(item / per_req);
+// Persistent workgroups (as many as fit on the GPU) stride over the items
+// (request, row, chunk) in request-major order.  Each keeps two items in
+// flight: the loads of the next item are issued before the current one is
+// reduced, and the reductions synchronise through LDS only, so the prefetch
+// stays outstanding.  Per item: the chunk max and, for sampling rows, the fp32
+// sum of exp2((x - max) * log2e / T); for greedy rows the argmax (lowest
+// index); the chunk holding a row's draft token also stores that logit.  Rows
+// that no decision needs (draft rows of greedy requests, requests with an
+// invalid temperature) are skipped.
+
+// Row chunk of one streaming item, and so of one row partial.
+constexpr int kRowChunk = 4096;
+__host__ __device__ inline int row_chunks(int V) { return (V + kRowChunk - 1) / kRowChunk; }
+
+// Which rows of each request are streamed, 2 bits per request, kept in LDS.
+constexpr int kMaxStreamBatch = SV_MAX_BATCH;
+enum : uint32_t { kStreamTarget = 1u, kStreamDraft = 2u };
+
+struct StreamFlags {
+  uint32_t w[kMaxStreamBatch / 16];
+  __device__ inline uint32_t get(int b) const { return (w[b >> 4] >> ((b & 15) * 2)) & 3u; }
+};
+
+template <int DT, bool VEC, int NT>
+struct StreamItem {
+  using Raw = RawSlice<DT, VEC, kRowChunk / (NT * (VEC ? Elem<DT>::kVec : 1)), NT>;
+  Raw raw;
+  float t;      // temperature of the request
+  int32_t tok;  // draft token of the row (sampling rows below gamma), else -1
+};
+
+// Item order: request-major, rows (target 0..gamma, then draft), then chunks.
+struct RowItem {
+  int b, k, c;
+};
+__device__ inline RowItem decode_item(const ChainArgs& a, long long item) {
+  const int per_req = (2 * a.gamma + 1) * a.nchunk;
   const int rem = static_cast<int>(item % per_req);
-  const int k = rem / a.nchunk;  // target rows 0..G, then draft rows
-  const int c = rem % a.nchunk;
-  const float T = a.temperature[b];
-  const int cls = request_class(a, T);
-  if (cls == 2) {  // nothing is read for this request
-    if (k == 0 && c == 0) write_invalid(a, b);
-    return;
-  }
-  const bool sampling = T > 0.0f;
-  if (k > G && !(sampling && a.draft != nullptr)) return;  // draft rows are read only when sampling
-  const int pos = k <= G ? k : k - G - 1;                    // draft position of this row
+  return RowItem{static_cast<int>(item / per_req), rem / a.nchunk, rem % a.nchunk};
+}
+
+__device__ inline bool stream_needed(const ChainArgs& a, const StreamFlags& fl, long long item) {
+  const RowItem r = decode_item(a, item);
+  const int b = r.b, k = r.k;
+  const uint32_t f = fl.get(b);
+  return k <= a.gamma ? (f & kStreamTarget) != 0 : (f & kStreamDraft) != 0;
+}
+
+__device__ inline long long stream_next(const ChainArgs& a, const StreamFlags& fl, long long item, long long items) {
+  while (item < items && !stream_needed(a, fl, item)) item += gridDim.x;
+  return item;
+}
+
+template <int DT, bool VEC, int NT>
+__device__ inline void stream_issue(const ChainArgs& a, long long item, StreamItem<DT, VEC, NT>& it) {
+  const int G = a.gamma;
+  const RowItem r = decode_item(a, item);
+  const int b = r.b, k = r.k, c = r.c;
+  const int pos = k <= G ? k : k - G - 1;
   const void* row = (k <= G) ? row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + k, a.V)
                              : row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + pos, a.V);
-  const int c0 = c * kChunk;
-  const int c1 = min(a.V, c0 + kChunk);
-  const int32_t tok = (sampling && pos < G) ? a.tokens[static_cast<size_t>(b) * G + pos] : -1;
-  const bool has_gather = tok >= c0 && tok < c1;
-  Slice<DT, VEC> s;
-  s.load(row, c0, c1);
-  if (has_gather) {
-#pragma unroll
-    for (int j = 0; j < s.kItems; ++j)
-#pragma unroll
-      for (int e = 0; e < s.kPer; ++e)
-        if (s.index(c0, j, e) == tok) s_gather = s.x[j][e];
-  }
+  const int c0 = c * kRowChunk;
+  it.raw.load(row, c0, min(a.V, c0 + kRowChunk));
+  it.t = a.temperature[b];
+  it.tok = pos < G ? a.tokens[static_cast<size_t>(b) * G + pos] : -1;
+}
+
+// NT == kWave: one wave per workgroup, reductions within the wave only;
+// otherwise the waves combine through LDS.
+template <int DT, bool VEC, int NT>
+__device__ inline void stream_reduce(const ChainArgs& a, long long item, const StreamItem<DT, VEC, NT>& it) {
+  using Raw = typename StreamItem<DT, VEC, NT>::Raw;
+  __shared__ float s_a[kWaves];
+  __shared__ int s_i[kWaves];
+  const int G = a.gamma;
+  const int R = 2 * G + 1;
+  const RowItem r = decode_item(a, item);
+  const int b = r.b, k = r.k, c = r.c;
+  const int c0 = c * kRowChunk;
+  const int c1 = min(a.V, c0 + kRowChunk);
+  const bool sampling = it.t > 0.0f;
+  auto val = [&](int j, int e) -> float { return it.raw.at(j, e); };
   float m = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < s.kItems; ++j)
+  for (int j = 0; j < Raw::kItems; ++j)
 #pragma unroll
-    for (int e = 0; e < s.kPer; ++e) m = fmaxf(m, s.x[j][e]);
+    for (int e = 0; e < Raw::kPer; ++e) m = fmaxf(m, val(j, e));
+  const int w = threadIdx.x / kWave;
+  const bool lane0 = (threadIdx.x % kWave) == 0;
   float out_m;
   int32_t out_v;
   if (!sampling) {
-    // chunk max first; only threads holding it look for its lowest index
+    // chunk max first; only the lanes holding it look for its lowest index
     const float wm = wave_max(m);
-    if ((threadIdx.x % kWave) == 0) s_wm[threadIdx.x / kWave] = wm;
-    __syncthreads();
-    float bm = s_wm[0];
+    float bm = wm;
+    if constexpr (NT != kWave) {
+      if (lane0) s_a[w] = wm;
+      lds_barrier();
+      bm = s_a[0];
 #pragma unroll
-    for (int i = 1; i < kWaves; ++i) bm = fmaxf(bm, s_wm[i]);
+      for (int i = 1; i < NT / kWave; ++i) bm = fmaxf(bm, s_a[i]);
+    }
     int idx = 0x7fffffff;
     if (m == bm) {
 #pragma unroll
-      for (int j = s.kItems - 1; j >= 0; --j)
+      for (int j = Raw::kItems - 1; j >= 0; --j)
 #pragma unroll
-        for (int e = s.kPer - 1; e >= 0; --e) {
-          const int kk = s.index(c0, j, e);
-          if (s.x[j][e] == bm && kk < c1) idx = kk;
+        for (int e = Raw::kPer - 1; e >= 0; --e) {
+          const int kk = Raw::index(c0, j, e);
+          if (kk < c1 && it.raw.at(j, e) == bm) idx = kk;
         }
     }
-    const ArgMax best = block_argmax(ArgMax{bm, idx});
+    int bi = wave_min(idx);
+    if constexpr (NT != kWave) {
+      lds_barrier();  // s_a has been read
+      if (lane0) s_i[w] = bi;
+      lds_barrier();
+      bi = s_i[0];
+#pragma unroll
+      for (int i = 1; i < NT / kWave; ++i) bi = min(bi, s_i[i]);
+    }
     out_m = bm;
-    out_v = best.i;
+    out_v = bi;
   } else {
-    const float sc = 1.4426950408889634f / T;
+    const float sc = 1.4426950408889634f / it.t;
     float z = 0.0f;
     if (m != -INFINITY) {
       const float msc = m * sc;
 #pragma unroll
-      for (int j = 0; j < s.kItems; ++j)
+      for (int j = 0; j < Raw::kItems; ++j)
 #pragma unroll
-        for (int e = 0; e < s.kPer; ++e) z += __builtin_amdgcn_exp2f(__builtin_fmaf(s.x[j][e], sc, -msc));
+        for (int e = 0; e < Raw::kPer; ++e) z += __builtin_amdgcn_exp2f(__builtin_fmaf(val(j, e), sc, -msc));
     }
-    const MaxSum ms = block_maxsum(MaxSum{m, z}, sc);
-    out_m = ms.m;
-    out_v = __float_as_int(ms.z);
+    MaxSum r = wave_maxsum(MaxSum{m, z}, sc);
+    if constexpr (NT != kWave) {
+      if (lane0) {
+        s_a[w] = r.m;
+        s_i[w] = __float_as_int(r.z);
+      }
+      lds_barrier();
+      r = MaxSum{s_a[0], __int_as_float(s_i[0])};
+#pragma unroll
+      for (int i = 1; i < NT / kWave; ++i) r = maxsum_combine(r, MaxSum{s_a[i], __int_as_float(s_i[i])}, sc);
+    }
+    out_m = r.m;
+    out_v = __float_as_int(r.z);
   }
-  // hand the partial (and the gathered logit) over; the last workgroup of the
-  // request decides it
+  if (it.tok >= c0 && it.tok < c1) {  // the lane holding the draft token stores its logit
+#pragma unroll
+    for (int j = 0; j < Raw::kItems; ++j)
+#pragma unroll
+      for (int e = 0; e < Raw::kPer; ++e)
+        if (Raw::index(c0, j, e) == it.tok) a.gathers[static_cast<size_t>(b) * R + k] = it.raw.at(j, e);
+  }
   if (threadIdx.x == 0) {
-    store_coherent(reinterpret_cast<uint64_t*>(a.partials + (static_cast<size_t>(b) * R + k) * a.nchunk + c),
-                   pack_partial(out_m, out_v));
-    if (has_gather)
-      store_coherent(reinterpret_cast<uint32_t*>(a.gathers) + static_cast<size_t>(b) * R + k,
-                     __float_as_uint(s_gather));
-    const uint32_t total = static_cast<uint32_t>(needed_rows(a, T) * a.nchunk);
-    s_last = arrive(a.counters + static_cast<size_t>(b) * kCounterStride + kRowCounter) == total - 1;
+    RowPartial p;
+    p.m = out_m;
+    p.v = out_v;
+    a.partials[(static_cast<size_t>(b) * R + k) * a.nchunk + c] = p;
   }
-  __syncthreads();
-  if (s_last) decide_and_publish<DT>(a, b);
-  __syncthreads();  // LDS is reused by the next item
+  if constexpr (NT != kWave) lds_barrier();  // s_a / s_i are reused by the next item
 }
 
-// LOOP: more items than workgroups, which stride over them.  Without the loop
-// nothing is hoisted across items, which keeps the register count (and so the
-// occupancy of the streaming part) where a single item needs it.
-template <int DT, bool VEC, bool LOOP>
-__global__ __launch_bounds__(kThreads) void chain_row_stats(ChainArgs a) {
-  if constexpr (LOOP) {
-    const long long items = static_cast<long long>(a.B) * (2 * a.gamma + 1) * a.nchunk;
-    for (long long item = blockIdx.x; item < items; item += gridDim.x) row_stats_item<DT, VEC>(a, item);
+// The last chunk of a row: words past the row's end (loaded from a clamped
+// address) become -inf before the reduction.  Vector groups lie wholly inside
+// or outside the row (V is a multiple of the vector width on that path).
+template <int DT, bool VEC, int NT>
+__device__ inline void stream_reduce_any(const ChainArgs& a, long long item, StreamItem<DT, VEC, NT>& it) {
+  using Raw = typename StreamItem<DT, VEC, NT>::Raw;
+  const int c0 = decode_item(a, item).c * kRowChunk;
+  const int c1 = min(a.V, c0 + kRowChunk);
+  if (c1 - c0 != Raw::kSpan) {
+    constexpr uint32_t kNegInf = DT == 0 ? (VEC ? 0xff80ff80u : 0xff80u) : 0xff800000u;
+#pragma unroll
+    for (int j = 0; j < Raw::kItems; ++j)
+      if (Raw::index(c0, j, 0) >= c1) {
+#pragma unroll
+        for (int q = 0; q < (VEC ? 4 : 1); ++q) it.raw.w[j][q] = kNegInf;
+      }
+  }
+  stream_reduce<DT, VEC, NT>(a, item, it);
+}
+
+// One item per workgroup of one wave (no prefetch, no barriers): the grid
+// covers every item.
+constexpr int kOnceThreads = kWave;
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kOnceThreads) void chain_stream_once(ChainArgs a) {
+  constexpr int NT = kOnceThreads;
+  const long long item = blockIdx.x;
+  const RowItem r = decode_item(a, item);
+  const int b = r.b, k = r.k;
+  StreamItem<DT, VEC, NT> x;
+  if (k <= a.gamma) {
+    stream_issue<DT, VEC, NT>(a, item, x);  // target rows: the loads do not wait for the temperature
+    if (!temp_ok(x.t)) return;
   } else {
-    row_stats_item<DT, VEC>(a, blockIdx.x);
+    const float T = a.temperature[b];
+    if (!(temp_ok(T) && T > 0.0f && a.draft != nullptr)) return;
+    stream_issue<DT, VEC, NT>(a, item, x);
+  }
+  stream_reduce_any<DT, VEC, NT>(a, item, x);
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void chain_stream(ChainArgs a) {
+  __shared__ StreamFlags s_flags;
+  for (int i = threadIdx.x; i < (a.B + 15) / 16; i += kThreads) {
+    uint32_t word = 0;
+    for (int q = 0; q < 16; ++q) {
+      const int b = i * 16 + q;
+      if (b >= a.B) break;
+      const float T = a.temperature[b];
+      uint32_t f = 0;
+      if (temp_ok(T)) f = kStreamTarget | ((T > 0.0f && a.draft != nullptr) ? kStreamDraft : 0u);
+      word |= f << (q * 2);
+    }
+    s_flags.w[i] = word;
+  }
+  __syncthreads();
+  const long long items = static_cast<long long>(a.B) * (2 * a.gamma + 1) * a.nchunk;
+  long long ia = stream_next(a, s_flags, blockIdx.x, items);
+  if (ia >= items) return;
+  StreamItem<DT, VEC, kThreads> x, y;
+  stream_issue<DT, VEC, kThreads>(a, ia, x);
+  for (;;) {
+    const long long ib = stream_next(a, s_flags, ia + gridDim.x, items);
+    if (ib < items) stream_issue<DT, VEC, kThreads>(a, ib, y);
+    stream_reduce_any<DT, VEC, kThreads>(a, ia, x);
+    if (ib >= items) break;
+    const long long ic = stream_next(a, s_flags, ib + gridDim.x, items);
+    if (ic < items) stream_issue<DT, VEC, kThreads>(a, ic, x);
+    stream_reduce_any<DT, VEC, kThreads>(a, ib, y);
+    if (ic >= items) break;
+    ia = ic;
   }
 }
 
 // ---------------------------------------------------------------------------
 // launch 2: draw units, and the draw by the last unit of each request
 // ---------------------------------------------------------------------------
+// A draw unit is kUnitItems vector groups per thread: 2048 * kUnitItems logits
+// on the bf16 vector path.
+constexpr int kUnitItems = 2;
+template <int DT, bool VEC>
+using UnitSlice = Slice<DT, VEC, kUnitItems>;
+
 // Weight of a unit in the final draw (rzt, rzd: reciprocal normalisers).
 __device__ inline double unit_weight(double pos_t, double pos_d, double all_t, bool residual,
                                      double rzt, double rzd) {
@@ -423,8 +635,8 @@ __device__ inline double unit_field(const UnitRec* r, int f) { return load_coher
 // unit where the running weight first exceeds u * W, then an fp64 block scan
 // of that unit's logits for the token.
 template <int DT, bool VEC>
-__device__ void draw_token(const ChainArgs& a, int b, const Pending& d) {
-  using S = Slice<DT, VEC, 1>;
+__device__ void draw_token(const ChainArgs& a, int b, const Pending& d, const Exp2Table& tab) {
+  using S = UnitSlice<DT, VEC>;
   __shared__ int s_unit, s_first, s_lastpos, s_hit, s_lasttok;
   __shared__ double s_before;
   // the last unit of a request draws while other units still compute: let
@@ -499,39 +711,45 @@ __device__ void draw_token(const ChainArgs& a, int b, const Pending& d) {
     if (tid == 0) { s_unit = lp; s_before = bsum[0]; }
     __syncthreads();
   }
-  // 3) fp64 block scan of the crossing unit: thread t owns kPer logits
+  // 3) fp64 block scans of the crossing unit, one per vector group (group j
+  //    of all threads precedes group j + 1); thread t owns kPer logits of each
   const int c0 = s_unit * S::kSpan;
   const int c1 = min(a.V, c0 + S::kSpan);
   const double l2t = kLog2e / static_cast<double>(d.t);
   const int trow = d.mode == kModeResidual ? d.n : G;
   S st;
   st.load(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + trow, a.V), c0, c1);
-  double wk[S::kPer];
-  if (residual) {
-    S sd;
-    sd.load(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + d.n, a.V), c0, c1);
-#pragma unroll
-    for (int e = 0; e < S::kPer; ++e)
-      wk[e] = fmax(0.0, exp_scaled(st.x[0][e], d.mt, l2t) * rzt - exp_scaled(sd.x[0][e], d.md, l2t) * rzd);
-  } else {
-#pragma unroll
-    for (int e = 0; e < S::kPer; ++e) wk[e] = exp_scaled(st.x[0][e], d.mt, l2t);
-  }
-  double own = 0.0;
-  int last_pos = -1;
-#pragma unroll
-  for (int e = 0; e < S::kPer; ++e) {
-    own += wk[e];
-    if (wk[e] > 0.0) last_pos = S::index(c0, 0, e);
-  }
+  S sd;
+  if (residual) sd.load(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + d.n, a.V), c0, c1);
   if (tid == 0) { s_hit = 0x7fffffff; s_lasttok = -1; }
-  double total;
-  double run = s_before + block_exclusive_scan(own, &total);
   int hit = 0x7fffffff;
+  int last_pos = -1;
+  double run0 = s_before;
 #pragma unroll
-  for (int e = 0; e < S::kPer; ++e) {
-    run += wk[e];
-    if (hit == 0x7fffffff && wk[e] > 0.0 && run > target) hit = S::index(c0, 0, e);
+  for (int j = 0; j < S::kItems; ++j) {
+    double wk[S::kPer];
+    if (residual) {
+#pragma unroll
+      for (int e = 0; e < S::kPer; ++e)
+        wk[e] = fmax(0.0, exp_scaled(st.x[j][e], d.mt, l2t, tab) * rzt - exp_scaled(sd.x[j][e], d.md, l2t, tab) * rzd);
+    } else {
+#pragma unroll
+      for (int e = 0; e < S::kPer; ++e) wk[e] = exp_scaled(st.x[j][e], d.mt, l2t, tab);
+    }
+    double own = 0.0;
+#pragma unroll
+    for (int e = 0; e < S::kPer; ++e) {
+      own += wk[e];
+      if (wk[e] > 0.0) last_pos = S::index(c0, j, e);
+    }
+    double total;
+    double run = run0 + block_exclusive_scan(own, &total);
+    run0 += total;
+#pragma unroll
+    for (int e = 0; e < S::kPer; ++e) {
+      run += wk[e];
+      if (hit == 0x7fffffff && wk[e] > 0.0 && run > target) hit = S::index(c0, j, e);
+    }
   }
   hit = wave_min(hit);
   last_pos = wave_max_int(last_pos);
@@ -575,14 +793,92 @@ __device__ int nth_drawing_request(const ChainArgs& a, int p) {
   return s_b;
 }
 
+// Unit `unit` of request b (a class-0 request): waits for the decision, then
+// adds its share of the final draw and counts itself in; the last unit of the
+// request draws and returns the request's draw records to zero.
 template <int DT, bool VEC>
-__device__ void unit_item(const ChainArgs& a, long long item) {
-  using S = Slice<DT, VEC, 1>;
+__device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& tab) {
+  using S = UnitSlice<DT, VEC>;
   __shared__ double s_w[4][kWaves];
   __shared__ int s_last;
-  __shared__ Pending s_pending;
-  const int unit = static_cast<int>(item % a.nunit);
   const int G = a.gamma;
+  const Pending d = wait_pending(a, b);
+  if (d.valid == 0 && threadIdx.x == 0) a.out_n[b] = -1;  // gave up waiting
+  const bool draw = d.valid == kPendingDraw;
+  UnitRec* rec = a.units + static_cast<size_t>(b) * a.nunit + unit;
+  if (draw) {
+    const double l2t = kLog2e / static_cast<double>(d.t);
+    const int c0 = unit * S::kSpan;
+    const int c1 = min(a.V, c0 + S::kSpan);
+    const bool residual = d.mode == kModeResidual;
+    const int trow = residual ? d.n : G;
+    S st;
+    st.load(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + trow, a.V), c0, c1);
+    double pos_t = 0.0, pos_d = 0.0, all_t = 0.0, all_d = 0.0;
+    if (residual) {
+      S sd;
+      sd.load(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + d.n, a.V), c0, c1);
+#pragma unroll
+      for (int j = 0; j < S::kItems; ++j)
+#pragma unroll
+        for (int e = 0; e < S::kPer; ++e) {
+          const double et = exp_scaled(st.x[j][e], d.mt, l2t, tab);
+          const double ed = exp_scaled(sd.x[j][e], d.md, l2t, tab);
+          all_t += et;
+          all_d += ed;
+          if (et * d.zd > ed * d.zt) {  // p > q under the pass-1 normalisers
+            pos_t += et;
+            pos_d += ed;
+          }
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < S::kItems; ++j)
+#pragma unroll
+        for (int e = 0; e < S::kPer; ++e) all_t += exp_scaled(st.x[j][e], d.mt, l2t, tab);
+    }
+    pos_t = wave_sum(pos_t);
+    pos_d = wave_sum(pos_d);
+    all_t = wave_sum(all_t);
+    all_d = wave_sum(all_d);
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x % kWave) == 0) {
+      s_w[kUnitPosT][w] = pos_t;
+      s_w[kUnitPosD][w] = pos_d;
+      s_w[kUnitAllT][w] = all_t;
+      s_w[kUnitAllD][w] = all_d;
+    }
+    __syncthreads();
+    // wave 0 hands the record over (one field per lane)
+    if (threadIdx.x < kUnitFields) {
+      double v = 0.0;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) v += s_w[threadIdx.x][i];
+      store_coherent_f64(&rec->f[threadIdx.x], v);
+    }
+  }
+  if (threadIdx.x == 0)
+    s_last = arrive(a.counters + static_cast<size_t>(b) * kCounterStride + kUnitCounter) ==
+             static_cast<uint32_t>(a.nunit - 1);
+  __syncthreads();
+  if (s_last) {
+    if (draw) {
+      draw_token<DT, VEC>(a, b, d, tab);
+      unsigned long long* wz = reinterpret_cast<unsigned long long*>(a.units + static_cast<size_t>(b) * a.nunit);
+      const int nw = a.nunit * static_cast<int>(sizeof(UnitRec) / 8);
+      for (int i = threadIdx.x; i < nw; i += kThreads) wz[i] = 0ull;
+    }
+    if (threadIdx.x < kWireWords) a.pending[b].w[threadIdx.x] = 0ull;
+    if (threadIdx.x == 0) store_coherent(a.counters + static_cast<size_t>(b) * kCounterStride + kUnitCounter, 0u);
+  }
+  __syncthreads();  // LDS is reused by the next item
+}
+
+// Unit item of the separate unit launch: with few requests the unit items go
+// only to class-0 requests; otherwise request = item / nunit.
+template <int DT, bool VEC>
+__device__ void unit_item(const ChainArgs& a, long long item, const Exp2Table& tab) {
+  const int unit = static_cast<int>(item % a.nunit);
   int b;
   if (a.B <= kCompactMaxBatch) {
     static_assert(kCompactMaxBatch <= kThreads, "one temperature per thread");
@@ -592,83 +888,55 @@ __device__ void unit_item(const ChainArgs& a, long long item) {
     b = static_cast<int>(item / a.nunit);
     if (request_class(a, a.temperature[b]) != 0) return;
   }
-  if (threadIdx.x == 0) s_pending = a.pending[b];  // cleared only after this unit has arrived
-  __syncthreads();
-  const Pending d = s_pending;
-  if (d.valid != 1) return;  // invalid request: launch 1 wrote its outputs
-  // this unit's share of the final draw
-  const double l2t = kLog2e / static_cast<double>(d.t);
-  const int c0 = unit * S::kSpan;
-  const int c1 = min(a.V, c0 + S::kSpan);
-  const bool residual = d.mode == kModeResidual;
-  const int trow = residual ? d.n : G;
-  S st;
-  st.load(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + trow, a.V), c0, c1);
-  double pos_t = 0.0, pos_d = 0.0, all_t = 0.0, all_d = 0.0;
-  if (residual) {
-    S sd;
-    sd.load(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + d.n, a.V), c0, c1);
-#pragma unroll
-    for (int e = 0; e < S::kPer; ++e) {
-      const double et = exp_scaled(st.x[0][e], d.mt, l2t);
-      const double ed = exp_scaled(sd.x[0][e], d.md, l2t);
-      all_t += et;
-      all_d += ed;
-      if (et * d.zd > ed * d.zt) {  // p > q under the pass-1 normalisers
-        pos_t += et;
-        pos_d += ed;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < S::kPer; ++e) all_t += exp_scaled(st.x[0][e], d.mt, l2t);
-  }
-  pos_t = wave_sum(pos_t);
-  pos_d = wave_sum(pos_d);
-  all_t = wave_sum(all_t);
-  all_d = wave_sum(all_d);
-  const int w = threadIdx.x / kWave;
-  if ((threadIdx.x % kWave) == 0) {
-    s_w[kUnitPosT][w] = pos_t;
-    s_w[kUnitPosD][w] = pos_d;
-    s_w[kUnitAllT][w] = all_t;
-    s_w[kUnitAllD][w] = all_d;
-  }
-  __syncthreads();
-  // wave 0 hands the record over (one field per lane) and counts the unit in
-  if (threadIdx.x < kUnitFields) {
-    double v = 0.0;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) v += s_w[threadIdx.x][i];
-    store_coherent_f64(&a.units[static_cast<size_t>(b) * a.nunit + unit].f[threadIdx.x], v);
-  }
-  if (threadIdx.x == 0)
-    s_last = arrive(a.counters + static_cast<size_t>(b) * kCounterStride + kUnitCounter) ==
-             static_cast<uint32_t>(a.nunit - 1);
-  __syncthreads();
-  if (s_last) {
-    draw_token<DT, VEC>(a, b, d);
-    unsigned long long* wz = reinterpret_cast<unsigned long long*>(a.units + static_cast<size_t>(b) * a.nunit);
-    const int nw = a.nunit * static_cast<int>(sizeof(UnitRec) / 8);
-    for (int i = threadIdx.x; i < nw; i += kThreads) wz[i] = 0ull;
-    unsigned long long* pz = reinterpret_cast<unsigned long long*>(a.pending + b);
-    if (threadIdx.x < static_cast<int>(sizeof(Pending) / 8)) pz[threadIdx.x] = 0ull;
-    if (threadIdx.x == 0) store_coherent(a.counters + static_cast<size_t>(b) * kCounterStride + kUnitCounter, 0u);
-  }
-  __syncthreads();  // LDS is reused by the next item
+  unit_work<DT, VEC>(a, b, unit, tab);
 }
 
-// The draw of the last unit needs more registers than the unit sums; holding
-// the kernel to 64 registers keeps eight waves per SIMD for the sums at the
-// cost of a few spills on the draw path.
-template <int DT, bool VEC, bool LOOP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void chain_units(ChainArgs a) {
-  if constexpr (LOOP) {
-    const long long items = static_cast<long long>(a.B) * a.nunit;
-    for (long long item = blockIdx.x; item < items; item += gridDim.x) unit_item<DT, VEC>(a, item);
-  } else {
-    unit_item<DT, VEC>(a, blockIdx.x);
+
+// ---------------------------------------------------------------------------
+// launch 2: decisions, draw units and draws
+// ---------------------------------------------------------------------------
+// Blocks [0, B) decide request b.  The blocks after them are unit items, each
+// waiting only for the decision of its own request, made by a lower-numbered
+// block: workgroups are dispatched in block order, so that block is running
+// or done and the wait ends.  With B <= kCompactMaxBatch the unit items go to
+// the requests that draw, in request order, and the rest exit at once.
+template <int DT>
+__device__ void decide_request(const ChainArgs& a, int b, const Exp2Table& tab) {
+  if (request_class(a, a.temperature[b]) == 2) write_invalid(a, b);  // nothing was streamed
+  else decide_and_publish<DT>(a, b, tab);
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void chain_draw(ChainArgs a) {
+  __shared__ Exp2Table tab;
+  exp2_table_init(tab);
+  __syncthreads();
+  const long long blk = blockIdx.x;
+  if (blk < a.B) decide_request<DT>(a, static_cast<int>(blk), tab);
+  else unit_item<DT, VEC>(a, blk - a.B, tab);
+}
+
+// Very large shapes: decisions and units in launches of their own, each with
+// a capped grid whose workgroups stride over the items (no unit waits: every
+// decision is made by the time the unit launch starts).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void chain_decide(ChainArgs a) {
+  __shared__ Exp2Table tab;
+  exp2_table_init(tab);
+  __syncthreads();
+  for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
+    decide_request<DT>(a, b, tab);
+    __syncthreads();
   }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void chain_units(ChainArgs a) {
+  __shared__ Exp2Table tab;
+  exp2_table_init(tab);
+  __syncthreads();
+  const long long items = static_cast<long long>(a.B) * a.nunit;
+  for (long long item = blockIdx.x; item < items; item += gridDim.x) unit_item<DT, VEC>(a, item, tab);
 }
 
 // ---------------------------------------------------------------------------
@@ -686,40 +954,69 @@ static int units_for(int V, int kper) {
 // Sized for the largest draw-unit count (scalar path: kThreads logits per unit).
 static ChainLayout chain_layout(int B, int gamma, int V) {
   ChainLayout L{};
-  const size_t nchunk = static_cast<size_t>(num_chunks(V));
+  const size_t nchunk = static_cast<size_t>(row_chunks(V));
   const size_t R = 2 * static_cast<size_t>(gamma) + 1;
   const size_t nunit = static_cast<size_t>(units_for(V, 1));
   size_t off = 0;
   L.partials = off; off = align_up(off + static_cast<size_t>(B) * R * nchunk * sizeof(RowPartial));
   L.gathers = off;  off = align_up(off + static_cast<size_t>(B) * R * sizeof(float));
-  L.pending = off;  off = align_up(off + static_cast<size_t>(B) * sizeof(Pending));
+  L.pending = off;  off = align_up(off + static_cast<size_t>(B) * sizeof(PendingWire));
   L.units = off;    off = align_up(off + static_cast<size_t>(B) * nunit * sizeof(UnitRec));
   L.counters = off; off = align_up(off + static_cast<size_t>(B) * kCounterStride * sizeof(uint32_t));
   L.total = off;
   return L;
 }
 
-// Grids of the two launches are capped; their workgroups stride over the
-// remaining items.
+// Grids of launch 2 in its split form are capped; their workgroups stride.
 constexpr long long kMaxGrid = 1 << 20;
+
+// Workgroups of chain_stream that fit on the current device at once.
+template <int DT, bool VEC>
+static long long stream_capacity() {
+  static long long cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_stream<DT, VEC>, kThreads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 || cus < 1)
+      return 1024;
+    cached[dev] = static_cast<long long>(per_cu) * cus;
+  }
+  return cached[dev];
+}
+
+// Test hook: a positive value in this environment variable caps every grid
+// at that many workgroups and selects the split form of launch 2.
+static long long test_grid_cap() {
+  const char* v = getenv("SV_CHAIN_TEST_GRID_CAP");
+  return v ? atoll(v) : 0;
+}
 
 template <int DT, bool VEC>
 static int launch_chain(ChainArgs a, hipStream_t stream) {
   const long long items = static_cast<long long>(a.B) * (2 * a.gamma + 1) * a.nchunk;
-  a.nunit = units_for(a.V, Slice<DT, VEC, 1>::kPer);
+  a.nunit = units_for(a.V, UnitSlice<DT, VEC>::kPer * kUnitItems);
   const long long units = static_cast<long long>(a.B) * a.nunit;
-  if (items <= kMaxGrid)
-    launch(SV_K_CHAIN_ROW_STATS, chain_row_stats<DT, VEC, false>, dim3(static_cast<unsigned>(items)), dim3(kThreads),
-           0, stream, a);
+  const long long cap = test_grid_cap();
+  long long sg = stream_capacity<DT, VEC>();
+  if (cap > 0 && cap < sg) sg = cap;
+  if (getenv("SV_CHAIN_STREAM_PERSISTENT") != nullptr || items > kMaxGrid || cap > 0)
+    launch(SV_K_CHAIN_STREAM, chain_stream<DT, VEC>, dim3(static_cast<unsigned>(items < sg ? items : sg)),
+           dim3(kThreads), 0, stream, a);
   else
-    launch(SV_K_CHAIN_ROW_STATS, chain_row_stats<DT, VEC, true>, dim3(static_cast<unsigned>(kMaxGrid)), dim3(kThreads),
-           0, stream, a);
-  if (units <= kMaxGrid)
-    launch(SV_K_CHAIN_UNITS, chain_units<DT, VEC, false>, dim3(static_cast<unsigned>(units)), dim3(kThreads), 0,
+    launch(SV_K_CHAIN_STREAM, chain_stream_once<DT, VEC>, dim3(static_cast<unsigned>(items)), dim3(kOnceThreads), 0,
            stream, a);
-  else
-    launch(SV_K_CHAIN_UNITS, chain_units<DT, VEC, true>, dim3(static_cast<unsigned>(kMaxGrid)), dim3(kThreads), 0,
+  if (cap <= 0 && a.B + units <= kMaxGrid) {
+    launch(SV_K_CHAIN_DRAW, chain_draw<DT, VEC>, dim3(static_cast<unsigned>(a.B + units)), dim3(kThreads), 0,
            stream, a);
+  } else {
+    const long long g = cap > 0 ? cap : kMaxGrid;
+    launch(SV_K_CHAIN_DECIDE, chain_decide<DT>, dim3(static_cast<unsigned>(a.B < g ? a.B : g)), dim3(kThreads), 0,
+           stream, a);
+    launch(SV_K_CHAIN_UNITS, chain_units<DT, VEC>, dim3(static_cast<unsigned>(units < g ? units : g)),
+           dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
@@ -760,12 +1057,12 @@ extern "C" int spec_verify_chain(const void* target_logits, const void* draft_lo
   a.B = B;
   a.gamma = gamma;
   a.V = V;
-  a.nchunk = num_chunks(V);
+  a.nchunk = row_chunks(V);
   a.out_tokens = out_tokens;
   a.out_n = out_num_accepted;
   a.partials = reinterpret_cast<RowPartial*>(ws + L.partials);
   a.gathers = reinterpret_cast<float*>(ws + L.gathers);
-  a.pending = reinterpret_cast<Pending*>(ws + L.pending);
+  a.pending = reinterpret_cast<PendingWire*>(ws + L.pending);
   a.units = reinterpret_cast<UnitRec*>(ws + L.units);
   a.counters = reinterpret_cast<uint32_t*>(ws + L.counters);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);

@@ -152,6 +152,105 @@ __host__ __device__ inline double exp2_nonpos(double t_in) {
 // e^y for y <= 0.
 __host__ __device__ inline double exp_nonpos(double y) { return exp2_nonpos(y * kLog2e); }
 
+// 2^(j/64) for j = 0..63, held in LDS by the workgroups that use exp2_tab.
+struct Exp2Table {
+  double v[64];
+};
+
+// Fills the table, one entry per thread of the first wave (the caller
+// synchronises before use).  Entries come from the same reduction as
+// exp2_nonpos with the Taylor series carried to degree 14 (truncation below
+// 1e-18 on |f| <= 1/2).
+__device__ inline void exp2_table_init(Exp2Table& tab) {
+  const int j = threadIdx.x;
+  if (j < 64) {
+    const double f = j / 64.0 - 0.5;  // 2^(j/64) = 2^0.5 * 2^f
+    double p = 1.0, term = 1.0;
+    constexpr double kLn2 = 0x1.62e42fefa39efp-1;
+#pragma unroll
+    for (int i = 1; i <= 14; ++i) {
+      term *= f * kLn2 / i;
+      p += term;
+    }
+    tab.v[j] = p * 0x1.6a09e667f3bcdp+0;  // sqrt(2)
+  }
+}
+
+// 2^t for t <= 0 (t = -inf gives 0) from the table: t = n + j/64 + f with
+// n, j integers (j in [0, 64)) and |f| <= 1/128; 2^f by its Taylor series to
+// degree 5 (truncation below 4e-17); the product is scaled by 2^n.
+__device__ inline double exp2_tab(double t_in, const Exp2Table& tab) {
+  constexpr double kShift = 0x1.8p52;
+  const double t = __builtin_fmax(t_in, -1100.0);
+  const double sh = __builtin_fma(t, 64.0, kShift);  // round(64 t) in the low word
+  const double kd = sh - kShift;
+  const double f = __builtin_fma(kd, -0x1p-6, t);   // exact: t - k/64
+  struct Words { uint32_t lo, hi; };
+  const int k = static_cast<int>(__builtin_bit_cast(Words, sh).lo);
+  double p = 0x1.5d87fe78a6731p-10;                  // ln2^5 / 5!
+  p = __builtin_fma(p, f, 0x1.3b2ab6fba4e77p-7);
+  p = __builtin_fma(p, f, 0x1.c6b08d704a0c0p-5);
+  p = __builtin_fma(p, f, 0x1.ebfbdff82c58fp-3);
+  p = __builtin_fma(p, f, 0x1.62e42fefa39efp-1);
+  p = __builtin_fma(p, f, 1.0);
+  return __builtin_ldexp(p * tab.v[k & 63], k >> 6);
+}
+
+// ---------------------------------------------------------------------------
+// raw (still packed) slices for prefetching
+// ---------------------------------------------------------------------------
+// The element layout of Slice (for NT threads), kept as loaded (16-byte words, or single
+// elements on the scalar path) so that two items can be in flight per thread
+// at the cost of the raw words only; elements are unpacked where they are used.
+template <int DT, bool VEC, int ITEMS, int NT = kThreads>
+struct RawSlice {
+  static constexpr int kPer = VEC ? Elem<DT>::kVec : 1;
+  static constexpr int kItems = ITEMS;
+  static constexpr int kSpan = NT * kPer * ITEMS;
+  uint32_t w[ITEMS][VEC ? 4 : 1];
+
+  __device__ static inline int index(int c0, int j, int e) {
+    return c0 + (j * NT + static_cast<int>(threadIdx.x)) * kPer + e;
+  }
+
+  // Issues the loads of [c0, c1) of `row` (c1 - c0 <= kSpan) from clamped,
+  // in-range addresses, with no branches between them.
+  __device__ inline void load(const void* row, int c0, int c1) {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const int k0 = index(c0, j, 0);
+      const int k = k0 < c1 ? k0 : c0;
+      if constexpr (VEC) {
+        const uint4 v = Elem<DT>::raw(row, k);
+        w[j][0] = v.x; w[j][1] = v.y; w[j][2] = v.z; w[j][3] = v.w;
+      } else if constexpr (DT == 0) {
+        w[j][0] = static_cast<const uint16_t*>(row)[k];
+      } else {
+        w[j][0] = static_cast<const uint32_t*>(row)[k];
+      }
+    }
+  }
+
+  // Element e of group j as float (no range check).
+  __device__ inline float at(int j, int e) const {
+    if constexpr (VEC) {
+      if constexpr (DT == 0) return __uint_as_float((e & 1) ? (w[j][e >> 1] & 0xffff0000u) : (w[j][e >> 1] << 16));
+      else return __uint_as_float(w[j][e]);
+    } else {
+      if constexpr (DT == 0) return __uint_as_float(w[j][0] << 16);
+      else return __uint_as_float(w[j][0]);
+    }
+  }
+};
+
+// Workgroup barrier that orders LDS accesses only: global loads still in
+// flight (prefetched data) stay in flight across it.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------------------
 // reductions
 // ---------------------------------------------------------------------------

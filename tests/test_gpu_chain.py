@@ -208,7 +208,44 @@ def test_kernel_timer_counts_every_launch(batched):
     with sv.KernelTimer(64) as timer:
         for _ in range(4):
             timed = sv.verify_chain(tgt, drf, tok, u, T)
-    for name in ("chain_row_stats", "chain_units"):
+    for name in ("chain_stream", "chain_draw"):
         assert timer.launches[name] == 4
         assert 0.0 < timer.mean_us(name) < 1e5
     assert torch.equal(plain[0], timed[0].cpu()) and torch.equal(plain[1], timed[1].cpu())
+
+
+@pytest.mark.parametrize("cap", [37, 1000])
+def test_split_form_with_striding_workgroups(cap, monkeypatch):
+    """The split form (decisions and draw units in launches of their own, used
+    when one grid would be too large) with a small workgroup cap, so that
+    every workgroup strides over several items; it must agree with the oracle
+    and leave the workspace zeroed."""
+    monkeypatch.setenv("SV_CHAIN_TEST_GRID_CAP", str(cap))
+    ci = synth.chain_inputs(131, B=24, gamma=3, V=40000, dtype="bf16", family="peaked",
+                            draft_sigma=(0.3, 2.0), temperature=0.8, greedy_odd=True)
+    dev = torch.device("cuda")
+    need = sv.lib().sv_chain_workspace_bytes(ci.B, ci.gamma, ci.V, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    tgt = to_device_logits(ci.target, ci.dtype)
+    drf = to_device_logits(ci.draft, ci.dtype)
+    tok = to_device(ci.draft_tokens.astype(np.int32))
+    T = to_device(ci.temperature)
+    u_sets = [ci.uniforms] + [ci.fresh_uniforms(700 + s) for s in range(7)]
+    refs = oracle_chain_many(ci, u_sets)
+    tally = Tally()
+    for u, ref in zip(u_sets, refs):
+        with sv.KernelTimer(8) as timer:
+            ot, on = sv.verify_chain(tgt, drf, tok, to_device(u), T, ws=ws)
+            torch.cuda.synchronize()
+        for name in ("chain_stream", "chain_decide", "chain_units"):
+            assert timer.launches.get(name) == 1, name
+        assert int(ws.count_nonzero()) == 0
+        tally.add(compare_chain(ref, ot.cpu().numpy(), on.cpu().numpy()))
+    tally.check(f"split form cap={cap}")
+
+
+def test_persistent_stream_variant(monkeypatch, batched):
+    """The persistent, prefetching form of the streaming launch agrees with the
+    oracle on the batched workload."""
+    monkeypatch.setenv("SV_CHAIN_STREAM_PERSISTENT", "1")
+    parity(batched, 20, label="persistent stream, batched")
