@@ -167,7 +167,7 @@ def main():
     rows = ci.B * (ci.gamma + 1)
     rd, sm = read_bytes(ci), small_bytes(ci)
     call_us = 1e3 * ms_per_step
-    dominant = "chain_stream"
+    dominant = "chain_verify"
     k_us = kt.mean_us(dominant)
     achieved = rd / (k_us * 1e-6) / 1e9
     traffic = stored_traffic(dominant)

@@ -209,8 +209,8 @@ SV_API int spec_probs_debug(const void* target_logits, const void* draft_logits,
  * a session are recorded in launch order.
  * ---------------------------------------------------------------------- */
 typedef enum {
-  SV_K_CHAIN_STREAM = 0,      /* chain: per-(row, chunk) max / exp-sum / argmax over the logits */
-  SV_K_CHAIN_DRAW = 1,        /* chain: accept tests, per-unit draw sums and inverse-CDF draws */
+  SV_K_CHAIN_VERIFY = 0,      /* chain: row statistics, accept tests and draws in one launch */
+  SV_K_CHAIN_STREAM = 1,      /* chain, very large shapes: row statistics in a launch of their own */
   SV_K_CHAIN_DECIDE = 2,      /* chain, very large shapes: accept tests in a launch of their own */
   SV_K_CHAIN_UNITS = 3,       /* chain, very large shapes: draw sums and draws in a launch of their own */
   SV_K_TREE_INIT = 4,

@@ -3,34 +3,37 @@
 // close-reading notes 02, section 4, and CMU 15-779 lecture 17 notes, sections
 // 2.2-2.4).  See include/specverify.h for the contract.
 //
-// Two launches on the caller's stream:
+// One launch of one-wave workgroups on the caller's stream (chain_verify),
+// whose blocks fall into three parts:
 //
-//  1. chain_row_stats  one workgroup per (request, row, chunk) of kChunk
-//                      logits, request-major: the chunk max and, for sampling
-//                      rows, the fp32 sum of exp2((x - max) * log2e / T); for
-//                      greedy rows the argmax (lowest index).  The workgroup
-//                      whose chunk holds a row's draft token also hands over
-//                      that logit.  Draft rows of greedy requests are not
-//                      read.  The last workgroup of a request to finish
-//                      merges the request's partials in fp64, runs the
-//                      gamma-step test (u <= tau, tau = 1 if q <= p else p / q;
-//                      greedy: argmax equality), writes the accepted tokens
-//                      and the count, and for a sampling request leaves the
-//                      pending final draw for launch 2.  Early requests are
-//                      decided while later ones still stream.
-//  2. chain_units      one workgroup per (sampling request, draw unit) of
-//                      kThreads * kPer logits: fp64 sums of exp((x - max) / T)
-//                      of the draw's target and draft rows over the unit (all,
-//                      and where p > q).  The last unit of a request to finish
-//                      does the draw: fp64 normalisers, the residual (or bonus)
-//                      weight of every unit, and an fp64 block scan of the
-//                      crossing unit -- the smallest k with C_k > u * W.
+//  1. stream items  one per (request, row, chunk of kRowChunk logits),
+//                   request-major: the chunk max and, for a sampling row, the
+//                   fp32 sum of exp2((x - max) * log2e / T); for a greedy row
+//                   the argmax (lowest index).  Every result is one
+//                   self-marked 64-bit word, so stream items never wait for
+//                   anything.  Draft rows of greedy requests are not read.
+//  2. decide items  one per request: waits until every word of its request
+//                   carries its mark, merges the chunks in fp64, reads the
+//                   logits of the draft tokens from the input rows, runs the
+//                   gamma-step test (u <= tau, tau = 1 if q <= p else p / q;
+//                   greedy: argmax equality), writes the accepted tokens and
+//                   the count, and publishes a sampling request's final draw.
+//  3. draw units    per drawing request, one per span of the draw's rows:
+//                   fp64 sums of exp((x - max) / T) over the span (all, and
+//                   where p > q); the last unit of the request to count in
+//                   draws the token -- the smallest k with C_k > u * W.
 //
-// Whoever finishes last also returns the workspace words it consumed to zero.
+// Workgroups are dispatched in block order and every wait is for lower blocks,
+// so each wait ends.  The decide items and units are dispatched while the last
+// stream items are still in flight: early requests are decided and drawn under
+// the streaming of later ones.  Very large shapes run the same three parts as
+// three launches (chain_stream, chain_decide, chain_units) with capped grids
+// whose workgroups stride over the items.  Whoever consumes a workspace word
+// last returns it to zero.
 //
 // Precision: the accept test needs p(x)/q(x) to ~1e-6 and uses the fp32 chunk
 // sums merged in fp64; the final draw uses fp64 exponentials and fp64
-// normalisers summed in launch 2, so the inverse CDF matches an fp64
+// normalisers summed by the units, so the inverse CDF matches an fp64
 // reference except where u lies within a few ulps of a CDF step.
 #include <stdlib.h>
 
@@ -42,10 +45,18 @@ namespace sv {
 // ---------------------------------------------------------------------------
 // workspace records
 // ---------------------------------------------------------------------------
-struct RowPartial {  // one (row, chunk), handed over as one 64-bit word
-  float m;           // chunk max
-  int32_t v;         // float bits of the exp-sum (sampling) or the argmax (greedy)
-};
+// One (row, chunk) result in one 64-bit word: the chunk max's float bits in
+// the low half; above them the exp-sum's float bits (sampling) or the argmax
+// (greedy), with bit 63 set as the mark -- neither value uses that bit (sums
+// are >= 0, indices < 2^31).  A zero word is "not yet written".
+constexpr uint64_t kMark = 1ull << 63;
+
+__device__ inline uint64_t pack_partial(float m, int32_t v) {
+  return kMark | (static_cast<uint64_t>(static_cast<uint32_t>(v)) << 32) | __float_as_uint(m);
+}
+__device__ inline float partial_max(uint64_t w) { return __uint_as_float(static_cast<uint32_t>(w)); }
+__device__ inline int32_t partial_value(uint64_t w) { return static_cast<int32_t>((w >> 32) & 0x7fffffffu); }
+__device__ inline bool marked(uint64_t w) { return (w & kMark) != 0; }
 
 // Per (request, draw unit), fp64: sums over the unit of the target (t) and
 // draft (d) exponentials, over all tokens and over the tokens with p > q.
@@ -54,9 +65,10 @@ struct UnitRec {
   double f[kUnitFields];
 };
 
-// A sampling request's final draw, decided in launch 1 and drawn in launch 2.
+// A sampling request's final draw, decided by its decide item and drawn by
+// its units.
 struct Pending {
-  int32_t valid;  // 1 while a draw is pending
+  int32_t valid;  // kPendingDraw or kPendingNone once published
   int32_t n;      // accepted drafts; the draw fills out_tokens[b][n]
   int32_t mode;   // kModeResidual / kModeBonus
   float u;        // u[b][gamma]
@@ -76,8 +88,8 @@ struct PendingWire {
   uint64_t w[kWireWords];
 };
 
-static_assert(sizeof(RowPartial) == 8, "row partials are one 64-bit word");
 static_assert(sizeof(UnitRec) % 8 == 0 && sizeof(Pending) % 8 == 0, "records are cleared in 64-bit words");
+static_assert(kWireWords <= kWave, "one wire word per lane");
 
 enum : int32_t { kModeResidual = 1, kModeBonus = 2 };
 enum : int32_t { kPendingDraw = 1, kPendingNone = 2 };  // Pending::valid once published
@@ -92,10 +104,10 @@ struct ChainArgs {
   const float* uniforms;
   const float* temperature;
   int B, gamma, V, nchunk, nunit;
+  long long nstream;  // stream items: B * (2 * gamma + 1) * nchunk
   int32_t* out_tokens;
   int32_t* out_n;
-  RowPartial* partials;  // [B][2*gamma+1][nchunk]
-  float* gathers;        // [B][2*gamma+1] logit of the draft token in each row
+  uint64_t* partials;    // [B][2*gamma+1][nchunk] marked (row, chunk) words
   PendingWire* pending;  // [B]
   UnitRec* units;        // [B][nunit]
   uint32_t* counters;    // [B][kCounterStride]
@@ -110,12 +122,8 @@ __device__ inline const void* row_ptr(const void* base, size_t row, int V) {
 }
 
 // exp((x - m) / T) for x <= m, in fp64, given l2t = log2(e) / T (the
-// difference is taken in fp64, so it is exact for fp32 logits too).
-__device__ inline double exp_scaled(float x, float m, double l2t) {
-  return exp2_nonpos((static_cast<double>(x) - static_cast<double>(m)) * l2t);
-}
-
-// The same with the LDS table of the calling workgroup.
+// difference is taken in fp64, so it is exact for fp32 logits too), with the
+// LDS table of the calling workgroup.
 __device__ inline double exp_scaled(float x, float m, double l2t, const Exp2Table& tab) {
   return exp2_tab((static_cast<double>(x) - static_cast<double>(m)) * l2t, tab);
 }
@@ -134,8 +142,12 @@ __device__ inline int needed_rows(const ChainArgs& a, float T) {
   return (T > 0.0f && a.draft != nullptr) ? 2 * a.gamma + 1 : a.gamma + 1;
 }
 
+// Upper bound on the polls of a waiting workgroup (seconds at the least);
+// every wait is for workgroups dispatched before the waiting one, so the bound
+// only guards against a broken dispatch order.
+constexpr uint32_t kSpinLimit = 1u << 22;
 
-// Thread t < kWireWords of the calling workgroup stores word t.
+// Lane t < kWireWords stores word t of the record.
 __device__ inline void publish_pending(PendingWire* wire, const Pending& d) {
   const int t = threadIdx.x;
   if (t < kWireWords) {
@@ -150,259 +162,49 @@ __device__ inline void publish_pending(PendingWire* wire, const Pending& d) {
   }
 }
 
-// Upper bound on the polls of a unit waiting for its request's decision
-// (about 2 s); the decision is always made by workgroups dispatched before the
-// waiting one, so the bound only guards against a broken dispatch order.
-constexpr uint32_t kSpinLimit = 1u << 22;
-
-// Waits (thread 0 polls, the workgroup then reads the copy in LDS) until the
-// decision of request b is published and returns it; valid = 0 means the
-// wait gave up.
+// Waits until the decision of request b is published (lane t polls word t)
+// and returns it to every lane; valid = 0 means the wait gave up.
 __device__ Pending wait_pending(const ChainArgs& a, int b) {
-  __shared__ Pending s_p;
-  if (threadIdx.x == 0) {
-    const PendingWire* wire = a.pending + b;
-    struct Dwords { uint32_t v[kWireWords]; };
-    Dwords got{};
-    bool whole = false;
-    for (uint32_t spin = 0; !whole && spin < kSpinLimit; ++spin) {
-      if ((load_coherent(&wire->w[0]) >> 32) != 0) {
-        asm volatile("" ::: "memory");
-        whole = true;
-#pragma unroll
-        for (int i = 0; i < kWireWords; ++i) {
-          const uint64_t w = load_coherent(&wire->w[i]);
-          whole = whole && (w >> 32) != 0;
-          got.v[i] = static_cast<uint32_t>(w);
-        }
-      }
-      if (!whole) __builtin_amdgcn_s_sleep(8);
+  const int lane = threadIdx.x;
+  const PendingWire* wire = a.pending + b;
+  uint64_t w = 0;
+  bool whole = false;
+  for (uint32_t spin = 0; spin < kSpinLimit; ++spin) {
+    if (lane < kWireWords) w = load_coherent(&wire->w[lane]);
+    const uint64_t got = __ballot(lane < kWireWords && (w >> 32) != 0);
+    if (got == (1ull << kWireWords) - 1ull) {
+      whole = true;
+      break;
     }
-    Pending d = __builtin_bit_cast(Pending, got);
-    if (!whole) d.valid = 0;
-    s_p = d;
+    __builtin_amdgcn_s_sleep(4);
   }
-  __syncthreads();
-  const Pending d = s_p;
-  __syncthreads();
+  struct Dwords { uint32_t v[kWireWords]; };
+  Dwords got{};
+#pragma unroll
+  for (int i = 0; i < kWireWords; ++i) got.v[i] = static_cast<uint32_t>(read_lane(static_cast<int>(w), i));
+  Pending d = __builtin_bit_cast(Pending, got);
+  if (!whole) d.valid = 0;
   return d;
 }
 
 __device__ void write_invalid(const ChainArgs& a, int b) {
   const int G = a.gamma;
-  for (int i = threadIdx.x; i <= G; i += kThreads) a.out_tokens[static_cast<size_t>(b) * (G + 1) + i] = -1;
+  for (int i = threadIdx.x; i <= G; i += kWave) a.out_tokens[static_cast<size_t>(b) * (G + 1) + i] = -1;
   if (threadIdx.x == 0) a.out_n[b] = -1;
 }
 
 // ---------------------------------------------------------------------------
-// the decision of request b
+// part 1: streaming row statistics
 // ---------------------------------------------------------------------------
-// Merges the request's chunk partials in fp64: one thread per group of chunks
-// of a row takes the group max, then rescales every chunk sum to it (all
-// exponentials independent of each other); one thread per row combines the
-// groups the same way.  Then the drafts are tested in order; tokens [0, n]
-// (all but a sampling request's slot n) and the count are written, a
-// drawing request's outcome is published to its units, and the partials and
-// gathered logits return to zero.
-template <int DT>
-__device__ void decide_and_publish(const ChainArgs& a, int b, const Exp2Table& tab) {
-  constexpr int kMaxRows = 2 * SV_MAX_GAMMA + 1;
-  __shared__ float s_gm[kThreads];
-  __shared__ double s_gz[kThreads];
-  __shared__ int32_t s_garg[kThreads];
-  __shared__ float s_m[kMaxRows];
-  __shared__ double s_z[kMaxRows];
-  __shared__ int32_t s_arg[kMaxRows];
-  __shared__ float s_xt[SV_MAX_GAMMA], s_xd[SV_MAX_GAMMA];
-  __shared__ int32_t s_ok[SV_MAX_GAMMA];
-  __shared__ int32_t s_n;
-  __shared__ Pending s_pend;
-  const int tid = threadIdx.x;
-  const int G = a.gamma;
-  const int R = 2 * G + 1;
-  const float T = a.temperature[b];
-  const bool sampling = T > 0.0f;
-  const double l2t = sampling ? kLog2e / static_cast<double>(T) : 0.0;
-  const int nrows = needed_rows(a, T);
-  // one round of loads: the chunk partials (in groups of chunks, one group per
-  // thread), the draft tokens, their gathered logits and the uniforms
-  const int gpr = max(1, min((a.nchunk + 3) / 4, kThreads / nrows));  // groups per row
-  const int gs = (a.nchunk + gpr - 1) / gpr;                           // chunks per group
-  int bad = 0;
-  if (tid < G) {
-    const int32_t x = a.tokens[static_cast<size_t>(b) * G + tid];
-    bad |= (x < 0 || x >= a.V);
-    if (sampling && a.draft != nullptr) {
-      s_xt[tid] = a.gathers[static_cast<size_t>(b) * R + tid];
-      s_xd[tid] = a.gathers[static_cast<size_t>(b) * R + G + 1 + tid];
-    }
-  }
-  if (sampling && tid <= G) {
-    const float u = a.uniforms[static_cast<size_t>(b) * (G + 1) + tid];
-    bad |= !(u >= 0.0f && u < 1.0f);
-  }
-  if (sampling && G > 0 && a.draft == nullptr) bad = 1;
-  if (tid < nrows * gpr) {
-    const int r = tid / gpr;
-    const int g = tid % gpr;
-    const RowPartial* p = a.partials + (static_cast<size_t>(b) * R + r) * a.nchunk;
-    const int cb = g * gs;
-    const int ce = min(a.nchunk, cb + gs);
-    float m = -INFINITY;
-    double z = 0.0;
-    ArgMax best{-INFINITY, 0x7fffffff};
-    for (int c0 = cb; c0 < ce; c0 += 4) {
-      RowPartial w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = p[min(c0 + i, ce - 1)];
-      if (!sampling) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (c0 + i < ce) best = argmax_combine(best, ArgMax{w[i].m, w[i].v});
-      } else {
-        float m4 = m;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (c0 + i < ce) m4 = fmaxf(m4, w[i].m);
-        if (m4 != -INFINITY) {
-          double z4 = (m != -INFINITY) ? z * exp_scaled(m, m4, l2t, tab) : 0.0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (c0 + i < ce && w[i].m != -INFINITY)
-              z4 += static_cast<double>(__int_as_float(w[i].v)) * exp_scaled(w[i].m, m4, l2t, tab);
-          m = m4;
-          z = z4;
-        }
-      }
-    }
-    if (sampling) {
-      s_gm[tid] = m;
-      s_gz[tid] = z;
-    } else {
-      s_gm[tid] = best.v;
-      s_garg[tid] = best.i;
-    }
-  }
-  bad = __syncthreads_or(bad);
-  if (!bad) {
-    // combine the groups of each row
-    if (tid < nrows) {
-      if (!sampling) {
-        ArgMax best{-INFINITY, 0x7fffffff};
-        for (int g = 0; g < gpr; ++g)
-          best = argmax_combine(best, ArgMax{s_gm[tid * gpr + g], s_garg[tid * gpr + g]});
-        s_m[tid] = best.v;
-        s_arg[tid] = best.i;
-      } else {
-        float m = -INFINITY;
-        for (int g = 0; g < gpr; ++g) m = fmaxf(m, s_gm[tid * gpr + g]);
-        double z = 0.0;
-        for (int g = 0; g < gpr; ++g) {
-          const float gm = s_gm[tid * gpr + g];
-          if (gm != -INFINITY) z += s_gz[tid * gpr + g] * exp_scaled(gm, m, l2t, tab);
-        }
-        s_m[tid] = m;
-        s_z[tid] = z;
-      }
-    }
-    __syncthreads();
-    if (tid < G) {
-      const int32_t x = a.tokens[static_cast<size_t>(b) * G + tid];
-      int ok;
-      if (!sampling) {
-        ok = (x == s_arg[tid]);
-      } else {
-        const double p = exp_scaled(s_xt[tid], s_m[tid], l2t, tab) / s_z[tid];
-        const double q = exp_scaled(s_xd[tid], s_m[G + 1 + tid], l2t, tab) / s_z[G + 1 + tid];
-        const double tau = (q <= p) ? 1.0 : p / q;
-        const double u = static_cast<double>(a.uniforms[static_cast<size_t>(b) * (G + 1) + tid]);
-        ok = (u <= tau);
-      }
-      s_ok[tid] = ok;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int n = 0;
-      while (n < G && s_ok[n]) ++n;
-      s_n = n;
-      if (sampling) {
-        Pending d{};
-        d.valid = kPendingDraw;
-        d.n = n;
-        d.mode = n < G ? kModeResidual : kModeBonus;
-        d.u = a.uniforms[static_cast<size_t>(b) * (G + 1) + G];
-        d.t = T;
-        d.mt = s_m[n];
-        d.zt = s_z[n];
-        if (n < G) {
-          d.md = s_m[G + 1 + n];
-          d.zd = s_z[G + 1 + n];
-        }
-        s_pend = d;
-      }
-    }
-  }
-  if (tid == 0 && bad) {
-    Pending d{};
-    d.valid = kPendingNone;
-    s_pend = d;
-  }
-  __syncthreads();
-  // a request with draw units hears the outcome in every case: the draw, or
-  // that there is none
-  if (request_class(a, T) == 0) publish_pending(a.pending + b, s_pend);
-  // outputs: tokens [0, n), greedy: the argmax at slot n, the rest -1; slot n
-  // of a sampling request is filled by its draw
-  int32_t* out = a.out_tokens + static_cast<size_t>(b) * (G + 1);
-  const int n = bad ? -1 : s_n;
-  for (int i = tid; i <= G; i += kThreads) {
-    int32_t v = -1;
-    if (!bad) {
-      if (sampling && i == n) continue;
-      if (i < n) v = a.tokens[static_cast<size_t>(b) * G + i];
-      else if (i == n) v = s_arg[n];
-    }
-    out[i] = v;
-  }
-  if (tid == 0) a.out_n[b] = n;
-  // the workspace words of this request back to zero
-  unsigned long long* pz = reinterpret_cast<unsigned long long*>(a.partials + static_cast<size_t>(b) * R * a.nchunk);
-  for (int i = tid; i < nrows * a.nchunk; i += kThreads) pz[i] = 0ull;
-  if (tid < R) a.gathers[static_cast<size_t>(b) * R + tid] = 0.0f;
-}
-
-// ---------------------------------------------------------------------------
-// launch 1: streaming row statistics
-// ---------------------------------------------------------------------------
-// Persistent workgroups (as many as fit on the GPU) stride over the items
-// (request, row, chunk) in request-major order.  Each keeps two items in
-// flight: the loads of the next item are issued before the current one is
-// reduced, and the reductions synchronise through LDS only, so the prefetch
-// stays outstanding.  Per item: the chunk max and, for sampling rows, the fp32
-// sum of exp2((x - max) * log2e / T); for greedy rows the argmax (lowest
-// index); the chunk holding a row's draft token also stores that logit.  Rows
-// that no decision needs (draft rows of greedy requests, requests with an
-// invalid temperature) are skipped.
-
-// Row chunk of one streaming item, and so of one row partial.
+// Row chunk of one stream item, and so of one row partial.
 constexpr int kRowChunk = 4096;
 __host__ __device__ inline int row_chunks(int V) { return (V + kRowChunk - 1) / kRowChunk; }
-
-// Which rows of each request are streamed, 2 bits per request, kept in LDS.
-constexpr int kMaxStreamBatch = SV_MAX_BATCH;
-enum : uint32_t { kStreamTarget = 1u, kStreamDraft = 2u };
-
-struct StreamFlags {
-  uint32_t w[kMaxStreamBatch / 16];
-  __device__ inline uint32_t get(int b) const { return (w[b >> 4] >> ((b & 15) * 2)) & 3u; }
-};
 
 template <int DT, bool VEC, int NT>
 struct StreamItem {
   using Raw = RawSlice<DT, VEC, kRowChunk / (NT * (VEC ? Elem<DT>::kVec : 1)), NT>;
   Raw raw;
-  float t;      // temperature of the request
-  int32_t tok;  // draft token of the row (sampling rows below gamma), else -1
+  float t;  // temperature of the request
 };
 
 // Item order: request-major, rows (target 0..gamma, then draft), then chunks.
@@ -415,22 +217,9 @@ __device__ inline RowItem decode_item(const ChainArgs& a, long long item) {
   return RowItem{static_cast<int>(item / per_req), rem / a.nchunk, rem % a.nchunk};
 }
 
-__device__ inline bool stream_needed(const ChainArgs& a, const StreamFlags& fl, long long item) {
-  const RowItem r = decode_item(a, item);
-  const int b = r.b, k = r.k;
-  const uint32_t f = fl.get(b);
-  return k <= a.gamma ? (f & kStreamTarget) != 0 : (f & kStreamDraft) != 0;
-}
-
-__device__ inline long long stream_next(const ChainArgs& a, const StreamFlags& fl, long long item, long long items) {
-  while (item < items && !stream_needed(a, fl, item)) item += gridDim.x;
-  return item;
-}
-
 template <int DT, bool VEC, int NT>
-__device__ inline void stream_issue(const ChainArgs& a, long long item, StreamItem<DT, VEC, NT>& it) {
+__device__ inline void stream_issue(const ChainArgs& a, const RowItem& r, StreamItem<DT, VEC, NT>& it) {
   const int G = a.gamma;
-  const RowItem r = decode_item(a, item);
   const int b = r.b, k = r.k, c = r.c;
   const int pos = k <= G ? k : k - G - 1;
   const void* row = (k <= G) ? row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + k, a.V)
@@ -438,19 +227,18 @@ __device__ inline void stream_issue(const ChainArgs& a, long long item, StreamIt
   const int c0 = c * kRowChunk;
   it.raw.load(row, c0, min(a.V, c0 + kRowChunk));
   it.t = a.temperature[b];
-  it.tok = pos < G ? a.tokens[static_cast<size_t>(b) * G + pos] : -1;
 }
 
 // NT == kWave: one wave per workgroup, reductions within the wave only;
 // otherwise the waves combine through LDS.
 template <int DT, bool VEC, int NT>
-__device__ inline void stream_reduce(const ChainArgs& a, long long item, const StreamItem<DT, VEC, NT>& it) {
+__device__ inline void stream_reduce(const ChainArgs& a, const RowItem& r, const StreamItem<DT, VEC, NT>& it) {
   using Raw = typename StreamItem<DT, VEC, NT>::Raw;
-  __shared__ float s_a[kWaves];
-  __shared__ int s_i[kWaves];
+  constexpr int kNW = NT / kWave;
+  __shared__ float s_a[kNW];
+  __shared__ int s_i[kNW];
   const int G = a.gamma;
   const int R = 2 * G + 1;
-  const RowItem r = decode_item(a, item);
   const int b = r.b, k = r.k, c = r.c;
   const int c0 = c * kRowChunk;
   const int c1 = min(a.V, c0 + kRowChunk);
@@ -469,12 +257,12 @@ __device__ inline void stream_reduce(const ChainArgs& a, long long item, const S
     // chunk max first; only the lanes holding it look for its lowest index
     const float wm = wave_max(m);
     float bm = wm;
-    if constexpr (NT != kWave) {
+    if constexpr (kNW > 1) {
       if (lane0) s_a[w] = wm;
       lds_barrier();
       bm = s_a[0];
 #pragma unroll
-      for (int i = 1; i < NT / kWave; ++i) bm = fmaxf(bm, s_a[i]);
+      for (int i = 1; i < kNW; ++i) bm = fmaxf(bm, s_a[i]);
     }
     int idx = 0x7fffffff;
     if (m == bm) {
@@ -487,13 +275,13 @@ __device__ inline void stream_reduce(const ChainArgs& a, long long item, const S
         }
     }
     int bi = wave_min(idx);
-    if constexpr (NT != kWave) {
+    if constexpr (kNW > 1) {
       lds_barrier();  // s_a has been read
       if (lane0) s_i[w] = bi;
       lds_barrier();
       bi = s_i[0];
 #pragma unroll
-      for (int i = 1; i < NT / kWave; ++i) bi = min(bi, s_i[i]);
+      for (int i = 1; i < kNW; ++i) bi = min(bi, s_i[i]);
     }
     out_m = bm;
     out_v = bi;
@@ -507,76 +295,621 @@ __device__ inline void stream_reduce(const ChainArgs& a, long long item, const S
 #pragma unroll
         for (int e = 0; e < Raw::kPer; ++e) z += __builtin_amdgcn_exp2f(__builtin_fmaf(val(j, e), sc, -msc));
     }
-    MaxSum r = wave_maxsum(MaxSum{m, z}, sc);
-    if constexpr (NT != kWave) {
+    MaxSum rs = wave_maxsum(MaxSum{m, z}, sc);
+    if constexpr (kNW > 1) {
       if (lane0) {
-        s_a[w] = r.m;
-        s_i[w] = __float_as_int(r.z);
+        s_a[w] = rs.m;
+        s_i[w] = __float_as_int(rs.z);
       }
       lds_barrier();
-      r = MaxSum{s_a[0], __int_as_float(s_i[0])};
+      rs = MaxSum{s_a[0], __int_as_float(s_i[0])};
 #pragma unroll
-      for (int i = 1; i < NT / kWave; ++i) r = maxsum_combine(r, MaxSum{s_a[i], __int_as_float(s_i[i])}, sc);
+      for (int i = 1; i < kNW; ++i) rs = maxsum_combine(rs, MaxSum{s_a[i], __int_as_float(s_i[i])}, sc);
     }
-    out_m = r.m;
-    out_v = __float_as_int(r.z);
+    out_m = rs.m;
+    out_v = __float_as_int(rs.z);
   }
-  if (it.tok >= c0 && it.tok < c1) {  // the lane holding the draft token stores its logit
-#pragma unroll
-    for (int j = 0; j < Raw::kItems; ++j)
-#pragma unroll
-      for (int e = 0; e < Raw::kPer; ++e)
-        if (Raw::index(c0, j, e) == it.tok) a.gathers[static_cast<size_t>(b) * R + k] = it.raw.at(j, e);
-  }
-  if (threadIdx.x == 0) {
-    RowPartial p;
-    p.m = out_m;
-    p.v = out_v;
-    a.partials[(static_cast<size_t>(b) * R + k) * a.nchunk + c] = p;
-  }
-  if constexpr (NT != kWave) lds_barrier();  // s_a / s_i are reused by the next item
+  if (threadIdx.x == 0)
+    store_coherent(&a.partials[(static_cast<size_t>(b) * R + k) * a.nchunk + c], pack_partial(out_m, out_v));
+  if constexpr (kNW > 1) lds_barrier();  // s_a / s_i are reused by the next item
 }
 
-// The last chunk of a row: words past the row's end (loaded from a clamped
-// address) become -inf before the reduction.  Vector groups lie wholly inside
-// or outside the row (V is a multiple of the vector width on that path).
-template <int DT, bool VEC, int NT>
-__device__ inline void stream_reduce_any(const ChainArgs& a, long long item, StreamItem<DT, VEC, NT>& it) {
-  using Raw = typename StreamItem<DT, VEC, NT>::Raw;
-  const int c0 = decode_item(a, item).c * kRowChunk;
-  const int c1 = min(a.V, c0 + kRowChunk);
+// Words of a RawSlice past `c1` (loaded from a clamped address) become -inf.
+// Vector groups lie wholly inside or outside the row (V is a multiple of the
+// vector width on that path).
+template <int DT, bool VEC, typename Raw>
+__device__ inline void pad_tail(Raw& raw, int c0, int c1) {
   if (c1 - c0 != Raw::kSpan) {
     constexpr uint32_t kNegInf = DT == 0 ? (VEC ? 0xff80ff80u : 0xff80u) : 0xff800000u;
 #pragma unroll
     for (int j = 0; j < Raw::kItems; ++j)
       if (Raw::index(c0, j, 0) >= c1) {
 #pragma unroll
-        for (int q = 0; q < (VEC ? 4 : 1); ++q) it.raw.w[j][q] = kNegInf;
+        for (int q = 0; q < (VEC ? 4 : 1); ++q) raw.w[j][q] = kNegInf;
       }
   }
-  stream_reduce<DT, VEC, NT>(a, item, it);
 }
 
-// One item per workgroup of one wave (no prefetch, no barriers): the grid
-// covers every item.
-constexpr int kOnceThreads = kWave;
+template <int DT, bool VEC, int NT>
+__device__ inline void stream_reduce_any(const ChainArgs& a, const RowItem& r, StreamItem<DT, VEC, NT>& it) {
+  const int c0 = r.c * kRowChunk;
+  pad_tail<DT, VEC>(it.raw, c0, min(a.V, c0 + kRowChunk));
+  stream_reduce<DT, VEC, NT>(a, r, it);
+}
 
+// One stream item in a one-wave workgroup (no prefetch, no barriers).
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kOnceThreads) void chain_stream_once(ChainArgs a) {
-  constexpr int NT = kOnceThreads;
-  const long long item = blockIdx.x;
-  const RowItem r = decode_item(a, item);
-  const int b = r.b, k = r.k;
-  StreamItem<DT, VEC, NT> x;
-  if (k <= a.gamma) {
-    stream_issue<DT, VEC, NT>(a, item, x);  // target rows: the loads do not wait for the temperature
+__device__ inline void stream_once(const ChainArgs& a, const RowItem& r) {
+  StreamItem<DT, VEC, kWave> x;
+  if (r.k <= a.gamma) {
+    stream_issue<DT, VEC, kWave>(a, r, x);  // target rows: the loads do not wait for the temperature
     if (!temp_ok(x.t)) return;
   } else {
-    const float T = a.temperature[b];
+    const float T = a.temperature[r.b];
     if (!(temp_ok(T) && T > 0.0f && a.draft != nullptr)) return;
-    stream_issue<DT, VEC, NT>(a, item, x);
+    stream_issue<DT, VEC, kWave>(a, r, x);
   }
-  stream_reduce_any<DT, VEC, NT>(a, item, x);
+  stream_reduce_any<DT, VEC, kWave>(a, r, x);
+}
+
+// ---------------------------------------------------------------------------
+// part 2: the decision of request b (one wave)
+// ---------------------------------------------------------------------------
+// Lane s takes slot s = row * gpr + group: a group of consecutive chunks of a
+// row, polled kPoll words at a time until all carry their mark, then merged in
+// fp64 (the group's max first, then every chunk sum rescaled to it, the
+// exponentials independent of each other).  One lane per row combines the
+// groups the same way.  The drafts are then tested in order; tokens [0, n]
+// (all but a sampling request's slot n) and the count are written, a drawing
+// request's outcome is published to its units, and the request's partials
+// return to zero.
+constexpr int kPoll = 8;
+constexpr int kMaxRows = 2 * SV_MAX_GAMMA + 1;
+constexpr int kMaxSlots = 2 * kWave;  // nrows * gpr <= max(kWave, kMaxRows)
+static_assert(kMaxRows <= kMaxSlots, "slots cover the rows");
+
+// Polls words [c0, min(c0 + kPoll, ce)) of p until all are marked (reads
+// beyond ce repeat word ce - 1); false if the wait gave up.
+__device__ inline bool poll_words(const uint64_t* p, int c0, int ce, uint64_t (&w)[kPoll]) {
+  for (uint32_t spin = 0; spin < kSpinLimit; ++spin) {
+    bool all = true;
+#pragma unroll
+    for (int i = 0; i < kPoll; ++i) {
+      w[i] = load_coherent(p + min(c0 + i, ce - 1));
+      all = all && marked(w[i]);
+    }
+    if (all) return true;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return false;
+}
+
+template <int DT>
+__device__ void decide_request(const ChainArgs& a, int b, const Exp2Table& tab) {
+  __shared__ float s_gm[kMaxSlots];
+  __shared__ double s_gz[kMaxSlots];
+  __shared__ int32_t s_garg[kMaxSlots];
+  __shared__ float s_m[kMaxRows];
+  __shared__ double s_z[kMaxRows];
+  __shared__ int32_t s_arg[kMaxRows];
+  const int lane = threadIdx.x;
+  const int G = a.gamma;
+  const int R = 2 * G + 1;
+  const float T = a.temperature[b];
+  if (request_class(a, T) == 2) {  // nothing was streamed
+    write_invalid(a, b);
+    return;
+  }
+  const bool sampling = T > 0.0f;
+  const double l2t = sampling ? kLog2e / static_cast<double>(T) : 0.0;
+  const int nrows = needed_rows(a, T);
+  const int gpr = max(1, min(a.nchunk, kWave / nrows));  // groups per row
+  const int gs = (a.nchunk + gpr - 1) / gpr;              // chunks per group
+  const int nslots = nrows * gpr;
+  int bad = 0;
+  int32_t x = -1;
+  float u = 0.0f;
+  if (lane < G) {
+    x = a.tokens[static_cast<size_t>(b) * G + lane];
+    bad |= (x < 0 || x >= a.V);
+  }
+  if (sampling && lane <= G) {
+    u = a.uniforms[static_cast<size_t>(b) * (G + 1) + lane];
+    bad |= !(u >= 0.0f && u < 1.0f);
+  }
+  if (sampling && G > 0 && a.draft == nullptr) bad = 1;
+  // the logits of the draft tokens in target row i and draft row i
+  float xt = 0.0f, xd = 0.0f;
+  if (sampling && lane < G && x >= 0 && x < a.V) {
+    xt = Elem<DT>::at(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + lane, a.V), x);
+    if (a.draft != nullptr) xd = Elem<DT>::at(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + lane, a.V), x);
+  }
+  // every partial of the needed rows, whatever the verdict: they are all
+  // written, and returned to zero below
+  const uint64_t* pb = a.partials + static_cast<size_t>(b) * R * a.nchunk;
+  for (int s = lane; s < nslots; s += kWave) {
+    const int r = s / gpr;
+    const int g = s % gpr;
+    const uint64_t* p = pb + static_cast<size_t>(r) * a.nchunk;
+    const int cb = g * gs;
+    const int ce = min(a.nchunk, cb + gs);
+    float m = -INFINITY;
+    double z = 0.0;
+    ArgMax best{-INFINITY, 0x7fffffff};
+    for (int c0 = cb; c0 < ce; c0 += kPoll) {
+      uint64_t w[kPoll];
+      if (!poll_words(p, c0, ce, w)) bad = 1;
+      if (!sampling) {
+#pragma unroll
+        for (int i = 0; i < kPoll; ++i)
+          if (c0 + i < ce) best = argmax_combine(best, ArgMax{partial_max(w[i]), partial_value(w[i])});
+      } else {
+        float m8 = m;
+#pragma unroll
+        for (int i = 0; i < kPoll; ++i)
+          if (c0 + i < ce) m8 = fmaxf(m8, partial_max(w[i]));
+        if (m8 != -INFINITY) {
+          double z8 = (m != -INFINITY) ? z * exp_scaled(m, m8, l2t, tab) : 0.0;
+#pragma unroll
+          for (int i = 0; i < kPoll; ++i) {
+            const float wm = partial_max(w[i]);
+            if (c0 + i < ce && wm != -INFINITY)
+              z8 += static_cast<double>(__int_as_float(partial_value(w[i]))) * exp_scaled(wm, m8, l2t, tab);
+          }
+          m = m8;
+          z = z8;
+        }
+      }
+    }
+    if (sampling) {
+      s_gm[s] = m;
+      s_gz[s] = z;
+    } else {
+      s_gm[s] = best.v;
+      s_garg[s] = best.i;
+    }
+  }
+  __syncthreads();
+  // combine the groups of each row
+  for (int r = lane; r < nrows; r += kWave) {
+    if (!sampling) {
+      ArgMax best{-INFINITY, 0x7fffffff};
+      for (int g = 0; g < gpr; ++g) best = argmax_combine(best, ArgMax{s_gm[r * gpr + g], s_garg[r * gpr + g]});
+      s_m[r] = best.v;
+      s_arg[r] = best.i;
+    } else {
+      float m = -INFINITY;
+      for (int g = 0; g < gpr; ++g) m = fmaxf(m, s_gm[r * gpr + g]);
+      double z = 0.0;
+      for (int g = 0; g < gpr; ++g) {
+        const float gm = s_gm[r * gpr + g];
+        if (gm != -INFINITY) z += s_gz[r * gpr + g] * exp_scaled(gm, m, l2t, tab);
+      }
+      s_m[r] = m;
+      s_z[r] = z;
+    }
+  }
+  __syncthreads();
+  const bool any_bad = __any(bad);
+  int n = -1;
+  if (!any_bad) {
+    int ok = 1;
+    if (lane < G) {
+      if (!sampling) {
+        ok = (x == s_arg[lane]);
+      } else {
+        const double p = exp_scaled(xt, s_m[lane], l2t, tab) / s_z[lane];
+        const double q = exp_scaled(xd, s_m[G + 1 + lane], l2t, tab) / s_z[G + 1 + lane];
+        const double tau = (q <= p) ? 1.0 : p / q;
+        ok = (static_cast<double>(u) <= tau);
+      }
+    }
+    const uint64_t fail = __ballot(lane < G && !ok);
+    n = fail ? static_cast<int>(__builtin_ctzll(fail)) : G;
+  }
+  // a request with draw units hears the outcome in every case: the draw, or
+  // that there is none
+  if (request_class(a, T) == 0) {
+    Pending d{};
+    if (any_bad) {
+      d.valid = kPendingNone;
+    } else {
+      d.valid = kPendingDraw;
+      d.n = n;
+      d.mode = n < G ? kModeResidual : kModeBonus;
+      d.u = read_lane(u, G);
+      d.t = T;
+      d.mt = s_m[n];
+      d.zt = s_z[n];
+      if (n < G) {
+        d.md = s_m[G + 1 + n];
+        d.zd = s_z[G + 1 + n];
+      }
+    }
+    publish_pending(a.pending + b, d);
+  }
+  // outputs: tokens [0, n), greedy: the argmax at slot n, the rest -1; slot n
+  // of a sampling request is filled by its draw
+  if (lane <= G) {
+    int32_t v = -1;
+    bool write = true;
+    if (!any_bad) {
+      if (lane < n) v = x;
+      else if (lane == n) {
+        if (sampling) write = false;
+        else v = s_arg[n];
+      }
+    }
+    if (write) a.out_tokens[static_cast<size_t>(b) * (G + 1) + lane] = v;
+  }
+  if (lane == 0) a.out_n[b] = n;
+  // the workspace words of this request back to zero
+  uint64_t* pz = a.partials + static_cast<size_t>(b) * R * a.nchunk;
+  for (int i = lane; i < nrows * a.nchunk; i += kWave) store_coherent(pz + i, 0ull);
+}
+
+// ---------------------------------------------------------------------------
+// part 3: draw units, and the draw by the last unit of each request
+// ---------------------------------------------------------------------------
+// A draw unit covers kUnitSpan logits: one 16-byte group per lane for bf16,
+// two for fp32, eight single logits on the scalar path.  Small units spread
+// the draw of the last requests over many SIMDs.
+constexpr int kUnitSpan = 512;
+template <int DT, bool VEC>
+struct Unit {
+  static constexpr int kItems = kUnitSpan / (kWave * (VEC ? Elem<DT>::kVec : 1));
+  using Raw = RawSlice<DT, VEC, kItems, kWave>;
+  static constexpr int kSpan = Raw::kSpan;
+  static_assert(kSpan == kUnitSpan, "one span for every path");
+};
+
+__device__ inline double unit_field(const UnitRec* r, int f) { return load_coherent_f64(&r->f[f]); }
+
+// Weight of a unit in the final draw (rzt, rzd: reciprocal normalisers).
+__device__ inline double unit_weight(double pos_t, double pos_d, double all_t, bool residual, double rzt, double rzd) {
+  return residual ? (pos_t * rzt - pos_d * rzd) : all_t;
+}
+
+// The draw of request b from its unit records: fp64 normalisers, the weight W
+// of the draw (residual mass, or the target normaliser for a bonus draw), the
+// unit where the running weight first exceeds u * W, then an fp64 wave scan
+// of that unit's logits for the token.  With up to kDrawCache * kWave units
+// the records are read once and kept in registers (lane l holds units l,
+// l + kWave, ...); otherwise they are read again for each pass.
+constexpr int kDrawCache = 5;
+
+template <int DT, bool VEC>
+__device__ void draw_token(const ChainArgs& a, int b, const Pending& d, const Exp2Table& tab) {
+  using U = Unit<DT, VEC>;
+  using Raw = typename U::Raw;
+  const int G = a.gamma;
+  const int lane = threadIdx.x;
+  const UnitRec* ur = a.units + static_cast<size_t>(b) * a.nunit;
+  const bool cached = a.nunit <= kDrawCache * kWave;
+  // 1) the totals: fp64 normalisers of the draw's rows, and the residual mass
+  double f[kDrawCache][kUnitFields];
+  double tot[kUnitFields] = {0.0, 0.0, 0.0, 0.0};
+  if (cached) {
+#pragma unroll
+    for (int q = 0; q < kDrawCache; ++q) {
+      const int i = q * kWave + lane;
+#pragma unroll
+      for (int k = 0; k < kUnitFields; ++k) {
+        f[q][k] = i < a.nunit ? unit_field(ur + i, k) : 0.0;
+        tot[k] += f[q][k];
+      }
+    }
+  } else {
+    for (int i = lane; i < a.nunit; i += kWave)
+#pragma unroll
+      for (int k = 0; k < kUnitFields; ++k) tot[k] += unit_field(ur + i, k);
+  }
+#pragma unroll
+  for (int k = 0; k < kUnitFields; ++k) tot[k] = wave_sum(tot[k]);
+  // p = e_t / zt and q = e_d / zd are formed with the reciprocals throughout
+  const double rzt = 1.0 / tot[kUnitAllT], rzd = 1.0 / tot[kUnitAllD];
+  // an empty residual (p and q equal up to rounding) draws from p of that
+  // position instead
+  const bool residual = d.mode == kModeResidual && (tot[kUnitPosT] * rzt - tot[kUnitPosD] * rzd > 0.0);
+  auto weight_of = [&](int i) -> double {
+    return unit_weight(unit_field(ur + i, kUnitPosT), unit_field(ur + i, kUnitPosD), unit_field(ur + i, kUnitAllT),
+                       residual, rzt, rzd);
+  };
+  double wc[kDrawCache];
+#pragma unroll
+  for (int q = 0; q < kDrawCache; ++q) wc[q] = unit_weight(f[q][kUnitPosT], f[q][kUnitPosD], f[q][kUnitAllT], residual, rzt, rzd);
+  double W = 0.0;
+  if (cached) {
+#pragma unroll
+    for (int q = 0; q < kDrawCache; ++q) W += wc[q];
+  } else {
+    for (int i = lane; i < a.nunit; i += kWave) W += weight_of(i);
+  }
+  W = wave_sum(W);
+  const double target = static_cast<double>(d.u) * W;
+  // 2) crossing unit: wave scans of the unit weights in unit order
+  int unit = -1, last_unit = -1;
+  double before_unit = 0.0, carry = 0.0;
+  auto scan_batch = [&](int base, double wu) -> bool {
+    const int i = base + lane;
+    const double inc = wave_inclusive_sum(wu);
+    const double before = carry + lane_move<kDppWaveShr1>(inc);  // lane 0 receives 0
+    const uint64_t pos = __ballot(i < a.nunit && wu > 0.0);
+    if (pos) last_unit = base + 63 - static_cast<int>(__builtin_clzll(pos));
+    const uint64_t hit = __ballot(i < a.nunit && before + wu > target);
+    if (hit) {
+      const int l = static_cast<int>(__builtin_ctzll(hit));
+      unit = base + l;
+      before_unit = read_lane(before, l);
+      return true;
+    }
+    carry += read_lane(inc, kWave - 1);
+    return false;
+  };
+  if (cached) {
+#pragma unroll
+    for (int q = 0; q < kDrawCache; ++q)
+      if (q * kWave < a.nunit && scan_batch(q * kWave, wc[q])) break;
+  } else {
+    for (int base = 0; base < a.nunit; base += kWave)
+      if (scan_batch(base, base + lane < a.nunit ? weight_of(base + lane) : 0.0)) break;
+  }
+  if (unit < 0) {  // rounding left u * W at the very top: take the last positive unit
+    unit = last_unit < 0 ? 0 : last_unit;
+    double bsum = 0.0;
+    if (cached) {
+#pragma unroll
+      for (int q = 0; q < kDrawCache; ++q)
+        if (q * kWave + lane < unit) bsum += wc[q];
+    } else {
+      for (int i = lane; i < unit; i += kWave) bsum += weight_of(i);
+    }
+    before_unit = wave_sum(bsum);
+  }
+  // 3) fp64 wave scans of the crossing unit, one per vector group (group j of
+  //    all lanes precedes group j + 1); lane t owns kPer logits of each
+  const int c0 = unit * U::kSpan;
+  const int c1 = min(a.V, c0 + U::kSpan);
+  const double l2t = kLog2e / static_cast<double>(d.t);
+  const int trow = d.mode == kModeResidual ? d.n : G;
+  Raw st, sd;
+  st.load(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + trow, a.V), c0, c1);
+  if (residual) sd.load(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + d.n, a.V), c0, c1);
+  pad_tail<DT, VEC>(st, c0, c1);
+  if (residual) pad_tail<DT, VEC>(sd, c0, c1);
+  int hit = 0x7fffffff;
+  int last_pos = -1;
+  double run0 = before_unit;
+  // group j sits in group 0 of the slices after j shifts
+#pragma unroll 1
+  for (int j = 0; j < Raw::kItems; ++j) {
+    double wk[Raw::kPer];
+    if (residual) {
+#pragma unroll
+      for (int e = 0; e < Raw::kPer; ++e)
+        wk[e] = fmax(0.0, exp_scaled(st.at(0, e), d.mt, l2t, tab) * rzt - exp_scaled(sd.at(0, e), d.md, l2t, tab) * rzd);
+    } else {
+#pragma unroll
+      for (int e = 0; e < Raw::kPer; ++e) wk[e] = exp_scaled(st.at(0, e), d.mt, l2t, tab);
+    }
+    st.shift();
+    sd.shift();
+    double own = 0.0;
+#pragma unroll
+    for (int e = 0; e < Raw::kPer; ++e) {
+      own += wk[e];
+      if (wk[e] > 0.0) last_pos = Raw::index(c0, j, e);
+    }
+    const double inc = wave_inclusive_sum(own);
+    double run = run0 + lane_move<kDppWaveShr1>(inc);
+    run0 += read_lane(inc, kWave - 1);
+#pragma unroll
+    for (int e = 0; e < Raw::kPer; ++e) {
+      run += wk[e];
+      if (hit == 0x7fffffff && wk[e] > 0.0 && run > target) hit = Raw::index(c0, j, e);
+    }
+  }
+  hit = wave_min(hit);
+  last_pos = wave_max_int(last_pos);
+  if (lane == 0) a.out_tokens[static_cast<size_t>(b) * (G + 1) + d.n] = (hit != 0x7fffffff) ? hit : last_pos;
+}
+
+// The drawing requests (class 0) of a batch of at most kRankMaxBatch: lane l
+// of mask k stands for request k * kWave + l.  The ranking reads only the
+// temperatures, which no workgroup changes.
+constexpr int kRankMaxBatch = 4 * kWave;
+struct DrawingSet {
+  uint64_t m[kRankMaxBatch / kWave];
+  int count;
+};
+
+__device__ inline DrawingSet drawing_requests(const ChainArgs& a) {
+  const int lane = threadIdx.x;
+  DrawingSet s{};
+  bool v[kRankMaxBatch / kWave];
+#pragma unroll
+  for (int k = 0; k < kRankMaxBatch / kWave; ++k) {
+    const int i = k * kWave + lane;
+    v[k] = i < a.B && request_class(a, a.temperature[i]) == 0;
+  }
+#pragma unroll
+  for (int k = 0; k < kRankMaxBatch / kWave; ++k) {
+    s.m[k] = __ballot(v[k]);
+    s.count += __popcll(s.m[k]);
+  }
+  return s;
+}
+
+// The p-th drawing request (0-based, request order); p < s.count.
+__device__ inline int nth_drawing(const DrawingSet& s, int p) {
+  const int lane = threadIdx.x;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int seen = 0;
+#pragma unroll
+  for (int k = 0; k < kRankMaxBatch / kWave; ++k) {
+    const int c = __popcll(s.m[k]);
+    if (p < seen + c) {
+      const uint64_t at = __ballot(((s.m[k] >> lane) & 1ull) && __popcll(s.m[k] & below) == p - seen);
+      return k * kWave + static_cast<int>(__builtin_ctzll(at));
+    }
+    seen += c;
+  }
+  return -1;
+}
+
+// Unit `unit` of request b (a class-0 request): waits for the decision, then
+// adds its share of the final draw and counts itself in; the last unit of the
+// request draws and returns the request's draw records to zero.
+template <int DT, bool VEC>
+__device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& tab) {
+  using U = Unit<DT, VEC>;
+  using Raw = typename U::Raw;
+  const int G = a.gamma;
+  const int lane = threadIdx.x;
+  const Pending d = wait_pending(a, b);
+  if (d.valid == 0 && lane == 0) a.out_n[b] = -1;  // gave up waiting
+  const bool draw = d.valid == kPendingDraw;
+  UnitRec* rec = a.units + static_cast<size_t>(b) * a.nunit + unit;
+  if (draw) {
+    const double l2t = kLog2e / static_cast<double>(d.t);
+    const int c0 = unit * U::kSpan;
+    const int c1 = min(a.V, c0 + U::kSpan);
+    const bool residual = d.mode == kModeResidual;
+    const int trow = residual ? d.n : G;
+    Raw st, sd;
+    st.load(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + trow, a.V), c0, c1);
+    if (residual) sd.load(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + d.n, a.V), c0, c1);
+    pad_tail<DT, VEC>(st, c0, c1);
+    double pos_t = 0.0, pos_d = 0.0, all_t = 0.0, all_d = 0.0;
+    // one group at a time: group j sits in group 0 of the slices after j shifts
+    if (residual) {
+      pad_tail<DT, VEC>(sd, c0, c1);
+#pragma unroll 1
+      for (int j = 0; j < Raw::kItems; ++j) {
+#pragma unroll
+        for (int e = 0; e < Raw::kPer; ++e) {
+          const double et = exp_scaled(st.at(0, e), d.mt, l2t, tab);
+          const double ed = exp_scaled(sd.at(0, e), d.md, l2t, tab);
+          all_t += et;
+          all_d += ed;
+          if (et * d.zd > ed * d.zt) {  // p > q under the pass-1 normalisers
+            pos_t += et;
+            pos_d += ed;
+          }
+        }
+        st.shift();
+        sd.shift();
+      }
+    } else {
+#pragma unroll 1
+      for (int j = 0; j < Raw::kItems; ++j) {
+#pragma unroll
+        for (int e = 0; e < Raw::kPer; ++e) all_t += exp_scaled(st.at(0, e), d.mt, l2t, tab);
+        st.shift();
+      }
+    }
+    pos_t = wave_sum(pos_t);
+    pos_d = wave_sum(pos_d);
+    all_t = wave_sum(all_t);
+    all_d = wave_sum(all_d);
+    // lane f hands over field f
+    if (lane < kUnitFields) {
+      const double v = lane == kUnitAllT ? all_t : lane == kUnitAllD ? all_d : lane == kUnitPosT ? pos_t : pos_d;
+      store_coherent_f64(&rec->f[lane], v);
+    }
+  }
+  uint32_t old = 0;
+  if (lane == 0) old = arrive(a.counters + static_cast<size_t>(b) * kCounterStride + kUnitCounter);
+  const bool last = read_lane(static_cast<int>(old), 0) == a.nunit - 1;
+  if (last) {
+    if (draw) {
+      // the last unit of a request draws while other units may still compute:
+      // let its wave issue first on its SIMD
+      __builtin_amdgcn_s_setprio(3);
+      draw_token<DT, VEC>(a, b, d, tab);
+      __builtin_amdgcn_s_setprio(0);
+      uint64_t* wz = reinterpret_cast<uint64_t*>(a.units + static_cast<size_t>(b) * a.nunit);
+      const int nw = a.nunit * static_cast<int>(sizeof(UnitRec) / 8);
+      for (int i = lane; i < nw; i += kWave) store_coherent(wz + i, 0ull);
+    }
+    if (lane < kWireWords) store_coherent(&a.pending[b].w[lane], 0ull);
+    if (lane == 0) store_coherent(a.counters + static_cast<size_t>(b) * kCounterStride + kUnitCounter, 0u);
+  }
+}
+
+// A pool of `count` workgroups (this one is number `w`) strides over the unit
+// tasks (drawing request, unit) in request order, so greedy requests take no
+// workgroups and each task waits only for its own request's decision.
+template <int DT, bool VEC>
+__device__ void unit_pool(const ChainArgs& a, long long w, long long count, const Exp2Table& tab) {
+  if (a.B <= kRankMaxBatch) {
+    const DrawingSet ds = drawing_requests(a);
+    const long long tasks = static_cast<long long>(ds.count) * a.nunit;
+    for (long long t = w; t < tasks; t += count)
+      unit_work<DT, VEC>(a, nth_drawing(ds, static_cast<int>(t / a.nunit)), static_cast<int>(t % a.nunit), tab);
+  } else {
+    const long long tasks = static_cast<long long>(a.B) * a.nunit;
+    for (long long t = w; t < tasks; t += count) {
+      const int b = static_cast<int>(t / a.nunit);
+      if (request_class(a, a.temperature[b]) == 0) unit_work<DT, VEC>(a, b, static_cast<int>(t % a.nunit), tab);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// kernels
+// ---------------------------------------------------------------------------
+// Blocks come in one segment per request -- its stream items, then its
+// decide item, which so waits about as long as its own request's loads take --
+// followed by the unit pool.  Each workgroup keeps at most 80 VGPRs, so six
+// waves of stream items share a SIMD.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(6))) void chain_verify(ChainArgs a) {
+  __shared__ Exp2Table tab;
+  const long long blk = blockIdx.x;
+  const long long per_req = a.nstream / a.B;  // stream items of one request
+  const long long nseg = a.nstream + a.B;
+  if (blk < nseg) {
+    const int b = static_cast<int>(blk / (per_req + 1));
+    const int rem = static_cast<int>(blk - b * (per_req + 1));
+    if (rem < per_req) {
+      stream_once<DT, VEC>(a, RowItem{b, rem / a.nchunk, rem % a.nchunk});
+      return;
+    }
+    exp2_table_init(tab);
+    __syncthreads();
+    decide_request<DT>(a, b, tab);
+    return;
+  }
+  exp2_table_init(tab);
+  __syncthreads();
+  unit_pool<DT, VEC>(a, blk - nseg, static_cast<long long>(gridDim.x) - nseg, tab);
+}
+
+// Very large shapes: the three parts as three launches.  Persistent
+// workgroups (as many as fit on the GPU) stride over the stream items in
+// request-major order, keeping two items in flight: the loads of the next
+// item are issued before the current one is reduced, and the reductions
+// synchronise through LDS only, so the prefetch stays outstanding.  Rows that
+// no decision needs (draft rows of greedy requests, requests with an invalid
+// temperature) are skipped.
+enum : uint32_t { kStreamTarget = 1u, kStreamDraft = 2u };
+
+// Which rows of each request are streamed, 2 bits per request, kept in LDS.
+struct StreamFlags {
+  uint32_t w[SV_MAX_BATCH / 16];
+  __device__ inline uint32_t get(int b) const { return (w[b >> 4] >> ((b & 15) * 2)) & 3u; }
+};
+
+__device__ inline bool stream_needed(const ChainArgs& a, const StreamFlags& fl, long long item) {
+  const RowItem r = decode_item(a, item);
+  const uint32_t f = fl.get(r.b);
+  return r.k <= a.gamma ? (f & kStreamTarget) != 0 : (f & kStreamDraft) != 0;
+}
+
+__device__ inline long long stream_next(const ChainArgs& a, const StreamFlags& fl, long long item) {
+  while (item < a.nstream && !stream_needed(a, fl, item)) item += gridDim.x;
+  return item;
 }
 
 template <int DT, bool VEC>
@@ -595,371 +928,59 @@ __global__ __launch_bounds__(kThreads) void chain_stream(ChainArgs a) {
     s_flags.w[i] = word;
   }
   __syncthreads();
-  const long long items = static_cast<long long>(a.B) * (2 * a.gamma + 1) * a.nchunk;
-  long long ia = stream_next(a, s_flags, blockIdx.x, items);
-  if (ia >= items) return;
+  long long ia = stream_next(a, s_flags, blockIdx.x);
+  if (ia >= a.nstream) return;
   StreamItem<DT, VEC, kThreads> x, y;
-  stream_issue<DT, VEC, kThreads>(a, ia, x);
+  stream_issue<DT, VEC, kThreads>(a, decode_item(a, ia), x);
   for (;;) {
-    const long long ib = stream_next(a, s_flags, ia + gridDim.x, items);
-    if (ib < items) stream_issue<DT, VEC, kThreads>(a, ib, y);
-    stream_reduce_any<DT, VEC, kThreads>(a, ia, x);
-    if (ib >= items) break;
-    const long long ic = stream_next(a, s_flags, ib + gridDim.x, items);
-    if (ic < items) stream_issue<DT, VEC, kThreads>(a, ic, x);
-    stream_reduce_any<DT, VEC, kThreads>(a, ib, y);
-    if (ic >= items) break;
+    const long long ib = stream_next(a, s_flags, ia + gridDim.x);
+    if (ib < a.nstream) stream_issue<DT, VEC, kThreads>(a, decode_item(a, ib), y);
+    stream_reduce_any<DT, VEC, kThreads>(a, decode_item(a, ia), x);
+    if (ib >= a.nstream) break;
+    const long long ic = stream_next(a, s_flags, ib + gridDim.x);
+    if (ic < a.nstream) stream_issue<DT, VEC, kThreads>(a, decode_item(a, ic), x);
+    stream_reduce_any<DT, VEC, kThreads>(a, decode_item(a, ib), y);
+    if (ic >= a.nstream) break;
     ia = ic;
   }
 }
 
-// ---------------------------------------------------------------------------
-// launch 2: draw units, and the draw by the last unit of each request
-// ---------------------------------------------------------------------------
-// A draw unit is kUnitItems vector groups per thread: 2048 * kUnitItems logits
-// on the bf16 vector path.
-constexpr int kUnitItems = 2;
-template <int DT, bool VEC>
-using UnitSlice = Slice<DT, VEC, kUnitItems>;
-
-// Weight of a unit in the final draw (rzt, rzd: reciprocal normalisers).
-__device__ inline double unit_weight(double pos_t, double pos_d, double all_t, bool residual,
-                                     double rzt, double rzd) {
-  return residual ? (pos_t * rzt - pos_d * rzd) : all_t;
-}
-
-__device__ inline double unit_field(const UnitRec* r, int f) { return load_coherent_f64(&r->f[f]); }
-
-// The draw of request b from its unit records: fp64 normalisers, the weight W
-// of the draw (residual mass, or the target normaliser for a bonus draw), the
-// unit where the running weight first exceeds u * W, then an fp64 block scan
-// of that unit's logits for the token.
-template <int DT, bool VEC>
-__device__ void draw_token(const ChainArgs& a, int b, const Pending& d, const Exp2Table& tab) {
-  using S = UnitSlice<DT, VEC>;
-  __shared__ int s_unit, s_first, s_lastpos, s_hit, s_lasttok;
-  __shared__ double s_before;
-  // the last unit of a request draws while other units still compute: let
-  // its waves issue first on their SIMDs
-  __builtin_amdgcn_s_setprio(3);
-  const int G = a.gamma;
-  const int tid = threadIdx.x;
-  const UnitRec* ur = a.units + static_cast<size_t>(b) * a.nunit;
-  // 1) one round of loads; with at most kThreads units (the usual case) each
-  //    thread keeps its unit's sums in registers for the scan below
-  const bool one_batch = a.nunit <= kThreads;
-  double mine[kUnitFields] = {0.0, 0.0, 0.0, 0.0};
-  double tot[kUnitFields] = {0.0, 0.0, 0.0, 0.0};
-  for (int i = tid; i < a.nunit; i += kThreads) {
-#pragma unroll
-    for (int f = 0; f < kUnitFields; ++f) {
-      const double v = unit_field(ur + i, f);
-      tot[f] += v;
-      if (one_batch) mine[f] = v;
-    }
-  }
-  block_sum_doubles<kUnitFields>(tot);
-  // p = e_t / zt and q = e_d / zd are formed with the reciprocals throughout
-  const double rzt = 1.0 / tot[kUnitAllT], rzd = 1.0 / tot[kUnitAllD];
-  // an empty residual (p and q equal up to rounding) draws from p of that
-  // position instead
-  const bool residual = d.mode == kModeResidual && (tot[kUnitPosT] * rzt - tot[kUnitPosD] * rzd > 0.0);
-  auto weight_of = [&](int i) -> double {
-    if (one_batch) return unit_weight(mine[kUnitPosT], mine[kUnitPosD], mine[kUnitAllT], residual, rzt, rzd);
-    return unit_weight(unit_field(ur + i, kUnitPosT), unit_field(ur + i, kUnitPosD),
-                       unit_field(ur + i, kUnitAllT), residual, rzt, rzd);
-  };
-  double W;
-  {
-    double ws[1] = {0.0};
-    for (int i = tid; i < a.nunit; i += kThreads) ws[0] += weight_of(i);
-    block_sum_doubles<1>(ws);
-    W = ws[0];
-  }
-  const double target = static_cast<double>(d.u) * W;
-  // 2) crossing unit: block scan of the unit weights in unit order
-  if (tid == 0) { s_unit = -1; s_lastpos = -1; }
-  __syncthreads();
-  double carry = 0.0;
-  for (int base = 0; base < a.nunit; base += kThreads) {
-    const int i = base + tid;
-    const double wu = i < a.nunit ? weight_of(i) : 0.0;
-    double total;
-    const double before = carry + block_exclusive_scan(wu, &total);
-    if (tid == 0) s_first = 0x7fffffff;
-    __syncthreads();
-    const int lp = wave_max_int((i < a.nunit && wu > 0.0) ? i : -1);
-    const int fi = wave_min((i < a.nunit && before + wu > target) ? i : 0x7fffffff);
-    if ((tid % kWave) == 0) {
-      atomicMax(&s_lastpos, lp);
-      atomicMin(&s_first, fi);
-    }
-    __syncthreads();
-    if (s_first != 0x7fffffff && i == s_first) {
-      s_unit = i;
-      s_before = before;
-    }
-    __syncthreads();
-    carry += total;
-    if (s_unit >= 0) break;
-  }
-  if (s_unit < 0) {  // rounding left u * W at the very top: take the last positive unit
-    const int lp = s_lastpos < 0 ? 0 : s_lastpos;
-    double bsum[1] = {0.0};
-    for (int i = tid; i < lp; i += kThreads) bsum[0] += weight_of(i);
-    block_sum_doubles<1>(bsum);
-    if (tid == 0) { s_unit = lp; s_before = bsum[0]; }
-    __syncthreads();
-  }
-  // 3) fp64 block scans of the crossing unit, one per vector group (group j
-  //    of all threads precedes group j + 1); thread t owns kPer logits of each
-  const int c0 = s_unit * S::kSpan;
-  const int c1 = min(a.V, c0 + S::kSpan);
-  const double l2t = kLog2e / static_cast<double>(d.t);
-  const int trow = d.mode == kModeResidual ? d.n : G;
-  S st;
-  st.load(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + trow, a.V), c0, c1);
-  S sd;
-  if (residual) sd.load(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + d.n, a.V), c0, c1);
-  if (tid == 0) { s_hit = 0x7fffffff; s_lasttok = -1; }
-  int hit = 0x7fffffff;
-  int last_pos = -1;
-  double run0 = s_before;
-#pragma unroll
-  for (int j = 0; j < S::kItems; ++j) {
-    double wk[S::kPer];
-    if (residual) {
-#pragma unroll
-      for (int e = 0; e < S::kPer; ++e)
-        wk[e] = fmax(0.0, exp_scaled(st.x[j][e], d.mt, l2t, tab) * rzt - exp_scaled(sd.x[j][e], d.md, l2t, tab) * rzd);
-    } else {
-#pragma unroll
-      for (int e = 0; e < S::kPer; ++e) wk[e] = exp_scaled(st.x[j][e], d.mt, l2t, tab);
-    }
-    double own = 0.0;
-#pragma unroll
-    for (int e = 0; e < S::kPer; ++e) {
-      own += wk[e];
-      if (wk[e] > 0.0) last_pos = S::index(c0, j, e);
-    }
-    double total;
-    double run = run0 + block_exclusive_scan(own, &total);
-    run0 += total;
-#pragma unroll
-    for (int e = 0; e < S::kPer; ++e) {
-      run += wk[e];
-      if (hit == 0x7fffffff && wk[e] > 0.0 && run > target) hit = S::index(c0, j, e);
-    }
-  }
-  hit = wave_min(hit);
-  last_pos = wave_max_int(last_pos);
-  if ((tid % kWave) == 0) {
-    atomicMin(&s_hit, hit);
-    atomicMax(&s_lasttok, last_pos);
-  }
-  __syncthreads();
-  if (tid == 0)
-    a.out_tokens[static_cast<size_t>(b) * (G + 1) + d.n] = (s_hit != 0x7fffffff) ? s_hit : s_lasttok;
-  __syncthreads();
-  __builtin_amdgcn_s_setprio(0);
-}
-
-// Requests for unit items: with few requests, unit items are handed out only
-// to the requests that can have a final draw (class 0), in request order, so
-// that greedy and invalid requests occupy no workgroups; otherwise request =
-// item / nunit.  The ranking reads only the temperatures, which no workgroup
-// changes (the pending records are cleared as draws finish).
-constexpr int kCompactMaxBatch = 256;
-
-// The p-th class-0 request (0-based, request order), or -1.
-__device__ int nth_drawing_request(const ChainArgs& a, int p) {
-  __shared__ int s_cnt[kWaves];
-  __shared__ int s_b;
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int w = tid / kWave;
-  if (tid == 0) s_b = -1;
-  const int i = tid;
-  const bool v = i < a.B && request_class(a, a.temperature[i]) == 0;
-  const uint64_t m = __ballot(v);
-  if (lane == 0) s_cnt[w] = __popcll(m);
-  __syncthreads();
-  int before = __popcll(m & ((1ull << lane) - 1ull));
-#pragma unroll
-  for (int k = 0; k < kWaves; ++k)
-    if (k < w) before += s_cnt[k];
-  if (v && before == p) s_b = i;
-  __syncthreads();
-  return s_b;
-}
-
-// Unit `unit` of request b (a class-0 request): waits for the decision, then
-// adds its share of the final draw and counts itself in; the last unit of the
-// request draws and returns the request's draw records to zero.
-template <int DT, bool VEC>
-__device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& tab) {
-  using S = UnitSlice<DT, VEC>;
-  __shared__ double s_w[4][kWaves];
-  __shared__ int s_last;
-  const int G = a.gamma;
-  const Pending d = wait_pending(a, b);
-  if (d.valid == 0 && threadIdx.x == 0) a.out_n[b] = -1;  // gave up waiting
-  const bool draw = d.valid == kPendingDraw;
-  UnitRec* rec = a.units + static_cast<size_t>(b) * a.nunit + unit;
-  if (draw) {
-    const double l2t = kLog2e / static_cast<double>(d.t);
-    const int c0 = unit * S::kSpan;
-    const int c1 = min(a.V, c0 + S::kSpan);
-    const bool residual = d.mode == kModeResidual;
-    const int trow = residual ? d.n : G;
-    S st;
-    st.load(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + trow, a.V), c0, c1);
-    double pos_t = 0.0, pos_d = 0.0, all_t = 0.0, all_d = 0.0;
-    if (residual) {
-      S sd;
-      sd.load(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + d.n, a.V), c0, c1);
-#pragma unroll
-      for (int j = 0; j < S::kItems; ++j)
-#pragma unroll
-        for (int e = 0; e < S::kPer; ++e) {
-          const double et = exp_scaled(st.x[j][e], d.mt, l2t, tab);
-          const double ed = exp_scaled(sd.x[j][e], d.md, l2t, tab);
-          all_t += et;
-          all_d += ed;
-          if (et * d.zd > ed * d.zt) {  // p > q under the pass-1 normalisers
-            pos_t += et;
-            pos_d += ed;
-          }
-        }
-    } else {
-#pragma unroll
-      for (int j = 0; j < S::kItems; ++j)
-#pragma unroll
-        for (int e = 0; e < S::kPer; ++e) all_t += exp_scaled(st.x[j][e], d.mt, l2t, tab);
-    }
-    pos_t = wave_sum(pos_t);
-    pos_d = wave_sum(pos_d);
-    all_t = wave_sum(all_t);
-    all_d = wave_sum(all_d);
-    const int w = threadIdx.x / kWave;
-    if ((threadIdx.x % kWave) == 0) {
-      s_w[kUnitPosT][w] = pos_t;
-      s_w[kUnitPosD][w] = pos_d;
-      s_w[kUnitAllT][w] = all_t;
-      s_w[kUnitAllD][w] = all_d;
-    }
-    __syncthreads();
-    // wave 0 hands the record over (one field per lane)
-    if (threadIdx.x < kUnitFields) {
-      double v = 0.0;
-#pragma unroll
-      for (int i = 0; i < kWaves; ++i) v += s_w[threadIdx.x][i];
-      store_coherent_f64(&rec->f[threadIdx.x], v);
-    }
-  }
-  if (threadIdx.x == 0)
-    s_last = arrive(a.counters + static_cast<size_t>(b) * kCounterStride + kUnitCounter) ==
-             static_cast<uint32_t>(a.nunit - 1);
-  __syncthreads();
-  if (s_last) {
-    if (draw) {
-      draw_token<DT, VEC>(a, b, d, tab);
-      unsigned long long* wz = reinterpret_cast<unsigned long long*>(a.units + static_cast<size_t>(b) * a.nunit);
-      const int nw = a.nunit * static_cast<int>(sizeof(UnitRec) / 8);
-      for (int i = threadIdx.x; i < nw; i += kThreads) wz[i] = 0ull;
-    }
-    if (threadIdx.x < kWireWords) a.pending[b].w[threadIdx.x] = 0ull;
-    if (threadIdx.x == 0) store_coherent(a.counters + static_cast<size_t>(b) * kCounterStride + kUnitCounter, 0u);
-  }
-  __syncthreads();  // LDS is reused by the next item
-}
-
-// Unit item of the separate unit launch: with few requests the unit items go
-// only to class-0 requests; otherwise request = item / nunit.
-template <int DT, bool VEC>
-__device__ void unit_item(const ChainArgs& a, long long item, const Exp2Table& tab) {
-  const int unit = static_cast<int>(item % a.nunit);
-  int b;
-  if (a.B <= kCompactMaxBatch) {
-    static_assert(kCompactMaxBatch <= kThreads, "one temperature per thread");
-    b = nth_drawing_request(a, static_cast<int>(item / a.nunit));
-    if (b < 0) return;
-  } else {
-    b = static_cast<int>(item / a.nunit);
-    if (request_class(a, a.temperature[b]) != 0) return;
-  }
-  unit_work<DT, VEC>(a, b, unit, tab);
-}
-
-
-// ---------------------------------------------------------------------------
-// launch 2: decisions, draw units and draws
-// ---------------------------------------------------------------------------
-// Blocks [0, B) decide request b.  The blocks after them are unit items, each
-// waiting only for the decision of its own request, made by a lower-numbered
-// block: workgroups are dispatched in block order, so that block is running
-// or done and the wait ends.  With B <= kCompactMaxBatch the unit items go to
-// the requests that draw, in request order, and the rest exit at once.
 template <int DT>
-__device__ void decide_request(const ChainArgs& a, int b, const Exp2Table& tab) {
-  if (request_class(a, a.temperature[b]) == 2) write_invalid(a, b);  // nothing was streamed
-  else decide_and_publish<DT>(a, b, tab);
-}
-
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void chain_draw(ChainArgs a) {
-  __shared__ Exp2Table tab;
-  exp2_table_init(tab);
-  __syncthreads();
-  const long long blk = blockIdx.x;
-  if (blk < a.B) decide_request<DT>(a, static_cast<int>(blk), tab);
-  else unit_item<DT, VEC>(a, blk - a.B, tab);
-}
-
-// Very large shapes: decisions and units in launches of their own, each with
-// a capped grid whose workgroups stride over the items (no unit waits: every
-// decision is made by the time the unit launch starts).
-template <int DT>
-__global__ __launch_bounds__(kThreads) void chain_decide(ChainArgs a) {
+__global__ __launch_bounds__(kWave) void chain_decide(ChainArgs a) {
   __shared__ Exp2Table tab;
   exp2_table_init(tab);
   __syncthreads();
   for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
     decide_request<DT>(a, b, tab);
-    __syncthreads();
+    __syncthreads();  // LDS is reused by the next request
   }
 }
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void chain_units(ChainArgs a) {
+__global__ __launch_bounds__(kWave) void chain_units(ChainArgs a) {
   __shared__ Exp2Table tab;
   exp2_table_init(tab);
   __syncthreads();
-  const long long items = static_cast<long long>(a.B) * a.nunit;
-  for (long long item = blockIdx.x; item < items; item += gridDim.x) unit_item<DT, VEC>(a, item, tab);
+  unit_pool<DT, VEC>(a, blockIdx.x, gridDim.x, tab);
 }
 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct ChainLayout {
-  size_t partials, gathers, pending, units, counters, total;
+  size_t partials, pending, units, counters, total;
 };
 
-static int units_for(int V, int kper) {
-  const int span = kThreads * kper;
-  return (V + span - 1) / span;
-}
+static int units_for(int V, int span) { return (V + span - 1) / span; }
 
-// Sized for the largest draw-unit count (scalar path: kThreads logits per unit).
+// Sized for the largest draw-unit count (the smallest unit span).
 static ChainLayout chain_layout(int B, int gamma, int V) {
   ChainLayout L{};
   const size_t nchunk = static_cast<size_t>(row_chunks(V));
   const size_t R = 2 * static_cast<size_t>(gamma) + 1;
-  const size_t nunit = static_cast<size_t>(units_for(V, 1));
+  const size_t nunit = static_cast<size_t>(units_for(V, kUnitSpan));
   size_t off = 0;
-  L.partials = off; off = align_up(off + static_cast<size_t>(B) * R * nchunk * sizeof(RowPartial));
-  L.gathers = off;  off = align_up(off + static_cast<size_t>(B) * R * sizeof(float));
+  L.partials = off; off = align_up(off + static_cast<size_t>(B) * R * nchunk * sizeof(uint64_t));
   L.pending = off;  off = align_up(off + static_cast<size_t>(B) * sizeof(PendingWire));
   L.units = off;    off = align_up(off + static_cast<size_t>(B) * nunit * sizeof(UnitRec));
   L.counters = off; off = align_up(off + static_cast<size_t>(B) * kCounterStride * sizeof(uint32_t));
@@ -967,8 +988,10 @@ static ChainLayout chain_layout(int B, int gamma, int V) {
   return L;
 }
 
-// Grids of launch 2 in its split form are capped; their workgroups stride.
+// Largest grid of any launch; larger work runs in the three-launch form.
 constexpr long long kMaxGrid = 1 << 20;
+// Workgroups of the unit pool (at most; fewer when the batch has fewer tasks).
+constexpr long long kUnitPool = 16384;
 
 // Workgroups of chain_stream that fit on the current device at once.
 template <int DT, bool VEC>
@@ -986,8 +1009,9 @@ static long long stream_capacity() {
   return cached[dev];
 }
 
-// Test hook: a positive value in this environment variable caps every grid
-// at that many workgroups and selects the split form of launch 2.
+// Test hooks: a positive value in SV_CHAIN_TEST_GRID_CAP caps every grid at
+// that many workgroups and selects the three-launch form; SV_CHAIN_SPLIT
+// selects the three-launch form alone.
 static long long test_grid_cap() {
   const char* v = getenv("SV_CHAIN_TEST_GRID_CAP");
   return v ? atoll(v) : 0;
@@ -995,27 +1019,24 @@ static long long test_grid_cap() {
 
 template <int DT, bool VEC>
 static int launch_chain(ChainArgs a, hipStream_t stream) {
-  const long long items = static_cast<long long>(a.B) * (2 * a.gamma + 1) * a.nchunk;
-  a.nunit = units_for(a.V, UnitSlice<DT, VEC>::kPer * kUnitItems);
+  a.nunit = units_for(a.V, Unit<DT, VEC>::kSpan);
+  a.nstream = static_cast<long long>(a.B) * (2 * a.gamma + 1) * a.nchunk;
   const long long units = static_cast<long long>(a.B) * a.nunit;
+  const long long pool = units < kUnitPool ? units : kUnitPool;
   const long long cap = test_grid_cap();
-  long long sg = stream_capacity<DT, VEC>();
-  if (cap > 0 && cap < sg) sg = cap;
-  if (getenv("SV_CHAIN_STREAM_PERSISTENT") != nullptr || items > kMaxGrid || cap > 0)
-    launch(SV_K_CHAIN_STREAM, chain_stream<DT, VEC>, dim3(static_cast<unsigned>(items < sg ? items : sg)),
-           dim3(kThreads), 0, stream, a);
-  else
-    launch(SV_K_CHAIN_STREAM, chain_stream_once<DT, VEC>, dim3(static_cast<unsigned>(items)), dim3(kOnceThreads), 0,
-           stream, a);
-  if (cap <= 0 && a.B + units <= kMaxGrid) {
-    launch(SV_K_CHAIN_DRAW, chain_draw<DT, VEC>, dim3(static_cast<unsigned>(a.B + units)), dim3(kThreads), 0,
-           stream, a);
+  const long long fused = a.nstream + a.B + pool;
+  if (cap <= 0 && getenv("SV_CHAIN_SPLIT") == nullptr && fused <= kMaxGrid) {
+    launch(SV_K_CHAIN_VERIFY, chain_verify<DT, VEC>, dim3(static_cast<unsigned>(fused)), dim3(kWave), 0, stream, a);
   } else {
+    long long sg = stream_capacity<DT, VEC>();
+    if (cap > 0 && cap < sg) sg = cap;
     const long long g = cap > 0 ? cap : kMaxGrid;
-    launch(SV_K_CHAIN_DECIDE, chain_decide<DT>, dim3(static_cast<unsigned>(a.B < g ? a.B : g)), dim3(kThreads), 0,
-           stream, a);
-    launch(SV_K_CHAIN_UNITS, chain_units<DT, VEC>, dim3(static_cast<unsigned>(units < g ? units : g)),
+    launch(SV_K_CHAIN_STREAM, chain_stream<DT, VEC>, dim3(static_cast<unsigned>(a.nstream < sg ? a.nstream : sg)),
            dim3(kThreads), 0, stream, a);
+    launch(SV_K_CHAIN_DECIDE, chain_decide<DT>, dim3(static_cast<unsigned>(a.B < g ? a.B : g)), dim3(kWave), 0,
+           stream, a);
+    launch(SV_K_CHAIN_UNITS, chain_units<DT, VEC>, dim3(static_cast<unsigned>(units < g ? units : g)), dim3(kWave),
+           0, stream, a);
   }
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
@@ -1060,8 +1081,7 @@ extern "C" int spec_verify_chain(const void* target_logits, const void* draft_lo
   a.nchunk = row_chunks(V);
   a.out_tokens = out_tokens;
   a.out_n = out_num_accepted;
-  a.partials = reinterpret_cast<RowPartial*>(ws + L.partials);
-  a.gathers = reinterpret_cast<float*>(ws + L.gathers);
+  a.partials = reinterpret_cast<uint64_t*>(ws + L.partials);
   a.pending = reinterpret_cast<PendingWire*>(ws + L.pending);
   a.units = reinterpret_cast<UnitRec*>(ws + L.units);
   a.counters = reinterpret_cast<uint32_t*>(ws + L.counters);

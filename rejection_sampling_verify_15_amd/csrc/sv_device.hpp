@@ -231,6 +231,15 @@ struct RawSlice {
     }
   }
 
+  // Moves group j + 1 to group j (the last group keeps its words): a loop
+  // that works on group 0 and shifts stays in registers without unrolling.
+  __device__ inline void shift() {
+#pragma unroll
+    for (int j = 0; j + 1 < ITEMS; ++j)
+#pragma unroll
+      for (int q = 0; q < (VEC ? 4 : 1); ++q) w[j][q] = w[j + 1][q];
+  }
+
   // Element e of group j as float (no range check).
   __device__ inline float at(int j, int e) const {
     if constexpr (VEC) {

@@ -51,7 +51,7 @@ def test_status_strings(lib):
 
 def test_kernel_names_and_timing_validation(lib):
     names = [lib.sv_kernel_name(k).decode() for k in range(binding.SV_K_COUNT)]
-    assert names[0] == "chain_stream" and len(set(names)) == binding.SV_K_COUNT
+    assert names[0] == "chain_verify" and len(set(names)) == binding.SV_K_COUNT
     assert lib.sv_kernel_name(-1) == b"unknown" and lib.sv_kernel_name(binding.SV_K_COUNT) == b"unknown"
     assert lib.sv_timing_begin(0) == sv.SV_ERR_SHAPE
     assert lib.sv_timing_begin((1 << 20) + 1) == sv.SV_ERR_SHAPE
