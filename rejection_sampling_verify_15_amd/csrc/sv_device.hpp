@@ -122,64 +122,36 @@ struct Slice {
 // ---------------------------------------------------------------------------
 constexpr double kLog2e = 0x1.71547652b82fep+0;
 
-// 2^t for t <= 0 (t = -inf gives 0), relative error about 3e-13 for results
-// above 2^-1022 (below, the denormal result is rounded by the final scaling).
-// t = n + f with n an integer (rounded by adding and subtracting 1.5 * 2^52)
-// and |f| <= 1/2; 2^f = e^(f ln 2) by its Taylor series to degree 10
-// (truncation below 3.1e-13); then the result is scaled by 2^n.
-__host__ __device__ inline double exp2_nonpos(double t_in) {
-  constexpr double kShift = 0x1.8p52;
-  const double t = __builtin_fmax(t_in, -1100.0);  // -inf -> 2^-1100 -> 0
-  const double sh = t + kShift;
-  const double n = sh - kShift;
-  const double f = t - n;
-  double p = 0x1.e4cf5158b8ecap-28;          // ln2^10 / 10!
-  p = __builtin_fma(p, f, 0x1.b5253d395e7c4p-24);
-  p = __builtin_fma(p, f, 0x1.62c0223a5c824p-20);
-  p = __builtin_fma(p, f, 0x1.ffcbfc588b0c7p-17);
-  p = __builtin_fma(p, f, 0x1.430912f86c787p-13);
-  p = __builtin_fma(p, f, 0x1.5d87fe78a6731p-10);
-  p = __builtin_fma(p, f, 0x1.3b2ab6fba4e77p-7);
-  p = __builtin_fma(p, f, 0x1.c6b08d704a0c0p-5);
-  p = __builtin_fma(p, f, 0x1.ebfbdff82c58fp-3);
-  p = __builtin_fma(p, f, 0x1.62e42fefa39efp-1);  // ln2
-  p = __builtin_fma(p, f, 1.0);
-  struct Words { uint32_t lo, hi; };
-  const int ni = static_cast<int>(__builtin_bit_cast(Words, sh).lo);  // n, two's complement
-  return __builtin_ldexp(p, ni);
-}
-
-// e^y for y <= 0.
-__host__ __device__ inline double exp_nonpos(double y) { return exp2_nonpos(y * kLog2e); }
-
 // 2^(j/64) for j = 0..63, held in LDS by the workgroups that use exp2_tab.
 struct Exp2Table {
   double v[64];
 };
 
+// Entry j of the table: 2^(j/64) = sqrt(2) * 2^f with f = j/64 - 1/2, 2^f by
+// the Taylor series of e^(f ln 2) carried to degree 14 (truncation below 1e-18
+// on |f| <= 1/2).
+__host__ __device__ inline double exp2_table_entry(int j) {
+  const double f = j / 64.0 - 0.5;
+  constexpr double kLn2 = 0x1.62e42fefa39efp-1;
+  double p = 1.0, term = 1.0;
+  for (int i = 1; i <= 14; ++i) {
+    term *= f * kLn2 / i;
+    p += term;
+  }
+  return p * 0x1.6a09e667f3bcdp+0;  // sqrt(2)
+}
+
 // Fills the table, one entry per thread of the first wave (the caller
-// synchronises before use).  Entries come from the same reduction as
-// exp2_nonpos with the Taylor series carried to degree 14 (truncation below
-// 1e-18 on |f| <= 1/2).
+// synchronises before use).
 __device__ inline void exp2_table_init(Exp2Table& tab) {
   const int j = threadIdx.x;
-  if (j < 64) {
-    const double f = j / 64.0 - 0.5;  // 2^(j/64) = 2^0.5 * 2^f
-    double p = 1.0, term = 1.0;
-    constexpr double kLn2 = 0x1.62e42fefa39efp-1;
-#pragma unroll
-    for (int i = 1; i <= 14; ++i) {
-      term *= f * kLn2 / i;
-      p += term;
-    }
-    tab.v[j] = p * 0x1.6a09e667f3bcdp+0;  // sqrt(2)
-  }
+  if (j < 64) tab.v[j] = exp2_table_entry(j);
 }
 
 // 2^t for t <= 0 (t = -inf gives 0) from the table: t = n + j/64 + f with
 // n, j integers (j in [0, 64)) and |f| <= 1/128; 2^f by its Taylor series to
 // degree 5 (truncation below 4e-17); the product is scaled by 2^n.
-__device__ inline double exp2_tab(double t_in, const Exp2Table& tab) {
+__host__ __device__ inline double exp2_tab(double t_in, const Exp2Table& tab) {
   constexpr double kShift = 0x1.8p52;
   const double t = __builtin_fmax(t_in, -1100.0);
   const double sh = __builtin_fma(t, 64.0, kShift);  // round(64 t) in the low word

@@ -1,0 +1,36 @@
+"""Host checks of the device math the kernels share (no GPU needed).
+
+The final draw's weights use the table-based fp64 exponential exp2_tab; its
+error bound is pinned here against long-double exp2l, compiled from the same
+header the kernels include."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(ROOT, "rejection_sampling_verify_15_amd", "csrc")
+
+
+def _hipcc():
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    return None
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc is needed to build the host check")
+def test_table_exp2_error_bound(tmp_path):
+    exe = tmp_path / "exp2_table_check"
+    cmd = [_hipcc(), "-O2", "-std=c++17", "-I", CSRC, "-I", os.path.join(ROOT, "include"),
+           "-o", str(exe), os.path.join(HERE, "exp2_table_check.cpp")]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    vals = dict(zip(out[0::2], out[1::2]))
+    assert vals["zero_ok"] == "1"
+    assert int(vals["count"]) > 5_000_000
+    # degree-5 Taylor on |f| <= 1/128 truncates below 4e-17; table entries and
+    # the Horner steps add a few ulps
+    assert float(vals["max_rel"]) < 1.5e-15, vals
