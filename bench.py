@@ -1,6 +1,6 @@
 """Benchmark of the chain verification step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 Workload: the batched chain verification, B=64 requests, gamma=4, V=128256,
 bf16 logits; even requests sample at T=0.7, odd requests are greedy (draft
@@ -12,6 +12,11 @@ than the 256 MB Infinity Cache.
 Prints one JSON line: verified (request x position) rows per second, the
 achieved algorithmic HBM bandwidth against the 8 TB/s peak, and the fp64
 oracle timed on this host's cores on a bounded sample.
+
+Other workloads (--workload) report the same line for the single-request
+latency case (B=1, V=32000, also replayed from a HIP graph), the deep case
+(B=256, gamma=8, V=151936, Zipf logits) and the token-tree cases (B=32, 64
+nodes, greedy or naive sampling; rows are node rows).
 """
 from __future__ import annotations
 
@@ -101,13 +106,250 @@ def cpu_baseline(ci, budget_s: float = 15.0):
                       f"fresh uniforms, numpy fp64, {wall:.1f} s wall, {cpu:.1f} s CPU"}
 
 
+WORKLOADS = ("batched", "single", "deep", "tree-greedy", "tree-sampling")
+
+
+def percentiles(xs):
+    xs = np.sort(np.asarray(xs, dtype=np.float64))
+    return {f"p{q}": float(np.percentile(xs, q)) for q in (10, 50, 90, 99)}
+
+
+def time_calls(torch, stream, step, k):
+    """The timed region: k calls between two events (ms), and the host time
+    spent enqueueing them (us per call)."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    h0 = time.perf_counter()
+    for i in range(k):
+        step(i)
+    host_us = 1e6 * (time.perf_counter() - h0) / k
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b), host_us
+
+
+def per_call_us(torch, stream, step, k):
+    """Device time of each call from an event recorded between consecutive
+    calls (the events add a little to each)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(k):
+        step(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [1e3 * ev[i].elapsed_time(ev[i + 1]) for i in range(k)]
+
+
+def chain_case(name, synth):
+    if name == "batched":
+        return synth.batched_chain(), ("batched chain verify: B=64, gamma=4, V=128256, bf16 logits, "
+                                       "even requests sample at T=0.7, odd requests greedy")
+    if name == "single":
+        return synth.single_chain(), ("single-request chain verify: B=1, gamma=4, V=32000, bf16 logits, "
+                                      "T=1, fixed logits with fresh uniforms every call (latency)")
+    return synth.deep_chain(), ("deep chain verify: B=256, gamma=8, V=151936, bf16 Zipf logits, T=1")
+
+
+def run_chain(args, torch, synth, sv):
+    dev = torch.device("cuda:0")
+    ci, desc = chain_case(args.workload, synth)
+    set_bytes = ci.target.nbytes + ci.draft.nbytes
+    # the single-request case is latency-bound and meant to run from cache;
+    # the others rotate over enough copies to read past the Infinity Cache
+    R = 1 if args.workload == "single" else max(2, math.ceil(2 * MALL_BYTES / set_bytes) + 1)
+
+    def dl(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    tgt0, drf0 = dl(ci.target), dl(ci.draft)
+    sets = [(tgt0, drf0)] + [(tgt0.clone(), drf0.clone()) for _ in range(R - 1)]
+    tok = torch.from_numpy(ci.draft_tokens.astype(np.int32)).to(dev)
+    n_u = 64 if args.workload == "single" else 1
+    u_sets = [torch.from_numpy(ci.uniforms if j == 0 else ci.fresh_uniforms(50_000 + j)).to(dev) for j in range(n_u)]
+    T = torch.from_numpy(ci.temperature).to(dev)
+    out_t = torch.empty((ci.B, ci.gamma + 1), dtype=torch.int32, device=dev)
+    out_n = torch.empty((ci.B,), dtype=torch.int32, device=dev)
+    ws = sv.workspace(sv.lib().sv_chain_workspace_bytes(ci.B, ci.gamma, ci.V, sv.SV_BF16), dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        t, d = sets[i % R]
+        sv.verify_chain(t, d, tok, u_sets[i % n_u], T, out_tokens=out_t, out_num_accepted=out_n, ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    total_ms, host_us = time_calls(torch, stream, step, args.steps)
+    # the same steps again with a pair of events attached to every kernel
+    # dispatch: per-kernel durations (the attached events add a few
+    # microseconds between launches, so the whole-call figure comes from the
+    # region above)
+    with sv.KernelTimer(4 * args.steps) as kt:
+        events_ms, _ = time_calls(torch, stream, step, args.steps)
+    calls = per_call_us(torch, stream, step, min(args.steps, 2000))
+
+    rows = ci.B * (ci.gamma + 1)
+    rd, sm = read_bytes(ci), small_bytes(ci)
+    call_us = 1e3 * total_ms / args.steps
+    dominant = "chain_verify"
+    k_us = kt.mean_us(dominant)
+    achieved = rd / (k_us * 1e-6) / 1e9
+    result = head(args, rows * args.steps / (total_ms * 1e-3), total_ms,
+                  {"workload": desc, "B": ci.B, "gamma": ci.gamma, "V": ci.V, "rotating_input_sets": R})
+    result.update({
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": stored_traffic(dominant) if args.workload == "batched" else None,
+                     "kernel": dominant, "kernel_us": k_us, "algorithmic_bytes": rd},
+        "kernels_us": {name: kt.mean_us(name) for name in kt.launches},
+        "whole_call": {"us": call_us, "us_with_kernel_events": 1e3 * events_ms / args.steps,
+                       "per_call_us": percentiles(calls), "host_enqueue_us": host_us,
+                       "algorithmic_bytes": rd + sm,
+                       "GBps": (rd + sm) / (call_us * 1e-6) / 1e9,
+                       "frac": (rd + sm) / (call_us * 1e-6) / 1e9 / PEAK_HBM_GBPS},
+    })
+    if args.workload == "single":
+        result["graph_replay"] = graph_replay(torch, stream, sv, sets[0], tok, u_sets[0], T, out_t, out_n, ws,
+                                              args.steps)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(ci)
+    return result
+
+
+def graph_replay(torch, stream, sv, tgt_drf, tok, u, T, out_t, out_n, ws, steps):
+    """Latency of one call captured in a HIP graph and replayed: per replay
+    device time (events between replays); the first replay's outputs are
+    checked against an eager call."""
+    t, d = tgt_drf
+    sv.verify_chain(t, d, tok, u, T, out_tokens=out_t, out_num_accepted=out_n, ws=ws)
+    torch.cuda.synchronize()
+    eager = (out_t.clone(), out_n.clone())
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            sv.verify_chain(t, d, tok, u, T, out_tokens=out_t, out_num_accepted=out_n, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(eager[0], out_t) and torch.equal(eager[1], out_n))
+    k = min(steps, 2000)
+    times = per_call_us(torch, torch.cuda.current_stream(), lambda i: g.replay(), k)
+    return {"per_call_us": percentiles(times), "replays": k, "matches_eager": same}
+
+
+def run_tree(args, torch, synth, sv, oracle_sample=True):
+    dev = torch.device("cuda:0")
+    temp = 0.0 if args.workload == "tree-greedy" else 1.0
+    ti = synth.tree_inputs(temperature=temp)
+    desc = (f"token-tree verify ({'greedy' if temp == 0 else 'naive sampling, T=1'}): B=32, N=64 nodes, "
+            f"depth <= 8, branching 1..4, V=128256, bf16 logits")
+    R = max(2, math.ceil(2 * MALL_BYTES / ti.logits.nbytes) + 1)
+    lg0 = torch.from_numpy(np.ascontiguousarray(ti.logits).view(np.int16)).to(dev).view(torch.bfloat16)
+    sets = [lg0] + [lg0.clone() for _ in range(R - 1)]
+    tok = torch.from_numpy(ti.node_tokens).to(dev)
+    par = torch.from_numpy(ti.parents).to(dev)
+    u = torch.from_numpy(ti.uniforms).to(dev)
+    T = torch.from_numpy(ti.temperature).to(dev)
+    ws = sv.workspace(sv.lib().sv_tree_workspace_bytes(ti.B, ti.N, ti.V, sv.SV_BF16), dev)
+    stream = torch.cuda.current_stream(dev)
+    outs = {}
+
+    def step(i):
+        outs["r"] = sv.verify_tree(sets[i % R], tok, par, u, T, ti.max_depth, ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    total_ms, host_us = time_calls(torch, stream, step, args.steps)
+    with sv.KernelTimer(64 * args.steps) as kt:
+        events_ms, _ = time_calls(torch, stream, step, args.steps)
+    calls = per_call_us(torch, stream, step, min(args.steps, 2000))
+    nacc = outs["r"][2].cpu().numpy()
+    visited = int(np.sum(nacc + 1))  # the root and every accepted node are read
+    es = 2
+    rd = visited * ti.V * es
+    call_us = 1e3 * total_ms / args.steps
+    per_call = {name: kt.ms[name] * 1e3 / args.steps for name in kt.launches}
+    dominant = max(per_call, key=per_call.get)
+    node_us = per_call.get("tree_node_pass", 0.0)
+    achieved = rd / (node_us * 1e-6) / 1e9 if node_us > 0 else 0.0
+    result = head(args, ti.B * ti.N * args.steps / (total_ms * 1e-3), total_ms,
+                  {"workload": desc, "B": ti.B, "N": ti.N, "V": ti.V, "max_depth": ti.max_depth,
+                   "rotating_input_sets": R, "visited_nodes_per_call": visited})
+    result.update({
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "kernel": "tree_node_pass",
+                     "kernel_us_per_call": node_us, "algorithmic_bytes": rd,
+                     "note": "bytes of the visited nodes' rows per call over the summed duration of "
+                             "that call's tree_node_pass launches"},
+        "kernels_us_per_call": per_call,
+        "launches_per_call": {name: kt.launches[name] / args.steps for name in kt.launches},
+        "whole_call": {"us": call_us, "us_with_kernel_events": 1e3 * events_ms / args.steps,
+                       "per_call_us": percentiles(calls), "host_enqueue_us": host_us,
+                       "algorithmic_bytes": rd, "GBps": rd / (call_us * 1e-6) / 1e9,
+                       "frac": rd / (call_us * 1e-6) / 1e9 / PEAK_HBM_GBPS},
+    })
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_tree(ti)
+    return result
+
+
+def cpu_baseline_tree(ti, budget_s: float = 15.0):
+    """The oracle's tree verification on the same batch, request by request,
+    until the budget is spent; the unit is node rows per second."""
+    import oracle
+    rows = requests = 0
+    w0 = time.perf_counter()
+    c0 = time.process_time()
+    while time.perf_counter() - w0 < budget_s:
+        for b in range(ti.B):
+            oracle.verify_tree(ti.logits[b:b + 1], ti.node_tokens[b:b + 1], ti.parents[b:b + 1],
+                               ti.uniforms[b:b + 1], ti.temperature[b:b + 1], ti.dtype, ti.max_depth)
+            rows += ti.N
+            requests += 1
+            if time.perf_counter() - w0 >= budget_s:
+                break
+    wall = time.perf_counter() - w0
+    cpu = time.process_time() - c0
+    return {"value": rows / wall, "unit": "rows/s", "cores": max(1, round(cpu / wall)), "kind": "oracle",
+            "sample": f"{requests} tree verifications ({rows} node rows) of the same batch, numpy fp64, "
+                      f"{wall:.1f} s wall, {cpu:.1f} s CPU"}
+
+
+def head(args, value, total_ms, config):
+    return {
+        "metric": METRIC,
+        "value": value,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": config,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed calls (default 200; 10000 for the single-request workload)")
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", choices=WORKLOADS, default="batched",
+                    help="batched is the headline; the others are reported alongside it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 10000 if args.workload == "single" else 200
     if args.gpus != 1:
         print("bench.py measures one GPU only: requests shard across GPUs with no exchange, so a "
               "multi-GPU figure is N independent copies of this one", file=sys.stderr)
@@ -119,86 +361,10 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
-    dev = torch.device("cuda:0")
-    ci = synth.batched_chain()
-    set_bytes = ci.target.nbytes + ci.draft.nbytes
-    R = max(2, math.ceil(2 * MALL_BYTES / set_bytes) + 1)
-
-    def dl(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-    tgt0, drf0 = dl(ci.target), dl(ci.draft)
-    sets = [(tgt0, drf0)] + [(tgt0.clone(), drf0.clone()) for _ in range(R - 1)]
-    tok = torch.from_numpy(ci.draft_tokens.astype(np.int32)).to(dev)
-    u = torch.from_numpy(ci.uniforms).to(dev)
-    T = torch.from_numpy(ci.temperature).to(dev)
-    out_t = torch.empty((ci.B, ci.gamma + 1), dtype=torch.int32, device=dev)
-    out_n = torch.empty((ci.B,), dtype=torch.int32, device=dev)
-    ws = sv.workspace(sv.lib().sv_chain_workspace_bytes(ci.B, ci.gamma, ci.V, sv.SV_BF16), dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step(i):
-        t, d = sets[i % R]
-        sv.verify_chain(t, d, tok, u, T, out_tokens=out_t, out_num_accepted=out_n, ws=ws)
-
-    def timed(k):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for i in range(k):
-            step(i)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # the timed region
-    total_ms = timed(args.steps)
-    # the same steps again with a pair of events attached to every kernel
-    # dispatch: per-kernel durations (the attached events themselves add a few
-    # microseconds between launches, so the whole-call figure comes from the
-    # region above)
-    with sv.KernelTimer(4 * args.steps) as kt:
-        events_ms = timed(args.steps)
-
-    ms_per_step = total_ms / args.steps
-    rows = ci.B * (ci.gamma + 1)
-    rd, sm = read_bytes(ci), small_bytes(ci)
-    call_us = 1e3 * ms_per_step
-    dominant = "chain_verify"
-    k_us = kt.mean_us(dominant)
-    achieved = rd / (k_us * 1e-6) / 1e9
-    traffic = stored_traffic(dominant)
-
-    result = {
-        "metric": METRIC,
-        "value": rows * args.steps / (total_ms * 1e-3),
-        "unit": "rows/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "batched chain verify: B=64, gamma=4, V=128256, bf16 logits, "
-                               "even requests sample at T=0.7, odd requests greedy",
-                   "B": ci.B, "gamma": ci.gamma, "V": ci.V, "rotating_input_sets": R},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "kernel": dominant, "kernel_us": k_us, "algorithmic_bytes": rd},
-        "kernels_us": {name: kt.mean_us(name) for name in kt.launches},
-        "whole_call": {"us": call_us, "us_with_kernel_events": 1e3 * events_ms / args.steps,
-                       "algorithmic_bytes": rd + sm,
-                       "GBps": (rd + sm) / (call_us * 1e-6) / 1e9,
-                       "frac": (rd + sm) / (call_us * 1e-6) / 1e9 / PEAK_HBM_GBPS},
-    }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(ci)
+    if args.workload.startswith("tree"):
+        result = run_tree(args, torch, synth, sv)
+    else:
+        result = run_chain(args, torch, synth, sv)
     print(json.dumps(result), flush=True)
 
 

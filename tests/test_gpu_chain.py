@@ -271,3 +271,43 @@ def test_three_launch_form_batched(monkeypatch, batched):
     workload."""
     monkeypatch.setenv("SV_CHAIN_SPLIT", "1")
     parity(batched, 20, label="three launches, batched")
+
+
+def test_graph_capture_replays_match_eager():
+    """One call captured in a HIP graph and replayed several times, with eager
+    calls (on other uniforms) and synchronisations between the replays: every
+    replay gives the eager result for the captured inputs, and the shared
+    workspace stays zero."""
+    ci = synth.single_chain()
+    dev = torch.device("cuda")
+    tgt = to_device_logits(ci.target, ci.dtype)
+    drf = to_device_logits(ci.draft, ci.dtype)
+    tok = to_device(ci.draft_tokens.astype(np.int32))
+    T = to_device(ci.temperature)
+    u0 = to_device(ci.uniforms)
+    need = sv.lib().sv_chain_workspace_bytes(ci.B, ci.gamma, ci.V, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    out_t = torch.empty((ci.B, ci.gamma + 1), dtype=torch.int32, device=dev)
+    out_n = torch.empty((ci.B,), dtype=torch.int32, device=dev)
+    sv.verify_chain(tgt, drf, tok, u0, T, out_tokens=out_t, out_num_accepted=out_n, ws=ws)
+    torch.cuda.synchronize()
+    want_t, want_n = out_t.clone(), out_n.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            sv.verify_chain(tgt, drf, tok, u0, T, out_tokens=out_t, out_num_accepted=out_n, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(4):
+        out_t.fill_(-7)
+        out_n.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_t, want_t) and torch.equal(out_n, want_n), f"replay {r}"
+        assert int(ws.count_nonzero()) == 0
+        # eager work on other uniforms between the replays
+        other_t, other_n = sv.verify_chain(tgt, drf, tok, to_device(ci.fresh_uniforms(4242 + r)), T, ws=ws)
+        torch.cuda.synchronize()
+        assert int(other_n.item()) >= 0
