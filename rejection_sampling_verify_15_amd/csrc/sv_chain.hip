@@ -128,6 +128,13 @@ __device__ inline double exp_scaled(float x, float m, double l2t, const Exp2Tabl
   return exp2_tab((static_cast<double>(x) - static_cast<double>(m)) * l2t, tab);
 }
 
+// The same for a whole row: ml2t = m * l2t once per row, then one fused
+// multiply-add per logit.  Rounding ml2t shifts every exponent of the row by
+// the same amount, which the row's own normaliser cancels.
+__device__ inline double exp_row(float x, double ml2t, double l2t, const Exp2Table& tab) {
+  return exp2_tab(__builtin_fma(static_cast<double>(x), l2t, -ml2t), tab);
+}
+
 // Request classes: 0 samples with its draft rows or has gamma == 0 (it has a
 // final draw), 1 is greedy or cannot sample (target rows only), 2 has an
 // invalid temperature.
@@ -671,6 +678,7 @@ __device__ void draw_token(const ChainArgs& a, int b, const Pending& d, const Ex
   const int c0 = unit * U::kSpan;
   const int c1 = min(a.V, c0 + U::kSpan);
   const double l2t = kLog2e / static_cast<double>(d.t);
+  const double mtl = static_cast<double>(d.mt) * l2t, mdl = static_cast<double>(d.md) * l2t;
   const int trow = d.mode == kModeResidual ? d.n : G;
   Raw st, sd;
   st.load(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + trow, a.V), c0, c1);
@@ -687,10 +695,10 @@ __device__ void draw_token(const ChainArgs& a, int b, const Pending& d, const Ex
     if (residual) {
 #pragma unroll
       for (int e = 0; e < Raw::kPer; ++e)
-        wk[e] = fmax(0.0, exp_scaled(st.at(0, e), d.mt, l2t, tab) * rzt - exp_scaled(sd.at(0, e), d.md, l2t, tab) * rzd);
+        wk[e] = fmax(0.0, exp_row(st.at(0, e), mtl, l2t, tab) * rzt - exp_row(sd.at(0, e), mdl, l2t, tab) * rzd);
     } else {
 #pragma unroll
-      for (int e = 0; e < Raw::kPer; ++e) wk[e] = exp_scaled(st.at(0, e), d.mt, l2t, tab);
+      for (int e = 0; e < Raw::kPer; ++e) wk[e] = exp_row(st.at(0, e), mtl, l2t, tab);
     }
     st.shift();
     sd.shift();
@@ -772,6 +780,9 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& 
   UnitRec* rec = a.units + static_cast<size_t>(b) * a.nunit + unit;
   if (draw) {
     const double l2t = kLog2e / static_cast<double>(d.t);
+    const double mtl = static_cast<double>(d.mt) * l2t, mdl = static_cast<double>(d.md) * l2t;
+    // p > q under the pass-1 normalisers: e_t * zd > e_d * zt, i.e. e_t > e_d * zt / zd
+    const double ratio = d.zt / d.zd;
     const int c0 = unit * U::kSpan;
     const int c1 = min(a.V, c0 + U::kSpan);
     const bool residual = d.mode == kModeResidual;
@@ -788,11 +799,11 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& 
       for (int j = 0; j < Raw::kItems; ++j) {
 #pragma unroll
         for (int e = 0; e < Raw::kPer; ++e) {
-          const double et = exp_scaled(st.at(0, e), d.mt, l2t, tab);
-          const double ed = exp_scaled(sd.at(0, e), d.md, l2t, tab);
+          const double et = exp_row(st.at(0, e), mtl, l2t, tab);
+          const double ed = exp_row(sd.at(0, e), mdl, l2t, tab);
           all_t += et;
           all_d += ed;
-          if (et * d.zd > ed * d.zt) {  // p > q under the pass-1 normalisers
+          if (et > ed * ratio) {
             pos_t += et;
             pos_d += ed;
           }
@@ -804,7 +815,7 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& 
 #pragma unroll 1
       for (int j = 0; j < Raw::kItems; ++j) {
 #pragma unroll
-        for (int e = 0; e < Raw::kPer; ++e) all_t += exp_scaled(st.at(0, e), d.mt, l2t, tab);
+        for (int e = 0; e < Raw::kPer; ++e) all_t += exp_row(st.at(0, e), mtl, l2t, tab);
         st.shift();
       }
     }
@@ -840,15 +851,23 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& 
 // A pool of `count` workgroups (this one is number `w`) strides over the unit
 // tasks (drawing request, unit) in request order, so greedy requests take no
 // workgroups and each task waits only for its own request's decision.
+// The caller's LDS table is filled here, once the workgroup is known to have
+// work.
 template <int DT, bool VEC>
-__device__ void unit_pool(const ChainArgs& a, long long w, long long count, const Exp2Table& tab) {
+__device__ void unit_pool(const ChainArgs& a, long long w, long long count, Exp2Table& tab) {
   if (a.B <= kRankMaxBatch) {
     const DrawingSet ds = drawing_requests(a);
     const long long tasks = static_cast<long long>(ds.count) * a.nunit;
+    if (w >= tasks) return;
+    exp2_table_init(tab);
+    __syncthreads();
     for (long long t = w; t < tasks; t += count)
       unit_work<DT, VEC>(a, nth_drawing(ds, static_cast<int>(t / a.nunit)), static_cast<int>(t % a.nunit), tab);
   } else {
     const long long tasks = static_cast<long long>(a.B) * a.nunit;
+    if (w >= tasks) return;
+    exp2_table_init(tab);
+    __syncthreads();
     for (long long t = w; t < tasks; t += count) {
       const int b = static_cast<int>(t / a.nunit);
       if (request_class(a, a.temperature[b]) == 0) unit_work<DT, VEC>(a, b, static_cast<int>(t % a.nunit), tab);
@@ -881,8 +900,6 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(6))) void
     decide_request<DT>(a, b, tab);
     return;
   }
-  exp2_table_init(tab);
-  __syncthreads();
   unit_pool<DT, VEC>(a, blk - nseg, static_cast<long long>(gridDim.x) - nseg, tab);
 }
 
@@ -959,8 +976,6 @@ __global__ __launch_bounds__(kWave) void chain_decide(ChainArgs a) {
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void chain_units(ChainArgs a) {
   __shared__ Exp2Table tab;
-  exp2_table_init(tab);
-  __syncthreads();
   unit_pool<DT, VEC>(a, blockIdx.x, gridDim.x, tab);
 }
 

@@ -31,6 +31,6 @@ def test_table_exp2_error_bound(tmp_path):
     vals = dict(zip(out[0::2], out[1::2]))
     assert vals["zero_ok"] == "1"
     assert int(vals["count"]) > 5_000_000
-    # degree-5 Taylor on |f| <= 1/128 truncates below 4e-17; table entries and
-    # the Horner steps add a few ulps
-    assert float(vals["max_rel"]) < 1.5e-15, vals
+    # degree-4 Taylor on |f| <= 1/128 truncates below 4e-14 (the inverse-CDF
+    # draw needs about 1e-10); table entries and the Horner steps add ulps
+    assert float(vals["max_rel"]) < 5e-14, vals
