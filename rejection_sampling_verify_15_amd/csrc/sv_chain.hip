@@ -105,6 +105,7 @@ struct ChainArgs {
   const float* temperature;
   int B, gamma, V, nchunk, nunit;
   long long nstream;  // stream items: B * (2 * gamma + 1) * nchunk
+  int per_req;        // stream items of one request: (2 * gamma + 1) * nchunk
   int32_t* out_tokens;
   int32_t* out_n;
   uint64_t* partials;    // [B][2*gamma+1][nchunk] marked (row, chunk) words
@@ -606,6 +607,11 @@ __device__ void draw_token(const ChainArgs& a, int b, const Pending& d, const Ex
         tot[k] += f[q][k];
       }
     }
+    // the records are in registers: return them to zero now, so that the
+    // stores drain while the draw goes on
+    uint64_t* wz = reinterpret_cast<uint64_t*>(a.units + static_cast<size_t>(b) * a.nunit);
+    const int nw = a.nunit * static_cast<int>(sizeof(UnitRec) / 8);
+    for (int i = lane; i < nw; i += kWave) store_coherent(wz + i, 0ull);
   } else {
     for (int i = lane; i < a.nunit; i += kWave)
 #pragma unroll
@@ -720,6 +726,11 @@ __device__ void draw_token(const ChainArgs& a, int b, const Pending& d, const Ex
   hit = wave_min(hit);
   last_pos = wave_max_int(last_pos);
   if (lane == 0) a.out_tokens[static_cast<size_t>(b) * (G + 1) + d.n] = (hit != 0x7fffffff) ? hit : last_pos;
+  if (!cached) {
+    uint64_t* wz = reinterpret_cast<uint64_t*>(a.units + static_cast<size_t>(b) * a.nunit);
+    const int nw = a.nunit * static_cast<int>(sizeof(UnitRec) / 8);
+    for (int i = lane; i < nw; i += kWave) store_coherent(wz + i, 0ull);
+  }
 }
 
 // The drawing requests (class 0) of a batch of at most kRankMaxBatch: lane l
@@ -833,18 +844,17 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& 
   if (lane == 0) old = arrive(a.counters + static_cast<size_t>(b) * kCounterStride + kUnitCounter);
   const bool last = read_lane(static_cast<int>(old), 0) == a.nunit - 1;
   if (last) {
+    // every unit of the request has read the decision and counted in: both
+    // words return to zero before the draw (which returns the records)
+    if (lane < kWireWords) store_coherent(&a.pending[b].w[lane], 0ull);
+    if (lane == 0) store_coherent(a.counters + static_cast<size_t>(b) * kCounterStride + kUnitCounter, 0u);
     if (draw) {
       // the last unit of a request draws while other units may still compute:
       // let its wave issue first on its SIMD
       __builtin_amdgcn_s_setprio(3);
       draw_token<DT, VEC>(a, b, d, tab);
       __builtin_amdgcn_s_setprio(0);
-      uint64_t* wz = reinterpret_cast<uint64_t*>(a.units + static_cast<size_t>(b) * a.nunit);
-      const int nw = a.nunit * static_cast<int>(sizeof(UnitRec) / 8);
-      for (int i = lane; i < nw; i += kWave) store_coherent(wz + i, 0ull);
     }
-    if (lane < kWireWords) store_coherent(&a.pending[b].w[lane], 0ull);
-    if (lane == 0) store_coherent(a.counters + static_cast<size_t>(b) * kCounterStride + kUnitCounter, 0u);
   }
 }
 
@@ -853,24 +863,28 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& 
 // workgroups and each task waits only for its own request's decision.
 // The caller's LDS table is filled here, once the workgroup is known to have
 // work.
+// Task counts fit in 32 bits (B * nunit < 2^31 within the shape limits).
 template <int DT, bool VEC>
-__device__ void unit_pool(const ChainArgs& a, long long w, long long count, Exp2Table& tab) {
+__device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count, Exp2Table& tab) {
+  const uint32_t nunit = static_cast<uint32_t>(a.nunit);
   if (a.B <= kRankMaxBatch) {
     const DrawingSet ds = drawing_requests(a);
-    const long long tasks = static_cast<long long>(ds.count) * a.nunit;
+    const uint32_t tasks = static_cast<uint32_t>(ds.count) * nunit;
     if (w >= tasks) return;
     exp2_table_init(tab);
     __syncthreads();
-    for (long long t = w; t < tasks; t += count)
-      unit_work<DT, VEC>(a, nth_drawing(ds, static_cast<int>(t / a.nunit)), static_cast<int>(t % a.nunit), tab);
+    for (uint32_t t = w; t < tasks; t += count) {
+      const uint32_t p = t / nunit;
+      unit_work<DT, VEC>(a, nth_drawing(ds, static_cast<int>(p)), static_cast<int>(t - p * nunit), tab);
+    }
   } else {
-    const long long tasks = static_cast<long long>(a.B) * a.nunit;
+    const uint32_t tasks = static_cast<uint32_t>(a.B) * nunit;
     if (w >= tasks) return;
     exp2_table_init(tab);
     __syncthreads();
-    for (long long t = w; t < tasks; t += count) {
-      const int b = static_cast<int>(t / a.nunit);
-      if (request_class(a, a.temperature[b]) == 0) unit_work<DT, VEC>(a, b, static_cast<int>(t % a.nunit), tab);
+    for (uint32_t t = w; t < tasks; t += count) {
+      const uint32_t b = t / nunit;
+      if (request_class(a, a.temperature[b]) == 0) unit_work<DT, VEC>(a, static_cast<int>(b), static_cast<int>(t - b * nunit), tab);
     }
   }
 }
@@ -885,22 +899,25 @@ __device__ void unit_pool(const ChainArgs& a, long long w, long long count, Exp2
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(6))) void chain_verify(ChainArgs a) {
   __shared__ Exp2Table tab;
-  const long long blk = blockIdx.x;
-  const long long per_req = a.nstream / a.B;  // stream items of one request
-  const long long nseg = a.nstream + a.B;
+  // 32-bit index arithmetic: this grid has at most kMaxGrid blocks
+  const uint32_t blk = blockIdx.x;
+  const uint32_t seg = static_cast<uint32_t>(a.per_req) + 1u;
+  const uint32_t nseg = static_cast<uint32_t>(a.B) * seg;
   if (blk < nseg) {
-    const int b = static_cast<int>(blk / (per_req + 1));
-    const int rem = static_cast<int>(blk - b * (per_req + 1));
-    if (rem < per_req) {
-      stream_once<DT, VEC>(a, RowItem{b, rem / a.nchunk, rem % a.nchunk});
+    const uint32_t b = blk / seg;
+    const uint32_t rem = blk - b * seg;
+    if (rem < static_cast<uint32_t>(a.per_req)) {
+      const uint32_t k = rem / static_cast<uint32_t>(a.nchunk);
+      stream_once<DT, VEC>(a, RowItem{static_cast<int>(b), static_cast<int>(k),
+                                      static_cast<int>(rem - k * static_cast<uint32_t>(a.nchunk))});
       return;
     }
     exp2_table_init(tab);
     __syncthreads();
-    decide_request<DT>(a, b, tab);
+    decide_request<DT>(a, static_cast<int>(b), tab);
     return;
   }
-  unit_pool<DT, VEC>(a, blk - nseg, static_cast<long long>(gridDim.x) - nseg, tab);
+  unit_pool<DT, VEC>(a, blk - nseg, gridDim.x - nseg, tab);
 }
 
 // Very large shapes: the three parts as three launches.  Persistent
@@ -1036,6 +1053,7 @@ template <int DT, bool VEC>
 static int launch_chain(ChainArgs a, hipStream_t stream) {
   a.nunit = units_for(a.V, Unit<DT, VEC>::kSpan);
   a.nstream = static_cast<long long>(a.B) * (2 * a.gamma + 1) * a.nchunk;
+  a.per_req = (2 * a.gamma + 1) * a.nchunk;
   const long long units = static_cast<long long>(a.B) * a.nunit;
   const long long pool = units < kUnitPool ? units : kUnitPool;
   const long long cap = test_grid_cap();
