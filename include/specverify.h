@@ -220,7 +220,8 @@ typedef enum {
   SV_K_PROBS_RESIDUAL = 8,
   SV_K_PROBS_FINALIZE = 9,
   SV_K_WORKSPACE_CLEAR = 10,
-  SV_K_COUNT = 11
+  SV_K_TREE_VERIFY = 11,      /* tree: every depth step of every request in one launch */
+  SV_K_COUNT = 12
 } sv_kernel;
 
 /* Name of a kernel id (static storage; "unknown" outside [0, SV_K_COUNT)). */

@@ -39,7 +39,7 @@ EXPORTS = {
     "sv_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
                                      ctypes.c_int]),
 }
-SV_K_COUNT = 11
+SV_K_COUNT = 12
 
 _LIB = None
 _LOCK = threading.Lock()

@@ -3,7 +3,23 @@
 // include/specverify.h for the contract.
 //
 // Path descent: only the rows of visited nodes are read (at most max_depth+1
-// per request).  One step per depth level, two launches per step:
+// per request).
+//
+// One launch, `tree_verify`, of one-wave workgroups: an init item per request
+// (validation, outputs, the root as the level-0 node), then for each depth
+// level and each request a run of stream items over 2048-logit chunks of that
+// level's node row -- the chunk max and argmax (greedy), or the chunk max and
+// the fp64 sums of exp((x - max) / T) of each lane's logits (sampling) -- and
+// a choose item, which merges them, picks the token (argmax, or the
+// inverse-CDF draw narrowed chunk -> lane -> logit), looks for the child that
+// carries it and publishes that child as the next level's node, or stops the
+// request.  Every block waits only for lower-numbered blocks.  A chunk word is
+// tagged with its level, so one buffer serves every level without clearing;
+// the items of levels after a request's stop count themselves out on a `done`
+// word and the last of them returns it to zero.
+//
+// Shapes whose grid or chunk count is too large for one launch use the
+// multi-launch form: one step per depth level, two launches per step:
 //   tree_node_pass   one workgroup per (request, chunk) of the current node's
 //                    row: argmax (greedy) or the chunk max and the fp64 sum of
 //                    exp((x - max) / T) (sampling);
@@ -13,6 +29,10 @@
 //                    looks for a child carrying it and either descends or
 //                    emits the token and stops.
 // A request that has stopped costs one early-exiting workgroup per launch.
+#include <stdlib.h>
+
+#include <algorithm>
+
 #include "sv_device.hpp"
 #include "sv_host.hpp"
 
@@ -264,16 +284,472 @@ __global__ __launch_bounds__(kThreads) void tree_choose(TreeArgs a) {
   }
 }
 
-struct TreeLayout {
-  size_t state, partials, total;
+// ---------------------------------------------------------------------------
+// single launch
+// ---------------------------------------------------------------------------
+constexpr int kTreeChunk = 2048;           // logits per stream item
+constexpr int kTreeChunkCache = 4;         // chunk words per lane in a choose item
+constexpr int kTreeMaxChunks = kTreeChunkCache * kWave;
+constexpr int kTreeLevels = SV_MAX_TREE_DEPTH + 1;
+constexpr int kDoneStride = 16;            // 64-bit words per request: one 128-byte line
+constexpr uint64_t kTreeMark = 1ull << 63;
+constexpr uint32_t kTreeSpinLimit = 1u << 22;
+
+struct TreeFused {
+  const void* logits;
+  const int32_t* tokens;
+  const int32_t* parents;
+  const float* uniforms;
+  const float* temperature;
+  int B, N, V, max_depth, nchunk;  // nchunk: chunks of kTreeChunk logits
+  int32_t* out_tokens;
+  int32_t* out_path;
+  int32_t* out_n;
+  uint64_t* state;   // [B][kTreeLevels]: marked node of each level
+  uint64_t* done;    // [B][kDoneStride]: word 0 marked (stop level + 1), word 1 the count of finished levels
+  uint32_t* lcount;  // [B][kTreeLevels]: items of a level after the stop that have seen it
+  uint64_t* chunks;  // [B][nchunk]: level-tagged chunk max (and argmax)
+  double* totals;    // [B][nchunk]: fp64 exp-sum of the chunk relative to its max (sampling)
+  double* lanes;     // [B][nchunk][kWave]: the same per lane (sampling)
 };
+
+// A chunk as one contiguous run of kRun logits per lane (lane l holds
+// [c0 + l * kRun, c0 + (l + 1) * kRun)), so that a lane's sum is one stretch of
+// the chunk's CDF.  Loaded as kItems groups of kPer logits from clamped
+// addresses; groups past the row's end become -inf.
+template <int DT, bool VEC>
+struct LaneRun {
+  static constexpr int kPer = VEC ? Elem<DT>::kVec : 1;
+  static constexpr int kItems = kTreeChunk / (kWave * kPer);
+  static constexpr int kRun = kItems * kPer;
+  uint32_t w[kItems][VEC ? 4 : 1];
+
+  __device__ static inline int index(int c0, int j, int e) {
+    return c0 + static_cast<int>(threadIdx.x) * kRun + j * kPer + e;
+  }
+  __device__ inline void load(const void* row, int c0, int c1) {
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+      const int k0 = index(c0, j, 0);
+      const int k = k0 < c1 ? k0 : c0;
+      if constexpr (VEC) {
+        const uint4 v = Elem<DT>::raw(row, k);
+        w[j][0] = v.x; w[j][1] = v.y; w[j][2] = v.z; w[j][3] = v.w;
+      } else if constexpr (DT == 0) {
+        w[j][0] = static_cast<const uint16_t*>(row)[k];
+      } else {
+        w[j][0] = static_cast<const uint32_t*>(row)[k];
+      }
+    }
+    constexpr uint32_t kNegInf = DT == 0 ? (VEC ? 0xff80ff80u : 0xff80u) : 0xff800000u;
+#pragma unroll
+    for (int j = 0; j < kItems; ++j)
+      if (index(c0, j, 0) >= c1) {
+#pragma unroll
+        for (int q = 0; q < (VEC ? 4 : 1); ++q) w[j][q] = kNegInf;
+      }
+  }
+  __device__ inline float at(int j, int e) const {
+    if constexpr (VEC) {
+      if constexpr (DT == 0) return __uint_as_float((e & 1) ? (w[j][e >> 1] & 0xffff0000u) : (w[j][e >> 1] << 16));
+      else return __uint_as_float(w[j][e]);
+    } else {
+      if constexpr (DT == 0) return __uint_as_float(w[j][0] << 16);
+      else return __uint_as_float(w[j][0]);
+    }
+  }
+};
+
+// [63] mark, [62:56] level + 1, [55:32] argmax (greedy), [31:0] max bits.
+__device__ inline uint64_t tree_chunk_word(int level, float m, int idx) {
+  return kTreeMark | (static_cast<uint64_t>(level + 1) << 56) |
+         (static_cast<uint64_t>(static_cast<uint32_t>(idx) & 0xffffffu) << 32) | __float_as_uint(m);
+}
+__device__ inline bool chunk_at_level(uint64_t w, int level) {
+  return (w >> 56) == (0x80ull | static_cast<uint64_t>(level + 1));
+}
+
+__device__ inline int levels_of(const TreeFused& a) { return a.max_depth + 1; }
+
+template <int DT>
+__device__ inline const void* fused_row(const TreeFused& a, int b, int node) {
+  return static_cast<const char*>(a.logits) +
+         (static_cast<size_t>(b) * a.N + node) * static_cast<size_t>(a.V) * Elem<DT>::kBytes;
+}
+
+// Waits until level d of request b has its node (returned), or the request
+// stopped before level d (-1), or the wait gave up (-2).  A reader that sees
+// the stop counts itself out on its level's counter; the last of a level's
+// nchunk + 1 items counts the level out on the request's counter, and the
+// last level to finish returns the done word to zero.  (Counting in two
+// steps keeps the number of atomics on any one address to nchunk + 1.)
+__device__ int tree_wait_level(const TreeFused& a, int b, int d) {
+  const uint64_t* sw = a.state + static_cast<size_t>(b) * kTreeLevels + d;
+  uint64_t* dw = a.done + static_cast<size_t>(b) * kDoneStride;
+  int node = -2;
+  uint64_t dn = 0;
+  for (uint32_t spin = 0; spin < kTreeSpinLimit; ++spin) {
+    const uint64_t sv = load_coherent(sw);
+    dn = load_coherent(dw);
+    if (sv & kTreeMark) {
+      node = static_cast<int>(static_cast<uint32_t>(sv));
+      break;
+    }
+    if (dn & kTreeMark) {
+      node = -1;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  if (node == -1 && threadIdx.x == 0) {
+    // the levels stop+1 .. max_depth each have nchunk + 1 readers
+    const int stop = static_cast<int>(static_cast<uint32_t>(dn)) - 1;
+    const uint32_t levels = static_cast<uint32_t>(levels_of(a) - 1 - stop);
+    uint32_t* lc = a.lcount + static_cast<size_t>(b) * kTreeLevels + d;
+    if (arrive(lc) == static_cast<uint32_t>(a.nchunk)) {
+      store_coherent(lc, 0u);
+      if (arrive(reinterpret_cast<uint32_t*>(dw + 1)) == levels - 1) {
+        store_coherent(dw, 0ull);
+        store_coherent(dw + 1, 0ull);
+      }
+    }
+  }
+  return node;
+}
+
+// Stops request b at level d (nothing is published when no level follows).
+__device__ inline void tree_publish_stop(const TreeFused& a, int b, int d) {
+  if (d + 1 < levels_of(a) && threadIdx.x == 0)
+    store_coherent(a.done + static_cast<size_t>(b) * kDoneStride,
+                   kTreeMark | static_cast<uint64_t>(static_cast<uint32_t>(d + 1)));
+}
+
+// Init item: validation (as tree_init); a valid request gets the root as its
+// level-0 node, an invalid one its -1 outputs and the stop before level 0.
+// Every output word has exactly one writer in the launch (this item for an
+// invalid request; for a valid one the choose item of each level writes that
+// level's slot and the last one the padding and the count), so no two XCDs'
+// caches ever hold the same output bytes.
+__device__ void tree_fused_init(const TreeFused& a, int b) {
+  __shared__ int32_t s_par[SV_MAX_TREE_NODES];
+  const int lane = threadIdx.x;
+  const int L1 = levels_of(a);
+  const int32_t* par = a.parents + static_cast<size_t>(b) * a.N;
+  const int32_t* tok = a.tokens + static_cast<size_t>(b) * a.N;
+  for (int i = lane; i < a.N; i += kWave) s_par[i] = par[i];
+  __syncthreads();
+  const float T = a.temperature[b];
+  int bad = !tree_temp_ok(T);
+  const bool sampling = !bad && T > 0.0f;
+  for (int i = lane; i < a.N; i += kWave) {
+    if (i == 0) {
+      bad |= (s_par[0] != -1);
+    } else {
+      const int p = s_par[i];
+      bad |= (p < 0 || p >= i);
+      const int32_t t = tok[i];
+      bad |= (t < 0 || t >= a.V);
+      if (p >= 0 && p < i) {
+        int n = i, depth = 0;
+        while (n > 0 && depth <= a.max_depth) {
+          const int q = s_par[n];
+          if (q < 0 || q >= n) { depth = a.max_depth + 1; break; }
+          n = q;
+          ++depth;
+        }
+        bad |= (depth > a.max_depth);
+      }
+    }
+    if (sampling) {
+      const float u = a.uniforms[static_cast<size_t>(b) * a.N + i];
+      bad |= !(u >= 0.0f && u < 1.0f);
+    }
+  }
+  const bool any_bad = __any(bad);
+  if (any_bad) {
+    for (int i = lane; i < L1; i += kWave) {
+      a.out_tokens[static_cast<size_t>(b) * L1 + i] = -1;
+      a.out_path[static_cast<size_t>(b) * L1 + i] = -1;
+    }
+    if (lane == 0) {
+      a.out_n[b] = -1;
+      store_coherent(a.done + static_cast<size_t>(b) * kDoneStride, kTreeMark);  // stopped before level 0
+    }
+  } else if (lane == 0) {
+    store_coherent(a.state + static_cast<size_t>(b) * kTreeLevels, kTreeMark);  // node 0 at level 0
+  }
+}
+
+// Stream item: chunk c of the level-d node row of request b.
+template <int DT, bool VEC>
+__device__ void tree_fused_stream(const TreeFused& a, int b, int d, int c, Exp2Table& tab) {
+  using Raw = LaneRun<DT, VEC>;
+  const float T = a.temperature[b];
+  const int node = tree_wait_level(a, b, d);
+  if (node < 0) return;
+  if (T != 0.0f) {
+    exp2_table_init(tab);
+    __syncthreads();
+  }
+  const int c0 = c * kTreeChunk;
+  const int c1 = min(a.V, c0 + kTreeChunk);
+  Raw raw;
+  raw.load(fused_row<DT>(a, b, node), c0, c1);
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < Raw::kItems; ++j)
+#pragma unroll
+    for (int e = 0; e < Raw::kPer; ++e) m = fmaxf(m, raw.at(j, e));
+  m = wave_max(m);
+  const size_t slot = static_cast<size_t>(b) * a.nchunk + c;
+  if (T == 0.0f) {
+    int idx = 0x7fffffff;
+#pragma unroll
+    for (int j = Raw::kItems - 1; j >= 0; --j)
+#pragma unroll
+      for (int e = Raw::kPer - 1; e >= 0; --e) {
+        const int k = Raw::index(c0, j, e);
+        if (k < c1 && raw.at(j, e) == m) idx = k;
+      }
+    idx = wave_min(idx);
+    if (threadIdx.x == 0) store_coherent(a.chunks + slot, tree_chunk_word(d, m, idx));
+    return;
+  }
+  // sampling: fp64 sums of exp((x - m) / T) per lane and over the chunk
+  const double l2t = kLog2e / static_cast<double>(T);
+  const double ml2t = static_cast<double>(m) * l2t;
+  double sl = 0.0;
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < Raw::kItems; ++j)
+#pragma unroll
+      for (int e = 0; e < Raw::kPer; ++e)
+        sl += exp2_tab(__builtin_fma(static_cast<double>(raw.at(j, e)), l2t, -ml2t), tab);
+  }
+  store_coherent_f64(a.lanes + slot * kWave + threadIdx.x, sl);
+  const double tot = wave_sum(sl);
+  if (threadIdx.x == 0) store_coherent_f64(a.totals + slot, tot);
+  wait_memory();  // the sums are in place before the chunk word announces them
+  if (threadIdx.x == 0) store_coherent(a.chunks + slot, tree_chunk_word(d, m, 0));
+}
+
+// Choose item of level d of request b.
+template <int DT, bool VEC>
+__device__ void tree_fused_choose(const TreeFused& a, int b, int d, Exp2Table& tab) {
+  constexpr int kLaneElems = LaneRun<DT, VEC>::kRun;  // logits per lane of a chunk
+  const int lane = threadIdx.x;
+  const float T = a.temperature[b];
+  const int node = tree_wait_level(a, b, d);
+  if (node < 0) return;
+  const bool greedy = T == 0.0f;
+  if (!greedy) {
+    exp2_table_init(tab);
+    __syncthreads();
+  }
+  const float u = greedy ? 0.0f : a.uniforms[static_cast<size_t>(b) * a.N + node];
+  // the first kWave nodes' parents and tokens, loaded while the chunks finish
+  const int32_t* par = a.parents + static_cast<size_t>(b) * a.N;
+  const int32_t* tk = a.tokens + static_cast<size_t>(b) * a.N;
+  const int32_t my_par = lane < a.N ? par[lane] : -1;
+  const int32_t my_tok = lane < a.N ? tk[lane] : -1;
+  // every chunk word of this level (lane l holds chunks l, l + kWave, ...)
+  uint64_t w[kTreeChunkCache];
+  bool lost = false;
+  for (uint32_t spin = 0;; ++spin) {
+    bool all = true;
+#pragma unroll
+    for (int q = 0; q < kTreeChunkCache; ++q) {
+      const int c = q * kWave + lane;
+      w[q] = c < a.nchunk ? load_coherent(a.chunks + static_cast<size_t>(b) * a.nchunk + c) : 0ull;
+      all = all && (c >= a.nchunk || chunk_at_level(w[q], d));
+    }
+    if (__all(all)) break;
+    if (spin >= kTreeSpinLimit) { lost = true; break; }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  int token;
+  if (greedy) {
+    ArgMax best{-INFINITY, 0x7fffffff};
+#pragma unroll
+    for (int q = 0; q < kTreeChunkCache; ++q)
+      if (q * kWave + lane < a.nchunk)
+        best = argmax_combine(best, ArgMax{__uint_as_float(static_cast<uint32_t>(w[q])),
+                                           static_cast<int>((w[q] >> 32) & 0xffffffu)});
+    token = wave_argmax(best).i;
+  } else {
+    const double l2t = kLog2e / static_cast<double>(T);
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kTreeChunkCache; ++q)
+      if (q * kWave + lane < a.nchunk) m = fmaxf(m, __uint_as_float(static_cast<uint32_t>(w[q])));
+    m = wave_max(m);
+    const double* tp = a.totals + static_cast<size_t>(b) * a.nchunk;
+    double wc[kTreeChunkCache];
+    double Z = 0.0;
+#pragma unroll
+    for (int q = 0; q < kTreeChunkCache; ++q) {
+      const int c = q * kWave + lane;
+      const float mc = __uint_as_float(static_cast<uint32_t>(w[q]));
+      wc[q] = (c < a.nchunk && mc != -INFINITY)
+                  ? load_coherent_f64(tp + c) *
+                        exp2_tab((static_cast<double>(mc) - static_cast<double>(m)) * l2t, tab)
+                  : 0.0;
+      Z += wc[q];
+    }
+    Z = wave_sum(Z);
+    const double target = static_cast<double>(u) * Z;
+    // crossing chunk (the last positive one if rounding leaves u * Z on top)
+    int chunk = -1, last_chunk = -1;
+    double before = 0.0, carry = 0.0;
+#pragma unroll
+    for (int q = 0; q < kTreeChunkCache; ++q) {
+      if (chunk < 0 && q * kWave < a.nchunk) {
+        const double inc = wave_inclusive_sum(wc[q]);
+        const double bef = carry + lane_move<kDppWaveShr1>(inc);
+        const uint64_t pos = __ballot(wc[q] > 0.0);
+        if (pos) last_chunk = q * kWave + 63 - static_cast<int>(__builtin_clzll(pos));
+        const uint64_t hit = __ballot(bef + wc[q] > target && q * kWave + lane < a.nchunk);
+        if (hit) {
+          const int l = static_cast<int>(__builtin_ctzll(hit));
+          chunk = q * kWave + l;
+          before = read_lane(bef, l);
+        }
+        carry += read_lane(inc, kWave - 1);
+      }
+    }
+    if (chunk < 0) {
+      chunk = last_chunk < 0 ? 0 : last_chunk;
+      double bs = 0.0;
+#pragma unroll
+      for (int q = 0; q < kTreeChunkCache; ++q)
+        if (q * kWave + lane < chunk) bs += wc[q];
+      before = wave_sum(bs);
+    }
+    // crossing lane of that chunk: its per-lane sums, rescaled to the row max
+    const uint64_t cw = load_coherent(a.chunks + static_cast<size_t>(b) * a.nchunk + chunk);
+    const float mcs = __uint_as_float(static_cast<uint32_t>(cw));
+    const double scale = mcs != -INFINITY ? exp2_tab((static_cast<double>(mcs) - static_cast<double>(m)) * l2t, tab) : 0.0;
+    const double wl = load_coherent_f64(a.lanes + (static_cast<size_t>(b) * a.nchunk + chunk) * kWave + lane) * scale;
+    int cl = -1;
+    {
+      const double inc = wave_inclusive_sum(wl);
+      const double bef = before + lane_move<kDppWaveShr1>(inc);
+      const uint64_t hit = __ballot(bef + wl > target);
+      if (hit) {
+        cl = static_cast<int>(__builtin_ctzll(hit));
+        before = read_lane(bef, cl);
+      } else {
+        const uint64_t pos = __ballot(wl > 0.0);
+        cl = pos ? 63 - static_cast<int>(__builtin_clzll(pos)) : 0;
+        double bs = lane < cl ? wl : 0.0;
+        before = before + wave_sum(bs);
+      }
+    }
+    // the logits of that lane (lane i takes the i-th of them, in index order)
+    const int c0 = chunk * kTreeChunk;
+    const int c1 = min(a.V, c0 + kTreeChunk);
+    const int k = c0 + cl * kLaneElems + lane;
+    const bool have = lane < kLaneElems && k < c1;
+    const void* row = fused_row<DT>(a, b, node);
+    const double x = have ? static_cast<double>(Elem<DT>::at(row, k)) : 0.0;
+    const double wk = have ? exp2_tab(__builtin_fma(x, l2t, -static_cast<double>(m) * l2t), tab) : 0.0;
+    const double inc = wave_inclusive_sum(wk);
+    const uint64_t hit = __ballot(wk > 0.0 && before + inc > target);
+    const uint64_t pos = __ballot(wk > 0.0);
+    const int li = hit ? static_cast<int>(__builtin_ctzll(hit)) : (pos ? 63 - static_cast<int>(__builtin_clzll(pos)) : 0);
+    token = read_lane(k, li);
+  }
+  // the lowest-index child of the node that carries the token
+  int child = (lane > node && lane < a.N && my_par == node && my_tok == token) ? lane : 0x7fffffff;
+  for (int j = kWave + lane; j < a.N; j += kWave)
+    if (j > node && par[j] == node && tk[j] == token) child = min(child, j);
+  child = wave_min(child);
+  const int L1 = levels_of(a);
+  int32_t* ot = a.out_tokens + static_cast<size_t>(b) * L1;
+  int32_t* op = a.out_path + static_cast<size_t>(b) * L1;
+  if (lane == 0) {
+    store_coherent(a.state + static_cast<size_t>(b) * kTreeLevels + d, 0ull);  // every reader of this level is done
+    ot[d] = lost ? -1 : token;
+  }
+  if (!lost && child != 0x7fffffff) {
+    if (lane == 0) {
+      op[d] = child;
+      store_coherent(a.state + static_cast<size_t>(b) * kTreeLevels + d + 1,
+                     kTreeMark | static_cast<uint64_t>(static_cast<uint32_t>(child)));
+    }
+    return;
+  }
+  // the stop: this level's path slot and every later slot are padding
+  for (int i = d + lane; i < L1; i += kWave) {
+    if (i > d) ot[i] = -1;
+    op[i] = -1;
+  }
+  if (lane == 0) a.out_n[b] = lost ? -1 : d;
+  tree_publish_stop(a, b, d);
+  // the request's chunk words (and sums) back to zero
+  for (int c = lane; c < a.nchunk; c += kWave) store_coherent(a.chunks + static_cast<size_t>(b) * a.nchunk + c, 0ull);
+  if (!greedy) {
+    for (int c = lane; c < a.nchunk; c += kWave) store_coherent_f64(a.totals + static_cast<size_t>(b) * a.nchunk + c, 0.0);
+    uint64_t* lz = reinterpret_cast<uint64_t*>(a.lanes + static_cast<size_t>(b) * a.nchunk * kWave);
+    for (int i = lane; i < a.nchunk * kWave; i += kWave) store_coherent(lz + i, 0ull);
+  }
+}
+
+// Blocks: B init items, then per level d = 0 .. max_depth and per request b
+// its nchunk stream items and its choose item.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kWave) void tree_verify(TreeFused a) {
+  __shared__ Exp2Table tab;
+  const uint32_t blk = blockIdx.x;
+  if (blk < static_cast<uint32_t>(a.B)) {
+    tree_fused_init(a, static_cast<int>(blk));
+    return;
+  }
+  const uint32_t per_b = static_cast<uint32_t>(a.nchunk) + 1u;
+  const uint32_t per_level = static_cast<uint32_t>(a.B) * per_b;
+  const uint32_t r = blk - static_cast<uint32_t>(a.B);
+  const uint32_t d = r / per_level;
+  const uint32_t r2 = r - d * per_level;
+  const uint32_t b = r2 / per_b;
+  const uint32_t j = r2 - b * per_b;
+  if (j < static_cast<uint32_t>(a.nchunk))
+    tree_fused_stream<DT, VEC>(a, static_cast<int>(b), static_cast<int>(d), static_cast<int>(j), tab);
+  else
+    tree_fused_choose<DT, VEC>(a, static_cast<int>(b), static_cast<int>(d), tab);
+}
+
+struct TreeLayout {
+  size_t state, partials, total;                       // multi-launch form
+  size_t f_state, f_done, f_lcount, f_chunks, f_totals, f_lanes;  // single launch (same buffer)
+  size_t f_total;
+};
+
+static int tree_fused_chunks(int V) { return (V + kTreeChunk - 1) / kTreeChunk; }
 
 static TreeLayout tree_layout(int B, int V) {
   TreeLayout L{};
   L.state = 0;
   L.partials = align_up(static_cast<size_t>(B) * sizeof(TreeState));
   L.total = align_up(L.partials + static_cast<size_t>(B) * num_chunks(V) * sizeof(NodePartial));
+  const size_t nc = static_cast<size_t>(tree_fused_chunks(V));
+  size_t off = 0;
+  L.f_state = off;  off = align_up(off + static_cast<size_t>(B) * kTreeLevels * sizeof(uint64_t));
+  L.f_done = off;   off = align_up(off + static_cast<size_t>(B) * kDoneStride * sizeof(uint64_t));
+  L.f_lcount = off; off = align_up(off + static_cast<size_t>(B) * kTreeLevels * sizeof(uint32_t));
+  L.f_chunks = off; off = align_up(off + static_cast<size_t>(B) * nc * sizeof(uint64_t));
+  L.f_totals = off; off = align_up(off + static_cast<size_t>(B) * nc * sizeof(double));
+  L.f_lanes = off;  off = align_up(off + static_cast<size_t>(B) * nc * kWave * sizeof(double));
+  L.f_total = off;
   return L;
+}
+
+// The single launch serves shapes with at most kTreeMaxChunks chunks and a
+// grid within kTreeMaxGrid blocks (and no test hook asking otherwise).
+constexpr long long kTreeMaxGrid = 1 << 20;
+static bool tree_fused_fits(int B, int V, int max_depth) {
+  if (getenv("SV_TREE_SPLIT") != nullptr) return false;
+  const long long nc = tree_fused_chunks(V);
+  return nc <= kTreeMaxChunks && B + static_cast<long long>(max_depth + 1) * B * (nc + 1) <= kTreeMaxGrid;
 }
 
 template <int DT, bool VEC>
@@ -296,7 +772,9 @@ extern "C" size_t sv_tree_workspace_bytes(int B, int N, int V, int dtype) {
   (void)dtype;
   (void)N;
   if (B < 0 || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > SV_MAX_VOCAB) return 0;
-  return tree_layout(B, V).total;
+  const TreeLayout L = tree_layout(B, V);
+  // either form may run (it depends on max_depth, given at call time)
+  return tree_fused_chunks(V) <= kTreeMaxChunks ? std::max(L.total, L.f_total) : L.total;
 }
 
 extern "C" int spec_verify_tree(const void* target_logits, const int32_t* node_tokens,
@@ -316,8 +794,43 @@ extern "C" int spec_verify_tree(const void* target_logits, const int32_t* node_t
   const size_t es = dtype == SV_BF16 ? 2 : 4;
   if (!aligned(target_logits, es)) return SV_ERR_ALIGN;
   const TreeLayout L = tree_layout(B, V);
-  if (workspace_bytes < L.total || !aligned(workspace, 256)) return SV_ERR_WORKSPACE;
+  const bool fused = tree_fused_fits(B, V, max_depth);
+  if (workspace_bytes < (fused ? L.f_total : L.total) || !aligned(workspace, 256)) return SV_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const int kv = dtype == SV_BF16 ? Elem<0>::kVec : Elem<1>::kVec;
+  const bool vec = (V % kv == 0) && aligned(target_logits, 16);
+  if (fused) {
+    TreeFused f{};
+    f.logits = target_logits;
+    f.tokens = node_tokens;
+    f.parents = parents;
+    f.uniforms = uniforms;
+    f.temperature = temperature;
+    f.B = B;
+    f.N = N;
+    f.V = V;
+    f.max_depth = max_depth;
+    f.nchunk = tree_fused_chunks(V);
+    f.out_tokens = out_tokens;
+    f.out_path = out_path_nodes;
+    f.out_n = out_num_accepted;
+    f.state = reinterpret_cast<uint64_t*>(ws + L.f_state);
+    f.done = reinterpret_cast<uint64_t*>(ws + L.f_done);
+    f.lcount = reinterpret_cast<uint32_t*>(ws + L.f_lcount);
+    f.chunks = reinterpret_cast<uint64_t*>(ws + L.f_chunks);
+    f.totals = reinterpret_cast<double*>(ws + L.f_totals);
+    f.lanes = reinterpret_cast<double*>(ws + L.f_lanes);
+    const dim3 grid(static_cast<unsigned>(B + static_cast<long long>(max_depth + 1) * B * (f.nchunk + 1)));
+    if (dtype == SV_BF16) {
+      if (vec) launch(SV_K_TREE_VERIFY, tree_verify<0, true>, grid, dim3(kWave), 0, stream, f);
+      else launch(SV_K_TREE_VERIFY, tree_verify<0, false>, grid, dim3(kWave), 0, stream, f);
+    } else {
+      if (vec) launch(SV_K_TREE_VERIFY, tree_verify<1, true>, grid, dim3(kWave), 0, stream, f);
+      else launch(SV_K_TREE_VERIFY, tree_verify<1, false>, grid, dim3(kWave), 0, stream, f);
+    }
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+  }
   TreeArgs a{};
   a.logits = target_logits;
   a.tokens = node_tokens;
@@ -334,9 +847,6 @@ extern "C" int spec_verify_tree(const void* target_logits, const int32_t* node_t
   a.out_n = out_num_accepted;
   a.state = reinterpret_cast<TreeState*>(ws + L.state);
   a.partials = reinterpret_cast<NodePartial*>(ws + L.partials);
-  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  const int kv = dtype == SV_BF16 ? Elem<0>::kVec : Elem<1>::kVec;
-  const bool vec = (V % kv == 0) && aligned(target_logits, 16);
   if (dtype == SV_BF16) return vec ? launch_tree<0, true>(a, stream) : launch_tree<0, false>(a, stream);
   return vec ? launch_tree<1, true>(a, stream) : launch_tree<1, false>(a, stream);
 }

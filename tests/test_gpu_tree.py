@@ -98,3 +98,39 @@ def test_depth_cap_enforced():
                              ti.dtype, 2)
     compare_tree(ref, *gpu[0]).check("depth cap")
     assert (ref.num_accepted == gpu[0][2]).all()
+
+
+def test_multi_launch_form(monkeypatch):
+    """The multi-launch form (one step per depth level, used when the single
+    launch's grid would be too large) agrees with the oracle."""
+    monkeypatch.setenv("SV_TREE_SPLIT", "1")
+    for T in (0.0, 0.8):
+        ti = synth.tree_inputs(seed=305, B=12, N=40, V=3000, max_depth=6, temperature=T, draft_sigma=0.3)
+        tree_parity(ti, 10, f"multi-launch T={T}")
+
+
+def test_single_launch_returns_workspace_to_zero():
+    """Calls on one explicit workspace with invalid requests, early stops, deep
+    accepts and mixed modes: the oracle agrees each time and every workspace
+    word is zero again after each call."""
+    ti = synth.tree_inputs(seed=306, B=10, N=48, V=5000, max_depth=7, temperature=0.9, draft_sigma=0.3)
+    ti.temperature[::3] = 0.0
+    ti.parents[4, 6] = 9          # invalid: parent after the child
+    dev = torch.device("cuda")
+    need = sv.lib().sv_tree_workspace_bytes(ti.B, ti.N, ti.V, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    lg = to_device_logits(ti.logits, ti.dtype)
+    tok = to_device(ti.node_tokens.astype(np.int32))
+    par = to_device(ti.parents.astype(np.int32))
+    T = to_device(ti.temperature.astype(np.float32))
+    rng = np.random.default_rng(11)
+    tally = Tally()
+    for r in range(6):
+        u = ti.uniforms if r == 0 else synth.uniforms(rng, (ti.B, ti.N))
+        ot, op, on = sv.verify_tree(lg, tok, par, to_device(u), T, ti.max_depth, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0, f"call {r}"
+        ref = oracle.verify_tree(ti.logits, ti.node_tokens, ti.parents, u, ti.temperature, ti.dtype, ti.max_depth)
+        tally.add(compare_tree(ref, ot.cpu().numpy(), op.cpu().numpy(), on.cpu().numpy()))
+    print(f"[tree workspace] {tally}", flush=True)
+    tally.check("tree workspace")
