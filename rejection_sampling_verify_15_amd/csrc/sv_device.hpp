@@ -1,11 +1,13 @@
 // Device building blocks shared by the libspecverify kernels (gfx950, wave64).
 //
-// Row streaming: a (row, chunk) work item covers kChunk consecutive logits of
-// one vocabulary row.  A 256-thread workgroup reads it with 16-byte loads
-// (8 bf16 or 4 fp32 per lane); load j of the workgroup covers one contiguous
-// span of kThreads * kVec elements, so every wave reads 1 KiB contiguous per
-// instruction.  Rows that are not 16-byte aligned, or whose length is not a
-// multiple of the vector width, take the scalar variant of the same loops.
+// Rows are read with 16-byte loads (8 bf16 or 4 fp32 per lane) laid out so
+// that load j of a wave (or workgroup) covers one contiguous span, every wave
+// reading 1 KiB contiguous per instruction.  Rows that are not 16-byte
+// aligned, or whose length is not a multiple of the vector width, take the
+// scalar variant of the same loops.  The single-launch chain and tree
+// kernels work in one-wave workgroups (RawSlice with NT = kWave); the
+// multi-launch forms and the debug-probabilities kernels use 256-thread
+// workgroups over kChunk-logit (row, chunk) items (Slice).
 #pragma once
 
 #include <hip/hip_runtime.h>
