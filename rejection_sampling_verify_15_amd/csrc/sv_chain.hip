@@ -894,10 +894,10 @@ __device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count, Exp2Ta
 // ---------------------------------------------------------------------------
 // Blocks come in one segment per request -- its stream items, then its
 // decide item, which so waits about as long as its own request's loads take --
-// followed by the unit pool.  Each workgroup keeps at most 80 VGPRs, so six
-// waves of stream items share a SIMD.
+// followed by the unit pool.  Each workgroup keeps at most 96 VGPRs, so five
+// waves share a SIMD (six would force the draw path to spill).
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(6))) void chain_verify(ChainArgs a) {
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(5))) void chain_verify(ChainArgs a) {
   __shared__ Exp2Table tab;
   // 32-bit index arithmetic: this grid has at most kMaxGrid blocks
   const uint32_t blk = blockIdx.x;
