@@ -165,6 +165,13 @@ __global__ __launch_bounds__(kThreads) void probs_finalize(ProbsArgs a) {
       a.resid[static_cast<size_t>(b) * a.gamma + k] = rv;
     }
   }
+  // the request's partials back to zero once every thread has read its rows
+  // (thread k also reads draft row gamma + 1 + k)
+  __syncthreads();
+  ProbPartial* pp = a.partials + static_cast<size_t>(b) * R * a.nchunk;
+  for (int i = threadIdx.x; i < R * a.nchunk; i += kThreads) pp[i] = ProbPartial{};
+  double* rp = a.resid_part + static_cast<size_t>(b) * a.gamma * a.nchunk;
+  for (int i = threadIdx.x; i < a.gamma * a.nchunk; i += kThreads) rp[i] = 0.0;
 }
 
 struct ProbsLayout {

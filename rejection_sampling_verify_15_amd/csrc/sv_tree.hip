@@ -63,6 +63,7 @@ struct TreeArgs {
   int32_t* out_n;
   TreeState* state;
   NodePartial* partials;  // [B][nchunk]
+  int last;               // set for the last tree_choose launch: it returns the workspace to zero
 };
 
 __device__ inline bool tree_temp_ok(float t) { return isfinite(t) && (t == 0.0f || t >= 1.17549435e-38f); }
@@ -179,6 +180,12 @@ __global__ __launch_bounds__(kThreads) void tree_node_pass(TreeArgs a) {
   if (threadIdx.x == 0) a.partials[static_cast<size_t>(b) * a.nchunk + c] = out;
 }
 
+// The request's node partials back to zero (the last step, once they are read).
+__device__ inline void tree_clear_partials(const TreeArgs& a, int b) {
+  NodePartial* p = a.partials + static_cast<size_t>(b) * a.nchunk;
+  for (int c = threadIdx.x; c < a.nchunk; c += kThreads) p[c] = NodePartial{};
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void tree_choose(TreeArgs a) {
   __shared__ int s_chunk, s_hit, s_last, s_child, s_token;
@@ -186,7 +193,14 @@ __global__ __launch_bounds__(kThreads) void tree_choose(TreeArgs a) {
   __shared__ double s_before, s_target;
   const int b = blockIdx.x;
   const TreeState st = a.state[b];
-  if (!st.active) return;
+  if (!st.active) {
+    // every thread has read active == 0, so zeroing the state splits no one
+    if (a.last) {
+      tree_clear_partials(a, b);
+      if (threadIdx.x == 0) a.state[b] = TreeState{};
+    }
+    return;
+  }
   const float T = a.temperature[b];
   const NodePartial* p = a.partials + static_cast<size_t>(b) * a.nchunk;
   const bool greedy = T == 0.0f;
@@ -227,6 +241,7 @@ __global__ __launch_bounds__(kThreads) void tree_choose(TreeArgs a) {
     }
   }
   __syncthreads();
+  if (a.last) tree_clear_partials(a, b);  // only thread 0 read them, before the barrier
   if (!greedy) {
     const double inv_t = 1.0 / static_cast<double>(T);
     constexpr int kPerThread = kChunk / kThreads;
@@ -275,11 +290,11 @@ __global__ __launch_bounds__(kThreads) void tree_choose(TreeArgs a) {
     if (child != 0x7fffffff) {
       a.out_tokens[static_cast<size_t>(b) * L1 + st.len] = c_tok;
       a.out_path[static_cast<size_t>(b) * L1 + st.len] = child;
-      a.state[b] = TreeState{child, st.len + 1, 1, 0};
+      a.state[b] = a.last ? TreeState{} : TreeState{child, st.len + 1, 1, 0};
     } else {
       a.out_tokens[static_cast<size_t>(b) * L1 + st.len] = c_tok;
       a.out_n[b] = st.len;
-      a.state[b] = TreeState{st.node, st.len, 0, 0};
+      a.state[b] = a.last ? TreeState{} : TreeState{st.node, st.len, 0, 0};
     }
   }
 }
@@ -753,12 +768,14 @@ static bool tree_fused_fits(int B, int V, int max_depth) {
 }
 
 template <int DT, bool VEC>
-static int launch_tree(const TreeArgs& a, hipStream_t stream) {
+static int launch_tree(TreeArgs a, hipStream_t stream) {
   const long long n = static_cast<long long>(a.B) * a.nchunk;
   if (n > 0x7fffffffLL) return SV_ERR_SHAPE;
+  a.last = 0;
   launch(SV_K_TREE_INIT, tree_init, dim3(a.B), dim3(kThreads), a.N * sizeof(int32_t), stream, a);
   for (int step = 0; step <= a.max_depth; ++step) {
     launch(SV_K_TREE_NODE_PASS, tree_node_pass<DT, VEC>, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, stream, a);
+    a.last = step == a.max_depth;
     launch(SV_K_TREE_CHOOSE, tree_choose<DT>, dim3(a.B), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;

@@ -19,6 +19,17 @@ WINDOW = 1e-5
 MAX_MISMATCH_RATE = 1e-4
 
 
+def assert_shared_workspace_zero(label=""):
+    """Every entry point shares the binding's cached workspace of the current
+    stream and must leave it zero-filled: the single-launch kernels count and
+    flag through it and take nonzero words for another call's progress."""
+    import rejection_sampling_verify_15_amd as sv
+    torch.cuda.synchronize()
+    ws = sv.workspace(0, torch.device("cuda", torch.cuda.current_device()))
+    nz = int(ws.count_nonzero())
+    assert nz == 0, f"{label}: {nz} nonzero workspace bytes after the call"
+
+
 @dataclasses.dataclass
 class Tally:
     decisions: int = 0

@@ -6,7 +6,8 @@ import torch
 import oracle
 import synth
 import rejection_sampling_verify_15_amd as sv
-from parity import (Tally, compare_chain, oracle_chain_many, to_device, to_device_logits)
+from parity import (Tally, assert_shared_workspace_zero, compare_chain, oracle_chain_many, to_device,
+                    to_device_logits)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,7 +23,7 @@ def run_gpu(ci, u_sets, draft_on_device=True):
         ud = to_device(np.asarray(u, dtype=np.float32))
         ot, on = sv.verify_chain(tgt, drf, tok, ud, T)
         outs.append((ot, on))
-    torch.cuda.synchronize()
+    assert_shared_workspace_zero("chain")
     return [(ot.cpu().numpy(), on.cpu().numpy()) for ot, on in outs]
 
 

@@ -7,7 +7,7 @@ import torch
 import oracle
 import synth
 import rejection_sampling_verify_15_amd as sv
-from parity import to_device, to_device_logits
+from parity import assert_shared_workspace_zero, to_device, to_device_logits
 
 pytestmark = pytest.mark.gpu
 
@@ -17,7 +17,7 @@ def check_probs(ci, label):
     drf = to_device_logits(ci.draft, ci.dtype)
     out = sv.probs_debug(tgt, drf, to_device(ci.draft_tokens.astype(np.int32)),
                          to_device(ci.temperature.astype(np.float32)))
-    torch.cuda.synchronize()
+    assert_shared_workspace_zero(label)
     got = {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
     ref = oracle.probs_debug(ci.target, ci.draft, ci.draft_tokens, ci.temperature, ci.dtype)
     for k, rv in (("p_at_draft", ref.p_at_draft), ("q_at_draft", ref.q_at_draft)):

@@ -6,7 +6,7 @@ import torch
 import oracle
 import synth
 import rejection_sampling_verify_15_amd as sv
-from parity import Tally, compare_tree, to_device, to_device_logits
+from parity import Tally, assert_shared_workspace_zero, compare_tree, to_device, to_device_logits
 
 pytestmark = pytest.mark.gpu
 
@@ -19,7 +19,7 @@ def run_tree(ti, u_sets):
     outs = []
     for u in u_sets:
         outs.append(sv.verify_tree(lg, tok, par, to_device(np.asarray(u, np.float32)), T, ti.max_depth))
-    torch.cuda.synchronize()
+    assert_shared_workspace_zero("tree")
     return [tuple(x.cpu().numpy() for x in o) for o in outs]
 
 
@@ -107,6 +107,23 @@ def test_multi_launch_form(monkeypatch):
     for T in (0.0, 0.8):
         ti = synth.tree_inputs(seed=305, B=12, N=40, V=3000, max_depth=6, temperature=T, draft_sigma=0.3)
         tree_parity(ti, 10, f"multi-launch T={T}")
+
+
+def test_single_launch_after_the_other_forms_on_the_shared_workspace(monkeypatch):
+    """The debug-probabilities call and the multi-launch tree form run on the
+    same cached workspace as the single-launch tree kernel, which counts and
+    flags through it: each leaves it zero, so sampled tree calls after them
+    still agree with the oracle."""
+    ci = synth.chain_inputs(207, B=12, gamma=5, V=70000, dtype="bf16", family="peaked",
+                            draft_sigma=0.5, temperature=0.9)
+    sv.probs_debug(to_device_logits(ci.target, ci.dtype), to_device_logits(ci.draft, ci.dtype),
+                   to_device(ci.draft_tokens.astype(np.int32)), to_device(ci.temperature.astype(np.float32)))
+    assert_shared_workspace_zero("probs")
+    ti = synth.tree_inputs(seed=307, B=20, N=48, V=40000, max_depth=7, temperature=1.0, draft_sigma=0.3)
+    monkeypatch.setenv("SV_TREE_SPLIT", "1")
+    tree_parity(ti, 3, "multi-launch before single")
+    monkeypatch.delenv("SV_TREE_SPLIT")
+    tree_parity(ti, 6, "single after multi-launch", seed=4)
 
 
 def test_single_launch_returns_workspace_to_zero():
