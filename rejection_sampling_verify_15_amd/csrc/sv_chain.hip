@@ -20,16 +20,20 @@
 //                   the count, and publishes a sampling request's final draw.
 //  3. draw units    per drawing request, one per span of the draw's rows:
 //                   fp64 sums of exp((x - max) / T) over the span (all, and
-//                   where p > q); the last unit of the request to count in
-//                   draws the token -- the smallest k with C_k > u * W.
+//                   where p > q), handed back as one self-marked record.  The
+//                   decide item, which waits for the records, draws the token
+//                   -- the smallest k with C_k > u * W (for large batches the
+//                   last unit of the request to count itself in draws).
 //
-// Workgroups are dispatched in block order and every wait is for lower blocks,
-// so each wait ends.  The decide items and units are dispatched while the last
-// stream items are still in flight: early requests are decided and drawn under
-// the streaming of later ones.  Very large shapes run the same three parts as
+// Workgroups are dispatched in block order and every wait is for lower blocks
+// (but for a decide item's wait for its units, bounded below), so each wait
+// ends.  The decide items and units are dispatched while the last stream items
+// are still in flight: early requests are decided and drawn under the
+// streaming of later ones.  Very large shapes run the same three parts as
 // three launches (chain_stream, chain_decide, chain_units) with capped grids
-// whose workgroups stride over the items.  Whoever consumes a workspace word
-// last returns it to zero.
+// whose workgroups stride over the items; there the last unit of a request to
+// count itself in draws.  Whoever consumes a workspace word last returns it to
+// zero.
 //
 // Precision: the accept test needs p(x)/q(x) to ~1e-6 and uses the fp32 chunk
 // sums merged in fp64; the final draw uses fp64 exponentials and fp64
@@ -60,6 +64,8 @@ __device__ inline bool marked(uint64_t w) { return (w & kMark) != 0; }
 
 // Per (request, draw unit), fp64: sums over the unit of the target (t) and
 // draft (d) exponentials, over all tokens and over the tokens with p > q.
+// Each field is stored negated: the sums are >= 0, so a stored field has its
+// sign bit set (-0.0 included) and a zero word is "not yet written".
 enum : int { kUnitAllT = 0, kUnitAllD = 1, kUnitPosT = 2, kUnitPosD = 3, kUnitFields = 4 };
 struct UnitRec {
   double f[kUnitFields];
@@ -392,7 +398,12 @@ __device__ inline bool poll_words(const uint64_t* p, int c0, int ce, uint64_t (&
   return false;
 }
 
-template <int DT>
+template <int DT, bool VEC>
+__device__ void draw_token(const ChainArgs& a, int b, const Pending& d, const Exp2Table& tab, bool zero_wire);
+
+// With kDraws (the single launch), the decide item of a drawing request then
+// waits for its units' records and draws the token itself.
+template <int DT, bool VEC, bool kDraws>
 __device__ void decide_request(const ChainArgs& a, int b, const Exp2Table& tab) {
   __shared__ float s_gm[kMaxSlots];
   __shared__ double s_gz[kMaxSlots];
@@ -517,8 +528,8 @@ __device__ void decide_request(const ChainArgs& a, int b, const Exp2Table& tab) 
   }
   // a request with draw units hears the outcome in every case: the draw, or
   // that there is none
+  Pending d{};
   if (request_class(a, T) == 0) {
-    Pending d{};
     if (any_bad) {
       d.valid = kPendingNone;
     } else {
@@ -554,6 +565,12 @@ __device__ void decide_request(const ChainArgs& a, int b, const Exp2Table& tab) 
   // the workspace words of this request back to zero
   uint64_t* pz = a.partials + static_cast<size_t>(b) * R * a.nchunk;
   for (int i = lane; i < nrows * a.nchunk; i += kWave) store_coherent(pz + i, 0ull);
+  if (kDraws && request_class(a, T) == 0) {
+    // the draw runs beside other requests' units: let this wave issue first
+    __builtin_amdgcn_s_setprio(3);
+    draw_token<DT, VEC>(a, b, d, tab, true);
+    __builtin_amdgcn_s_setprio(0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -571,7 +588,8 @@ struct Unit {
   static_assert(kSpan == kUnitSpan, "one span for every path");
 };
 
-__device__ inline double unit_field(const UnitRec* r, int f) { return load_coherent_f64(&r->f[f]); }
+__device__ inline bool field_marked(double v) { return __double_as_longlong(v) < 0; }
+__device__ inline double unit_field(const UnitRec* r, int f) { return -load_coherent_f64(&r->f[f]); }
 
 // Weight of a unit in the final draw (rzt, rzd: reciprocal normalisers).
 __device__ inline double unit_weight(double pos_t, double pos_d, double all_t, bool residual, double rzt, double rzd) {
@@ -586,31 +604,78 @@ __device__ inline double unit_weight(double pos_t, double pos_d, double all_t, b
 // l + kWave, ...); otherwise they are read again for each pass.
 constexpr int kDrawCache = 5;
 
+// Waits until every record of request b carries its mark (every unit has read
+// the decision and handed its sums back); with `cached`, lane l returns the
+// values of records l, l + kWave, ... in f, each field read until it arrives.
+// False if the wait gave up.
+__device__ bool wait_records(const ChainArgs& a, int b, bool cached, double (&f)[kDrawCache][kUnitFields]) {
+  const UnitRec* ur = a.units + static_cast<size_t>(b) * a.nunit;
+  const int lane = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < kDrawCache; ++q)
+#pragma unroll
+    for (int k = 0; k < kUnitFields; ++k) f[q][k] = (q * kWave + lane < a.nunit) ? 0.0 : -0.0;
+  bool whole = false;
+  for (uint32_t spin = 0; spin < kSpinLimit; ++spin) {
+    bool all = true;
+    if (cached) {
+#pragma unroll
+      for (int q = 0; q < kDrawCache; ++q)
+#pragma unroll
+        for (int k = 0; k < kUnitFields; ++k) {
+          if (!field_marked(f[q][k])) f[q][k] = load_coherent_f64(&ur[q * kWave + lane].f[k]);
+          all &= field_marked(f[q][k]);
+        }
+    } else {
+      for (int i = lane; i < a.nunit; i += kWave)
+#pragma unroll
+        for (int k = 0; k < kUnitFields; ++k) all &= field_marked(load_coherent_f64(&ur[i].f[k]));
+    }
+    if (__all(all)) {
+      whole = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+#pragma unroll
+  for (int q = 0; q < kDrawCache; ++q)
+#pragma unroll
+    for (int k = 0; k < kUnitFields; ++k) f[q][k] = -f[q][k];
+  return whole;
+}
+
+// Also returns the request's records (and, with `zero_wire`, its decision
+// wire, which every unit has read once its record is in) to zero; a request
+// without a draw only has that done.
 template <int DT, bool VEC>
-__device__ void draw_token(const ChainArgs& a, int b, const Pending& d, const Exp2Table& tab) {
+__device__ void draw_token(const ChainArgs& a, int b, const Pending& d, const Exp2Table& tab, bool zero_wire) {
   using U = Unit<DT, VEC>;
   using Raw = typename U::Raw;
   const int G = a.gamma;
   const int lane = threadIdx.x;
   const UnitRec* ur = a.units + static_cast<size_t>(b) * a.nunit;
   const bool cached = a.nunit <= kDrawCache * kWave;
+  uint64_t* wz = reinterpret_cast<uint64_t*>(a.units + static_cast<size_t>(b) * a.nunit);
+  const int nw = a.nunit * static_cast<int>(sizeof(UnitRec) / 8);
   // 1) the totals: fp64 normalisers of the draw's rows, and the residual mass
   double f[kDrawCache][kUnitFields];
+  if (!wait_records(a, b, cached, f)) {
+    if (lane == 0) a.out_n[b] = -1;  // gave up waiting for the units
+    return;
+  }
+  if (zero_wire && lane < kWireWords) store_coherent(&a.pending[b].w[lane], 0ull);
+  if (d.valid != kPendingDraw) {
+    for (int i = lane; i < nw; i += kWave) store_coherent(wz + i, 0ull);
+    return;
+  }
   double tot[kUnitFields] = {0.0, 0.0, 0.0, 0.0};
   if (cached) {
 #pragma unroll
-    for (int q = 0; q < kDrawCache; ++q) {
-      const int i = q * kWave + lane;
+    for (int q = 0; q < kDrawCache; ++q)
 #pragma unroll
-      for (int k = 0; k < kUnitFields; ++k) {
-        f[q][k] = i < a.nunit ? unit_field(ur + i, k) : 0.0;
-        tot[k] += f[q][k];
-      }
-    }
+      for (int k = 0; k < kUnitFields; ++k) tot[k] += f[q][k];
     // the records are in registers: return them to zero now, so that the
     // stores drain while the draw goes on
-    uint64_t* wz = reinterpret_cast<uint64_t*>(a.units + static_cast<size_t>(b) * a.nunit);
-    const int nw = a.nunit * static_cast<int>(sizeof(UnitRec) / 8);
     for (int i = lane; i < nw; i += kWave) store_coherent(wz + i, 0ull);
   } else {
     for (int i = lane; i < a.nunit; i += kWave)
@@ -726,11 +791,8 @@ __device__ void draw_token(const ChainArgs& a, int b, const Pending& d, const Ex
   hit = wave_min(hit);
   last_pos = wave_max_int(last_pos);
   if (lane == 0) a.out_tokens[static_cast<size_t>(b) * (G + 1) + d.n] = (hit != 0x7fffffff) ? hit : last_pos;
-  if (!cached) {
-    uint64_t* wz = reinterpret_cast<uint64_t*>(a.units + static_cast<size_t>(b) * a.nunit);
-    const int nw = a.nunit * static_cast<int>(sizeof(UnitRec) / 8);
+  if (!cached)
     for (int i = lane; i < nw; i += kWave) store_coherent(wz + i, 0ull);
-  }
 }
 
 // The drawing requests (class 0) of a batch of at most kRankMaxBatch: lane l
@@ -777,9 +839,10 @@ __device__ inline int nth_drawing(const DrawingSet& s, int p) {
 }
 
 // Unit `unit` of request b (a class-0 request): waits for the decision, then
-// adds its share of the final draw and counts itself in; the last unit of the
-// request draws and returns the request's draw records to zero.
-template <int DT, bool VEC>
+// hands back its share of the final draw as a marked record (zeros when there
+// is no draw).  With kCounted it also counts itself in, and the last unit of
+// the request draws.
+template <int DT, bool VEC, bool kCounted>
 __device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& tab) {
   using U = Unit<DT, VEC>;
   using Raw = typename U::Raw;
@@ -789,6 +852,7 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& 
   if (d.valid == 0 && lane == 0) a.out_n[b] = -1;  // gave up waiting
   const bool draw = d.valid == kPendingDraw;
   UnitRec* rec = a.units + static_cast<size_t>(b) * a.nunit + unit;
+  double pos_t = 0.0, pos_d = 0.0, all_t = 0.0, all_d = 0.0;
   if (draw) {
     const double l2t = kLog2e / static_cast<double>(d.t);
     const double mtl = static_cast<double>(d.mt) * l2t, mdl = static_cast<double>(d.md) * l2t;
@@ -802,7 +866,6 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& 
     st.load(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + trow, a.V), c0, c1);
     if (residual) sd.load(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + d.n, a.V), c0, c1);
     pad_tail<DT, VEC>(st, c0, c1);
-    double pos_t = 0.0, pos_d = 0.0, all_t = 0.0, all_d = 0.0;
     // one group at a time: group j sits in group 0 of the slices after j shifts
     if (residual) {
       pad_tail<DT, VEC>(sd, c0, c1);
@@ -834,27 +897,26 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& 
     pos_d = wave_sum(pos_d);
     all_t = wave_sum(all_t);
     all_d = wave_sum(all_d);
-    // lane f hands over field f
-    if (lane < kUnitFields) {
-      const double v = lane == kUnitAllT ? all_t : lane == kUnitAllD ? all_d : lane == kUnitPosT ? pos_t : pos_d;
-      store_coherent_f64(&rec->f[lane], v);
-    }
   }
+  // lane f hands over field f, negated (the mark)
+  if (lane < kUnitFields) {
+    const double v = lane == kUnitAllT ? all_t : lane == kUnitAllD ? all_d : lane == kUnitPosT ? pos_t : pos_d;
+    store_coherent_f64(&rec->f[lane], -v);
+  }
+  if constexpr (!kCounted) return;
   uint32_t old = 0;
   if (lane == 0) old = arrive(a.counters + static_cast<size_t>(b) * kCounterStride + kUnitCounter);
   const bool last = read_lane(static_cast<int>(old), 0) == a.nunit - 1;
   if (last) {
     // every unit of the request has read the decision and counted in: both
-    // words return to zero before the draw (which returns the records)
+    // words return to zero before the draw, which returns the records
     if (lane < kWireWords) store_coherent(&a.pending[b].w[lane], 0ull);
     if (lane == 0) store_coherent(a.counters + static_cast<size_t>(b) * kCounterStride + kUnitCounter, 0u);
-    if (draw) {
-      // the last unit of a request draws while other units may still compute:
-      // let its wave issue first on its SIMD
-      __builtin_amdgcn_s_setprio(3);
-      draw_token<DT, VEC>(a, b, d, tab);
-      __builtin_amdgcn_s_setprio(0);
-    }
+    // the last unit of a request draws while other units may still compute:
+    // let its wave issue first on its SIMD
+    __builtin_amdgcn_s_setprio(3);
+    draw_token<DT, VEC>(a, b, d, tab, false);
+    __builtin_amdgcn_s_setprio(0);
   }
 }
 
@@ -864,7 +926,7 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& 
 // The caller's LDS table is filled here, once the workgroup is known to have
 // work.
 // Task counts fit in 32 bits (B * nunit < 2^31 within the shape limits).
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool kCounted>
 __device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count, Exp2Table& tab) {
   const uint32_t nunit = static_cast<uint32_t>(a.nunit);
   if (a.B <= kRankMaxBatch) {
@@ -875,7 +937,7 @@ __device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count, Exp2Ta
     __syncthreads();
     for (uint32_t t = w; t < tasks; t += count) {
       const uint32_t p = t / nunit;
-      unit_work<DT, VEC>(a, nth_drawing(ds, static_cast<int>(p)), static_cast<int>(t - p * nunit), tab);
+      unit_work<DT, VEC, kCounted>(a, nth_drawing(ds, static_cast<int>(p)), static_cast<int>(t - p * nunit), tab);
     }
   } else {
     const uint32_t tasks = static_cast<uint32_t>(a.B) * nunit;
@@ -884,7 +946,8 @@ __device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count, Exp2Ta
     __syncthreads();
     for (uint32_t t = w; t < tasks; t += count) {
       const uint32_t b = t / nunit;
-      if (request_class(a, a.temperature[b]) == 0) unit_work<DT, VEC>(a, static_cast<int>(b), static_cast<int>(t - b * nunit), tab);
+      if (request_class(a, a.temperature[b]) == 0)
+        unit_work<DT, VEC, kCounted>(a, static_cast<int>(b), static_cast<int>(t - b * nunit), tab);
     }
   }
 }
@@ -894,8 +957,14 @@ __device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count, Exp2Ta
 // ---------------------------------------------------------------------------
 // Blocks come in one segment per request -- its stream items, then its
 // decide item, which so waits about as long as its own request's loads take --
-// followed by the unit pool.  Each workgroup keeps at most 96 VGPRs, so five
+// followed by the unit pool.  Up to kDecideDrawsMax requests, a decide item
+// then waits for its units' records and draws: the only wait for higher
+// blocks, and one that always ends, since those few hundred waiting items at
+// most leave most of every XCD's 600-odd wave slots to the units.  Larger
+// batches count their units in and the last one draws.  Each workgroup keeps at most 96 VGPRs, so five
 // waves share a SIMD (six would force the draw path to spill).
+constexpr int kDecideDrawsMax = 256;
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(5))) void chain_verify(ChainArgs a) {
   __shared__ Exp2Table tab;
@@ -914,10 +983,12 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(5))) void
     }
     exp2_table_init(tab);
     __syncthreads();
-    decide_request<DT>(a, static_cast<int>(b), tab);
+    if (a.B <= kDecideDrawsMax) decide_request<DT, VEC, true>(a, static_cast<int>(b), tab);
+    else decide_request<DT, VEC, false>(a, static_cast<int>(b), tab);
     return;
   }
-  unit_pool<DT, VEC>(a, blk - nseg, gridDim.x - nseg, tab);
+  if (a.B <= kDecideDrawsMax) unit_pool<DT, VEC, false>(a, blk - nseg, gridDim.x - nseg, tab);
+  else unit_pool<DT, VEC, true>(a, blk - nseg, gridDim.x - nseg, tab);
 }
 
 // Very large shapes: the three parts as three launches.  Persistent
@@ -979,13 +1050,13 @@ __global__ __launch_bounds__(kThreads) void chain_stream(ChainArgs a) {
   }
 }
 
-template <int DT>
+template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void chain_decide(ChainArgs a) {
   __shared__ Exp2Table tab;
   exp2_table_init(tab);
   __syncthreads();
   for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
-    decide_request<DT>(a, b, tab);
+    decide_request<DT, VEC, false>(a, b, tab);
     __syncthreads();  // LDS is reused by the next request
   }
 }
@@ -993,7 +1064,7 @@ __global__ __launch_bounds__(kWave) void chain_decide(ChainArgs a) {
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void chain_units(ChainArgs a) {
   __shared__ Exp2Table tab;
-  unit_pool<DT, VEC>(a, blockIdx.x, gridDim.x, tab);
+  unit_pool<DT, VEC, true>(a, blockIdx.x, gridDim.x, tab);
 }
 
 // ---------------------------------------------------------------------------
@@ -1066,7 +1137,7 @@ static int launch_chain(ChainArgs a, hipStream_t stream) {
     const long long g = cap > 0 ? cap : kMaxGrid;
     launch(SV_K_CHAIN_STREAM, chain_stream<DT, VEC>, dim3(static_cast<unsigned>(a.nstream < sg ? a.nstream : sg)),
            dim3(kThreads), 0, stream, a);
-    launch(SV_K_CHAIN_DECIDE, chain_decide<DT>, dim3(static_cast<unsigned>(a.B < g ? a.B : g)), dim3(kWave), 0,
+    launch(SV_K_CHAIN_DECIDE, chain_decide<DT, VEC>, dim3(static_cast<unsigned>(a.B < g ? a.B : g)), dim3(kWave), 0,
            stream, a);
     launch(SV_K_CHAIN_UNITS, chain_units<DT, VEC>, dim3(static_cast<unsigned>(units < g ? units : g)), dim3(kWave),
            0, stream, a);
