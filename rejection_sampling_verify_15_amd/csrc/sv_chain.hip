@@ -576,10 +576,11 @@ __device__ void decide_request(const ChainArgs& a, int b, const Exp2Table& tab) 
 // ---------------------------------------------------------------------------
 // part 3: draw units, and the draw by the last unit of each request
 // ---------------------------------------------------------------------------
-// A draw unit covers kUnitSpan logits: one 16-byte group per lane for bf16,
-// two for fp32, eight single logits on the scalar path.  Small units spread
-// the draw of the last requests over many SIMDs.
-constexpr int kUnitSpan = 512;
+// A draw unit covers kUnitSpan logits: two 16-byte groups per lane for bf16,
+// four for fp32, sixteen single logits on the scalar path.  Small units spread
+// the draw of the last requests over many SIMDs, but each unit also costs
+// its round trips and a wave slot: 1024 measured faster than 512 or 2048.
+constexpr int kUnitSpan = 1024;
 template <int DT, bool VEC>
 struct Unit {
   static constexpr int kItems = kUnitSpan / (kWave * (VEC ? Elem<DT>::kVec : 1));
