@@ -129,17 +129,16 @@ __device__ inline const void* row_ptr(const void* base, size_t row, int V) {
 }
 
 // exp((x - m) / T) for x <= m, in fp64, given l2t = log2(e) / T (the
-// difference is taken in fp64, so it is exact for fp32 logits too), with the
-// LDS table of the calling workgroup.
-__device__ inline double exp_scaled(float x, float m, double l2t, const Exp2Table& tab) {
-  return exp2_tab((static_cast<double>(x) - static_cast<double>(m)) * l2t, tab);
+// difference is taken in fp64, so it is exact for fp32 logits too).
+__device__ inline double exp_scaled(float x, float m, double l2t) {
+  return exp2_neg((static_cast<double>(x) - static_cast<double>(m)) * l2t);
 }
 
 // The same for a whole row: ml2t = m * l2t once per row, then one fused
 // multiply-add per logit.  Rounding ml2t shifts every exponent of the row by
 // the same amount, which the row's own normaliser cancels.
-__device__ inline double exp_row(float x, double ml2t, double l2t, const Exp2Table& tab) {
-  return exp2_tab(__builtin_fma(static_cast<double>(x), l2t, -ml2t), tab);
+__device__ inline double exp_row(float x, double ml2t, double l2t) {
+  return exp2_neg(__builtin_fma(static_cast<double>(x), l2t, -ml2t));
 }
 
 // Request classes: 0 samples with its draft rows or has gamma == 0 (it has a
@@ -399,12 +398,12 @@ __device__ inline bool poll_words(const uint64_t* p, int c0, int ce, uint64_t (&
 }
 
 template <int DT, bool VEC>
-__device__ void draw_token(const ChainArgs& a, int b, const Pending& d, const Exp2Table& tab, bool zero_wire);
+__device__ void draw_token(const ChainArgs& a, int b, const Pending& d, bool zero_wire);
 
 // With kDraws (the single launch), the decide item of a drawing request then
 // waits for its units' records and draws the token itself.
 template <int DT, bool VEC, bool kDraws>
-__device__ void decide_request(const ChainArgs& a, int b, const Exp2Table& tab) {
+__device__ void decide_request(const ChainArgs& a, int b) {
   __shared__ float s_gm[kMaxSlots];
   __shared__ double s_gz[kMaxSlots];
   __shared__ int32_t s_garg[kMaxSlots];
@@ -468,12 +467,12 @@ __device__ void decide_request(const ChainArgs& a, int b, const Exp2Table& tab) 
         for (int i = 0; i < kPoll; ++i)
           if (c0 + i < ce) m8 = fmaxf(m8, partial_max(w[i]));
         if (m8 != -INFINITY) {
-          double z8 = (m != -INFINITY) ? z * exp_scaled(m, m8, l2t, tab) : 0.0;
+          double z8 = (m != -INFINITY) ? z * exp_scaled(m, m8, l2t) : 0.0;
 #pragma unroll
           for (int i = 0; i < kPoll; ++i) {
             const float wm = partial_max(w[i]);
             if (c0 + i < ce && wm != -INFINITY)
-              z8 += static_cast<double>(__int_as_float(partial_value(w[i]))) * exp_scaled(wm, m8, l2t, tab);
+              z8 += static_cast<double>(__int_as_float(partial_value(w[i]))) * exp_scaled(wm, m8, l2t);
           }
           m = m8;
           z = z8;
@@ -502,7 +501,7 @@ __device__ void decide_request(const ChainArgs& a, int b, const Exp2Table& tab) 
       double z = 0.0;
       for (int g = 0; g < gpr; ++g) {
         const float gm = s_gm[r * gpr + g];
-        if (gm != -INFINITY) z += s_gz[r * gpr + g] * exp_scaled(gm, m, l2t, tab);
+        if (gm != -INFINITY) z += s_gz[r * gpr + g] * exp_scaled(gm, m, l2t);
       }
       s_m[r] = m;
       s_z[r] = z;
@@ -517,8 +516,8 @@ __device__ void decide_request(const ChainArgs& a, int b, const Exp2Table& tab) 
       if (!sampling) {
         ok = (x == s_arg[lane]);
       } else {
-        const double p = exp_scaled(xt, s_m[lane], l2t, tab) / s_z[lane];
-        const double q = exp_scaled(xd, s_m[G + 1 + lane], l2t, tab) / s_z[G + 1 + lane];
+        const double p = exp_scaled(xt, s_m[lane], l2t) / s_z[lane];
+        const double q = exp_scaled(xd, s_m[G + 1 + lane], l2t) / s_z[G + 1 + lane];
         const double tau = (q <= p) ? 1.0 : p / q;
         ok = (static_cast<double>(u) <= tau);
       }
@@ -568,7 +567,7 @@ __device__ void decide_request(const ChainArgs& a, int b, const Exp2Table& tab) 
   if (kDraws && request_class(a, T) == 0) {
     // the draw runs beside other requests' units: let this wave issue first
     __builtin_amdgcn_s_setprio(3);
-    draw_token<DT, VEC>(a, b, d, tab, true);
+    draw_token<DT, VEC>(a, b, d, true);
     __builtin_amdgcn_s_setprio(0);
   }
 }
@@ -649,7 +648,7 @@ __device__ bool wait_records(const ChainArgs& a, int b, bool cached, double (&f)
 // wire, which every unit has read once its record is in) to zero; a request
 // without a draw only has that done.
 template <int DT, bool VEC>
-__device__ void draw_token(const ChainArgs& a, int b, const Pending& d, const Exp2Table& tab, bool zero_wire) {
+__device__ void draw_token(const ChainArgs& a, int b, const Pending& d, bool zero_wire) {
   using U = Unit<DT, VEC>;
   using Raw = typename U::Raw;
   const int G = a.gamma;
@@ -767,10 +766,10 @@ __device__ void draw_token(const ChainArgs& a, int b, const Pending& d, const Ex
     if (residual) {
 #pragma unroll
       for (int e = 0; e < Raw::kPer; ++e)
-        wk[e] = fmax(0.0, exp_row(st.at(0, e), mtl, l2t, tab) * rzt - exp_row(sd.at(0, e), mdl, l2t, tab) * rzd);
+        wk[e] = fmax(0.0, exp_row(st.at(0, e), mtl, l2t) * rzt - exp_row(sd.at(0, e), mdl, l2t) * rzd);
     } else {
 #pragma unroll
-      for (int e = 0; e < Raw::kPer; ++e) wk[e] = exp_row(st.at(0, e), mtl, l2t, tab);
+      for (int e = 0; e < Raw::kPer; ++e) wk[e] = exp_row(st.at(0, e), mtl, l2t);
     }
     st.shift();
     sd.shift();
@@ -844,7 +843,7 @@ __device__ inline int nth_drawing(const DrawingSet& s, int p) {
 // is no draw).  With kCounted it also counts itself in, and the last unit of
 // the request draws.
 template <int DT, bool VEC, bool kCounted>
-__device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& tab) {
+__device__ void unit_work(const ChainArgs& a, int b, int unit) {
   using U = Unit<DT, VEC>;
   using Raw = typename U::Raw;
   const int G = a.gamma;
@@ -874,8 +873,8 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& 
       for (int j = 0; j < Raw::kItems; ++j) {
 #pragma unroll
         for (int e = 0; e < Raw::kPer; ++e) {
-          const double et = exp_row(st.at(0, e), mtl, l2t, tab);
-          const double ed = exp_row(sd.at(0, e), mdl, l2t, tab);
+          const double et = exp_row(st.at(0, e), mtl, l2t);
+          const double ed = exp_row(sd.at(0, e), mdl, l2t);
           all_t += et;
           all_d += ed;
           if (et > ed * ratio) {
@@ -890,7 +889,7 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& 
 #pragma unroll 1
       for (int j = 0; j < Raw::kItems; ++j) {
 #pragma unroll
-        for (int e = 0; e < Raw::kPer; ++e) all_t += exp_row(st.at(0, e), mtl, l2t, tab);
+        for (int e = 0; e < Raw::kPer; ++e) all_t += exp_row(st.at(0, e), mtl, l2t);
         st.shift();
       }
     }
@@ -916,7 +915,7 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& 
     // the last unit of a request draws while other units may still compute:
     // let its wave issue first on its SIMD
     __builtin_amdgcn_s_setprio(3);
-    draw_token<DT, VEC>(a, b, d, tab, false);
+    draw_token<DT, VEC>(a, b, d, false);
     __builtin_amdgcn_s_setprio(0);
   }
 }
@@ -924,31 +923,25 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit, const Exp2Table& 
 // A pool of `count` workgroups (this one is number `w`) strides over the unit
 // tasks (drawing request, unit) in request order, so greedy requests take no
 // workgroups and each task waits only for its own request's decision.
-// The caller's LDS table is filled here, once the workgroup is known to have
-// work.
 // Task counts fit in 32 bits (B * nunit < 2^31 within the shape limits).
 template <int DT, bool VEC, bool kCounted>
-__device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count, Exp2Table& tab) {
+__device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count) {
   const uint32_t nunit = static_cast<uint32_t>(a.nunit);
   if (a.B <= kRankMaxBatch) {
     const DrawingSet ds = drawing_requests(a);
     const uint32_t tasks = static_cast<uint32_t>(ds.count) * nunit;
     if (w >= tasks) return;
-    exp2_table_init(tab);
-    __syncthreads();
     for (uint32_t t = w; t < tasks; t += count) {
       const uint32_t p = t / nunit;
-      unit_work<DT, VEC, kCounted>(a, nth_drawing(ds, static_cast<int>(p)), static_cast<int>(t - p * nunit), tab);
+      unit_work<DT, VEC, kCounted>(a, nth_drawing(ds, static_cast<int>(p)), static_cast<int>(t - p * nunit));
     }
   } else {
     const uint32_t tasks = static_cast<uint32_t>(a.B) * nunit;
     if (w >= tasks) return;
-    exp2_table_init(tab);
-    __syncthreads();
     for (uint32_t t = w; t < tasks; t += count) {
       const uint32_t b = t / nunit;
       if (request_class(a, a.temperature[b]) == 0)
-        unit_work<DT, VEC, kCounted>(a, static_cast<int>(b), static_cast<int>(t - b * nunit), tab);
+        unit_work<DT, VEC, kCounted>(a, static_cast<int>(b), static_cast<int>(t - b * nunit));
     }
   }
 }
@@ -968,7 +961,6 @@ constexpr int kDecideDrawsMax = 256;
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(5))) void chain_verify(ChainArgs a) {
-  __shared__ Exp2Table tab;
   // 32-bit index arithmetic: this grid has at most kMaxGrid blocks
   const uint32_t blk = blockIdx.x;
   const uint32_t seg = static_cast<uint32_t>(a.per_req) + 1u;
@@ -982,14 +974,12 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(5))) void
                                       static_cast<int>(rem - k * static_cast<uint32_t>(a.nchunk))});
       return;
     }
-    exp2_table_init(tab);
-    __syncthreads();
-    if (a.B <= kDecideDrawsMax) decide_request<DT, VEC, true>(a, static_cast<int>(b), tab);
-    else decide_request<DT, VEC, false>(a, static_cast<int>(b), tab);
+    if (a.B <= kDecideDrawsMax) decide_request<DT, VEC, true>(a, static_cast<int>(b));
+    else decide_request<DT, VEC, false>(a, static_cast<int>(b));
     return;
   }
-  if (a.B <= kDecideDrawsMax) unit_pool<DT, VEC, false>(a, blk - nseg, gridDim.x - nseg, tab);
-  else unit_pool<DT, VEC, true>(a, blk - nseg, gridDim.x - nseg, tab);
+  if (a.B <= kDecideDrawsMax) unit_pool<DT, VEC, false>(a, blk - nseg, gridDim.x - nseg);
+  else unit_pool<DT, VEC, true>(a, blk - nseg, gridDim.x - nseg);
 }
 
 // Very large shapes: the three parts as three launches.  Persistent
@@ -1053,19 +1043,15 @@ __global__ __launch_bounds__(kThreads) void chain_stream(ChainArgs a) {
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void chain_decide(ChainArgs a) {
-  __shared__ Exp2Table tab;
-  exp2_table_init(tab);
-  __syncthreads();
   for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
-    decide_request<DT, VEC, false>(a, b, tab);
+    decide_request<DT, VEC, false>(a, b);
     __syncthreads();  // LDS is reused by the next request
   }
 }
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void chain_units(ChainArgs a) {
-  __shared__ Exp2Table tab;
-  unit_pool<DT, VEC, true>(a, blockIdx.x, gridDim.x, tab);
+  unit_pool<DT, VEC, true>(a, blockIdx.x, gridDim.x);
 }
 
 // ---------------------------------------------------------------------------

@@ -124,54 +124,29 @@ struct Slice {
 // ---------------------------------------------------------------------------
 constexpr double kLog2e = 0x1.71547652b82fep+0;
 
-// 2^(j/64) for j = 0..63, held in LDS by the workgroups that use exp2_tab.
-struct Exp2Table {
-  double v[64];
-};
-
-// Entry j of the table: 2^(j/64) = e^y with y = j ln2 / 64 in [0, 0.69), by
-// its Taylor series to degree 17 (truncation below 2e-19), evaluated by
-// Horner's rule on the 1/k! constants; entry 0 is exactly 1.
-__host__ __device__ inline double exp2_table_entry(int j) {
-  constexpr double kInvFact[18] = {
-      0x1.0000000000000p+0,  0x1.0000000000000p+0,  0x1.0000000000000p-1,  0x1.5555555555555p-3,
-      0x1.5555555555555p-5,  0x1.1111111111111p-7,  0x1.6c16c16c16c17p-10, 0x1.a01a01a01a01ap-13,
-      0x1.a01a01a01a01ap-16, 0x1.71de3a556c734p-19, 0x1.27e4fb7789f5cp-22, 0x1.ae64567f544e4p-26,
-      0x1.1eed8eff8d898p-29, 0x1.6124613a86d09p-33, 0x1.93974a8c07c9dp-37, 0x1.ae7f3e733b81fp-41,
-      0x1.ae7f3e733b81fp-45, 0x1.952c77030ad4ap-49};
-  const double y = j * (0x1.62e42fefa39efp-1 / 64.0);  // j ln 2 / 64
-  double p = kInvFact[17];
-#pragma unroll
-  for (int k = 16; k >= 0; --k) p = __builtin_fma(p, y, kInvFact[k]);
-  return p;
-}
-
-// Fills the table, one entry per thread of the first wave (the caller
-// synchronises before use).
-__device__ inline void exp2_table_init(Exp2Table& tab) {
-  const int j = threadIdx.x;
-  if (j < 64) tab.v[j] = exp2_table_entry(j);
-}
-
-// 2^t for t <= 0 (t = -inf gives 0; t a few ulps above 0 is fine too) from
-// the table: t = n + j/64 + f with n, j integers (j in [0, 64)) and
-// |f| <= 1/128; 2^f by its Taylor series to degree 4 (truncation below
-// 4e-14, far inside what the inverse-CDF draw needs); the product is scaled
-// by 2^n.
-__host__ __device__ inline double exp2_tab(double t_in, const Exp2Table& tab) {
-  constexpr double kShift = 0x1.8p52;
+// 2^t for t <= 0 (t = -inf gives 0; t a few ulps above 0 is fine too): t =
+// n + f with n = round(t) and |f| <= 1/2, and 2^f = e^(f ln 2) by its Taylor
+// series to degree 10 -- the constants are (ln 2)^k / k! -- evaluated by
+// Horner's rule (relative truncation at most 3.1e-13, at f = -1/2: far inside
+// the 1e-10 the inverse-CDF draw needs); the result is scaled by 2^n.  No table, so no
+// shared-memory reads on the dependent path of each exponential.
+__host__ __device__ inline double exp2_neg(double t_in) {
+  constexpr double kShift = 0x1.8p52;  // adding it rounds to an integer
   const double t = __builtin_fmax(t_in, -1100.0);
-  const double sh = __builtin_fma(t, 64.0, kShift);  // round(64 t) in the low word
-  const double kd = sh - kShift;
-  const double f = __builtin_fma(kd, -0x1p-6, t);   // exact: t - k/64
-  struct Words { uint32_t lo, hi; };
-  const int k = static_cast<int>(__builtin_bit_cast(Words, sh).lo);
-  double p = 0x1.3b2ab6fba4e77p-7;                   // ln2^4 / 4!
+  const double n = (t + kShift) - kShift;
+  const double f = t - n;  // exact, |f| <= 1/2
+  double p = 0x1.e4cf5158b8ecap-28;
+  p = __builtin_fma(p, f, 0x1.b5253d395e7c4p-24);
+  p = __builtin_fma(p, f, 0x1.62c0223a5c824p-20);
+  p = __builtin_fma(p, f, 0x1.ffcbfc588b0c7p-17);
+  p = __builtin_fma(p, f, 0x1.430912f86c787p-13);
+  p = __builtin_fma(p, f, 0x1.5d87fe78a6731p-10);
+  p = __builtin_fma(p, f, 0x1.3b2ab6fba4e77p-7);
   p = __builtin_fma(p, f, 0x1.c6b08d704a0c0p-5);
   p = __builtin_fma(p, f, 0x1.ebfbdff82c58fp-3);
   p = __builtin_fma(p, f, 0x1.62e42fefa39efp-1);
   p = __builtin_fma(p, f, 1.0);
-  return __builtin_ldexp(p * tab.v[k & 63], k >> 6);
+  return __builtin_ldexp(p, static_cast<int>(n));
 }
 
 // ---------------------------------------------------------------------------

@@ -497,15 +497,11 @@ __device__ void tree_fused_init(const TreeFused& a, int b) {
 
 // Stream item: chunk c of the level-d node row of request b.
 template <int DT, bool VEC>
-__device__ void tree_fused_stream(const TreeFused& a, int b, int d, int c, Exp2Table& tab) {
+__device__ void tree_fused_stream(const TreeFused& a, int b, int d, int c) {
   using Raw = LaneRun<DT, VEC>;
   const float T = a.temperature[b];
   const int node = tree_wait_level(a, b, d);
   if (node < 0) return;
-  if (T != 0.0f) {
-    exp2_table_init(tab);
-    __syncthreads();
-  }
   const int c0 = c * kTreeChunk;
   const int c1 = min(a.V, c0 + kTreeChunk);
   Raw raw;
@@ -539,7 +535,7 @@ __device__ void tree_fused_stream(const TreeFused& a, int b, int d, int c, Exp2T
     for (int j = 0; j < Raw::kItems; ++j)
 #pragma unroll
       for (int e = 0; e < Raw::kPer; ++e)
-        sl += exp2_tab(__builtin_fma(static_cast<double>(raw.at(j, e)), l2t, -ml2t), tab);
+        sl += exp2_neg(__builtin_fma(static_cast<double>(raw.at(j, e)), l2t, -ml2t));
   }
   store_coherent_f64(a.lanes + slot * kWave + threadIdx.x, sl);
   const double tot = wave_sum(sl);
@@ -550,17 +546,13 @@ __device__ void tree_fused_stream(const TreeFused& a, int b, int d, int c, Exp2T
 
 // Choose item of level d of request b.
 template <int DT, bool VEC>
-__device__ void tree_fused_choose(const TreeFused& a, int b, int d, Exp2Table& tab) {
+__device__ void tree_fused_choose(const TreeFused& a, int b, int d) {
   constexpr int kLaneElems = LaneRun<DT, VEC>::kRun;  // logits per lane of a chunk
   const int lane = threadIdx.x;
   const float T = a.temperature[b];
   const int node = tree_wait_level(a, b, d);
   if (node < 0) return;
   const bool greedy = T == 0.0f;
-  if (!greedy) {
-    exp2_table_init(tab);
-    __syncthreads();
-  }
   const float u = greedy ? 0.0f : a.uniforms[static_cast<size_t>(b) * a.N + node];
   // the first kWave nodes' parents and tokens, loaded while the chunks finish
   const int32_t* par = a.parents + static_cast<size_t>(b) * a.N;
@@ -607,7 +599,7 @@ __device__ void tree_fused_choose(const TreeFused& a, int b, int d, Exp2Table& t
       const float mc = __uint_as_float(static_cast<uint32_t>(w[q]));
       wc[q] = (c < a.nchunk && mc != -INFINITY)
                   ? load_coherent_f64(tp + c) *
-                        exp2_tab((static_cast<double>(mc) - static_cast<double>(m)) * l2t, tab)
+                        exp2_neg((static_cast<double>(mc) - static_cast<double>(m)) * l2t)
                   : 0.0;
       Z += wc[q];
     }
@@ -643,7 +635,7 @@ __device__ void tree_fused_choose(const TreeFused& a, int b, int d, Exp2Table& t
     // crossing lane of that chunk: its per-lane sums, rescaled to the row max
     const uint64_t cw = load_coherent(a.chunks + static_cast<size_t>(b) * a.nchunk + chunk);
     const float mcs = __uint_as_float(static_cast<uint32_t>(cw));
-    const double scale = mcs != -INFINITY ? exp2_tab((static_cast<double>(mcs) - static_cast<double>(m)) * l2t, tab) : 0.0;
+    const double scale = mcs != -INFINITY ? exp2_neg((static_cast<double>(mcs) - static_cast<double>(m)) * l2t) : 0.0;
     const double wl = load_coherent_f64(a.lanes + (static_cast<size_t>(b) * a.nchunk + chunk) * kWave + lane) * scale;
     int cl = -1;
     {
@@ -667,7 +659,7 @@ __device__ void tree_fused_choose(const TreeFused& a, int b, int d, Exp2Table& t
     const bool have = lane < kLaneElems && k < c1;
     const void* row = fused_row<DT>(a, b, node);
     const double x = have ? static_cast<double>(Elem<DT>::at(row, k)) : 0.0;
-    const double wk = have ? exp2_tab(__builtin_fma(x, l2t, -static_cast<double>(m) * l2t), tab) : 0.0;
+    const double wk = have ? exp2_neg(__builtin_fma(x, l2t, -static_cast<double>(m) * l2t)) : 0.0;
     const double inc = wave_inclusive_sum(wk);
     const uint64_t hit = __ballot(wk > 0.0 && before + inc > target);
     const uint64_t pos = __ballot(wk > 0.0);
@@ -714,7 +706,6 @@ __device__ void tree_fused_choose(const TreeFused& a, int b, int d, Exp2Table& t
 // its nchunk stream items and its choose item.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void tree_verify(TreeFused a) {
-  __shared__ Exp2Table tab;
   const uint32_t blk = blockIdx.x;
   if (blk < static_cast<uint32_t>(a.B)) {
     tree_fused_init(a, static_cast<int>(blk));
@@ -728,9 +719,9 @@ __global__ __launch_bounds__(kWave) void tree_verify(TreeFused a) {
   const uint32_t b = r2 / per_b;
   const uint32_t j = r2 - b * per_b;
   if (j < static_cast<uint32_t>(a.nchunk))
-    tree_fused_stream<DT, VEC>(a, static_cast<int>(b), static_cast<int>(d), static_cast<int>(j), tab);
+    tree_fused_stream<DT, VEC>(a, static_cast<int>(b), static_cast<int>(d), static_cast<int>(j));
   else
-    tree_fused_choose<DT, VEC>(a, static_cast<int>(b), static_cast<int>(d), tab);
+    tree_fused_choose<DT, VEC>(a, static_cast<int>(b), static_cast<int>(d));
 }
 
 struct TreeLayout {
