@@ -41,6 +41,8 @@
 // reference except where u lies within a few ulps of a CDF step.
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "sv_device.hpp"
 #include "sv_host.hpp"
 
@@ -397,12 +399,12 @@ __device__ inline bool poll_words(const uint64_t* p, int c0, int ce, uint64_t (&
   return false;
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, int SPAN>
 __device__ void draw_token(const ChainArgs& a, int b, const Pending& d, bool zero_wire);
 
 // With kDraws (the single launch), the decide item of a drawing request then
-// waits for its units' records and draws the token itself.
-template <int DT, bool VEC, bool kDraws>
+// waits for its units' records (of SPAN logits each) and draws the token itself.
+template <int DT, bool VEC, int SPAN, bool kDraws>
 __device__ void decide_request(const ChainArgs& a, int b) {
   __shared__ float s_gm[kMaxSlots];
   __shared__ double s_gz[kMaxSlots];
@@ -567,7 +569,7 @@ __device__ void decide_request(const ChainArgs& a, int b) {
   if (kDraws && request_class(a, T) == 0) {
     // the draw runs beside other requests' units: let this wave issue first
     __builtin_amdgcn_s_setprio(3);
-    draw_token<DT, VEC>(a, b, d, true);
+    draw_token<DT, VEC, SPAN>(a, b, d, true);
     __builtin_amdgcn_s_setprio(0);
   }
 }
@@ -575,17 +577,20 @@ __device__ void decide_request(const ChainArgs& a, int b) {
 // ---------------------------------------------------------------------------
 // part 3: draw units, and the draw by the last unit of each request
 // ---------------------------------------------------------------------------
-// A draw unit covers kUnitSpan logits: two 16-byte groups per lane for bf16,
-// four for fp32, sixteen single logits on the scalar path.  Small units spread
-// the draw of the last requests over many SIMDs, but each unit also costs
-// its round trips and a wave slot: 1024 measured faster than 512 or 2048.
-constexpr int kUnitSpan = 1024;
-template <int DT, bool VEC>
+// A draw unit covers SPAN logits: 512 (one 16-byte group per lane for bf16,
+// two for fp32, eight single logits on the scalar path) or 1024.  Small units
+// spread a draw over many SIMDs, which a lone request's latency wants; but
+// each unit also costs its round trips and a wave slot, and from a couple of
+// thousand 512-logit units on, 1024 measured faster (2048 was slower again).
+constexpr int kUnitSpanSmall = 512;
+constexpr int kUnitSpanLarge = 1024;
+constexpr long long kSmallSpanUnits = 2048;  // B * ceil(V / 512) up to which units span 512
+template <int DT, bool VEC, int SPAN>
 struct Unit {
-  static constexpr int kItems = kUnitSpan / (kWave * (VEC ? Elem<DT>::kVec : 1));
+  static constexpr int kItems = SPAN / (kWave * (VEC ? Elem<DT>::kVec : 1));
   using Raw = RawSlice<DT, VEC, kItems, kWave>;
   static constexpr int kSpan = Raw::kSpan;
-  static_assert(kSpan == kUnitSpan, "one span for every path");
+  static_assert(kSpan == SPAN, "one span for every path");
 };
 
 __device__ inline bool field_marked(double v) { return __double_as_longlong(v) < 0; }
@@ -647,9 +652,9 @@ __device__ bool wait_records(const ChainArgs& a, int b, bool cached, double (&f)
 // Also returns the request's records (and, with `zero_wire`, its decision
 // wire, which every unit has read once its record is in) to zero; a request
 // without a draw only has that done.
-template <int DT, bool VEC>
+template <int DT, bool VEC, int SPAN>
 __device__ void draw_token(const ChainArgs& a, int b, const Pending& d, bool zero_wire) {
-  using U = Unit<DT, VEC>;
+  using U = Unit<DT, VEC, SPAN>;
   using Raw = typename U::Raw;
   const int G = a.gamma;
   const int lane = threadIdx.x;
@@ -842,9 +847,9 @@ __device__ inline int nth_drawing(const DrawingSet& s, int p) {
 // hands back its share of the final draw as a marked record (zeros when there
 // is no draw).  With kCounted it also counts itself in, and the last unit of
 // the request draws.
-template <int DT, bool VEC, bool kCounted>
+template <int DT, bool VEC, int SPAN, bool kCounted>
 __device__ void unit_work(const ChainArgs& a, int b, int unit) {
-  using U = Unit<DT, VEC>;
+  using U = Unit<DT, VEC, SPAN>;
   using Raw = typename U::Raw;
   const int G = a.gamma;
   const int lane = threadIdx.x;
@@ -915,7 +920,7 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit) {
     // the last unit of a request draws while other units may still compute:
     // let its wave issue first on its SIMD
     __builtin_amdgcn_s_setprio(3);
-    draw_token<DT, VEC>(a, b, d, false);
+    draw_token<DT, VEC, SPAN>(a, b, d, false);
     __builtin_amdgcn_s_setprio(0);
   }
 }
@@ -924,7 +929,7 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit) {
 // tasks (drawing request, unit) in request order, so greedy requests take no
 // workgroups and each task waits only for its own request's decision.
 // Task counts fit in 32 bits (B * nunit < 2^31 within the shape limits).
-template <int DT, bool VEC, bool kCounted>
+template <int DT, bool VEC, int SPAN, bool kCounted>
 __device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count) {
   const uint32_t nunit = static_cast<uint32_t>(a.nunit);
   if (a.B <= kRankMaxBatch) {
@@ -933,7 +938,7 @@ __device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count) {
     if (w >= tasks) return;
     for (uint32_t t = w; t < tasks; t += count) {
       const uint32_t p = t / nunit;
-      unit_work<DT, VEC, kCounted>(a, nth_drawing(ds, static_cast<int>(p)), static_cast<int>(t - p * nunit));
+      unit_work<DT, VEC, SPAN, kCounted>(a, nth_drawing(ds, static_cast<int>(p)), static_cast<int>(t - p * nunit));
     }
   } else {
     const uint32_t tasks = static_cast<uint32_t>(a.B) * nunit;
@@ -941,7 +946,7 @@ __device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count) {
     for (uint32_t t = w; t < tasks; t += count) {
       const uint32_t b = t / nunit;
       if (request_class(a, a.temperature[b]) == 0)
-        unit_work<DT, VEC, kCounted>(a, static_cast<int>(b), static_cast<int>(t - b * nunit));
+        unit_work<DT, VEC, SPAN, kCounted>(a, static_cast<int>(b), static_cast<int>(t - b * nunit));
     }
   }
 }
@@ -959,7 +964,7 @@ __device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count) {
 // waves share a SIMD (six would force the draw path to spill).
 constexpr int kDecideDrawsMax = 256;
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, int SPAN>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(5))) void chain_verify(ChainArgs a) {
   // 32-bit index arithmetic: this grid has at most kMaxGrid blocks
   const uint32_t blk = blockIdx.x;
@@ -974,12 +979,12 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(5))) void
                                       static_cast<int>(rem - k * static_cast<uint32_t>(a.nchunk))});
       return;
     }
-    if (a.B <= kDecideDrawsMax) decide_request<DT, VEC, true>(a, static_cast<int>(b));
-    else decide_request<DT, VEC, false>(a, static_cast<int>(b));
+    if (a.B <= kDecideDrawsMax) decide_request<DT, VEC, SPAN, true>(a, static_cast<int>(b));
+    else decide_request<DT, VEC, SPAN, false>(a, static_cast<int>(b));
     return;
   }
-  if (a.B <= kDecideDrawsMax) unit_pool<DT, VEC, false>(a, blk - nseg, gridDim.x - nseg);
-  else unit_pool<DT, VEC, true>(a, blk - nseg, gridDim.x - nseg);
+  if (a.B <= kDecideDrawsMax) unit_pool<DT, VEC, SPAN, false>(a, blk - nseg, gridDim.x - nseg);
+  else unit_pool<DT, VEC, SPAN, true>(a, blk - nseg, gridDim.x - nseg);
 }
 
 // Very large shapes: the three parts as three launches.  Persistent
@@ -1044,14 +1049,14 @@ __global__ __launch_bounds__(kThreads) void chain_stream(ChainArgs a) {
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void chain_decide(ChainArgs a) {
   for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
-    decide_request<DT, VEC, false>(a, b);
+    decide_request<DT, VEC, kUnitSpanLarge, false>(a, b);
     __syncthreads();  // LDS is reused by the next request
   }
 }
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void chain_units(ChainArgs a) {
-  unit_pool<DT, VEC, true>(a, blockIdx.x, gridDim.x);
+  unit_pool<DT, VEC, kUnitSpanLarge, true>(a, blockIdx.x, gridDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1068,7 +1073,7 @@ static ChainLayout chain_layout(int B, int gamma, int V) {
   ChainLayout L{};
   const size_t nchunk = static_cast<size_t>(row_chunks(V));
   const size_t R = 2 * static_cast<size_t>(gamma) + 1;
-  const size_t nunit = static_cast<size_t>(units_for(V, kUnitSpan));
+  const size_t nunit = static_cast<size_t>(units_for(V, kUnitSpanSmall));
   size_t off = 0;
   L.partials = off; off = align_up(off + static_cast<size_t>(B) * R * nchunk * sizeof(uint64_t));
   L.pending = off;  off = align_up(off + static_cast<size_t>(B) * sizeof(PendingWire));
@@ -1109,26 +1114,32 @@ static long long test_grid_cap() {
 
 template <int DT, bool VEC>
 static int launch_chain(ChainArgs a, hipStream_t stream) {
-  a.nunit = units_for(a.V, Unit<DT, VEC>::kSpan);
   a.nstream = static_cast<long long>(a.B) * (2 * a.gamma + 1) * a.nchunk;
   a.per_req = (2 * a.gamma + 1) * a.nchunk;
-  const long long units = static_cast<long long>(a.B) * a.nunit;
-  const long long pool = units < kUnitPool ? units : kUnitPool;
   const long long cap = test_grid_cap();
+  // the single launch, with 512- or 1024-logit draw units
+  const bool small = static_cast<long long>(a.B) * units_for(a.V, kUnitSpanSmall) <= kSmallSpanUnits;
+  a.nunit = units_for(a.V, small ? kUnitSpanSmall : kUnitSpanLarge);
+  const long long pool = std::min(static_cast<long long>(a.B) * a.nunit, kUnitPool);
   const long long fused = a.nstream + a.B + pool;
   if (cap <= 0 && getenv("SV_CHAIN_SPLIT") == nullptr && fused <= kMaxGrid) {
-    launch(SV_K_CHAIN_VERIFY, chain_verify<DT, VEC>, dim3(static_cast<unsigned>(fused)), dim3(kWave), 0, stream, a);
-  } else {
-    long long sg = stream_capacity<DT, VEC>();
-    if (cap > 0 && cap < sg) sg = cap;
-    const long long g = cap > 0 ? cap : kMaxGrid;
-    launch(SV_K_CHAIN_STREAM, chain_stream<DT, VEC>, dim3(static_cast<unsigned>(a.nstream < sg ? a.nstream : sg)),
-           dim3(kThreads), 0, stream, a);
-    launch(SV_K_CHAIN_DECIDE, chain_decide<DT, VEC>, dim3(static_cast<unsigned>(a.B < g ? a.B : g)), dim3(kWave), 0,
-           stream, a);
-    launch(SV_K_CHAIN_UNITS, chain_units<DT, VEC>, dim3(static_cast<unsigned>(units < g ? units : g)), dim3(kWave),
-           0, stream, a);
+    const dim3 grid(static_cast<unsigned>(fused));
+    if (small) launch(SV_K_CHAIN_VERIFY, chain_verify<DT, VEC, kUnitSpanSmall>, grid, dim3(kWave), 0, stream, a);
+    else launch(SV_K_CHAIN_VERIFY, chain_verify<DT, VEC, kUnitSpanLarge>, grid, dim3(kWave), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
   }
+  // three launches, with 1024-logit draw units
+  a.nunit = units_for(a.V, kUnitSpanLarge);
+  const long long units = static_cast<long long>(a.B) * a.nunit;
+  long long sg = stream_capacity<DT, VEC>();
+  if (cap > 0 && cap < sg) sg = cap;
+  const long long g = cap > 0 ? cap : kMaxGrid;
+  launch(SV_K_CHAIN_STREAM, chain_stream<DT, VEC>, dim3(static_cast<unsigned>(std::min(a.nstream, sg))),
+         dim3(kThreads), 0, stream, a);
+  launch(SV_K_CHAIN_DECIDE, chain_decide<DT, VEC>, dim3(static_cast<unsigned>(std::min<long long>(a.B, g))),
+         dim3(kWave), 0, stream, a);
+  launch(SV_K_CHAIN_UNITS, chain_units<DT, VEC>, dim3(static_cast<unsigned>(std::min(units, g))), dim3(kWave), 0,
+         stream, a);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
