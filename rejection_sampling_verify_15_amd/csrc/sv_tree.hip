@@ -5,18 +5,20 @@
 // Path descent: only the rows of visited nodes are read (at most max_depth+1
 // per request).
 //
-// One launch, `tree_verify`, of one-wave workgroups: an init item per request
-// (validation, outputs, the root as the level-0 node), then for each depth
-// level and each request a run of stream items over 2048-logit chunks of that
-// level's node row -- the chunk max and argmax (greedy), or the chunk max and
-// the fp64 sums of exp((x - max) / T) of each lane's logits (sampling) -- and
-// a choose item, which merges them, picks the token (argmax, or the
-// inverse-CDF draw narrowed chunk -> lane -> logit), looks for the child that
-// carries it and publishes that child as the next level's node, or stops the
-// request.  Every block waits only for lower-numbered blocks.  A chunk word is
-// tagged with its level, so one buffer serves every level without clearing;
-// the items of levels after a request's stop count themselves out on a `done`
-// word and the last of them returns it to zero.
+// One launch, `tree_verify`, of one-wave workgroups that loop over the depth
+// levels: per request a choose workgroup and one stream workgroup per
+// 2048-logit chunk of a row.  The choose workgroup validates the request and
+// publishes the root as its level-0 node.  At each level every stream
+// workgroup reduces its chunk of that level's node row -- the chunk max and
+// argmax (greedy), or the chunk max and the fp64 sums of exp((x - max) / T)
+// of each lane's logits (sampling) -- and the choose workgroup merges them,
+// picks the token (argmax, or the inverse-CDF draw narrowed chunk -> lane ->
+// logit), looks for the child that carries it and publishes that child as the
+// next level's node, or stops the request.  A chunk word is tagged with its
+// level, so one buffer serves every level without clearing; once the request
+// stops, each stream workgroup returns its chunk's words to zero and the last
+// workgroup of the request its control words.  The grid is B * (nchunk + 1)
+// workgroups whatever the depth.
 //
 // Shapes whose grid or chunk count is too large for one launch use the
 // multi-launch form: one step per depth level, two launches per step:
@@ -305,8 +307,8 @@ __global__ __launch_bounds__(kThreads) void tree_choose(TreeArgs a) {
 constexpr int kTreeChunk = 2048;           // logits per stream item
 constexpr int kTreeChunkCache = 4;         // chunk words per lane in a choose item
 constexpr int kTreeMaxChunks = kTreeChunkCache * kWave;
-constexpr int kTreeLevels = SV_MAX_TREE_DEPTH + 1;
-constexpr int kDoneStride = 16;            // 64-bit words per request: one 128-byte line
+constexpr int kCtlStride = 16;             // control words per request: one 128-byte line
+constexpr int kCtlNode = 0, kCtlStop = 1, kCtlExit = 2;
 constexpr uint64_t kTreeMark = 1ull << 63;
 constexpr uint32_t kTreeSpinLimit = 1u << 22;
 
@@ -320,9 +322,7 @@ struct TreeFused {
   int32_t* out_tokens;
   int32_t* out_path;
   int32_t* out_n;
-  uint64_t* state;   // [B][kTreeLevels]: marked node of each level
-  uint64_t* done;    // [B][kDoneStride]: word 0 marked (stop level + 1), word 1 the count of finished levels
-  uint32_t* lcount;  // [B][kTreeLevels]: items of a level after the stop that have seen it
+  uint64_t* ctl;     // [B][kCtlStride]: node word, stop word and exit count of each request
   uint64_t* chunks;  // [B][nchunk]: level-tagged chunk max (and argmax)
   double* totals;    // [B][nchunk]: fp64 exp-sum of the chunk relative to its max (sampling)
   double* lanes;     // [B][nchunk][kWave]: the same per lane (sampling)
@@ -392,60 +392,46 @@ __device__ inline const void* fused_row(const TreeFused& a, int b, int node) {
          (static_cast<size_t>(b) * a.N + node) * static_cast<size_t>(a.V) * Elem<DT>::kBytes;
 }
 
-// Waits until level d of request b has its node (returned), or the request
-// stopped before level d (-1), or the wait gave up (-2).  A reader that sees
-// the stop counts itself out on its level's counter; the last of a level's
-// nchunk + 1 items counts the level out on the request's counter, and the
-// last level to finish returns the done word to zero.  (Counting in two
-// steps keeps the number of atomics on any one address to nchunk + 1.)
-__device__ int tree_wait_level(const TreeFused& a, int b, int d) {
-  const uint64_t* sw = a.state + static_cast<size_t>(b) * kTreeLevels + d;
-  uint64_t* dw = a.done + static_cast<size_t>(b) * kDoneStride;
-  int node = -2;
-  uint64_t dn = 0;
+// Control words of request b: the node word (marked, the level above bit 32,
+// the node below it), the stop word (marked once the request has stopped)
+// and the count of the request's workgroups that are done with both.
+__device__ inline uint64_t* tree_ctl(const TreeFused& a, int b) { return a.ctl + static_cast<size_t>(b) * kCtlStride; }
+__device__ inline uint64_t node_word(int level, int node) {
+  return kTreeMark | (static_cast<uint64_t>(level) << 32) | static_cast<uint32_t>(node);
+}
+
+// Waits until request b's node word is that of level d (returns the node) or
+// the request has stopped (-1); -2 if the wait gave up.
+__device__ int tree_wait_node(const TreeFused& a, int b, int d) {
+  const uint64_t* cw = tree_ctl(a, b);
+  const uint64_t want = node_word(d, 0) >> 32;
   for (uint32_t spin = 0; spin < kTreeSpinLimit; ++spin) {
-    const uint64_t sv = load_coherent(sw);
-    dn = load_coherent(dw);
-    if (sv & kTreeMark) {
-      node = static_cast<int>(static_cast<uint32_t>(sv));
-      break;
-    }
-    if (dn & kTreeMark) {
-      node = -1;
-      break;
-    }
+    const uint64_t nv = load_coherent(cw + kCtlNode);
+    const uint64_t sv = load_coherent(cw + kCtlStop);
+    if ((nv >> 32) == want) return static_cast<int>(static_cast<uint32_t>(nv));
+    if (sv & kTreeMark) return -1;
     __builtin_amdgcn_s_sleep(2);
   }
-  if (node == -1 && threadIdx.x == 0) {
-    // the levels stop+1 .. max_depth each have nchunk + 1 readers
-    const int stop = static_cast<int>(static_cast<uint32_t>(dn)) - 1;
-    const uint32_t levels = static_cast<uint32_t>(levels_of(a) - 1 - stop);
-    uint32_t* lc = a.lcount + static_cast<size_t>(b) * kTreeLevels + d;
-    if (arrive(lc) == static_cast<uint32_t>(a.nchunk)) {
-      store_coherent(lc, 0u);
-      if (arrive(reinterpret_cast<uint32_t*>(dw + 1)) == levels - 1) {
-        store_coherent(dw, 0ull);
-        store_coherent(dw + 1, 0ull);
-      }
-    }
+  return -2;
+}
+
+// A workgroup of request b is done with the request; the last of its
+// nchunk + 1 workgroups returns the control words to zero.
+__device__ inline void tree_exit(const TreeFused& a, int b) {
+  if (threadIdx.x != 0) return;
+  uint64_t* cw = tree_ctl(a, b);
+  if (arrive(reinterpret_cast<uint32_t*>(cw + kCtlExit)) == static_cast<uint32_t>(a.nchunk)) {
+    store_coherent(cw + kCtlNode, 0ull);
+    store_coherent(cw + kCtlStop, 0ull);
+    store_coherent(cw + kCtlExit, 0ull);
   }
-  return node;
 }
 
-// Stops request b at level d (nothing is published when no level follows).
-__device__ inline void tree_publish_stop(const TreeFused& a, int b, int d) {
-  if (d + 1 < levels_of(a) && threadIdx.x == 0)
-    store_coherent(a.done + static_cast<size_t>(b) * kDoneStride,
-                   kTreeMark | static_cast<uint64_t>(static_cast<uint32_t>(d + 1)));
-}
-
-// Init item: validation (as tree_init); a valid request gets the root as its
-// level-0 node, an invalid one its -1 outputs and the stop before level 0.
-// Every output word has exactly one writer in the launch (this item for an
-// invalid request; for a valid one the choose item of each level writes that
-// level's slot and the last one the padding and the count), so no two XCDs'
-// caches ever hold the same output bytes.
-__device__ void tree_fused_init(const TreeFused& a, int b) {
+// Validation (as tree_init), by the choose workgroup before level 0: a valid
+// request gets the root as its level-0 node, an invalid one its -1 outputs
+// and the stop.  Every output word of a request is written by its choose
+// workgroup alone, so no two XCDs' caches ever hold the same output bytes.
+__device__ bool tree_validate(const TreeFused& a, int b) {
   __shared__ int32_t s_par[SV_MAX_TREE_NODES];
   const int lane = threadIdx.x;
   const int L1 = levels_of(a);
@@ -488,20 +474,18 @@ __device__ void tree_fused_init(const TreeFused& a, int b) {
     }
     if (lane == 0) {
       a.out_n[b] = -1;
-      store_coherent(a.done + static_cast<size_t>(b) * kDoneStride, kTreeMark);  // stopped before level 0
+      store_coherent(tree_ctl(a, b) + kCtlStop, kTreeMark);
     }
   } else if (lane == 0) {
-    store_coherent(a.state + static_cast<size_t>(b) * kTreeLevels, kTreeMark);  // node 0 at level 0
+    store_coherent(tree_ctl(a, b) + kCtlNode, node_word(0, 0));
   }
+  return !any_bad;
 }
 
-// Stream item: chunk c of the level-d node row of request b.
+// Chunk c of the row of node `node`, the level-d node of request b.
 template <int DT, bool VEC>
-__device__ void tree_fused_stream(const TreeFused& a, int b, int d, int c) {
+__device__ void tree_stream_chunk(const TreeFused& a, int b, int d, int c, int node, float T) {
   using Raw = LaneRun<DT, VEC>;
-  const float T = a.temperature[b];
-  const int node = tree_wait_level(a, b, d);
-  if (node < 0) return;
   const int c0 = c * kTreeChunk;
   const int c1 = min(a.V, c0 + kTreeChunk);
   Raw raw;
@@ -544,14 +528,13 @@ __device__ void tree_fused_stream(const TreeFused& a, int b, int d, int c) {
   if (threadIdx.x == 0) store_coherent(a.chunks + slot, tree_chunk_word(d, m, 0));
 }
 
-// Choose item of level d of request b.
+// The choice at level d of request b, whose node there is `node`: returns
+// the child it descends to (published as the next level's node), or -1 once
+// the request has stopped (the stop published).
 template <int DT, bool VEC>
-__device__ void tree_fused_choose(const TreeFused& a, int b, int d) {
+__device__ int tree_choose_level(const TreeFused& a, int b, int d, int node, float T) {
   constexpr int kLaneElems = LaneRun<DT, VEC>::kRun;  // logits per lane of a chunk
   const int lane = threadIdx.x;
-  const float T = a.temperature[b];
-  const int node = tree_wait_level(a, b, d);
-  if (node < 0) return;
   const bool greedy = T == 0.0f;
   const float u = greedy ? 0.0f : a.uniforms[static_cast<size_t>(b) * a.N + node];
   // the first kWave nodes' parents and tokens, loaded while the chunks finish
@@ -674,59 +657,75 @@ __device__ void tree_fused_choose(const TreeFused& a, int b, int d) {
   const int L1 = levels_of(a);
   int32_t* ot = a.out_tokens + static_cast<size_t>(b) * L1;
   int32_t* op = a.out_path + static_cast<size_t>(b) * L1;
-  if (lane == 0) {
-    store_coherent(a.state + static_cast<size_t>(b) * kTreeLevels + d, 0ull);  // every reader of this level is done
-    ot[d] = lost ? -1 : token;
-  }
-  if (!lost && child != 0x7fffffff) {
+  if (lane == 0) ot[d] = lost ? -1 : token;
+  if (!lost && child != 0x7fffffff && d + 1 < L1) {
     if (lane == 0) {
       op[d] = child;
-      store_coherent(a.state + static_cast<size_t>(b) * kTreeLevels + d + 1,
-                     kTreeMark | static_cast<uint64_t>(static_cast<uint32_t>(child)));
+      store_coherent(tree_ctl(a, b) + kCtlNode, node_word(d + 1, child));
     }
-    return;
+    return child;
   }
   // the stop: this level's path slot and every later slot are padding
   for (int i = d + lane; i < L1; i += kWave) {
     if (i > d) ot[i] = -1;
     op[i] = -1;
   }
-  if (lane == 0) a.out_n[b] = lost ? -1 : d;
-  tree_publish_stop(a, b, d);
-  // the request's chunk words (and sums) back to zero
-  for (int c = lane; c < a.nchunk; c += kWave) store_coherent(a.chunks + static_cast<size_t>(b) * a.nchunk + c, 0ull);
-  if (!greedy) {
-    for (int c = lane; c < a.nchunk; c += kWave) store_coherent_f64(a.totals + static_cast<size_t>(b) * a.nchunk + c, 0.0);
-    uint64_t* lz = reinterpret_cast<uint64_t*>(a.lanes + static_cast<size_t>(b) * a.nchunk * kWave);
-    for (int i = lane; i < a.nchunk * kWave; i += kWave) store_coherent(lz + i, 0ull);
+  if (lane == 0) {
+    a.out_n[b] = lost ? -1 : d;
+    store_coherent(tree_ctl(a, b) + kCtlStop, kTreeMark);
   }
+  return -1;
 }
 
-// Blocks: B init items, then per level d = 0 .. max_depth and per request b
-// its nchunk stream items and its choose item.
+// Stream workgroup of chunk c of request b: chunk c of each level's node row
+// until the request stops (the stop follows the last level's choice, whose
+// reads are then complete); then the chunk's words return to zero.
+template <int DT, bool VEC>
+__device__ void tree_stream_loop(const TreeFused& a, int b, int c) {
+  const float T = a.temperature[b];
+  for (int d = 0;; ++d) {
+    const int node = tree_wait_node(a, b, d);
+    if (node < 0) break;
+    tree_stream_chunk<DT, VEC>(a, b, d, c, node, T);
+  }
+  const size_t slot = static_cast<size_t>(b) * a.nchunk + c;
+  if (threadIdx.x == 0) {
+    store_coherent(a.chunks + slot, 0ull);
+    store_coherent_f64(a.totals + slot, 0.0);
+  }
+  store_coherent_f64(a.lanes + slot * kWave + threadIdx.x, 0.0);
+  tree_exit(a, b);
+}
+
+// Choose workgroup of request b: validation, then the choice at each level.
+template <int DT, bool VEC>
+__device__ void tree_choose_loop(const TreeFused& a, int b) {
+  if (tree_validate(a, b)) {
+    const float T = a.temperature[b];
+    int node = 0;
+    for (int d = 0; node >= 0; ++d) node = tree_choose_level<DT, VEC>(a, b, d, node, T);
+  }
+  tree_exit(a, b);
+}
+
+// Blocks: per request b its choose workgroup, then its nchunk stream
+// workgroups; each loops over the depth levels until the request stops.  A
+// workgroup waits only for workgroups of its own request, whose blocks are
+// contiguous.  Blocks are dispatched in order on each XCD and a request never
+// waits for a later one, so the lowest unfinished request always gets all of
+// its nchunk + 1 <= 257 workgroups resident: every wait ends.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void tree_verify(TreeFused a) {
-  const uint32_t blk = blockIdx.x;
-  if (blk < static_cast<uint32_t>(a.B)) {
-    tree_fused_init(a, static_cast<int>(blk));
-    return;
-  }
   const uint32_t per_b = static_cast<uint32_t>(a.nchunk) + 1u;
-  const uint32_t per_level = static_cast<uint32_t>(a.B) * per_b;
-  const uint32_t r = blk - static_cast<uint32_t>(a.B);
-  const uint32_t d = r / per_level;
-  const uint32_t r2 = r - d * per_level;
-  const uint32_t b = r2 / per_b;
-  const uint32_t j = r2 - b * per_b;
-  if (j < static_cast<uint32_t>(a.nchunk))
-    tree_fused_stream<DT, VEC>(a, static_cast<int>(b), static_cast<int>(d), static_cast<int>(j));
-  else
-    tree_fused_choose<DT, VEC>(a, static_cast<int>(b), static_cast<int>(d));
+  const uint32_t b = blockIdx.x / per_b;
+  const uint32_t j = blockIdx.x - b * per_b;
+  if (j == 0) tree_choose_loop<DT, VEC>(a, static_cast<int>(b));
+  else tree_stream_loop<DT, VEC>(a, static_cast<int>(b), static_cast<int>(j - 1u));
 }
 
 struct TreeLayout {
   size_t state, partials, total;                       // multi-launch form
-  size_t f_state, f_done, f_lcount, f_chunks, f_totals, f_lanes;  // single launch (same buffer)
+  size_t f_ctl, f_chunks, f_totals, f_lanes;  // single launch (same buffer)
   size_t f_total;
 };
 
@@ -739,9 +738,7 @@ static TreeLayout tree_layout(int B, int V) {
   L.total = align_up(L.partials + static_cast<size_t>(B) * num_chunks(V) * sizeof(NodePartial));
   const size_t nc = static_cast<size_t>(tree_fused_chunks(V));
   size_t off = 0;
-  L.f_state = off;  off = align_up(off + static_cast<size_t>(B) * kTreeLevels * sizeof(uint64_t));
-  L.f_done = off;   off = align_up(off + static_cast<size_t>(B) * kDoneStride * sizeof(uint64_t));
-  L.f_lcount = off; off = align_up(off + static_cast<size_t>(B) * kTreeLevels * sizeof(uint32_t));
+  L.f_ctl = off;    off = align_up(off + static_cast<size_t>(B) * kCtlStride * sizeof(uint64_t));
   L.f_chunks = off; off = align_up(off + static_cast<size_t>(B) * nc * sizeof(uint64_t));
   L.f_totals = off; off = align_up(off + static_cast<size_t>(B) * nc * sizeof(double));
   L.f_lanes = off;  off = align_up(off + static_cast<size_t>(B) * nc * kWave * sizeof(double));
@@ -752,10 +749,10 @@ static TreeLayout tree_layout(int B, int V) {
 // The single launch serves shapes with at most kTreeMaxChunks chunks and a
 // grid within kTreeMaxGrid blocks (and no test hook asking otherwise).
 constexpr long long kTreeMaxGrid = 1 << 20;
-static bool tree_fused_fits(int B, int V, int max_depth) {
+static bool tree_fused_fits(int B, int V) {
   if (getenv("SV_TREE_SPLIT") != nullptr) return false;
   const long long nc = tree_fused_chunks(V);
-  return nc <= kTreeMaxChunks && B + static_cast<long long>(max_depth + 1) * B * (nc + 1) <= kTreeMaxGrid;
+  return nc <= kTreeMaxChunks && static_cast<long long>(B) * (nc + 1) <= kTreeMaxGrid;
 }
 
 template <int DT, bool VEC>
@@ -802,7 +799,7 @@ extern "C" int spec_verify_tree(const void* target_logits, const int32_t* node_t
   const size_t es = dtype == SV_BF16 ? 2 : 4;
   if (!aligned(target_logits, es)) return SV_ERR_ALIGN;
   const TreeLayout L = tree_layout(B, V);
-  const bool fused = tree_fused_fits(B, V, max_depth);
+  const bool fused = tree_fused_fits(B, V);
   if (workspace_bytes < (fused ? L.f_total : L.total) || !aligned(workspace, 256)) return SV_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
@@ -823,13 +820,11 @@ extern "C" int spec_verify_tree(const void* target_logits, const int32_t* node_t
     f.out_tokens = out_tokens;
     f.out_path = out_path_nodes;
     f.out_n = out_num_accepted;
-    f.state = reinterpret_cast<uint64_t*>(ws + L.f_state);
-    f.done = reinterpret_cast<uint64_t*>(ws + L.f_done);
-    f.lcount = reinterpret_cast<uint32_t*>(ws + L.f_lcount);
+    f.ctl = reinterpret_cast<uint64_t*>(ws + L.f_ctl);
     f.chunks = reinterpret_cast<uint64_t*>(ws + L.f_chunks);
     f.totals = reinterpret_cast<double*>(ws + L.f_totals);
     f.lanes = reinterpret_cast<double*>(ws + L.f_lanes);
-    const dim3 grid(static_cast<unsigned>(B + static_cast<long long>(max_depth + 1) * B * (f.nchunk + 1)));
+    const dim3 grid(static_cast<unsigned>(static_cast<long long>(B) * (f.nchunk + 1)));
     if (dtype == SV_BF16) {
       if (vec) launch(SV_K_TREE_VERIFY, tree_verify<0, true>, grid, dim3(kWave), 0, stream, f);
       else launch(SV_K_TREE_VERIFY, tree_verify<0, false>, grid, dim3(kWave), 0, stream, f);
