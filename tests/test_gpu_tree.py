@@ -109,6 +109,16 @@ def test_multi_launch_form(monkeypatch):
         tree_parity(ti, 10, f"multi-launch T={T}")
 
 
+def test_more_workgroups_than_fit_at_once():
+    """2048 small trees: 6144 workgroups of the single launch (a choose and two
+    stream workgroups per request), more than the GPU holds at once, so later
+    requests start only as earlier ones finish; every request still agrees
+    with the oracle and the workspace returns to zero."""
+    ti = synth.tree_inputs(seed=308, B=2048, N=16, V=3000, max_depth=5, temperature=0.9, draft_sigma=0.3)
+    ti.temperature[::4] = 0.0
+    tree_parity(ti, 2, "2048 trees")
+
+
 def test_single_launch_after_the_other_forms_on_the_shared_workspace(monkeypatch):
     """The debug-probabilities call and the multi-launch tree form run on the
     same cached workspace as the single-launch tree kernel, which counts and
