@@ -384,6 +384,23 @@ __device__ inline bool chunk_at_level(uint64_t w, int level) {
   return (w >> 56) == (0x80ull | static_cast<uint64_t>(level + 1));
 }
 
+// The fp64 sums of a sampling chunk travel tagged: the sign bit set as the
+// mark (the sums are >= 0) and level + 1 in the low 7 bits of the mantissa,
+// which the reader clears (a relative change below 3e-14, far under what the
+// draw needs).  The choose workgroup so tells this level's sums from an
+// earlier level's without a flag, and the stream workgroup need not wait for
+// their stores before it publishes its chunk word.
+constexpr uint64_t kSumTag = 0x7full;
+__device__ inline uint64_t tag_sum(double v, int level) {
+  return ((static_cast<uint64_t>(__double_as_longlong(v)) & ~kSumTag) | static_cast<uint64_t>(level + 1)) | kTreeMark;
+}
+__device__ inline bool sum_at_level(uint64_t w, int level) {
+  return (w & kTreeMark) != 0 && (w & kSumTag) == static_cast<uint64_t>(level + 1);
+}
+__device__ inline double sum_value(uint64_t w) {
+  return __longlong_as_double(static_cast<long long>(w & ~(kTreeMark | kSumTag)));
+}
+
 __device__ inline int levels_of(const TreeFused& a) { return a.max_depth + 1; }
 
 template <int DT>
@@ -521,11 +538,12 @@ __device__ void tree_stream_chunk(const TreeFused& a, int b, int d, int c, int n
       for (int e = 0; e < Raw::kPer; ++e)
         sl += exp2_neg(__builtin_fma(static_cast<double>(raw.at(j, e)), l2t, -ml2t));
   }
-  store_coherent_f64(a.lanes + slot * kWave + threadIdx.x, sl);
+  store_coherent(reinterpret_cast<uint64_t*>(a.lanes) + slot * kWave + threadIdx.x, tag_sum(sl, d));
   const double tot = wave_sum(sl);
-  if (threadIdx.x == 0) store_coherent_f64(a.totals + slot, tot);
-  wait_memory();  // the sums are in place before the chunk word announces them
-  if (threadIdx.x == 0) store_coherent(a.chunks + slot, tree_chunk_word(d, m, 0));
+  if (threadIdx.x == 0) {
+    store_coherent(reinterpret_cast<uint64_t*>(a.totals) + slot, tag_sum(tot, d));
+    store_coherent(a.chunks + slot, tree_chunk_word(d, m, 0));
+  }
 }
 
 // The choice at level d of request b, whose node there is `node`: returns
@@ -573,7 +591,21 @@ __device__ int tree_choose_level(const TreeFused& a, int b, int d, int node, flo
     for (int q = 0; q < kTreeChunkCache; ++q)
       if (q * kWave + lane < a.nchunk) m = fmaxf(m, __uint_as_float(static_cast<uint32_t>(w[q])));
     m = wave_max(m);
-    const double* tp = a.totals + static_cast<size_t>(b) * a.nchunk;
+    // the chunk totals of this level (each arrives with or soon after its word)
+    const uint64_t* tp = reinterpret_cast<const uint64_t*>(a.totals) + static_cast<size_t>(b) * a.nchunk;
+    uint64_t tw[kTreeChunkCache];
+    for (uint32_t spin = 0;; ++spin) {
+      bool all = true;
+#pragma unroll
+      for (int q = 0; q < kTreeChunkCache; ++q) {
+        const int c = q * kWave + lane;
+        tw[q] = c < a.nchunk ? load_coherent(tp + c) : 0ull;
+        all &= (c >= a.nchunk || sum_at_level(tw[q], d));
+      }
+      if (__all(all)) break;
+      if (spin >= kTreeSpinLimit) { lost = true; break; }
+      __builtin_amdgcn_s_sleep(2);
+    }
     double wc[kTreeChunkCache];
     double Z = 0.0;
 #pragma unroll
@@ -581,8 +613,7 @@ __device__ int tree_choose_level(const TreeFused& a, int b, int d, int node, flo
       const int c = q * kWave + lane;
       const float mc = __uint_as_float(static_cast<uint32_t>(w[q]));
       wc[q] = (c < a.nchunk && mc != -INFINITY)
-                  ? load_coherent_f64(tp + c) *
-                        exp2_neg((static_cast<double>(mc) - static_cast<double>(m)) * l2t)
+                  ? sum_value(tw[q]) * exp2_neg((static_cast<double>(mc) - static_cast<double>(m)) * l2t)
                   : 0.0;
       Z += wc[q];
     }
@@ -619,7 +650,15 @@ __device__ int tree_choose_level(const TreeFused& a, int b, int d, int node, flo
     const uint64_t cw = load_coherent(a.chunks + static_cast<size_t>(b) * a.nchunk + chunk);
     const float mcs = __uint_as_float(static_cast<uint32_t>(cw));
     const double scale = mcs != -INFINITY ? exp2_neg((static_cast<double>(mcs) - static_cast<double>(m)) * l2t) : 0.0;
-    const double wl = load_coherent_f64(a.lanes + (static_cast<size_t>(b) * a.nchunk + chunk) * kWave + lane) * scale;
+    const uint64_t* lp = reinterpret_cast<const uint64_t*>(a.lanes) + (static_cast<size_t>(b) * a.nchunk + chunk) * kWave;
+    uint64_t lw = 0;
+    for (uint32_t spin = 0;; ++spin) {
+      lw = load_coherent(lp + lane);
+      if (__all(sum_at_level(lw, d))) break;
+      if (spin >= kTreeSpinLimit) { lost = true; break; }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    const double wl = sum_value(lw) * scale;
     int cl = -1;
     {
       const double inc = wave_inclusive_sum(wl);
