@@ -348,7 +348,8 @@ struct LaneRun {
       const int k0 = index(c0, j, 0);
       const int k = k0 < c1 ? k0 : c0;
       if constexpr (VEC) {
-        const uint4 v = Elem<DT>::raw(row, k);
+        // cached: the choose workgroup soon re-reads a run of the row
+        const uint4 v = load_row16_cached(static_cast<const char*>(row) + static_cast<size_t>(k) * Elem<DT>::kBytes);
         w[j][0] = v.x; w[j][1] = v.y; w[j][2] = v.z; w[j][3] = v.w;
       } else if constexpr (DT == 0) {
         w[j][0] = static_cast<const uint16_t*>(row)[k];
