@@ -109,6 +109,46 @@ def test_multi_launch_form(monkeypatch):
         tree_parity(ti, 10, f"multi-launch T={T}")
 
 
+def test_graph_capture_replays_match_eager():
+    """One tree call captured in a HIP graph and replayed several times, with
+    eager calls (on other uniforms) and synchronisations between the replays:
+    every replay gives the eager result for the captured inputs, and the
+    workspace stays zero (the kernel leaves it so; no memset is captured)."""
+    ti = synth.tree_inputs(seed=309, B=12, N=40, V=5000, max_depth=6, temperature=0.9, draft_sigma=0.3)
+    ti.temperature[::3] = 0.0
+    dev = torch.device("cuda")
+    lg = to_device_logits(ti.logits, ti.dtype)
+    tok = to_device(ti.node_tokens.astype(np.int32))
+    par = to_device(ti.parents.astype(np.int32))
+    T = to_device(ti.temperature.astype(np.float32))
+    u0 = to_device(ti.uniforms)
+    need = sv.lib().sv_tree_workspace_bytes(ti.B, ti.N, ti.V, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    want = [x.clone() for x in sv.verify_tree(lg, tok, par, u0, T, ti.max_depth, ws=ws)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            got = sv.verify_tree(lg, tok, par, u0, T, ti.max_depth, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    for r in range(4):
+        for x in got:
+            x.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(got, want):
+            assert torch.equal(x, y), f"replay {r}"
+        assert int(ws.count_nonzero()) == 0
+        # eager work on other uniforms between the replays
+        sv.verify_tree(lg, tok, par, to_device(synth.uniforms(rng, (ti.B, ti.N))), T, ti.max_depth, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
+
+
 def test_more_workgroups_than_fit_at_once():
     """2048 small trees: 6144 workgroups of the single launch (a choose and two
     stream workgroups per request), more than the GPU holds at once, so later
