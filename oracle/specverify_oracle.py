@@ -324,6 +324,48 @@ def verify_tree(logits: np.ndarray, node_tokens: np.ndarray, parents: np.ndarray
 
 
 # ---------------------------------------------------------------------------
+# tree attention mask and depth positions
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class TreeMaskResult:
+    mask: np.ndarray        # [B, N, N] bool: node i may attend to node j
+    depth: np.ndarray       # [B, N] int32 edges from the root, -1 => invalid request
+    tree_depth: np.ndarray  # [B] int32 depth of the deepest node, -1 => invalid request
+
+
+def tree_attention_mask(parents: np.ndarray, max_depth: int) -> TreeMaskResult:
+    """Topology-aware causal mask and depth positions of a depth-first
+    linearised token tree (lecture 17 notes section 4.3, tree-parallel
+    decoding: steps 2 and 3, and the remark that positions follow depth;
+    exercise 5).
+
+    Row i allows node i itself and every node on its path to the root, the
+    root included, and nothing else of the tree: a node placed earlier in the
+    linear order on another branch stays hidden.  The verified prefix before
+    the root is visible to every row and is not part of the mask.  Nodes at
+    equal depth share a position offset, depth(i) being the number of edges
+    from the root.  A malformed parent array (R9) or a node deeper than
+    max_depth makes the request invalid (R11): all-false rows, depth -1."""
+    parents = np.asarray(parents, dtype=np.int64)
+    B, N = parents.shape
+    mask = np.zeros((B, N, N), dtype=bool)
+    depth = np.full((B, N), -1, dtype=np.int32)
+    tree_depth = np.full(B, -1, dtype=np.int32)
+    for b in range(B):
+        d = tree_node_depths(parents[b])
+        if d is None or np.any(d > max_depth):
+            continue
+        for i in range(N):
+            j = i
+            while j >= 0:          # node i, then each ancestor up to the root
+                mask[b, i, j] = True
+                j = int(parents[b, j])
+        depth[b] = d
+        tree_depth[b] = int(d.max())
+    return TreeMaskResult(mask, depth, tree_depth)
+
+
+# ---------------------------------------------------------------------------
 # debug probabilities
 # ---------------------------------------------------------------------------
 @dataclasses.dataclass

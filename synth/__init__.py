@@ -374,6 +374,24 @@ def dfs_relabel(children):
     return order, new_id
 
 
+def tree_parent_arrays(seed: int, B: int, N: int, max_depth: int, max_branch: int = 4,
+                       dfs: bool = True) -> np.ndarray:
+    """[B, N] int32 parent arrays of random trees grown by random_tree_shape:
+    depth-first relabelled when dfs, else left in creation order (every
+    parent still precedes its children, but sibling subtrees interleave)."""
+    (r_shape,) = _streams(seed, 1)
+    parents = np.empty((B, N), dtype=np.int32)
+    for b in range(B):
+        par_c, ch_c = random_tree_shape(r_shape, N, max_depth, max_branch)
+        if not dfs:
+            parents[b] = par_c
+            continue
+        _, new_id = dfs_relabel(ch_c)
+        for old in range(N):
+            parents[b, new_id[old]] = -1 if par_c[old] < 0 else new_id[par_c[old]]
+    return parents
+
+
 def tree_inputs(seed: int = SEED_BASE + 5, B: int = 32, N: int = 64, V: int = 128256,
                 max_depth: int = 8, temperature: float = 0.0, dtype: str = "bf16",
                 family: str = "peaked", draft_sigma: float = 1.0,
