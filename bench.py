@@ -15,8 +15,9 @@ oracle timed on this host's cores on a bounded sample.
 
 Other workloads (--workload) report the same line for the single-request
 latency case (B=1, V=32000, also replayed from a HIP graph), the deep case
-(B=256, gamma=8, V=151936, Zipf logits) and the token-tree cases (B=32, 64
-nodes, greedy or naive sampling; rows are node rows).
+(B=256, gamma=8, V=151936, Zipf logits), the token-tree cases (B=32, 64
+nodes, greedy or naive sampling; rows are node rows) and the tree attention
+mask builder on the same tree shape (rows are mask rows).
 """
 from __future__ import annotations
 
@@ -106,7 +107,7 @@ def cpu_baseline(ci, budget_s: float = 15.0):
                       f"fresh uniforms, numpy fp64, {wall:.1f} s wall, {cpu:.1f} s CPU"}
 
 
-WORKLOADS = ("batched", "single", "deep", "tree-greedy", "tree-sampling")
+WORKLOADS = ("batched", "single", "deep", "tree-greedy", "tree-sampling", "tree-mask")
 
 
 def percentiles(xs):
@@ -299,6 +300,79 @@ def run_tree(args, torch, synth, sv, oracle_sample=True):
     return result
 
 
+def mask_bytes(B, N) -> int:
+    """Parents read; row words, depths and tree depths written."""
+    return B * N * 4 + B * N * ((N + 63) // 64) * 8 + B * N * 4 + B * 4
+
+
+def run_mask(args, torch, synth, sv):
+    """spec_tree_mask on the token-tree workload's shape (B=32, N=64, depth
+    <= 8), plus the same timing at B=4096, N=256 to show the store-bound
+    regime.  Rows are mask rows (one per node)."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def measure(B, N, max_depth, steps):
+        par = torch.from_numpy(synth.tree_parent_arrays(15005, B, N, max_depth, 4)).to(dev)
+        m = torch.empty((B, N, (N + 63) // 64), dtype=torch.int64, device=dev)
+        d = torch.empty((B, N), dtype=torch.int32, device=dev)
+        t = torch.empty((B,), dtype=torch.int32, device=dev)
+
+        def step(i):
+            sv.tree_mask(par, max_depth, m, d, t)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        total_ms, host_us = time_calls(torch, stream, step, steps)
+        with sv.KernelTimer(4 * steps) as kt:
+            time_calls(torch, stream, step, steps)
+        k_us = kt.mean_us("tree_mask")
+        nb = mask_bytes(B, N)
+        return {"B": B, "N": N, "max_depth": max_depth, "call_us": 1e3 * total_ms / steps,
+                "kernel_us": k_us, "host_enqueue_us": host_us, "algorithmic_bytes": nb,
+                "GBps": nb / (k_us * 1e-6) / 1e9, "rows_per_s": B * N / (total_ms * 1e-3 / steps),
+                "total_ms": total_ms}
+
+    small = measure(32, 64, 8, args.steps)
+    large = measure(4096, 256, 16, max(20, args.steps // 10))
+    result = head(args, small["rows_per_s"], small["total_ms"],
+                  {"workload": "tree attention mask and depth positions: B=32 trees of N=64 nodes, "
+                               "depth <= 8, branching 1..4 (the token-tree verify shape)",
+                   "B": 32, "N": 64, "max_depth": 8},
+                  metric="tree mask rows/sec (one row per node) and achieved HBM GB/s vs peak, 1 GPU")
+    result["dtype"] = "int32/uint64"
+    result.update({
+        "roofline": {"bound": "hbm", "achieved": small["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": small["GBps"] / PEAK_HBM_GBPS, "traffic": None, "kernel": "tree_mask",
+                     "kernel_us_per_call": small["kernel_us"],
+                     "algorithmic_bytes": small["algorithmic_bytes"],
+                     "note": "32.9 KB per call: the launch and the walk's dependent LDS reads set the "
+                             "time, not bytes; large_shape shows the store-bound regime"},
+        "large_shape": {k: v for k, v in large.items() if k != "total_ms"},
+    })
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_mask(synth.tree_parent_arrays(15005, 32, 64, 8, 4), 8)
+    return result
+
+
+def cpu_baseline_mask(parents, max_depth, budget_s: float = 10.0):
+    """The oracle's mask on the same batch, repeated until the budget is spent."""
+    import oracle
+    rows = calls = 0
+    w0 = time.perf_counter()
+    c0 = time.process_time()
+    while time.perf_counter() - w0 < budget_s:
+        oracle.tree_attention_mask(parents, max_depth)
+        rows += parents.size
+        calls += 1
+    wall = time.perf_counter() - w0
+    cpu = time.process_time() - c0
+    return {"value": rows / wall, "unit": "rows/s", "cores": max(1, round(cpu / wall)), "kind": "oracle",
+            "sample": f"{calls} masks of the same B=32, N=64 batch ({rows} rows), python loops, "
+                      f"{wall:.1f} s wall, {cpu:.1f} s CPU"}
+
+
 def cpu_baseline_tree(ti, budget_s: float = 15.0):
     """The oracle's tree verification on the same batch, request by request,
     until the budget is spent; the unit is node rows per second."""
@@ -321,9 +395,9 @@ def cpu_baseline_tree(ti, budget_s: float = 15.0):
                       f"{wall:.1f} s wall, {cpu:.1f} s CPU"}
 
 
-def head(args, value, total_ms, config):
+def head(args, value, total_ms, config, metric=METRIC):
     return {
-        "metric": METRIC,
+        "metric": metric,
         "value": value,
         "unit": "rows/s",
         "n_gpus": 1,
@@ -362,7 +436,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
-    if args.workload.startswith("tree"):
+    if args.workload == "tree-mask":
+        result = run_mask(args, torch, synth, sv)
+    elif args.workload.startswith("tree"):
         result = run_tree(args, torch, synth, sv)
     else:
         result = run_chain(args, torch, synth, sv)

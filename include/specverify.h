@@ -168,6 +168,38 @@ SV_API int spec_verify_tree(const void* target_logits, const int32_t* node_token
                      size_t workspace_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * Tree attention mask and depth positions: the inputs of the one forward
+ * pass that scores a whole token tree (CMU 15-779 lecture 17 notes, section
+ * 4.3: a depth-first linearised tree, a topology-aware causal mask under
+ * which each node sees only itself and its ancestors, and positions by
+ * depth; exercise 5).
+ *
+ * parents        [B][N]        int32   parents[b][0] == -1, 0 <= parents[b][i] < i
+ *                                      (any order with parents first; depth-first
+ *                                      is the one the verifier's KV layout uses)
+ * out_mask       [B][N][words] uint64  words = ceil(N / 64); bit (j % 64) of word
+ *                                      j / 64 of row i is 1 iff node j is node i
+ *                                      or one of its ancestors (the root
+ *                                      included).  Byte for byte this is each
+ *                                      row's bits packed little-endian, bit j of
+ *                                      the row at byte j / 8, bit j % 8.  The
+ *                                      verified prefix before the root is
+ *                                      visible to every row and not included.
+ * out_depth      [B][N]        int32   edges from the root (root 0); the position
+ *                                      id of node i is the root's position plus
+ *                                      out_depth[b][i]
+ * out_tree_depth [B]           int32   deepest node's depth; may be NULL
+ * A request whose parent array is malformed, or with a node deeper than
+ * max_depth, gets all-zero rows and -1 depths (and tree depth -1).
+ * Limits: B >= 0 (B == 0 is a no-op), 1 <= N <= SV_MAX_TREE_NODES,
+ *         0 <= max_depth <= SV_MAX_TREE_DEPTH; out_mask 8-byte aligned
+ *         (SV_ERR_ALIGN otherwise).  No workspace.
+ * ---------------------------------------------------------------------- */
+SV_API int spec_tree_mask(const int32_t* parents, int B, int N, int max_depth,
+                   uint64_t* out_mask, int32_t* out_depth, int32_t* out_tree_depth,
+                   void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * Debug probabilities for every draft position i < gamma, whether or not
  * verification would reach it:
  *   p_at_draft[b][i]    = p_i(x_i)
@@ -221,7 +253,8 @@ typedef enum {
   SV_K_PROBS_FINALIZE = 9,
   SV_K_WORKSPACE_CLEAR = 10,
   SV_K_TREE_VERIFY = 11,      /* tree: every depth step of every request in one launch */
-  SV_K_COUNT = 12
+  SV_K_TREE_MASK = 12,        /* tree attention mask and depth positions */
+  SV_K_COUNT = 13
 } sv_kernel;
 
 /* Name of a kernel id (static storage; "unknown" outside [0, SV_K_COUNT)). */

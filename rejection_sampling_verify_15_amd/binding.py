@@ -34,12 +34,14 @@ EXPORTS = {
     "sv_probs_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "spec_probs_debug": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 4 +
                          [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "spec_tree_mask": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int] +
+                       [ctypes.c_void_p] * 4),
     "sv_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
     "sv_timing_begin": (ctypes.c_int, [ctypes.c_int]),
     "sv_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
                                      ctypes.c_int]),
 }
-SV_K_COUNT = 12
+SV_K_COUNT = 13
 
 _LIB = None
 _LOCK = threading.Lock()
@@ -201,6 +203,36 @@ def verify_tree(logits: torch.Tensor, node_tokens: torch.Tensor, parents: torch.
                             _ptr(out_path), _ptr(out_n), _ptr(ws), ws.numel(), _stream_handle(dev))
     _check(st, "spec_verify_tree")
     return out_tokens, out_path, out_n
+
+
+def tree_mask(parents: torch.Tensor, max_depth: int, out_mask: Optional[torch.Tensor] = None,
+              out_depth: Optional[torch.Tensor] = None,
+              out_tree_depth: Optional[torch.Tensor] = None):
+    """spec_tree_mask over device tensors.  parents [B, N] int32.  Returns
+    (mask [B, N, ceil(N/64)] int64 holding the uint64 row words, depth [B, N]
+    int32, tree_depth [B] int32)."""
+    _need_cuda(parents, "parents")
+    if parents.dim() != 2 or parents.dtype != torch.int32:
+        raise ValueError("parents must be int32 with shape [B, N]")
+    B, N = parents.shape
+    dev = parents.device
+    words = (N + 63) // 64
+    if out_mask is None:
+        out_mask = torch.empty((B, N, words), dtype=torch.int64, device=dev)
+    if out_depth is None:
+        out_depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if out_tree_depth is None:
+        out_tree_depth = torch.empty((B,), dtype=torch.int32, device=dev)
+    for name, t, shape, dtype in (("out_mask", out_mask, (B, N, words), torch.int64),
+                                  ("out_depth", out_depth, (B, N), torch.int32),
+                                  ("out_tree_depth", out_tree_depth, (B,), torch.int32)):
+        _need_cuda(t, name)
+        if tuple(t.shape) != shape or t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype} with shape {shape}")
+    st = lib().spec_tree_mask(_ptr(parents), B, N, int(max_depth), _ptr(out_mask), _ptr(out_depth),
+                              _ptr(out_tree_depth), _stream_handle(dev))
+    _check(st, "spec_tree_mask")
+    return out_mask, out_depth, out_tree_depth
 
 
 def probs_debug(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
