@@ -11,8 +11,8 @@ float64, written from these sources (cited by page title and section):
 * CMU 15-779 lecture 17 notes ("LLM serving (2): speculative decoding"),
   sections 2.2-2.4 (greedy verification, speculative sampling, Algorithm 1),
   4.3 (the topology-aware causal mask and depth positions of tree-parallel
-  decoding), 4.4 (VerifyGreedy on a token tree) and 4.5 (naive sampling on a
-  tree).
+  decoding), 4.4 (VerifyGreedy on a token tree) and 4.5 (naive sampling and multi-step
+  speculative sampling on a tree).
 * "LLM speculative decoding close-reading notes 02: original speculative
   decoding", sections 4 (the full algorithm with uniforms r_i), 5.1 (residual
   normaliser), 10 (greedy special case) and 11.3 (per-request RNG streams).
@@ -29,4 +29,5 @@ from .specverify_oracle import (  # noqa: F401
     logits_to_f64, softmax_t, accept_threshold, inverse_cdf_draw,
     chain_distributions, chain_decide_request, verify_chain,
     verify_tree, probs_debug, tree_node_depths, TreeMaskResult, tree_attention_mask,
+    mss_thresholds, mss_node, mss_proposals, tree_children, verify_tree_mss,
 )

@@ -36,6 +36,22 @@ R11 bad input makes a whole request invalid (count -1, tokens -1): a draft
     token or tree node token outside [0, V), a temperature that is negative,
     not finite, or positive but below the smallest normal float32, a sampling request with a uniform outside [0, 1), a
     malformed parent array, or a tree deeper than max_depth.
+R12 MSS on a tree (T > 0): the children of node n are tested in index order;
+    a child whose token repeats an earlier sibling's is skipped (only the
+    first child carrying a token can be reached, as in R9).  The children are
+    taken to be drawn without replacement from q_n = softmax(draft_n / T), so
+    the j-th tested child is tested against q_n with the earlier tested
+    children's tokens removed and renormalised (lecture 17 notes section 4.5,
+    the fix that keeps MSS unbiased; exercise 7).
+R13 MSS degenerate cases (reachable only through rounding or impossible
+    draws): a rejection that leaves the residual without mass makes the node
+    draw from p_n; once the tested children's tokens hold all of q_n's mass,
+    the remaining children are not tested and the node draws from the
+    current residual.
+R14 MSS uniforms: accept_uniforms[b, j] is the test of node j as a child
+    (entry 0 is never used); draw_uniforms[b, n] is the draw when the descent
+    stops at node n.  A sampling request needs both in [0, 1) (entry 0 of
+    accept_uniforms excepted).
 """
 from __future__ import annotations
 
@@ -311,6 +327,164 @@ def verify_tree(logits: np.ndarray, node_tokens: np.ndarray, parents: np.ndarray
                 if int(par[j]) == node and int(tok[j]) == c:
                     nxt = j
                     break
+            if nxt < 0:
+                break
+            path.append(nxt)
+            node = nxt
+        emitted = [int(tok[j]) for j in path] + [c]
+        out[b, :len(emitted)] = emitted
+        path_out[b, :len(path)] = path
+        nacc[b] = len(path)
+        decisions[b] = dec
+    return TreeResult(out, path_out, nacc, decisions)
+
+
+# ---------------------------------------------------------------------------
+# multi-step speculative sampling on a token tree (MSS)
+# ---------------------------------------------------------------------------
+def mss_thresholds(p: np.ndarray, proposals):
+    """Multi-step speculative sampling at one node along the path on which
+    every proposal is rejected (lecture 17 notes section 4.5,
+    VerifyStochastic; exercise 6).
+
+    p is the target distribution at the node; proposals is the list of
+    (token x_j, q_j) in test order, q_j being the distribution x_j was drawn
+    from.  The residual starts as r_1 = p.  Proposal j is accepted with
+    probability tau_j = min(1, r_j(x_j) / q_j(x_j)) (R2); on rejection the
+    residual becomes r_{j+1} = norm(max(0, r_j - q_j)).
+
+    Returns (taus, residuals): tau_j for each proposal reached, and r_{j+1}
+    after each rejection.  The lists stop early where a rejection has
+    probability zero (tau_j == 1), and residuals[j] is None where a rejection
+    leaves no residual mass (R13)."""
+    r = np.asarray(p, dtype=np.float64)
+    taus, residuals = [], []
+    for x, q in proposals:
+        tau = accept_threshold(float(r[x]), float(q[x]))
+        taus.append(tau)
+        if tau >= 1.0:
+            break
+        w = residual_weights(r, q)
+        W = float(w.sum())
+        if W <= 0.0:
+            residuals.append(None)
+            break
+        r = w / W
+        residuals.append(r)
+    return taus, residuals
+
+
+def mss_node(p: np.ndarray, proposals, u_accept, u_draw: float):
+    """One node's MSS decision with the caller's uniforms: the first proposal
+    j with u_accept[j] <= tau_j is accepted; if none is, the token is drawn
+    from the last residual with u_draw (R4), or from p where the residual is
+    empty (R13).  Returns (accepted index or -1, token, decisions)."""
+    taus, residuals = mss_thresholds(p, proposals)
+    dec: List[Decision] = []
+    for j, tau in enumerate(taus):
+        u = float(u_accept[j])
+        ok = u <= tau
+        dec.append(Decision("accept", j, u, tau, int(ok), abs(u - tau)))
+        if ok:
+            return j, int(proposals[j][0]), dec
+    w = p if not residuals else residuals[-1]
+    if w is None:
+        w = p
+    c, margin = inverse_cdf_draw(w, u_draw)
+    dec.append(Decision("draw", -1, float(u_draw), float("nan"), c, margin))
+    return -1, c, dec
+
+
+def mss_proposals(q: np.ndarray, tokens):
+    """Children drawn without replacement from q, tested in order (R12): the
+    j-th child's distribution q_j is q with the tokens of the earlier children
+    removed and renormalised (lecture 17 notes section 4.5: the fix that
+    keeps MSS unbiased for sampled children; exercise 7).  Stops where the
+    earlier children hold all of q's mass (R13)."""
+    proposals = []
+    qj = np.asarray(q, dtype=np.float64)
+    for x in tokens:
+        proposals.append((int(x), qj))
+        rest = qj.copy()
+        rest[x] = 0.0
+        s = float(rest.sum())
+        if s <= 0.0:
+            break
+        qj = rest / s
+    return proposals
+
+
+def tree_children(par: np.ndarray, tok: np.ndarray, node: int):
+    """Children of `node` in index order, skipping a child whose token repeats
+    an earlier sibling's (R12).  Returns (node ids, tokens)."""
+    ids, seen = [], set()
+    for j in range(node + 1, len(par)):
+        if int(par[j]) == node and int(tok[j]) not in seen:
+            ids.append(j)
+            seen.add(int(tok[j]))
+    return ids, [int(tok[j]) for j in ids]
+
+
+def verify_tree_mss(logits: np.ndarray, draft_logits: np.ndarray, node_tokens: np.ndarray,
+                    parents: np.ndarray, accept_uniforms: np.ndarray, draw_uniforms: np.ndarray,
+                    temperature: np.ndarray, dtype: str, max_depth: int,
+                    requests=None) -> TreeResult:
+    """Tree verification by multi-step speculative sampling (lecture 17 notes
+    section 4.5, VerifyStochastic with the children sampled without
+    replacement; section 4.4 VerifyGreedy for T == 0).
+
+    At node n with target p_n and draft q_n = softmax(draft_logits[n] / T)
+    (the distribution n's children were drawn from), the children are tested
+    in index order as in mss_node, child j with accept_uniforms[b, j].  An
+    accepted child becomes the next node; if every child is rejected, or n
+    has none, the token drawn with draw_uniforms[b, n] is emitted and the
+    descent stops.  Greedy requests descend by argmax as in verify_tree."""
+    B, N, V = logits.shape
+    L1 = max_depth + 1
+    out = np.full((B, L1), -1, dtype=np.int32)
+    path_out = np.full((B, L1), -1, dtype=np.int32)
+    nacc = np.full(B, -1, dtype=np.int32)
+    decisions: List[List[Decision]] = [[] for _ in range(B)]
+    todo = range(B) if requests is None else requests
+    for b in todo:
+        T = float(np.float32(temperature[b]))
+        par = np.asarray(parents[b], dtype=np.int64)
+        tok = np.asarray(node_tokens[b], dtype=np.int64)
+        depth = tree_node_depths(par)
+        if depth is None or not _temperature_ok(T) or np.any(depth > max_depth):
+            continue
+        if N > 1 and (np.any(tok[1:] < 0) or np.any(tok[1:] >= V)):
+            continue
+        ua = np.asarray(accept_uniforms[b], dtype=np.float32).astype(np.float64)
+        ud = np.asarray(draw_uniforms[b], dtype=np.float32).astype(np.float64)
+        if T > 0.0:
+            used = np.concatenate([ua[1:], ud])
+            if not np.all(np.isfinite(used)) or np.any(used < 0.0) or np.any(used >= 1.0):
+                continue
+        node = 0
+        path: List[int] = []
+        dec: List[Decision] = []
+        while True:
+            row = logits_to_f64(logits[b, node], dtype)
+            if T == 0.0:
+                c = int(np.argmax(row))
+                dec.append(Decision("greedy", node, float("nan"), float("nan"), c, float("inf")))
+                nxt = -1
+                for j in range(node + 1, N):
+                    if int(par[j]) == node and int(tok[j]) == c:
+                        nxt = j
+                        break
+            else:
+                p = softmax_t(row, T)
+                ids, toks = tree_children(par, tok, node)
+                props = []
+                if ids:
+                    q = softmax_t(logits_to_f64(draft_logits[b, node], dtype), T)
+                    props = mss_proposals(q, toks)
+                ids = ids[:len(props)]
+                j, c, d = mss_node(p, props, [ua[i] for i in ids], float(ud[node]))
+                dec.extend(d)
+                nxt = ids[j] if j >= 0 else -1
             if nxt < 0:
                 break
             path.append(nxt)
