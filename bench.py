@@ -16,8 +16,9 @@ oracle timed on this host's cores on a bounded sample.
 Other workloads (--workload) report the same line for the single-request
 latency case (B=1, V=32000, also replayed from a HIP graph), the deep case
 (B=256, gamma=8, V=151936, Zipf logits), the token-tree cases (B=32, 64
-nodes, greedy or naive sampling; rows are node rows) and the tree attention
-mask builder on the same tree shape (rows are mask rows).
+nodes, greedy, naive sampling or multi-step speculative sampling; rows are
+node rows) and the tree attention mask builder on the same tree shape (rows
+are mask rows).
 """
 from __future__ import annotations
 
@@ -107,7 +108,7 @@ def cpu_baseline(ci, budget_s: float = 15.0):
                       f"fresh uniforms, numpy fp64, {wall:.1f} s wall, {cpu:.1f} s CPU"}
 
 
-WORKLOADS = ("batched", "single", "deep", "tree-greedy", "tree-sampling", "tree-mask")
+WORKLOADS = ("batched", "single", "deep", "tree-greedy", "tree-sampling", "tree-mss", "tree-mask")
 
 
 def percentiles(xs):
@@ -244,23 +245,40 @@ def graph_replay(torch, stream, sv, tgt_drf, tok, u, T, out_t, out_n, ws, steps)
 
 def run_tree(args, torch, synth, sv, oracle_sample=True):
     dev = torch.device("cuda:0")
+    mss = args.workload == "tree-mss"
     temp = 0.0 if args.workload == "tree-greedy" else 1.0
-    ti = synth.tree_inputs(temperature=temp)
-    desc = (f"token-tree verify ({'greedy' if temp == 0 else 'naive sampling, T=1'}): B=32, N=64 nodes, "
-            f"depth <= 8, branching 1..4, V=128256, bf16 logits")
-    R = max(2, math.ceil(2 * MALL_BYTES / ti.logits.nbytes) + 1)
-    lg0 = torch.from_numpy(np.ascontiguousarray(ti.logits).view(np.int16)).to(dev).view(torch.bfloat16)
+    ti = synth.tree_inputs(temperature=temp, keep_draft=mss)
+    mode = ("greedy" if temp == 0 else
+            "multi-step speculative sampling, T=1, children drawn without replacement from each node's "
+            "draft row" if mss else "naive sampling, T=1")
+    desc = (f"token-tree verify ({mode}): B=32, N=64 nodes, depth <= 8, branching 1..4, V=128256, "
+            f"bf16 logits")
+    set_bytes = ti.logits.nbytes * (2 if mss else 1)
+    R = max(2, math.ceil(2 * MALL_BYTES / set_bytes) + 1)
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    lg0 = dev_bf16(ti.logits)
     sets = [lg0] + [lg0.clone() for _ in range(R - 1)]
+    if mss:
+        dr0 = dev_bf16(ti.draft_logits)
+        dsets = [dr0] + [dr0.clone() for _ in range(R - 1)]
+        ud = torch.from_numpy(ti.draw_uniforms).to(dev)
     tok = torch.from_numpy(ti.node_tokens).to(dev)
     par = torch.from_numpy(ti.parents).to(dev)
     u = torch.from_numpy(ti.uniforms).to(dev)
     T = torch.from_numpy(ti.temperature).to(dev)
-    ws = sv.workspace(sv.lib().sv_tree_workspace_bytes(ti.B, ti.N, ti.V, sv.SV_BF16), dev)
+    query = sv.lib().sv_tree_mss_workspace_bytes if mss else sv.lib().sv_tree_workspace_bytes
+    ws = sv.workspace(query(ti.B, ti.N, ti.V, sv.SV_BF16), dev)
     stream = torch.cuda.current_stream(dev)
     outs = {}
 
     def step(i):
-        outs["r"] = sv.verify_tree(sets[i % R], tok, par, u, T, ti.max_depth, ws=ws)
+        if mss:
+            outs["r"] = sv.verify_tree_mss(sets[i % R], dsets[i % R], tok, par, u, ud, T, ti.max_depth, ws=ws)
+        else:
+            outs["r"] = sv.verify_tree(sets[i % R], tok, par, u, T, ti.max_depth, ws=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -270,9 +288,16 @@ def run_tree(args, torch, synth, sv, oracle_sample=True):
         events_ms, _ = time_calls(torch, stream, step, args.steps)
     calls = per_call_us(torch, stream, step, min(args.steps, 2000))
     nacc = outs["r"][2].cpu().numpy()
+    path = outs["r"][1].cpu().numpy()
     visited = int(np.sum(nacc + 1))  # the root and every accepted node are read
     es = 2
-    rd = visited * ti.V * es
+    rows = visited
+    if mss:
+        # a visited node with children also has its draft row read
+        for b in range(ti.B):
+            for n in [0] + [int(x) for x in path[b, :nacc[b]]]:
+                rows += int(np.any(ti.parents[b] == n))
+    rd = rows * ti.V * es
     call_us = 1e3 * total_ms / args.steps
     per_call = {name: kt.ms[name] * 1e3 / args.steps for name in kt.launches}
     dominant = max(per_call, key=per_call.get)  # tree_verify; tree_node_pass in the multi-launch form
@@ -285,9 +310,11 @@ def run_tree(args, torch, synth, sv, oracle_sample=True):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "kernel": dominant,
                      "kernel_us_per_call": dom_us, "algorithmic_bytes": rd,
-                     "note": "bytes of the visited nodes' rows per call over the summed duration of "
+                     "note": "bytes of the visited nodes' rows (and, for MSS, the draft rows of "
+                             "visited nodes that have children) per call over the summed duration of "
                              f"that call's {dominant} launches; the descent is a chain of dependent "
-                             "levels, so the time is latency, not bytes"},
+                             "levels (and, for MSS, of residual passes), so the time is latency, not "
+                             "bytes"},
         "kernels_us_per_call": per_call,
         "launches_per_call": {name: kt.launches[name] / args.steps for name in kt.launches},
         "whole_call": {"us": call_us, "us_with_kernel_events": 1e3 * events_ms / args.steps,
@@ -295,8 +322,9 @@ def run_tree(args, torch, synth, sv, oracle_sample=True):
                        "algorithmic_bytes": rd, "GBps": rd / (call_us * 1e-6) / 1e9,
                        "frac": rd / (call_us * 1e-6) / 1e9 / PEAK_HBM_GBPS},
     })
+    result["config"]["rows_read_per_call"] = rows
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_tree(ti)
+        result["cpu_baseline"] = cpu_baseline_tree(ti, mss=mss)
     return result
 
 
@@ -373,7 +401,7 @@ def cpu_baseline_mask(parents, max_depth, budget_s: float = 10.0):
                       f"{wall:.1f} s wall, {cpu:.1f} s CPU"}
 
 
-def cpu_baseline_tree(ti, budget_s: float = 15.0):
+def cpu_baseline_tree(ti, budget_s: float = 15.0, mss: bool = False):
     """The oracle's tree verification on the same batch, request by request,
     until the budget is spent; the unit is node rows per second."""
     import oracle
@@ -382,8 +410,13 @@ def cpu_baseline_tree(ti, budget_s: float = 15.0):
     c0 = time.process_time()
     while time.perf_counter() - w0 < budget_s:
         for b in range(ti.B):
-            oracle.verify_tree(ti.logits[b:b + 1], ti.node_tokens[b:b + 1], ti.parents[b:b + 1],
-                               ti.uniforms[b:b + 1], ti.temperature[b:b + 1], ti.dtype, ti.max_depth)
+            if mss:
+                oracle.verify_tree_mss(ti.logits[b:b + 1], ti.draft_logits[b:b + 1], ti.node_tokens[b:b + 1],
+                                       ti.parents[b:b + 1], ti.uniforms[b:b + 1], ti.draw_uniforms[b:b + 1],
+                                       ti.temperature[b:b + 1], ti.dtype, ti.max_depth)
+            else:
+                oracle.verify_tree(ti.logits[b:b + 1], ti.node_tokens[b:b + 1], ti.parents[b:b + 1],
+                                   ti.uniforms[b:b + 1], ti.temperature[b:b + 1], ti.dtype, ti.max_depth)
             rows += ti.N
             requests += 1
             if time.perf_counter() - w0 >= budget_s:

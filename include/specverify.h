@@ -168,6 +168,52 @@ SV_API int spec_verify_tree(const void* target_logits, const int32_t* node_token
                      size_t workspace_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * Token-tree verification by multi-step speculative sampling, MSS (CMU
+ * 15-779 lecture 17 notes, section 4.5: VerifyStochastic, unbiased when the
+ * children are sampled without replacement and q_j is renormalised, and
+ * exercises 6-7; section 4.4 VerifyGreedy for T == 0).
+ *
+ * Node n's children were drawn without replacement from
+ * q_n = softmax(draft_logits[b][n] / T).  At node n, with p_n =
+ * softmax(target_logits[b][n] / T) and the residual r = p_n: the children are
+ * tested in index order, skipping a child whose token an earlier sibling
+ * already carries.  Child j (token x) is tested against q_j = q_n without the
+ * tokens tested before, renormalised: accept iff accept_uniforms[b][j] <= tau,
+ * tau = 1 if q_j(x) <= r(x) else r(x)/q_j(x).  An accepted child becomes the
+ * next node.  A rejection sets r = norm(max(0, r - q_j)).  If every child is
+ * rejected, or n has none, the node emits a token drawn from r (p_n for a
+ * leaf) with draw_uniforms[b][n] and the descent stops.  Two degenerate cases
+ * only arise through rounding or impossible draws.  A rejection that leaves r
+ * without mass draws from p_n instead.  Once the tested tokens hold all of
+ * q_n's mass, later children are not tested.  T == 0 is greedy descent, as in
+ * spec_verify_tree; draft logits and uniforms are then not read.
+ *
+ * target_logits   [B][N][V]  dtype  target row of each node
+ * draft_logits    [B][N][V]  dtype  draft row of each node (rows of leaves are
+ *                                   never read)
+ * node_tokens     [B][N]     int32  as spec_verify_tree
+ * parents         [B][N]     int32  as spec_verify_tree
+ * accept_uniforms [B][N]     float  entry j: the test of node j (entry 0 unused)
+ * draw_uniforms   [B][N]     float  entry n: the draw when the descent stops at n
+ * temperature     [B]        float  0 greedy, > 0 MSS
+ * out_tokens, out_path_nodes, out_num_accepted: as spec_verify_tree.
+ * A request is invalid (-1) if any node has more than 64 children, or, for
+ * a sampling request, if accept_uniforms[b][1..N-1] or draw_uniforms[b] leave
+ * [0, 1).
+ * Limits: as spec_verify_tree, and V <= 524288 with B * (ceil(V / 2048) + 1)
+ * <= 2^20 (SV_ERR_SHAPE otherwise; the workspace query then returns 0).
+ * ---------------------------------------------------------------------- */
+SV_API size_t sv_tree_mss_workspace_bytes(int B, int N, int V, int dtype);
+
+SV_API int spec_verify_tree_mss(const void* target_logits, const void* draft_logits,
+                         const int32_t* node_tokens, const int32_t* parents,
+                         const float* accept_uniforms, const float* draw_uniforms,
+                         const float* temperature, int B, int N, int V, int max_depth,
+                         int dtype, int32_t* out_tokens, int32_t* out_path_nodes,
+                         int32_t* out_num_accepted, void* workspace,
+                         size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * Tree attention mask and depth positions: the inputs of the one forward
  * pass that scores a whole token tree (CMU 15-779 lecture 17 notes, section
  * 4.3: a depth-first linearised tree, a topology-aware causal mask under
@@ -254,7 +300,8 @@ typedef enum {
   SV_K_WORKSPACE_CLEAR = 10,
   SV_K_TREE_VERIFY = 11,      /* tree: every depth step of every request in one launch */
   SV_K_TREE_MASK = 12,        /* tree attention mask and depth positions */
-  SV_K_COUNT = 13
+  SV_K_TREE_MSS = 13,         /* tree: multi-step speculative sampling, one launch */
+  SV_K_COUNT = 14
 } sv_kernel;
 
 /* Name of a kernel id (static storage; "unknown" outside [0, SV_K_COUNT)). */

@@ -52,6 +52,8 @@ R14 MSS uniforms: accept_uniforms[b, j] is the test of node j as a child
     (entry 0 is never used); draw_uniforms[b, n] is the draw when the descent
     stops at node n.  A sampling request needs both in [0, 1) (entry 0 of
     accept_uniforms excepted).
+R15 MSS trees allow at most 64 children per node (a contract limit of the
+    library, not of the method); a tree with a wider node is invalid (R11).
 """
 from __future__ import annotations
 
@@ -425,6 +427,9 @@ def tree_children(par: np.ndarray, tok: np.ndarray, node: int):
     return ids, [int(tok[j]) for j in ids]
 
 
+MSS_MAX_CHILDREN = 64
+
+
 def verify_tree_mss(logits: np.ndarray, draft_logits: np.ndarray, node_tokens: np.ndarray,
                     parents: np.ndarray, accept_uniforms: np.ndarray, draw_uniforms: np.ndarray,
                     temperature: np.ndarray, dtype: str, max_depth: int,
@@ -454,6 +459,8 @@ def verify_tree_mss(logits: np.ndarray, draft_logits: np.ndarray, node_tokens: n
         if depth is None or not _temperature_ok(T) or np.any(depth > max_depth):
             continue
         if N > 1 and (np.any(tok[1:] < 0) or np.any(tok[1:] >= V)):
+            continue
+        if N > 1 and np.bincount(par[1:], minlength=N).max() > MSS_MAX_CHILDREN:    # R15
             continue
         ua = np.asarray(accept_uniforms[b], dtype=np.float32).astype(np.float64)
         ud = np.asarray(draw_uniforms[b], dtype=np.float32).astype(np.float64)

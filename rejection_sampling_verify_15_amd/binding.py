@@ -34,6 +34,9 @@ EXPORTS = {
     "sv_probs_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "spec_probs_debug": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 4 +
                          [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "sv_tree_mss_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "spec_verify_tree_mss": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 5 +
+                             [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
     "spec_tree_mask": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int] +
                        [ctypes.c_void_p] * 4),
     "sv_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
@@ -41,7 +44,7 @@ EXPORTS = {
     "sv_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
                                      ctypes.c_int]),
 }
-SV_K_COUNT = 13
+SV_K_COUNT = 14
 
 _LIB = None
 _LOCK = threading.Lock()
@@ -202,6 +205,44 @@ def verify_tree(logits: torch.Tensor, node_tokens: torch.Tensor, parents: torch.
                             _ptr(temperature), B, N, V, int(max_depth), dt, _ptr(out_tokens),
                             _ptr(out_path), _ptr(out_n), _ptr(ws), ws.numel(), _stream_handle(dev))
     _check(st, "spec_verify_tree")
+    return out_tokens, out_path, out_n
+
+
+def verify_tree_mss(logits: torch.Tensor, draft_logits: torch.Tensor, node_tokens: torch.Tensor,
+                    parents: torch.Tensor, accept_uniforms: torch.Tensor, draw_uniforms: torch.Tensor,
+                    temperature: torch.Tensor, max_depth: int, ws: Optional[torch.Tensor] = None):
+    """spec_verify_tree_mss over device tensors (multi-step speculative
+    sampling; greedy descent for T == 0).  Returns (out_tokens, out_path_nodes,
+    out_num_accepted) with shapes [B, max_depth+1], [B, max_depth+1], [B]."""
+    _need_cuda(logits, "logits")
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, N, V]")
+    B, N, V = logits.shape
+    dev = logits.device
+    dt = _dtype_code(logits)
+    _need_cuda(draft_logits, "draft_logits")
+    if draft_logits.dtype != logits.dtype or tuple(draft_logits.shape) != (B, N, V):
+        raise ValueError("draft_logits must match logits' dtype and shape [B, N, V]")
+    for name, t, shape, dtype in (("node_tokens", node_tokens, (B, N), torch.int32),
+                                  ("parents", parents, (B, N), torch.int32),
+                                  ("accept_uniforms", accept_uniforms, (B, N), torch.float32),
+                                  ("draw_uniforms", draw_uniforms, (B, N), torch.float32),
+                                  ("temperature", temperature, (B,), torch.float32)):
+        _need_cuda(t, name)
+        if tuple(t.shape) != shape or t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype} with shape {shape}")
+    out_tokens = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    out_path = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    out_n = torch.empty((B,), dtype=torch.int32, device=dev)
+    L = lib()
+    nbytes = L.sv_tree_mss_workspace_bytes(B, N, V, dt)
+    if ws is None:
+        ws = workspace(max(int(nbytes), 256), dev)
+    st = L.spec_verify_tree_mss(_ptr(logits), _ptr(draft_logits), _ptr(node_tokens), _ptr(parents),
+                                _ptr(accept_uniforms), _ptr(draw_uniforms), _ptr(temperature),
+                                B, N, V, int(max_depth), dt, _ptr(out_tokens), _ptr(out_path),
+                                _ptr(out_n), _ptr(ws), ws.numel(), _stream_handle(dev))
+    _check(st, "spec_verify_tree_mss")
     return out_tokens, out_path, out_n
 
 

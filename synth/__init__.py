@@ -318,6 +318,9 @@ class TreeInputs:
     parents     : [B, N] int32, parents[:,0] = -1, 0 <= parents[:,i] < i
     uniforms    : [B, N] float32, one per node (used when the node is visited)
     temperature : [B] float32, 0 => greedy descent, > 0 => naive sampling
+    draft_logits  : [B, N, V] draft logits of every node (the row its children
+                    were drawn from), or None when not kept
+    draw_uniforms : [B, N] float32, a second uniform per node, or None
     """
     logits: np.ndarray
     node_tokens: np.ndarray
@@ -331,6 +334,8 @@ class TreeInputs:
     max_depth: int
     name: str = ""
     recipe: str = ""
+    draft_logits: Optional[np.ndarray] = None
+    draw_uniforms: Optional[np.ndarray] = None
 
 
 def random_tree_shape(rng, N: int, max_depth: int, max_branch: int = 4):
@@ -395,11 +400,16 @@ def tree_parent_arrays(seed: int, B: int, N: int, max_depth: int, max_branch: in
 def tree_inputs(seed: int = SEED_BASE + 5, B: int = 32, N: int = 64, V: int = 128256,
                 max_depth: int = 8, temperature: float = 0.0, dtype: str = "bf16",
                 family: str = "peaked", draft_sigma: float = 1.0,
-                max_branch: int = 4, name: str = "tree") -> TreeInputs:
+                max_branch: int = 4, name: str = "tree", keep_draft: bool = False) -> TreeInputs:
     """Token trees: random shape (<= max_depth, branching 1..max_branch),
     depth-first relabelled; per-node target logits from `family`; the children
     of each node are drawn without replacement from the draft softmax at that
-    node (draft logits = node target logits + N(0, draft_sigma^2), T = 1)."""
+    node (draft logits = node target logits + N(0, draft_sigma^2), T = 1).
+
+    With keep_draft, every node's draft row is kept (rounded to dtype, and the
+    children are drawn from exactly that rounded row), and a second uniform
+    array is drawn; the target rows, shapes and first uniforms are the same
+    as without it."""
     r_shape, r_tgt, r_noise, r_tok, r_u = _streams(seed, 5)
     fam = FAMILIES[family]
     parents = np.empty((B, N), dtype=np.int32)
@@ -407,6 +417,7 @@ def tree_inputs(seed: int = SEED_BASE + 5, B: int = 32, N: int = 64, V: int = 12
     logits32 = fam(r_tgt, B * N, V).reshape(B, N, V)
     stored = _as_dtype(logits32, dtype)
     del logits32
+    draft = np.empty_like(stored) if keep_draft else None
     for b in range(B):
         par_c, ch_c = random_tree_shape(r_shape, N, max_depth, max_branch)
         order, new_id = dfs_relabel(ch_c)
@@ -414,19 +425,27 @@ def tree_inputs(seed: int = SEED_BASE + 5, B: int = 32, N: int = 64, V: int = 12
             parents[b, new_id[old]] = -1 if par_c[old] < 0 else new_id[par_c[old]]
         for old in order:
             kids = ch_c[old]
-            if not kids:
-                continue
             n = new_id[old]
+            if not kids and not keep_draft:
+                continue
             row = _widen(stored[b, n], dtype).astype(np.float32)
             d = row + r_noise.standard_normal(V, dtype=np.float32) * np.float32(draft_sigma)
+            if keep_draft:
+                draft[b, n] = _as_dtype(d, dtype)
+                d = _widen(draft[b, n], dtype).astype(np.float32)
+            if not kids:
+                continue
             keys = d + gumbel(r_tok, V)
             top = np.argpartition(-keys, len(kids) - 1)[:len(kids)]
             top = top[np.argsort(-keys[top], kind="stable")]
             for c_old, tok in zip(kids, top):
                 tokens[b, new_id[c_old]] = int(tok)
     u = uniforms(r_u, (B, N))
+    u2 = uniforms(r_u, (B, N)) if keep_draft else None
     T = np.full(B, temperature, dtype=np.float32)
     recipe = (f"seed={seed} family={family} draft_sigma={draft_sigma} T={temperature} "
-              f"max_depth={max_depth} branch=1..{max_branch} dtype={dtype}")
-    return TreeInputs(stored, tokens, parents, u, T, dtype, B, N, V, max_depth, name, recipe)
+              f"max_depth={max_depth} branch=1..{max_branch} dtype={dtype}"
+              + (" draft rows kept" if keep_draft else ""))
+    return TreeInputs(stored, tokens, parents, u, T, dtype, B, N, V, max_depth, name, recipe,
+                      draft, u2)
 

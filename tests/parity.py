@@ -134,6 +134,55 @@ def compare_tree(res, tok_gpu, path_gpu, n_gpu, requests=None) -> Tally:
     return tally
 
 
+def mss_levels(decisions):
+    """The oracle's MSS decisions grouped by tree level: a level ends with an
+    accepted test, a draw or a greedy choice."""
+    levels, cur = [], []
+    for d in decisions:
+        cur.append(d)
+        if d.kind != "accept" or d.outcome == 1:
+            levels.append(cur)
+            cur = []
+    if cur:
+        levels.append(cur)
+    return levels
+
+
+def compare_tree_mss(res, tok_gpu, path_gpu, n_gpu, requests=None) -> Tally:
+    """Level by level: the GPU agrees at level d when its token and path slot
+    there equal the oracle's.  A disagreement is a boundary mismatch if one of
+    the level's decisions (accept tests and draw) lies within the window of
+    its threshold, and a hard failure otherwise; later levels are not
+    compared."""
+    tally = Tally()
+    B = res.out_tokens.shape[0]
+    todo = range(B) if requests is None else requests
+    for b in todo:
+        t = Tally()
+        n_or = int(res.num_accepted[b])
+        if n_or < 0:
+            if int(n_gpu[b]) != -1 or (tok_gpu[b] != -1).any() or (path_gpu[b] != -1).any():
+                t.hard.append((b, "invalid tree not flagged"))
+            tally.add(t)
+            continue
+        for d, decs in enumerate(mss_levels(res.decisions[b])):
+            t.decisions += len(decs)
+            near = [x for x in decs if x.margin < WINDOW]
+            t.in_window += len(near)
+            if int(tok_gpu[b, d]) != int(res.out_tokens[b, d]) or int(path_gpu[b, d]) != int(res.out_path[b, d]):
+                if near:
+                    t.mismatches += 1
+                else:
+                    t.hard.append((b, d, [(x.kind, x.margin) for x in decs]))
+                break
+        else:
+            if (int(n_gpu[b]) != n_or or not np.array_equal(tok_gpu[b], res.out_tokens[b])
+                    or not np.array_equal(path_gpu[b], res.out_path[b])):
+                t.hard.append((b, "tree outputs differ although decisions agree"))
+        tally.add(t)
+    return tally
+
+
 # ---------------------------------------------------------------------------
 # device transfer
 # ---------------------------------------------------------------------------

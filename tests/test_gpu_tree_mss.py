@@ -1,0 +1,139 @@
+"""GPU parity of spec_verify_tree_mss (multi-step speculative sampling on
+token trees) against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import rejection_sampling_verify_15_amd as sv
+from parity import Tally, assert_shared_workspace_zero, compare_tree_mss, to_device, to_device_logits
+
+pytestmark = pytest.mark.gpu
+
+
+def run_mss(ti, u_pairs, T=None):
+    lg = to_device_logits(ti.logits, ti.dtype)
+    dl = to_device_logits(ti.draft_logits, ti.dtype)
+    tok = to_device(ti.node_tokens.astype(np.int32))
+    par = to_device(ti.parents.astype(np.int32))
+    Tt = to_device((ti.temperature if T is None else T).astype(np.float32))
+    outs = []
+    for ua, ud in u_pairs:
+        o = sv.verify_tree_mss(lg, dl, tok, par, to_device(np.asarray(ua, np.float32)),
+                               to_device(np.asarray(ud, np.float32)), Tt, ti.max_depth)
+        outs.append(tuple(x.cpu().numpy() for x in o))
+    assert_shared_workspace_zero("tree mss")
+    return outs
+
+
+def mss_parity(ti, n_sets, label, seed=5, T=None, parents=None):
+    rng = np.random.default_rng(seed)
+    pairs = [(ti.uniforms, ti.draw_uniforms)] + [
+        (synth.uniforms(rng, (ti.B, ti.N)), synth.uniforms(rng, (ti.B, ti.N))) for _ in range(n_sets - 1)]
+    if parents is not None:
+        ti.parents = parents
+    temp = ti.temperature if T is None else T
+    print(f"[{label}] B={ti.B} N={ti.N} V={ti.V} dtype={ti.dtype} sets={n_sets}", flush=True)
+    gpu = run_mss(ti, pairs, temp)
+    tally = Tally()
+    for (ot, op, on), (ua, ud) in zip(gpu, pairs):
+        ref = oracle.verify_tree_mss(ti.logits, ti.draft_logits, ti.node_tokens, ti.parents, ua, ud,
+                                     temp, ti.dtype, ti.max_depth)
+        tally.add(compare_tree_mss(ref, ot, op, on))
+    print(f"[{label}] {tally}", flush=True)
+    tally.check(label)
+    return tally, gpu
+
+
+def test_mss_tree_workload():
+    """B=32 trees of 64 nodes over V=128256, children drawn without
+    replacement from each node's draft row, T=1."""
+    ti = synth.tree_inputs(temperature=1.0, keep_draft=True)
+    t, gpu = mss_parity(ti, 3, "mss tree workload")
+    assert max(int(on.max()) for _, _, on in gpu) >= 1
+
+
+@pytest.mark.parametrize("sigma", [0.3, 2.0])
+def test_mss_small_trees_many_rounds(sigma):
+    """Close drafts (many accepts) and far drafts (many rejections, so many
+    residual passes per node)."""
+    ti = synth.tree_inputs(seed=15400 + int(10 * sigma), B=24, N=40, V=3000, max_depth=6,
+                           temperature=1.0, draft_sigma=sigma, family="gauss", keep_draft=True)
+    t, gpu = mss_parity(ti, 25, f"mss small trees sigma={sigma}")
+    if sigma < 1.0:
+        assert max(int(on.max()) for _, _, on in gpu) >= 2
+
+
+def test_mss_f32_scalar_path_and_temperature():
+    ti = synth.tree_inputs(seed=15410, B=16, N=30, V=4001, max_depth=8, temperature=0.8,
+                           dtype="f32", family="gauss", draft_sigma=0.5, keep_draft=True)
+    mss_parity(ti, 8, "mss f32 V=4001")
+
+
+def test_mss_mixed_greedy_and_sampling():
+    """Odd requests greedy (argmax descent, draft rows unread), even MSS."""
+    ti = synth.tree_inputs(seed=15420, B=20, N=24, V=5000, max_depth=5, temperature=1.0,
+                           family="peaked", draft_sigma=0.5, keep_draft=True)
+    T = np.where(np.arange(ti.B) % 2 == 1, 0.0, 1.0).astype(np.float32)
+    mss_parity(ti, 6, "mss mixed greedy", T=T)
+    g = oracle.verify_tree(ti.logits, ti.node_tokens, ti.parents, ti.uniforms, T, ti.dtype, ti.max_depth)
+    (ot, op, on), = run_mss(ti, [(ti.uniforms, ti.draw_uniforms)], T)
+    odd = np.arange(ti.B) % 2 == 1
+    assert np.array_equal(ot[odd], g.out_tokens[odd]) and np.array_equal(on[odd], g.num_accepted[odd])
+
+
+def test_mss_wide_nodes_and_deep_chain():
+    """A root with 64 children (the limit), one with 65 (invalid), and a chain
+    64 deep."""
+    V = 700
+    rng = np.random.default_rng(15430)
+    B, N = 3, 66
+    parents = np.zeros((B, N), np.int32)
+    parents[:, 0] = -1
+    parents[0, 65] = 1                        # root: 64 children, node 1: one
+    parents[2] = np.arange(-1, N - 1)         # a chain
+    parents[2, 65] = 0
+    tl = synth.bf16_round_bits(rng.standard_normal((B, N, V)).astype(np.float32) * 0.5)
+    dl = synth.bf16_round_bits(synth.bf16_bits_as_float32(tl) + rng.standard_normal((B, N, V)).astype(np.float32) * 2.0)
+    tok = np.zeros((B, N), np.int32)
+    for b in range(B):
+        for n in range(N):
+            kids = [j for j in range(N) if parents[b, j] == n]
+            if kids:
+                q = oracle.softmax_t(synth.bf16_bits_as_float32(dl[b, n]).astype(np.float64), 1.0)
+                picks = rng.choice(V, size=len(kids), replace=False, p=q)
+                tok[b, kids] = picks
+    ti = synth.TreeInputs(tl, tok, parents, synth.uniforms(rng, (B, N)), np.ones(B, np.float32), "bf16",
+                          B, N, V, 64, "wide", "hand-built", dl, synth.uniforms(rng, (B, N)))
+    t, gpu = mss_parity(ti, 10, "mss wide nodes and chain")
+    for _, _, on in gpu:
+        assert on[1] == -1 and on[0] >= 0 and on[2] >= 0
+
+
+def test_mss_invalid_inputs():
+    ti = synth.tree_inputs(seed=15440, B=6, N=12, V=1000, max_depth=5, temperature=1.0,
+                           family="gauss", draft_sigma=0.3, keep_draft=True)
+    ua, ud = ti.uniforms.copy(), ti.draw_uniforms.copy()
+    ua[0, 0] = 7.0                 # never used: still valid
+    ua[1, 5] = 1.0
+    ud[2, 0] = -0.1
+    ti.parents[3, 4] = 9
+    ti.temperature[4] = -1.0
+    ti.node_tokens[5, 3] = ti.V
+    ti.uniforms, ti.draw_uniforms = ua, ud
+    t, gpu = mss_parity(ti, 1, "mss invalid")
+    on = gpu[0][2]
+    assert on[0] >= 0 and (on[1:] == -1).all()
+
+
+def test_mss_rejects_unsupported_shapes():
+    dev = torch.device("cuda:0")
+    L = sv.lib()
+    assert L.sv_tree_mss_workspace_bytes(4, 8, 600000, sv.SV_BF16) == 0      # over 256 chunks
+    assert L.sv_tree_mss_workspace_bytes(4, 8, 128256, sv.SV_BF16) > 0
+    x = torch.zeros((1, 2, 600000), dtype=torch.bfloat16, device=dev)
+    i2 = torch.zeros((1, 2), dtype=torch.int32, device=dev)
+    f2 = torch.zeros((1, 2), dtype=torch.float32, device=dev)
+    with pytest.raises(sv.SVError):
+        sv.verify_tree_mss(x, x, i2, i2, f2, f2, torch.ones(1, device=dev), 1)
