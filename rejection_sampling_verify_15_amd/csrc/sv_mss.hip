@@ -50,6 +50,9 @@ constexpr int kSlotT = 0, kSlotD = 1, kSlotTotP = 2, kSlotTotD = 3, kSlotTotR = 
 // children of one node (a node's tested children are held one per lane of
 // the choose workgroup)
 constexpr int kMssMaxChildren = kWave;
+// logits per stream workgroup (32 per lane; halving it doubles the
+// workgroups, and fewer requests then fit at once)
+constexpr int kMssChunk = kTreeChunk;
 
 struct MssArgs {
   const void* target;
@@ -107,6 +110,39 @@ __device__ inline MssParams mss_params(float T, float Mt, float Md, double Zt, d
   return q;
 }
 
+// The scalars of a residual pass travel tagged with the pass (the maxima as
+// chunk-style words, Z_t, Z_d and A as tagged doubles), so the pass word needs
+// no wait for their stores.  A tagged double loses its low 7 mantissa bits;
+// the choose workgroup uses the same truncated values (trunc7) throughout.
+struct MssScalars {
+  float Mt, Md;
+  double Zt, Zd, A;
+};
+__device__ inline double trunc7(double v) { return sum_value(tag_sum(v, 0)); }
+
+__device__ bool mss_wait_scalars(const MssArgs& a, int b, uint32_t s, MssScalars& sc) {
+  const uint64_t* cw = mss_ctl(a, b);
+  const int tag = pass_tag(s);
+  for (uint32_t spin = 0; spin < kTreeSpinLimit; ++spin) {
+    const uint64_t wmt = load_coherent(cw + kPrmMt);
+    const uint64_t wmd = load_coherent(cw + kPrmMd);
+    const uint64_t wzt = load_coherent(cw + kPrmZt);
+    const uint64_t wzd = load_coherent(cw + kPrmZd);
+    const uint64_t wa = load_coherent(cw + kPrmA);
+    if (chunk_at_level(wmt, tag) && chunk_at_level(wmd, tag) && sum_at_level(wzt, tag) &&
+        sum_at_level(wzd, tag) && sum_at_level(wa, tag)) {
+      sc.Mt = __uint_as_float(static_cast<uint32_t>(wmt));
+      sc.Md = __uint_as_float(static_cast<uint32_t>(wmd));
+      sc.Zt = sum_value(wzt);
+      sc.Zd = sum_value(wzd);
+      sc.A = sum_value(wa);
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return false;
+}
+
 // Waits for pass s of request b: its pass word, or 0 once the request has
 // stopped (or the wait gave up).
 __device__ uint64_t mss_wait_pass(const MssArgs& a, int b, uint32_t s) {
@@ -135,21 +171,23 @@ __device__ inline void mss_exit(const MssArgs& a, int b) {
 // ---------------------------------------------------------------------------
 template <int DT, bool VEC>
 __device__ void mss_stream_loop(const MssArgs& a, int b, int c) {
-  using Raw = LaneRun<DT, VEC>;
+  using Raw = LaneRun<DT, VEC, kMssChunk>;
   const float T = a.temperature[b];
   const bool greedy = T == 0.0f;
   const double l2t = greedy ? 0.0 : kLog2e / static_cast<double>(T);
-  const int c0 = c * kTreeChunk;
-  const int c1 = min(a.V, c0 + kTreeChunk);
+  const int c0 = c * kMssChunk;
+  const int c1 = min(a.V, c0 + kMssChunk);
   const int lane = threadIdx.x;
   uint64_t* slot = mss_slot(a, b, c);
   uint64_t* lp_out = mss_lanes(a, b, c, 0);
   uint64_t* lr_out = mss_lanes(a, b, c, 1);
-  Raw rt, rd;
-  // the node's stats, stored again under every later pass's tag
+  // The node's chunk of both rows (the residual passes recompute their fp64
+  // exponentials from it) and its stats, stored again under every later
+  // pass's tag.
   float mt = -INFINITY, md = -INFINITY;
   int arg = 0;
   double lp = 0.0, tot_p = 0.0, tot_d = 0.0;
+  Raw rt, rd;
   for (uint32_t s = 0;; ++s) {
     const uint64_t pw = mss_wait_pass(a, b, s);
     if (pw == 0) break;
@@ -207,19 +245,15 @@ __device__ void mss_stream_loop(const MssArgs& a, int b, int c) {
         }
       }
     } else {
-      // residual pass: the scalars were complete before the pass word
-      const uint64_t* cw = mss_ctl(a, b);
-      const float Mt = __uint_as_float(static_cast<uint32_t>(load_coherent(cw + kPrmMt)));
-      const float Md = __uint_as_float(static_cast<uint32_t>(load_coherent(cw + kPrmMd)));
-      const double Zt = load_coherent_f64(reinterpret_cast<const double*>(cw + kPrmZt));
-      const double Zd = load_coherent_f64(reinterpret_cast<const double*>(cw + kPrmZd));
-      const double A = load_coherent_f64(reinterpret_cast<const double*>(cw + kPrmA));
-      const MssParams q = mss_params(T, Mt, Md, Zt, Zd, A);
+      // residual pass: the scalars carry this pass's tag
+      MssScalars sc;
+      if (!mss_wait_scalars(a, b, s, sc)) break;
+      const MssParams q = mss_params(T, sc.Mt, sc.Md, sc.Zt, sc.Zd, sc.A);
 #pragma unroll
       for (int j = 0; j < Raw::kItems; ++j)
 #pragma unroll
         for (int e = 0; e < Raw::kPer; ++e)
-          lr += mss_weight(mss_p(static_cast<double>(rt.at(j, e)), q), mss_q(static_cast<double>(rd.at(j, e)), q), A);
+          lr += mss_weight(mss_p(static_cast<double>(rt.at(j, e)), q), mss_q(static_cast<double>(rd.at(j, e)), q), sc.A);
       tot_r = wave_sum(lr);
     }
     store_coherent(lp_out + lane, tag_sum(lp, tag));
@@ -343,43 +377,48 @@ struct Tested {
   int count;
 };
 
+// The request's tree in LDS, filled by the choose workgroup's validation and
+// read at every level: parents, node tokens and children counts.
+struct MssTree {
+  int32_t par[SV_MAX_TREE_NODES];
+  int32_t tok[SV_MAX_TREE_NODES];
+  int32_t kids[SV_MAX_TREE_NODES];
+};
+
 // Validation by the choose workgroup (as the naive-sampling tree kernel, plus
-// both uniform arrays for sampling requests).  A valid request gets its first
-// stats pass, an invalid one its -1 outputs and the stop.
-__device__ bool mss_validate(const MssArgs& a, int b) {
-  __shared__ int32_t s_par[SV_MAX_TREE_NODES];
-  __shared__ int32_t s_kids[SV_MAX_TREE_NODES];
+// both uniform arrays for sampling requests and the children limit).  An
+// invalid request gets its -1 outputs and the stop.
+__device__ bool mss_validate(const MssArgs& a, int b, MssTree& t) {
   const int lane = threadIdx.x;
   const int L1 = a.max_depth + 1;
   const int32_t* par = a.parents + static_cast<size_t>(b) * a.N;
   const int32_t* tok = a.tokens + static_cast<size_t>(b) * a.N;
   for (int i = lane; i < a.N; i += kWave) {
-    s_par[i] = par[i];
-    s_kids[i] = 0;
+    t.par[i] = par[i];
+    t.tok[i] = tok[i];
+    t.kids[i] = 0;
   }
   __syncthreads();
-  // children per node (a node's tested children are held one per lane)
   for (int i = lane + 1; i < a.N; i += kWave) {
-    const int p = s_par[i];
-    if (p >= 0 && p < i) atomicAdd(&s_kids[p], 1);
+    const int p = t.par[i];
+    if (p >= 0 && p < i) atomicAdd(&t.kids[p], 1);
   }
   __syncthreads();
   const float T = a.temperature[b];
   int bad = !tree_temp_ok(T);
   const bool sampling = !bad && T > 0.0f;
   for (int i = lane; i < a.N; i += kWave) {
-    bad |= (s_kids[i] > kMssMaxChildren);
+    bad |= (t.kids[i] > kMssMaxChildren);
     if (i == 0) {
-      bad |= (s_par[0] != -1);
+      bad |= (t.par[0] != -1);
     } else {
-      const int p = s_par[i];
+      const int p = t.par[i];
       bad |= (p < 0 || p >= i);
-      const int32_t t = tok[i];
-      bad |= (t < 0 || t >= a.V);
+      bad |= (t.tok[i] < 0 || t.tok[i] >= a.V);
       if (p >= 0 && p < i) {
         int n = i, depth = 0;
         while (n > 0 && depth <= a.max_depth) {
-          const int q = s_par[n];
+          const int q = t.par[n];
           if (q < 0 || q >= n) { depth = a.max_depth + 1; break; }
           n = q;
           ++depth;
@@ -410,39 +449,45 @@ __device__ bool mss_validate(const MssArgs& a, int b) {
   return !any_bad;
 }
 
-// The children of `node` in index order, kWave at a time: calls f(id, token)
-// for each until f returns false.
-template <typename F>
-__device__ inline void mss_for_children(const MssArgs& a, int b, int node, F f) {
+// The children of `node` in index order, one per lane (at most kWave after
+// validation): lane i gets the i-th child's id and token; returns the count.
+__device__ inline int mss_children(const MssArgs& a, const MssTree& t, int node, int& id, int& tk) {
   const int lane = threadIdx.x;
-  const int32_t* par = a.parents + static_cast<size_t>(b) * a.N;
-  const int32_t* tk = a.tokens + static_cast<size_t>(b) * a.N;
-  for (int base = node + 1; base < a.N; base += kWave) {
+  int count = 0;
+  id = -1;
+  tk = -1;
+  for (int base = node + 1; base < a.N && count < t.kids[node]; base += kWave) {
     const int j = base + lane;
-    const bool kid = j < a.N && par[j] == node;
-    const int t = kid ? tk[j] : -1;
-    uint64_t m = __ballot(kid);
-    while (m) {
-      const int l = static_cast<int>(__builtin_ctzll(m));
-      m &= m - 1;
-      if (!f(base + l, read_lane(t, l))) return;
+    const bool kid = j < a.N && t.par[j] == node;
+    const uint64_t m = __ballot(kid);
+    const int slot = count + __popcll(m & ((1ull << lane) - 1ull));
+    // lane `slot` takes child j: route through LDS-free lane moves
+    for (uint64_t r = m; r; r &= r - 1) {
+      const int l = static_cast<int>(__builtin_ctzll(r));
+      const int at = read_lane(slot, l);
+      const int jj = base + l;
+      if (lane == at) {
+        id = jj;
+        tk = t.tok[jj];
+      }
     }
+    count += __popcll(m);
   }
+  return count;
 }
 
-// Publishes pass s (a residual pass carries its scalars, complete before the
-// pass word is).
+// Publishes pass s; a residual pass carries its scalars, tagged with s.
 __device__ inline void mss_publish(const MssArgs& a, int b, uint32_t s, int kind, int node, float Mt = 0.0f,
                                    float Md = 0.0f, double Zt = 0.0, double Zd = 0.0, double A = 0.0) {
   if (threadIdx.x != 0) return;
   uint64_t* cw = mss_ctl(a, b);
   if (kind == kPassResidual) {
-    store_coherent(cw + kPrmMt, static_cast<uint64_t>(__float_as_uint(Mt)));
-    store_coherent(cw + kPrmMd, static_cast<uint64_t>(__float_as_uint(Md)));
-    store_coherent(cw + kPrmZt, static_cast<uint64_t>(__double_as_longlong(Zt)));
-    store_coherent(cw + kPrmZd, static_cast<uint64_t>(__double_as_longlong(Zd)));
-    store_coherent(cw + kPrmA, static_cast<uint64_t>(__double_as_longlong(A)));
-    wait_memory();
+    const int tag = pass_tag(s);
+    store_coherent(cw + kPrmMt, tree_chunk_word(tag, Mt, 0));
+    store_coherent(cw + kPrmMd, tree_chunk_word(tag, Md, 0));
+    store_coherent(cw + kPrmZt, tag_sum(Zt, tag));
+    store_coherent(cw + kPrmZd, tag_sum(Zd, tag));
+    store_coherent(cw + kPrmA, tag_sum(A, tag));
   }
   store_coherent(cw + kMssPass, pass_word(s, kind, node));
 }
@@ -470,9 +515,9 @@ __device__ inline void mss_stop(const MssArgs& a, int b, int d, int token, bool 
 
 // The choose workgroup of request b: validation, then each level's decision.
 template <int DT, bool VEC>
-__device__ void mss_choose_loop(const MssArgs& a, int b) {
-  constexpr int kRun = LaneRun<DT, VEC>::kRun;
-  if (!mss_validate(a, b)) return;
+__device__ void mss_choose_loop(const MssArgs& a, int b, MssTree& tree) {
+  constexpr int kRun = LaneRun<DT, VEC, kMssChunk>::kRun;
+  if (!mss_validate(a, b, tree)) return;
   const int lane = threadIdx.x;
   const float T = a.temperature[b];
   const bool greedy = T == 0.0f;
@@ -482,11 +527,18 @@ __device__ void mss_choose_loop(const MssArgs& a, int b) {
   int32_t* op = a.out_path + static_cast<size_t>(b) * L1;
   uint32_t s = 0;
   int node = 0;
-  bool has_kids = false;
-  mss_for_children(a, b, 0, [&](int, int) { has_kids = true; return false; });
-  mss_publish(a, b, s, (!greedy && has_kids) ? kPassStatsDraft : kPassStats, node);
+  mss_publish(a, b, s, (!greedy && tree.kids[0] > 0) ? kPassStatsDraft : kPassStats, node);
   for (int d = 0;; ++d) {
-    // the node's stats
+    // the node's children, one per lane, and (sampling) their two logits and
+    // accept uniforms, loaded while the stats pass runs
+    int kid = -1, ktok = -1;
+    const int nk = mss_children(a, tree, node, kid, ktok);
+    float tv = 0.0f, dv = 0.0f, uv = 0.0f;
+    if (!greedy && lane < nk) {
+      tv = Elem<DT>::at(mss_row<DT>(a.target, a, b, node), ktok);
+      dv = Elem<DT>::at(mss_row<DT>(a.draft, a, b, node), ktok);
+      uv = a.acc_u[static_cast<size_t>(b) * a.N + kid];
+    }
     uint64_t wt[kTreeChunkCache];
     if (!mss_poll_slots(a, b, kSlotT, s, false, wt)) { mss_stop(a, b, d, -1, true); return; }
     if (greedy) {
@@ -497,12 +549,9 @@ __device__ void mss_choose_loop(const MssArgs& a, int b) {
           best = argmax_combine(best, ArgMax{__uint_as_float(static_cast<uint32_t>(wt[q])),
                                              static_cast<int>((wt[q] >> 32) & 0xffffffu)});
       const int token = wave_argmax(best).i;
-      int child = -1;
-      mss_for_children(a, b, node, [&](int id, int t) {
-        if (t == token) { child = id; return false; }
-        return true;
-      });
-      if (child < 0 || d + 1 >= L1) { mss_stop(a, b, d, token, false); return; }
+      const uint64_t hit = __ballot(lane < nk && ktok == token);
+      if (!hit || d + 1 >= L1) { mss_stop(a, b, d, token, false); return; }
+      const int child = read_lane(kid, static_cast<int>(__builtin_ctzll(hit)));
       if (lane == 0) { ot[d] = token; op[d] = child; }
       node = child;
       ++s;
@@ -527,21 +576,17 @@ __device__ void mss_choose_loop(const MssArgs& a, int b) {
                   : 0.0;
       Zt += pc[q];
     }
-    Zt = wave_sum(Zt);
-    // the children, up to kWave at a time: lane i holds the i-th child of the
-    // current batch with its two logits
-    bool kids = false;
-    mss_for_children(a, b, node, [&](int, int) { kids = true; return false; });
+    Zt = trunc7(wave_sum(Zt));
     int token = -1, child = -1;
     bool lost = false;
-    // where the final draw takes its weights from: P (the stats pass) or the
+    // the final draw takes its weights from P (the stats pass) or from the
     // residual of the last residual pass
     bool from_residual = false;
     double A = 0.0;
     Tested tx{-1, 0.0, 0.0, 0.0, 0};
     float Md = -INFINITY;
     double Zd = 1.0;
-    if (kids) {
+    if (nk > 0) {
       uint64_t wd[kTreeChunkCache], wdt[kTreeChunkCache];
       if (!mss_poll_slots(a, b, kSlotD, s, false, wd) || !mss_poll_slots(a, b, kSlotTotD, s, true, wdt)) {
         mss_stop(a, b, d, -1, true);
@@ -559,32 +604,28 @@ __device__ void mss_choose_loop(const MssArgs& a, int b) {
                   ? sum_value(wdt[q]) * exp2_neg((static_cast<double>(mc) - static_cast<double>(Md)) * l2t)
                   : 0.0;
       }
-      Zd = wave_sum(Zd);
+      Zd = trunc7(wave_sum(Zd));
       const MssParams prm0 = mss_params(T, Mt, Md, Zt, Zd, 0.0);
-      const void* trow = mss_row<DT>(a.target, a, b, node);
-      const void* drow = mss_row<DT>(a.draft, a, b, node);
+      // lane i: P and Q at the i-th child's token
+      const double Pk = lane < nk ? mss_p(static_cast<double>(tv), prm0) : 0.0;
+      const double Qk = lane < nk ? mss_q(static_cast<double>(dv), prm0) : 0.0;
       double Nn = 1.0, S = 1.0;
-      mss_for_children(a, b, node, [&](int id, int t) {
+      for (int i = 0; i < nk; ++i) {
+        const int t = read_lane(ktok, i);
         // a token tested already at this node is skipped
-        if (__any(lane < tx.count && tx.tok == t)) return true;
-        double P = 0.0, Q = 0.0;
-        if (lane == 0) {
-          P = mss_p(static_cast<double>(Elem<DT>::at(trow, t)), prm0);
-          Q = mss_q(static_cast<double>(Elem<DT>::at(drow, t)), prm0);
-        }
-        P = read_lane(P, 0);
-        Q = read_lane(Q, 0);
+        if (__any(lane < tx.count && tx.tok == t)) continue;
+        const double P = read_lane(Pk, i);
+        const double Q = read_lane(Qk, i);
         const double r = mss_weight(P, Q, A) / Nn;
         const double qj = Q / S;
         const double tau = qj <= r ? 1.0 : r / qj;
-        const float u = a.acc_u[static_cast<size_t>(b) * a.N + id];
-        if (static_cast<double>(u) <= tau) {
-          child = id;
+        if (static_cast<double>(read_lane(uv, i)) <= tau) {
+          child = read_lane(kid, i);
           token = t;
-          return false;
+          break;
         }
         // rejected: the residual moves to A + N / S, the token is frozen
-        const double A2 = A + Nn / S;
+        const double A2 = trunc7(A + Nn / S);
         if (lane == tx.count) {
           tx.tok = t;
           tx.P = P;
@@ -597,27 +638,25 @@ __device__ void mss_choose_loop(const MssArgs& a, int b) {
         ++s;
         mss_publish(a, b, s, kPassResidual, node, Mt, Md, Zt, Zd, A);
         uint64_t wr[kTreeChunkCache];
-        if (!mss_poll_slots(a, b, kSlotTotR, s, true, wr)) { lost = true; return false; }
+        if (!mss_poll_slots(a, b, kSlotTotR, s, true, wr)) { lost = true; break; }
         double G = 0.0;
 #pragma unroll
         for (int q = 0; q < kTreeChunkCache; ++q)
           if (q * kWave + lane < a.nchunk) G += sum_value(wr[q]);
         const double fix = lane < tx.count ? tx.F - mss_weight(tx.P, tx.Q, A) : 0.0;
         Nn = wave_sum(G + fix);
-        if (!(Nn > 0.0)) { from_residual = false; return false; }  // empty residual: draw from P
+        if (!(Nn > 0.0)) { from_residual = false; break; }  // empty residual: draw from P
         from_residual = true;
-        return S > 0.0;  // no draft mass left: no later child can have been drawn
-      });
+        if (!(S > 0.0)) break;  // no draft mass left: no later child can have been drawn
+      }
     }
     if (lost) { mss_stop(a, b, d, -1, true); return; }
     if (child >= 0) {
       if (d + 1 >= L1) { mss_stop(a, b, d, token, false); return; }  // unreachable after validation
       if (lane == 0) { ot[d] = token; op[d] = child; }
       node = child;
-      has_kids = false;
-      mss_for_children(a, b, node, [&](int, int) { has_kids = true; return false; });
       ++s;
-      mss_publish(a, b, s, has_kids ? kPassStatsDraft : kPassStats, node);
+      mss_publish(a, b, s, tree.kids[node] > 0 ? kPassStatsDraft : kPassStats, node);
       continue;
     }
     // the final draw: chunk -> lane -> logit
@@ -634,7 +673,7 @@ __device__ void mss_choose_loop(const MssArgs& a, int b) {
       for (int r = 0; r < tx.count; ++r) {
         const int xt = read_lane(tx.tok, r);
         const double delta = read_lane(lane == r ? tx.F - mss_weight(tx.P, tx.Q, A) : 0.0, r);
-        const int cc = xt / kTreeChunk;
+        const int cc = xt / kMssChunk;
 #pragma unroll
         for (int q = 0; q < kTreeChunkCache; ++q)
           if (q * kWave + lane == cc) wc[q] += delta;
@@ -650,8 +689,8 @@ __device__ void mss_choose_loop(const MssArgs& a, int b) {
     const double target = static_cast<double>(ud) * W;
     double before = 0.0;
     const int chunk = mss_cross_chunks(wc, a.nchunk, target, before);
-    const int c0 = chunk * kTreeChunk;
-    const int c1 = min(a.V, c0 + kTreeChunk);
+    const int c0 = chunk * kMssChunk;
+    const int c1 = min(a.V, c0 + kMssChunk);
     uint64_t lw = 0;
     if (!mss_poll_lanes(a, b, chunk, from_residual ? 1 : 0, s, lw)) { mss_stop(a, b, d, -1, true); return; }
     double wl = sum_value(lw);
@@ -701,7 +740,8 @@ __global__ __launch_bounds__(kWave) void tree_mss(MssArgs a) {
   const uint32_t b = blockIdx.x / per_b;
   const uint32_t j = blockIdx.x - b * per_b;
   if (j == 0) {
-    mss_choose_loop<DT, VEC>(a, static_cast<int>(b));
+    __shared__ MssTree tree;
+    mss_choose_loop<DT, VEC>(a, static_cast<int>(b), tree);
     mss_exit(a, static_cast<int>(b));
   } else {
     mss_stream_loop<DT, VEC>(a, static_cast<int>(b), static_cast<int>(j - 1u));
@@ -712,7 +752,7 @@ struct MssLayout {
   size_t ctl, slots, lanes, total;
 };
 
-int mss_chunks(int V) { return (V + kTreeChunk - 1) / kTreeChunk; }
+int mss_chunks(int V) { return (V + kMssChunk - 1) / kMssChunk; }
 
 MssLayout mss_layout(int B, int V) {
   const size_t nc = static_cast<size_t>(mss_chunks(V));

@@ -20,10 +20,10 @@ constexpr uint32_t kTreeSpinLimit = 1u << 22;
 // [c0 + l * kRun, c0 + (l + 1) * kRun)), so that a lane's sum is one stretch of
 // the chunk's CDF.  Loaded as kItems groups of kPer logits from clamped
 // addresses; groups past the row's end become -inf.
-template <int DT, bool VEC>
+template <int DT, bool VEC, int CHUNK = kTreeChunk>
 struct LaneRun {
   static constexpr int kPer = VEC ? Elem<DT>::kVec : 1;
-  static constexpr int kItems = kTreeChunk / (kWave * kPer);
+  static constexpr int kItems = CHUNK / (kWave * kPer);
   static constexpr int kRun = kItems * kPer;
   uint32_t w[kItems][VEC ? 4 : 1];
 
