@@ -54,6 +54,10 @@ R14 MSS uniforms: accept_uniforms[b, j] is the test of node j as a child
     accept_uniforms excepted).
 R15 MSS trees allow at most 64 children per node (a contract limit of the
     library, not of the method); a tree with a wider node is invalid (R11).
+R16 ragged rounds: request b drafts gammas[b] tokens in arrays padded to
+    gamma; it is exactly the round of gammas[b] drafts (R3 with gamma =
+    gammas[b]: its final draw takes uniforms[b, gammas[b]]), reads nothing
+    past that length, and is invalid if gammas[b] is outside [0, gamma].
 """
 from __future__ import annotations
 
@@ -253,6 +257,63 @@ def verify_chain(target: np.ndarray, draft: Optional[np.ndarray], draft_tokens: 
         nacc[b] = n
         decisions[b] = dec
     return ChainResult(out, nacc, decisions)
+
+
+@dataclasses.dataclass
+class RaggedChainResult:
+    out_tokens: np.ndarray        # [B, gamma+1] int32, -1 padded
+    num_accepted: np.ndarray      # [B] int32, -1 => invalid request
+    accept_prob: np.ndarray       # [B, gamma] float64: tau of each test taken, -1 elsewhere
+    decisions: List[List[Decision]]
+
+
+def verify_chain_ragged(target: np.ndarray, draft: Optional[np.ndarray], draft_tokens: np.ndarray,
+                        uniforms: np.ndarray, temperature: np.ndarray, gammas: np.ndarray,
+                        dtype: str, requests=None) -> RaggedChainResult:
+    """Chain verification with a draft length per request (R16).
+
+    The arrays are padded to gamma = target.shape[1] - 1.  Request b with
+    g = gammas[b] is the round of g drafts: its tests use draft_tokens[b, :g]
+    and uniforms[b, :g] against target rows 0..g-1 and draft rows 0..g-1, and
+    its final draw (residual or bonus from target row g) uses uniforms[b, g].
+    Nothing past g is read.  accept_prob[b, i] is tau of the test at position
+    i when that test is taken (greedy: 1 if the draft equals the argmax, else
+    0), and -1 for positions not tested; over draft tokens x ~ q its mean is
+    sum_x min(p, q), the position's acceptance rate (lecture 17 notes section
+    2.3; close-reading notes section 5.1), so the taus of a round give an
+    unbiased acceptance estimate for choosing the next round's length."""
+    B, G1, V = target.shape
+    gamma = G1 - 1
+    out = np.full((B, gamma + 1), -1, dtype=np.int32)
+    nacc = np.full(B, -1, dtype=np.int32)
+    acc = np.full((B, gamma), -1.0, dtype=np.float64)
+    decisions: List[List[Decision]] = [[] for _ in range(B)]
+    todo = range(B) if requests is None else requests
+    for b in todo:
+        g = int(gammas[b])
+        if not 0 <= g <= gamma:
+            continue
+        T = float(np.float32(temperature[b]))
+        toks = np.asarray(draft_tokens[b, :g], dtype=np.int64)
+        u = np.asarray(uniforms[b, :g + 1], dtype=np.float32)
+        if _request_invalid(toks, u, T, V):
+            continue
+        tgt = logits_to_f64(target[b, :g + 1], dtype)
+        if T > 0.0:
+            drf = logits_to_f64(draft[b, :g], dtype)
+            P, Q = chain_distributions(tgt, drf, T)
+        else:
+            P, Q = None, None
+        emitted, n, dec = chain_decide_request(P, Q, tgt, toks, u, T)
+        out[b, :len(emitted)] = emitted
+        nacc[b] = n
+        for d in dec:
+            if d.kind == "accept":
+                acc[b, d.position] = d.threshold
+            elif d.kind == "greedy" and d.position < g:
+                acc[b, d.position] = 1.0 if int(toks[d.position]) == d.outcome else 0.0
+        decisions[b] = dec
+    return RaggedChainResult(out, nacc, acc, decisions)
 
 
 # ---------------------------------------------------------------------------
