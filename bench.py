@@ -15,7 +15,9 @@ oracle timed on this host's cores on a bounded sample.
 
 Other workloads (--workload) report the same line for the single-request
 latency case (B=1, V=32000, also replayed from a HIP graph), the deep case
-(B=256, gamma=8, V=151936, Zipf logits), the token-tree cases (B=32, 64
+(B=256, gamma=8, V=151936, Zipf logits), the batched inputs as a ragged call
+(request b drafts 1 + b % 4 tokens; rows are the rounds' own rows), the
+token-tree cases (B=32, 64
 nodes, greedy, naive sampling or multi-step speculative sampling; rows are
 node rows) and the tree attention mask builder on the same tree shape (rows
 are mask rows).
@@ -40,13 +42,17 @@ PEAK_HBM_GBPS = 8000.0
 MALL_BYTES = 256 << 20
 
 
-def read_bytes(ci) -> int:
-    """Logit bytes the path must read once: 2*gamma+1 rows of a sampling
-    request (gamma+1 target, gamma draft), gamma+1 target rows of a greedy one."""
+def read_bytes(ci, gammas=None) -> int:
+    """Logit bytes the path must read once: 2*g+1 rows of a sampling request
+    (g+1 target, g draft), g+1 target rows of a greedy one, g being gamma or
+    the request's own length in a ragged call."""
     es = 2 if ci.dtype == "bf16" else 4
-    rows = sum((2 * ci.gamma + 1) if float(ci.temperature[b]) > 0 else (ci.gamma + 1)
-               for b in range(ci.B))
+    g = [ci.gamma] * ci.B if gammas is None else [int(x) for x in gammas]
+    rows = sum((2 * g[b] + 1) if float(ci.temperature[b]) > 0 else (g[b] + 1) for b in range(ci.B))
     return rows * ci.V * es
+
+
+RAGGED_LENGTHS = (1, 2, 3, 4)    # request b drafts RAGGED_LENGTHS[b % 4] tokens
 
 
 def small_bytes(ci) -> int:
@@ -80,7 +86,7 @@ def stored_traffic(kernel: str):
     return k.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(ci, budget_s: float = 15.0):
+def cpu_baseline(ci, budget_s: float = 15.0, gammas=None):
     """The fp64 oracle as it stands, timed on this host's cores: it verifies
     the same batch over and over with fresh uniforms until the budget is
     spent.  `cores` is the CPU time it used divided by the wall time."""
@@ -93,9 +99,14 @@ def cpu_baseline(ci, budget_s: float = 15.0):
     while time.perf_counter() - w0 < budget_s:
         u = ci.uniforms if passes == 0 else ci.fresh_uniforms(90_000 + passes)
         for b in range(ci.B):
-            oracle.verify_chain(ci.target[b:b + 1], ci.draft[b:b + 1], ci.draft_tokens[b:b + 1],
-                                u[b:b + 1], ci.temperature[b:b + 1], ci.dtype)
-            rows += ci.gamma + 1
+            if gammas is None:
+                oracle.verify_chain(ci.target[b:b + 1], ci.draft[b:b + 1], ci.draft_tokens[b:b + 1],
+                                    u[b:b + 1], ci.temperature[b:b + 1], ci.dtype)
+                rows += ci.gamma + 1
+            else:
+                oracle.verify_chain_ragged(ci.target[b:b + 1], ci.draft[b:b + 1], ci.draft_tokens[b:b + 1],
+                                           u[b:b + 1], ci.temperature[b:b + 1], gammas[b:b + 1], ci.dtype)
+                rows += int(gammas[b]) + 1
             requests += 1
             if time.perf_counter() - w0 >= budget_s:
                 break
@@ -108,7 +119,7 @@ def cpu_baseline(ci, budget_s: float = 15.0):
                       f"fresh uniforms, numpy fp64, {wall:.1f} s wall, {cpu:.1f} s CPU"}
 
 
-WORKLOADS = ("batched", "single", "deep", "tree-greedy", "tree-sampling", "tree-mss", "tree-mask")
+WORKLOADS = ("batched", "single", "deep", "ragged", "tree-greedy", "tree-sampling", "tree-mss", "tree-mask")
 
 
 def percentiles(xs):
@@ -149,6 +160,10 @@ def chain_case(name, synth):
     if name == "batched":
         return synth.batched_chain(), ("batched chain verify: B=64, gamma=4, V=128256, bf16 logits, "
                                        "even requests sample at T=0.7, odd requests greedy")
+    if name == "ragged":
+        return synth.batched_chain(), ("ragged chain verify: the batched inputs (B=64, gamma padded to 4, "
+                                       "V=128256, bf16, even requests T=0.7, odd greedy) with request b "
+                                       "drafting 1 + b % 4 tokens")
     if name == "single":
         return synth.single_chain(), ("single-request chain verify: B=1, gamma=4, V=32000, bf16 logits, "
                                       "T=1, fixed logits with fresh uniforms every call (latency)")
@@ -175,10 +190,16 @@ def run_chain(args, torch, synth, sv):
     out_n = torch.empty((ci.B,), dtype=torch.int32, device=dev)
     ws = sv.workspace(sv.lib().sv_chain_workspace_bytes(ci.B, ci.gamma, ci.V, sv.SV_BF16), dev)
     stream = torch.cuda.current_stream(dev)
+    ragged = args.workload == "ragged"
+    gam = np.array([RAGGED_LENGTHS[b % len(RAGGED_LENGTHS)] for b in range(ci.B)], np.int32) if ragged else None
+    gam_d = torch.from_numpy(gam).to(dev) if ragged else None
 
     def step(i):
         t, d = sets[i % R]
-        sv.verify_chain(t, d, tok, u_sets[i % n_u], T, out_tokens=out_t, out_num_accepted=out_n, ws=ws)
+        if ragged:
+            sv.verify_chain_ragged(t, d, tok, u_sets[i % n_u], T, gam_d, ws=ws)
+        else:
+            sv.verify_chain(t, d, tok, u_sets[i % n_u], T, out_tokens=out_t, out_num_accepted=out_n, ws=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -192,14 +213,17 @@ def run_chain(args, torch, synth, sv):
         events_ms, _ = time_calls(torch, stream, step, args.steps)
     calls = per_call_us(torch, stream, step, min(args.steps, 2000))
 
-    rows = ci.B * (ci.gamma + 1)
-    rd, sm = read_bytes(ci), small_bytes(ci)
+    rows = ci.B * (ci.gamma + 1) if gam is None else int(np.sum(gam + 1))
+    rd, sm = read_bytes(ci, gam), small_bytes(ci)
     call_us = 1e3 * total_ms / args.steps
     dominant = "chain_verify"
     k_us = kt.mean_us(dominant)
     achieved = rd / (k_us * 1e-6) / 1e9
-    result = head(args, rows * args.steps / (total_ms * 1e-3), total_ms,
-                  {"workload": desc, "B": ci.B, "gamma": ci.gamma, "V": ci.V, "rotating_input_sets": R})
+    cfg = {"workload": desc, "B": ci.B, "gamma": ci.gamma, "V": ci.V, "rotating_input_sets": R}
+    if ragged:
+        cfg["lengths"] = "1 + b % 4"
+        cfg["rows_per_call"] = rows
+    result = head(args, rows * args.steps / (total_ms * 1e-3), total_ms, cfg)
     result.update({
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
@@ -216,7 +240,7 @@ def run_chain(args, torch, synth, sv):
         result["graph_replay"] = graph_replay(torch, stream, sv, sets[0], tok, u_sets[0], T, out_t, out_n, ws,
                                               args.steps)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(ci)
+        result["cpu_baseline"] = cpu_baseline(ci, gammas=gam)
     return result
 
 

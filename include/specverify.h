@@ -133,6 +133,42 @@ SV_API int spec_verify_chain(const void* target_logits, const void* draft_logits
                       void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * Ragged chain verification: a draft length per request in one call, and the
+ * acceptance probability of every test taken.
+ *
+ * The arrays keep spec_verify_chain's layout, padded to gamma (the longest
+ * round).  Request b drafts g = gammas[b] tokens: it is exactly the round of
+ * g drafts -- tests on draft_tokens[b][0..g-1] with uniforms[b][0..g-1]
+ * against target and draft rows 0..g-1, then the residual draw or the bonus
+ * draw from target row g, with uniforms[b][g].  Nothing past g is read (rows,
+ * tokens or uniforms); out_tokens[b] holds n + 1 tokens then -1 up to
+ * gamma + 1 entries.  A length outside [0, gamma] makes the request invalid.
+ * The rows past a request's length are skipped by the streaming, so a batch
+ * of short rounds reads only its own rows.
+ *
+ * gammas           [B]         int32  g of each request, in [0, gamma];
+ *                                     NULL means every request drafts gamma
+ * out_accept_prob  [B][gamma]  float  optional (NULL): tau of each test taken,
+ *                                     i.e. positions 0..n (the rejected one
+ *                                     included), -1 for the rest.  tau =
+ *                                     min(1, p(x)/q(x)) for sampling, 1 or 0
+ *                                     (draft == argmax) for greedy.  Over
+ *                                     x ~ q, tau averages to sum_k min(p, q):
+ *                                     the mean of a round's taus is an
+ *                                     unbiased acceptance-rate estimate for
+ *                                     choosing the next round's length
+ *                                     (lecture 17 notes, section 2.3).
+ * Everything else as spec_verify_chain (same workspace query); draft_logits
+ * is required when gamma > 0.
+ * ---------------------------------------------------------------------- */
+SV_API int spec_verify_chain_ragged(const void* target_logits, const void* draft_logits,
+                             const int32_t* draft_tokens, const float* uniforms,
+                             const float* temperature, const int32_t* gammas, int B, int gamma,
+                             int V, int dtype, int32_t* out_tokens, int32_t* out_num_accepted,
+                             float* out_accept_prob, void* workspace, size_t workspace_bytes,
+                             void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * Token-tree verification (CMU 15-779 lecture 17 notes, section 4.4
  * VerifyGreedy for T == 0 and section 4.5 naive sampling for T > 0).
  *

@@ -28,6 +28,8 @@ EXPORTS = {
     "sv_chain_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "spec_verify_chain": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 +
                           [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "spec_verify_chain_ragged": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 +
+                                 [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
     "sv_tree_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "spec_verify_tree": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 +
                          [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
@@ -174,6 +176,50 @@ def verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_toke
                              _ptr(out_num_accepted), _ptr(ws), ws.numel(), _stream_handle(dev))
     _check(st, "spec_verify_chain")
     return out_tokens, out_num_accepted
+
+
+def verify_chain_ragged(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: torch.Tensor,
+                        uniforms: torch.Tensor, temperature: torch.Tensor,
+                        gammas: Optional[torch.Tensor], want_accept_prob: bool = True,
+                        ws: Optional[torch.Tensor] = None):
+    """spec_verify_chain_ragged over device tensors: request b drafts
+    gammas[b] tokens in arrays padded to gamma (gammas [B] int32, or None for
+    all gamma).  Returns (out_tokens [B, gamma+1], out_num_accepted [B],
+    accept_prob [B, gamma] float32 or None)."""
+    _need_cuda(target, "target")
+    if target.dim() != 3:
+        raise ValueError("target must be [B, gamma+1, V]")
+    B, G1, V = target.shape
+    gamma = G1 - 1
+    dev = target.device
+    dt = _dtype_code(target)
+    if gamma > 0:
+        if draft is None:
+            raise ValueError("draft is required when gamma > 0")
+        _need_cuda(draft, "draft")
+        if draft.dtype != target.dtype or tuple(draft.shape) != (B, gamma, V):
+            raise ValueError("draft must match target's dtype with shape [B, gamma, V]")
+    checks = [("draft_tokens", draft_tokens, (B, gamma), torch.int32),
+              ("uniforms", uniforms, (B, gamma + 1), torch.float32),
+              ("temperature", temperature, (B,), torch.float32)]
+    if gammas is not None:
+        checks.append(("gammas", gammas, (B,), torch.int32))
+    for name, t, shape, dtype in checks:
+        _need_cuda(t, name)
+        if tuple(t.shape) != shape or t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype} with shape {shape}")
+    out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+    out_n = torch.empty((B,), dtype=torch.int32, device=dev)
+    acc = torch.empty((B, gamma), dtype=torch.float32, device=dev) if want_accept_prob and gamma > 0 else None
+    L = lib()
+    nbytes = L.sv_chain_workspace_bytes(B, gamma, V, dt)
+    if ws is None:
+        ws = workspace(nbytes, dev)
+    st = L.spec_verify_chain_ragged(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
+                                    _ptr(temperature), _ptr(gammas), B, gamma, V, dt, _ptr(out_tokens),
+                                    _ptr(out_n), _ptr(acc), _ptr(ws), ws.numel(), _stream_handle(dev))
+    _check(st, "spec_verify_chain_ragged")
+    return out_tokens, out_n, acc
 
 
 def verify_tree(logits: torch.Tensor, node_tokens: torch.Tensor, parents: torch.Tensor,

@@ -120,6 +120,8 @@ struct ChainArgs {
   PendingWire* pending;  // [B]
   UnitRec* units;        // [B][nunit]
   uint32_t* counters;    // [B][kCounterStride]
+  const int32_t* gammas; // [B] draft length of each request (ragged calls), or NULL: all gamma
+  float* out_tau;        // [B][gamma] tau of each test taken, -1 elsewhere; or NULL
 };
 
 // T must be 0 (greedy) or a finite positive normal float.
@@ -152,9 +154,28 @@ __device__ inline int request_class(const ChainArgs& a, float T) {
   return 1;
 }
 
-// Rows of a request that are read: target rows, plus draft rows when sampling.
-__device__ inline int needed_rows(const ChainArgs& a, float T) {
-  return (T > 0.0f && a.draft != nullptr) ? 2 * a.gamma + 1 : a.gamma + 1;
+// Draft length of request b: gamma, or in a ragged call its own length (-1
+// when that lies outside [0, gamma]).  The arrays keep gamma's padded layout.
+__device__ inline int req_gamma(const ChainArgs& a, int b) {
+  if (!a.gammas) return a.gamma;
+  const int g = a.gammas[b];
+  return (g >= 0 && g <= a.gamma) ? g : -1;
+}
+
+// Rows of a request of length g that are read: target rows 0..g, plus draft
+// rows 0..g-1 when sampling (none for an invalid length).
+__device__ inline int needed_rows(const ChainArgs& a, float T, int g) {
+  if (g < 0) return 0;
+  return (T > 0.0f && a.draft != nullptr) ? 2 * g + 1 : g + 1;
+}
+
+// Partial row of the lr-th needed row of a request of length g: target rows
+// sit at 0..gamma, draft rows at gamma+1..2*gamma.
+__device__ inline int phys_row(const ChainArgs& a, int g, int lr) { return lr <= g ? lr : a.gamma + 1 + (lr - g - 1); }
+
+// Whether row k (partial-row numbering) of a request of length g is read.
+__device__ inline bool row_in_round(const ChainArgs& a, int g, int k) {
+  return g >= 0 && (k <= a.gamma ? k <= g : k - a.gamma - 1 < g);
 }
 
 // Upper bound on the polls of a waiting workgroup (seconds at the least);
@@ -356,6 +377,7 @@ __device__ inline void stream_reduce_any(const ChainArgs& a, const RowItem& r, S
 template <int DT, bool VEC>
 __device__ inline void stream_once(const ChainArgs& a, const RowItem& r) {
   StreamItem<DT, VEC, kWave> x;
+  if (a.gammas && !row_in_round(a, req_gamma(a, r.b), r.k)) return;  // past the request's length
   if (r.k <= a.gamma) {
     stream_issue<DT, VEC, kWave>(a, r, x);  // target rows: the loads do not wait for the temperature
     if (!temp_ok(x.t)) return;
@@ -418,29 +440,34 @@ __device__ void decide_request(const ChainArgs& a, int b) {
   const float T = a.temperature[b];
   if (request_class(a, T) == 2) {  // nothing was streamed
     write_invalid(a, b);
+    if (a.out_tau)
+      for (int i = lane; i < G; i += kWave) a.out_tau[static_cast<size_t>(b) * G + i] = -1.0f;
     return;
   }
   const bool sampling = T > 0.0f;
   const double l2t = sampling ? kLog2e / static_cast<double>(T) : 0.0;
-  const int nrows = needed_rows(a, T);
-  const int gpr = max(1, min(a.nchunk, kWave / nrows));  // groups per row
+  // the request's own length (a ragged call); rows are numbered logically:
+  // target rows 0..Gb, then draft rows 0..Gb-1
+  const int Gb = req_gamma(a, b);
+  const int nrows = needed_rows(a, T, Gb);
+  const int gpr = nrows > 0 ? max(1, min(a.nchunk, kWave / nrows)) : 1;  // groups per row
   const int gs = (a.nchunk + gpr - 1) / gpr;              // chunks per group
   const int nslots = nrows * gpr;
-  int bad = 0;
+  int bad = Gb < 0;
   int32_t x = -1;
   float u = 0.0f;
-  if (lane < G) {
+  if (lane < Gb) {
     x = a.tokens[static_cast<size_t>(b) * G + lane];
     bad |= (x < 0 || x >= a.V);
   }
-  if (sampling && lane <= G) {
+  if (sampling && lane <= Gb) {
     u = a.uniforms[static_cast<size_t>(b) * (G + 1) + lane];
     bad |= !(u >= 0.0f && u < 1.0f);
   }
-  if (sampling && G > 0 && a.draft == nullptr) bad = 1;
+  if (sampling && Gb > 0 && a.draft == nullptr) bad = 1;
   // the logits of the draft tokens in target row i and draft row i
   float xt = 0.0f, xd = 0.0f;
-  if (sampling && lane < G && x >= 0 && x < a.V) {
+  if (sampling && lane < Gb && x >= 0 && x < a.V) {
     xt = Elem<DT>::at(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + lane, a.V), x);
     if (a.draft != nullptr) xd = Elem<DT>::at(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + lane, a.V), x);
   }
@@ -450,7 +477,7 @@ __device__ void decide_request(const ChainArgs& a, int b) {
   for (int s = lane; s < nslots; s += kWave) {
     const int r = s / gpr;
     const int g = s % gpr;
-    const uint64_t* p = pb + static_cast<size_t>(r) * a.nchunk;
+    const uint64_t* p = pb + static_cast<size_t>(phys_row(a, Gb, r)) * a.nchunk;
     const int cb = g * gs;
     const int ce = min(a.nchunk, cb + gs);
     float m = -INFINITY;
@@ -512,21 +539,27 @@ __device__ void decide_request(const ChainArgs& a, int b) {
   __syncthreads();
   const bool any_bad = __any(bad);
   int n = -1;
+  double tau = -1.0;
   if (!any_bad) {
     int ok = 1;
-    if (lane < G) {
+    if (lane < Gb) {
       if (!sampling) {
         ok = (x == s_arg[lane]);
+        tau = ok ? 1.0 : 0.0;
       } else {
         const double p = exp_scaled(xt, s_m[lane], l2t) / s_z[lane];
-        const double q = exp_scaled(xd, s_m[G + 1 + lane], l2t) / s_z[G + 1 + lane];
-        const double tau = (q <= p) ? 1.0 : p / q;
+        const double q = exp_scaled(xd, s_m[Gb + 1 + lane], l2t) / s_z[Gb + 1 + lane];
+        tau = (q <= p) ? 1.0 : p / q;
         ok = (static_cast<double>(u) <= tau);
       }
     }
-    const uint64_t fail = __ballot(lane < G && !ok);
-    n = fail ? static_cast<int>(__builtin_ctzll(fail)) : G;
+    const uint64_t fail = __ballot(lane < Gb && !ok);
+    n = fail ? static_cast<int>(__builtin_ctzll(fail)) : Gb;
   }
+  // the tests taken: positions 0..n (the first rejection included)
+  if (a.out_tau)
+    for (int i = lane; i < G; i += kWave)
+      a.out_tau[static_cast<size_t>(b) * G + i] = (i == lane && i <= n && i < Gb) ? static_cast<float>(tau) : -1.0f;
   // a request with draw units hears the outcome in every case: the draw, or
   // that there is none
   Pending d{};
@@ -535,15 +568,15 @@ __device__ void decide_request(const ChainArgs& a, int b) {
       d.valid = kPendingNone;
     } else {
       d.valid = kPendingDraw;
-      d.n = n;
-      d.mode = n < G ? kModeResidual : kModeBonus;
-      d.u = read_lane(u, G);
+      d.n = n;  // the row of the draw: the rejected position, or Gb for the bonus
+      d.mode = n < Gb ? kModeResidual : kModeBonus;
+      d.u = read_lane(u, Gb);
       d.t = T;
       d.mt = s_m[n];
       d.zt = s_z[n];
-      if (n < G) {
-        d.md = s_m[G + 1 + n];
-        d.zd = s_z[G + 1 + n];
+      if (n < Gb) {
+        d.md = s_m[Gb + 1 + n];
+        d.zd = s_z[Gb + 1 + n];
       }
     }
     publish_pending(a.pending + b, d);
@@ -565,7 +598,10 @@ __device__ void decide_request(const ChainArgs& a, int b) {
   if (lane == 0) a.out_n[b] = n;
   // the workspace words of this request back to zero
   uint64_t* pz = a.partials + static_cast<size_t>(b) * R * a.nchunk;
-  for (int i = lane; i < nrows * a.nchunk; i += kWave) store_coherent(pz + i, 0ull);
+  for (int i = lane; i < nrows * a.nchunk; i += kWave) {
+    const int r = i / a.nchunk;
+    store_coherent(pz + static_cast<size_t>(phys_row(a, Gb, r)) * a.nchunk + (i - r * a.nchunk), 0ull);
+  }
   if (kDraws && request_class(a, T) == 0) {
     // the draw runs beside other requests' units: let this wave issue first
     __builtin_amdgcn_s_setprio(3);
@@ -755,7 +791,7 @@ __device__ void draw_token(const ChainArgs& a, int b, const Pending& d, bool zer
   const int c1 = min(a.V, c0 + U::kSpan);
   const double l2t = kLog2e / static_cast<double>(d.t);
   const double mtl = static_cast<double>(d.mt) * l2t, mdl = static_cast<double>(d.md) * l2t;
-  const int trow = d.mode == kModeResidual ? d.n : G;
+  const int trow = d.n;  // the rejected position, or the request's length for the bonus
   Raw st, sd;
   st.load(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + trow, a.V), c0, c1);
   if (residual) sd.load(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + d.n, a.V), c0, c1);
@@ -866,7 +902,7 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit) {
     const int c0 = unit * U::kSpan;
     const int c1 = min(a.V, c0 + U::kSpan);
     const bool residual = d.mode == kModeResidual;
-    const int trow = residual ? d.n : G;
+    const int trow = d.n;  // the rejected position, or the request's length for the bonus
     Raw st, sd;
     st.load(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + trow, a.V), c0, c1);
     if (residual) sd.load(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + d.n, a.V), c0, c1);
@@ -1005,7 +1041,8 @@ struct StreamFlags {
 __device__ inline bool stream_needed(const ChainArgs& a, const StreamFlags& fl, long long item) {
   const RowItem r = decode_item(a, item);
   const uint32_t f = fl.get(r.b);
-  return r.k <= a.gamma ? (f & kStreamTarget) != 0 : (f & kStreamDraft) != 0;
+  if (!(r.k <= a.gamma ? (f & kStreamTarget) != 0 : (f & kStreamDraft) != 0)) return false;
+  return !a.gammas || row_in_round(a, req_gamma(a, r.b), r.k);
 }
 
 __device__ inline long long stream_next(const ChainArgs& a, const StreamFlags& fl, long long item) {
@@ -1154,11 +1191,10 @@ extern "C" size_t sv_chain_workspace_bytes(int B, int gamma, int V, int dtype) {
   return chain_layout(B, gamma, V).total;
 }
 
-extern "C" int spec_verify_chain(const void* target_logits, const void* draft_logits,
-                                 const int32_t* draft_tokens, const float* uniforms,
-                                 const float* temperature, int B, int gamma, int V, int dtype,
-                                 int32_t* out_tokens, int32_t* out_num_accepted,
-                                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+static int chain_entry(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                       const float* uniforms, const float* temperature, const int32_t* gammas, int B, int gamma,
+                       int V, int dtype, int32_t* out_tokens, int32_t* out_num_accepted, float* out_tau,
+                       void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (dtype != SV_BF16 && dtype != SV_F32) return SV_ERR_DTYPE;
   if (B < 0 || B > SV_MAX_BATCH || gamma < 0 || gamma > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB)
     return SV_ERR_SHAPE;
@@ -1187,9 +1223,32 @@ extern "C" int spec_verify_chain(const void* target_logits, const void* draft_lo
   a.pending = reinterpret_cast<PendingWire*>(ws + L.pending);
   a.units = reinterpret_cast<UnitRec*>(ws + L.units);
   a.counters = reinterpret_cast<uint32_t*>(ws + L.counters);
+  a.gammas = gammas;
+  a.out_tau = gamma > 0 ? out_tau : nullptr;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const int kv = dtype == SV_BF16 ? Elem<0>::kVec : Elem<1>::kVec;
   const bool vec = (V % kv == 0) && aligned(target_logits, 16) && (!a.draft || aligned(a.draft, 16));
   if (dtype == SV_BF16) return vec ? launch_chain<0, true>(a, stream) : launch_chain<0, false>(a, stream);
   return vec ? launch_chain<1, true>(a, stream) : launch_chain<1, false>(a, stream);
+}
+
+extern "C" int spec_verify_chain(const void* target_logits, const void* draft_logits,
+                                 const int32_t* draft_tokens, const float* uniforms,
+                                 const float* temperature, int B, int gamma, int V, int dtype,
+                                 int32_t* out_tokens, int32_t* out_num_accepted,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return chain_entry(target_logits, draft_logits, draft_tokens, uniforms, temperature, nullptr, B, gamma, V,
+                     dtype, out_tokens, out_num_accepted, nullptr, workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" int spec_verify_chain_ragged(const void* target_logits, const void* draft_logits,
+                                        const int32_t* draft_tokens, const float* uniforms,
+                                        const float* temperature, const int32_t* gammas, int B, int gamma,
+                                        int V, int dtype, int32_t* out_tokens, int32_t* out_num_accepted,
+                                        float* out_accept_prob, void* workspace, size_t workspace_bytes,
+                                        void* hip_stream) {
+  if (B > 0 && gamma > 0 && !draft_logits) return SV_ERR_NULL;
+  return chain_entry(target_logits, draft_logits, draft_tokens, uniforms, temperature, gammas, B, gamma, V,
+                     dtype, out_tokens, out_num_accepted, out_accept_prob, workspace, workspace_bytes,
+                     hip_stream);
 }

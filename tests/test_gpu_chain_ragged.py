@@ -1,0 +1,119 @@
+"""GPU parity of spec_verify_chain_ragged (a draft length per request, and the
+acceptance probability of every test taken) against the fp64 oracle,
+through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import rejection_sampling_verify_15_amd as sv
+from parity import Tally, assert_shared_workspace_zero, compare_chain, to_device, to_device_logits
+
+pytestmark = pytest.mark.gpu
+
+
+def run_ragged(ci, gam, u_sets, target=None, draft=None, tokens=None):
+    tgt = to_device_logits(ci.target if target is None else target, ci.dtype)
+    drf = to_device_logits(ci.draft if draft is None else draft, ci.dtype)
+    tok = to_device((ci.draft_tokens if tokens is None else tokens).astype(np.int32))
+    T = to_device(ci.temperature.astype(np.float32))
+    g = None if gam is None else to_device(np.asarray(gam, np.int32))
+    outs = []
+    for u in u_sets:
+        ot, on, acc = sv.verify_chain_ragged(tgt, drf, tok, to_device(np.asarray(u, np.float32)), T, g)
+        outs.append((ot.cpu().numpy(), on.cpu().numpy(), acc.cpu().numpy()))
+    assert_shared_workspace_zero("chain ragged")
+    return outs
+
+
+def check_accept_prob(ref, ot, on, acc, label):
+    """Where the GPU and the oracle agree on a request, its taus agree to the
+    1e-5 relative bar of p(x)/q(x) (pass-1 fp32 exponentials), with the same
+    -1 pattern."""
+    agree = (on == ref.num_accepted) & np.all(ot == ref.out_tokens, axis=1) & (ref.num_accepted >= 0)
+    assert agree.mean() > 0.95, label
+    a, r = acc[agree].astype(np.float64), ref.accept_prob[agree]
+    assert np.array_equal(a < 0, r < 0), label
+    m = r >= 0
+    assert np.all(np.abs(a[m] - r[m]) <= 1e-5 * np.abs(r[m]) + 1e-7), (label, np.abs(a[m] - r[m]).max())
+    bad = ref.num_accepted < 0
+    assert (acc[bad] == -1.0).all(), label
+
+
+def ragged_parity(ci, gam, n_sets, label, seed=7):
+    u_sets = [ci.uniforms] + [ci.fresh_uniforms(seed * 1000 + s) for s in range(n_sets - 1)]
+    print(f"[{label}] B={ci.B} gamma={ci.gamma} V={ci.V} dtype={ci.dtype} sets={n_sets}", flush=True)
+    gpu = run_ragged(ci, gam, u_sets)
+    tally = Tally()
+    gfull = np.full(ci.B, ci.gamma, np.int32) if gam is None else gam
+    for (ot, on, acc), u in zip(gpu, u_sets):
+        ref = oracle.verify_chain_ragged(ci.target, ci.draft, ci.draft_tokens, u, ci.temperature, gfull, ci.dtype)
+        tally.add(compare_chain(ref, ot, on))
+        check_accept_prob(ref, ot, on, acc, label)
+    print(f"[{label}] {tally}", flush=True)
+    tally.check(label)
+    return gpu
+
+
+def test_ragged_batched_shape():
+    """B=64, gamma up to 4, V=128256 bf16, even requests sampling at T=0.7 and
+    odd ones greedy; lengths 0..4."""
+    ci = synth.batched_chain()
+    gam = (np.arange(ci.B) * 7 % 5).astype(np.int32)
+    gpu = ragged_parity(ci, gam, 4, "ragged batched")
+    for _, on, _ in gpu:
+        assert (on <= gam).all()
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 20000), ("f32", 9999)])
+def test_ragged_small_many_rounds(dtype, V):
+    ci = synth.chain_inputs(15600, B=40, gamma=6, V=V, dtype=dtype, family="gauss",
+                            draft_sigma=(0.2, 1.5), temperature=1.0, greedy_odd=True)
+    gam = (np.arange(ci.B) % 7).astype(np.int32)
+    ragged_parity(ci, gam, 25, f"ragged {dtype} V={V}")
+
+
+def test_nothing_past_the_length_is_read_and_bad_lengths():
+    ci = synth.chain_inputs(15610, B=24, gamma=5, V=3000, dtype="bf16", family="peaked",
+                            draft_sigma=(0.3, 2.0), temperature=0.8, greedy_odd=True)
+    gam = (np.arange(ci.B) % 6).astype(np.int32)
+    gam[5], gam[11] = -1, 6
+    tgt, drf, tok, u = ci.target.copy(), ci.draft.copy(), ci.draft_tokens.copy(), ci.uniforms.copy()
+    nan16 = np.uint16(0x7fc0)
+    for b in range(ci.B):
+        g = max(int(gam[b]), 0)
+        tgt[b, g + 1:] = nan16
+        drf[b, g:] = nan16
+        tok[b, g:] = -3
+        u[b, g + 1:] = 7.0
+    clean = run_ragged(ci, gam, [ci.uniforms])[0]
+    dirty = run_ragged(ci, gam, [u], target=tgt, draft=drf, tokens=tok)[0]
+    ok = np.ones(ci.B, bool)
+    ok[[5, 11]] = False
+    for x, y in zip(clean, dirty):
+        assert np.array_equal(x[ok], y[ok])
+    ref = oracle.verify_chain_ragged(ci.target, ci.draft, ci.draft_tokens, ci.uniforms, ci.temperature, gam, "bf16")
+    t = compare_chain(ref, clean[0], clean[1])
+    t.check("ragged clean")
+    assert (clean[1][~ok] == -1).all() and (clean[0][~ok] == -1).all() and (clean[2][~ok] == -1).all()
+
+
+def test_null_lengths_equal_the_fixed_call():
+    ci = synth.chain_inputs(15620, B=16, gamma=4, V=20000, dtype="bf16", family="peaked",
+                            draft_sigma=(0.3, 2.0), temperature=0.7, greedy_odd=True)
+    (ot, on, acc), = run_ragged(ci, None, [ci.uniforms])
+    tgt = to_device_logits(ci.target, ci.dtype)
+    drf = to_device_logits(ci.draft, ci.dtype)
+    ft, fn = sv.verify_chain(tgt, drf, to_device(ci.draft_tokens.astype(np.int32)),
+                             to_device(ci.uniforms), to_device(ci.temperature))
+    assert np.array_equal(ot, ft.cpu().numpy()) and np.array_equal(on, fn.cpu().numpy())
+    assert (acc[np.arange(ci.B), 0] >= 0).all()
+
+
+def test_ragged_three_launch_form(monkeypatch):
+    monkeypatch.setenv("SV_CHAIN_SPLIT", "1")
+    ci = synth.chain_inputs(15630, B=20, gamma=8, V=30000, dtype="bf16", family="zipf",
+                            draft_sigma=0.8, temperature=1.0)
+    gam = (np.arange(ci.B) * 3 % 9).astype(np.int32)
+    ragged_parity(ci, gam, 6, "ragged three-launch")
