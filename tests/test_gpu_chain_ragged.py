@@ -117,3 +117,42 @@ def test_ragged_three_launch_form(monkeypatch):
                             draft_sigma=0.8, temperature=1.0)
     gam = (np.arange(ci.B) * 3 % 9).astype(np.int32)
     ragged_parity(ci, gam, 6, "ragged three-launch")
+
+
+def test_ragged_graph_capture_replays_match_eager():
+    """One ragged call captured in a HIP graph and replayed, with eager calls
+    on other uniforms between the replays: every replay gives the eager
+    result and the workspace stays zero."""
+    ci = synth.chain_inputs(15640, B=24, gamma=5, V=20000, dtype="bf16", family="peaked",
+                            draft_sigma=(0.3, 2.0), temperature=0.8, greedy_odd=True)
+    gam = (np.arange(ci.B) % 6).astype(np.int32)
+    dev = torch.device("cuda")
+    tgt = to_device_logits(ci.target, ci.dtype)
+    drf = to_device_logits(ci.draft, ci.dtype)
+    tok = to_device(ci.draft_tokens.astype(np.int32))
+    T = to_device(ci.temperature)
+    g_d = to_device(gam)
+    u0 = to_device(ci.uniforms)
+    need = sv.lib().sv_chain_workspace_bytes(ci.B, ci.gamma, ci.V, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    want = [x.clone() for x in sv.verify_chain_ragged(tgt, drf, tok, u0, T, g_d, ws=ws)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            got = sv.verify_chain_ragged(tgt, drf, tok, u0, T, g_d, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(4):
+        for x in got:
+            x.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(got, want):
+            assert torch.equal(x, y), f"replay {r}"
+        assert int(ws.count_nonzero()) == 0
+        sv.verify_chain_ragged(tgt, drf, tok, to_device(ci.fresh_uniforms(15641 + r)), T, g_d, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0

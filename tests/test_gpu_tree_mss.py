@@ -137,3 +137,54 @@ def test_mss_rejects_unsupported_shapes():
     f2 = torch.zeros((1, 2), dtype=torch.float32, device=dev)
     with pytest.raises(sv.SVError):
         sv.verify_tree_mss(x, x, i2, i2, f2, f2, torch.ones(1, device=dev), 1)
+
+
+def test_mss_more_workgroups_than_fit_at_once():
+    """1024 trees over V=20000: 11 workgroups per request (a choose and ten
+    stream workgroups), 11264 in all, more than the GPU holds at once; later
+    requests start only as earlier ones finish."""
+    ti = synth.tree_inputs(seed=15450, B=1024, N=16, V=20000, max_depth=5, temperature=1.0,
+                           family="gauss", draft_sigma=1.0, keep_draft=True)
+    ti.temperature[::4] = 0.0
+    mss_parity(ti, 2, "mss 1024 trees")
+
+
+def test_mss_graph_capture_replays_match_eager():
+    """One MSS call captured in a HIP graph and replayed several times, with
+    eager calls on other uniforms between the replays: every replay gives the
+    eager result and the workspace stays zero."""
+    ti = synth.tree_inputs(seed=15460, B=12, N=30, V=5000, max_depth=6, temperature=1.0,
+                           family="gauss", draft_sigma=1.0, keep_draft=True)
+    ti.temperature[::3] = 0.0
+    dev = torch.device("cuda")
+    lg = to_device_logits(ti.logits, ti.dtype)
+    dl = to_device_logits(ti.draft_logits, ti.dtype)
+    tok = to_device(ti.node_tokens.astype(np.int32))
+    par = to_device(ti.parents.astype(np.int32))
+    T = to_device(ti.temperature.astype(np.float32))
+    ua, ud = to_device(ti.uniforms), to_device(ti.draw_uniforms)
+    need = sv.lib().sv_tree_mss_workspace_bytes(ti.B, ti.N, ti.V, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    want = [x.clone() for x in sv.verify_tree_mss(lg, dl, tok, par, ua, ud, T, ti.max_depth, ws=ws)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            got = sv.verify_tree_mss(lg, dl, tok, par, ua, ud, T, ti.max_depth, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    for r in range(4):
+        for x in got:
+            x.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(got, want):
+            assert torch.equal(x, y), f"replay {r}"
+        assert int(ws.count_nonzero()) == 0
+        sv.verify_tree_mss(lg, dl, tok, par, to_device(synth.uniforms(rng, (ti.B, ti.N))),
+                           to_device(synth.uniforms(rng, (ti.B, ti.N))), T, ti.max_depth, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
