@@ -138,27 +138,26 @@ struct Slice {
 constexpr double kLog2e = 0x1.71547652b82fep+0;
 
 // 2^t for t <= 0 (t = -inf gives 0; t a few ulps above 0 is fine too): t =
-// n + f with n = round(t) and |f| <= 1/2, and 2^f = e^(f ln 2) by its Taylor
-// series to degree 10 -- the constants are (ln 2)^k / k! -- evaluated by
-// Horner's rule (relative truncation at most 3.1e-13, at f = -1/2: far inside
-// the 1e-10 the inverse-CDF draw needs); the result is scaled by 2^n.  No table, so no
-// shared-memory reads on the dependent path of each exponential.
+// n + f with n = rint(t) and |f| <= 1/2, 2^f = 1 + f q(f), and the result
+// scaled by 2^n.  q is the degree-8 polynomial interpolating (2^f - 1) / f at
+// the nine Chebyshev nodes of [-1/2, 1/2] (exp2_coefficients.py derives the
+// constants); the relative error is at most 3.7e-14 (at f = -1/2), far inside
+// the 1e-10 the inverse-CDF draw needs, and 2^0 is exactly 1.  No table, so no shared-memory
+// reads on the dependent path of each exponential.
 __host__ __device__ inline double exp2_neg(double t_in) {
-  constexpr double kShift = 0x1.8p52;  // adding it rounds to an integer
   const double t = __builtin_fmax(t_in, -1100.0);
-  const double n = (t + kShift) - kShift;
+  const double n = __builtin_rint(t);
   const double f = t - n;  // exact, |f| <= 1/2
-  double p = 0x1.e4cf5158b8ecap-28;
-  p = __builtin_fma(p, f, 0x1.b5253d395e7c4p-24);
-  p = __builtin_fma(p, f, 0x1.62c0223a5c824p-20);
-  p = __builtin_fma(p, f, 0x1.ffcbfc588b0c7p-17);
-  p = __builtin_fma(p, f, 0x1.430912f86c787p-13);
-  p = __builtin_fma(p, f, 0x1.5d87fe78a6731p-10);
-  p = __builtin_fma(p, f, 0x1.3b2ab6fba4e77p-7);
-  p = __builtin_fma(p, f, 0x1.c6b08d704a0c0p-5);
-  p = __builtin_fma(p, f, 0x1.ebfbdff82c58fp-3);
-  p = __builtin_fma(p, f, 0x1.62e42fefa39efp-1);
-  p = __builtin_fma(p, f, 1.0);
+  double q = 0x1.b63880a30e9ffp-24;
+  q = __builtin_fma(q, f, 0x1.63d136366db24p-20);
+  q = __builtin_fma(q, f, 0x1.ffcb9515a8016p-17);
+  q = __builtin_fma(q, f, 0x1.4308ac85aa947p-13);
+  q = __builtin_fma(q, f, 0x1.5d87fe86fe88ep-10);
+  q = __builtin_fma(q, f, 0x1.3b2ab7181b755p-7);
+  q = __builtin_fma(q, f, 0x1.c6b08d7047e52p-5);
+  q = __builtin_fma(q, f, 0x1.ebfbdff823cedp-3);
+  q = __builtin_fma(q, f, 0x1.62e42fefa39efp-1);
+  const double p = __builtin_fma(q, f, 1.0);
   return __builtin_ldexp(p, static_cast<int>(n));
 }
 
