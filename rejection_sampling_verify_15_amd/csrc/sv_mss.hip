@@ -23,7 +23,8 @@
 //   stats pass     target chunk max and argmax, fp64 lane sums of
 //                  exp((x - m) / T) and their total; with the draft, its chunk
 //                  max and sum (sampling nodes that have children)
-//   residual pass  fp64 lane sums of max(0, P - A Q) and their total
+//   residual pass  fp64 lane sums of max(0, P - A Q) and their total, P from
+//                  the stats pass's exponentials kept in registers
 // Every pass rewrites every result slot under its own tag (sequence number
 // mod 127), so a slot holds this pass's value or the previous pass's, whose
 // tags differ.  The choose workgroup then decides: argmax descent; or the
@@ -181,13 +182,17 @@ __device__ void mss_stream_loop(const MssArgs& a, int b, int c) {
   uint64_t* slot = mss_slot(a, b, c);
   uint64_t* lp_out = mss_lanes(a, b, c, 0);
   uint64_t* lr_out = mss_lanes(a, b, c, 1);
-  // The node's chunk of both rows (the residual passes recompute their fp64
-  // exponentials from it) and its stats, stored again under every later
-  // pass's tag.
+  // The node's chunk of both rows and its stats, stored again under every
+  // later pass's tag.  The target's fp64 exponentials (relative to the chunk
+  // max) are kept rounded to fp32, so a residual pass computes only the
+  // draft's; the rounding (relative 6e-8 per logit, unbiased) reaches the
+  // residual's sums alone -- the tests' normalisers and the chunk and lane
+  // narrowing of a draw, whose logit scan recomputes fp64 weights.
   float mt = -INFINITY, md = -INFINITY;
   int arg = 0;
   double lp = 0.0, tot_p = 0.0, tot_d = 0.0;
   Raw rt, rd;
+  float et[Raw::kItems * Raw::kPer];
   for (uint32_t s = 0;; ++s) {
     const uint64_t pw = mss_wait_pass(a, b, s);
     if (pw == 0) break;
@@ -216,13 +221,20 @@ __device__ void mss_stream_loop(const MssArgs& a, int b, int c) {
             if (k < c1 && rt.at(j, e) == mt) idx = k;
           }
         arg = wave_min(idx);
-      } else if (mt != -INFINITY) {
+      } else if (mt == -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < Raw::kItems * Raw::kPer; ++i) et[i] = 0.0f;
+      } else {
         const double ml = static_cast<double>(mt) * l2t;
 #pragma unroll
         for (int j = 0; j < Raw::kItems; ++j)
 #pragma unroll
           for (int e = 0; e < Raw::kPer; ++e)
-            lp += exp2_neg(__builtin_fma(static_cast<double>(rt.at(j, e)), l2t, -ml));
+          {
+            const double x = exp2_neg(__builtin_fma(static_cast<double>(rt.at(j, e)), l2t, -ml));
+            et[j * Raw::kPer + e] = static_cast<float>(x);
+            lp += x;
+          }
         tot_p = wave_sum(lp);
       }
       if (kind == kPassStatsDraft) {
@@ -249,11 +261,15 @@ __device__ void mss_stream_loop(const MssArgs& a, int b, int c) {
       MssScalars sc;
       if (!mss_wait_scalars(a, b, s, sc)) break;
       const MssParams q = mss_params(T, sc.Mt, sc.Md, sc.Zt, sc.Zd, sc.A);
+      // P from the stats pass's exponentials, rescaled to the row
+      const double fp = mt != -INFINITY
+                            ? exp2_neg((static_cast<double>(mt) - static_cast<double>(sc.Mt)) * l2t) / sc.Zt : 0.0;
 #pragma unroll
       for (int j = 0; j < Raw::kItems; ++j)
 #pragma unroll
         for (int e = 0; e < Raw::kPer; ++e)
-          lr += mss_weight(mss_p(static_cast<double>(rt.at(j, e)), q), mss_q(static_cast<double>(rd.at(j, e)), q), sc.A);
+          lr += mss_weight(static_cast<double>(et[j * Raw::kPer + e]) * fp,
+                           mss_q(static_cast<double>(rd.at(j, e)), q), sc.A);
       tot_r = wave_sum(lr);
     }
     store_coherent(lp_out + lane, tag_sum(lp, tag));
