@@ -18,6 +18,9 @@ float64, written from these sources (cited by page title and section):
   normaliser), 10 (greedy special case) and 11.3 (per-request RNG streams).
 * "Speculative decoding: draft, verify and payoff", chapter 2 section 2 (the
   four steps of one round).
+* "LLM speculative decoding close-reading notes 02", section 5.4 (any
+  decoding strategy applied alike to p and q keeps the method exact: the
+  consistent top-k filter).
 
 Every reading the pages leave open (which uniform feeds the final draw, the
 inverse-CDF convention, tie-breaks, the empty residual, the tree contract) is
@@ -28,6 +31,7 @@ from .specverify_oracle import (  # noqa: F401
     ChainResult, TreeResult, ProbsResult,
     logits_to_f64, softmax_t, accept_threshold, inverse_cdf_draw,
     chain_distributions, chain_decide_request, verify_chain, RaggedChainResult, verify_chain_ragged,
+    topk_filter, verify_chain_topk, TOPK_MAX, TOPK_MAX_KEPT,
     verify_tree, probs_debug, tree_node_depths, TreeMaskResult, tree_attention_mask,
     mss_thresholds, mss_node, mss_proposals, tree_children, verify_tree_mss,
 )

@@ -58,6 +58,17 @@ R16 ragged rounds: request b drafts gammas[b] tokens in arrays padded to
     gamma; it is exactly the round of gammas[b] drafts (R3 with gamma =
     gammas[b]: its final draw takes uniforms[b, gammas[b]]), reads nothing
     past that length, and is invalid if gammas[b] is outside [0, gamma].
+R17 consistent top-k (close-reading notes 02, section 5.4: the method stays
+    exact when the same decoding rule is applied to p and q): a sampling
+    request with top_k[b] = k filters every target and draft row it uses
+    alike, keeping the logits >= the row's min(k, V)-th largest value
+    (counted with multiplicity, so ties at that value are all kept) and
+    setting the rest to -inf before the temperature softmax; verification
+    then runs unchanged (R1-R8).  Greedy requests ignore k (the argmax is
+    always kept).  Only top-k is taken up; top-p is not.
+R18 top-k contract limits of the library (not of the method): 1 <= k <= 128
+    for a sampling request, and at most 256 kept logits per row (k plus the
+    ties at the threshold); a request outside them is invalid (R11).
 """
 from __future__ import annotations
 
@@ -314,6 +325,61 @@ def verify_chain_ragged(target: np.ndarray, draft: Optional[np.ndarray], draft_t
                 acc[b, d.position] = 1.0 if int(toks[d.position]) == d.outcome else 0.0
         decisions[b] = dec
     return RaggedChainResult(out, nacc, acc, decisions)
+
+
+# ---------------------------------------------------------------------------
+# consistent top-k (R17, R18)
+# ---------------------------------------------------------------------------
+TOPK_MAX = 128
+TOPK_MAX_KEPT = 256
+
+
+def topk_filter(row_f64: np.ndarray, k: int):
+    """R17: keep the logits >= the min(k, V)-th largest value of the row (ties
+    included), -inf elsewhere.  Returns (filtered row, kept count)."""
+    row = np.asarray(row_f64, dtype=np.float64)
+    V = row.shape[0]
+    kk = min(int(k), V)
+    thr = np.sort(row)[V - kk]            # ascending order: the kk-th largest
+    keep = row >= thr
+    return np.where(keep, row, -np.inf), int(np.count_nonzero(keep))
+
+
+def verify_chain_topk(target: np.ndarray, draft: Optional[np.ndarray], draft_tokens: np.ndarray,
+                      uniforms: np.ndarray, temperature: np.ndarray, top_k: np.ndarray,
+                      dtype: str, requests=None) -> ChainResult:
+    """Chain verification with p and q both filtered to their top-k logits
+    (R17, R18); otherwise as verify_chain."""
+    B, G1, V = target.shape
+    gamma = G1 - 1
+    out = np.full((B, gamma + 1), -1, dtype=np.int32)
+    nacc = np.full(B, -1, dtype=np.int32)
+    decisions: List[List[Decision]] = [[] for _ in range(B)]
+    todo = range(B) if requests is None else requests
+    for b in todo:
+        T = float(np.float32(temperature[b]))
+        toks = np.asarray(draft_tokens[b], dtype=np.int64)
+        u = np.asarray(uniforms[b], dtype=np.float32)
+        if _request_invalid(toks, u, T, V):
+            continue
+        tgt = logits_to_f64(target[b], dtype)
+        if T > 0.0:
+            k = int(top_k[b])
+            if not 1 <= k <= TOPK_MAX:
+                continue
+            ft = [topk_filter(r, k) for r in tgt]
+            fd = [topk_filter(r, k) for r in logits_to_f64(draft[b], dtype)] if gamma > 0 else []
+            if max(c for _, c in ft + fd) > TOPK_MAX_KEPT:
+                continue
+            P, Q = chain_distributions(np.array([r for r, _ in ft]),
+                                       np.array([r for r, _ in fd]).reshape(gamma, V), T)
+        else:
+            P, Q = None, None
+        emitted, n, dec = chain_decide_request(P, Q, tgt, toks, u, T)
+        out[b, :len(emitted)] = emitted
+        nacc[b] = n
+        decisions[b] = dec
+    return ChainResult(out, nacc, decisions)
 
 
 # ---------------------------------------------------------------------------
