@@ -88,6 +88,8 @@ typedef enum {
 #define SV_MAX_VOCAB (1 << 24)
 #define SV_MAX_TREE_NODES 1024
 #define SV_MAX_TREE_DEPTH 64
+#define SV_MAX_TOPK 128          /* top_k of a sampling request in spec_verify_chain_topk */
+#define SV_TOPK_MAX_KEPT 256     /* logits a filtered row may keep (k plus ties at the k-th value) */
 
 /* Text for a status code (static storage; never NULL). */
 SV_API const char* sv_status_string(int status);
@@ -130,6 +132,42 @@ SV_API int spec_verify_chain(const void* target_logits, const void* draft_logits
                       const int32_t* draft_tokens, const float* uniforms,
                       const float* temperature, int B, int gamma, int V, int dtype,
                       int32_t* out_tokens, int32_t* out_num_accepted,
+                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Chain verification under a consistent top-k filter.
+ *
+ * Every target and draft row of a sampling request is filtered alike before
+ * the temperature softmax: the logits >= the row's min(k, V)-th largest
+ * value are kept (so every logit equal to that value stays; a row may keep
+ * more than k) and the rest count as -inf.  p' and q' are the softmax of the
+ * filtered rows; the test, the residual draw from norm(max(0, p' - q')) and
+ * the bonus draw from p' are those of spec_verify_chain.  Applying the same
+ * rule to both sides keeps the method exact for the filtered target (the
+ * close-reading notes 02, section 5.4), so the draft tokens must have been
+ * drawn from the filtered q'.  A draft token below its draft row's threshold
+ * has q' = 0 and is accepted (tau = 1 when q' <= p'), as in the unfiltered
+ * call.  Greedy requests (T == 0) ignore top_k: the argmax is always kept.
+ *
+ * The arguments are spec_verify_chain's, plus
+ * top_k            [B]   int32   k of each request, 1 <= k <= SV_MAX_TOPK for
+ *                                a sampling request (k >= V keeps the whole
+ *                                row, which then must fit the kept limit)
+ * and draft_logits is required whenever gamma > 0.  A sampling request is
+ * invalid (count -1, tokens -1) if its k is outside [1, SV_MAX_TOPK] or any
+ * of its rows keeps more than SV_TOPK_MAX_KEPT logits; the other invalid
+ * inputs are those of spec_verify_chain.  Logits are finite or -inf.
+ * Work: one workgroup per row read finds the row's threshold and kept
+ * logits (a sampling row is visited three times, the later visits through
+ * the caches); the test and the draws then touch only the kept logits.
+ * Limits as spec_verify_chain.  Returns an sv_status.
+ * ---------------------------------------------------------------------- */
+SV_API size_t sv_chain_topk_workspace_bytes(int B, int gamma, int V, int dtype);
+
+SV_API int spec_verify_chain_topk(const void* target_logits, const void* draft_logits,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      const float* temperature, const int32_t* top_k, int B, int gamma, int V,
+                      int dtype, int32_t* out_tokens, int32_t* out_num_accepted,
                       void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------------
@@ -337,7 +375,9 @@ typedef enum {
   SV_K_TREE_VERIFY = 11,      /* tree: every depth step of every request in one launch */
   SV_K_TREE_MASK = 12,        /* tree attention mask and depth positions */
   SV_K_TREE_MSS = 13,         /* tree: multi-step speculative sampling, one launch */
-  SV_K_COUNT = 14
+  SV_K_TOPK_ROWS = 14,        /* chain under top-k: each row's max, threshold and kept logits */
+  SV_K_TOPK_DECIDE = 15,      /* chain under top-k: accept tests and draws over the kept logits */
+  SV_K_COUNT = 16
 } sv_kernel;
 
 /* Name of a kernel id (static storage; "unknown" outside [0, SV_K_COUNT)). */

@@ -19,6 +19,7 @@ import torch
 SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_ALIGN, SV_ERR_HIP = range(7)
 SV_BF16, SV_F32 = 0, 1
 SV_MAX_GAMMA = 32
+SV_MAX_TOPK = 128
 
 EXPORTS = {
     # name: (restype, argtypes)
@@ -30,6 +31,9 @@ EXPORTS = {
                           [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]),
     "spec_verify_chain_ragged": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 +
                                  [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "sv_chain_topk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "spec_verify_chain_topk": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 +
+                               [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]),
     "sv_tree_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "spec_verify_tree": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 +
                          [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
@@ -46,7 +50,7 @@ EXPORTS = {
     "sv_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
                                      ctypes.c_int]),
 }
-SV_K_COUNT = 14
+SV_K_COUNT = 16
 
 _LIB = None
 _LOCK = threading.Lock()
@@ -220,6 +224,45 @@ def verify_chain_ragged(target: torch.Tensor, draft: Optional[torch.Tensor], dra
                                     _ptr(out_n), _ptr(acc), _ptr(ws), ws.numel(), _stream_handle(dev))
     _check(st, "spec_verify_chain_ragged")
     return out_tokens, out_n, acc
+
+
+def verify_chain_topk(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: torch.Tensor,
+                      uniforms: torch.Tensor, temperature: torch.Tensor, top_k: torch.Tensor,
+                      ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """spec_verify_chain_topk over device tensors: as verify_chain, with p and
+    q of every sampling request filtered to their rows' top-k logits
+    (top_k [B] int32).  Returns (out_tokens [B, gamma+1], out_num_accepted [B])."""
+    _need_cuda(target, "target")
+    if target.dim() != 3:
+        raise ValueError("target must be [B, gamma+1, V]")
+    B, G1, V = target.shape
+    gamma = G1 - 1
+    dev = target.device
+    dt = _dtype_code(target)
+    if gamma > 0:
+        if draft is None:
+            raise ValueError("draft is required when gamma > 0")
+        _need_cuda(draft, "draft")
+        if draft.dtype != target.dtype or tuple(draft.shape) != (B, gamma, V):
+            raise ValueError("draft must match target's dtype with shape [B, gamma, V]")
+    for name, t, shape, dtype in (("draft_tokens", draft_tokens, (B, gamma), torch.int32),
+                                  ("uniforms", uniforms, (B, gamma + 1), torch.float32),
+                                  ("temperature", temperature, (B,), torch.float32),
+                                  ("top_k", top_k, (B,), torch.int32)):
+        _need_cuda(t, name)
+        if tuple(t.shape) != shape or t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype} with shape {shape}")
+    out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+    out_n = torch.empty((B,), dtype=torch.int32, device=dev)
+    L = lib()
+    nbytes = L.sv_chain_topk_workspace_bytes(B, gamma, V, dt)
+    if ws is None:
+        ws = workspace(nbytes, dev)
+    st = L.spec_verify_chain_topk(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
+                                  _ptr(temperature), _ptr(top_k), B, gamma, V, dt, _ptr(out_tokens),
+                                  _ptr(out_n), _ptr(ws), ws.numel(), _stream_handle(dev))
+    _check(st, "spec_verify_chain_topk")
+    return out_tokens, out_n
 
 
 def verify_tree(logits: torch.Tensor, node_tokens: torch.Tensor, parents: torch.Tensor,

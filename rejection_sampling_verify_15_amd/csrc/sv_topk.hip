@@ -1,0 +1,534 @@
+// Chain verification under a consistent top-k filter: every target and draft
+// row of a sampling request keeps its min(k, V) largest logits (all logits
+// equal to the k-th largest included) and drops the rest before the
+// temperature softmax, the same rule on both sides, which keeps the method
+// exact for the filtered target (close-reading notes 02, section 5.4).  The
+// test and the draws are then those of the unfiltered call (Leviathan et
+// al.'s Algorithm 1 as restated in the close-reading notes 02, section 4).
+// See include/specverify.h for the contract.
+//
+// Two launches on the caller's stream, with no waits between workgroups:
+//
+//  1. topk_rows    one 1024-thread workgroup per (request, row read), each
+//                  wave owning a contiguous tile of the row.  The row's max
+//                  and lowest-index argmax come first.  For a sampling row the
+//                  k-th largest thread maximum bounds the k-th largest logit
+//                  from below (k threads hold a logit at least that large),
+//                  so only the logits at or above it -- about k of them --
+//                  are collected in LDS and sorted (bitonic) for the exact
+//                  k-th largest value.  Should more than 1024 pass the bound,
+//                  a bisection over order-preserving keys takes over.  The
+//                  logits >= that value are then compacted in vocabulary
+//                  order into the row's kept list.  A sampling row is so
+//                  visited three times; the visits after the first read it
+//                  again through the caches.
+//  2. topk_decide  one wave per request: fp64 normalisers over the kept
+//                  lists, the gamma-step test (tau = 1 if q' <= p' else
+//                  p'/q', p' and q' zero below their row's threshold), and
+//                  the residual or bonus draw by inverse CDF over the kept
+//                  list of the draw's target row: max(0, p' - q') vanishes
+//                  outside it, so no row is read again in full.  It returns
+//                  the workspace it read to zero.
+#include <algorithm>
+
+#include "sv_device.hpp"
+#include "sv_host.hpp"
+
+namespace sv {
+namespace {
+
+constexpr int kTopkMax = SV_MAX_TOPK;
+constexpr int kTopkKept = SV_TOPK_MAX_KEPT;
+constexpr int kRowThreads = 1024;
+constexpr int kRowWaves = kRowThreads / kWave;
+constexpr int kCand = kRowThreads;   // logits the exact selection sorts at most
+constexpr int kMaxRowsTopk = 2 * SV_MAX_GAMMA + 1;
+constexpr int kNoIndex = 0x7fffffff;
+
+// One per (request, row).  A sampling row: its kept count, the threshold (the
+// k-th largest logit), max and argmax; a greedy row: count 0 and its argmax.
+// A row that was not read stays all zero.
+struct TopkHead {
+  int32_t count;
+  float thr;
+  float max;
+  int32_t arg;
+};
+struct TopkEntry {
+  int32_t idx;
+  float val;
+};
+
+struct TopkArgs {
+  const void* target;
+  const void* draft;
+  const int32_t* tokens;
+  const float* uniforms;
+  const float* temperature;
+  const int32_t* top_k;
+  int B, gamma, V;
+  int tile;  // logits per wave of a row workgroup (a multiple of its step)
+  int32_t* out_tokens;
+  int32_t* out_n;
+  TopkHead* heads;   // [B][2*gamma+1]
+  TopkEntry* lists;  // [B][2*gamma+1][kTopkKept], vocabulary order
+};
+
+// T must be 0 (greedy) or a finite positive normal float.
+__device__ inline bool topk_temp_ok(float t) { return isfinite(t) && (t == 0.0f || t >= 1.17549435e-38f); }
+
+// Unsigned keys in the order of the floats (-0 just below +0; no NaNs).
+__device__ inline uint32_t order_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float key_float(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k); }
+
+__device__ inline double exp_scaled_t(float x, float m, double l2t) {
+  return exp2_neg((static_cast<double>(x) - static_cast<double>(m)) * l2t);
+}
+
+// The logits one wave of a row workgroup owns: [t0, t1), visited one wave
+// step at a time; at step s lane l holds the kPer logits from
+// t0 + s * kStep + l * kPer.  Every visit reads the tile through the caches,
+// where the next visit finds it again.
+template <int DT, bool VEC>
+struct RowTile {
+  static constexpr int kPer = VEC ? Elem<DT>::kVec : 1;
+  static constexpr int kStep = kWave * kPer;
+  const void* row;
+  int t0, t1;
+
+  __device__ inline void read(int i0, float (&x)[kPer]) const {
+    if constexpr (VEC) {
+      const void* p = static_cast<const char*>(row) + static_cast<size_t>(i0) * Elem<DT>::kBytes;
+      Elem<DT>::unpack(load_row16_cached(p), x);
+    } else {
+      x[0] = Elem<DT>::at(row, i0);
+    }
+  }
+
+  // f(i0, x, valid) for every step, every lane taking part (valid is false
+  // past the tile), so f may use wave-wide operations.
+  template <typename F>
+  __device__ inline void each(F&& f) const {
+    const int lane = threadIdx.x % kWave;
+    constexpr int kU = 4;  // steps whose loads are in flight together
+    for (int base = t0; base < t1; base += kU * kStep) {
+      float x[kU][kPer];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i0 = base + u * kStep + lane * kPer;
+        if (i0 < t1) read(i0, x[u]);
+        else
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) x[u][e] = -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i0 = base + u * kStep + lane * kPer;
+        f(i0, x[u], i0 < t1);
+      }
+    }
+  }
+};
+
+// Sorts kRowThreads floats in LDS into descending order (one per thread).
+__device__ inline void bitonic_desc(float* s) {
+  const int t = threadIdx.x;
+  for (int size = 2; size <= kRowThreads; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      const int p = t ^ stride;
+      if (p > t) {
+        const float x = s[t], y = s[p];
+        const bool up = (t & size) != 0;  // this run is sorted ascending
+        if (up ? (x > y) : (x < y)) {
+          s[t] = y;
+          s[p] = x;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Sum of one int per thread over the workgroup; every thread receives it.
+__device__ inline int block_count(int v, int* s_red) {
+  const int w = threadIdx.x / kWave;
+  v = wave_sum(v);
+  __syncthreads();  // s_red is free again
+  if (threadIdx.x % kWave == 0) s_red[w] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < kRowWaves; ++i) t += s_red[i];
+  return t;
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
+  __shared__ float s_sort[kRowThreads];
+  __shared__ float s_cand[kCand];
+  __shared__ TopkEntry s_keep[kRowWaves][kTopkKept];
+  __shared__ int s_cnt[kRowWaves];
+  __shared__ int s_red[kRowWaves];
+  __shared__ float s_am_v[kRowWaves];
+  __shared__ int s_am_i[kRowWaves];
+  __shared__ int s_ncand;
+  using Tile = RowTile<DT, VEC>;
+  constexpr int kPer = Tile::kPer;
+  const int G = a.gamma;
+  const int R = 2 * G + 1;
+  const int b = static_cast<int>(blockIdx.x / static_cast<unsigned>(R));
+  const int k = static_cast<int>(blockIdx.x - static_cast<unsigned>(b) * R);
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int w = tid / kWave;
+  const float T = a.temperature[b];
+  if (!topk_temp_ok(T)) return;
+  const bool sampling = T > 0.0f;
+  if (!sampling && k > G) return;  // greedy requests read target rows only
+  int kk = 0;
+  if (sampling) {
+    const int kr = a.top_k[b];
+    if (kr < 1 || kr > kTopkMax) return;  // an invalid request: nothing is read
+    kk = min(kr, a.V);
+  }
+  Tile tile;
+  tile.row = k <= G ? static_cast<const char*>(a.target) +
+                          (static_cast<size_t>(b) * (G + 1) + k) * static_cast<size_t>(a.V) * Elem<DT>::kBytes
+                    : static_cast<const char*>(a.draft) +
+                          (static_cast<size_t>(b) * G + (k - G - 1)) * static_cast<size_t>(a.V) * Elem<DT>::kBytes;
+  tile.t0 = min(a.V, w * a.tile);
+  tile.t1 = min(a.V, tile.t0 + a.tile);
+  // 1) max, lowest-index argmax, and this thread's own max
+  ArgMax best{-INFINITY, kNoIndex};
+  tile.each([&](int i0, const float (&x)[kPer], bool valid) {
+    if (valid)
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        if (x[e] > best.v || best.i == kNoIndex) best = ArgMax{x[e], i0 + e};
+  });
+  const float own_max = best.v;
+  ArgMax wb = wave_argmax(best);
+  if (lane == 0) {
+    s_am_v[w] = wb.v;
+    s_am_i[w] = wb.i;
+  }
+  __syncthreads();
+  ArgMax rb{-INFINITY, kNoIndex};
+#pragma unroll
+  for (int i = 0; i < kRowWaves; ++i) rb = argmax_combine(rb, ArgMax{s_am_v[i], s_am_i[i]});
+  TopkHead* head = a.heads + static_cast<size_t>(b) * R + k;
+  if (!sampling) {
+    if (tid == 0) *head = TopkHead{0, -INFINITY, rb.v, rb.i};
+    return;
+  }
+  // 2) a lower bound: the kk-th largest thread maximum
+  s_sort[tid] = own_max;
+  if (tid == 0) s_ncand = 0;
+  bitonic_desc(s_sort);
+  const float lowb = s_sort[kk - 1];
+  // 3) the logits at or above it
+  tile.each([&](int, const float (&x)[kPer], bool valid) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      if (valid && x[e] >= lowb) {
+        const int slot = atomicAdd(&s_ncand, 1);
+        if (slot < kCand) s_cand[slot] = x[e];
+      }
+  });
+  __syncthreads();
+  const int ncand = s_ncand;
+  float thr;
+  if (ncand <= kCand) {
+    if (tid >= ncand) s_cand[tid] = -INFINITY;
+    bitonic_desc(s_cand);
+    thr = s_cand[kk - 1];
+  } else {
+    // bisection over keys: the largest key t with at least kk logits >= t
+    uint32_t lo = 0u, hi = order_key(rb.v) + 1u;
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + (hi - lo) / 2u;
+      int c = 0;
+      tile.each([&](int, const float (&x)[kPer], bool valid) {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) c += (valid && order_key(x[e]) >= mid) ? 1 : 0;
+      });
+      if (block_count(c, s_red) >= kk) lo = mid;
+      else hi = mid;
+    }
+    thr = key_float(lo);
+  }
+  // 4) the kept logits in vocabulary order: staged per wave, then copied out
+  int wcount = 0;
+  const uint64_t below = (1ull << lane) - 1ull;
+  tile.each([&](int i0, const float (&x)[kPer], bool valid) {
+    int n = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) n += (valid && x[e] >= thr) ? 1 : 0;
+    const uint64_t b0 = __ballot(n & 1), b1 = __ballot(n & 2), b2 = __ballot(n & 4), b3 = __ballot(n & 8);
+    if (b0 | b1 | b2 | b3) {
+      int pos = wcount + __popcll(b0 & below) + 2 * __popcll(b1 & below) + 4 * __popcll(b2 & below) +
+                8 * __popcll(b3 & below);
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        if (valid && x[e] >= thr) {
+          if (pos < kTopkKept) s_keep[w][pos] = TopkEntry{i0 + e, x[e]};
+          ++pos;
+        }
+      wcount += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2) + 8 * __popcll(b3);
+    }
+  });
+  if (lane == 0) s_cnt[w] = wcount;
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < kRowWaves; ++i) total += s_cnt[i];
+  if (total <= kTopkKept) {
+    TopkEntry* out = a.lists + (static_cast<size_t>(b) * R + k) * kTopkKept;
+    for (int i = tid; i < total; i += kRowThreads) {
+      int ww = 0, off = 0;
+      while (i - off >= s_cnt[ww]) {
+        off += s_cnt[ww];
+        ++ww;
+      }
+      out[i] = s_keep[ww][i - off];
+    }
+  }
+  if (tid == 0) *head = TopkHead{total, thr, rb.v, rb.i};
+}
+
+// One wave per request.
+template <int DT>
+__global__ __launch_bounds__(kWave) void topk_decide(TopkArgs a) {
+  __shared__ TopkHead s_h[kMaxRowsTopk];
+  __shared__ double s_z[kMaxRowsTopk];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int G = a.gamma;
+  const int R = 2 * G + 1;
+  const int V = a.V;
+  TopkHead* hb = a.heads + static_cast<size_t>(b) * R;
+  TopkEntry* lb = a.lists + static_cast<size_t>(b) * R * kTopkKept;
+  for (int r = lane; r < R; r += kWave) s_h[r] = hb[r];
+  __syncthreads();
+  const float T = a.temperature[b];
+  const bool tok_t = topk_temp_ok(T);
+  const bool sampling = tok_t && T > 0.0f;
+  int bad = !tok_t;
+  if (sampling) {
+    const int kr = a.top_k[b];
+    bad |= (kr < 1 || kr > kTopkMax);
+    for (int r = lane; r < R; r += kWave) bad |= s_h[r].count > kTopkKept;
+  }
+  int32_t x = -1;
+  float u = 0.0f;
+  if (lane < G) {
+    x = a.tokens[static_cast<size_t>(b) * G + lane];
+    bad |= (x < 0 || x >= V);
+  }
+  if (sampling && lane <= G) {
+    u = a.uniforms[static_cast<size_t>(b) * (G + 1) + lane];
+    bad |= !(u >= 0.0f && u < 1.0f);
+  }
+  const bool any_bad = __any(bad);
+  const double l2t = sampling ? kLog2e / static_cast<double>(T) : 0.0;
+  int n = -1;
+  int32_t drawn = -1;
+  if (!any_bad) {
+    if (sampling) {
+      // fp64 normalisers over the kept lists
+      for (int r = 0; r < R; ++r) {
+        const TopkEntry* e = lb + static_cast<size_t>(r) * kTopkKept;
+        const int c = s_h[r].count;
+        double z = 0.0;
+        for (int j = lane; j < c; j += kWave) z += exp_scaled_t(e[j].val, s_h[r].max, l2t);
+        z = wave_sum(z);
+        if (lane == 0) s_z[r] = z;
+      }
+      __syncthreads();
+    }
+    int ok = 1;
+    if (lane < G) {
+      if (!sampling) {
+        ok = (x == s_h[lane].arg);
+      } else {
+        const TopkHead ht = s_h[lane], hd = s_h[G + 1 + lane];
+        const float xt = Elem<DT>::at(static_cast<const char*>(a.target) +
+                                          (static_cast<size_t>(b) * (G + 1) + lane) * static_cast<size_t>(V) *
+                                              Elem<DT>::kBytes,
+                                      x);
+        const float xd = Elem<DT>::at(static_cast<const char*>(a.draft) +
+                                          (static_cast<size_t>(b) * G + lane) * static_cast<size_t>(V) *
+                                              Elem<DT>::kBytes,
+                                      x);
+        const double p = xt >= ht.thr ? exp_scaled_t(xt, ht.max, l2t) / s_z[lane] : 0.0;
+        const double q = xd >= hd.thr ? exp_scaled_t(xd, hd.max, l2t) / s_z[G + 1 + lane] : 0.0;
+        const double tau = (q <= p) ? 1.0 : p / q;
+        ok = static_cast<double>(u) <= tau;
+      }
+    }
+    const uint64_t fail = __ballot(lane < G && !ok);
+    n = fail ? static_cast<int>(__builtin_ctzll(fail)) : G;
+    if (!sampling) {
+      drawn = s_h[n].arg;
+    } else {
+      // the draw over the kept list of target row n: lane l holds entries
+      // 4l .. 4l+3 (vocabulary order runs lane by lane)
+      constexpr int kPerLane = kTopkKept / kWave;
+      const bool residual = n < G;
+      const TopkHead ht = s_h[n];
+      const TopkHead hd = residual ? s_h[G + 1 + n] : TopkHead{0, 0.0f, 0.0f, 0};
+      const double rzt = 1.0 / s_z[n];
+      const double rzd = residual ? 1.0 / s_z[G + 1 + n] : 0.0;
+      const TopkEntry* e = lb + static_cast<size_t>(n) * kTopkKept;
+      const char* drow = residual ? static_cast<const char*>(a.draft) +
+                                        (static_cast<size_t>(b) * G + n) * static_cast<size_t>(V) * Elem<DT>::kBytes
+                                  : nullptr;
+      int idx[kPerLane];
+      double pw[kPerLane], wk[kPerLane];
+      double own = 0.0, own_p = 0.0;
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) {
+        const int pos = lane * kPerLane + j;
+        idx[j] = kNoIndex;
+        pw[j] = 0.0;
+        wk[j] = 0.0;
+        if (pos < ht.count) {
+          const TopkEntry t = e[pos];
+          idx[j] = t.idx;
+          pw[j] = exp_scaled_t(t.val, ht.max, l2t) * rzt;
+          if (residual) {
+            const float d = Elem<DT>::at(drow, t.idx);
+            const double q = d >= hd.thr ? exp_scaled_t(d, hd.max, l2t) * rzd : 0.0;
+            wk[j] = fmax(0.0, pw[j] - q);
+          } else {
+            wk[j] = pw[j];
+          }
+        }
+        own += wk[j];
+        own_p += pw[j];
+      }
+      double W = wave_sum(own);
+      if (residual && !(W > 0.0)) {  // an empty residual: draw from p' of that position
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) wk[j] = pw[j];
+        own = own_p;
+        W = wave_sum(own);
+      }
+      const double target = static_cast<double>(read_lane(u, G)) * W;
+      double run = lane_move<kDppWaveShr1>(wave_inclusive_sum(own));  // lane 0 receives 0
+      int hit = kNoIndex, last = -1;
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) {
+        run += wk[j];
+        if (wk[j] > 0.0) {
+          last = idx[j];
+          if (hit == kNoIndex && run > target) hit = idx[j];
+        }
+      }
+      hit = wave_min(hit);
+      last = wave_max_int(last);
+      drawn = hit != kNoIndex ? hit : last;
+    }
+  }
+  if (lane <= G) {
+    int32_t v = -1;
+    if (!any_bad) v = lane < n ? x : (lane == n ? drawn : -1);
+    a.out_tokens[static_cast<size_t>(b) * (G + 1) + lane] = v;
+  }
+  if (lane == 0) a.out_n[b] = any_bad ? -1 : n;
+  // the workspace this request used back to zero: the kept lists written,
+  // then the heads
+  for (int r = 0; r < R; ++r) {
+    const int c = s_h[r].count <= kTopkKept ? s_h[r].count : 0;
+    uint64_t* z = reinterpret_cast<uint64_t*>(lb + static_cast<size_t>(r) * kTopkKept);
+    for (int j = lane; j < c; j += kWave) z[j] = 0ull;
+  }
+  uint32_t* hz = reinterpret_cast<uint32_t*>(hb);
+  for (int i = lane; i < R * 4; i += kWave) hz[i] = 0u;
+}
+
+struct TopkLayout {
+  size_t heads, lists, total;
+};
+
+TopkLayout topk_layout(int B, int gamma) {
+  const size_t R = 2 * static_cast<size_t>(gamma) + 1;
+  TopkLayout L{};
+  size_t off = 0;
+  L.heads = off;
+  off = align_up(off + static_cast<size_t>(B) * R * sizeof(TopkHead));
+  L.lists = off;
+  off = align_up(off + static_cast<size_t>(B) * R * kTopkKept * sizeof(TopkEntry));
+  L.total = off;
+  return L;
+}
+
+template <int DT, bool VEC>
+void launch_topk(const TopkArgs& a, hipStream_t stream) {
+  const unsigned rows = static_cast<unsigned>(a.B) * static_cast<unsigned>(2 * a.gamma + 1);
+  launch(SV_K_TOPK_ROWS, topk_rows<DT, VEC>, dim3(rows), dim3(kRowThreads), 0, stream, a);
+  launch(SV_K_TOPK_DECIDE, topk_decide<DT>, dim3(static_cast<unsigned>(a.B)), dim3(kWave), 0, stream, a);
+}
+
+}  // namespace
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" size_t sv_chain_topk_workspace_bytes(int B, int gamma, int V, int dtype) {
+  (void)dtype;
+  if (B < 0 || B > SV_MAX_BATCH || gamma < 0 || gamma > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB) return 0;
+  return topk_layout(B, gamma).total;
+}
+
+extern "C" int spec_verify_chain_topk(const void* target_logits, const void* draft_logits,
+                                      const int32_t* draft_tokens, const float* uniforms,
+                                      const float* temperature, const int32_t* top_k, int B, int gamma, int V,
+                                      int dtype, int32_t* out_tokens, int32_t* out_num_accepted, void* workspace,
+                                      size_t workspace_bytes, void* hip_stream) {
+  if (dtype != SV_BF16 && dtype != SV_F32) return SV_ERR_DTYPE;
+  if (B < 0 || B > SV_MAX_BATCH || gamma < 0 || gamma > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB)
+    return SV_ERR_SHAPE;
+  if (B == 0) return SV_OK;
+  if (!target_logits || !temperature || !uniforms || !top_k || !out_tokens || !out_num_accepted || !workspace)
+    return SV_ERR_NULL;
+  if (gamma > 0 && (!draft_tokens || !draft_logits)) return SV_ERR_NULL;
+  const size_t es = dtype == SV_BF16 ? 2 : 4;
+  if (!aligned(target_logits, es) || (gamma > 0 && !aligned(draft_logits, es))) return SV_ERR_ALIGN;
+  const TopkLayout L = topk_layout(B, gamma);
+  if (workspace_bytes < L.total || !aligned(workspace, 256)) return SV_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  TopkArgs a{};
+  a.target = target_logits;
+  a.draft = gamma > 0 ? draft_logits : nullptr;
+  a.tokens = draft_tokens;
+  a.uniforms = uniforms;
+  a.temperature = temperature;
+  a.top_k = top_k;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.out_tokens = out_tokens;
+  a.out_n = out_num_accepted;
+  a.heads = reinterpret_cast<TopkHead*>(ws + L.heads);
+  a.lists = reinterpret_cast<TopkEntry*>(ws + L.lists);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const int kv = dtype == SV_BF16 ? Elem<0>::kVec : Elem<1>::kVec;
+  const bool vec = (V % kv == 0) && aligned(target_logits, 16) && (!a.draft || aligned(a.draft, 16));
+  const int per = vec ? kv : 1;
+  const int step = kWave * per;
+  const int per_wave = (V + kRowWaves - 1) / kRowWaves;
+  a.tile = (per_wave + step - 1) / step * step;
+  if (dtype == SV_BF16) {
+    if (vec) launch_topk<0, true>(a, stream);
+    else launch_topk<0, false>(a, stream);
+  } else {
+    if (vec) launch_topk<1, true>(a, stream);
+    else launch_topk<1, false>(a, stream);
+  }
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
