@@ -17,6 +17,7 @@ Other workloads (--workload) report the same line for the single-request
 latency case (B=1, V=32000, also replayed from a HIP graph), the deep case
 (B=256, gamma=8, V=151936, Zipf logits), the batched inputs as a ragged call
 (request b drafts 1 + b % 4 tokens; rows are the rounds' own rows), the
+batched inputs under a consistent top-k filter (k=50 on p and q), the
 token-tree cases (B=32, 64
 nodes, greedy, naive sampling or multi-step speculative sampling; rows are
 node rows) and the tree attention mask builder on the same tree shape (rows
@@ -86,7 +87,10 @@ def stored_traffic(kernel: str):
     return k.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(ci, budget_s: float = 15.0, gammas=None):
+TOPK = 50                        # k of every sampling request in the top-k workload
+
+
+def cpu_baseline(ci, budget_s: float = 15.0, gammas=None, top_k=None):
     """The fp64 oracle as it stands, timed on this host's cores: it verifies
     the same batch over and over with fresh uniforms until the budget is
     spent.  `cores` is the CPU time it used divided by the wall time."""
@@ -99,7 +103,11 @@ def cpu_baseline(ci, budget_s: float = 15.0, gammas=None):
     while time.perf_counter() - w0 < budget_s:
         u = ci.uniforms if passes == 0 else ci.fresh_uniforms(90_000 + passes)
         for b in range(ci.B):
-            if gammas is None:
+            if top_k is not None:
+                oracle.verify_chain_topk(ci.target[b:b + 1], ci.draft[b:b + 1], ci.draft_tokens[b:b + 1],
+                                         u[b:b + 1], ci.temperature[b:b + 1], top_k[b:b + 1], ci.dtype)
+                rows += ci.gamma + 1
+            elif gammas is None:
                 oracle.verify_chain(ci.target[b:b + 1], ci.draft[b:b + 1], ci.draft_tokens[b:b + 1],
                                     u[b:b + 1], ci.temperature[b:b + 1], ci.dtype)
                 rows += ci.gamma + 1
@@ -119,7 +127,7 @@ def cpu_baseline(ci, budget_s: float = 15.0, gammas=None):
                       f"fresh uniforms, numpy fp64, {wall:.1f} s wall, {cpu:.1f} s CPU"}
 
 
-WORKLOADS = ("batched", "single", "deep", "ragged", "tree-greedy", "tree-sampling", "tree-mss", "tree-mask")
+WORKLOADS = ("batched", "single", "deep", "ragged", "topk", "tree-greedy", "tree-sampling", "tree-mss", "tree-mask")
 
 
 def percentiles(xs):
@@ -164,6 +172,12 @@ def chain_case(name, synth):
         return synth.batched_chain(), ("ragged chain verify: the batched inputs (B=64, gamma padded to 4, "
                                        "V=128256, bf16, even requests T=0.7, odd greedy) with request b "
                                        "drafting 1 + b % 4 tokens")
+    if name == "topk":
+        ci = synth.batched_chain()
+        ci.draft_tokens = synth.topk_draft_tokens(ci, np.full(ci.B, TOPK), 51_000)
+        return ci, ("consistent top-k chain verify: the batched inputs (B=64, gamma=4, V=128256, bf16, even "
+                    f"requests T=0.7, odd greedy), p and q of every sampling request filtered to k={TOPK}, "
+                    "draft tokens drawn from the filtered draft rows")
     if name == "single":
         return synth.single_chain(), ("single-request chain verify: B=1, gamma=4, V=32000, bf16 logits, "
                                       "T=1, fixed logits with fresh uniforms every call (latency)")
@@ -188,9 +202,14 @@ def run_chain(args, torch, synth, sv):
     T = torch.from_numpy(ci.temperature).to(dev)
     out_t = torch.empty((ci.B, ci.gamma + 1), dtype=torch.int32, device=dev)
     out_n = torch.empty((ci.B,), dtype=torch.int32, device=dev)
-    ws = sv.workspace(sv.lib().sv_chain_workspace_bytes(ci.B, ci.gamma, ci.V, sv.SV_BF16), dev)
+    topk = args.workload == "topk"
+    ws_bytes = (sv.lib().sv_chain_topk_workspace_bytes if topk else sv.lib().sv_chain_workspace_bytes)(
+        ci.B, ci.gamma, ci.V, sv.SV_BF16)
+    ws = sv.workspace(ws_bytes, dev)
     stream = torch.cuda.current_stream(dev)
     ragged = args.workload == "ragged"
+    k_np = np.full(ci.B, TOPK, np.int32)
+    k_d = torch.from_numpy(k_np).to(dev)
     gam = np.array([RAGGED_LENGTHS[b % len(RAGGED_LENGTHS)] for b in range(ci.B)], np.int32) if ragged else None
     gam_d = torch.from_numpy(gam).to(dev) if ragged else None
 
@@ -198,6 +217,8 @@ def run_chain(args, torch, synth, sv):
         t, d = sets[i % R]
         if ragged:
             sv.verify_chain_ragged(t, d, tok, u_sets[i % n_u], T, gam_d, ws=ws)
+        elif topk:
+            sv.verify_chain_topk(t, d, tok, u_sets[i % n_u], T, k_d, ws=ws)
         else:
             sv.verify_chain(t, d, tok, u_sets[i % n_u], T, out_tokens=out_t, out_num_accepted=out_n, ws=ws)
 
@@ -216,13 +237,15 @@ def run_chain(args, torch, synth, sv):
     rows = ci.B * (ci.gamma + 1) if gam is None else int(np.sum(gam + 1))
     rd, sm = read_bytes(ci, gam), small_bytes(ci)
     call_us = 1e3 * total_ms / args.steps
-    dominant = "chain_verify"
+    dominant = "topk_rows" if topk else "chain_verify"
     k_us = kt.mean_us(dominant)
     achieved = rd / (k_us * 1e-6) / 1e9
     cfg = {"workload": desc, "B": ci.B, "gamma": ci.gamma, "V": ci.V, "rotating_input_sets": R}
     if ragged:
         cfg["lengths"] = "1 + b % 4"
         cfg["rows_per_call"] = rows
+    if topk:
+        cfg["top_k"] = TOPK
     result = head(args, rows * args.steps / (total_ms * 1e-3), total_ms, cfg)
     result.update({
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -240,7 +263,7 @@ def run_chain(args, torch, synth, sv):
         result["graph_replay"] = graph_replay(torch, stream, sv, sets[0], tok, u_sets[0], T, out_t, out_n, ws,
                                               args.steps)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(ci, gammas=gam)
+        result["cpu_baseline"] = cpu_baseline(ci, gammas=gam, top_k=k_np if topk else None)
     return result
 
 

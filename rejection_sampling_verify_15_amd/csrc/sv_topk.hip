@@ -15,13 +15,14 @@
 //                  k-th largest thread maximum bounds the k-th largest logit
 //                  from below (k threads hold a logit at least that large),
 //                  so only the logits at or above it -- about k of them --
-//                  are collected in LDS and sorted (bitonic) for the exact
-//                  k-th largest value.  Should more than 1024 pass the bound,
-//                  a bisection over order-preserving keys takes over.  The
-//                  logits >= that value are then compacted in vocabulary
-//                  order into the row's kept list.  A sampling row is so
-//                  visited three times; the visits after the first read it
-//                  again through the caches.
+//                  are collected in LDS with their indices, and the exact
+//                  k-th largest value is found among them by a bit-by-bit
+//                  search over order-preserving keys; each kept logit's rank
+//                  by index places it in the row's kept list.  A
+//                  sampling row is so visited twice, the second time through
+//                  the caches.  Should more than 1024 logits pass the bound,
+//                  a bisection over the whole row finds the value and one
+//                  more visit compacts the kept logits in vocabulary order.
 //  2. topk_decide  one wave per request: fp64 normalisers over the kept
 //                  lists, the gamma-step test (tau = 1 if q' <= p' else
 //                  p'/q', p' and q' zero below their row's threshold), and
@@ -42,6 +43,10 @@ constexpr int kTopkKept = SV_TOPK_MAX_KEPT;
 constexpr int kRowThreads = 1024;
 constexpr int kRowWaves = kRowThreads / kWave;
 constexpr int kCand = kRowThreads;   // logits the exact selection sorts at most
+// steps of a tile visit whose loads are in flight together (bf16 unpacks to
+// twice the registers; more of its steps spill)
+constexpr int kInFlight = 16;
+constexpr int kInFlightBf16 = 8;
 constexpr int kMaxRowsTopk = 2 * SV_MAX_GAMMA + 1;
 constexpr int kNoIndex = 0x7fffffff;
 
@@ -99,58 +104,64 @@ struct RowTile {
   const void* row;
   int t0, t1;
 
-  __device__ inline void read(int i0, float (&x)[kPer]) const {
-    if constexpr (VEC) {
-      const void* p = static_cast<const char*>(row) + static_cast<size_t>(i0) * Elem<DT>::kBytes;
-      Elem<DT>::unpack(load_row16_cached(p), x);
-    } else {
-      x[0] = Elem<DT>::at(row, i0);
-    }
-  }
-
   // f(i0, x, valid) for every step, every lane taking part (valid is false
   // past the tile), so f may use wave-wide operations.
   template <typename F>
   __device__ inline void each(F&& f) const {
     const int lane = threadIdx.x % kWave;
-    constexpr int kU = 4;  // steps whose loads are in flight together
+    constexpr int kU = DT == 0 ? kInFlightBf16 : kInFlight;
     for (int base = t0; base < t1; base += kU * kStep) {
-      float x[kU][kPer];
+      if constexpr (VEC) {
+        // the raw groups stay packed until their step is visited
+        uint4 w[kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int i0 = base + u * kStep + lane * kPer;
-        if (i0 < t1) read(i0, x[u]);
-        else
+        for (int u = 0; u < kU; ++u) {
+          const int i0 = base + u * kStep + lane * kPer;
+          if (i0 < t1)
+            w[u] = load_row16_cached(static_cast<const char*>(row) + static_cast<size_t>(i0) * Elem<DT>::kBytes);
+          else
+            w[u] = make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
-          for (int e = 0; e < kPer; ++e) x[u][e] = -INFINITY;
-      }
+        for (int u = 0; u < kU; ++u) {
+          const int i0 = base + u * kStep + lane * kPer;
+          float x[kPer];
+          Elem<DT>::unpack(w[u], x);
+          f(i0, x, i0 < t1);
+        }
+      } else {
+        float x[kU][1];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int i0 = base + u * kStep + lane * kPer;
-        f(i0, x[u], i0 < t1);
+        for (int u = 0; u < kU; ++u) {
+          const int i0 = base + u * kStep + lane;
+          x[u][0] = i0 < t1 ? Elem<DT>::at(row, i0) : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) f(base + u * kStep + lane, x[u], base + u * kStep + lane < t1);
       }
     }
   }
 };
 
-// Sorts kRowThreads floats in LDS into descending order (one per thread).
-__device__ inline void bitonic_desc(float* s) {
-  const int t = threadIdx.x;
-  for (int size = 2; size <= kRowThreads; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      __syncthreads();
-      const int p = t ^ stride;
-      if (p > t) {
-        const float x = s[t], y = s[p];
-        const bool up = (t & size) != 0;  // this run is sorted ascending
-        if (up ? (x > y) : (x < y)) {
-          s[t] = y;
-          s[p] = x;
-        }
-      }
-    }
+// The kk-th largest of one key per thread (0 stands for none): the largest
+// t with at least kk keys >= t, built from the top bit down with one ballot
+// count per bit.  s_buf holds 2 * kRowWaves ints (alternate rounds use
+// alternate halves, so one barrier per bit suffices).
+__device__ inline uint32_t block_kth_key(uint32_t key, int kk, int* s_buf) {
+  const int w = threadIdx.x / kWave;
+  uint32_t ans = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = ans | (1u << bit);
+    const int n = __popcll(__ballot(key >= c));
+    int* buf = s_buf + (bit & 1) * kRowWaves;
+    if (threadIdx.x % kWave == 0) buf[w] = n;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < kRowWaves; ++i) t += buf[i];
+    if (t >= kk) ans = c;
   }
-  __syncthreads();
+  return ans;
 }
 
 // Sum of one int per thread over the workgroup; every thread receives it.
@@ -168,8 +179,12 @@ __device__ inline int block_count(int v, int* s_red) {
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
-  __shared__ float s_sort[kRowThreads];
+  __shared__ int s_bits[2 * kRowWaves];
+  __shared__ float s_kv[kTopkKept];
+  __shared__ int s_ki[kTopkKept];
+  __shared__ int s_nkept;
   __shared__ float s_cand[kCand];
+  __shared__ int s_cidx[kCand];
   __shared__ TopkEntry s_keep[kRowWaves][kTopkKept];
   __shared__ int s_cnt[kRowWaves];
   __shared__ int s_red[kRowWaves];
@@ -226,27 +241,53 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
     return;
   }
   // 2) a lower bound: the kk-th largest thread maximum
-  s_sort[tid] = own_max;
-  if (tid == 0) s_ncand = 0;
-  bitonic_desc(s_sort);
-  const float lowb = s_sort[kk - 1];
-  // 3) the logits at or above it
-  tile.each([&](int, const float (&x)[kPer], bool valid) {
+  if (tid == 0) {
+    s_ncand = 0;
+    s_nkept = 0;
+  }
+  const float lowb = key_float(block_kth_key(order_key(own_max), kk, s_bits));
+  // 3) the logits at or above it, with their indices
+  tile.each([&](int i0, const float (&x)[kPer], bool valid) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e)
       if (valid && x[e] >= lowb) {
         const int slot = atomicAdd(&s_ncand, 1);
-        if (slot < kCand) s_cand[slot] = x[e];
+        if (slot < kCand) {
+          s_cand[slot] = x[e];
+          s_cidx[slot] = i0 + e;
+        }
       }
   });
   __syncthreads();
   const int ncand = s_ncand;
-  float thr;
   if (ncand <= kCand) {
-    if (tid >= ncand) s_cand[tid] = -INFINITY;
-    bitonic_desc(s_cand);
-    thr = s_cand[kk - 1];
-  } else {
+    // every logit >= the threshold is a candidate: the kk-th largest
+    // candidate is the threshold; the kept ones are gathered and each
+    // written at its rank by index
+    const bool mine = tid < ncand;
+    const float cv = mine ? s_cand[tid] : -INFINITY;
+    const int ci = mine ? s_cidx[tid] : kNoIndex;
+    const float thr = key_float(block_kth_key(mine ? order_key(cv) : 0u, kk, s_bits));
+    if (mine && cv >= thr) {
+      const int slot = atomicAdd(&s_nkept, 1);
+      if (slot < kTopkKept) {
+        s_kv[slot] = cv;
+        s_ki[slot] = ci;
+      }
+    }
+    __syncthreads();
+    const int kept = s_nkept;
+    if (kept <= kTopkKept && tid < kept) {
+      const int my = s_ki[tid];
+      int rank = 0;
+      for (int j = 0; j < kept; ++j) rank += s_ki[j] < my ? 1 : 0;
+      a.lists[(static_cast<size_t>(b) * R + k) * kTopkKept + rank] = TopkEntry{my, s_kv[tid]};
+    }
+    if (tid == 0) *head = TopkHead{kept, thr, rb.v, rb.i};
+    return;
+  }
+  float thr;
+  {
     // bisection over keys: the largest key t with at least kk logits >= t
     uint32_t lo = 0u, hi = order_key(rb.v) + 1u;
     while (hi - lo > 1u) {
@@ -396,7 +437,7 @@ __global__ __launch_bounds__(kWave) void topk_decide(TopkArgs a) {
         idx[j] = kNoIndex;
         pw[j] = 0.0;
         wk[j] = 0.0;
-        if (pos < ht.count) {
+        if (pos < ht.count && e[pos].idx >= 0 && e[pos].idx < V) {
           const TopkEntry t = e[pos];
           idx[j] = t.idx;
           pw[j] = exp_scaled_t(t.val, ht.max, l2t) * rzt;

@@ -264,6 +264,26 @@ def chain_inputs(seed: int, B: int, gamma: int, V: int, dtype: str = "bf16",
     return ChainInputs(target, draft, toks, u, T, dtype, B, gamma, V, name, recipe)
 
 
+def topk_draft_tokens(ci: ChainInputs, top_k, seed: int) -> np.ndarray:
+    """Draft tokens of a draft model that decodes with top-k: Gumbel-max over
+    the k largest stored draft logits of each row (k per request, clamped to
+    [1, V]); argmax rows for greedy requests."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((ci.B, ci.gamma), dtype=np.int32)
+    for b in range(ci.B):
+        d = _widen(ci.draft[b], ci.dtype).astype(np.float32)
+        t = float(ci.temperature[b])
+        for i in range(ci.gamma):
+            if t > 0.0:
+                k = min(max(int(top_k[b]), 1), ci.V)
+                top = np.argpartition(-d[i], k - 1)[:k]
+                keys = d[i, top] / np.float32(t) + gumbel(rng, (k,))
+                out[b, i] = int(top[np.argmax(keys)])
+            else:
+                out[b, i] = int(np.argmax(d[i]))
+    return out
+
+
 def toy_chain(seed: int = SEED_BASE + 1, B: int = 4096, gamma: int = 4, V: int = 5):
     """V=5 fp32 toy: target N(0,1), draft = target + N(0, 0.5^2), T = 1."""
     return chain_inputs(seed, B, gamma, V, dtype="f32", family="gauss",
