@@ -9,7 +9,7 @@
 //
 // Two launches on the caller's stream, with no waits between workgroups:
 //
-//  1. topk_rows    one 1024-thread workgroup per (request, row read), each
+//  1. topk_rows    one 512-thread workgroup per (request, row read), each
 //                  wave owning a contiguous tile of the row.  The row's max
 //                  and lowest-index argmax come first.  For a sampling row the
 //                  k-th largest thread maximum bounds the k-th largest logit
@@ -20,7 +20,7 @@
 //                  search over order-preserving keys; each kept logit's rank
 //                  by index places it in the row's kept list.  A
 //                  sampling row is so visited twice, the second time through
-//                  the caches.  Should more than 1024 logits pass the bound,
+//                  the caches.  Should more than 512 logits pass the bound,
 //                  a bisection over the whole row finds the value and one
 //                  more visit compacts the kept logits in vocabulary order.
 //  2. topk_decide  one wave per request: fp64 normalisers over the kept
@@ -40,7 +40,7 @@ namespace {
 
 constexpr int kTopkMax = SV_MAX_TOPK;
 constexpr int kTopkKept = SV_TOPK_MAX_KEPT;
-constexpr int kRowThreads = 1024;
+constexpr int kRowThreads = 512;  // two workgroups per CU at this kernel's registers
 constexpr int kRowWaves = kRowThreads / kWave;
 constexpr int kCand = kRowThreads;   // logits the exact selection sorts at most
 // steps of a tile visit whose loads are in flight together (bf16 unpacks to
@@ -374,20 +374,51 @@ __global__ __launch_bounds__(kWave) void topk_decide(TopkArgs a) {
     u = a.uniforms[static_cast<size_t>(b) * (G + 1) + lane];
     bad |= !(u >= 0.0f && u < 1.0f);
   }
+  // the logits of the draft tokens, loaded before the normalisers are formed
+  float xt = 0.0f, xd = 0.0f;
+  if (sampling && lane < G && x >= 0 && x < V) {
+    xt = Elem<DT>::at(static_cast<const char*>(a.target) +
+                          (static_cast<size_t>(b) * (G + 1) + lane) * static_cast<size_t>(V) * Elem<DT>::kBytes,
+                      x);
+    xd = Elem<DT>::at(static_cast<const char*>(a.draft) +
+                          (static_cast<size_t>(b) * G + lane) * static_cast<size_t>(V) * Elem<DT>::kBytes,
+                      x);
+  }
   const bool any_bad = __any(bad);
   const double l2t = sampling ? kLog2e / static_cast<double>(T) : 0.0;
   int n = -1;
   int32_t drawn = -1;
   if (!any_bad) {
     if (sampling) {
-      // fp64 normalisers over the kept lists
-      for (int r = 0; r < R; ++r) {
-        const TopkEntry* e = lb + static_cast<size_t>(r) * kTopkKept;
-        const int c = s_h[r].count;
-        double z = 0.0;
-        for (int j = lane; j < c; j += kWave) z += exp_scaled_t(e[j].val, s_h[r].max, l2t);
-        z = wave_sum(z);
-        if (lane == 0) s_z[r] = z;
+      // fp64 normalisers over the kept lists, the loads of four rows in
+      // flight at once (lane l sums entries l, l + 64, ... of a row)
+      constexpr int kQ = kTopkKept / kWave;
+      constexpr int kRows = 4;
+      for (int r0 = 0; r0 < R; r0 += kRows) {
+        float v[kRows][kQ];
+#pragma unroll
+        for (int rr = 0; rr < kRows; ++rr) {
+          const int r = min(r0 + rr, R - 1);
+          const int c = r0 + rr < R ? s_h[r].count : 0;
+          const TopkEntry* e = lb + static_cast<size_t>(r) * kTopkKept;
+#pragma unroll
+          for (int q = 0; q < kQ; ++q) {
+            const int j = lane + q * kWave;
+            v[rr][q] = j < c ? e[j].val : -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int rr = 0; rr < kRows; ++rr) {
+          const int r = r0 + rr;
+          if (r < R) {
+            double z = 0.0;
+#pragma unroll
+            for (int q = 0; q < kQ; ++q)
+              if (v[rr][q] != -INFINITY) z += exp_scaled_t(v[rr][q], s_h[r].max, l2t);
+            z = wave_sum(z);
+            if (lane == 0) s_z[r] = z;
+          }
+        }
       }
       __syncthreads();
     }
@@ -397,14 +428,6 @@ __global__ __launch_bounds__(kWave) void topk_decide(TopkArgs a) {
         ok = (x == s_h[lane].arg);
       } else {
         const TopkHead ht = s_h[lane], hd = s_h[G + 1 + lane];
-        const float xt = Elem<DT>::at(static_cast<const char*>(a.target) +
-                                          (static_cast<size_t>(b) * (G + 1) + lane) * static_cast<size_t>(V) *
-                                              Elem<DT>::kBytes,
-                                      x);
-        const float xd = Elem<DT>::at(static_cast<const char*>(a.draft) +
-                                          (static_cast<size_t>(b) * G + lane) * static_cast<size_t>(V) *
-                                              Elem<DT>::kBytes,
-                                      x);
         const double p = xt >= ht.thr ? exp_scaled_t(xt, ht.max, l2t) / s_z[lane] : 0.0;
         const double q = xd >= hd.thr ? exp_scaled_t(xd, hd.max, l2t) / s_z[G + 1 + lane] : 0.0;
         const double tau = (q <= p) ? 1.0 : p / q;
