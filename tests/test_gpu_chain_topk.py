@@ -164,3 +164,67 @@ def test_top1_with_argmax_drafts_equals_the_greedy_call():
     assert one.sum() >= 12
     assert np.array_equal(ot[one], gt[one]) and np.array_equal(on[one], gn[one])
     assert on.max() >= 2
+
+
+def test_topk_longest_draft_interleaved_with_the_plain_call():
+    """gamma = 32 (65 rows per request), and top-k calls alternating with
+    plain calls on the one shared workspace: each matches its oracle."""
+    ci = synth.chain_inputs(15960, B=6, gamma=32, V=5000, dtype="bf16", family="gauss",
+                            draft_sigma=(0.02, 0.3), temperature=1.0, greedy_odd=True)
+    k = np.array([128, 1, 40, 7, 99, 3], np.int32)
+    toks = filtered_draft_tokens(ci, k, 15961)
+    tgt, drf = to_device_logits(ci.target, ci.dtype), to_device_logits(ci.draft, ci.dtype)
+    tok, T, kd = to_device(toks), to_device(ci.temperature), to_device(k)
+    t_topk, t_plain = Tally(), Tally()
+    deepest = 0
+    for s in range(6):
+        u = ci.uniforms if s == 0 else ci.fresh_uniforms(15962 + s)
+        ot, on = sv.verify_chain_topk(tgt, drf, tok, to_device(u), T, kd)
+        ref = oracle.verify_chain_topk(ci.target, ci.draft, toks, u, ci.temperature, k, "bf16")
+        t_topk.add(compare_chain(ref, ot.cpu().numpy(), on.cpu().numpy()))
+        deepest = max(deepest, int(on.max()))
+        pt, pn = sv.verify_chain(tgt, drf, tok, to_device(u), T)
+        pref = oracle.verify_chain(ci.target, ci.draft, toks, u, ci.temperature, "bf16")
+        t_plain.add(compare_chain(pref, pt.cpu().numpy(), pn.cpu().numpy()))
+        assert_shared_workspace_zero("topk then plain")
+    print(f"[topk gamma=32] {t_topk} deepest={deepest}; [plain] {t_plain}", flush=True)
+    t_topk.check("topk gamma=32")
+    t_plain.check("plain after topk")
+    assert deepest >= 8
+
+
+def test_topk_graph_capture_replays_match_eager():
+    """One top-k call captured in a HIP graph and replayed, with eager calls
+    on other uniforms between the replays: every replay gives the eager
+    result and the workspace stays zero."""
+    import torch
+    ci = synth.chain_inputs(15970, B=12, gamma=4, V=20000, dtype="bf16", family="peaked",
+                            draft_sigma=(0.3, 2.0), temperature=0.8, greedy_odd=True)
+    k = np.full(ci.B, 32, np.int32)
+    toks = filtered_draft_tokens(ci, k, 15971)
+    dev = torch.device("cuda")
+    tgt, drf = to_device_logits(ci.target, ci.dtype), to_device_logits(ci.draft, ci.dtype)
+    tok, T, kd, u0 = to_device(toks), to_device(ci.temperature), to_device(k), to_device(ci.uniforms)
+    need = sv.lib().sv_chain_topk_workspace_bytes(ci.B, ci.gamma, ci.V, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    want = [x.clone() for x in sv.verify_chain_topk(tgt, drf, tok, u0, T, kd, ws=ws)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            got = sv.verify_chain_topk(tgt, drf, tok, u0, T, kd, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(4):
+        for x in got:
+            x.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(got, want):
+            assert torch.equal(x, y), f"replay {r}"
+        assert int(ws.count_nonzero()) == 0
+        sv.verify_chain_topk(tgt, drf, tok, to_device(ci.fresh_uniforms(15972 + r)), T, kd, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
