@@ -31,7 +31,7 @@ from .specverify_oracle import (  # noqa: F401
     ChainResult, TreeResult, ProbsResult,
     logits_to_f64, softmax_t, accept_threshold, inverse_cdf_draw,
     chain_distributions, chain_decide_request, verify_chain, RaggedChainResult, verify_chain_ragged,
-    topk_filter, verify_chain_topk, TOPK_MAX, TOPK_MAX_KEPT,
+    topk_filter, topp_filter, verify_chain_topk, TOPK_MAX, TOPK_MAX_KEPT,
     verify_tree, probs_debug, tree_node_depths, TreeMaskResult, tree_attention_mask,
     mss_thresholds, mss_node, mss_proposals, tree_children, verify_tree_mss,
 )

@@ -69,6 +69,12 @@ R17 consistent top-k (close-reading notes 02, section 5.4: the method stays
 R18 top-k contract limits of the library (not of the method): 1 <= k <= 128
     for a sampling request, and at most 256 kept logits per row (k plus the
     ties at the threshold); a request outside them is invalid (R11).
+R19 top-p after top-k (the same rule on both sides, as R17): with top_p[b] =
+    p in (0, 1], every row the top-k filter left is filtered again on its
+    temperature softmax r over the kept logits: the threshold rises to the
+    largest kept logit v whose mass M(v) = sum of r over the kept logits >= v
+    reaches p, and the logits >= v stay (ties at v included).  p = 1 keeps
+    the top-k set; p outside (0, 1] makes the request invalid.
 """
 from __future__ import annotations
 
@@ -345,11 +351,30 @@ def topk_filter(row_f64: np.ndarray, k: int):
     return np.where(keep, row, -np.inf), int(np.count_nonzero(keep))
 
 
+def topp_filter(filtered_row: np.ndarray, p: float, T: float):
+    """R19: on a row the top-k filter left (-inf elsewhere), keep the logits
+    >= the largest kept value v with M(v) >= p, where M(v) is the
+    temperature-softmax mass of the kept logits >= v.  Returns (filtered
+    row, kept count)."""
+    row = np.asarray(filtered_row, dtype=np.float64)
+    kept = np.isfinite(row)
+    if p < 1.0:
+        r = softmax_t(row, T)
+        best = -np.inf
+        for v in row[kept]:
+            if r[row >= v].sum() >= p and v > best:
+                best = v
+        if np.isfinite(best):
+            kept = kept & (row >= best)
+    return np.where(kept, row, -np.inf), int(np.count_nonzero(kept))
+
+
 def verify_chain_topk(target: np.ndarray, draft: Optional[np.ndarray], draft_tokens: np.ndarray,
                       uniforms: np.ndarray, temperature: np.ndarray, top_k: np.ndarray,
-                      dtype: str, requests=None) -> ChainResult:
+                      dtype: str, requests=None, top_p: Optional[np.ndarray] = None) -> ChainResult:
     """Chain verification with p and q both filtered to their top-k logits
-    (R17, R18); otherwise as verify_chain."""
+    (R17, R18), then, with top_p, to their top-p mass (R19); otherwise as
+    verify_chain."""
     B, G1, V = target.shape
     gamma = G1 - 1
     out = np.full((B, gamma + 1), -1, dtype=np.int32)
@@ -371,6 +396,12 @@ def verify_chain_topk(target: np.ndarray, draft: Optional[np.ndarray], draft_tok
             fd = [topk_filter(r, k) for r in logits_to_f64(draft[b], dtype)] if gamma > 0 else []
             if max(c for _, c in ft + fd) > TOPK_MAX_KEPT:
                 continue
+            if top_p is not None:
+                pp = float(np.float32(top_p[b]))
+                if not 0.0 < pp <= 1.0:
+                    continue
+                ft = [topp_filter(r, pp, T) for r, _ in ft]
+                fd = [topp_filter(r, pp, T) for r, _ in fd]
             P, Q = chain_distributions(np.array([r for r, _ in ft]),
                                        np.array([r for r, _ in fd]).reshape(gamma, V), T)
         else:

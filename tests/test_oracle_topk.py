@@ -182,3 +182,99 @@ def test_contract_limits():
     tgt[1, 1, :256] = 9.0
     got = oracle.verify_chain_topk(tgt, ci.draft, ci.draft_tokens, ci.uniforms, T, k, "f32")
     assert got.num_accepted[1] >= 0
+
+
+# ---------------------------------------------------------------------------
+# top-p after top-k (R19)
+# ---------------------------------------------------------------------------
+def library_topp_mask(row, k, p, T):
+    """Sort the top-k logits, cumulate their softmax mass in that order and
+    cut at the first position reaching p (rows without ties)."""
+    keep, _ = library_topk_mask(row, k)
+    x = torch.as_tensor(np.asarray(row, np.float64))
+    kept_vals = x[torch.as_tensor(keep)]
+    srt = torch.sort(kept_vals, descending=True).values
+    cum = torch.cumsum(torch.softmax(srt / T, 0), 0)
+    cut = int(torch.nonzero(cum >= p)[0]) if p < 1.0 else len(srt) - 1
+    return (x >= srt[cut]).numpy() & keep
+
+
+def library_topkp_probs(row, k, p, T):
+    keep = library_topp_mask(row, k, p, T)
+    x = torch.as_tensor(np.asarray(row, np.float64)) / T
+    x = torch.where(torch.as_tensor(keep), x, torch.tensor(-np.inf, dtype=torch.float64))
+    return torch.softmax(x, 0).numpy()
+
+
+def test_topp_cut_matches_sorted_cumsum():
+    rng = np.random.default_rng(15860)
+    for _ in range(300):
+        V = int(rng.integers(2, 300))
+        row = rng.standard_normal(V) * rng.uniform(0.3, 3.0)
+        k = int(rng.integers(1, 129))
+        p = float(rng.choice([1e-6, 0.1, 0.5, 0.8, 0.9, 0.95, 0.999, 1.0]))
+        T = float(rng.uniform(0.3, 2.0))
+        fk, _ = oracle.topk_filter(row, k)
+        fp, count = oracle.topp_filter(fk, p, T)
+        want = library_topp_mask(row, k, p, T)
+        assert np.array_equal(np.isfinite(fp), want) and count == want.sum()
+
+
+def test_topp_keeps_every_tie_at_the_cut():
+    row = np.array([5.0, 3.0, 1.0, 3.0, 3.0, -2.0])
+    fk, _ = oracle.topk_filter(row, 6)
+    r = oracle.softmax_t(fk, 1.0)
+    p = r[0] + r[1] / 2.0                      # the cut falls inside the three tied 3.0s
+    fp, count = oracle.topp_filter(fk, p, 1.0)
+    assert count == 4 and np.isfinite(fp[[0, 1, 3, 4]]).all() and not np.isfinite(fp[[2, 5]]).any()
+    fp, count = oracle.topp_filter(fk, r[0] * 0.999, 1.0)
+    assert count == 1 and np.isfinite(fp[0])
+
+
+def decider_topkp(tgt_rows, drf_rows, k, p, T):
+    def decide(tokens, u):
+        res = oracle.verify_chain_topk(tgt_rows[None].astype(np.float32), drf_rows[None].astype(np.float32),
+                                       np.asarray([tokens], np.int32), np.asarray([u], np.float32),
+                                       np.array([T], np.float32), np.array([k], np.int32), "f32",
+                                       top_p=np.array([p], np.float32))
+        n = int(res.num_accepted[0])
+        return [int(t) for t in res.out_tokens[0, :n + 1]], n
+    return decide
+
+
+def test_emitted_tokens_follow_the_top_k_top_p_target():
+    cut_any = False
+    for seed, V, G, k, p, T in ((15870, 6, 2, 5, 0.7, 0.9), (15871, 5, 1, 4, 0.5, 1.2), (15872, 6, 2, 6, 0.9, 0.6)):
+        rng = np.random.default_rng(seed)
+        tgt = np.round(rng.standard_normal((G + 1, V)) * 1.5, 2).astype(np.float32)
+        drf = (tgt[:G] + np.round(rng.standard_normal((G, V)), 2)).astype(np.float32)
+        pf = float(np.float32(p))
+        P = [library_topkp_probs(tgt[i], k, pf, T) for i in range(G + 1)]
+        Q = [library_topkp_probs(drf[i], k, pf, T) for i in range(G)]
+        law = enumerate_round(P, Q, decider_topkp(tgt, drf, k, p, T))
+        reach, cond = slot_marginals(law, V, G + 1)
+        for s in range(G + 1):
+            if reach[s] > 1e-12:
+                np.testing.assert_allclose(cond[s], P[s], atol=1e-12)
+        cut_any = cut_any or (P[0] > 0).sum() < min(k, V)
+    assert cut_any                              # top-p cut below the top-k set somewhere
+
+
+def test_topp_special_cases_and_limits():
+    ci = synth.chain_inputs(15880, B=30, gamma=4, V=500, dtype="f32", family="gauss",
+                            draft_sigma=(0.1, 1.0), temperature=0.9)
+    k = np.full(ci.B, 40, np.int32)
+    plain = oracle.verify_chain_topk(ci.target, ci.draft, ci.draft_tokens, ci.uniforms, ci.temperature, k, "f32")
+    one = oracle.verify_chain_topk(ci.target, ci.draft, ci.draft_tokens, ci.uniforms, ci.temperature, k, "f32",
+                                   top_p=np.ones(ci.B, np.float32))
+    assert np.array_equal(plain.out_tokens, one.out_tokens) and np.array_equal(plain.num_accepted, one.num_accepted)
+    # a tiny p keeps the maximum alone (no ties in fp32 gaussian rows): greedy
+    toks = np.argmax(ci.draft, axis=2).astype(np.int32)
+    tiny = oracle.verify_chain_topk(ci.target, ci.draft, toks, ci.uniforms, ci.temperature, k, "f32",
+                                    top_p=np.full(ci.B, 1e-6, np.float32))
+    greedy = oracle.verify_chain(ci.target, ci.draft, toks, ci.uniforms, np.zeros(ci.B, np.float32), "f32")
+    assert np.array_equal(tiny.out_tokens, greedy.out_tokens)
+    bad = np.array([0.0, -0.5, 1.5, np.nan] + [0.9] * (ci.B - 4), np.float32)
+    got = oracle.verify_chain_topk(ci.target, ci.draft, ci.draft_tokens, ci.uniforms, ci.temperature, k, "f32",
+                                   top_p=bad)
+    assert (got.num_accepted[:4] == -1).all() and (got.num_accepted[4:] >= 0).all()
