@@ -153,9 +153,18 @@ SV_API int spec_verify_chain(const void* target_logits, const void* draft_logits
  * top_k            [B]   int32   k of each request, 1 <= k <= SV_MAX_TOPK for
  *                                a sampling request (k >= V keeps the whole
  *                                row, which then must fit the kept limit)
+ * top_p            [B]   float   optional (NULL: no top-p): p in (0, 1] of each
+ *                                request.  After the top-k filter, every row
+ *                                is filtered again, alike on both sides: its
+ *                                threshold rises to the largest kept logit v
+ *                                whose mass -- the temperature softmax over
+ *                                the kept logits, summed over those >= v --
+ *                                reaches p, and the logits >= v stay.  p = 1
+ *                                keeps the top-k set.
  * and draft_logits is required whenever gamma > 0.  A sampling request is
- * invalid (count -1, tokens -1) if its k is outside [1, SV_MAX_TOPK] or any
- * of its rows keeps more than SV_TOPK_MAX_KEPT logits; the other invalid
+ * invalid (count -1, tokens -1) if its k is outside [1, SV_MAX_TOPK], its p
+ * (when given) outside (0, 1], or any of its rows keeps more than
+ * SV_TOPK_MAX_KEPT logits after the top-k filter; the other invalid
  * inputs are those of spec_verify_chain.  Logits are finite or -inf.
  * Work: one workgroup per row read finds the row's threshold and kept
  * logits (a sampling row is visited three times, the later visits through
@@ -166,7 +175,8 @@ SV_API size_t sv_chain_topk_workspace_bytes(int B, int gamma, int V, int dtype);
 
 SV_API int spec_verify_chain_topk(const void* target_logits, const void* draft_logits,
                       const int32_t* draft_tokens, const float* uniforms,
-                      const float* temperature, const int32_t* top_k, int B, int gamma, int V,
+                      const float* temperature, const int32_t* top_k, const float* top_p,
+                      int B, int gamma, int V,
                       int dtype, int32_t* out_tokens, int32_t* out_num_accepted,
                       void* workspace, size_t workspace_bytes, void* hip_stream);
 

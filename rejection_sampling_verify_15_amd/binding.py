@@ -32,7 +32,7 @@ EXPORTS = {
     "spec_verify_chain_ragged": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 +
                                  [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
     "sv_chain_topk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
-    "spec_verify_chain_topk": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 +
+    "spec_verify_chain_topk": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 4 +
                                [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]),
     "sv_tree_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "spec_verify_tree": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 +
@@ -228,10 +228,12 @@ def verify_chain_ragged(target: torch.Tensor, draft: Optional[torch.Tensor], dra
 
 def verify_chain_topk(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: torch.Tensor,
                       uniforms: torch.Tensor, temperature: torch.Tensor, top_k: torch.Tensor,
+                      top_p: Optional[torch.Tensor] = None,
                       ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """spec_verify_chain_topk over device tensors: as verify_chain, with p and
     q of every sampling request filtered to their rows' top-k logits
-    (top_k [B] int32).  Returns (out_tokens [B, gamma+1], out_num_accepted [B])."""
+    (top_k [B] int32), then, with top_p ([B] float32), to their top-p mass.
+    Returns (out_tokens [B, gamma+1], out_num_accepted [B])."""
     _need_cuda(target, "target")
     if target.dim() != 3:
         raise ValueError("target must be [B, gamma+1, V]")
@@ -248,7 +250,10 @@ def verify_chain_topk(target: torch.Tensor, draft: Optional[torch.Tensor], draft
     for name, t, shape, dtype in (("draft_tokens", draft_tokens, (B, gamma), torch.int32),
                                   ("uniforms", uniforms, (B, gamma + 1), torch.float32),
                                   ("temperature", temperature, (B,), torch.float32),
-                                  ("top_k", top_k, (B,), torch.int32)):
+                                  ("top_k", top_k, (B,), torch.int32),
+                                  ("top_p", top_p, (B,), torch.float32)):
+        if t is None and name == "top_p":
+            continue
         _need_cuda(t, name)
         if tuple(t.shape) != shape or t.dtype != dtype:
             raise ValueError(f"{name} must be {dtype} with shape {shape}")
@@ -259,7 +264,7 @@ def verify_chain_topk(target: torch.Tensor, draft: Optional[torch.Tensor], draft
     if ws is None:
         ws = workspace(nbytes, dev)
     st = L.spec_verify_chain_topk(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
-                                  _ptr(temperature), _ptr(top_k), B, gamma, V, dt, _ptr(out_tokens),
+                                  _ptr(temperature), _ptr(top_k), _ptr(top_p), B, gamma, V, dt, _ptr(out_tokens),
                                   _ptr(out_n), _ptr(ws), ws.numel(), _stream_handle(dev))
     _check(st, "spec_verify_chain_topk")
     return out_tokens, out_n

@@ -23,6 +23,9 @@
 //                  the caches.  Should more than 512 logits pass the bound,
 //                  a bisection over the whole row finds the value and one
 //                  more visit compacts the kept logits in vocabulary order.
+//                  With top-p, the threshold then rises to the largest kept
+//                  logit whose softmax mass over the kept logits at or above
+//                  it reaches p.
 //  2. topk_decide  one wave per request: fp64 normalisers over the kept
 //                  lists, the gamma-step test (tau = 1 if q' <= p' else
 //                  p'/q', p' and q' zero below their row's threshold), and
@@ -71,6 +74,7 @@ struct TopkArgs {
   const float* uniforms;
   const float* temperature;
   const int32_t* top_k;
+  const float* top_p;  // [B] or NULL: no top-p
   int B, gamma, V;
   int tile;  // logits per wave of a row workgroup (a multiple of its step)
   int32_t* out_tokens;
@@ -164,6 +168,30 @@ __device__ inline uint32_t block_kth_key(uint32_t key, int kk, int* s_buf) {
   return ans;
 }
 
+__device__ inline double block_sum_f64(double v, double* s_red) {
+  const int w = threadIdx.x / kWave;
+  v = wave_sum(v);
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) s_red[w] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < kRowWaves; ++i) t += s_red[i];
+  return t;
+}
+
+__device__ inline float block_max_f32(float v, float* s_red) {
+  const int w = threadIdx.x / kWave;
+  v = wave_max(v);
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) s_red[w] = v;
+  __syncthreads();
+  float t = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kRowWaves; ++i) t = fmaxf(t, s_red[i]);
+  return t;
+}
+
 // Sum of one int per thread over the workgroup; every thread receives it.
 __device__ inline int block_count(int v, int* s_red) {
   const int w = threadIdx.x / kWave;
@@ -182,6 +210,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
   __shared__ int s_bits[2 * kRowWaves];
   __shared__ float s_kv[kTopkKept];
   __shared__ int s_ki[kTopkKept];
+  __shared__ double s_e[kTopkKept];
+  __shared__ double s_dred[kRowWaves];
+  __shared__ float s_fred[kRowWaves];
   __shared__ int s_nkept;
   __shared__ float s_cand[kCand];
   __shared__ int s_cidx[kCand];
@@ -205,10 +236,15 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
   const bool sampling = T > 0.0f;
   if (!sampling && k > G) return;  // greedy requests read target rows only
   int kk = 0;
+  float pp = 1.0f;
   if (sampling) {
     const int kr = a.top_k[b];
     if (kr < 1 || kr > kTopkMax) return;  // an invalid request: nothing is read
     kk = min(kr, a.V);
+    if (a.top_p) {
+      pp = a.top_p[b];
+      if (!(pp > 0.0f && pp <= 1.0f)) return;
+    }
   }
   Tile tile;
   tile.row = k <= G ? static_cast<const char*>(a.target) +
@@ -246,6 +282,41 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
     s_nkept = 0;
   }
   const float lowb = key_float(block_kth_key(order_key(own_max), kk, s_bits));
+  // The end of every sampling row: the kept logits sit in s_kv / s_ki (in
+  // any order) when there are at most kTopkKept of them.  With top-p the
+  // threshold rises to the largest kept value whose mass (the kept logits at
+  // or above it, under the temperature softmax over the kept ones) reaches
+  // p; then every kept logit is written at its rank by index.
+  auto finish = [&](int kept, float thr) {
+    if (kept <= kTopkKept && pp < 1.0f) {
+      const double l2t = kLog2e / static_cast<double>(T);
+      double e = 0.0;
+      if (tid < kept) {
+        e = exp_scaled_t(s_kv[tid], rb.v, l2t);
+        s_e[tid] = e;
+      }
+      const double z = block_sum_f64(e, s_dred);  // its barriers publish s_e
+      float cand = -INFINITY;
+      if (tid < kept) {
+        const float my = s_kv[tid];
+        double m = 0.0;
+        for (int j = 0; j < kept; ++j) m += s_kv[j] >= my ? s_e[j] : 0.0;
+        if (m >= static_cast<double>(pp) * z) cand = my;
+      }
+      const float vp = block_max_f32(cand, s_fred);
+      if (vp > thr) {
+        thr = vp;
+        kept = block_count(tid < kept && s_kv[tid] >= vp ? 1 : 0, s_red);
+      }
+    }
+    if (kept <= kTopkKept && tid < kTopkKept && s_kv[tid] >= thr && tid < s_nkept) {
+      const int my = s_ki[tid];
+      int rank = 0;
+      for (int j = 0; j < s_nkept; ++j) rank += (s_kv[j] >= thr && s_ki[j] < my) ? 1 : 0;
+      a.lists[(static_cast<size_t>(b) * R + k) * kTopkKept + rank] = TopkEntry{my, s_kv[tid]};
+    }
+    if (tid == 0) *head = TopkHead{kept, thr, rb.v, rb.i};
+  };
   // 3) the logits at or above it, with their indices
   tile.each([&](int i0, const float (&x)[kPer], bool valid) {
 #pragma unroll
@@ -276,14 +347,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
       }
     }
     __syncthreads();
-    const int kept = s_nkept;
-    if (kept <= kTopkKept && tid < kept) {
-      const int my = s_ki[tid];
-      int rank = 0;
-      for (int j = 0; j < kept; ++j) rank += s_ki[j] < my ? 1 : 0;
-      a.lists[(static_cast<size_t>(b) * R + k) * kTopkKept + rank] = TopkEntry{my, s_kv[tid]};
-    }
-    if (tid == 0) *head = TopkHead{kept, thr, rb.v, rb.i};
+    finish(s_nkept, thr);
     return;
   }
   float thr;
@@ -328,17 +392,19 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
 #pragma unroll
   for (int i = 0; i < kRowWaves; ++i) total += s_cnt[i];
   if (total <= kTopkKept) {
-    TopkEntry* out = a.lists + (static_cast<size_t>(b) * R + k) * kTopkKept;
     for (int i = tid; i < total; i += kRowThreads) {
       int ww = 0, off = 0;
       while (i - off >= s_cnt[ww]) {
         off += s_cnt[ww];
         ++ww;
       }
-      out[i] = s_keep[ww][i - off];
+      s_kv[i] = s_keep[ww][i - off].val;
+      s_ki[i] = s_keep[ww][i - off].idx;
     }
   }
-  if (tid == 0) *head = TopkHead{total, thr, rb.v, rb.i};
+  if (tid == 0) s_nkept = min(total, kTopkKept);
+  __syncthreads();
+  finish(total, thr);
 }
 
 // One wave per request.
@@ -362,6 +428,10 @@ __global__ __launch_bounds__(kWave) void topk_decide(TopkArgs a) {
   if (sampling) {
     const int kr = a.top_k[b];
     bad |= (kr < 1 || kr > kTopkMax);
+    if (a.top_p) {
+      const float pr = a.top_p[b];
+      bad |= !(pr > 0.0f && pr <= 1.0f);
+    }
     for (int r = lane; r < R; r += kWave) bad |= s_h[r].count > kTopkKept;
   }
   int32_t x = -1;
@@ -551,7 +621,8 @@ extern "C" size_t sv_chain_topk_workspace_bytes(int B, int gamma, int V, int dty
 
 extern "C" int spec_verify_chain_topk(const void* target_logits, const void* draft_logits,
                                       const int32_t* draft_tokens, const float* uniforms,
-                                      const float* temperature, const int32_t* top_k, int B, int gamma, int V,
+                                      const float* temperature, const int32_t* top_k, const float* top_p,
+                                      int B, int gamma, int V,
                                       int dtype, int32_t* out_tokens, int32_t* out_num_accepted, void* workspace,
                                       size_t workspace_bytes, void* hip_stream) {
   if (dtype != SV_BF16 && dtype != SV_F32) return SV_ERR_DTYPE;
@@ -573,6 +644,7 @@ extern "C" int spec_verify_chain_topk(const void* target_logits, const void* dra
   a.uniforms = uniforms;
   a.temperature = temperature;
   a.top_k = top_k;
+  a.top_p = top_p;
   a.B = B;
   a.gamma = gamma;
   a.V = V;

@@ -12,31 +12,33 @@ from parity import Tally, assert_shared_workspace_zero, compare_chain, to_device
 pytestmark = pytest.mark.gpu
 
 
-def run_topk(ci, top_k, u_sets, target=None, draft=None, tokens=None):
+def run_topk(ci, top_k, u_sets, target=None, draft=None, tokens=None, top_p=None):
     tgt = to_device_logits(ci.target if target is None else target, ci.dtype)
     drf = to_device_logits(ci.draft if draft is None else draft, ci.dtype)
     tok = to_device((ci.draft_tokens if tokens is None else tokens).astype(np.int32))
     T = to_device(ci.temperature.astype(np.float32))
     k = to_device(np.asarray(top_k, np.int32))
+    pd = None if top_p is None else to_device(np.asarray(top_p, np.float32))
     outs = []
     for u in u_sets:
-        ot, on = sv.verify_chain_topk(tgt, drf, tok, to_device(np.asarray(u, np.float32)), T, k)
+        ot, on = sv.verify_chain_topk(tgt, drf, tok, to_device(np.asarray(u, np.float32)), T, k, top_p=pd)
         outs.append((ot.cpu().numpy(), on.cpu().numpy()))
     assert_shared_workspace_zero("chain topk")
     return outs
 
 
-def topk_parity(ci, top_k, n_sets, label, seed=9, target=None, draft=None, tokens=None):
+def topk_parity(ci, top_k, n_sets, label, seed=9, target=None, draft=None, tokens=None, top_p=None):
     u_sets = [ci.uniforms] + [ci.fresh_uniforms(seed * 1000 + s) for s in range(n_sets - 1)]
     print(f"[{label}] B={ci.B} gamma={ci.gamma} V={ci.V} dtype={ci.dtype} sets={n_sets}", flush=True)
-    gpu = run_topk(ci, top_k, u_sets, target, draft, tokens)
+    gpu = run_topk(ci, top_k, u_sets, target, draft, tokens, top_p)
     tgt = ci.target if target is None else target
     drf = ci.draft if draft is None else draft
     tok = ci.draft_tokens if tokens is None else tokens
     tally = Tally()
     refs = []
     for (ot, on), u in zip(gpu, u_sets):
-        ref = oracle.verify_chain_topk(tgt, drf, tok, u, ci.temperature, np.asarray(top_k), ci.dtype)
+        ref = oracle.verify_chain_topk(tgt, drf, tok, u, ci.temperature, np.asarray(top_k), ci.dtype,
+                                       top_p=None if top_p is None else np.asarray(top_p, np.float32))
         tally.add(compare_chain(ref, ot, on))
         refs.append(ref)
     print(f"[{label}] {tally}", flush=True)
@@ -44,7 +46,7 @@ def topk_parity(ci, top_k, n_sets, label, seed=9, target=None, draft=None, token
     return gpu, refs
 
 
-def filtered_draft_tokens(ci, top_k, seed):
+def filtered_draft_tokens(ci, top_k, seed, top_p=None):
     """Draft tokens drawn from the filtered draft distributions (the
     consistent setting), by Gumbel-max over the kept logits."""
     rng = np.random.default_rng(seed)
@@ -57,6 +59,8 @@ def filtered_draft_tokens(ci, top_k, seed):
             if T > 0.0:
                 # requests with an invalid k draw from a clamped one
                 f, _ = oracle.topk_filter(d[i], min(max(int(top_k[b]), 1), oracle.TOPK_MAX))
+                if top_p is not None and 0.0 < float(top_p[b]) < 1.0:
+                    f, _ = oracle.topp_filter(f, float(np.float32(top_p[b])), T)
                 toks[b, i] = int(np.argmax(f / T + rng.gumbel(size=ci.V)))
             else:
                 toks[b, i] = int(np.argmax(d[i]))
@@ -228,3 +232,61 @@ def test_topk_graph_capture_replays_match_eager():
         sv.verify_chain_topk(tgt, drf, tok, to_device(ci.fresh_uniforms(15972 + r)), T, kd, ws=ws)
         torch.cuda.synchronize()
         assert int(ws.count_nonzero()) == 0
+
+
+def test_topp_batched_shape():
+    """The batched shape with k = 50 and p = 0.9 on every sampling request."""
+    ci = synth.batched_chain()
+    k = np.full(ci.B, 50, np.int32)
+    p = np.full(ci.B, 0.9, np.float32)
+    toks = filtered_draft_tokens(ci, k, 15980, top_p=p)
+    gpu, refs = topk_parity(ci, k, 3, "topk+topp batched", tokens=toks, top_p=p)
+    assert all((r.num_accepted >= 0).all() for r in refs)
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 3000), ("f32", 999), ("bf16", 20001)])
+def test_topp_small_many_rounds(dtype, V):
+    ci = synth.chain_inputs(15985 + V % 89, B=40, gamma=5, V=V, dtype=dtype, family="gauss",
+                            draft_sigma=(0.1, 1.5), temperature=0.8, greedy_odd=True)
+    rng = np.random.default_rng(15986)
+    k = rng.integers(1, 129, size=ci.B).astype(np.int32)
+    p = rng.choice(np.array([0.2, 0.5, 0.8, 0.9, 0.97, 1.0], np.float32), size=ci.B)
+    toks = filtered_draft_tokens(ci, k, 15987, top_p=p)
+    topk_parity(ci, k, 12, f"topk+topp {dtype} V={V}", tokens=toks, top_p=p)
+
+
+def test_topp_after_the_bisection_fallback_and_bad_p():
+    """Flat rows (the bisection path) with top-p, and p values outside
+    (0, 1] (invalid requests)."""
+    B, G, V = 8, 2, 20000
+    rng = np.random.default_rng(15990)
+    tgt = np.full((B, G + 1, V), -1.0, np.float32)
+    drf = np.full((B, G, V), -1.0, np.float32)
+    for b in range(B):
+        for r in range(G + 1):
+            s0 = int(rng.integers(0, V - 200))
+            tgt[b, r, s0:s0 + 200] = rng.uniform(2.0, 6.0, 200).astype(np.float32)
+        for r in range(G):
+            s0 = int(rng.integers(0, V - 200))
+            drf[b, r, s0:s0 + 200] = rng.uniform(2.0, 6.0, 200).astype(np.float32)
+    ci = synth.ChainInputs(tgt, drf, np.zeros((B, G), np.int32), synth.uniforms(rng, (B, G + 1)),
+                           np.full(B, 1.0, np.float32), "f32", B, G, V, "flat", "flat background")
+    k = np.array([128, 64, 100, 128, 128, 50, 50, 50], np.int32)
+    p = np.array([0.5, 0.9, 0.99, 1.0, 0.05, 0.0, 1.5, np.nan], np.float32)
+    toks = filtered_draft_tokens(ci, k, 15991, top_p=np.where(np.isfinite(p) & (p > 0) & (p <= 1), p, 1.0))
+    gpu, refs = topk_parity(ci, k, 6, "topk+topp bisection", tokens=toks, top_p=p)
+    on = gpu[0][1]
+    assert (on[:5] >= 0).all() and (on[5:] == -1).all()
+
+
+def test_tiny_top_p_with_argmax_drafts_equals_the_greedy_call():
+    ci = synth.chain_inputs(15995, B=32, gamma=4, V=30000, dtype="f32", family="gauss",
+                            draft_sigma=(0.05, 0.8), temperature=0.8)
+    toks = np.argmax(ci.draft, axis=2).astype(np.int32)
+    k = np.full(ci.B, 64, np.int32)
+    p = np.full(ci.B, 1e-6, np.float32)
+    gpu, _ = topk_parity(ci, k, 1, "topk+topp tiny p", tokens=toks, top_p=p)
+    ot, on = gpu[0]
+    gt, gn = sv.verify_chain(to_device_logits(ci.target, ci.dtype), None, to_device(toks), to_device(ci.uniforms),
+                             to_device(np.zeros(ci.B, np.float32)))
+    assert np.array_equal(ot, gt.cpu().numpy()) and np.array_equal(on, gn.cpu().numpy())
