@@ -205,7 +205,9 @@ __device__ inline int block_count(int v, int* s_red) {
   return t;
 }
 
-template <int DT, bool VEC>
+// TOPP: top_p is given (a separate instantiation, so that calls without it
+// carry none of its work).
+template <int DT, bool VEC, bool TOPP>
 __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
   __shared__ int s_bits[2 * kRowWaves];
   __shared__ float s_kv[kTopkKept];
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
     const int kr = a.top_k[b];
     if (kr < 1 || kr > kTopkMax) return;  // an invalid request: nothing is read
     kk = min(kr, a.V);
-    if (a.top_p) {
+    if constexpr (TOPP) {
       pp = a.top_p[b];
       if (!(pp > 0.0f && pp <= 1.0f)) return;
     }
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
   // or above it, under the temperature softmax over the kept ones) reaches
   // p; then every kept logit is written at its rank by index.
   auto finish = [&](int kept, float thr) {
-    if (kept <= kTopkKept && pp < 1.0f) {
+    if (TOPP && kept <= kTopkKept && pp < 1.0f) {
       const double l2t = kLog2e / static_cast<double>(T);
       double e = 0.0;
       if (tid < kept) {
@@ -312,7 +314,11 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
     if (kept <= kTopkKept && tid < kTopkKept && s_kv[tid] >= thr && tid < s_nkept) {
       const int my = s_ki[tid];
       int rank = 0;
-      for (int j = 0; j < s_nkept; ++j) rank += (s_kv[j] >= thr && s_ki[j] < my) ? 1 : 0;
+      if constexpr (TOPP) {
+        for (int j = 0; j < s_nkept; ++j) rank += (s_kv[j] >= thr && s_ki[j] < my) ? 1 : 0;
+      } else {  // every staged logit is kept
+        for (int j = 0; j < s_nkept; ++j) rank += s_ki[j] < my ? 1 : 0;
+      }
       a.lists[(static_cast<size_t>(b) * R + k) * kTopkKept + rank] = TopkEntry{my, s_kv[tid]};
     }
     if (tid == 0) *head = TopkHead{kept, thr, rb.v, rb.i};
@@ -604,7 +610,10 @@ TopkLayout topk_layout(int B, int gamma) {
 template <int DT, bool VEC>
 void launch_topk(const TopkArgs& a, hipStream_t stream) {
   const unsigned rows = static_cast<unsigned>(a.B) * static_cast<unsigned>(2 * a.gamma + 1);
-  launch(SV_K_TOPK_ROWS, topk_rows<DT, VEC>, dim3(rows), dim3(kRowThreads), 0, stream, a);
+  if (a.top_p)
+    launch(SV_K_TOPK_ROWS, topk_rows<DT, VEC, true>, dim3(rows), dim3(kRowThreads), 0, stream, a);
+  else
+    launch(SV_K_TOPK_ROWS, topk_rows<DT, VEC, false>, dim3(rows), dim3(kRowThreads), 0, stream, a);
   launch(SV_K_TOPK_DECIDE, topk_decide<DT>, dim3(static_cast<unsigned>(a.B)), dim3(kWave), 0, stream, a);
 }
 
