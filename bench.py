@@ -90,7 +90,7 @@ def stored_traffic(kernel: str):
 TOPK = 50                        # k of every sampling request in the top-k workload
 
 
-def cpu_baseline(ci, budget_s: float = 15.0, gammas=None, top_k=None):
+def cpu_baseline(ci, budget_s: float = 15.0, gammas=None, top_k=None, top_p=None):
     """The fp64 oracle as it stands, timed on this host's cores: it verifies
     the same batch over and over with fresh uniforms until the budget is
     spent.  `cores` is the CPU time it used divided by the wall time."""
@@ -105,7 +105,8 @@ def cpu_baseline(ci, budget_s: float = 15.0, gammas=None, top_k=None):
         for b in range(ci.B):
             if top_k is not None:
                 oracle.verify_chain_topk(ci.target[b:b + 1], ci.draft[b:b + 1], ci.draft_tokens[b:b + 1],
-                                         u[b:b + 1], ci.temperature[b:b + 1], top_k[b:b + 1], ci.dtype)
+                                         u[b:b + 1], ci.temperature[b:b + 1], top_k[b:b + 1], ci.dtype,
+                                         top_p=None if top_p is None else top_p[b:b + 1])
                 rows += ci.gamma + 1
             elif gammas is None:
                 oracle.verify_chain(ci.target[b:b + 1], ci.draft[b:b + 1], ci.draft_tokens[b:b + 1],
@@ -210,6 +211,8 @@ def run_chain(args, torch, synth, sv):
     ragged = args.workload == "ragged"
     k_np = np.full(ci.B, TOPK, np.int32)
     k_d = torch.from_numpy(k_np).to(dev)
+    p_np = np.full(ci.B, args.top_p, np.float32) if topk and args.top_p is not None else None
+    p_d = torch.from_numpy(p_np).to(dev) if p_np is not None else None
     gam = np.array([RAGGED_LENGTHS[b % len(RAGGED_LENGTHS)] for b in range(ci.B)], np.int32) if ragged else None
     gam_d = torch.from_numpy(gam).to(dev) if ragged else None
 
@@ -218,7 +221,7 @@ def run_chain(args, torch, synth, sv):
         if ragged:
             sv.verify_chain_ragged(t, d, tok, u_sets[i % n_u], T, gam_d, ws=ws)
         elif topk:
-            sv.verify_chain_topk(t, d, tok, u_sets[i % n_u], T, k_d, ws=ws)
+            sv.verify_chain_topk(t, d, tok, u_sets[i % n_u], T, k_d, top_p=p_d, ws=ws)
         else:
             sv.verify_chain(t, d, tok, u_sets[i % n_u], T, out_tokens=out_t, out_num_accepted=out_n, ws=ws)
 
@@ -246,6 +249,8 @@ def run_chain(args, torch, synth, sv):
         cfg["rows_per_call"] = rows
     if topk:
         cfg["top_k"] = TOPK
+        if p_np is not None:
+            cfg["top_p"] = args.top_p
     result = head(args, rows * args.steps / (total_ms * 1e-3), total_ms, cfg)
     result.update({
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -263,7 +268,7 @@ def run_chain(args, torch, synth, sv):
         result["graph_replay"] = graph_replay(torch, stream, sv, sets[0], tok, u_sets[0], T, out_t, out_n, ws,
                                               args.steps)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(ci, gammas=gam, top_k=k_np if topk else None)
+        result["cpu_baseline"] = cpu_baseline(ci, gammas=gam, top_k=k_np if topk else None, top_p=p_np)
     return result
 
 
@@ -502,6 +507,8 @@ def main():
     ap.add_argument("--workload", choices=WORKLOADS, default="batched",
                     help="batched is the headline; the others are reported alongside it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--top-p", type=float, default=None,
+                    help="topk workload: also filter to this top-p mass after top-k (draft tokens stay top-k draws)")
     args = ap.parse_args()
     if args.steps is None:
         args.steps = 10000 if args.workload == "single" else 200
