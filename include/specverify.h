@@ -167,8 +167,9 @@ SV_API int spec_verify_chain(const void* target_logits, const void* draft_logits
  * SV_TOPK_MAX_KEPT logits after the top-k filter; the other invalid
  * inputs are those of spec_verify_chain.  Logits are finite or -inf.
  * Work: one workgroup per row read finds the row's threshold and kept
- * logits (a sampling row is visited three times, the later visits through
- * the caches); the test and the draws then touch only the kept logits.
+ * logits (a sampling row is visited twice, the second visit mostly through
+ * the caches, and more often only when more than 512 logits reach the first
+ * bound); the test and the draws then touch only the kept logits.
  * Limits as spec_verify_chain.  Returns an sv_status.
  * ---------------------------------------------------------------------- */
 SV_API size_t sv_chain_topk_workspace_bytes(int B, int gamma, int V, int dtype);

@@ -65,7 +65,7 @@ R17 consistent top-k (close-reading notes 02, section 5.4: the method stays
     (counted with multiplicity, so ties at that value are all kept) and
     setting the rest to -inf before the temperature softmax; verification
     then runs unchanged (R1-R8).  Greedy requests ignore k (the argmax is
-    always kept).  Only top-k is taken up; top-p is not.
+    always kept).
 R18 top-k contract limits of the library (not of the method): 1 <= k <= 128
     for a sampling request, and at most 256 kept logits per row (k plus the
     ties at the threshold); a request outside them is invalid (R11).
@@ -134,6 +134,13 @@ def accept_threshold(p_x: float, q_x: float) -> float:
     if q_x <= p_x:
         return 1.0
     return p_x / q_x
+
+
+def accepts(u: float, tau: float) -> bool:
+    """The accept test of one draft token (R1): accept iff u <= tau.  The
+    close-reading notes (section 4, the full algorithm) accept draft i when
+    r_i <= min(1, p(x)/q(x)), equality included."""
+    return u <= tau
 
 
 def residual_weights(p: np.ndarray, q: np.ndarray) -> np.ndarray:
@@ -225,7 +232,7 @@ def chain_decide_request(P, Q, target_f64, tokens, u, T):
         x = int(tokens[i])
         tau = accept_threshold(P[i][x], Q[i][x])
         ui = float(u[i])
-        ok = ui <= tau                                     # R1
+        ok = accepts(ui, tau)                              # R1
         decisions.append(Decision("accept", i, ui, tau, int(ok), abs(ui - tau)))
         if ok:
             emitted.append(x)
@@ -543,7 +550,7 @@ def mss_node(p: np.ndarray, proposals, u_accept, u_draw: float):
     dec: List[Decision] = []
     for j, tau in enumerate(taus):
         u = float(u_accept[j])
-        ok = u <= tau
+        ok = accepts(u, tau)
         dec.append(Decision("accept", j, u, tau, int(ok), abs(u - tau)))
         if ok:
             return j, int(proposals[j][0]), dec
