@@ -74,7 +74,8 @@ typedef enum {
   SV_ERR_DTYPE = 3,       /* dtype is not one of sv_dtype */
   SV_ERR_WORKSPACE = 4,   /* workspace too small or not 256-byte aligned */
   SV_ERR_ALIGN = 5,       /* a logit pointer is not aligned to its element size */
-  SV_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed */
+  SV_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed */
+  SV_ERR_SCRATCH = 7      /* spec_verify_chain_noalloc: the shape needs more than SV_CHAIN_SCRATCH_BYTES */
 } sv_status;
 
 typedef enum {
@@ -133,6 +134,33 @@ SV_API int spec_verify_chain(const void* target_logits, const void* draft_logits
                       const float* temperature, int B, int gamma, int V, int dtype,
                       int32_t* out_tokens, int32_t* out_num_accepted,
                       void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Chain verification that allocates nothing and takes no workspace.
+ *
+ * For callers that cannot allocate device memory or size a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Arguments, results and error behaviour are those of
+ * spec_verify_chain, which this call runs with the same kernels; the
+ * workspace is instead a static device array of SV_CHAIN_SCRATCH_BYTES that
+ * the library keeps on each GPU it runs on until the process ends.  The
+ * first call on a GPU zero-fills that array with a fill kernel on
+ * `hip_stream`; every call that completes leaves it zero again.
+ * A shape whose workspace (sv_chain_workspace_bytes) exceeds
+ * SV_CHAIN_SCRATCH_BYTES returns SV_ERR_SCRATCH without launching anything.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams without ordering between them) race and give
+ * unspecified results.  A call with B == 0 launches only the zero-fill of
+ * the array on `hip_stream`: that is how to reset it after a call that did
+ * not complete (a bounded wait that gave up, which only a dispatch order the
+ * hardware does not use can cause; its requests report -1).
+ * ---------------------------------------------------------------------- */
+#define SV_CHAIN_SCRATCH_BYTES (8u << 20)
+
+SV_API int spec_verify_chain_noalloc(const void* target_logits, const void* draft_logits,
+                              const int32_t* draft_tokens, const float* uniforms,
+                              const float* temperature, int B, int gamma, int V, int dtype,
+                              int32_t* out_tokens, int32_t* out_num_accepted, void* hip_stream);
 
 /* ------------------------------------------------------------------------
  * Chain verification under a consistent top-k filter.

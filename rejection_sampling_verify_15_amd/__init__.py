@@ -6,11 +6,11 @@ package is a thin argument-marshalling binding over it.
 """
 from . import build  # noqa: F401
 from .binding import (  # noqa: F401
-    KernelTimer, SVError, lib, library_path, probs_debug, tree_mask, verify_chain,
+    KernelTimer, SVError, lib, library_path, probs_debug, tree_mask, verify_chain, verify_chain_noalloc,
     verify_chain_ragged, verify_chain_topk, verify_tree, verify_tree_mss, workspace,
-    SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_ALIGN, SV_ERR_HIP,
+    SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_ALIGN, SV_ERR_HIP, SV_ERR_SCRATCH,
     SV_BF16, SV_F32,
 )
 
-__all__ = ["verify_chain", "verify_chain_ragged", "verify_chain_topk", "verify_tree", "verify_tree_mss", "tree_mask", "probs_debug", "lib", "SVError", "workspace",
+__all__ = ["verify_chain", "verify_chain_noalloc", "verify_chain_ragged", "verify_chain_topk", "verify_tree", "verify_tree_mss", "tree_mask", "probs_debug", "lib", "SVError", "workspace",
            "KernelTimer"]

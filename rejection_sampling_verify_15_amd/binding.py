@@ -16,7 +16,7 @@ from typing import Optional, Tuple
 import torch
 
 
-SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_ALIGN, SV_ERR_HIP = range(7)
+SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_ALIGN, SV_ERR_HIP, SV_ERR_SCRATCH = range(8)
 SV_BF16, SV_F32 = 0, 1
 SV_MAX_GAMMA = 32
 SV_MAX_TOPK = 128
@@ -29,6 +29,8 @@ EXPORTS = {
     "sv_chain_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "spec_verify_chain": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 +
                           [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "spec_verify_chain_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 +
+                                  [ctypes.c_void_p] * 3),
     "spec_verify_chain_ragged": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 +
                                  [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
     "sv_chain_topk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
@@ -179,6 +181,39 @@ def verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_toke
                              _ptr(temperature), B, gamma, V, dt, _ptr(out_tokens),
                              _ptr(out_num_accepted), _ptr(ws), ws.numel(), _stream_handle(dev))
     _check(st, "spec_verify_chain")
+    return out_tokens, out_num_accepted
+
+
+def verify_chain_noalloc(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: torch.Tensor,
+                         uniforms: torch.Tensor, temperature: torch.Tensor,
+                         out_tokens: torch.Tensor, out_num_accepted: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """spec_verify_chain_noalloc over device tensors: verify_chain with the
+    library's static scratch array as its workspace.  The caller passes the
+    outputs (out_tokens [B, gamma+1] int32, out_num_accepted [B] int32), so
+    nothing is allocated on the call."""
+    _need_cuda(target, "target")
+    if target.dim() != 3:
+        raise ValueError("target must be [B, gamma+1, V]")
+    B, G1, V = target.shape
+    gamma = G1 - 1
+    dev = target.device
+    dt = _dtype_code(target)
+    if draft is not None:
+        _need_cuda(draft, "draft")
+        if draft.dtype != target.dtype or tuple(draft.shape) != (B, gamma, V):
+            raise ValueError("draft must match target's dtype with shape [B, gamma, V]")
+    for name, t, shape, dtype in (("draft_tokens", draft_tokens, (B, gamma), torch.int32),
+                                  ("uniforms", uniforms, (B, gamma + 1), torch.float32),
+                                  ("temperature", temperature, (B,), torch.float32),
+                                  ("out_tokens", out_tokens, (B, gamma + 1), torch.int32),
+                                  ("out_num_accepted", out_num_accepted, (B,), torch.int32)):
+        _need_cuda(t, name)
+        if tuple(t.shape) != shape or t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype} with shape {shape}")
+    st = lib().spec_verify_chain_noalloc(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
+                                         _ptr(temperature), B, gamma, V, dt, _ptr(out_tokens),
+                                         _ptr(out_num_accepted), _stream_handle(dev))
+    _check(st, "spec_verify_chain_noalloc")
     return out_tokens, out_num_accepted
 
 

@@ -107,6 +107,7 @@ extern "C" const char* sv_status_string(int status) {
     case SV_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case SV_ERR_ALIGN: return "logit pointer not aligned to its element size";
     case SV_ERR_HIP: return "HIP runtime error (launch failed)";
+    case SV_ERR_SCRATCH: return "shape needs more workspace than the static scratch array holds";
     default: return "unknown status";
   }
 }

@@ -42,6 +42,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "sv_device.hpp"
 #include "sv_host.hpp"
@@ -1191,19 +1192,30 @@ extern "C" size_t sv_chain_workspace_bytes(int B, int gamma, int V, int dtype) {
   return chain_layout(B, gamma, V).total;
 }
 
-static int chain_entry(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
-                       const float* uniforms, const float* temperature, const int32_t* gammas, int B, int gamma,
-                       int V, int dtype, int32_t* out_tokens, int32_t* out_num_accepted, float* out_tau,
-                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+// Host-side checks of a chain call that need no device (the workspace is
+// checked by chain_entry).
+static int chain_check(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                       const float* uniforms, const float* temperature, int B, int gamma, int V, int dtype,
+                       const int32_t* out_tokens, const int32_t* out_num_accepted) {
   if (dtype != SV_BF16 && dtype != SV_F32) return SV_ERR_DTYPE;
   if (B < 0 || B > SV_MAX_BATCH || gamma < 0 || gamma > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB)
     return SV_ERR_SHAPE;
   if (B == 0) return SV_OK;
-  if (!target_logits || !temperature || !uniforms || !out_tokens || !out_num_accepted || !workspace)
-    return SV_ERR_NULL;
+  if (!target_logits || !temperature || !uniforms || !out_tokens || !out_num_accepted) return SV_ERR_NULL;
   if (gamma > 0 && !draft_tokens) return SV_ERR_NULL;
   const size_t es = dtype == SV_BF16 ? 2 : 4;
   if (!aligned(target_logits, es) || (draft_logits && !aligned(draft_logits, es))) return SV_ERR_ALIGN;
+  return SV_OK;
+}
+
+static int chain_entry(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                       const float* uniforms, const float* temperature, const int32_t* gammas, int B, int gamma,
+                       int V, int dtype, int32_t* out_tokens, int32_t* out_num_accepted, float* out_tau,
+                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+  const int chk = chain_check(target_logits, draft_logits, draft_tokens, uniforms, temperature, B, gamma, V, dtype,
+                              out_tokens, out_num_accepted);
+  if (chk != SV_OK || B == 0) return chk;
+  if (!workspace) return SV_ERR_NULL;
   const ChainLayout L = chain_layout(B, gamma, V);
   if (workspace_bytes < L.total || !aligned(workspace, 256)) return SV_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
@@ -1251,4 +1263,61 @@ extern "C" int spec_verify_chain_ragged(const void* target_logits, const void* d
   return chain_entry(target_logits, draft_logits, draft_tokens, uniforms, temperature, gammas, B, gamma, V,
                      dtype, out_tokens, out_num_accepted, out_accept_prob, workspace, workspace_bytes,
                      hip_stream);
+}
+
+// ---------------------------------------------------------------------------
+// chain verification without a caller workspace
+// ---------------------------------------------------------------------------
+// The workspace of spec_verify_chain_noalloc: a static device array, one copy
+// per GPU, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, so its device address on each GPU is taken once with
+// hipGetSymbolAddress (with that GPU current) and only that address is used.
+__device__ __align__(256) unsigned char scratch[SV_CHAIN_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// The current device's copy of `scratch`, zero-filled by a fill kernel on
+// `stream` the first time it is handed out (*fresh is then true; every call
+// that completes leaves it zero again).
+static int scratch_on_current_device(hipStream_t stream, void** out, bool* fresh) {
+  *fresh = false;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SV_ERR_HIP;
+    const int st = sv_workspace_clear(p, SV_CHAIN_SCRATCH_BYTES, stream);
+    if (st != SV_OK) return st;
+    g_scratch_ptr[dev] = p;
+    *fresh = true;
+  }
+  *out = g_scratch_ptr[dev];
+  return SV_OK;
+}
+
+extern "C" int spec_verify_chain_noalloc(const void* target_logits, const void* draft_logits,
+                                         const int32_t* draft_tokens, const float* uniforms,
+                                         const float* temperature, int B, int gamma, int V, int dtype,
+                                         int32_t* out_tokens, int32_t* out_num_accepted, void* hip_stream) {
+  const int chk = chain_check(target_logits, draft_logits, draft_tokens, uniforms, temperature, B, gamma, V, dtype,
+                              out_tokens, out_num_accepted);
+  if (chk != SV_OK) return chk;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  void* ws = nullptr;
+  bool fresh = false;
+  if (B == 0) {  // the reset: zero-fill this GPU's array
+    const int st = scratch_on_current_device(stream, &ws, &fresh);
+    if (st != SV_OK) return st;
+    return fresh ? SV_OK : sv_workspace_clear(ws, SV_CHAIN_SCRATCH_BYTES, stream);
+  }
+  if (chain_layout(B, gamma, V).total > SV_CHAIN_SCRATCH_BYTES) return SV_ERR_SCRATCH;
+  const int st = scratch_on_current_device(stream, &ws, &fresh);
+  if (st != SV_OK) return st;
+  return chain_entry(target_logits, draft_logits, draft_tokens, uniforms, temperature, nullptr, B, gamma, V, dtype,
+                     out_tokens, out_num_accepted, nullptr, ws, SV_CHAIN_SCRATCH_BYTES, hip_stream);
 }

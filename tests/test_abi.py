@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         assert lib.sv_status_string(code)
     assert lib.sv_status_string(99) == b"unknown status"
     assert lib.sv_version().count(b".") == 2
