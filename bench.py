@@ -530,6 +530,9 @@ def main():
     else:
         result = run_chain(args, torch, synth, sv)
     print(json.dumps(result), flush=True)
+    # leave no device memory for torch's allocator to free during exit()
+    del result
+    sv.binding.release_workspaces()
 
 
 if __name__ == "__main__":

@@ -8,6 +8,7 @@ loudly: there is no CPU fallback.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 import threading
@@ -120,6 +121,25 @@ def _need_cuda(t: torch.Tensor, name: str):
 # workspaces: zero-filled at allocation, cached per (device, stream)
 # ---------------------------------------------------------------------------
 _WORKSPACES = {}
+
+
+def release_workspaces() -> None:
+    """Drops the cached workspaces and returns torch's cached device memory.
+
+    Registered with atexit: it runs while the interpreter is still whole, so
+    no device memory is left for torch's caching allocator to free from a
+    static destructor during exit(), after tools attached to the HIP runtime
+    (a profiler) may already have shut down."""
+    _WORKSPACES.clear()
+    try:
+        if torch.cuda.is_initialized():
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+    except RuntimeError:
+        pass
+
+
+atexit.register(release_workspaces)
 
 
 def workspace(nbytes: int, device: torch.device) -> torch.Tensor:

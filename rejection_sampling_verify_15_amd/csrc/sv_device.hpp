@@ -29,9 +29,13 @@ __host__ __device__ inline int num_chunks(int V) { return (V + kChunk - 1) / kCh
 // workgroup (the draw re-reads a row or two at most), so the lines need not
 // stay in the caches.  Measured on the chain kernels: batched 36.8 -> 36.0 us,
 // deep 288 -> 274 us.
+// The pointer is taken as a global-memory one (address space 1), so the load
+// is a global load rather than a flat one even where the compiler cannot
+// trace the pointer back to a kernel argument.
+typedef unsigned int U32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) U32x4* GlobalU32x4Ptr;
 __device__ inline uint4 load_row16(const void* p) {
-  typedef unsigned int U32x4 __attribute__((ext_vector_type(4)));
-  const U32x4 v = __builtin_nontemporal_load(static_cast<const U32x4*>(p));
+  const U32x4 v = __builtin_nontemporal_load((GlobalU32x4Ptr)(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
