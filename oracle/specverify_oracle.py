@@ -445,16 +445,29 @@ def tree_node_depths(parents: np.ndarray) -> Optional[np.ndarray]:
     return depth
 
 
+def _node_softmax(cache, key, logits_row, dtype, T):
+    """softmax_t of a node's row, memoised in `cache` (a dict, or None) under
+    `key`: the same logits give the same distribution, so a caller verifying
+    one batch of trees under many uniform sets computes each row once."""
+    if cache is not None and key in cache:
+        return cache[key]
+    p = softmax_t(logits_to_f64(logits_row, dtype), T)
+    if cache is not None:
+        cache[key] = p
+    return p
+
+
 def verify_tree(logits: np.ndarray, node_tokens: np.ndarray, parents: np.ndarray,
                 uniforms: np.ndarray, temperature: np.ndarray, dtype: str,
-                max_depth: int, requests=None) -> TreeResult:
+                max_depth: int, requests=None, dist_cache=None) -> TreeResult:
     """Tree verification of a batch (lecture 17 notes section 4.4 VerifyGreedy
     for T == 0, section 4.5 naive sampling for T > 0).
 
     Starting at the root: choose c = argmax p_n (greedy) or draw c from p_n
     with u[b, n] (naive sampling); if a child of n carries c, accept that
     child and continue from it, otherwise emit c and stop.  At a leaf the
-    chosen token is the extra token."""
+    chosen token is the extra token.  `dist_cache` (optional dict) keeps the
+    node distributions across calls on the same logits and temperatures."""
     B, N, V = logits.shape
     L1 = max_depth + 1
     out = np.full((B, L1), -1, dtype=np.int32)
@@ -482,12 +495,12 @@ def verify_tree(logits: np.ndarray, node_tokens: np.ndarray, parents: np.ndarray
         path: List[int] = []
         dec: List[Decision] = []
         while True:
-            row = logits_to_f64(logits[b, node], dtype)
             if T == 0.0:
-                c = int(np.argmax(row))
+                c = int(np.argmax(logits_to_f64(logits[b, node], dtype)))
                 dec.append(Decision("greedy", node, float("nan"), float("nan"), c, float("inf")))
             else:
-                c, margin = inverse_cdf_draw(softmax_t(row, T), float(u[node]))
+                p = _node_softmax(dist_cache, (b, node, "p", T), logits[b, node], dtype, T)
+                c, margin = inverse_cdf_draw(p, float(u[node]))
                 dec.append(Decision("draw", node, float(u[node]), float("nan"), c, margin))
             nxt = -1
             for j in range(node + 1, N):           # children in index order (R9)
@@ -598,7 +611,7 @@ MSS_MAX_CHILDREN = 64
 def verify_tree_mss(logits: np.ndarray, draft_logits: np.ndarray, node_tokens: np.ndarray,
                     parents: np.ndarray, accept_uniforms: np.ndarray, draw_uniforms: np.ndarray,
                     temperature: np.ndarray, dtype: str, max_depth: int,
-                    requests=None) -> TreeResult:
+                    requests=None, dist_cache=None) -> TreeResult:
     """Tree verification by multi-step speculative sampling (lecture 17 notes
     section 4.5, VerifyStochastic with the children sampled without
     replacement; section 4.4 VerifyGreedy for T == 0).
@@ -608,7 +621,9 @@ def verify_tree_mss(logits: np.ndarray, draft_logits: np.ndarray, node_tokens: n
     in index order as in mss_node, child j with accept_uniforms[b, j].  An
     accepted child becomes the next node; if every child is rejected, or n
     has none, the token drawn with draw_uniforms[b, n] is emitted and the
-    descent stops.  Greedy requests descend by argmax as in verify_tree."""
+    descent stops.  Greedy requests descend by argmax as in verify_tree.
+    `dist_cache` (optional dict) keeps the node distributions across calls on
+    the same logits and temperatures."""
     B, N, V = logits.shape
     L1 = max_depth + 1
     out = np.full((B, L1), -1, dtype=np.int32)
@@ -637,9 +652,8 @@ def verify_tree_mss(logits: np.ndarray, draft_logits: np.ndarray, node_tokens: n
         path: List[int] = []
         dec: List[Decision] = []
         while True:
-            row = logits_to_f64(logits[b, node], dtype)
             if T == 0.0:
-                c = int(np.argmax(row))
+                c = int(np.argmax(logits_to_f64(logits[b, node], dtype)))
                 dec.append(Decision("greedy", node, float("nan"), float("nan"), c, float("inf")))
                 nxt = -1
                 for j in range(node + 1, N):
@@ -647,11 +661,11 @@ def verify_tree_mss(logits: np.ndarray, draft_logits: np.ndarray, node_tokens: n
                         nxt = j
                         break
             else:
-                p = softmax_t(row, T)
+                p = _node_softmax(dist_cache, (b, node, "p", T), logits[b, node], dtype, T)
                 ids, toks = tree_children(par, tok, node)
                 props = []
                 if ids:
-                    q = softmax_t(logits_to_f64(draft_logits[b, node], dtype), T)
+                    q = _node_softmax(dist_cache, (b, node, "q", T), draft_logits[b, node], dtype, T)
                     props = mss_proposals(q, toks)
                 ids = ids[:len(props)]
                 j, c, d = mss_node(p, props, [ua[i] for i in ids], float(ud[node]))

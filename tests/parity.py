@@ -36,9 +36,18 @@ class Tally:
     in_window: int = 0
     mismatches: int = 0          # inside the window
     hard: list = dataclasses.field(default_factory=list)
+    greedy: int = 0              # of `decisions`, the argmax ones (exact by construction)
+
+    def count(self, d):
+        self.decisions += 1
+        if d.kind == "greedy":
+            self.greedy += 1
+        if d.margin < WINDOW:
+            self.in_window += 1
 
     def add(self, other: "Tally"):
         self.decisions += other.decisions
+        self.greedy += other.greedy
         self.in_window += other.in_window
         self.mismatches += other.mismatches
         self.hard.extend(other.hard)
@@ -51,8 +60,8 @@ class Tally:
                 f"{label}: boundary mismatches {self.mismatches}/{self.decisions} = {rate:.2e}")
 
     def __str__(self):
-        return (f"decisions={self.decisions} in_window={self.in_window} "
-                f"boundary_mismatches={self.mismatches} hard={len(self.hard)}")
+        return (f"decisions={self.decisions} (sampled={self.decisions - self.greedy}) "
+                f"in_window={self.in_window} boundary_mismatches={self.mismatches} hard={len(self.hard)}")
 
 
 def compare_chain_request(b, gamma, dec, emitted_or, n_or, tok_gpu, n_gpu) -> Tally:
@@ -63,9 +72,7 @@ def compare_chain_request(b, gamma, dec, emitted_or, n_or, tok_gpu, n_gpu) -> Ta
             t.hard.append((b, "invalid request not flagged", n_gpu))
         return t
     for d in dec:
-        t.decisions += 1
-        if d.margin < WINDOW:
-            t.in_window += 1
+        t.count(d)
         if d.kind == "accept":
             gpu_acc = int(n_gpu > d.position)
             same = gpu_acc == d.outcome
@@ -115,9 +122,7 @@ def compare_tree(res, tok_gpu, path_gpu, n_gpu, requests=None) -> Tally:
             tally.add(t)
             continue
         for step, d in enumerate(res.decisions[b]):
-            t.decisions += 1
-            if d.margin < WINDOW:
-                t.in_window += 1
+            t.count(d)
             # the GPU took the same decision at this step iff its output token
             # at slot `step` equals the oracle's choice
             if int(tok_gpu[b, step]) != d.outcome:
@@ -166,9 +171,9 @@ def compare_tree_mss(res, tok_gpu, path_gpu, n_gpu, requests=None) -> Tally:
             tally.add(t)
             continue
         for d, decs in enumerate(mss_levels(res.decisions[b])):
-            t.decisions += len(decs)
+            for x in decs:
+                t.count(x)
             near = [x for x in decs if x.margin < WINDOW]
-            t.in_window += len(near)
             if int(tok_gpu[b, d]) != int(res.out_tokens[b, d]) or int(path_gpu[b, d]) != int(res.out_path[b, d]):
                 if near:
                     t.mismatches += 1
