@@ -35,6 +35,13 @@
  *    a tree deeper than max_depth, draft_logits == NULL for a sampling
  *    request) marks that request invalid: its accepted count is -1 and all
  *    its output tokens are -1.  Other requests are unaffected.
+ *  - Every wait of one workgroup for another is bounded.  A wait that gives
+ *    up (which only a dispatch order the hardware does not use, or
+ *    SV_HOOK_SPIN_LIMIT, can cause) makes that request's accepted count
+ *    SV_GAVE_UP (-2); its output tokens are then unspecified, and the
+ *    workspace may hold stale words: zero it (sv_workspace_clear, or for
+ *    spec_verify_chain_noalloc a call with B == 0) before the next call that
+ *    uses it.  Other requests keep exact results.
  *  - Logits must be finite or -inf (masked); each row needs at least one
  *    finite entry.  NaN / +inf logits give unspecified tokens.
  *  - Inverse-CDF draws: with weights w_k in vocabulary order, C_k their
@@ -83,6 +90,9 @@ typedef enum {
   SV_F32 = 1              /* logits are IEEE float32 */
 } sv_dtype;
 
+/* Accepted count of a request whose bounded wait gave up. */
+#define SV_GAVE_UP (-2)
+
 /* Limits checked on the host (SV_ERR_SHAPE otherwise). */
 #define SV_MAX_GAMMA 32
 #define SV_MAX_BATCH 16384   /* requests per chain call */
@@ -122,7 +132,8 @@ SV_API int sv_workspace_clear(void* workspace, size_t bytes, void* hip_stream);
  *                                           rest is -1
  * out_num_accepted [B]              int32   n in [0, gamma] (n + 1 tokens are
  *                                           emitted; the caller rolls back
- *                                           gamma - n cached positions), or -1
+ *                                           gamma - n cached positions), -1
+ *                                           (invalid request) or SV_GAVE_UP
  * Limits: 0 <= B <= SV_MAX_BATCH (B == 0 is a no-op), 0 <= gamma <= SV_MAX_GAMMA,
  *         1 <= V <= SV_MAX_VOCAB.
  * Returns an sv_status.
@@ -267,7 +278,7 @@ SV_API int spec_verify_chain_ragged(const void* target_logits, const void* draft
  *                                        token; -1 padded
  * out_path_nodes [B][max_depth+1] int32  accepted node ids (their positions in
  *                                        the linearised KV cache); -1 padded
- * out_num_accepted [B]            int32  number of accepted nodes, or -1
+ * out_num_accepted [B]            int32  number of accepted nodes, -1 (invalid) or SV_GAVE_UP
  * Limits: B >= 0, 1 <= N <= SV_MAX_TREE_NODES, 1 <= V <= SV_MAX_VOCAB,
  *         0 <= max_depth <= SV_MAX_TREE_DEPTH.
  * ---------------------------------------------------------------------- */
@@ -425,6 +436,24 @@ SV_API const char* sv_kernel_name(int kernel);
 SV_API int sv_timing_begin(int capacity);
 
 SV_API int sv_timing_end(double* total_ms, int* launches, int n);
+
+/* ------------------------------------------------------------------------
+ * Test controls.  For tests only: they force paths that ordinary inputs of a
+ * test's size never take -- the multi-launch forms that very large shapes
+ * use, and give-ups of the bounded waits (SV_GAVE_UP) with every kernel still
+ * running to its end.  A control is process-wide and read by every later
+ * call on any thread; value 0 restores the default.  Production code never
+ * sets one.  Returns SV_ERR_SHAPE for an unknown control or a negative value.
+ * ---------------------------------------------------------------------- */
+typedef enum {
+  SV_HOOK_CHAIN_GRID_CAP = 0, /* > 0: chain calls use the three-launch form, grids capped at this many workgroups */
+  SV_HOOK_CHAIN_SPLIT = 1,    /* != 0: chain calls use the three-launch form */
+  SV_HOOK_TREE_SPLIT = 2,     /* != 0: spec_verify_tree uses its launch-per-step form */
+  SV_HOOK_SPIN_LIMIT = 3,     /* > 0: each bounded wait of the chain and tree kernels gives up after this many polls */
+  SV_HOOK_COUNT = 4
+} sv_hook;
+
+SV_API int sv_set_test_hook(int hook, long long value);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,7 @@ loudly: there is no CPU fallback.
 from __future__ import annotations
 
 import atexit
+import contextlib
 import ctypes
 import os
 import threading
@@ -19,6 +20,8 @@ import torch
 
 SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_ALIGN, SV_ERR_HIP, SV_ERR_SCRATCH = range(8)
 SV_BF16, SV_F32 = 0, 1
+SV_GAVE_UP = -2   # accepted count of a request whose bounded wait gave up
+SV_HOOK_CHAIN_GRID_CAP, SV_HOOK_CHAIN_SPLIT, SV_HOOK_TREE_SPLIT, SV_HOOK_SPIN_LIMIT = range(4)
 SV_MAX_GAMMA = 32
 SV_MAX_TOPK = 128
 
@@ -52,6 +55,7 @@ EXPORTS = {
     "sv_timing_begin": (ctypes.c_int, [ctypes.c_int]),
     "sv_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
                                      ctypes.c_int]),
+    "sv_set_test_hook": (ctypes.c_int, [ctypes.c_int, ctypes.c_longlong]),
 }
 SV_K_COUNT = 16
 
@@ -140,6 +144,35 @@ def release_workspaces() -> None:
 
 
 atexit.register(release_workspaces)
+
+
+@contextlib.contextmanager
+def library_control(hook: int, value: int):
+    """Sets one of the library's test controls (SV_HOOK_*) for the duration of
+    a with-block, then restores its default.  For tests only."""
+    _check(lib().sv_set_test_hook(int(hook), int(value)), "sv_set_test_hook")
+    try:
+        yield
+    finally:
+        lib().sv_set_test_hook(int(hook), 0)
+
+
+def recover(out_num_accepted: torch.Tensor, ws: Optional[torch.Tensor] = None) -> bool:
+    """Call once the stream is synchronised.  True if a request of the call
+    reports SV_GAVE_UP: the workspace that call used (`ws`, or the cached
+    workspace of the current stream when the call took the cached one) may
+    then hold stale words, and it is zero-filled here, on its device's
+    current stream, before anything uses it again."""
+    if not bool((out_num_accepted == SV_GAVE_UP).any()):
+        return False
+    if ws is None:
+        dev = out_num_accepted.device
+        ws = _WORKSPACES.get((dev.index, torch.cuda.current_stream(dev).cuda_stream))
+        if ws is None:
+            return True
+    stream = _stream_handle(ws.device) if ws.is_cuda else None
+    _check(lib().sv_workspace_clear(_ptr(ws), ws.numel(), stream), "sv_workspace_clear")
+    return True
 
 
 def workspace(nbytes: int, device: torch.device) -> torch.Tensor:

@@ -114,6 +114,20 @@ extern "C" const char* sv_status_string(int status) {
 
 extern "C" const char* sv_version(void) { return "0.1.0"; }
 
+namespace {
+std::atomic<long long> g_test_hooks[SV_HOOK_COUNT];
+}  // namespace
+
+long long sv::test_hook(int hook) {
+  return (hook >= 0 && hook < SV_HOOK_COUNT) ? g_test_hooks[hook].load(std::memory_order_relaxed) : 0;
+}
+
+extern "C" int sv_set_test_hook(int hook, long long value) {
+  if (hook < 0 || hook >= SV_HOOK_COUNT || value < 0) return SV_ERR_SHAPE;
+  g_test_hooks[hook].store(value, std::memory_order_relaxed);
+  return SV_OK;
+}
+
 extern "C" int sv_workspace_clear(void* workspace, size_t bytes, void* hip_stream) {
   if (bytes == 0) return SV_OK;
   if (!workspace) return SV_ERR_NULL;

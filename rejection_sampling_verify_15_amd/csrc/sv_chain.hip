@@ -123,6 +123,7 @@ struct ChainArgs {
   uint32_t* counters;    // [B][kCounterStride]
   const int32_t* gammas; // [B] draft length of each request (ragged calls), or NULL: all gamma
   float* out_tau;        // [B][gamma] tau of each test taken, -1 elsewhere; or NULL
+  uint32_t spin;         // poll bound of every wait (kSpinLimit unless a test lowers it)
 };
 
 // T must be 0 (greedy) or a finite positive normal float.
@@ -181,7 +182,8 @@ __device__ inline bool row_in_round(const ChainArgs& a, int g, int k) {
 
 // Upper bound on the polls of a waiting workgroup (seconds at the least);
 // every wait is for workgroups dispatched before the waiting one, so the bound
-// only guards against a broken dispatch order.
+// only guards against a broken dispatch order.  A wait that gives up makes
+// its request report SV_GAVE_UP.
 constexpr uint32_t kSpinLimit = 1u << 22;
 
 // Lane t < kWireWords stores word t of the record.
@@ -206,7 +208,7 @@ __device__ Pending wait_pending(const ChainArgs& a, int b) {
   const PendingWire* wire = a.pending + b;
   uint64_t w = 0;
   bool whole = false;
-  for (uint32_t spin = 0; spin < kSpinLimit; ++spin) {
+  for (uint32_t spin = 0; spin < a.spin; ++spin) {
     if (lane < kWireWords) w = load_coherent(&wire->w[lane]);
     const uint64_t got = __ballot(lane < kWireWords && (w >> 32) != 0);
     if (got == (1ull << kWireWords) - 1ull) {
@@ -407,9 +409,9 @@ constexpr int kMaxSlots = 2 * kWave;  // nrows * gpr <= max(kWave, kMaxRows)
 static_assert(kMaxRows <= kMaxSlots, "slots cover the rows");
 
 // Polls words [c0, min(c0 + kPoll, ce)) of p until all are marked (reads
-// beyond ce repeat word ce - 1); false if the wait gave up.
-__device__ inline bool poll_words(const uint64_t* p, int c0, int ce, uint64_t (&w)[kPoll]) {
-  for (uint32_t spin = 0; spin < kSpinLimit; ++spin) {
+// beyond ce repeat word ce - 1); false if the wait gave up after `limit` polls.
+__device__ inline bool poll_words(const uint64_t* p, int c0, int ce, uint64_t (&w)[kPoll], uint32_t limit) {
+  for (uint32_t spin = 0; spin < limit; ++spin) {
     bool all = true;
 #pragma unroll
     for (int i = 0; i < kPoll; ++i) {
@@ -423,10 +425,13 @@ __device__ inline bool poll_words(const uint64_t* p, int c0, int ce, uint64_t (&
 }
 
 template <int DT, bool VEC, int SPAN>
-__device__ void draw_token(const ChainArgs& a, int b, const Pending& d, bool zero_wire);
+__device__ bool draw_token(const ChainArgs& a, int b, const Pending& d, bool zero_wire);
 
 // With kDraws (the single launch), the decide item of a drawing request then
-// waits for its units' records (of SPAN logits each) and draws the token itself.
+// waits for its units' records (of SPAN logits each) and draws the token
+// itself.  The count of a drawing request is written by whoever draws (this
+// item, or with counted units the last unit), once the draw has its records:
+// so SV_GAVE_UP from any wait of the request reaches it through one writer.
 template <int DT, bool VEC, int SPAN, bool kDraws>
 __device__ void decide_request(const ChainArgs& a, int b) {
   __shared__ float s_gm[kMaxSlots];
@@ -455,6 +460,7 @@ __device__ void decide_request(const ChainArgs& a, int b) {
   const int gs = (a.nchunk + gpr - 1) / gpr;              // chunks per group
   const int nslots = nrows * gpr;
   int bad = Gb < 0;
+  int lost = 0;  // a wait of this item gave up
   int32_t x = -1;
   float u = 0.0f;
   if (lane < Gb) {
@@ -486,7 +492,10 @@ __device__ void decide_request(const ChainArgs& a, int b) {
     ArgMax best{-INFINITY, 0x7fffffff};
     for (int c0 = cb; c0 < ce; c0 += kPoll) {
       uint64_t w[kPoll];
-      if (!poll_words(p, c0, ce, w)) bad = 1;
+      if (!poll_words(p, c0, ce, w, a.spin)) {
+        bad = 1;
+        lost = 1;
+      }
       if (!sampling) {
 #pragma unroll
         for (int i = 0; i < kPoll; ++i)
@@ -539,6 +548,7 @@ __device__ void decide_request(const ChainArgs& a, int b) {
   }
   __syncthreads();
   const bool any_bad = __any(bad);
+  const bool any_lost = __any(lost);
   int n = -1;
   double tau = -1.0;
   if (!any_bad) {
@@ -564,9 +574,11 @@ __device__ void decide_request(const ChainArgs& a, int b) {
   // a request with draw units hears the outcome in every case: the draw, or
   // that there is none
   Pending d{};
-  if (request_class(a, T) == 0) {
+  const bool drawing = request_class(a, T) == 0;
+  if (drawing) {
     if (any_bad) {
       d.valid = kPendingNone;
+      d.n = any_lost ? SV_GAVE_UP : -1;  // the count the drawer writes
     } else {
       d.valid = kPendingDraw;
       d.n = n;  // the row of the draw: the rejected position, or Gb for the bonus
@@ -596,18 +608,19 @@ __device__ void decide_request(const ChainArgs& a, int b) {
     }
     if (write) a.out_tokens[static_cast<size_t>(b) * (G + 1) + lane] = v;
   }
-  if (lane == 0) a.out_n[b] = n;
+  if (lane == 0 && !drawing) a.out_n[b] = any_lost ? SV_GAVE_UP : n;
   // the workspace words of this request back to zero
   uint64_t* pz = a.partials + static_cast<size_t>(b) * R * a.nchunk;
   for (int i = lane; i < nrows * a.nchunk; i += kWave) {
     const int r = i / a.nchunk;
     store_coherent(pz + static_cast<size_t>(phys_row(a, Gb, r)) * a.nchunk + (i - r * a.nchunk), 0ull);
   }
-  if (kDraws && request_class(a, T) == 0) {
+  if (kDraws && drawing) {
     // the draw runs beside other requests' units: let this wave issue first
     __builtin_amdgcn_s_setprio(3);
-    draw_token<DT, VEC, SPAN>(a, b, d, true);
+    const bool whole = draw_token<DT, VEC, SPAN>(a, b, d, true);
     __builtin_amdgcn_s_setprio(0);
+    if (lane == 0) a.out_n[b] = whole ? d.n : SV_GAVE_UP;
   }
 }
 
@@ -658,7 +671,7 @@ __device__ bool wait_records(const ChainArgs& a, int b, bool cached, double (&f)
 #pragma unroll
     for (int k = 0; k < kUnitFields; ++k) f[q][k] = (q * kWave + lane < a.nunit) ? 0.0 : -0.0;
   bool whole = false;
-  for (uint32_t spin = 0; spin < kSpinLimit; ++spin) {
+  for (uint32_t spin = 0; spin < a.spin; ++spin) {
     bool all = true;
     if (cached) {
 #pragma unroll
@@ -688,9 +701,12 @@ __device__ bool wait_records(const ChainArgs& a, int b, bool cached, double (&f)
 
 // Also returns the request's records (and, with `zero_wire`, its decision
 // wire, which every unit has read once its record is in) to zero; a request
-// without a draw only has that done.
+// without a draw only has that done.  False if the wait for the records gave
+// up or a unit gave up waiting for the decision (its record then holds +inf
+// sums, which no real record can: every exponential is at most 1); the
+// token slot is then left alone.
 template <int DT, bool VEC, int SPAN>
-__device__ void draw_token(const ChainArgs& a, int b, const Pending& d, bool zero_wire) {
+__device__ bool draw_token(const ChainArgs& a, int b, const Pending& d, bool zero_wire) {
   using U = Unit<DT, VEC, SPAN>;
   using Raw = typename U::Raw;
   const int G = a.gamma;
@@ -701,14 +717,11 @@ __device__ void draw_token(const ChainArgs& a, int b, const Pending& d, bool zer
   const int nw = a.nunit * static_cast<int>(sizeof(UnitRec) / 8);
   // 1) the totals: fp64 normalisers of the draw's rows, and the residual mass
   double f[kDrawCache][kUnitFields];
-  if (!wait_records(a, b, cached, f)) {
-    if (lane == 0) a.out_n[b] = -1;  // gave up waiting for the units
-    return;
-  }
+  if (!wait_records(a, b, cached, f)) return false;
   if (zero_wire && lane < kWireWords) store_coherent(&a.pending[b].w[lane], 0ull);
   if (d.valid != kPendingDraw) {
     for (int i = lane; i < nw; i += kWave) store_coherent(wz + i, 0ull);
-    return;
+    return true;
   }
   double tot[kUnitFields] = {0.0, 0.0, 0.0, 0.0};
   if (cached) {
@@ -726,6 +739,11 @@ __device__ void draw_token(const ChainArgs& a, int b, const Pending& d, bool zer
   }
 #pragma unroll
   for (int k = 0; k < kUnitFields; ++k) tot[k] = wave_sum(tot[k]);
+  if (tot[kUnitAllT] == INFINITY) {  // a unit gave up
+    if (!cached)
+      for (int i = lane; i < nw; i += kWave) store_coherent(wz + i, 0ull);
+    return false;
+  }
   // p = e_t / zt and q = e_d / zd are formed with the reciprocals throughout
   const double rzt = 1.0 / tot[kUnitAllT], rzd = 1.0 / tot[kUnitAllD];
   // an empty residual (p and q equal up to rounding) draws from p of that
@@ -835,6 +853,7 @@ __device__ void draw_token(const ChainArgs& a, int b, const Pending& d, bool zer
   if (lane == 0) a.out_tokens[static_cast<size_t>(b) * (G + 1) + d.n] = (hit != 0x7fffffff) ? hit : last_pos;
   if (!cached)
     for (int i = lane; i < nw; i += kWave) store_coherent(wz + i, 0ull);
+  return true;
 }
 
 // The drawing requests (class 0) of a batch of at most kRankMaxBatch: lane l
@@ -882,8 +901,8 @@ __device__ inline int nth_drawing(const DrawingSet& s, int p) {
 
 // Unit `unit` of request b (a class-0 request): waits for the decision, then
 // hands back its share of the final draw as a marked record (zeros when there
-// is no draw).  With kCounted it also counts itself in, and the last unit of
-// the request draws.
+// is no draw, +inf when the wait gave up).  With kCounted it also counts
+// itself in, and the last unit of the request draws and writes the count.
 template <int DT, bool VEC, int SPAN, bool kCounted>
 __device__ void unit_work(const ChainArgs& a, int b, int unit) {
   using U = Unit<DT, VEC, SPAN>;
@@ -891,7 +910,6 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit) {
   const int G = a.gamma;
   const int lane = threadIdx.x;
   const Pending d = wait_pending(a, b);
-  if (d.valid == 0 && lane == 0) a.out_n[b] = -1;  // gave up waiting
   const bool draw = d.valid == kPendingDraw;
   UnitRec* rec = a.units + static_cast<size_t>(b) * a.nunit + unit;
   double pos_t = 0.0, pos_d = 0.0, all_t = 0.0, all_d = 0.0;
@@ -942,7 +960,8 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit) {
   }
   // lane f hands over field f, negated (the mark)
   if (lane < kUnitFields) {
-    const double v = lane == kUnitAllT ? all_t : lane == kUnitAllD ? all_d : lane == kUnitPosT ? pos_t : pos_d;
+    const double v = d.valid == 0 ? INFINITY
+                     : lane == kUnitAllT ? all_t : lane == kUnitAllD ? all_d : lane == kUnitPosT ? pos_t : pos_d;
     store_coherent_f64(&rec->f[lane], -v);
   }
   if constexpr (!kCounted) return;
@@ -957,8 +976,9 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit) {
     // the last unit of a request draws while other units may still compute:
     // let its wave issue first on its SIMD
     __builtin_amdgcn_s_setprio(3);
-    draw_token<DT, VEC, SPAN>(a, b, d, false);
+    const bool whole = draw_token<DT, VEC, SPAN>(a, b, d, false);
     __builtin_amdgcn_s_setprio(0);
+    if (lane == 0) a.out_n[b] = (d.valid != 0 && whole) ? d.n : SV_GAVE_UP;
   }
 }
 
@@ -1142,25 +1162,17 @@ static long long stream_capacity() {
   return cached[dev];
 }
 
-// Test hooks: a positive value in SV_CHAIN_TEST_GRID_CAP caps every grid at
-// that many workgroups and selects the three-launch form; SV_CHAIN_SPLIT
-// selects the three-launch form alone.
-static long long test_grid_cap() {
-  const char* v = getenv("SV_CHAIN_TEST_GRID_CAP");
-  return v ? atoll(v) : 0;
-}
-
 template <int DT, bool VEC>
 static int launch_chain(ChainArgs a, hipStream_t stream) {
   a.nstream = static_cast<long long>(a.B) * (2 * a.gamma + 1) * a.nchunk;
   a.per_req = (2 * a.gamma + 1) * a.nchunk;
-  const long long cap = test_grid_cap();
+  const long long cap = test_hook(SV_HOOK_CHAIN_GRID_CAP);
   // the single launch, with 512- or 1024-logit draw units
   const bool small = static_cast<long long>(a.B) * units_for(a.V, kUnitSpanSmall) <= kSmallSpanUnits;
   a.nunit = units_for(a.V, small ? kUnitSpanSmall : kUnitSpanLarge);
   const long long pool = std::min(static_cast<long long>(a.B) * a.nunit, kUnitPool);
   const long long fused = a.nstream + a.B + pool;
-  if (cap <= 0 && getenv("SV_CHAIN_SPLIT") == nullptr && fused <= kMaxGrid) {
+  if (cap <= 0 && test_hook(SV_HOOK_CHAIN_SPLIT) == 0 && fused <= kMaxGrid) {
     const dim3 grid(static_cast<unsigned>(fused));
     if (small) launch(SV_K_CHAIN_VERIFY, chain_verify<DT, VEC, kUnitSpanSmall>, grid, dim3(kWave), 0, stream, a);
     else launch(SV_K_CHAIN_VERIFY, chain_verify<DT, VEC, kUnitSpanLarge>, grid, dim3(kWave), 0, stream, a);
@@ -1237,6 +1249,7 @@ static int chain_entry(const void* target_logits, const void* draft_logits, cons
   a.counters = reinterpret_cast<uint32_t*>(ws + L.counters);
   a.gammas = gammas;
   a.out_tau = gamma > 0 ? out_tau : nullptr;
+  a.spin = spin_limit(kSpinLimit);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const int kv = dtype == SV_BF16 ? Elem<0>::kVec : Elem<1>::kVec;
   const bool vec = (V % kv == 0) && aligned(target_logits, 16) && (!a.draft || aligned(a.draft, 16));

@@ -17,6 +17,15 @@ inline bool aligned(const void* p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }
 
+// Value of a test control (sv_set_test_hook); 0 when unset.
+long long test_hook(int hook);
+
+// Poll bound of the bounded waits: `dflt`, or the SV_HOOK_SPIN_LIMIT control.
+inline uint32_t spin_limit(uint32_t dflt) {
+  const long long v = test_hook(SV_HOOK_SPIN_LIMIT);
+  return v > 0 ? static_cast<uint32_t>(v < 0xffffffffLL ? v : 0xffffffffLL) : dflt;
+}
+
 // Hands out the event pair of the next timed launch while a timing session is
 // open (sv_timing_begin); leaves both NULL otherwise.
 void timing_slot(int kernel, hipEvent_t* start, hipEvent_t* stop);

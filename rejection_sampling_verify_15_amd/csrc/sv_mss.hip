@@ -70,6 +70,7 @@ struct MssArgs {
   uint64_t* ctl;    // [B][kCtlStride]
   uint64_t* slots;  // [B][nchunk][kSlotWords]
   uint64_t* lanes;  // [B][nchunk][2][kWave]: lane sums of P (stats), of the residual
+  uint32_t spin;    // poll bound of every wait (kTreeSpinLimit unless a test lowers it)
 };
 
 __device__ inline uint64_t* mss_ctl(const MssArgs& a, int b) { return a.ctl + static_cast<size_t>(b) * kCtlStride; }
@@ -124,7 +125,7 @@ __device__ inline double trunc7(double v) { return sum_value(tag_sum(v, 0)); }
 __device__ bool mss_wait_scalars(const MssArgs& a, int b, uint32_t s, MssScalars& sc) {
   const uint64_t* cw = mss_ctl(a, b);
   const int tag = pass_tag(s);
-  for (uint32_t spin = 0; spin < kTreeSpinLimit; ++spin) {
+  for (uint32_t spin = 0; spin < a.spin; ++spin) {
     const uint64_t wmt = load_coherent(cw + kPrmMt);
     const uint64_t wmd = load_coherent(cw + kPrmMd);
     const uint64_t wzt = load_coherent(cw + kPrmZt);
@@ -148,7 +149,7 @@ __device__ bool mss_wait_scalars(const MssArgs& a, int b, uint32_t s, MssScalars
 // stopped (or the wait gave up).
 __device__ uint64_t mss_wait_pass(const MssArgs& a, int b, uint32_t s) {
   const uint64_t* cw = mss_ctl(a, b);
-  for (uint32_t spin = 0; spin < kTreeSpinLimit; ++spin) {
+  for (uint32_t spin = 0; spin < a.spin; ++spin) {
     const uint64_t pv = load_coherent(cw + kMssPass);
     if ((pv & kTreeMark) && ((pv >> 34) & 0x1fffffffull) == s) return pv;
     if (load_coherent(cw + kMssStop) & kTreeMark) return 0;
@@ -305,7 +306,7 @@ __device__ inline bool mss_poll_slots(const MssArgs& a, int b, int which, uint32
       all = all && (c >= a.nchunk || (sum ? sum_at_level(w[q], tag) : chunk_at_level(w[q], tag)));
     }
     if (__all(all)) return true;
-    if (spin >= kTreeSpinLimit) return false;
+    if (spin >= a.spin) return false;
     __builtin_amdgcn_s_sleep(2);
   }
 }
@@ -317,7 +318,7 @@ __device__ inline bool mss_poll_lanes(const MssArgs& a, int b, int c, int which,
   for (uint32_t spin = 0;; ++spin) {
     w = load_coherent(lp + threadIdx.x);
     if (__all(sum_at_level(w, tag))) return true;
-    if (spin >= kTreeSpinLimit) return false;
+    if (spin >= a.spin) return false;
     __builtin_amdgcn_s_sleep(2);
   }
 }
@@ -524,7 +525,7 @@ __device__ inline void mss_stop(const MssArgs& a, int b, int d, int token, bool 
     }
   }
   if (threadIdx.x == 0) {
-    a.out_n[b] = lost ? -1 : d;
+    a.out_n[b] = lost ? SV_GAVE_UP : d;
     store_coherent(mss_ctl(a, b) + kMssStop, kTreeMark);
   }
 }
@@ -835,6 +836,7 @@ extern "C" int spec_verify_tree_mss(const void* target_logits, const void* draft
   a.ctl = reinterpret_cast<uint64_t*>(ws + L.ctl);
   a.slots = reinterpret_cast<uint64_t*>(ws + L.slots);
   a.lanes = reinterpret_cast<uint64_t*>(ws + L.lanes);
+  a.spin = spin_limit(kTreeSpinLimit);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const int kv = dtype == SV_BF16 ? Elem<0>::kVec : Elem<1>::kVec;
   const bool vec = (V % kv == 0) && aligned(target_logits, 16) && aligned(draft_logits, 16);

@@ -320,6 +320,7 @@ struct TreeFused {
   uint64_t* chunks;  // [B][nchunk]: level-tagged chunk max (and argmax)
   double* totals;    // [B][nchunk]: fp64 exp-sum of the chunk relative to its max (sampling)
   double* lanes;     // [B][nchunk][kWave]: the same per lane (sampling)
+  uint32_t spin;     // poll bound of every wait (kTreeSpinLimit unless a test lowers it)
 };
 
 __device__ inline int levels_of(const TreeFused& a) { return a.max_depth + 1; }
@@ -343,7 +344,7 @@ __device__ inline uint64_t node_word(int level, int node) {
 __device__ int tree_wait_node(const TreeFused& a, int b, int d) {
   const uint64_t* cw = tree_ctl(a, b);
   const uint64_t want = node_word(d, 0) >> 32;
-  for (uint32_t spin = 0; spin < kTreeSpinLimit; ++spin) {
+  for (uint32_t spin = 0; spin < a.spin; ++spin) {
     const uint64_t nv = load_coherent(cw + kCtlNode);
     const uint64_t sv = load_coherent(cw + kCtlStop);
     if ((nv >> 32) == want) return static_cast<int>(static_cast<uint32_t>(nv));
@@ -493,7 +494,7 @@ __device__ int tree_choose_level(const TreeFused& a, int b, int d, int node, flo
       all = all && (c >= a.nchunk || chunk_at_level(w[q], d));
     }
     if (__all(all)) break;
-    if (spin >= kTreeSpinLimit) { lost = true; break; }
+    if (spin >= a.spin) { lost = true; break; }
     __builtin_amdgcn_s_sleep(2);
   }
   int token;
@@ -524,7 +525,7 @@ __device__ int tree_choose_level(const TreeFused& a, int b, int d, int node, flo
         all &= (c >= a.nchunk || sum_at_level(tw[q], d));
       }
       if (__all(all)) break;
-      if (spin >= kTreeSpinLimit) { lost = true; break; }
+      if (spin >= a.spin) { lost = true; break; }
       __builtin_amdgcn_s_sleep(2);
     }
     double wc[kTreeChunkCache];
@@ -576,7 +577,7 @@ __device__ int tree_choose_level(const TreeFused& a, int b, int d, int node, flo
     for (uint32_t spin = 0;; ++spin) {
       lw = load_coherent(lp + lane);
       if (__all(sum_at_level(lw, d))) break;
-      if (spin >= kTreeSpinLimit) { lost = true; break; }
+      if (spin >= a.spin) { lost = true; break; }
       __builtin_amdgcn_s_sleep(2);
     }
     const double wl = sum_value(lw) * scale;
@@ -631,7 +632,7 @@ __device__ int tree_choose_level(const TreeFused& a, int b, int d, int node, flo
     op[i] = -1;
   }
   if (lane == 0) {
-    a.out_n[b] = lost ? -1 : d;
+    a.out_n[b] = lost ? SV_GAVE_UP : d;
     store_coherent(tree_ctl(a, b) + kCtlStop, kTreeMark);
   }
   return -1;
@@ -710,7 +711,7 @@ static TreeLayout tree_layout(int B, int V) {
 // grid within kTreeMaxGrid blocks (and no test hook asking otherwise).
 constexpr long long kTreeMaxGrid = 1 << 20;
 static bool tree_fused_fits(int B, int V) {
-  if (getenv("SV_TREE_SPLIT") != nullptr) return false;
+  if (test_hook(SV_HOOK_TREE_SPLIT) != 0) return false;
   const long long nc = tree_fused_chunks(V);
   return nc <= kTreeMaxChunks && static_cast<long long>(B) * (nc + 1) <= kTreeMaxGrid;
 }
@@ -784,6 +785,7 @@ extern "C" int spec_verify_tree(const void* target_logits, const int32_t* node_t
     f.chunks = reinterpret_cast<uint64_t*>(ws + L.f_chunks);
     f.totals = reinterpret_cast<double*>(ws + L.f_totals);
     f.lanes = reinterpret_cast<double*>(ws + L.f_lanes);
+    f.spin = spin_limit(kTreeSpinLimit);
     const dim3 grid(static_cast<unsigned>(static_cast<long long>(B) * (f.nchunk + 1)));
     if (dtype == SV_BF16) {
       if (vec) launch(SV_K_TREE_VERIFY, tree_verify<0, true>, grid, dim3(kWave), 0, stream, f);

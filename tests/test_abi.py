@@ -141,3 +141,48 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "library_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         binding.lib()
+
+
+# ---------------------------------------------------------------------------
+# test controls and the recovery after a give-up (host logic only)
+# ---------------------------------------------------------------------------
+def test_test_hook_validation(lib):
+    assert lib.sv_set_test_hook(binding.SV_HOOK_SPIN_LIMIT + 1, 1) == sv.SV_ERR_SHAPE
+    assert lib.sv_set_test_hook(-1, 1) == sv.SV_ERR_SHAPE
+    assert lib.sv_set_test_hook(binding.SV_HOOK_CHAIN_SPLIT, -1) == sv.SV_ERR_SHAPE
+    for h in range(4):
+        assert lib.sv_set_test_hook(h, 0) == sv.SV_OK
+
+
+class FakeLib:
+    def __init__(self):
+        self.calls = []
+
+    def sv_set_test_hook(self, hook, value):
+        self.calls.append(("hook", hook, value))
+        return sv.SV_OK
+
+    def sv_workspace_clear(self, ptr, nbytes, stream):
+        self.calls.append(("clear", ptr.value, nbytes, stream))
+        return sv.SV_OK
+
+
+def test_library_control_restores_the_default(monkeypatch):
+    fake = FakeLib()
+    monkeypatch.setattr(binding, "lib", lambda: fake)
+    with pytest.raises(KeyError):
+        with sv.library_control(binding.SV_HOOK_SPIN_LIMIT, 7):
+            assert fake.calls == [("hook", binding.SV_HOOK_SPIN_LIMIT, 7)]
+            raise KeyError("the block fails")
+    assert fake.calls[-1] == ("hook", binding.SV_HOOK_SPIN_LIMIT, 0)
+
+
+def test_recover_clears_the_workspace_only_after_a_give_up(monkeypatch):
+    import torch
+    fake = FakeLib()
+    monkeypatch.setattr(binding, "lib", lambda: fake)
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    assert sv.recover(torch.tensor([0, 3, -1, 2], dtype=torch.int32), ws) is False
+    assert fake.calls == []
+    assert sv.recover(torch.tensor([0, sv.SV_GAVE_UP, -1], dtype=torch.int32), ws) is True
+    assert fake.calls == [("clear", ws.data_ptr(), 4096, None)]

@@ -237,12 +237,11 @@ def test_single_launch_returns_workspace_to_zero(batched):
 
 
 @pytest.mark.parametrize("cap", [37, 1000])
-def test_split_form_with_striding_workgroups(cap, monkeypatch):
+def test_split_form_with_striding_workgroups(cap):
     """The split form (decisions and draw units in launches of their own, used
     when one grid would be too large) with a small workgroup cap, so that
     every workgroup strides over several items; it must agree with the oracle
     and leave the workspace zeroed."""
-    monkeypatch.setenv("SV_CHAIN_TEST_GRID_CAP", str(cap))
     ci = synth.chain_inputs(131, B=24, gamma=3, V=40000, dtype="bf16", family="peaked",
                             draft_sigma=(0.3, 2.0), temperature=0.8, greedy_odd=True)
     dev = torch.device("cuda")
@@ -256,7 +255,7 @@ def test_split_form_with_striding_workgroups(cap, monkeypatch):
     refs = oracle_chain_many(ci, u_sets)
     tally = Tally()
     for u, ref in zip(u_sets, refs):
-        with sv.KernelTimer(8) as timer:
+        with sv.library_control(sv.SV_HOOK_CHAIN_GRID_CAP, cap), sv.KernelTimer(8) as timer:
             ot, on = sv.verify_chain(tgt, drf, tok, to_device(u), T, ws=ws)
             torch.cuda.synchronize()
         for name in ("chain_stream", "chain_decide", "chain_units"):
@@ -266,12 +265,12 @@ def test_split_form_with_striding_workgroups(cap, monkeypatch):
     tally.check(f"split form cap={cap}")
 
 
-def test_three_launch_form_batched(monkeypatch, batched):
+def test_three_launch_form_batched(batched):
     """The three-launch form (persistent, prefetching streaming launch, then
     decisions, then draw units) agrees with the oracle on the batched
     workload."""
-    monkeypatch.setenv("SV_CHAIN_SPLIT", "1")
-    parity(batched, 20, label="three launches, batched")
+    with sv.library_control(sv.SV_HOOK_CHAIN_SPLIT, 1):
+        parity(batched, 20, label="three launches, batched")
 
 
 def test_graph_capture_replays_match_eager():

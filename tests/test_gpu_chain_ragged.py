@@ -111,12 +111,12 @@ def test_null_lengths_equal_the_fixed_call():
     assert (acc[np.arange(ci.B), 0] >= 0).all()
 
 
-def test_ragged_three_launch_form(monkeypatch):
-    monkeypatch.setenv("SV_CHAIN_SPLIT", "1")
+def test_ragged_three_launch_form():
     ci = synth.chain_inputs(15630, B=20, gamma=8, V=30000, dtype="bf16", family="zipf",
                             draft_sigma=0.8, temperature=1.0)
     gam = (np.arange(ci.B) * 3 % 9).astype(np.int32)
-    ragged_parity(ci, gam, 6, "ragged three-launch")
+    with sv.library_control(sv.SV_HOOK_CHAIN_SPLIT, 1):
+        ragged_parity(ci, gam, 6, "ragged three-launch")
 
 
 def test_ragged_graph_capture_replays_match_eager():

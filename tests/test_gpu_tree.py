@@ -100,13 +100,13 @@ def test_depth_cap_enforced():
     assert (ref.num_accepted == gpu[0][2]).all()
 
 
-def test_multi_launch_form(monkeypatch):
+def test_multi_launch_form():
     """The multi-launch form (one step per depth level, used when the single
     launch's grid would be too large) agrees with the oracle."""
-    monkeypatch.setenv("SV_TREE_SPLIT", "1")
-    for T in (0.0, 0.8):
-        ti = synth.tree_inputs(seed=305, B=12, N=40, V=3000, max_depth=6, temperature=T, draft_sigma=0.3)
-        tree_parity(ti, 10, f"multi-launch T={T}")
+    with sv.library_control(sv.SV_HOOK_TREE_SPLIT, 1):
+        for T in (0.0, 0.8):
+            ti = synth.tree_inputs(seed=305, B=12, N=40, V=3000, max_depth=6, temperature=T, draft_sigma=0.3)
+            tree_parity(ti, 10, f"multi-launch T={T}")
 
 
 def test_graph_capture_replays_match_eager():
@@ -159,7 +159,7 @@ def test_more_workgroups_than_fit_at_once():
     tree_parity(ti, 2, "2048 trees")
 
 
-def test_single_launch_after_the_other_forms_on_the_shared_workspace(monkeypatch):
+def test_single_launch_after_the_other_forms_on_the_shared_workspace():
     """The debug-probabilities call and the multi-launch tree form run on the
     same cached workspace as the single-launch tree kernel, which counts and
     flags through it: each leaves it zero, so sampled tree calls after them
@@ -170,9 +170,8 @@ def test_single_launch_after_the_other_forms_on_the_shared_workspace(monkeypatch
                    to_device(ci.draft_tokens.astype(np.int32)), to_device(ci.temperature.astype(np.float32)))
     assert_shared_workspace_zero("probs")
     ti = synth.tree_inputs(seed=307, B=20, N=48, V=40000, max_depth=7, temperature=1.0, draft_sigma=0.3)
-    monkeypatch.setenv("SV_TREE_SPLIT", "1")
-    tree_parity(ti, 3, "multi-launch before single")
-    monkeypatch.delenv("SV_TREE_SPLIT")
+    with sv.library_control(sv.SV_HOOK_TREE_SPLIT, 1):
+        tree_parity(ti, 3, "multi-launch before single")
     tree_parity(ti, 6, "single after multi-launch", seed=4)
 
 
