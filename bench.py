@@ -30,6 +30,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -88,44 +89,6 @@ def stored_traffic(kernel: str):
 
 
 TOPK = 50                        # k of every sampling request in the top-k workload
-
-
-def cpu_baseline(ci, budget_s: float = 15.0, gammas=None, top_k=None, top_p=None):
-    """The fp64 oracle as it stands, timed on this host's cores: it verifies
-    the same batch over and over with fresh uniforms until the budget is
-    spent.  `cores` is the CPU time it used divided by the wall time."""
-    import oracle
-    rows = 0
-    passes = 0
-    requests = 0
-    w0 = time.perf_counter()
-    c0 = time.process_time()
-    while time.perf_counter() - w0 < budget_s:
-        u = ci.uniforms if passes == 0 else ci.fresh_uniforms(90_000 + passes)
-        for b in range(ci.B):
-            if top_k is not None:
-                oracle.verify_chain_topk(ci.target[b:b + 1], ci.draft[b:b + 1], ci.draft_tokens[b:b + 1],
-                                         u[b:b + 1], ci.temperature[b:b + 1], top_k[b:b + 1], ci.dtype,
-                                         top_p=None if top_p is None else top_p[b:b + 1])
-                rows += ci.gamma + 1
-            elif gammas is None:
-                oracle.verify_chain(ci.target[b:b + 1], ci.draft[b:b + 1], ci.draft_tokens[b:b + 1],
-                                    u[b:b + 1], ci.temperature[b:b + 1], ci.dtype)
-                rows += ci.gamma + 1
-            else:
-                oracle.verify_chain_ragged(ci.target[b:b + 1], ci.draft[b:b + 1], ci.draft_tokens[b:b + 1],
-                                           u[b:b + 1], ci.temperature[b:b + 1], gammas[b:b + 1], ci.dtype)
-                rows += int(gammas[b]) + 1
-            requests += 1
-            if time.perf_counter() - w0 >= budget_s:
-                break
-        passes += 1
-    wall = time.perf_counter() - w0
-    cpu = time.process_time() - c0
-    return {"value": rows / wall, "unit": "rows/s", "cores": max(1, round(cpu / wall)),
-            "kind": "oracle",
-            "sample": f"{requests} request verifications ({rows} rows) of the same batch with "
-                      f"fresh uniforms, numpy fp64, {wall:.1f} s wall, {cpu:.1f} s CPU"}
 
 
 WORKLOADS = ("batched", "single", "deep", "ragged", "topk", "tree-greedy", "tree-sampling", "tree-mss", "tree-mask")
@@ -267,8 +230,6 @@ def run_chain(args, torch, synth, sv):
     if args.workload == "single":
         result["graph_replay"] = graph_replay(torch, stream, sv, sets[0], tok, u_sets[0], T, out_t, out_n, ws,
                                               args.steps)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(ci, gammas=gam, top_k=k_np if topk else None, top_p=p_np)
     return result
 
 
@@ -375,8 +336,6 @@ def run_tree(args, torch, synth, sv, oracle_sample=True):
                        "frac": rd / (call_us * 1e-6) / 1e9 / PEAK_HBM_GBPS},
     })
     result["config"]["rows_read_per_call"] = rows
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_tree(ti, mss=mss)
     return result
 
 
@@ -431,53 +390,147 @@ def run_mask(args, torch, synth, sv):
                              "time, not bytes; large_shape shows the store-bound regime"},
         "large_shape": {k: v for k, v in large.items() if k != "total_ms"},
     })
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_mask(synth.tree_parent_arrays(15005, 32, 64, 8, 4), 8)
     return result
 
 
-def cpu_baseline_mask(parents, max_depth, budget_s: float = 10.0):
-    """The oracle's mask on the same batch, repeated until the budget is spent."""
-    import oracle
-    rows = calls = 0
-    w0 = time.perf_counter()
-    c0 = time.process_time()
-    while time.perf_counter() - w0 < budget_s:
-        oracle.tree_attention_mask(parents, max_depth)
-        rows += parents.size
-        calls += 1
-    wall = time.perf_counter() - w0
-    cpu = time.process_time() - c0
-    return {"value": rows / wall, "unit": "rows/s", "cores": max(1, round(cpu / wall)), "kind": "oracle",
-            "sample": f"{calls} masks of the same B=32, N=64 batch ({rows} rows), python loops, "
-                      f"{wall:.1f} s wall, {cpu:.1f} s CPU"}
+# ---------------------------------------------------------------------------
+# the oracle timed on the host (a child process started before the GPU is
+# touched; its pool forks from that child)
+# ---------------------------------------------------------------------------
+BOX_CPU_SHARE = 16          # host cores granted to a job that holds one GPU
+SINGLE_BUDGET_S = 10.0
+POOL_BUDGET_S = 6.0
+_BASELINE = {}
 
 
-def cpu_baseline_tree(ti, budget_s: float = 15.0, mss: bool = False):
-    """The oracle's tree verification on the same batch, request by request,
-    until the budget is spent; the unit is node rows per second."""
+def host_cpu() -> dict:
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    if model is None:
+        try:
+            out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+            for line in out.splitlines():
+                if line.startswith("Model name"):
+                    model = line.split(":", 1)[1].strip()
+        except (OSError, subprocess.SubprocessError):
+            pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(),
+            "cpus_in_affinity": len(os.sched_getaffinity(0))}
+
+
+def oracle_units(workload, top_p):
+    """The oracle's work on one workload's batch as (units, fn, what): fn(b, s)
+    verifies unit b (a request, a tree, or the whole mask batch) in pass s and
+    returns the rows that covers.  Chain passes after the first draw fresh
+    uniforms, as the GPU calls do."""
     import oracle
-    rows = requests = 0
-    w0 = time.perf_counter()
-    c0 = time.process_time()
-    while time.perf_counter() - w0 < budget_s:
-        for b in range(ti.B):
+    import synth
+
+    if workload == "tree-mask":
+        parents = synth.tree_parent_arrays(15005, 32, 64, 8, 4)
+
+        def fn(b, s):
+            oracle.tree_attention_mask(parents, 8)
+            return parents.size
+        return 1, fn, "masks of the B=32, N=64 batch (python loops)"
+    if workload.startswith("tree"):
+        mss = workload == "tree-mss"
+        ti = synth.tree_inputs(temperature=0.0 if workload == "tree-greedy" else 1.0, keep_draft=mss)
+
+        def fn(b, s):
+            sl = slice(b, b + 1)
             if mss:
-                oracle.verify_tree_mss(ti.logits[b:b + 1], ti.draft_logits[b:b + 1], ti.node_tokens[b:b + 1],
-                                       ti.parents[b:b + 1], ti.uniforms[b:b + 1], ti.draw_uniforms[b:b + 1],
-                                       ti.temperature[b:b + 1], ti.dtype, ti.max_depth)
+                oracle.verify_tree_mss(ti.logits[sl], ti.draft_logits[sl], ti.node_tokens[sl], ti.parents[sl],
+                                       ti.uniforms[sl], ti.draw_uniforms[sl], ti.temperature[sl], ti.dtype,
+                                       ti.max_depth)
             else:
-                oracle.verify_tree(ti.logits[b:b + 1], ti.node_tokens[b:b + 1], ti.parents[b:b + 1],
-                                   ti.uniforms[b:b + 1], ti.temperature[b:b + 1], ti.dtype, ti.max_depth)
-            rows += ti.N
-            requests += 1
-            if time.perf_counter() - w0 >= budget_s:
-                break
-    wall = time.perf_counter() - w0
-    cpu = time.process_time() - c0
-    return {"value": rows / wall, "unit": "rows/s", "cores": max(1, round(cpu / wall)), "kind": "oracle",
-            "sample": f"{requests} tree verifications ({rows} node rows) of the same batch, numpy fp64, "
-                      f"{wall:.1f} s wall, {cpu:.1f} s CPU"}
+                oracle.verify_tree(ti.logits[sl], ti.node_tokens[sl], ti.parents[sl], ti.uniforms[sl],
+                                   ti.temperature[sl], ti.dtype, ti.max_depth)
+            return ti.N
+        return ti.B, fn, "tree verifications of the batch, numpy fp64"
+    ci, _ = chain_case(workload, synth)
+    gam = (np.array([RAGGED_LENGTHS[b % len(RAGGED_LENGTHS)] for b in range(ci.B)], np.int32)
+           if workload == "ragged" else None)
+    k_np = np.full(ci.B, TOPK, np.int32) if workload == "topk" else None
+    p_np = np.full(ci.B, top_p, np.float32) if (k_np is not None and top_p is not None) else None
+    u_pass = {}
+
+    def fn(b, s):
+        if s not in u_pass:
+            u_pass.clear()
+            u_pass[s] = ci.uniforms if s == 0 else ci.fresh_uniforms(90_000 + s)
+        u, sl = u_pass[s], slice(b, b + 1)
+        if k_np is not None:
+            oracle.verify_chain_topk(ci.target[sl], ci.draft[sl], ci.draft_tokens[sl], u[sl], ci.temperature[sl],
+                                     k_np[sl], ci.dtype, top_p=None if p_np is None else p_np[sl])
+        elif gam is None:
+            oracle.verify_chain(ci.target[sl], ci.draft[sl], ci.draft_tokens[sl], u[sl], ci.temperature[sl],
+                                ci.dtype)
+        else:
+            oracle.verify_chain_ragged(ci.target[sl], ci.draft[sl], ci.draft_tokens[sl], u[sl],
+                                       ci.temperature[sl], gam[sl], ci.dtype)
+            return int(gam[b]) + 1
+        return ci.gamma + 1
+    return ci.B, fn, "request verifications of the batch with fresh uniforms per pass, numpy fp64"
+
+
+def _oracle_loop(job):
+    """Worker w of W walks the whole batch in order, starting at unit
+    w * units / W, with pass numbers of its own, until its budget is spent:
+    every worker sees the batch's mix of requests, as one process does."""
+    w, W, budget_s = job
+    units, fn = _BASELINE["units"], _BASELINE["fn"]
+    rows = n = 0
+    j = 0
+    w0, c0 = time.perf_counter(), time.process_time()
+    while time.perf_counter() - w0 < budget_s:
+        rows += fn((j + (w * units) // W) % units, (j // units) * W + w)
+        n += 1
+        j += 1
+    return rows, n, time.perf_counter() - w0, time.process_time() - c0
+
+
+def cpu_baseline_only(workload, top_p) -> dict:
+    """Single process, then a pool of min(16, CPUs in this process's affinity)
+    forked workers over the same batch; `value` is the pool's rate."""
+    import multiprocessing as mp
+
+    units, fn, what = oracle_units(workload, top_p)
+    _BASELINE.update(units=units, fn=fn)
+    rows1, n1, wall1, cpu1 = _oracle_loop((0, 1, SINGLE_BUDGET_S))
+    W = max(1, min(BOX_CPU_SHARE, len(os.sched_getaffinity(0))))
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(W) as pool:
+        parts = pool.map(_oracle_loop, [(w, W, POOL_BUDGET_S) for w in range(W)])
+    wall = time.perf_counter() - t0
+    rows, n, cpu = sum(p[0] for p in parts), sum(p[1] for p in parts), sum(p[3] for p in parts)
+    return {"value": rows / wall, "unit": "rows/s", "cores": W, "kind": "oracle",
+            "sample": f"{n} {what}, {W} single-threaded worker processes for {wall:.1f} s wall "
+                      f"({rows} rows, {cpu:.1f} s CPU)",
+            "single_process": {"value": rows1 / wall1, "unit": "rows/s", "cores": 1,
+                               "sample": f"{n1} units, {rows1} rows in {wall1:.1f} s wall, {cpu1:.1f} s CPU"},
+            "host": host_cpu()}
+
+
+def cpu_baseline_child(workload, top_p):
+    """Runs the oracle timing in a child process with one thread per process,
+    before this process touches the GPU."""
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", workload, "--cpu-baseline-only"]
+    if top_p is not None:
+        cmd += ["--top-p", repr(top_p)]
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600, env=env, cwd=ROOT)
+    lines = [x for x in r.stdout.splitlines() if x.startswith("{")]
+    if r.returncode != 0 or not lines:
+        raise RuntimeError(f"oracle timing failed (exit {r.returncode}): {r.stderr[-2000:]}")
+    return json.loads(lines[-1])
 
 
 def head(args, value, total_ms, config, metric=METRIC):
@@ -507,6 +560,8 @@ def main():
     ap.add_argument("--workload", choices=WORKLOADS, default="batched",
                     help="batched is the headline; the others are reported alongside it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-only", action="store_true",
+                    help="time the oracle on the host only and print its JSON (no GPU use)")
     ap.add_argument("--top-p", type=float, default=None,
                     help="topk workload: also filter to this top-p mass after top-k (draft tokens stay top-k draws)")
     args = ap.parse_args()
@@ -516,6 +571,10 @@ def main():
         print("bench.py measures one GPU only: requests shard across GPUs with no exchange, so a "
               "multi-GPU figure is N independent copies of this one", file=sys.stderr)
         sys.exit(2)
+    if args.cpu_baseline_only:
+        print(json.dumps(cpu_baseline_only(args.workload, args.top_p)), flush=True)
+        return
+    baseline = None if args.no_cpu_baseline else cpu_baseline_child(args.workload, args.top_p)
 
     import torch
     import synth
@@ -529,6 +588,8 @@ def main():
         result = run_tree(args, torch, synth, sv)
     else:
         result = run_chain(args, torch, synth, sv)
+    if baseline is not None:
+        result["cpu_baseline"] = baseline
     print(json.dumps(result), flush=True)
     # leave no device memory for torch's allocator to free during exit()
     del result
