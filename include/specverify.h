@@ -174,6 +174,29 @@ SV_API int spec_verify_chain_noalloc(const void* target_logits, const void* draf
                               int32_t* out_tokens, int32_t* out_num_accepted, void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * Chain verification with a scheduling hint (close-reading notes 02,
+ * section 4, as spec_verify_chain).
+ *
+ * sampling_hint  [B]  uint8, HOST memory, or NULL: nonzero where the caller
+ *                     expects request b to sample (temperature[b] > 0).
+ * The hint changes only the order in which the work is laid out on the GPU:
+ * the requests hinted to sample stream first, their draws then run while the
+ * other requests' rows stream.  Results are those of spec_verify_chain for
+ * any hint (a wrong hint costs time, not correctness); the kernel still takes
+ * every request's mode from its temperature.  The hint is read on the host
+ * during the call and may be freed when it returns.  It is used for batches of
+ * at most SV_HINT_MAX_BATCH requests and ignored otherwise (as is NULL).
+ * Everything else as spec_verify_chain (same workspace query).
+ * ---------------------------------------------------------------------- */
+#define SV_HINT_MAX_BATCH 256
+
+SV_API int spec_verify_chain_hinted(const void* target_logits, const void* draft_logits,
+                             const int32_t* draft_tokens, const float* uniforms,
+                             const float* temperature, const uint8_t* sampling_hint, int B, int gamma,
+                             int V, int dtype, int32_t* out_tokens, int32_t* out_num_accepted,
+                             void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * Chain verification under a consistent top-k filter.
  *
  * Every target and draft row of a sampling request is filtered alike before

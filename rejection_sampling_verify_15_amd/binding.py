@@ -23,6 +23,7 @@ SV_BF16, SV_F32 = 0, 1
 SV_GAVE_UP = -2   # accepted count of a request whose bounded wait gave up
 SV_HOOK_CHAIN_GRID_CAP, SV_HOOK_CHAIN_SPLIT, SV_HOOK_TREE_SPLIT, SV_HOOK_SPIN_LIMIT = range(4)
 SV_MAX_GAMMA = 32
+SV_HINT_MAX_BATCH = 256
 SV_MAX_TOPK = 128
 
 EXPORTS = {
@@ -35,6 +36,8 @@ EXPORTS = {
                           [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]),
     "spec_verify_chain_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 +
                                   [ctypes.c_void_p] * 3),
+    "spec_verify_chain_hinted": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 +
+                                 [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]),
     "spec_verify_chain_ragged": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 +
                                  [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
     "sv_chain_topk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
@@ -194,12 +197,33 @@ def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
+def sampling_hint_array(hint, B: int):
+    """A host byte array of the caller's expected modes (nonzero: samples),
+    from a sequence, numpy array or CPU tensor of B entries; an array this
+    function made is passed through, so a caller can build it once."""
+    if isinstance(hint, ctypes.Array) and hint._type_ is ctypes.c_uint8:
+        if len(hint) < B:
+            raise ValueError(f"sampling_hint must have {B} entries")
+        return hint
+    if isinstance(hint, torch.Tensor):
+        if hint.is_cuda:
+            raise ValueError("sampling_hint must be host data: the point is to avoid reading the device")
+        hint = hint.numpy()
+    vals = [1 if bool(x) else 0 for x in hint]
+    if len(vals) != B:
+        raise ValueError(f"sampling_hint must have {B} entries")
+    return (ctypes.c_uint8 * max(B, 1))(*vals)
+
+
 def verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: torch.Tensor,
                  uniforms: torch.Tensor, temperature: torch.Tensor,
                  out_tokens: Optional[torch.Tensor] = None,
                  out_num_accepted: Optional[torch.Tensor] = None,
-                 ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """spec_verify_chain over device tensors.
+                 ws: Optional[torch.Tensor] = None,
+                 sampling_hint=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """spec_verify_chain over device tensors (spec_verify_chain_hinted when
+    `sampling_hint`, host data of B truth values, says which requests the
+    caller expects to sample; it only changes the layout of the work).
 
     target [B, gamma+1, V] and draft [B, gamma, V] (bf16 or fp32, same dtype),
     draft_tokens [B, gamma] int32, uniforms [B, gamma+1] fp32,
@@ -230,6 +254,13 @@ def verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_toke
     nbytes = L.sv_chain_workspace_bytes(B, gamma, V, dt)
     if ws is None:
         ws = workspace(nbytes, dev)
+    if sampling_hint is not None:
+        hint = sampling_hint_array(sampling_hint, B)
+        st = L.spec_verify_chain_hinted(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
+                                        _ptr(temperature), hint, B, gamma, V, dt, _ptr(out_tokens),
+                                        _ptr(out_num_accepted), _ptr(ws), ws.numel(), _stream_handle(dev))
+        _check(st, "spec_verify_chain_hinted")
+        return out_tokens, out_num_accepted
     st = L.spec_verify_chain(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
                              _ptr(temperature), B, gamma, V, dt, _ptr(out_tokens),
                              _ptr(out_num_accepted), _ptr(ws), ws.numel(), _stream_handle(dev))

@@ -106,6 +106,15 @@ enum : int32_t { kPendingDraw = 1, kPendingNone = 2 };  // Pending::valid once p
 constexpr int kCounterStride = 32;  // uint32 words per request: one 128-byte line
 constexpr int kUnitCounter = 0;     // draw units of the request that have counted in
 
+// The block layout of a call with a sampling hint (batches of up to
+// SV_HINT_MAX_BATCH requests): the requests the caller expects to sample
+// first, then the unit pool, then the others.  nS < 0: no plan.
+struct ChainPlan {
+  int32_t nS;                          // requests hinted to sample: order[0, nS)
+  int32_t pool;                        // unit-pool workgroups after them
+  uint8_t order[SV_HINT_MAX_BATCH];    // request of each segment
+};
+
 struct ChainArgs {
   const void* target;
   const void* draft;
@@ -124,6 +133,7 @@ struct ChainArgs {
   const int32_t* gammas; // [B] draft length of each request (ragged calls), or NULL: all gamma
   float* out_tau;        // [B][gamma] tau of each test taken, -1 elsewhere; or NULL
   uint32_t spin;         // poll bound of every wait (kSpinLimit unless a test lowers it)
+  ChainPlan plan;        // block layout of a hinted call
 };
 
 // T must be 0 (greedy) or a finite positive normal float.
@@ -1020,28 +1030,132 @@ __device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count) {
 // batches count their units in and the last one draws.  Each workgroup keeps at most 96 VGPRs, so five
 // waves share a SIMD (six would force the draw path to spill).
 constexpr int kDecideDrawsMax = 256;
+static_assert(SV_HINT_MAX_BATCH <= kDecideDrawsMax, "hinted calls have their decide items draw");
+
+// What a block of chain_verify does: a stream item (request, row, chunk), a
+// decide item, or pool workgroup w of `count`.  Each part is called from one
+// place, so everything stays inlined into the kernel (a call would put the
+// arguments in scratch memory).
+struct BlockRole {
+  enum : int { kNone = 0, kStream = 1, kDecide = 2, kPool = 3, kDraftTail = 4 } kind;
+  RowItem item;
+  uint32_t w, count;
+};
+
+// Chunks of a hinted-greedy request's draft row that one tail workgroup takes.
+constexpr uint32_t kTailChunks = 4;
+
+// Default layout: one segment per request (its stream items, then its decide
+// item), then the unit pool.
+__device__ inline BlockRole default_role(const ChainArgs& a, uint32_t blk) {
+  const uint32_t seg = static_cast<uint32_t>(a.per_req) + 1u;
+  const uint32_t nseg = static_cast<uint32_t>(a.B) * seg;
+  BlockRole r{};
+  if (blk < nseg) {
+    const uint32_t b = blk / seg;
+    const uint32_t rem = blk - b * seg;
+    r.item.b = static_cast<int>(b);
+    if (rem < static_cast<uint32_t>(a.per_req)) {
+      const uint32_t k = rem / static_cast<uint32_t>(a.nchunk);
+      r.kind = BlockRole::kStream;
+      r.item.k = static_cast<int>(k);
+      r.item.c = static_cast<int>(rem - k * static_cast<uint32_t>(a.nchunk));
+    } else {
+      r.kind = BlockRole::kDecide;
+    }
+    return r;
+  }
+  r.kind = BlockRole::kPool;
+  r.w = blk - nseg;
+  r.count = gridDim.x - nseg;
+  return r;
+}
+
+// The layout of a hinted call: segments of the requests hinted to sample (all
+// rows, then the decide item), the unit pool, the target-row segments of the
+// other requests (target rows, then the decide item), and last those
+// requests' draft rows, kTailChunks chunks per workgroup, which stream only if
+// their request does sample after all.  So the greedy rows stream while the sampling requests are
+// decided and drawn.  A wrong hint costs time only: the pool ranks the
+// requests by their temperatures, and every request's rows are in the grid.
+// The waits for higher blocks (pool and decide items of a request that
+// samples against its hint) always end: the host keeps the pool and the
+// decide items well below the wave slots of the device, so stream items,
+// which never wait, always find slots.
+__device__ inline BlockRole planned_role(const ChainArgs& a, uint32_t blk) {
+  const uint32_t nc = static_cast<uint32_t>(a.nchunk);
+  const uint32_t nS = static_cast<uint32_t>(a.plan.nS);
+  const uint32_t nG = static_cast<uint32_t>(a.B) - nS;
+  const uint32_t segS = static_cast<uint32_t>(a.per_req) + 1u;
+  const uint32_t endS = nS * segS;
+  const uint32_t pool = static_cast<uint32_t>(a.plan.pool);
+  const uint32_t segT = static_cast<uint32_t>(a.gamma + 1) * nc;
+  const uint32_t endG = endS + pool + nG * (segT + 1u);
+  BlockRole r{};
+  if (blk < endS) {
+    const uint32_t s = blk / segS, rem = blk - s * segS;
+    r.item.b = a.plan.order[s];
+    if (rem < static_cast<uint32_t>(a.per_req)) {
+      const uint32_t k = rem / nc;
+      r.kind = BlockRole::kStream;
+      r.item.k = static_cast<int>(k);
+      r.item.c = static_cast<int>(rem - k * nc);
+    } else {
+      r.kind = BlockRole::kDecide;
+    }
+    return r;
+  }
+  if (blk < endS + pool) {
+    r.kind = BlockRole::kPool;
+    r.w = blk - endS;
+    r.count = pool;
+    return r;
+  }
+  if (blk < endG) {
+    const uint32_t q = blk - endS - pool, g = q / (segT + 1u), rem = q - g * (segT + 1u);
+    r.item.b = a.plan.order[nS + g];
+    if (rem < segT) {
+      const uint32_t k = rem / nc;
+      r.kind = BlockRole::kStream;
+      r.item.k = static_cast<int>(k);
+      r.item.c = static_cast<int>(rem - k * nc);
+    } else {
+      r.kind = BlockRole::kDecide;
+    }
+    return r;
+  }
+  const uint32_t per_row = (nc + kTailChunks - 1) / kTailChunks;
+  const uint32_t dr = static_cast<uint32_t>(a.gamma) * per_row;
+  const uint32_t q = blk - endG, g = q / dr, rem = q - g * dr;
+  if (g >= nG) return r;
+  const uint32_t k = rem / per_row;
+  r.kind = BlockRole::kDraftTail;
+  r.item = RowItem{a.plan.order[nS + g], a.gamma + 1 + static_cast<int>(k),
+                   static_cast<int>((rem - k * per_row) * kTailChunks)};
+  return r;
+}
 
 template <int DT, bool VEC, int SPAN>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(5))) void chain_verify(ChainArgs a) {
   // 32-bit index arithmetic: this grid has at most kMaxGrid blocks
-  const uint32_t blk = blockIdx.x;
-  const uint32_t seg = static_cast<uint32_t>(a.per_req) + 1u;
-  const uint32_t nseg = static_cast<uint32_t>(a.B) * seg;
-  if (blk < nseg) {
-    const uint32_t b = blk / seg;
-    const uint32_t rem = blk - b * seg;
-    if (rem < static_cast<uint32_t>(a.per_req)) {
-      const uint32_t k = rem / static_cast<uint32_t>(a.nchunk);
-      stream_once<DT, VEC>(a, RowItem{static_cast<int>(b), static_cast<int>(k),
-                                      static_cast<int>(rem - k * static_cast<uint32_t>(a.nchunk))});
-      return;
+  const BlockRole r = a.plan.nS >= 0 ? planned_role(a, blockIdx.x) : default_role(a, blockIdx.x);
+  const bool draws = a.B <= kDecideDrawsMax;
+  if (r.kind == BlockRole::kStream) {
+    stream_once<DT, VEC>(a, r.item);
+  } else if (r.kind == BlockRole::kDraftTail) {
+    const float T = a.temperature[r.item.b];
+    if (!(temp_ok(T) && T > 0.0f)) return;  // greedy as hinted: no draft rows
+    for (uint32_t j = 0; j < kTailChunks; ++j) {
+      const RowItem it{r.item.b, r.item.k, r.item.c + static_cast<int>(j)};
+      if (it.c < a.nchunk) stream_once<DT, VEC>(a, it);
     }
-    if (a.B <= kDecideDrawsMax) decide_request<DT, VEC, SPAN, true>(a, static_cast<int>(b));
-    else decide_request<DT, VEC, SPAN, false>(a, static_cast<int>(b));
-    return;
+  } else if (r.kind == BlockRole::kDecide) {
+    if (draws) decide_request<DT, VEC, SPAN, true>(a, r.item.b);
+    else decide_request<DT, VEC, SPAN, false>(a, r.item.b);
+  } else if (r.kind == BlockRole::kPool) {
+    if (draws) unit_pool<DT, VEC, SPAN, false>(a, r.w, r.count);
+    else unit_pool<DT, VEC, SPAN, true>(a, r.w, r.count);
   }
-  if (a.B <= kDecideDrawsMax) unit_pool<DT, VEC, SPAN, false>(a, blk - nseg, gridDim.x - nseg);
-  else unit_pool<DT, VEC, SPAN, true>(a, blk - nseg, gridDim.x - nseg);
 }
 
 // Very large shapes: the three parts as three launches.  Persistent
@@ -1162,6 +1276,44 @@ static long long stream_capacity() {
   return cached[dev];
 }
 
+// Wave slots of chain_verify on the current device (one-wave workgroups).
+template <int DT, bool VEC, int SPAN>
+static long long verify_capacity() {
+  static long long cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_verify<DT, VEC, SPAN>, kWave, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 || cus < 1)
+      return 0;
+    cached[dev] = static_cast<long long>(per_cu) * cus;
+  }
+  return cached[dev];
+}
+
+// The hinted layout's grid (0: the call runs unplanned).  With every request
+// hinted to sample, the pool is last, as in the default layout.  Otherwise it
+// gets one workgroup per unit of the requests hinted to sample, at least one
+// unit's worth (a request may sample against its hint), and at most what
+// leaves an eighth of the device's wave slots, beyond the decide items, to the
+// stream items after it.
+template <int DT, bool VEC, int SPAN>
+static long long planned_grid(ChainArgs& a) {
+  const long long nS = a.plan.nS, nG = a.B - nS, nc = a.nchunk;
+  if (nG == 0) {
+    a.plan.pool = static_cast<int32_t>(std::min(static_cast<long long>(a.B) * a.nunit, kUnitPool));
+  } else {
+    const long long cap = verify_capacity<DT, VEC, SPAN>();
+    const long long budget = cap - a.B - cap / 8;
+    const long long want = std::max<long long>(nS * a.nunit, a.nunit);
+    if (budget < a.nunit) return 0;
+    a.plan.pool = static_cast<int32_t>(std::min(want, budget));
+  }
+  return nS * (a.per_req + 1) + a.plan.pool + nG * ((a.gamma + 1) * nc + 1) +
+         nG * a.gamma * ((nc + kTailChunks - 1) / kTailChunks);
+}
+
 template <int DT, bool VEC>
 static int launch_chain(ChainArgs a, hipStream_t stream) {
   a.nstream = static_cast<long long>(a.B) * (2 * a.gamma + 1) * a.nchunk;
@@ -1173,11 +1325,18 @@ static int launch_chain(ChainArgs a, hipStream_t stream) {
   const long long pool = std::min(static_cast<long long>(a.B) * a.nunit, kUnitPool);
   const long long fused = a.nstream + a.B + pool;
   if (cap <= 0 && test_hook(SV_HOOK_CHAIN_SPLIT) == 0 && fused <= kMaxGrid) {
-    const dim3 grid(static_cast<unsigned>(fused));
+    long long n = fused;
+    if (a.plan.nS >= 0) {
+      const long long planned = small ? planned_grid<DT, VEC, kUnitSpanSmall>(a) : planned_grid<DT, VEC, kUnitSpanLarge>(a);
+      if (planned > 0 && planned <= kMaxGrid) n = planned;
+      else a.plan.nS = -1;
+    }
+    const dim3 grid(static_cast<unsigned>(n));
     if (small) launch(SV_K_CHAIN_VERIFY, chain_verify<DT, VEC, kUnitSpanSmall>, grid, dim3(kWave), 0, stream, a);
     else launch(SV_K_CHAIN_VERIFY, chain_verify<DT, VEC, kUnitSpanLarge>, grid, dim3(kWave), 0, stream, a);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
   }
+  a.plan.nS = -1;
   // three launches, with 1024-logit draw units
   a.nunit = units_for(a.V, kUnitSpanLarge);
   const long long units = static_cast<long long>(a.B) * a.nunit;
@@ -1223,7 +1382,8 @@ static int chain_check(const void* target_logits, const void* draft_logits, cons
 static int chain_entry(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                        const float* uniforms, const float* temperature, const int32_t* gammas, int B, int gamma,
                        int V, int dtype, int32_t* out_tokens, int32_t* out_num_accepted, float* out_tau,
-                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+                       void* workspace, size_t workspace_bytes, void* hip_stream,
+                       const uint8_t* sampling_hint = nullptr) {
   const int chk = chain_check(target_logits, draft_logits, draft_tokens, uniforms, temperature, B, gamma, V, dtype,
                               out_tokens, out_num_accepted);
   if (chk != SV_OK || B == 0) return chk;
@@ -1250,6 +1410,15 @@ static int chain_entry(const void* target_logits, const void* draft_logits, cons
   a.gammas = gammas;
   a.out_tau = gamma > 0 ? out_tau : nullptr;
   a.spin = spin_limit(kSpinLimit);
+  a.plan.nS = -1;
+  if (sampling_hint && B <= SV_HINT_MAX_BATCH) {
+    int s = 0;
+    for (int b = 0; b < B; ++b)
+      if (sampling_hint[b]) a.plan.order[s++] = static_cast<uint8_t>(b);
+    a.plan.nS = s;
+    for (int b = 0; b < B; ++b)
+      if (!sampling_hint[b]) a.plan.order[s++] = static_cast<uint8_t>(b);
+  }
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const int kv = dtype == SV_BF16 ? Elem<0>::kVec : Elem<1>::kVec;
   const bool vec = (V % kv == 0) && aligned(target_logits, 16) && (!a.draft || aligned(a.draft, 16));
@@ -1264,6 +1433,16 @@ extern "C" int spec_verify_chain(const void* target_logits, const void* draft_lo
                                  void* workspace, size_t workspace_bytes, void* hip_stream) {
   return chain_entry(target_logits, draft_logits, draft_tokens, uniforms, temperature, nullptr, B, gamma, V,
                      dtype, out_tokens, out_num_accepted, nullptr, workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" int spec_verify_chain_hinted(const void* target_logits, const void* draft_logits,
+                                        const int32_t* draft_tokens, const float* uniforms,
+                                        const float* temperature, const uint8_t* sampling_hint, int B, int gamma,
+                                        int V, int dtype, int32_t* out_tokens, int32_t* out_num_accepted,
+                                        void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return chain_entry(target_logits, draft_logits, draft_tokens, uniforms, temperature, nullptr, B, gamma, V,
+                     dtype, out_tokens, out_num_accepted, nullptr, workspace, workspace_bytes, hip_stream,
+                     sampling_hint);
 }
 
 extern "C" int spec_verify_chain_ragged(const void* target_logits, const void* draft_logits,
