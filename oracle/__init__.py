@@ -20,7 +20,7 @@ float64, written from these sources (cited by page title and section):
   four steps of one round).
 * "LLM speculative decoding close-reading notes 02", section 5.4 (any
   decoding strategy applied alike to p and q keeps the method exact: the
-  consistent top-k filter).
+  consistent top-k and top-p filters).
 
 Every reading the pages leave open (which uniform feeds the final draw, the
 inverse-CDF convention, tie-breaks, the empty residual, the tree contract) is
@@ -32,6 +32,7 @@ from .specverify_oracle import (  # noqa: F401
     logits_to_f64, softmax_t, accept_threshold, inverse_cdf_draw,
     chain_distributions, chain_decide_request, verify_chain, RaggedChainResult, verify_chain_ragged,
     topk_filter, topp_filter, verify_chain_topk, TOPK_MAX, TOPK_MAX_KEPT,
+    topp_cut, FilteredChainResult, filtered_distributions, filter_params, verify_chain_filtered,
     verify_tree, probs_debug, tree_node_depths, TreeMaskResult, tree_attention_mask,
     mss_thresholds, mss_node, mss_proposals, tree_children, verify_tree_mss,
 )

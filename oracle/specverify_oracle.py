@@ -75,6 +75,14 @@ R19 top-p after top-k (the same rule on both sides, as R17): with top_p[b] =
     largest kept logit v whose mass M(v) = sum of r over the kept logits >= v
     reaches p, and the logits >= v stay (ties at v included).  p = 1 keeps
     the top-k set; p outside (0, 1] makes the request invalid.
+R20 general consistent filter (the rules of R17 and R19 without the limits
+    of R18): a sampling request may carry top_k[b] = k >= 1 (k >= V keeps the
+    row whole), top_p[b] = p in (0, 1] (p = 1 cuts nothing), or both (top-k
+    first, then top-p over what top-k kept); either array may be absent.
+    k < 1, or p outside (0, 1], makes the request invalid (R11).  The top-p
+    cut is a floating-point decision: its margin is min(M(v*) - p,
+    p - M(v+)), v* the cut value and v+ the next larger kept value, which the
+    parity tests treat like a decision's distance to its threshold.
 """
 from __future__ import annotations
 
@@ -374,6 +382,109 @@ def topp_filter(filtered_row: np.ndarray, p: float, T: float):
         if np.isfinite(best):
             kept = kept & (row >= best)
     return np.where(kept, row, -np.inf), int(np.count_nonzero(kept))
+
+
+def topp_cut(filtered_row: np.ndarray, p: float, T: float):
+    """R19/R20 by sorting (a library sort as a step): the kept (finite)
+    values in descending order, their temperature-softmax masses summed value
+    by value (equal values together), and the first value whose cumulative
+    mass reaches p.  Returns (cut value, margin); (-inf, inf) when p >= 1 or
+    nothing is kept, i.e. nothing is cut."""
+    row = np.asarray(filtered_row, dtype=np.float64)
+    fin = np.isfinite(row)
+    if p >= 1.0 or not fin.any():
+        return -np.inf, np.inf
+    r = softmax_t(row, T)
+    vals, mass = row[fin], r[fin]
+    order = np.argsort(-vals, kind="stable")
+    vals, mass = vals[order], mass[order]
+    starts = np.concatenate(([0], 1 + np.nonzero(vals[1:] != vals[:-1])[0]))
+    cum = np.cumsum(np.add.reduceat(mass, starts))
+    j = min(int(np.searchsorted(cum, p, side="left")), len(cum) - 1)
+    below = cum[j - 1] if j > 0 else 0.0
+    return float(vals[starts[j]]), float(min(cum[j] - p, p - below))
+
+
+@dataclasses.dataclass
+class FilteredChainResult(ChainResult):
+    cut_margin: np.ndarray = None   # [B] smallest top-p cut margin of the request's rows (inf: none)
+
+
+def filtered_distributions(tgt_f64: np.ndarray, drf_f64: Optional[np.ndarray], T: float,
+                           k: Optional[int], p: Optional[float]):
+    """R20 on one request: every target and draft row filtered alike (top-k,
+    then top-p), then the temperature softmax.  Returns (P, Q, smallest cut
+    margin)."""
+    margin = np.inf
+
+    def filt(row):
+        nonlocal margin
+        f = row
+        if k is not None:
+            f, _ = topk_filter(f, k)
+        if p is not None:
+            v, m = topp_cut(f, p, T)
+            margin = min(margin, m)
+            f = np.where(f >= v, f, -np.inf)
+        return f
+
+    ft = np.array([filt(r) for r in tgt_f64])
+    fd = np.array([filt(r) for r in drf_f64]) if drf_f64 is not None and len(drf_f64) else \
+        np.zeros((0, tgt_f64.shape[1]))
+    P, Q = chain_distributions(ft, fd, T)
+    return P, Q, margin
+
+
+def filter_params(b: int, top_k, top_p):
+    """R20: (valid, k, p) of request b; k or p is None when its array is
+    absent or it cuts nothing."""
+    k = p = None
+    if top_k is not None:
+        k = int(top_k[b])
+        if k < 1:
+            return False, None, None
+    if top_p is not None:
+        p = float(np.float32(top_p[b]))
+        if not 0.0 < p <= 1.0:
+            return False, None, None
+        if p >= 1.0:
+            p = None
+    return True, k, p
+
+
+def verify_chain_filtered(target: np.ndarray, draft: Optional[np.ndarray], draft_tokens: np.ndarray,
+                          uniforms: np.ndarray, temperature: np.ndarray, dtype: str,
+                          top_k: Optional[np.ndarray] = None, top_p: Optional[np.ndarray] = None,
+                          requests=None) -> FilteredChainResult:
+    """Chain verification with p and q filtered alike by top-k and/or top-p
+    over the whole vocabulary (R20); otherwise as verify_chain."""
+    B, G1, V = target.shape
+    gamma = G1 - 1
+    out = np.full((B, gamma + 1), -1, dtype=np.int32)
+    nacc = np.full(B, -1, dtype=np.int32)
+    margins = np.full(B, np.inf)
+    decisions: List[List[Decision]] = [[] for _ in range(B)]
+    todo = range(B) if requests is None else requests
+    for b in todo:
+        T = float(np.float32(temperature[b]))
+        toks = np.asarray(draft_tokens[b], dtype=np.int64)
+        u = np.asarray(uniforms[b], dtype=np.float32)
+        if _request_invalid(toks, u, T, V):
+            continue
+        tgt = logits_to_f64(target[b], dtype)
+        if T > 0.0:
+            ok, k, p = filter_params(b, top_k, top_p)
+            if not ok:
+                continue
+            drf = logits_to_f64(draft[b], dtype) if gamma > 0 else None
+            P, Q, margins[b] = filtered_distributions(tgt, drf, T, k, p)
+        else:
+            P, Q = None, None
+        emitted, n, dec = chain_decide_request(P, Q, tgt, toks, u, T)
+        out[b, :len(emitted)] = emitted
+        nacc[b] = n
+        decisions[b] = dec
+    return FilteredChainResult(out, nacc, decisions, margins)
 
 
 def verify_chain_topk(target: np.ndarray, draft: Optional[np.ndarray], draft_tokens: np.ndarray,
