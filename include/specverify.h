@@ -174,6 +174,48 @@ SV_API int spec_verify_chain_noalloc(const void* target_logits, const void* draf
                               int32_t* out_tokens, int32_t* out_num_accepted, void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * Chain verification under a general consistent filter: top-k and/or top-p
+ * over the whole vocabulary (close-reading notes 02, section 5.4: a decoding
+ * rule applied alike to p and q keeps the method exact for the filtered
+ * target).
+ *
+ * Every target and draft row of a sampling request is cut alike before the
+ * temperature softmax, and the logits below its cut count as -inf:
+ *  - top-k: the cut is the row's min(k, V)-th largest logit (every logit
+ *    equal to it stays);
+ *  - top-p: over what top-k kept (the whole row without top-k), with r the
+ *    temperature softmax of those logits, the cut rises to the largest kept
+ *    logit v whose mass, the sum of r over the kept logits >= v, reaches p.
+ * p' and q' are the softmax of the cut rows; the test, the residual draw
+ * from norm(max(0, p' - q')) and the bonus draw from p' are those of
+ * spec_verify_chain, so the draft tokens must come from the cut q'.  A draft
+ * token below its draft row's cut has q' = 0 and is accepted.  Greedy
+ * requests (T == 0) ignore both filters.  Unlike spec_verify_chain_topk, no
+ * limit applies to k or to the number of logits a row keeps.
+ *
+ * The arguments are spec_verify_chain's, plus
+ * top_k   [B]  int32  optional (NULL: no top-k): k >= 1 of each request;
+ *                     k >= V keeps the whole row
+ * top_p   [B]  float  optional (NULL: no top-p): p in (0, 1]; 1 cuts nothing
+ * and draft_logits is required whenever gamma > 0.  A sampling request with
+ * k < 1 or p outside (0, 1] is invalid (count -1, tokens -1).
+ * Precision: the top-p masses are fp32 exponentials summed in fp64, so a cut
+ * can differ from an exact one only where p lies within about 1e-7 of the
+ * mass at the cut.  Work: one launch of one 512-thread workgroup per row of
+ * the sampling requests (searches over the row's keys, about eight passes
+ * per filter for bf16 logits, sixteen for fp32, all but the first through
+ * the caches), then the chain launch of spec_verify_chain with the cuts
+ * applied wherever a row is read.  Same workspace query as
+ * spec_verify_chain.  Returns an sv_status.
+ * ---------------------------------------------------------------------- */
+SV_API int spec_verify_chain_filtered(const void* target_logits, const void* draft_logits,
+                               const int32_t* draft_tokens, const float* uniforms,
+                               const float* temperature, const int32_t* top_k, const float* top_p,
+                               int B, int gamma, int V, int dtype, int32_t* out_tokens,
+                               int32_t* out_num_accepted, void* workspace, size_t workspace_bytes,
+                               void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * Chain verification with a scheduling hint (close-reading notes 02,
  * section 4, as spec_verify_chain).
  *
@@ -450,7 +492,8 @@ typedef enum {
   SV_K_TREE_MSS = 13,         /* tree: multi-step speculative sampling, one launch */
   SV_K_TOPK_ROWS = 14,        /* chain under top-k: each row's max, threshold and kept logits */
   SV_K_TOPK_DECIDE = 15,      /* chain under top-k: accept tests and draws over the kept logits */
-  SV_K_COUNT = 16
+  SV_K_FILTER_ROWS = 16,      /* filtered chain: the top-k / top-p cut of every sampling row */
+  SV_K_COUNT = 17
 } sv_kernel;
 
 /* Name of a kernel id (static storage; "unknown" outside [0, SV_K_COUNT)). */

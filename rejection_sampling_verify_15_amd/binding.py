@@ -38,6 +38,8 @@ EXPORTS = {
                                   [ctypes.c_void_p] * 3),
     "spec_verify_chain_hinted": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 +
                                  [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "spec_verify_chain_filtered": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 4 +
+                                   [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]),
     "spec_verify_chain_ragged": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 +
                                  [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
     "sv_chain_topk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
@@ -60,7 +62,7 @@ EXPORTS = {
                                      ctypes.c_int]),
     "sv_set_test_hook": (ctypes.c_int, [ctypes.c_int, ctypes.c_longlong]),
 }
-SV_K_COUNT = 16
+SV_K_COUNT = 17
 
 _LIB = None
 _LOCK = threading.Lock()
@@ -265,6 +267,55 @@ def verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_toke
                              _ptr(temperature), B, gamma, V, dt, _ptr(out_tokens),
                              _ptr(out_num_accepted), _ptr(ws), ws.numel(), _stream_handle(dev))
     _check(st, "spec_verify_chain")
+    return out_tokens, out_num_accepted
+
+
+def verify_chain_filtered(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: torch.Tensor,
+                          uniforms: torch.Tensor, temperature: torch.Tensor,
+                          top_k: Optional[torch.Tensor] = None, top_p: Optional[torch.Tensor] = None,
+                          out_tokens: Optional[torch.Tensor] = None,
+                          out_num_accepted: Optional[torch.Tensor] = None,
+                          ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """spec_verify_chain_filtered over device tensors: the chain call with p
+    and q cut alike by top-k (top_k [B] int32) and/or top-p (top_p [B] fp32)
+    over the whole vocabulary.  Shapes as verify_chain; draft is required
+    when gamma > 0."""
+    _need_cuda(target, "target")
+    if target.dim() != 3:
+        raise ValueError("target must be [B, gamma+1, V]")
+    B, G1, V = target.shape
+    gamma = G1 - 1
+    dev = target.device
+    dt = _dtype_code(target)
+    if gamma > 0:
+        if draft is None:
+            raise ValueError("draft is required when gamma > 0")
+        _need_cuda(draft, "draft")
+        if draft.dtype != target.dtype or tuple(draft.shape) != (B, gamma, V):
+            raise ValueError("draft must match target's dtype with shape [B, gamma, V]")
+    checks = [("draft_tokens", draft_tokens, (B, gamma), torch.int32),
+              ("uniforms", uniforms, (B, gamma + 1), torch.float32),
+              ("temperature", temperature, (B,), torch.float32)]
+    if top_k is not None:
+        checks.append(("top_k", top_k, (B,), torch.int32))
+    if top_p is not None:
+        checks.append(("top_p", top_p, (B,), torch.float32))
+    for name, t, shape, dtype in checks:
+        _need_cuda(t, name)
+        if tuple(t.shape) != shape or t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype} with shape {shape}")
+    if out_tokens is None:
+        out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    L = lib()
+    if ws is None:
+        ws = workspace(L.sv_chain_workspace_bytes(B, gamma, V, dt), dev)
+    st = L.spec_verify_chain_filtered(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
+                                      _ptr(temperature), _ptr(top_k), _ptr(top_p), B, gamma, V, dt,
+                                      _ptr(out_tokens), _ptr(out_num_accepted), _ptr(ws), ws.numel(),
+                                      _stream_handle(dev))
+    _check(st, "spec_verify_chain_filtered")
     return out_tokens, out_num_accepted
 
 

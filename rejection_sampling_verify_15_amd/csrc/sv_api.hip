@@ -58,7 +58,7 @@ extern "C" const char* sv_kernel_name(int kernel) {
   static const char* const names[SV_K_COUNT] = {
       "chain_verify", "chain_stream", "chain_decide", "chain_units", "tree_init", "tree_node_pass",
       "tree_choose", "probs_row_stats", "probs_residual", "probs_finalize", "fill_zero", "tree_verify",
-      "tree_mask", "tree_mss", "topk_rows", "topk_decide"};
+      "tree_mask", "tree_mss", "topk_rows", "topk_decide", "filter_rows"};
   return (kernel >= 0 && kernel < SV_K_COUNT) ? names[kernel] : "unknown";
 }
 

@@ -83,6 +83,7 @@ struct Pending {
   float u;        // u[b][gamma]
   float t;        // temperature
   float mt, md;   // maxima of the draw's target row and of draft row n
+  uint32_t thr_t, thr_d;  // their filter thresholds (stored keys; 0: none)
   int32_t pad;
   double zt, zd;  // their fp64-merged pass-1 normalisers
 };
@@ -133,6 +134,9 @@ struct ChainArgs {
   const int32_t* gammas; // [B] draft length of each request (ragged calls), or NULL: all gamma
   float* out_tau;        // [B][gamma] tau of each test taken, -1 elsewhere; or NULL
   uint32_t spin;         // poll bound of every wait (kSpinLimit unless a test lowers it)
+  const uint32_t* thr;   // [B][2*gamma+1] filter thresholds of a filtered call (key + 1, 0: none), or NULL
+  const int32_t* top_k;  // [B] of a filtered call, or NULL
+  const float* top_p;    // [B] of a filtered call, or NULL
   ChainPlan plan;        // block layout of a hinted call
 };
 
@@ -381,6 +385,10 @@ __device__ inline void pad_tail(Raw& raw, int c0, int c1) {
 
 template <int DT, bool VEC, int NT>
 __device__ inline void stream_reduce_any(const ChainArgs& a, const RowItem& r, StreamItem<DT, VEC, NT>& it) {
+  if (a.thr && it.t > 0.0f) {  // a filtered call: the row's cut applies to the sampling rows
+    const uint32_t stored = a.thr[static_cast<size_t>(r.b) * (2 * a.gamma + 1) + r.k];
+    if (stored) it.raw.mask_below(stored_threshold(stored));
+  }
   const int c0 = r.c * kRowChunk;
   pad_tail<DT, VEC>(it.raw, c0, min(a.V, c0 + kRowChunk));
   stream_reduce<DT, VEC, NT>(a, r, it);
@@ -482,11 +490,25 @@ __device__ void decide_request(const ChainArgs& a, int b) {
     bad |= !(u >= 0.0f && u < 1.0f);
   }
   if (sampling && Gb > 0 && a.draft == nullptr) bad = 1;
-  // the logits of the draft tokens in target row i and draft row i
+  if (sampling && a.top_k && a.top_k[b] < 1) bad = 1;
+  if (sampling && a.top_p) {
+    const float pp = a.top_p[b];
+    if (!(pp > 0.0f && pp <= 1.0f)) bad = 1;
+  }
+  // a filtered call: the cut of target row i (lane i <= Gb) and draft row i (lane i < Gb)
+  uint32_t thr_t = 0, thr_d = 0;
+  if (sampling && a.thr) {
+    if (lane <= Gb) thr_t = a.thr[static_cast<size_t>(b) * R + lane];
+    if (lane < Gb) thr_d = a.thr[static_cast<size_t>(b) * R + G + 1 + lane];
+  }
+  // the logits of the draft tokens in target row i and draft row i (-inf
+  // below a cut)
   float xt = 0.0f, xd = 0.0f;
   if (sampling && lane < Gb && x >= 0 && x < a.V) {
     xt = Elem<DT>::at(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + lane, a.V), x);
     if (a.draft != nullptr) xd = Elem<DT>::at(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + lane, a.V), x);
+    if (xt < stored_threshold(thr_t)) xt = -INFINITY;
+    if (xd < stored_threshold(thr_d)) xd = -INFINITY;
   }
   // every partial of the needed rows, whatever the verdict: they are all
   // written, and returned to zero below
@@ -597,9 +619,11 @@ __device__ void decide_request(const ChainArgs& a, int b) {
       d.t = T;
       d.mt = s_m[n];
       d.zt = s_z[n];
+      d.thr_t = static_cast<uint32_t>(read_lane(static_cast<int>(thr_t), n));
       if (n < Gb) {
         d.md = s_m[Gb + 1 + n];
         d.zd = s_z[Gb + 1 + n];
+        d.thr_d = static_cast<uint32_t>(read_lane(static_cast<int>(thr_d), n));
       }
     }
     publish_pending(a.pending + b, d);
@@ -619,12 +643,15 @@ __device__ void decide_request(const ChainArgs& a, int b) {
     if (write) a.out_tokens[static_cast<size_t>(b) * (G + 1) + lane] = v;
   }
   if (lane == 0 && !drawing) a.out_n[b] = any_lost ? SV_GAVE_UP : n;
-  // the workspace words of this request back to zero
+  // the workspace words of this request back to zero (the cuts travel in
+  // the decision, so no one reads them after this item)
   uint64_t* pz = a.partials + static_cast<size_t>(b) * R * a.nchunk;
   for (int i = lane; i < nrows * a.nchunk; i += kWave) {
     const int r = i / a.nchunk;
     store_coherent(pz + static_cast<size_t>(phys_row(a, Gb, r)) * a.nchunk + (i - r * a.nchunk), 0ull);
   }
+  if (a.thr)
+    for (int i = lane; i < R; i += kWave) const_cast<uint32_t*>(a.thr)[static_cast<size_t>(b) * R + i] = 0u;
   if (kDraws && drawing) {
     // the draw runs beside other requests' units: let this wave issue first
     __builtin_amdgcn_s_setprio(3);
@@ -824,6 +851,8 @@ __device__ bool draw_token(const ChainArgs& a, int b, const Pending& d, bool zer
   Raw st, sd;
   st.load(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + trow, a.V), c0, c1);
   if (residual) sd.load(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + d.n, a.V), c0, c1);
+  if (d.thr_t) st.mask_below(stored_threshold(d.thr_t));
+  if (residual && d.thr_d) sd.mask_below(stored_threshold(d.thr_d));
   pad_tail<DT, VEC>(st, c0, c1);
   if (residual) pad_tail<DT, VEC>(sd, c0, c1);
   int hit = 0x7fffffff;
@@ -935,6 +964,8 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit) {
     Raw st, sd;
     st.load(row_ptr<DT>(a.target, static_cast<size_t>(b) * (G + 1) + trow, a.V), c0, c1);
     if (residual) sd.load(row_ptr<DT>(a.draft, static_cast<size_t>(b) * G + d.n, a.V), c0, c1);
+    if (d.thr_t) st.mask_below(stored_threshold(d.thr_t));
+    if (residual && d.thr_d) sd.mask_below(stored_threshold(d.thr_d));
     pad_tail<DT, VEC>(st, c0, c1);
     // one group at a time: group j sits in group 0 of the slices after j shifts
     if (residual) {
@@ -1235,7 +1266,7 @@ __global__ __launch_bounds__(kWave) void chain_units(ChainArgs a) {
 // host side
 // ---------------------------------------------------------------------------
 struct ChainLayout {
-  size_t partials, pending, units, counters, total;
+  size_t partials, pending, units, counters, thr, total;
 };
 
 static int units_for(int V, int span) { return (V + span - 1) / span; }
@@ -1251,6 +1282,7 @@ static ChainLayout chain_layout(int B, int gamma, int V) {
   L.pending = off;  off = align_up(off + static_cast<size_t>(B) * sizeof(PendingWire));
   L.units = off;    off = align_up(off + static_cast<size_t>(B) * nunit * sizeof(UnitRec));
   L.counters = off; off = align_up(off + static_cast<size_t>(B) * kCounterStride * sizeof(uint32_t));
+  L.thr = off;      off = align_up(off + static_cast<size_t>(B) * R * sizeof(uint32_t));
   L.total = off;
   return L;
 }
@@ -1383,7 +1415,8 @@ static int chain_entry(const void* target_logits, const void* draft_logits, cons
                        const float* uniforms, const float* temperature, const int32_t* gammas, int B, int gamma,
                        int V, int dtype, int32_t* out_tokens, int32_t* out_num_accepted, float* out_tau,
                        void* workspace, size_t workspace_bytes, void* hip_stream,
-                       const uint8_t* sampling_hint = nullptr) {
+                       const uint8_t* sampling_hint = nullptr, const int32_t* top_k = nullptr,
+                       const float* top_p = nullptr, bool filtered = false) {
   const int chk = chain_check(target_logits, draft_logits, draft_tokens, uniforms, temperature, B, gamma, V, dtype,
                               out_tokens, out_num_accepted);
   if (chk != SV_OK || B == 0) return chk;
@@ -1410,6 +1443,11 @@ static int chain_entry(const void* target_logits, const void* draft_logits, cons
   a.gammas = gammas;
   a.out_tau = gamma > 0 ? out_tau : nullptr;
   a.spin = spin_limit(kSpinLimit);
+  if (filtered) {
+    a.thr = reinterpret_cast<uint32_t*>(ws + L.thr);
+    a.top_k = top_k;
+    a.top_p = top_p;
+  }
   a.plan.nS = -1;
   if (sampling_hint && B <= SV_HINT_MAX_BATCH) {
     int s = 0;
@@ -1420,6 +1458,11 @@ static int chain_entry(const void* target_logits, const void* draft_logits, cons
       if (!sampling_hint[b]) a.plan.order[s++] = static_cast<uint8_t>(b);
   }
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (filtered) {
+    const int st = launch_filter_rows(target_logits, a.draft, temperature, top_k, top_p, B, gamma, V, dtype,
+                                      const_cast<uint32_t*>(a.thr), stream);
+    if (st != SV_OK) return st;
+  }
   const int kv = dtype == SV_BF16 ? Elem<0>::kVec : Elem<1>::kVec;
   const bool vec = (V % kv == 0) && aligned(target_logits, 16) && (!a.draft || aligned(a.draft, 16));
   if (dtype == SV_BF16) return vec ? launch_chain<0, true>(a, stream) : launch_chain<0, false>(a, stream);
@@ -1433,6 +1476,18 @@ extern "C" int spec_verify_chain(const void* target_logits, const void* draft_lo
                                  void* workspace, size_t workspace_bytes, void* hip_stream) {
   return chain_entry(target_logits, draft_logits, draft_tokens, uniforms, temperature, nullptr, B, gamma, V,
                      dtype, out_tokens, out_num_accepted, nullptr, workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" int spec_verify_chain_filtered(const void* target_logits, const void* draft_logits,
+                                          const int32_t* draft_tokens, const float* uniforms,
+                                          const float* temperature, const int32_t* top_k, const float* top_p,
+                                          int B, int gamma, int V, int dtype, int32_t* out_tokens,
+                                          int32_t* out_num_accepted, void* workspace, size_t workspace_bytes,
+                                          void* hip_stream) {
+  if (B > 0 && gamma > 0 && !draft_logits) return SV_ERR_NULL;
+  return chain_entry(target_logits, draft_logits, draft_tokens, uniforms, temperature, nullptr, B, gamma, V,
+                     dtype, out_tokens, out_num_accepted, nullptr, workspace, workspace_bytes, hip_stream, nullptr,
+                     top_k, top_p, top_k != nullptr || top_p != nullptr);
 }
 
 extern "C" int spec_verify_chain_hinted(const void* target_logits, const void* draft_logits,

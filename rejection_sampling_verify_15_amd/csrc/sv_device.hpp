@@ -166,6 +166,23 @@ __host__ __device__ inline double exp2_neg(double t_in) {
 }
 
 // ---------------------------------------------------------------------------
+// order-preserving keys of logits (consistent top-k / top-p thresholds)
+// ---------------------------------------------------------------------------
+// An unsigned key that orders like the float (both zeros map to +0's key, so
+// they tie, as they compare equal); NaN is not a valid logit.
+__device__ inline uint32_t order_key(float x) {
+  const uint32_t u = x == 0.0f ? 0u : __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// A stored row threshold: 0 means no filter, otherwise key + 1.
+__device__ inline float stored_threshold(uint32_t stored) {
+  return stored ? key_value(stored - 1u) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
 // raw (still packed) slices for prefetching
 // ---------------------------------------------------------------------------
 // The element layout of Slice (for NT threads), kept as loaded (16-byte words, or single
@@ -207,6 +224,26 @@ struct RawSlice {
     for (int j = 0; j + 1 < ITEMS; ++j)
 #pragma unroll
       for (int q = 0; q < (VEC ? 4 : 1); ++q) w[j][q] = w[j + 1][q];
+  }
+
+  // Every element below `thr` becomes -inf (a consistent top-k / top-p
+  // filter applied to the loaded words).
+  __device__ inline void mask_below(float thr) {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j)
+#pragma unroll
+      for (int q = 0; q < (VEC ? 4 : 1); ++q) {
+        const uint32_t v = w[j][q];
+        if constexpr (DT == 0 && VEC) {
+          const uint32_t lo = __uint_as_float(v << 16) < thr ? 0xff80u : (v & 0xffffu);
+          const uint32_t hi = __uint_as_float(v & 0xffff0000u) < thr ? 0xff800000u : (v & 0xffff0000u);
+          w[j][q] = hi | lo;
+        } else if constexpr (DT == 0) {
+          w[j][q] = __uint_as_float(v << 16) < thr ? 0xff80u : v;
+        } else {
+          w[j][q] = __uint_as_float(v) < thr ? 0xff800000u : v;
+        }
+      }
   }
 
   // Element e of group j as float (no range check).

@@ -17,6 +17,12 @@ inline bool aligned(const void* p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }
 
+// The thresholds of a filtered chain call (sv_filter.hip): one launch over
+// the rows of the sampling requests, writing thr[b][row] = key + 1 of each
+// cut (0: none).  Returns an sv_status.
+int launch_filter_rows(const void* target, const void* draft, const float* temperature, const int32_t* top_k,
+                       const float* top_p, int B, int gamma, int V, int dtype, uint32_t* thr, hipStream_t stream);
+
 // Value of a test control (sv_set_test_hook); 0 when unset.
 long long test_hook(int hook);
 

@@ -238,3 +238,59 @@ def oracle_chain_many(ci, u_sets, requests=None):
             r.num_accepted[b] = n
             r.decisions[b] = dec
     return results
+
+
+# ---------------------------------------------------------------------------
+# the filtered chain (consistent top-k / top-p over the whole vocabulary)
+# ---------------------------------------------------------------------------
+def oracle_filtered_many(ci, u_sets, top_k=None, top_p=None):
+    """Oracle results of the filtered chain for each uniform set, computing
+    every request's filtered distributions once.  Each result carries the
+    smallest top-p cut margin of each request."""
+    import oracle
+    from oracle import specverify_oracle as so
+
+    B, G = ci.B, ci.gamma
+    results = [so.FilteredChainResult(np.full((B, G + 1), -1, dtype=np.int32), np.full(B, -1, dtype=np.int32),
+                                      [[] for _ in range(B)], np.full(B, np.inf)) for _ in u_sets]
+    for b in range(B):
+        T = float(np.float32(ci.temperature[b]))
+        toks = np.asarray(ci.draft_tokens[b], dtype=np.int64)
+        if so._request_invalid(toks, u_sets[0][b], T, ci.V):
+            continue
+        tgt = so.logits_to_f64(ci.target[b], ci.dtype)
+        margin = np.inf
+        if T > 0.0:
+            ok, k, p = so.filter_params(b, top_k, top_p)
+            if not ok:
+                continue
+            drf = so.logits_to_f64(ci.draft[b], ci.dtype) if G > 0 else None
+            P, Q, margin = so.filtered_distributions(tgt, drf, T, k, p)
+        else:
+            P = Q = None
+        for s, u in enumerate(u_sets):
+            emitted, n, dec = oracle.chain_decide_request(P, Q, tgt, toks, np.asarray(u[b], dtype=np.float32), T)
+            r = results[s]
+            r.out_tokens[b, :len(emitted)] = emitted
+            r.num_accepted[b] = n
+            r.decisions[b] = dec
+            r.cut_margin[b] = margin
+    return results
+
+
+def compare_filtered(res, tok_gpu, n_gpu) -> Tally:
+    """compare_chain, where a request whose top-p cut lies within the window
+    of p counts its decisions as in-window: a disagreement there is a
+    boundary mismatch, not a hard failure."""
+    tally = Tally()
+    near = [b for b in range(len(n_gpu)) if res.cut_margin[b] < WINDOW]
+    far = [b for b in range(len(n_gpu)) if res.cut_margin[b] >= WINDOW]
+    tally.add(compare_chain(res, tok_gpu, n_gpu, requests=far))
+    for b in near:
+        t = compare_chain(res, tok_gpu, n_gpu, requests=[b])
+        t.in_window += t.decisions - t.in_window
+        if t.hard:
+            t.mismatches += 1
+            t.hard = []
+        tally.add(t)
+    return tally

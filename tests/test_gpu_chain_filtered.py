@@ -1,0 +1,188 @@
+"""GPU parity of spec_verify_chain_filtered (consistent top-k and/or top-p
+over the whole vocabulary) against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import specverify_oracle as so
+import synth
+import rejection_sampling_verify_15_amd as sv
+from parity import (Tally, assert_shared_workspace_zero, compare_chain, compare_filtered, oracle_filtered_many,
+                    to_device, to_device_logits)
+
+pytestmark = pytest.mark.gpu
+
+
+def filtered_draft_tokens(ci, top_k, top_p, seed):
+    """Draft tokens of a draft model decoding with the same filter: Gumbel-max
+    over each cut draft row (argmax for greedy requests)."""
+    rng = np.random.default_rng(seed)
+    toks = np.empty((ci.B, ci.gamma), np.int32)
+    for b in range(ci.B):
+        T = float(np.float32(ci.temperature[b]))
+        d = so.logits_to_f64(ci.draft[b], ci.dtype)
+        ok, k, p = so.filter_params(b, top_k, top_p)
+        for i in range(ci.gamma):
+            if T > 0.0 and ok:
+                row = d[i]
+                if k is not None:
+                    row, _ = so.topk_filter(row, k)
+                if p is not None:
+                    v, _ = so.topp_cut(row, p, T)
+                    row = np.where(row >= v, row, -np.inf)
+                toks[b, i] = int(np.argmax(row / T + rng.gumbel(size=ci.V)))
+            else:
+                toks[b, i] = int(np.argmax(d[i]))
+    return toks
+
+
+def run_filtered(ci, top_k, top_p, u_sets, ws=None):
+    tgt = to_device_logits(ci.target, ci.dtype)
+    drf = to_device_logits(ci.draft, ci.dtype) if ci.gamma > 0 else None
+    tok = to_device(ci.draft_tokens.astype(np.int32))
+    T = to_device(ci.temperature.astype(np.float32))
+    kd = None if top_k is None else to_device(np.asarray(top_k, np.int32))
+    pd = None if top_p is None else to_device(np.asarray(top_p, np.float32))
+    outs = []
+    for u in u_sets:
+        ot, on = sv.verify_chain_filtered(tgt, drf, tok, to_device(np.asarray(u, np.float32)), T, kd, pd, ws=ws)
+        outs.append((ot.cpu().numpy(), on.cpu().numpy()))
+    if ws is None:
+        assert_shared_workspace_zero("chain filtered")
+    else:
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
+    return outs
+
+
+def filtered_parity(ci, top_k, top_p, n_sets, label, seed=3, ws=None):
+    u_sets = [ci.uniforms] + [ci.fresh_uniforms(seed * 1000 + s) for s in range(n_sets - 1)]
+    print(f"[{label}] B={ci.B} gamma={ci.gamma} V={ci.V} dtype={ci.dtype} sets={n_sets}", flush=True)
+    gpu = run_filtered(ci, top_k, top_p, u_sets, ws)
+    refs = oracle_filtered_many(ci, u_sets, top_k, top_p)
+    tally = Tally()
+    for (ot, on), ref in zip(gpu, refs):
+        tally.add(compare_filtered(ref, ot, on))
+    near = int((refs[0].cut_margin < 1e-5).sum())
+    print(f"[{label}] {tally} requests with a cut within 1e-5: {near}", flush=True)
+    tally.check(label)
+    return gpu, refs
+
+
+def batched_with(top_k, top_p, seed):
+    ci = synth.batched_chain()
+    ci.draft_tokens = filtered_draft_tokens(ci, top_k, top_p, seed)
+    return ci
+
+
+def test_topp_alone_batched_shape():
+    """B=64, gamma=4, V=128256 bf16 (even requests T=0.7, odd greedy), p=0.9
+    over the whole vocabulary, drafts drawn from the cut draft rows."""
+    p = np.full(64, 0.9, np.float32)
+    ci = batched_with(None, p, 16501)
+    gpu, refs = filtered_parity(ci, None, p, 3, "top-p 0.9 batched")
+    assert (gpu[0][1] >= 0).all()
+
+
+def test_topk_1024_batched_shape():
+    k = np.full(64, 1024, np.int32)
+    ci = batched_with(k, None, 16502)
+    filtered_parity(ci, k, None, 3, "top-k 1024 batched")
+
+
+def test_topk_1024_then_topp_batched_shape():
+    k = np.full(64, 1024, np.int32)
+    p = np.full(64, 0.8, np.float32)
+    ci = batched_with(k, p, 16503)
+    filtered_parity(ci, k, p, 3, "top-k 1024 + top-p 0.8 batched")
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 20001), ("bf16", 16384), ("f32", 9999), ("f32", 8192)])
+def test_small_many_rounds(dtype, V):
+    """Random k (1..3000 or none) and p (0.2..1 or none) per request, vector
+    and scalar paths, many uniform sets."""
+    ci = synth.chain_inputs(16510 + V % 97, B=16, gamma=3, V=V, dtype=dtype, family="gauss",
+                            draft_sigma=(0.3, 1.5), temperature=1.0, greedy_odd=False)
+    rng = np.random.default_rng(16511)
+    k = rng.integers(1, 3001, size=ci.B).astype(np.int32)
+    k[::4] = V + 7                                         # no top-k cut
+    p = rng.choice(np.array([0.2, 0.5, 0.9, 0.97, 1.0], np.float32), size=ci.B)
+    ci.draft_tokens = filtered_draft_tokens(ci, k, p, 16512)
+    filtered_parity(ci, k, p, 12, f"filtered {dtype} V={V}")
+
+
+def test_ties_and_masked_logits():
+    """Rows with many equal logits straddling the cuts, and -inf entries."""
+    ci = synth.chain_inputs(16520, B=12, gamma=3, V=4096, dtype="f32", family="gauss",
+                            draft_sigma=0.5, temperature=0.9)
+    rng = np.random.default_rng(16521)
+    for arr in (ci.target, ci.draft):
+        arr[...] = np.round(arr * 2.0) / 2.0                # few distinct values: ties everywhere
+        arr[:, :, rng.integers(0, ci.V, size=300)] = -np.inf
+    k = np.array([1, 2, 5, 40, 300, 1000, 4000, 17, 64, 3, 128, 9], np.int32)
+    p = np.array([1.0, 0.5, 0.9, 0.3, 0.95, 0.7, 0.99, 1.0, 0.6, 0.8, 0.4, 0.05], np.float32)
+    ci.draft_tokens = filtered_draft_tokens(ci, k, p, 16522)
+    filtered_parity(ci, k, p, 10, "filtered ties")
+
+
+def test_invalid_filters_and_greedy():
+    ci = synth.chain_inputs(16530, B=10, gamma=2, V=3000, dtype="bf16", family="peaked",
+                            draft_sigma=0.5, temperature=1.0)
+    ci.temperature[8:] = 0.0
+    k = np.array([0, -1, 5, 5, 5, 5, 50, 50, 0, 50], np.int32)
+    p = np.array([0.9, 0.9, 0.0, 1.5, np.nan, 0.9, 0.9, 1.0, 0.9, -1.0], np.float32)
+    gpu, refs = filtered_parity(ci, k, p, 2, "filtered invalid")
+    ot, on = gpu[0]
+    assert (on[[0, 1, 2, 3, 4]] == -1).all() and (ot[[0, 1, 2, 3, 4]] == -1).all()
+    assert (on[5:] >= 0).all()
+
+
+def test_top1_with_argmax_drafts_is_greedy():
+    ci = synth.chain_inputs(16540, B=20, gamma=4, V=5000, dtype="f32", family="gauss",
+                            draft_sigma=(0.1, 1.0), temperature=0.9)
+    ci.draft_tokens = np.argmax(ci.draft, axis=2).astype(np.int32)
+    gpu = run_filtered(ci, np.ones(ci.B, np.int32), None, [ci.uniforms])
+    tgt = to_device_logits(ci.target, ci.dtype)
+    drf = to_device_logits(ci.draft, ci.dtype)
+    gt, gn = sv.verify_chain(tgt, drf, to_device(ci.draft_tokens), to_device(ci.uniforms),
+                             to_device(np.zeros(ci.B, np.float32)))
+    assert np.array_equal(gpu[0][0], gt.cpu().numpy()) and np.array_equal(gpu[0][1], gn.cpu().numpy())
+
+
+def test_no_cut_is_the_plain_call():
+    """No filter array, k >= V or p = 1: the plain call's outputs, bit for bit."""
+    ci = synth.chain_inputs(16550, B=16, gamma=3, V=30000, dtype="bf16", family="zipf",
+                            draft_sigma=0.8, temperature=1.0, greedy_odd=True)
+    tgt = to_device_logits(ci.target, ci.dtype)
+    drf = to_device_logits(ci.draft, ci.dtype)
+    tok = to_device(ci.draft_tokens)
+    T = to_device(ci.temperature)
+    for s in range(3):
+        u = to_device(ci.uniforms if s == 0 else ci.fresh_uniforms(16551 + s))
+        pt, pn = sv.verify_chain(tgt, drf, tok, u, T)
+        plain = (pt.cpu().numpy(), pn.cpu().numpy())
+        for kw in ({}, {"top_k": to_device(np.full(ci.B, 30000, np.int32))},
+                   {"top_p": to_device(np.ones(ci.B, np.float32))}):
+            ft, fn = sv.verify_chain_filtered(tgt, drf, tok, u, T, **kw)
+            assert np.array_equal(ft.cpu().numpy(), plain[0]) and np.array_equal(fn.cpu().numpy(), plain[1]), kw
+    assert_shared_workspace_zero("filtered no cut")
+
+
+def test_three_launch_form_and_counted_draws():
+    """The cuts reach the persistent stream kernel of the three-launch form,
+    and the counted draws of batches over 256 requests."""
+    p = None
+    ci = synth.chain_inputs(16560, B=20, gamma=3, V=25000, dtype="bf16", family="peaked",
+                            draft_sigma=0.6, temperature=1.0)
+    k = np.full(ci.B, 700, np.int32)
+    p = np.full(ci.B, 0.85, np.float32)
+    ci.draft_tokens = filtered_draft_tokens(ci, k, p, 16561)
+    with sv.library_control(sv.SV_HOOK_CHAIN_SPLIT, 1):
+        filtered_parity(ci, k, p, 4, "filtered three launches")
+    big = synth.chain_inputs(16562, B=300, gamma=2, V=3000, dtype="bf16", family="gauss",
+                             draft_sigma=(0.3, 1.5), temperature=1.0, greedy_odd=True)
+    kb = np.full(big.B, 200, np.int32)
+    pb = np.full(big.B, 0.9, np.float32)
+    big.draft_tokens = filtered_draft_tokens(big, kb, pb, 16563)
+    filtered_parity(big, kb, pb, 2, "filtered B=300")
