@@ -22,10 +22,10 @@ latency case (B=1, V=32000, also replayed from a HIP graph), the deep case
 (B=256, gamma=8, V=151936, Zipf logits), the batched inputs as a ragged call
 (request b drafts 1 + b % 4 tokens; rows are the rounds' own rows), the
 batched inputs under a consistent top-k filter (k=50 on p and q), the
-token-tree cases (B=32, 64
-nodes, greedy, naive sampling or multi-step speculative sampling; rows are
-node rows) and the tree attention mask builder on the same tree shape (rows
-are mask rows).
+batched inputs under consistent top-p 0.9 over the whole vocabulary
+(spec_verify_chain_filtered), the token-tree cases (B=32, 64 nodes, greedy,
+naive sampling or multi-step speculative sampling; rows are node rows) and
+the tree attention mask builder on the same tree shape (rows are mask rows).
 """
 from __future__ import annotations
 
@@ -93,9 +93,10 @@ def stored_traffic(kernel: str):
 
 
 TOPK = 50                        # k of every sampling request in the top-k workload
+TOPP = 0.9                       # p of every sampling request in the top-p workload
 
 
-WORKLOADS = ("batched", "single", "deep", "ragged", "topk", "tree-greedy", "tree-sampling", "tree-mss", "tree-mask")
+WORKLOADS = ("batched", "single", "deep", "ragged", "topk", "topp", "tree-greedy", "tree-sampling", "tree-mss", "tree-mask")
 
 
 def percentiles(xs):
@@ -146,6 +147,12 @@ def chain_case(name, synth):
         return ci, ("consistent top-k chain verify: the batched inputs (B=64, gamma=4, V=128256, bf16, even "
                     f"requests T=0.7, odd greedy), p and q of every sampling request filtered to k={TOPK}, "
                     "draft tokens drawn from the filtered draft rows")
+    if name == "topp":
+        ci = synth.batched_chain()
+        ci.draft_tokens = synth.topp_draft_tokens(ci, np.full(ci.B, TOPP, np.float32), 52_000)
+        return ci, ("consistent top-p chain verify over the whole vocabulary: the batched inputs (B=64, gamma=4, "
+                    f"V=128256, bf16, even requests T=0.7, odd greedy), p and q of every sampling request cut to "
+                    f"their top-p={TOPP} mass, draft tokens drawn from the cut draft rows")
     if name == "single":
         return synth.single_chain(), ("single-request chain verify: B=1, gamma=4, V=32000, bf16 logits, "
                                       "T=1, fixed logits with fresh uniforms every call (latency)")
@@ -171,8 +178,11 @@ def run_chain(args, torch, synth, sv):
     out_t = torch.empty((ci.B, ci.gamma + 1), dtype=torch.int32, device=dev)
     out_n = torch.empty((ci.B,), dtype=torch.int32, device=dev)
     topk = args.workload == "topk"
-    ws_bytes = (sv.lib().sv_chain_topk_workspace_bytes if topk else sv.lib().sv_chain_workspace_bytes)(
-        ci.B, ci.gamma, ci.V, sv.SV_BF16)
+    topp = args.workload == "topp"
+    pp_d = torch.from_numpy(np.full(ci.B, TOPP, np.float32)).to(dev) if topp else None
+    ws_query = (sv.lib().sv_chain_topk_workspace_bytes if topk else
+                sv.lib().sv_chain_filtered_workspace_bytes if topp else sv.lib().sv_chain_workspace_bytes)
+    ws_bytes = ws_query(ci.B, ci.gamma, ci.V, sv.SV_BF16)
     ws = sv.workspace(ws_bytes, dev)
     stream = torch.cuda.current_stream(dev)
     ragged = args.workload == "ragged"
@@ -193,6 +203,9 @@ def run_chain(args, torch, synth, sv):
             sv.verify_chain_ragged(t, d, tok, u_sets[i % n_u], T, gam_d, ws=ws)
         elif topk:
             sv.verify_chain_topk(t, d, tok, u_sets[i % n_u], T, k_d, top_p=p_d, ws=ws)
+        elif topp:
+            sv.verify_chain_filtered(t, d, tok, u_sets[i % n_u], T, None, pp_d, out_tokens=out_t,
+                                     out_num_accepted=out_n, ws=ws)
         else:
             sv.verify_chain(t, d, tok, u_sets[i % n_u], T, out_tokens=out_t, out_num_accepted=out_n, ws=ws,
                             sampling_hint=hint)
@@ -213,14 +226,25 @@ def run_chain(args, torch, synth, sv):
     rd, sm = read_bytes(ci, gam), small_bytes(ci)
     call_us = 1e3 * total_ms / args.steps
     dominant = "topk_rows" if topk else "chain_verify"
+    rd_kernel = rd   # algorithmic bytes of one launch of the dominant kernel
+    if topp and kt.ms["filter_rows"] > kt.ms["chain_verify"]:
+        # the cuts' launch reads the sampling requests' rows only
+        dominant = "filter_rows"
+        rd_kernel = sum((2 * ci.gamma + 1) * ci.V * 2 for b in range(ci.B) if float(ci.temperature[b]) > 0)
     k_us = kt.mean_us(dominant)
-    achieved = rd / (k_us * 1e-6) / 1e9
+    if dominant == "filter_rows":
+        # the cuts take one launch per digit: all of them together against one
+        # read of the rows they cut
+        k_us = 1e3 * kt.ms["filter_rows"] / args.steps
+    achieved = rd_kernel / (k_us * 1e-6) / 1e9
     cfg = {"workload": desc, "B": ci.B, "gamma": ci.gamma, "V": ci.V, "rotating_input_sets": R}
     if hinted:
         cfg["sampling_hint"] = "host mask of the sampling requests (spec_verify_chain_hinted)"
     if ragged:
         cfg["lengths"] = "1 + b % 4"
         cfg["rows_per_call"] = rows
+    if topp:
+        cfg["top_p"] = TOPP
     if topk:
         cfg["top_k"] = TOPK
         if p_np is not None:
@@ -230,8 +254,9 @@ def run_chain(args, torch, synth, sv):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": stored_traffic(dominant) if args.workload == "batched" else None,
-                     "kernel": dominant, "kernel_us": k_us, "algorithmic_bytes": rd},
+                     "kernel": dominant, "kernel_us": k_us, "algorithmic_bytes": rd_kernel},
         "kernels_us": {name: kt.mean_us(name) for name in kt.launches},
+        "kernels_us_per_call": {name: 1e3 * kt.ms[name] / args.steps for name in kt.launches},
         "whole_call": {"us": call_us, "us_with_kernel_events": 1e3 * events_ms / args.steps,
                        "per_call_us": percentiles(calls), "host_enqueue_us": host_us,
                        "algorithmic_bytes": rd + sm,
@@ -482,6 +507,7 @@ def oracle_units(workload, top_p):
     gam = (np.array([RAGGED_LENGTHS[b % len(RAGGED_LENGTHS)] for b in range(ci.B)], np.int32)
            if workload == "ragged" else None)
     k_np = np.full(ci.B, TOPK, np.int32) if workload == "topk" else None
+    pp_np = np.full(ci.B, TOPP, np.float32) if workload == "topp" else None
     p_np = np.full(ci.B, top_p, np.float32) if (k_np is not None and top_p is not None) else None
     u_pass = {}
 
@@ -490,7 +516,10 @@ def oracle_units(workload, top_p):
             u_pass.clear()
             u_pass[s] = ci.uniforms if s == 0 else ci.fresh_uniforms(90_000 + s)
         u, sl = u_pass[s], slice(b, b + 1)
-        if k_np is not None:
+        if pp_np is not None:
+            oracle.verify_chain_filtered(ci.target[sl], ci.draft[sl], ci.draft_tokens[sl], u[sl], ci.temperature[sl],
+                                         ci.dtype, top_p=pp_np[sl])
+        elif k_np is not None:
             oracle.verify_chain_topk(ci.target[sl], ci.draft[sl], ci.draft_tokens[sl], u[sl], ci.temperature[sl],
                                      k_np[sl], ci.dtype, top_p=None if p_np is None else p_np[sl])
         elif gam is None:

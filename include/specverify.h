@@ -199,15 +199,23 @@ SV_API int spec_verify_chain_noalloc(const void* target_logits, const void* draf
  * top_p   [B]  float  optional (NULL: no top-p): p in (0, 1]; 1 cuts nothing
  * and draft_logits is required whenever gamma > 0.  A sampling request with
  * k < 1 or p outside (0, 1] is invalid (count -1, tokens -1).
- * Precision: the top-p masses are fp32 exponentials summed in fp64, so a cut
- * can differ from an exact one only where p lies within about 1e-7 of the
- * mass at the cut.  Work: one launch of one 512-thread workgroup per row of
- * the sampling requests (searches over the row's keys, about eight passes
- * per filter for bf16 logits, sixteen for fp32, all but the first through
- * the caches), then the chain launch of spec_verify_chain with the cuts
- * applied wherever a row is read.  Same workspace query as
- * spec_verify_chain.  Returns an sv_status.
+ * Precision: bf16 rows are cut exactly: their values are counted once and
+ * every distinct value's mass is count * 2^((v - max) / T) in fp64.  fp32
+ * rows take fp32 exponentials per logit on the scale of the row maximum,
+ * summed in fp64, so an fp32 cut can differ from an exact one only where p
+ * lies within about 1e-7 of the mass at the cut.  Work: one launch finds the
+ * cuts of all rows of the sampling requests (bf16: one read of each row;
+ * fp32: one read from HBM, then one pass from the caches per further digit
+ * of each search), then the chain launch of spec_verify_chain with the cuts
+ * applied wherever a row is read.  Rows are searched in groups of at most
+ * 1024 (B times 2 gamma + 1 rows in all); a group of bf16 rows also holds
+ * at most 256 MiB of counts (about 288 KiB per row at V = 128256).  The
+ * workspace comes from sv_chain_filtered_workspace_bytes (spec_verify_chain's
+ * plus that search area), zero-filled before the first call and left
+ * zero-filled by every call.  Returns an sv_status.
  * ---------------------------------------------------------------------- */
+SV_API size_t sv_chain_filtered_workspace_bytes(int B, int gamma, int V, int dtype);
+
 SV_API int spec_verify_chain_filtered(const void* target_logits, const void* draft_logits,
                                const int32_t* draft_tokens, const float* uniforms,
                                const float* temperature, const int32_t* top_k, const float* top_p,

@@ -32,6 +32,7 @@ EXPORTS = {
     "sv_version": (ctypes.c_char_p, []),
     "sv_workspace_clear": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "sv_chain_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "sv_chain_filtered_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "spec_verify_chain": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 +
                           [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]),
     "spec_verify_chain_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 +
@@ -310,7 +311,7 @@ def verify_chain_filtered(target: torch.Tensor, draft: Optional[torch.Tensor], d
         out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
     L = lib()
     if ws is None:
-        ws = workspace(L.sv_chain_workspace_bytes(B, gamma, V, dt), dev)
+        ws = workspace(L.sv_chain_filtered_workspace_bytes(B, gamma, V, dt), dev)
     st = L.spec_verify_chain_filtered(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
                                       _ptr(temperature), _ptr(top_k), _ptr(top_p), B, gamma, V, dt,
                                       _ptr(out_tokens), _ptr(out_num_accepted), _ptr(ws), ws.numel(),

@@ -1266,13 +1266,14 @@ __global__ __launch_bounds__(kWave) void chain_units(ChainArgs a) {
 // host side
 // ---------------------------------------------------------------------------
 struct ChainLayout {
-  size_t partials, pending, units, counters, thr, total;
+  size_t partials, pending, units, counters, thr, filt, total;
 };
 
 static int units_for(int V, int span) { return (V + span - 1) / span; }
 
 // Sized for the largest draw-unit count (the smallest unit span).
-static ChainLayout chain_layout(int B, int gamma, int V) {
+// A filtered call adds the filter's search area.
+static ChainLayout chain_layout(int B, int gamma, int V, bool filtered = false, int dtype = SV_BF16) {
   ChainLayout L{};
   const size_t nchunk = static_cast<size_t>(row_chunks(V));
   const size_t R = 2 * static_cast<size_t>(gamma) + 1;
@@ -1283,6 +1284,7 @@ static ChainLayout chain_layout(int B, int gamma, int V) {
   L.units = off;    off = align_up(off + static_cast<size_t>(B) * nunit * sizeof(UnitRec));
   L.counters = off; off = align_up(off + static_cast<size_t>(B) * kCounterStride * sizeof(uint32_t));
   L.thr = off;      off = align_up(off + static_cast<size_t>(B) * R * sizeof(uint32_t));
+  L.filt = off;     off += filtered ? filter_workspace_bytes(B, gamma, V, dtype) : 0;
   L.total = off;
   return L;
 }
@@ -1395,6 +1397,13 @@ extern "C" size_t sv_chain_workspace_bytes(int B, int gamma, int V, int dtype) {
   return chain_layout(B, gamma, V).total;
 }
 
+extern "C" size_t sv_chain_filtered_workspace_bytes(int B, int gamma, int V, int dtype) {
+  if (B < 0 || B > SV_MAX_BATCH || gamma < 0 || gamma > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB ||
+      (dtype != SV_BF16 && dtype != SV_F32))
+    return 0;
+  return chain_layout(B, gamma, V, true, dtype).total;
+}
+
 // Host-side checks of a chain call that need no device (the workspace is
 // checked by chain_entry).
 static int chain_check(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
@@ -1421,7 +1430,7 @@ static int chain_entry(const void* target_logits, const void* draft_logits, cons
                               out_tokens, out_num_accepted);
   if (chk != SV_OK || B == 0) return chk;
   if (!workspace) return SV_ERR_NULL;
-  const ChainLayout L = chain_layout(B, gamma, V);
+  const ChainLayout L = chain_layout(B, gamma, V, filtered, dtype);
   if (workspace_bytes < L.total || !aligned(workspace, 256)) return SV_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   ChainArgs a{};
@@ -1460,7 +1469,7 @@ static int chain_entry(const void* target_logits, const void* draft_logits, cons
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   if (filtered) {
     const int st = launch_filter_rows(target_logits, a.draft, temperature, top_k, top_p, B, gamma, V, dtype,
-                                      const_cast<uint32_t*>(a.thr), stream);
+                                      const_cast<uint32_t*>(a.thr), ws + L.filt, stream);
     if (st != SV_OK) return st;
   }
   const int kv = dtype == SV_BF16 ? Elem<0>::kVec : Elem<1>::kVec;

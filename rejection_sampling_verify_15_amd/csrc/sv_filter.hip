@@ -1,21 +1,43 @@
 // Thresholds of the general consistent filter (top-k and/or top-p over the
 // whole vocabulary, the same rule on the target and the draft rows: the
-// close-reading notes 02, section 5.4).  One 512-thread workgroup per
-// (request, row) of a sampling request finds the row's threshold t and
-// stores order_key(t) + 1 (0: nothing is cut); the chain kernel then treats
-// every logit below t as -inf.  See include/specverify.h for the contract.
+// close-reading notes 02, section 5.4).  Every row of a sampling request gets
+// a cut t, stored as order_key(t) + 1 (0: nothing is cut); the chain kernel
+// then treats every logit below t as -inf.  See include/specverify.h for the
+// contract.
 //
-// Both cuts are searches over order-preserving keys (16-bit for bf16 logits,
-// whose keys differ only in their top half, 32-bit for fp32), four-way: each
-// pass over the row (from the caches after the first) evaluates three probe
-// keys at once, with only a block reduction, no atomics.
-//  - top-k: the largest key kt with #{keys >= kt} >= min(k, V) is the k-th
-//    largest logit (every logit equal to it is kept);
-//  - top-p: over the keys >= kt, with Z the softmax mass of those logits, the
-//    largest key kp with mass(keys >= kp) >= p * Z is the cut value v*.
-// The masses are fp32 exponentials summed in fp64, so a cut can differ from
-// an fp64 reference only where p lies within about 1e-7 of the mass at the
-// cut.
+// Two searches, one launch per group of rows:
+//  - bf16 logits (the exact-count kernel, filter_rows_bf16, below): a bf16
+//    logit has one of 65536 values, so one read of the row counting every
+//    value gives both cuts exactly, with fp64 masses per value;
+//  - fp32 logits (filter_rows): radix selections over order-preserving
+//    32-bit keys, one digit at a time (12, 12, then 8 bits).
+// The cuts, over keys that order like the logits:
+//  - top-k counts: the largest key kt with #{keys >= kt} >= min(k, V), the
+//    k-th largest logit (every logit equal to it is kept);
+//  - top-p masses over the keys >= kt: the largest key kp whose mass
+//    mass(keys >= kp) reaches p * Z, Z the mass of all those keys.  Masses
+//    are on the scale of the row maximum M (the largest logit weighs 1), so a
+//    weight underflows only where the fp64 softmax's does.
+//
+// The fp32 radix search: the first digit, the one pass that reads the rows
+// from HBM, is split over S workgroups of kSlice logits per row: each builds
+// the histogram of its slice in LDS and adds its non-empty bins into the
+// row's histogram in the workspace.  The row's last workgroup to arrive
+// (nothing waits: the others simply end) reads the merged histogram back,
+// clears it, and takes every further digit itself, one pass over the whole
+// row per digit (from the caches), each a histogram in LDS of the elements
+// whose higher digits match the prefix chosen so far and a block scan from
+// the top for the next digit.  An element's top-p weight is
+// 2^((x - M) * log2(e) / T), 2^f in fp32 times 2^n in fp64, summed in fp64.
+// With top-p alone the split first pass does not know M yet: there each
+// element adds its weight relative to the largest value of its bin, and the
+// last workgroup rescales the bins once M is known; should the top bin be
+// too wide for that (a temperature so small that its top weighs more than
+// 2^900 on the scale of M), it takes digit 0 again on the scale of M.  With
+// top-k the first pass takes counts only, and the top-p digits follow the
+// top-k ones, each a pass of the last workgroup.  These masses have fp32
+// precision per element, so an fp32 cut can differ from an fp64 reference
+// only where p lies within about 1e-7 of the mass at the cut.
 #include "sv_device.hpp"
 #include "sv_host.hpp"
 
@@ -24,6 +46,31 @@ namespace {
 
 constexpr int kFilterThreads = 512;
 constexpr int kFilterWaves = kFilterThreads / kWave;
+// Logits per workgroup of the first digit (a multiple of every vector width).
+constexpr int kSlice = 65536;
+// Rows searched together; larger batches go through the launches in groups of
+// this many rows.
+constexpr int kFilterSlots = 1024;
+constexpr int kMaxBins = 1 << 12;
+constexpr size_t kQueueBytes = 256;  // the search area starts with the bf16 item counters
+// Largest log2 weight of the top bin's largest value on the scale of M for
+// which the first launch's bin-relative weights are kept.
+constexpr double kMaxTopLog2 = 900.0;
+
+// What the workgroups of a row share in the workspace besides the histogram
+// (all zero between calls).
+struct FilterState {
+  uint32_t arrivals;  // workgroups that have added their digit-0 bins
+  uint32_t max_key;   // order key of the row maximum
+  uint32_t pad[14];
+};
+static_assert(sizeof(FilterState) == 64, "state size");
+
+struct FilterSlot {
+  FilterState st;
+  uint32_t cnt[kMaxBins];
+  double mass[kMaxBins];
+};
 
 struct FilterArgs {
   const void* target;
@@ -32,6 +79,11 @@ struct FilterArgs {
   const int32_t* top_k;  // [B] or NULL
   const float* top_p;    // [B] or NULL
   int B, gamma, V;
+  int S;                 // slices per row
+  int row0;              // first row of this group
+  int group;             // rows in this group
+  void* slots;           // per-row search areas of the group (FilterSlot, or the bf16 parts)
+  uint32_t* queue;       // bf16 item counter and exit counter
   uint32_t* thr;         // [B][2 * gamma + 1]: key + 1, 0 = no cut
 };
 
@@ -39,8 +91,8 @@ __device__ inline bool filter_temp_ok(float t) { return isfinite(t) && t >= 1.17
 
 // Search key of a logit: bf16 keys differ only in their top 16 bits.
 template <int DT>
-__device__ inline uint32_t search_key(float x) {
-  return DT == 0 ? (order_key(x) >> 16) : order_key(x);
+__device__ inline uint32_t search_key(uint32_t key) {
+  return DT == 0 ? (key >> 16) : key;
 }
 // The full key of a search key (for bf16: the low half of a bf16 value's key
 // is 0 for a positive value and 0xffff for a negative one).
@@ -49,161 +101,1002 @@ __device__ inline uint32_t full_key(uint32_t k) {
   return DT == 0 ? ((k << 16) | ((k & 0x8000u) ? 0u : 0xffffu)) : k;
 }
 
-// Visits every element of the row: fn(x) per element, vector loads where the
-// row allows them.
-template <int DT, bool VEC, typename F>
-__device__ inline void for_row(const void* row, int V, F&& fn) {
-  if constexpr (VEC) {
-    constexpr int kv = Elem<DT>::kVec;
-    const int nv = V / kv;
-#pragma unroll 4
-    for (int i = threadIdx.x; i < nv; i += kFilterThreads) {
-      float x[kv];
-      Elem<DT>::unpack(Elem<DT>::raw(row, i * kv), x);
-#pragma unroll
-      for (int e = 0; e < kv; ++e) fn(x[e]);
-    }
-  } else {
-#pragma unroll 4
-    for (int i = threadIdx.x; i < V; i += kFilterThreads) fn(Elem<DT>::at(row, i));
-  }
+template <int DT> constexpr int kKeyBits = DT == 0 ? 16 : 32;
+// Digit widths, top first: bf16 keys 12 + 4 bits, fp32 keys 12 + 12 + 8.  A
+// wide first digit splits every binade into eight bins, so few lanes of a
+// wave add to the same bin at once.
+template <int DT> constexpr int kLevels = DT == 0 ? 2 : 3;
+template <int DT>
+__device__ inline int digit_bits(int level) {
+  return DT == 0 ? (level == 0 ? 12 : 4) : (level < 2 ? 12 : 8);
 }
 
-// Block-wide sums of NV values (every thread gets the totals).
-template <typename T, int NV>
-__device__ inline void block_sum(T (&v)[NV], T (*s)[NV]) {
-#pragma unroll
-  for (int k = 0; k < NV; ++k) v[k] = wave_sum(v[k]);
-  const int w = threadIdx.x / kWave;
-  __syncthreads();  // the previous pass has read s
-  if (threadIdx.x % kWave == 0)
-#pragma unroll
-    for (int k = 0; k < NV; ++k) s[w][k] = v[k];
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    T t = s[0][k];
-    for (int i = 1; i < kFilterWaves; ++i) t += s[i][k];
-    v[k] = t;
-  }
+// The largest search key whose top `bits` bits are `prefix`, and its value
+// (the top bins' largest keys are +inf and NaN patterns: their value is taken
+// as the largest finite float).
+template <int DT>
+__device__ inline float prefix_top_value(uint32_t prefix, int bits) {
+  const int shift = kKeyBits<DT> - bits;
+  const uint32_t k = shift > 0 ? ((prefix << shift) | ((1u << shift) - 1u)) : prefix;
+  return fminf(key_value(full_key<DT>(k)), 3.40282347e38f);
 }
 
-// The largest key kk in [lo, hi) whose weight W(kk) = sum of w(x) over the
-// row's elements with key >= kk (and key >= floor) reaches `want`, given
-// W(lo) >= want (hi is one past the largest key).  w(x) = 1 (counts, fp64 is
-// exact for them) or the exponential.
-template <int DT, bool VEC, bool kMass>
-__device__ uint32_t search(const void* row, int V, uint32_t lo, uint32_t hi, uint32_t floor, double want,
-                           float sc, float msc) {
-  __shared__ double s[kFilterWaves][3];
-  while (hi - lo > 1u) {
-    const uint64_t span = static_cast<uint64_t>(hi) - lo;
-    uint32_t q[3];
-#pragma unroll
-    for (int i = 0; i < 3; ++i) q[i] = lo + static_cast<uint32_t>((span * static_cast<uint64_t>(i + 1)) / 4u);
-    double acc[3] = {0.0, 0.0, 0.0};
-    for_row<DT, VEC>(row, V, [&](float x) {
-      const uint32_t k = search_key<DT>(x);
-      if (k < floor) return;
-      double wgt = 1.0;
-      if constexpr (kMass) wgt = static_cast<double>(__builtin_amdgcn_exp2f(__builtin_fmaf(x, sc, -msc)));
-#pragma unroll
-      for (int i = 0; i < 3; ++i) acc[i] += k >= q[i] ? wgt : 0.0;
-    });
-    block_sum<double, 3>(acc, s);
-    // W is non-increasing in the key: keep the last probe that still reaches
-    // `want` as lo and the first one that does not as hi
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      if (q[i] <= lo || q[i] >= hi) continue;
-      if (acc[i] >= want) lo = q[i];
-      else { hi = q[i]; break; }
-    }
-  }
-  return lo;
+// 2^t in fp64 for t <= 1100 (t < -1074 gives 0).
+__device__ inline double exp2_any(double t) {
+  if (t <= 0.0) return exp2_neg(t);
+  const double n = __builtin_ceil(t);
+  return __builtin_ldexp(exp2_neg(t - n), static_cast<int>(n));
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kFilterThreads) void filter_rows(FilterArgs a) {
-  __shared__ uint32_t s_k[kFilterWaves][2];
-  __shared__ double s_z[kFilterWaves][1];
+// What a row needs: which cuts apply (none for a greedy or invalid request,
+// for a draft row without draft logits, and for k >= V with p == 1).
+struct RowJob {
+  float T;
+  double k, p;
+  bool cut_k, cut_p;
+};
+
+__device__ inline bool row_job(const FilterArgs& a, int row, RowJob& j) {
   const int R = 2 * a.gamma + 1;
-  const int b = static_cast<int>(blockIdx.x) / R;
-  const int r = static_cast<int>(blockIdx.x) - b * R;
-  const float T = a.temperature[b];
-  if (!filter_temp_ok(T)) return;  // greedy or invalid: no cut
-  if (r > a.gamma && a.draft == nullptr) return;
+  const int b = row / R, r = row - b * R;
+  j.T = a.temperature[b];
+  if (!filter_temp_ok(j.T)) return false;
+  if (r > a.gamma && a.draft == nullptr) return false;
   int k = a.V;
   if (a.top_k) {
     k = a.top_k[b];
-    if (k < 1) return;  // invalid request: the decide item reports it
+    if (k < 1) return false;  // invalid request: the decide item reports it
     k = min(k, a.V);
   }
   float p = 1.0f;
   if (a.top_p) {
     p = a.top_p[b];
-    if (!(p > 0.0f && p <= 1.0f)) return;
+    if (!(p > 0.0f && p <= 1.0f)) return false;
   }
-  const bool cut_k = k < a.V, cut_p = p < 1.0f;
-  if (!cut_k && !cut_p) return;
+  j.k = static_cast<double>(k);
+  j.p = static_cast<double>(p);
+  j.cut_k = k < a.V;
+  j.cut_p = p < 1.0f;
+  return j.cut_k || j.cut_p;
+}
+
+template <int DT>
+__device__ inline const void* row_ptr(const FilterArgs& a, int row) {
+  const int R = 2 * a.gamma + 1;
+  const int b = row / R, r = row - b * R;
   const size_t es = Elem<DT>::kBytes;
-  const void* row = r <= a.gamma
+  return r <= a.gamma
       ? static_cast<const char*>(a.target) + (static_cast<size_t>(b) * (a.gamma + 1) + r) * a.V * es
       : static_cast<const char*>(a.draft) + (static_cast<size_t>(b) * a.gamma + (r - a.gamma - 1)) * a.V * es;
-  // the row's smallest and largest keys
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for_row<DT, VEC>(row, a.V, [&](float x) {
-    const uint32_t kk = search_key<DT>(x);
-    kmin = min(kmin, kk);
-    kmax = max(kmax, kk);
-  });
-  // wave reductions on ints: flipping the top bit maps unsigned order to signed
-  kmin = static_cast<uint32_t>(wave_min(static_cast<int>(kmin ^ 0x80000000u))) ^ 0x80000000u;
-  kmax = static_cast<uint32_t>(wave_max_int(static_cast<int>(kmax ^ 0x80000000u))) ^ 0x80000000u;
-  if (threadIdx.x % kWave == 0) {
-    s_k[threadIdx.x / kWave][0] = kmin;
-    s_k[threadIdx.x / kWave][1] = kmax;
+}
+
+// Visits n elements of a row slice in batches: each thread issues the loads
+// of kBatch vectors (or single elements) before it uses any of them, so a
+// pass keeps kBatch * 16 bytes per thread in flight.
+constexpr int kBatch = 8;
+template <int DT, bool VEC, int NT = kFilterThreads, typename F>
+__device__ inline void for_slice(const void* base, int n, F&& fn) {
+  if constexpr (VEC) {
+    constexpr int kv = Elem<DT>::kVec;
+    const int nv = n / kv;
+    for (int v0 = 0; v0 < nv; v0 += kBatch * NT) {
+      uint4 w[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = v0 + j * NT + static_cast<int>(threadIdx.x);
+        w[j] = Elem<DT>::raw(base, (i < nv ? i : 0) * kv);
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (v0 + j * NT + static_cast<int>(threadIdx.x) >= nv) continue;
+        float x[kv];
+        Elem<DT>::unpack(w[j], x);
+#pragma unroll
+        for (int e = 0; e < kv; ++e) fn(x[e]);
+      }
+    }
+  } else {
+    constexpr int kScalar = 4 * kBatch;
+    for (int i0 = 0; i0 < n; i0 += kScalar * NT) {
+      float x[kScalar];
+#pragma unroll
+      for (int j = 0; j < kScalar; ++j) {
+        const int i = i0 + j * NT + static_cast<int>(threadIdx.x);
+        x[j] = Elem<DT>::at(base, i < n ? i : 0);
+      }
+#pragma unroll
+      for (int j = 0; j < kScalar; ++j)
+        if (i0 + j * NT + static_cast<int>(threadIdx.x) < n) fn(x[j]);
+    }
+  }
+}
+
+struct FilterHist {
+  uint32_t cnt[kMaxBins];
+  double mass[kMaxBins];
+};
+
+// Block-wide maximum of an order key.
+__device__ inline uint32_t block_max_key(uint32_t k, int* s_red) {
+  int v = wave_max_int(static_cast<int>(k ^ 0x80000000u));
+  __syncthreads();  // earlier readers of s_red are done
+  if (threadIdx.x % kWave == 0) s_red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  v = s_red[0];
+  for (int i = 1; i < kFilterWaves; ++i) v = max(v, s_red[i]);
+  return static_cast<uint32_t>(v) ^ 0x80000000u;
+}
+
+// Block-wide sum (every thread gets it).
+__device__ inline double block_total(double v, double (*s_w)[1]) {
+  v = wave_sum(v);
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) s_w[threadIdx.x / kWave][0] = v;
+  __syncthreads();
+  double t = s_w[0][0];
+  for (int i = 1; i < kFilterWaves; ++i) t += s_w[i][0];
+  return t;
+}
+
+// The slice's histogram of digit `level` over the elements with search key
+// >= floor whose `above` higher bits equal `prefix`: counts per bin, and with
+// kMass the weights, relative to the bin's largest value (kBinTop) or to the
+// row maximum M.  Returns the thread's largest order key when kMax.
+template <int DT, bool VEC, bool kMass, bool kBinTop, bool kMax>
+__device__ uint32_t slice_hist(const void* base, int n, int width, int above, uint32_t prefix, uint32_t floor,
+                               float M, double l2t, FilterHist& h) {
+  constexpr int KB = kKeyBits<DT>;
+  const int nb = 1 << width;
+  for (int i = threadIdx.x; i < nb; i += kFilterThreads) {
+    h.cnt[i] = 0u;
+    if (kMass) h.mass[i] = 0.0;
   }
   __syncthreads();
-  for (int i = 0; i < kFilterWaves; ++i) {
-    kmin = min(kmin, s_k[i][0]);
-    kmax = max(kmax, s_k[i][1]);
+  const int shift = KB - above - width;
+  const float l2t_f = static_cast<float>(l2t);
+  const double Md = static_cast<double>(M);
+  uint32_t kmax = 0u;
+  for_slice<DT, VEC>(base, n, [&](float x) {
+    const uint32_t key = order_key(x);
+    if (kMax) kmax = max(kmax, key);
+    const uint32_t k = search_key<DT>(key);
+    if (k < floor) return;
+    if (above > 0 && (k >> (shift + width)) != prefix) return;
+    const uint32_t bin = (k >> shift) & static_cast<uint32_t>(nb - 1);
+    atomicAdd(&h.cnt[bin], 1u);
+    if constexpr (kMass) {
+      double w;
+      if constexpr (kBinTop) {
+        // x and its bin's top lie within an eighth of a binade, so x - top is
+        // exact in fp32
+        const float top = prefix_top_value<DT>(k >> shift, above + width);
+        const float t = fminf(fmaxf((x - top) * l2t_f, -1100.0f), 0.0f);
+        const float nn = __builtin_floorf(t);
+        w = __builtin_ldexp(static_cast<double>(__builtin_amdgcn_exp2f(t - nn)), static_cast<int>(nn));
+      } else {
+        const double t = __builtin_fmin(__builtin_fmax((static_cast<double>(x) - Md) * l2t, -1100.0), 0.0);
+        const double nn = __builtin_floor(t);
+        w = __builtin_ldexp(static_cast<double>(__builtin_amdgcn_exp2f(static_cast<float>(t - nn))),
+                            static_cast<int>(nn));
+      }
+      atomicAdd(&h.mass[bin], w);
+    }
+  });
+  __syncthreads();
+  return kmax;
+}
+
+// From the top bin down, the first bin b of the nb bins where above + v[b]
+// reaches `want`, with above the sum of v over the bins higher than b; the
+// lowest non-empty bin, with everything above it, when rounding leaves `want`
+// above the total.  Block scan: thread t takes ceil(nb / threads) consecutive
+// bins from the top.
+__device__ void find_from_top(const double* v, const uint32_t* cnt, int nb, double want, uint32_t* s_pick,
+                              double* s_above, double (*s_w)[1]) {
+  __syncthreads();  // earlier readers of s_w are done
+  const int t = threadIdx.x;
+  const int per = (nb + kFilterThreads - 1) / kFilterThreads;
+  double own = 0.0;
+  for (int j = 0; j < per; ++j) {
+    const int bin = nb - 1 - (t * per + j);
+    if (bin >= 0) own += v[bin];
   }
-  const uint32_t hi = kmax + 1u;
-  uint32_t cut = kmin;
-  if (cut_k) cut = search<DT, VEC, false>(row, a.V, kmin, hi, 0u, static_cast<double>(k), 0.0f, 0.0f);
-  if (cut_p) {
-    // exponentials relative to the row max, as the chain's stream items form them
-    const float m = key_value(full_key<DT>(kmax));
-    const float sc = 1.4426950408889634f / T;
-    const float msc = m * sc;
-    double z[1] = {0.0};
-    for_row<DT, VEC>(row, a.V, [&](float x) {
-      if (search_key<DT>(x) >= cut) z[0] += static_cast<double>(__builtin_amdgcn_exp2f(__builtin_fmaf(x, sc, -msc)));
-    });
-    block_sum<double, 1>(z, s_z);
-    cut = search<DT, VEC, true>(row, a.V, cut, hi, cut, static_cast<double>(p) * z[0], sc, msc);
+  // exclusive prefix over threads (higher bins first)
+  double inc = own;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const double o = __shfl_up(inc, d, kWave);
+    if (static_cast<int>(threadIdx.x % kWave) >= d) inc += o;
   }
-  if (threadIdx.x == 0) a.thr[static_cast<size_t>(b) * R + r] = full_key<DT>(cut) + 1u;
+  const int w = t / kWave;
+  if (t % kWave == kWave - 1) s_w[w][0] = inc;
+  if (t == 0) *s_pick = 0xffffffffu;
+  __syncthreads();
+  double base = 0.0;
+  for (int i = 0; i < w; ++i) base += s_w[i][0];
+  const double before = base + inc - own;
+  if (before < want && before + own >= want) {
+    double acc = before;
+    for (int j = 0; j < per; ++j) {
+      const int bin = nb - 1 - (t * per + j);
+      if (bin < 0) break;
+      if (acc + v[bin] >= want) {
+        *s_pick = static_cast<uint32_t>(bin);
+        *s_above = acc;
+        break;
+      }
+      acc += v[bin];
+    }
+  }
+  __syncthreads();
+  if (*s_pick == 0xffffffffu) {
+    int lowest = nb;
+    for (int j = 0; j < per; ++j) {
+      const int bin = nb - 1 - (t * per + j);
+      if (bin >= 0 && cnt[bin]) lowest = min(lowest, bin);
+    }
+    lowest = wave_min(lowest);
+    __syncthreads();
+    if (t % kWave == 0) s_w[w][0] = static_cast<double>(lowest);
+    __syncthreads();
+    int low = nb;
+    for (int i = 0; i < kFilterWaves; ++i) low = min(low, static_cast<int>(s_w[i][0]));
+    if (low >= nb) low = 0;
+    double part = 0.0;
+    for (int bin = low + 1 + t; bin < nb; bin += kFilterThreads) part += v[bin];
+    const double total = block_total(part, s_w);
+    if (t == 0) {
+      *s_pick = static_cast<uint32_t>(low);
+      *s_above = total;
+    }
+  }
+  __syncthreads();
+}
+
+// One search of the finishing workgroup: the digits of one cut, top first.
+// Digit 0 may come from the merged histogram already in s_h (have0); every
+// other digit is a pass of this workgroup over the whole row.  kMass: top-p
+// masses on the scale of M over the keys >= floor, else top-k counts.
+// Returns the cut's search key.
+template <int DT, bool VEC, bool kMass>
+__device__ uint32_t search_digits(const void* row, int V, bool have0, double want, uint32_t floor, float M,
+                                  double l2t, double p, FilterHist& h, uint32_t* s_pick, double* s_above,
+                                  double (*s_w)[1]) {
+  constexpr int L = kLevels<DT>;
+  uint32_t prefix = 0u;
+  int above = 0;
+  for (int level = 0; level < L; ++level) {
+    const int width = digit_bits<DT>(level);
+    const int nb = 1 << width;
+    if (level > 0 || !have0) slice_hist<DT, VEC, kMass, false, false>(row, V, width, above, prefix, floor, M, l2t, h);
+    if (!kMass) {
+      for (int bin = threadIdx.x; bin < nb; bin += kFilterThreads) h.mass[bin] = static_cast<double>(h.cnt[bin]);
+      __syncthreads();
+    } else if (level == 0) {
+      double part = 0.0;
+      for (int bin = threadIdx.x; bin < nb; bin += kFilterThreads) part += h.mass[bin];
+      want = p * block_total(part, s_w);
+    }
+    find_from_top(h.mass, h.cnt, nb, want, s_pick, s_above, s_w);
+    want -= *s_above;
+    prefix = (prefix << width) | *s_pick;
+    above += width;
+    __syncthreads();  // s_pick and s_above are read
+  }
+  return prefix;
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kFilterThreads) void filter_rows(FilterArgs a) {
+  __shared__ FilterHist s_h;
+  __shared__ uint32_t s_pick;
+  __shared__ double s_above;
+  __shared__ double s_w[kFilterWaves][1];
+  __shared__ int s_red[kFilterWaves];
+  __shared__ int s_last;
+  __shared__ uint32_t s_max;
+  const int local = static_cast<int>(blockIdx.x) / a.S;
+  const int slice = static_cast<int>(blockIdx.x) - local * a.S;
+  const int row_id = a.row0 + local;
+  RowJob j;
+  if (!row_job(a, row_id, j)) return;
+  FilterSlot& sl = static_cast<FilterSlot*>(a.slots)[local];
+  const double l2t = kLog2e / static_cast<double>(j.T);
+  const void* row = row_ptr<DT>(a, row_id);
+  constexpr int W0 = 12;  // digit 0 of either key width
+  const int nb0 = 1 << W0;
+
+  // digit 0 over this workgroup's slice: top-k counts, or (top-p alone) the
+  // counts and the bin-relative weights; and the slice maximum
+  const int s0 = slice * kSlice;
+  const int n = min(kSlice, a.V - s0);
+  const void* base = static_cast<const char*>(row) + static_cast<size_t>(s0) * Elem<DT>::kBytes;
+  const bool mass0 = !j.cut_k;
+  const uint32_t kmax = mass0 ? slice_hist<DT, VEC, true, true, true>(base, n, W0, 0, 0u, 0u, 0.0f, l2t, s_h)
+                              : slice_hist<DT, VEC, false, false, true>(base, n, W0, 0, 0u, 0u, 0.0f, l2t, s_h);
+  for (int bin = threadIdx.x; bin < nb0; bin += kFilterThreads) {
+    const uint32_t c = s_h.cnt[bin];
+    if (c) {
+      __hip_atomic_fetch_add(&sl.cnt[bin], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (mass0) __hip_atomic_fetch_add(&sl.mass[bin], s_h.mass[bin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  const uint32_t m = block_max_key(kmax, s_red);
+  if (threadIdx.x == 0) __hip_atomic_fetch_max(&sl.st.max_key, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = arrive(&sl.st.arrivals) == static_cast<uint32_t>(a.S - 1);
+  __syncthreads();
+  if (!s_last) return;
+
+  // the row's last workgroup: the merged histogram, cleared behind it (each
+  // thread issues all its loads before it waits for any), and the maximum
+  constexpr int kPer = kMaxBins / kFilterThreads;
+  {
+    uint32_t c[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) c[i] = load_coherent(&sl.cnt[i * kFilterThreads + threadIdx.x]);
+    double mm[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      mm[i] = (mass0 && c[i]) ? load_coherent_f64(&sl.mass[i * kFilterThreads + threadIdx.x]) : 0.0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int bin = i * kFilterThreads + static_cast<int>(threadIdx.x);
+      s_h.cnt[bin] = c[i];
+      s_h.mass[bin] = mm[i];
+      if (c[i]) {
+        store_coherent(&sl.cnt[bin], 0u);
+        if (mass0) store_coherent_f64(&sl.mass[bin], 0.0);
+      }
+    }
+  }
+  if (threadIdx.x == 0) {
+    s_max = load_coherent(&sl.st.max_key);  // every workgroup's maximum is in
+    store_coherent(&sl.st.arrivals, 0u);
+    store_coherent(&sl.st.max_key, 0u);
+  }
+  __syncthreads();
+  const float M = key_value(s_max);
+
+  uint32_t cut;
+  if (j.cut_k) {
+    const uint32_t floor_key = search_digits<DT, VEC, false>(row, a.V, true, j.k, 0u, M, l2t, j.p, s_h, &s_pick,
+                                                             &s_above, s_w);
+    cut = j.cut_p ? search_digits<DT, VEC, true>(row, a.V, false, 0.0, floor_key, M, l2t, j.p, s_h, &s_pick,
+                                                 &s_above, s_w)
+                  : floor_key;
+  } else {
+    // top-p alone: digit 0's weights put on the scale of M, unless the top
+    // bin is too wide for that
+    int hi = -1;
+    for (int bin = threadIdx.x; bin < nb0; bin += kFilterThreads)
+      if (s_h.cnt[bin]) hi = bin;
+    hi = wave_max_int(hi);
+    if (threadIdx.x % kWave == 0) s_red[threadIdx.x / kWave] = hi;
+    __syncthreads();
+    for (int i = 0; i < kFilterWaves; ++i) hi = max(hi, s_red[i]);
+    hi = max(hi, 0);
+    const double dtop =
+        (static_cast<double>(prefix_top_value<DT>(static_cast<uint32_t>(hi), W0)) - static_cast<double>(M)) * l2t;
+    const bool rescale = dtop <= kMaxTopLog2;
+    if (rescale) {
+      for (int bin = threadIdx.x; bin < nb0; bin += kFilterThreads) {
+        if (!s_h.cnt[bin]) continue;
+        const double d =
+            (static_cast<double>(prefix_top_value<DT>(static_cast<uint32_t>(bin), W0)) - static_cast<double>(M)) *
+            l2t;
+        s_h.mass[bin] *= exp2_any(__builtin_fmin(__builtin_fmax(d, -1100.0), kMaxTopLog2));
+      }
+    }
+    __syncthreads();
+    cut = search_digits<DT, VEC, true>(row, a.V, rescale, 0.0, 0u, M, l2t, j.p, s_h, &s_pick, &s_above, s_w);
+  }
+  if (threadIdx.x == 0) a.thr[row_id] = full_key<DT>(cut) + 1u;
+}
+
+
+// ---------------------------------------------------------------------------
+// bf16 rows: exact counts of every value, one read of each row
+// ---------------------------------------------------------------------------
+// A bf16 logit has one of 65536 values, so a row is fully described by how
+// many times each value occurs.  A row is cut into S slices of kB16Slice
+// logits; one persistent workgroup per CU takes the (row, slice) items in
+// turn, counts the slice's values in LDS (16-bit counters, two to a word: a
+// slice has fewer than 65536 logits) and writes the slice's part of the row:
+// for every non-empty 12-bit key prefix its count, its mass relative to the
+// prefix's top value and its eight counter words.
+// The row's last item to arrive (nothing waits: the others go on to their
+// next item) sums the S parts and finds both cuts.  The maximum M is the
+// largest value present (in the highest non-empty prefix); a value v weighs count(v) * 2^((v - M) * log2(e) /
+// T) in fp64, and a prefix's mass on that scale is its relative mass times
+// its top value's weight.  Top-k and top-p are scans from the top over the
+// 4096 prefixes, then over the 16 values of the chosen prefix (the only
+// counter words read back).  The last item also clears what the items wrote.
+// No row is read twice.
+constexpr int kB16Threads = 1024;
+constexpr int kB16Waves = kB16Threads / kWave;
+constexpr int kB16Slice = 65528;                 // a multiple of 8 below 65536: one value's count fits 16 bits
+constexpr int kB16Per = kMaxBins / kB16Threads;  // prefixes per thread (4 consecutive ones)
+constexpr size_t kB16PartBytes = kMaxBins * (4 + 8 + 32);  // counts, masses, counter words
+constexpr size_t kB16Head = 256;                                 // arrival counter
+// Largest log2 weight of the top prefix's top value on the scale of M for
+// which its relative mass is rescaled (beyond it the prefix is weighed value
+// by value: a tiny temperature).
+constexpr double kB16MaxTopLog2 = 900.0;
+
+__host__ __device__ inline size_t b16_slot_bytes(int S) { return kB16Head + static_cast<size_t>(S) * kB16PartBytes; }
+
+// One slice's part, structure of arrays so that consecutive prefixes are
+// consecutive words of every array.
+struct B16Part {
+  uint32_t* cnt12;  // [4096] logits per prefix
+  double* mass;     // [4096] mass relative to the prefix's top value
+  uint64_t* words;  // [4][4096]: counters 4q .. 4q + 3 of prefix b in words[q][b], 16 bits each, lowest first
+};
+__device__ inline B16Part b16_part(char* slot, int s) {
+  char* p = slot + kB16Head + static_cast<size_t>(s) * kB16PartBytes;
+  return B16Part{reinterpret_cast<uint32_t*>(p), reinterpret_cast<double*>(p + kMaxBins * 4),
+                 reinterpret_cast<uint64_t*>(p + kMaxBins * 12)};
+}
+
+// Weights of the 16 values of prefix `bin` relative to value `ref`: the
+// values of one prefix share sign and exponent, so they are evenly spaced
+// and their weights form a geometric sequence, w(s - 1) = w(s) * q from the
+// top value down.  Two fp64 exponentials per prefix; the rest are products.
+// The prefixes of inf and NaN values weigh 0 (only -inf is a valid logit
+// there).
+struct B16Weights {
+  double top, q;  // weight of the prefix's top value, ratio between neighbours
+};
+__device__ inline double b16_value(uint32_t k16) { return static_cast<double>(key_value(full_key<0>(k16))); }
+__device__ inline B16Weights b16_weights(int bin, double ref, double l2t) {
+  const double v15 = b16_value(static_cast<uint32_t>(16 * bin + 15));
+  const double v14 = b16_value(static_cast<uint32_t>(16 * bin + 14));
+  if (!__builtin_isfinite(v15) || !__builtin_isfinite(v14)) return B16Weights{0.0, 0.0};
+  return B16Weights{exp2_neg(__builtin_fmin((v15 - ref) * l2t, 0.0)), exp2_neg((v14 - v15) * l2t)};
+}
+__device__ inline void b16_unpack(const uint32_t (&w)[8], uint32_t (&c)[16]) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    c[2 * q] = w[q] & 0xffffu;
+    c[2 * q + 1] = w[q] >> 16;
+  }
+}
+__device__ inline void b16_add_quad(uint64_t two, uint32_t* c) {
+  c[0] += static_cast<uint32_t>(two) & 0xffffu;
+  c[1] += static_cast<uint32_t>(two) >> 16;
+  c[2] += static_cast<uint32_t>(two >> 32) & 0xffffu;
+  c[3] += static_cast<uint32_t>(two >> 48);
+}
+// Mass of the prefix's values with key >= floor16 (counts c) relative to ref.
+__device__ inline double b16_mass(const uint32_t (&c)[16], int bin, uint32_t floor16, double ref, double l2t) {
+  const B16Weights w = b16_weights(bin, ref, l2t);
+  double m = 0.0, x = w.top;
+#pragma unroll
+  for (int sb = 15; sb >= 0; --sb) {
+    if (c[sb] && static_cast<uint32_t>(16 * bin + sb) >= floor16) m += static_cast<double>(c[sb]) * x;
+    x *= w.q;
+  }
+  return m;
+}
+// Walks the 16 values of prefix `bin` from the top, in the order and
+// arithmetic of b16_mass: the first key >= floor16 where acc plus its count
+// (or its mass on the scale of Mv) reaches `want`; the lowest such key when
+// rounding leaves `want` above them all.
+__device__ inline uint32_t b16_walk(const uint32_t (&c)[16], int bin, uint32_t floor16, double acc, double want,
+                                    bool mass, double Mv, double l2t) {
+  const B16Weights w = b16_weights(bin, Mv, l2t);
+  uint32_t key = 0xffffffffu, low = static_cast<uint32_t>(16 * bin);
+  double x = w.top;
+#pragma unroll
+  for (int sb = 15; sb >= 0; --sb) {
+    const uint32_t k = static_cast<uint32_t>(16 * bin + sb);
+    const double ws = x;
+    x *= w.q;
+    if (!c[sb] || k < floor16) continue;
+    const double add = mass ? static_cast<double>(c[sb]) * ws : static_cast<double>(c[sb]);
+    if (key == 0xffffffffu && acc + add >= want) key = k;
+    acc += add;
+    low = k;
+  }
+  return key != 0xffffffffu ? key : low;
+}
+// The 16 counts of prefix `bin` summed over the S parts of a row.
+__device__ inline void b16_bin_counts(char* slot, int S, int bin, uint32_t (&c)[16]) {
+#pragma unroll
+  for (int sb = 0; sb < 16; ++sb) c[sb] = 0u;
+  for (int s = 0; s < S; ++s) {
+    const B16Part pt = b16_part(slot, s);
+    if (!load_coherent(&pt.cnt12[bin])) continue;
+    uint64_t two[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) two[q] = load_coherent(pt.words + q * kMaxBins + bin);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b16_add_quad(two[q], c + 4 * q);
+  }
+}
+
+// Block scan from the top over the kB16Per values each thread holds, thread
+// t holding prefixes 4095 - (kB16Per t + i): the first prefix (from the top)
+// where the running sum reaches `want`, and the sum above it; -1 when none
+// does.
+__device__ inline int b16_find(const double (&v)[kB16Per], double want, double* s_wd, int* s_pos, double* s_above,
+                               double* above_out) {
+  double own = 0.0;
+#pragma unroll
+  for (int i = 0; i < kB16Per; ++i) own += v[i];
+  double inc = own;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const double o = __shfl_up(inc, d, kWave);
+    if (static_cast<int>(threadIdx.x % kWave) >= d) inc += o;
+  }
+  const int w = threadIdx.x / kWave;
+  __syncthreads();  // earlier readers of s_wd and s_pos are done
+  if (threadIdx.x % kWave == kWave - 1) s_wd[w] = inc;
+  if (threadIdx.x == 0) *s_pos = 0x7fffffff;
+  __syncthreads();
+  double base = 0.0;
+  for (int i = 0; i < w; ++i) base += s_wd[i];
+  double acc = base + inc - own;
+  int pos = -1;
+  double above = 0.0;
+  if (acc < want) {
+#pragma unroll
+    for (int i = 0; i < kB16Per; ++i) {
+      if (pos < 0 && acc + v[i] >= want) {
+        pos = kB16Per * static_cast<int>(threadIdx.x) + i;
+        above = acc;
+      }
+      acc += v[i];
+    }
+  }
+  if (pos >= 0) atomicMin(s_pos, pos);
+  __syncthreads();
+  const int best = *s_pos;
+  if (pos >= 0 && pos == best) *s_above = above;
+  __syncthreads();
+  *above_out = *s_above;
+  return best == 0x7fffffff ? -1 : kMaxBins - 1 - best;
+}
+
+// The last item of a row: both cuts from the S parts, stored in thr, and
+// the parts cleared.
+__device__ __attribute__((noinline)) void b16_finish(const RowJob& j, char* slot, int S, uint32_t* thr, double* s_wd,
+                                                     int* s_wi, int* s_pos, double* s_above, uint32_t* s_key) {
+  const double l2t = kLog2e / static_cast<double>(j.T);
+  // this thread's four prefixes (index i: prefix bin0 + 3 - i, top first),
+  // counts and relative masses summed over the parts, in one round of loads
+  // per four parts; `seen` marks the non-empty (part, prefix) pairs of the
+  // first 8 parts, to clear them
+  const int bin0 = kMaxBins - kB16Per * (static_cast<int>(threadIdx.x) + 1);
+  uint32_t c12[kB16Per] = {0u, 0u, 0u, 0u};
+  double mrel[kB16Per] = {0.0, 0.0, 0.0, 0.0};
+  uint32_t seen = 0u;
+  constexpr int kPC = 4;
+  for (int s0 = 0; s0 < S; s0 += kPC) {
+    uint64_t cw[kPC][2], mw[kPC][4];
+#pragma unroll
+    for (int u = 0; u < kPC; ++u) {
+      const bool in = s0 + u < S;
+      const B16Part pt = b16_part(slot, in ? s0 + u : 0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) cw[u][h] = in ? load_coherent(reinterpret_cast<const uint64_t*>(pt.cnt12 + bin0) + h) : 0ull;
+#pragma unroll
+      for (int jj = 0; jj < kB16Per; ++jj) mw[u][jj] = in ? load_coherent(reinterpret_cast<const uint64_t*>(pt.mass + bin0 + jj)) : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kPC; ++u) {
+#pragma unroll
+      for (int jj = 0; jj < kB16Per; ++jj) {
+        const uint32_t cj = static_cast<uint32_t>(cw[u][jj / 2] >> (32 * (jj % 2)));
+        c12[kB16Per - 1 - jj] += cj;
+        mrel[kB16Per - 1 - jj] += __longlong_as_double(static_cast<long long>(mw[u][jj]));
+        if (cj && s0 + u < 8) seen |= 1u << (4 * (s0 + u) + jj);
+      }
+    }
+  }
+  // M: the highest non-empty prefix, block-wide, then its highest value
+  int top_bin = -1;
+#pragma unroll
+  for (int i = kB16Per - 1; i >= 0; --i)
+    if (c12[i]) top_bin = bin0 + kB16Per - 1 - i;
+  top_bin = wave_max_int(top_bin);
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) s_wi[threadIdx.x / kWave] = top_bin;
+  __syncthreads();
+  for (int i = 0; i < kB16Waves; ++i) top_bin = max(top_bin, s_wi[i]);
+  top_bin = max(top_bin, 0);
+  if (top_bin >= bin0 && top_bin < bin0 + kB16Per) {
+    uint32_t c[16];
+    b16_bin_counts(slot, S, top_bin, c);
+    uint32_t top = static_cast<uint32_t>(16 * top_bin);
+#pragma unroll
+    for (int sb = 0; sb < 16; ++sb)
+      if (c[sb]) top = static_cast<uint32_t>(16 * top_bin + sb);
+    *s_key = top;
+  }
+  __syncthreads();
+  const double Mv = b16_value(*s_key);
+  __syncthreads();
+
+  // masses on the scale of M: the relative mass times the weight of the
+  // prefix's top value; the top prefix, when that weight passes 2^900, value
+  // by value
+  double m[kB16Per];
+#pragma unroll
+  for (int i = 0; i < kB16Per; ++i) {
+    const int bin = bin0 + kB16Per - 1 - i;
+    m[i] = 0.0;
+    if (!c12[i]) continue;
+    const double v15 = b16_value(static_cast<uint32_t>(16 * bin + 15));
+    const double d = (v15 - Mv) * l2t;
+    if (bin != top_bin) {
+      m[i] = mrel[i] * exp2_neg(__builtin_fmin(d, 0.0));  // below M's prefix: v15 < M
+    } else if (d <= kB16MaxTopLog2) {
+      const double n = __builtin_ceil(__builtin_fmax(d, 0.0));
+      m[i] = mrel[i] * __builtin_ldexp(exp2_neg(__builtin_fmax(d, 0.0) - n), static_cast<int>(n));
+    } else {
+      uint32_t c[16];
+      b16_bin_counts(slot, S, bin, c);
+      m[i] = b16_mass(c, bin, 0u, Mv, l2t);
+    }
+  }
+
+  uint32_t floor16 = 0u;
+  double above = 0.0;
+  if (j.cut_k) {
+    double v[kB16Per];
+#pragma unroll
+    for (int i = 0; i < kB16Per; ++i) v[i] = static_cast<double>(c12[i]);  // counts are exact in fp64
+    const int bin = b16_find(v, j.k, s_wd, s_pos, s_above, &above);
+    if (bin < 0 && threadIdx.x == 0) *s_key = 0u;  // cannot happen: k < V
+    if (bin >= bin0 && bin < bin0 + kB16Per) {
+      uint32_t c[16];
+      b16_bin_counts(slot, S, bin, c);
+      *s_key = b16_walk(c, bin, 0u, above, j.k, false, Mv, l2t);
+    }
+    __syncthreads();
+    floor16 = *s_key;
+    __syncthreads();
+  }
+  uint32_t cut16 = floor16;
+  if (j.cut_p) {
+    // masses over the keys >= floor16: the top-k cut's own prefix value by
+    // value, the prefixes below it none
+    const int fbin = static_cast<int>(floor16 >> 4);
+#pragma unroll
+    for (int i = 0; i < kB16Per; ++i) {
+      const int bin = bin0 + kB16Per - 1 - i;
+      if (bin < fbin) {
+        m[i] = 0.0;
+      } else if (bin == fbin && j.cut_k && c12[i]) {
+        uint32_t c[16];
+        b16_bin_counts(slot, S, bin, c);
+        m[i] = b16_mass(c, bin, floor16, Mv, l2t);
+      }
+    }
+    double part = 0.0;
+#pragma unroll
+    for (int i = 0; i < kB16Per; ++i) part += m[i];
+    part = wave_sum(part);
+    __syncthreads();
+    if (threadIdx.x % kWave == 0) s_wd[threadIdx.x / kWave] = part;
+    __syncthreads();
+    double Z = 0.0;
+    for (int i = 0; i < kB16Waves; ++i) Z += s_wd[i];
+    const double want = j.p * Z;
+    const int bin = b16_find(m, want, s_wd, s_pos, s_above, &above);
+    if (bin >= 0) {
+      if (bin >= bin0 && bin < bin0 + kB16Per) {
+        uint32_t c[16];
+        b16_bin_counts(slot, S, bin, c);
+        *s_key = b16_walk(c, bin, floor16, above, want, true, Mv, l2t);
+      }
+    } else {
+      // rounding left `want` above the total: the lowest key >= floor16
+      // present (in the lowest non-empty prefix at or above the cut's)
+      int lowbin = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < kB16Per; ++i) {
+        const int b2 = bin0 + kB16Per - 1 - i;
+        if (c12[i] && b2 >= fbin) lowbin = min(lowbin, b2);
+      }
+      lowbin = wave_min(lowbin);
+      __syncthreads();
+      if (threadIdx.x % kWave == 0) s_wi[threadIdx.x / kWave] = lowbin;
+      __syncthreads();
+      for (int i = 0; i < kB16Waves; ++i) lowbin = min(lowbin, s_wi[i]);
+      if (lowbin != 0x7fffffff && lowbin >= bin0 && lowbin < bin0 + kB16Per) {
+        uint32_t c[16];
+        b16_bin_counts(slot, S, lowbin, c);
+        uint32_t low = static_cast<uint32_t>(16 * lowbin + 15);
+#pragma unroll
+        for (int sb = 15; sb >= 0; --sb)
+          if (c[sb] && static_cast<uint32_t>(16 * lowbin + sb) >= floor16) low = static_cast<uint32_t>(16 * lowbin + sb);
+        *s_key = low;
+      }
+      if (lowbin == 0x7fffffff && threadIdx.x == 0) *s_key = floor16;
+    }
+    __syncthreads();
+    cut16 = *s_key;
+  }
+  if (threadIdx.x == 0) *thr = full_key<0>(cut16) + 1u;
+
+  // clear every word the row's items wrote: the workspace is zero between
+  // calls
+  __syncthreads();  // all reads of the parts are done
+  for (int s = 0; s < S; ++s) {
+    const B16Part pt = b16_part(slot, s);
+    uint32_t nz = 0u;
+    if (s < 8) {
+      nz = (seen >> (4 * s)) & 0xfu;
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < kB16Per; ++jj)
+        if (load_coherent(&pt.cnt12[bin0 + jj])) nz |= 1u << jj;
+    }
+    if (!nz) continue;
+#pragma unroll
+    for (int jj = 0; jj < kB16Per; ++jj) {
+      if (!((nz >> jj) & 1u)) continue;
+      store_coherent(reinterpret_cast<uint64_t*>(pt.mass + bin0 + jj), 0ull);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) store_coherent(pt.words + q * kMaxBins + bin0 + jj, 0ull);
+    }
+    if (nz & 3u) store_coherent(reinterpret_cast<uint64_t*>(pt.cnt12 + bin0), 0ull);
+    if (nz & 12u) store_coherent(reinterpret_cast<uint64_t*>(pt.cnt12 + bin0 + 2), 0ull);
+  }
+}
+
+// A row's job as kept in LDS.
+struct B16Job {
+  float T, p;
+  int32_t k;
+  uint32_t cuts;  // bit 0: top-k, bit 1: top-p
+};
+__device__ inline B16Job b16_pack(const RowJob& j) {
+  return B16Job{j.T, static_cast<float>(j.p), static_cast<int32_t>(j.k), (j.cut_k ? 1u : 0u) | (j.cut_p ? 2u : 0u)};
+}
+__device__ inline RowJob b16_unpack_job(const B16Job& b) {
+  return RowJob{b.T, static_cast<double>(b.k), static_cast<double>(b.p), (b.cuts & 1u) != 0, (b.cuts & 2u) != 0};
+}
+
+// Where item `it` of the active rows' items reads: its row's job, the
+// slice's first logit and length.
+__device__ inline bool b16_item(const FilterArgs& a, const uint16_t* rows, const B16Job* jobs, long long it, RowJob& j,
+                                const void*& base, int& n, int& row_id, int& slice, int& local) {
+  local = rows[it / a.S];
+  j = b16_unpack_job(jobs[it / a.S]);
+  slice = static_cast<int>(it % a.S);
+  row_id = a.row0 + local;
+  const int s0 = slice * kB16Slice;
+  n = min(kB16Slice, a.V - s0);
+  base = static_cast<const char*>(row_ptr<0>(a, row_id)) + static_cast<size_t>(s0) * 2;
+  return true;
+}
+
+// Every workgroup first lists the group's rows that need a cut (one row per
+// thread); the items of those rows are then handed out in order by a counter
+// in the workspace, so no workgroup gets more than its share.  Each
+// workgroup takes its next item while it counts the current one, and on the
+// vector path issues the next slice's loads before it writes the current
+// part.  The last workgroup to leave resets the counter.
+template <bool VEC>
+__global__ __launch_bounds__(kB16Threads) void filter_rows_bf16(FilterArgs a) {
+  __shared__ uint4 s_pairs[(1 << 16) / 8];  // 65536 16-bit counters
+  __shared__ double s_wd[kB16Waves];
+  __shared__ int s_wi[kB16Waves];
+  __shared__ int s_pos;
+  __shared__ double s_above;
+  __shared__ uint32_t s_key;
+  __shared__ int s_last;
+  __shared__ uint32_t s_next;
+  __shared__ uint16_t s_rows[kFilterSlots];
+  __shared__ B16Job s_jobs[kFilterSlots];
+  __shared__ int s_nrows;
+  static_assert(kFilterSlots <= kB16Threads, "one row per thread");
+  constexpr int kv = Elem<0>::kVec;
+  uint32_t* pairs = reinterpret_cast<uint32_t*>(s_pairs);
+  uint32_t* head = a.queue;
+  uint32_t* exits = a.queue + 1;
+  for (int i = threadIdx.x; i < (1 << 16) / 8; i += kB16Threads) s_pairs[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x == 0) s_next = __hip_atomic_fetch_add(head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  {
+    // the rows that need a cut, in order
+    RowJob rj;
+    const bool need = static_cast<int>(threadIdx.x) < a.group && row_job(a, a.row0 + threadIdx.x, rj);
+    const uint64_t bal = __ballot(need);
+    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    if (lane == 0) s_wi[w] = __popcll(bal);
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int i = 0; i < kB16Waves; ++i) {
+      if (i < w) before += s_wi[i];
+      all += s_wi[i];
+    }
+    if (need) {
+      const int q = before + __popcll(bal & ((1ull << lane) - 1ull));
+      s_rows[q] = static_cast<uint16_t>(threadIdx.x);
+      s_jobs[q] = b16_pack(rj);
+    }
+    if (threadIdx.x == 0) s_nrows = all;
+    __syncthreads();
+  }
+  const long long items = static_cast<long long>(s_nrows) * a.S;
+  long long item = s_next;
+  RowJob j{};
+  const void* base = nullptr;
+  int n = 0, row_id = 0, slice = 0, local = 0;
+  bool act = item < items && b16_item(a, s_rows, s_jobs, item, j, base, n, row_id, slice, local);
+  uint4 w[kBatch];
+  auto issue = [&](const void* bp, int nn) {
+    const int nv = nn / kv;
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int i = q * kB16Threads + static_cast<int>(threadIdx.x);
+      w[q] = Elem<0>::raw(bp, (i < nv ? i : 0) * kv);
+    }
+  };
+  if (VEC && act) issue(base, n);
+  while (item < items) {
+    uint32_t nxt = 0u;
+    if (threadIdx.x == 0) nxt = __hip_atomic_fetch_add(head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (act) {
+      if constexpr (VEC) {
+        const int nv = n / kv;  // kBatch * kB16Threads vectors cover a slice
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          if (q * kB16Threads + static_cast<int>(threadIdx.x) >= nv) continue;
+          float x[kv];
+          Elem<0>::unpack(w[q], x);
+#pragma unroll
+          for (int e = 0; e < kv; ++e) {
+            const uint32_t k = order_key(x[e]) >> 16;
+            atomicAdd(&pairs[k >> 1], 1u << ((k & 1u) << 4));
+          }
+        }
+      } else {
+        for_slice<0, false, kB16Threads>(base, n, [&](float x) {
+          const uint32_t k = order_key(x) >> 16;
+          atomicAdd(&pairs[k >> 1], 1u << ((k & 1u) << 4));
+        });
+      }
+    }
+    if (threadIdx.x == 0) s_next = nxt;
+    __syncthreads();
+    const long long nitem = s_next;
+    RowJob nj{};
+    const void* nbase = nullptr;
+    int nn = 0, nrow = 0, nslice = 0, nlocal = 0;
+    const bool nact = nitem < items && b16_item(a, s_rows, s_jobs, nitem, nj, nbase, nn, nrow, nslice, nlocal);
+    // the next slice's loads go out before this part's stores
+    if (VEC && nact) issue(nbase, nn);
+    if (act) {
+      // the slice's part: thread t writes prefixes t + 1024 i (the count,
+      // relative mass and counter words of the non-empty ones), and clears
+      // the LDS counters it read
+      char* slot = static_cast<char*>(a.slots) + static_cast<size_t>(local) * b16_slot_bytes(a.S);
+      const double l2t = kLog2e / static_cast<double>(j.T);
+      const B16Part pt = b16_part(slot, slice);
+#pragma unroll 1
+      for (int i = 0; i < kB16Per; ++i) {
+        const int bin = i * kB16Threads + static_cast<int>(threadIdx.x);
+        const uint4 lo = s_pairs[2 * bin], hi = s_pairs[2 * bin + 1];
+        const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        uint32_t c[16];
+        b16_unpack(wd, c);
+        uint32_t tot = 0u;
+#pragma unroll
+        for (int sb = 0; sb < 16; ++sb) tot += c[sb];
+        if (!tot) continue;
+        s_pairs[2 * bin] = make_uint4(0u, 0u, 0u, 0u);
+        s_pairs[2 * bin + 1] = make_uint4(0u, 0u, 0u, 0u);
+        store_coherent(pt.cnt12 + bin, tot);
+        store_coherent(reinterpret_cast<uint64_t*>(pt.mass + bin),
+                       static_cast<uint64_t>(__double_as_longlong(b16_mass(c, bin, 0u, b16_value(16 * bin + 15), l2t))));
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          store_coherent(pt.words + q * kMaxBins + bin,
+                         static_cast<uint64_t>(wd[2 * q]) | (static_cast<uint64_t>(wd[2 * q + 1]) << 32));
+      }
+      wait_memory();
+      __syncthreads();
+      uint32_t* arrivals = reinterpret_cast<uint32_t*>(slot);
+      if (threadIdx.x == 0) s_last = arrive(arrivals) == static_cast<uint32_t>(a.S - 1);
+      __syncthreads();
+      if (s_last) {
+        if (threadIdx.x == 0) store_coherent(arrivals, 0u);
+        b16_finish(j, slot, a.S, a.thr + row_id, s_wd, s_wi, &s_pos, &s_above, &s_key);
+      }
+    }
+    __syncthreads();
+    item = nitem;
+    j = nj;
+    base = nbase;
+    n = nn;
+    row_id = nrow;
+    slice = nslice;
+    local = nlocal;
+    act = nact;
+  }
+  // the last workgroup out resets the counter for the next call
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(exits, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1) {
+    store_coherent(head, 0u);
+    store_coherent(exits, 0u);
+  }
 }
 
 }  // namespace
 
+int b16_slices(int V) { return (V + kB16Slice - 1) / kB16Slice; }
+
+// Rows searched together: at most kFilterSlots, and for bf16 rows no more
+// than fit in kB16GroupBytes of parts.
+constexpr size_t kB16GroupBytes = size_t(256) << 20;
+long long filter_group_rows(int V, int dtype) {
+  if (dtype != SV_BF16) return kFilterSlots;
+  const long long fit = static_cast<long long>(kB16GroupBytes / b16_slot_bytes(b16_slices(V)));
+  return fit < 1 ? 1 : (fit < kFilterSlots ? fit : kFilterSlots);
+}
+
+// Compute units of the current device (cached per device).
+long long device_cus() {
+  static long long cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+size_t filter_workspace_bytes(int B, int gamma, int V, int dtype) {
+  const long long rows = static_cast<long long>(B) * (2 * gamma + 1);
+  const long long group = filter_group_rows(V, dtype);
+  const long long slots = rows < group ? rows : group;
+  return kQueueBytes +
+         align_up(static_cast<size_t>(slots) * (dtype == SV_BF16 ? b16_slot_bytes(b16_slices(V)) : sizeof(FilterSlot)));
+}
+
 int launch_filter_rows(const void* target, const void* draft, const float* temperature, const int32_t* top_k,
-                       const float* top_p, int B, int gamma, int V, int dtype, uint32_t* thr, hipStream_t stream) {
-  FilterArgs a{target, gamma > 0 ? draft : nullptr, temperature, top_k, top_p, B, gamma, V, thr};
-  const long long n = static_cast<long long>(B) * (2 * gamma + 1);
-  if (n == 0 || (!top_k && !top_p)) return SV_OK;
-  if (n > 0x7fffffffLL) return SV_ERR_SHAPE;
-  const dim3 grid(static_cast<unsigned>(n));
+                       const float* top_p, int B, int gamma, int V, int dtype, uint32_t* thr, void* slots,
+                       hipStream_t stream) {
+  FilterArgs a{};
+  a.target = target;
+  a.draft = gamma > 0 ? draft : nullptr;
+  a.temperature = temperature;
+  a.top_k = top_k;
+  a.top_p = top_p;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.S = dtype == SV_BF16 ? b16_slices(V) : (V + kSlice - 1) / kSlice;
+  a.queue = static_cast<uint32_t*>(slots);
+  a.slots = static_cast<char*>(slots) + kQueueBytes;
+  a.thr = thr;
+  const long long rows = static_cast<long long>(B) * (2 * gamma + 1);
+  if (rows == 0 || (!top_k && !top_p)) return SV_OK;
   const int kv = dtype == SV_BF16 ? Elem<0>::kVec : Elem<1>::kVec;
   const bool vec = (V % kv == 0) && aligned(target, 16) && (!a.draft || aligned(a.draft, 16));
-  if (dtype == SV_BF16) {
-    if (vec) launch(SV_K_FILTER_ROWS, filter_rows<0, true>, grid, dim3(kFilterThreads), 0, stream, a);
-    else launch(SV_K_FILTER_ROWS, filter_rows<0, false>, grid, dim3(kFilterThreads), 0, stream, a);
-  } else {
-    if (vec) launch(SV_K_FILTER_ROWS, filter_rows<1, true>, grid, dim3(kFilterThreads), 0, stream, a);
-    else launch(SV_K_FILTER_ROWS, filter_rows<1, false>, grid, dim3(kFilterThreads), 0, stream, a);
+  const long long group = filter_group_rows(V, dtype);
+  for (long long r0 = 0; r0 < rows; r0 += group) {
+    a.row0 = static_cast<int>(r0);
+    const long long n = rows - r0 < group ? rows - r0 : group;
+    a.group = static_cast<int>(n);
+    const dim3 grid(static_cast<unsigned>(n * a.S));
+    if (dtype == SV_BF16) {
+      // persistent: one workgroup per CU (the LDS table allows no more)
+      const long long items = n * a.S;
+      const dim3 pgrid(static_cast<unsigned>(items < device_cus() ? items : device_cus()));
+      if (vec) launch(SV_K_FILTER_ROWS, filter_rows_bf16<true>, pgrid, dim3(kB16Threads), 0, stream, a);
+      else launch(SV_K_FILTER_ROWS, filter_rows_bf16<false>, pgrid, dim3(kB16Threads), 0, stream, a);
+    } else {
+      if (vec) launch(SV_K_FILTER_ROWS, filter_rows<1, true>, grid, dim3(kFilterThreads), 0, stream, a);
+      else launch(SV_K_FILTER_ROWS, filter_rows<1, false>, grid, dim3(kFilterThreads), 0, stream, a);
+    }
   }
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }

@@ -17,11 +17,16 @@ inline bool aligned(const void* p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }
 
-// The thresholds of a filtered chain call (sv_filter.hip): one launch over
-// the rows of the sampling requests, writing thr[b][row] = key + 1 of each
-// cut (0: none).  Returns an sv_status.
+// The thresholds of a filtered chain call (sv_filter.hip): launches over the
+// rows of the sampling requests, one per digit of each search, writing
+// thr[b][row] = key + 1 of each cut (0: none).  `slots` is the zero-filled
+// search area of filter_workspace_bytes(B, gamma, V, dtype) bytes, left
+// zero-filled.
+// Returns an sv_status.
 int launch_filter_rows(const void* target, const void* draft, const float* temperature, const int32_t* top_k,
-                       const float* top_p, int B, int gamma, int V, int dtype, uint32_t* thr, hipStream_t stream);
+                       const float* top_p, int B, int gamma, int V, int dtype, uint32_t* thr, void* slots,
+                       hipStream_t stream);
+size_t filter_workspace_bytes(int B, int gamma, int V, int dtype);
 
 // Value of a test control (sv_set_test_hook); 0 when unset.
 long long test_hook(int hook);

@@ -284,6 +284,33 @@ def topk_draft_tokens(ci: ChainInputs, top_k, seed: int) -> np.ndarray:
     return out
 
 
+def topp_draft_tokens(ci: ChainInputs, top_p, seed: int) -> np.ndarray:
+    """Draft tokens of a draft model that decodes with top-p (nucleus)
+    sampling over the whole vocabulary: the draft row's softmax at the
+    request's temperature, its values sorted in descending order, the
+    smallest prefix whose mass reaches p (every value equal to the last one
+    kept), then a Gumbel-max draw among the kept logits; argmax rows for
+    greedy requests."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((ci.B, ci.gamma), dtype=np.int32)
+    for b in range(ci.B):
+        d = _widen(ci.draft[b], ci.dtype).astype(np.float64)
+        t = float(ci.temperature[b])
+        for i in range(ci.gamma):
+            if t > 0.0:
+                z = d[i] / t
+                w = np.exp(z - z.max())
+                w /= w.sum()
+                order = np.argsort(-d[i], kind="stable")
+                cum = np.cumsum(w[order])
+                last = min(int(np.searchsorted(cum, float(np.float32(top_p[b])), side="left")), ci.V - 1)
+                keep = d[i] >= d[i][order[last]]
+                out[b, i] = int(np.argmax(np.where(keep, z + gumbel(rng, (ci.V,)), -np.inf)))
+            else:
+                out[b, i] = int(np.argmax(d[i]))
+    return out
+
+
 def toy_chain(seed: int = SEED_BASE + 1, B: int = 4096, gamma: int = 4, V: int = 5):
     """V=5 fp32 toy: target N(0,1), draft = target + N(0, 0.5^2), T = 1."""
     return chain_inputs(seed, B, gamma, V, dtype="f32", family="gauss",

@@ -63,6 +63,13 @@ def test_kernel_names_and_timing_validation(lib):
 
 
 def test_workspace_queries(lib):
+    base = lib.sv_chain_workspace_bytes(64, 4, 128256, 0)
+    # the filtered call adds its search area: exact counts for bf16 rows are
+    # larger than the fp32 radix histograms
+    assert lib.sv_chain_filtered_workspace_bytes(64, 4, 128256, 0) > lib.sv_chain_filtered_workspace_bytes(
+        64, 4, 128256, 1) > base
+    assert lib.sv_chain_filtered_workspace_bytes(64, 4, 128256, 7) == 0
+    assert lib.sv_chain_filtered_workspace_bytes(64, 33, 128256, 0) == 0
     assert lib.sv_chain_workspace_bytes(64, 4, 128256, 0) > 0
     assert lib.sv_chain_workspace_bytes(64, 33, 128256, 0) == 0   # gamma above the cap
     assert lib.sv_chain_workspace_bytes(64, 4, 0, 0) == 0

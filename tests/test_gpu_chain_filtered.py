@@ -186,3 +186,62 @@ def test_three_launch_form_and_counted_draws():
     pb = np.full(big.B, 0.9, np.float32)
     big.draft_tokens = filtered_draft_tokens(big, kb, pb, 16563)
     filtered_parity(big, kb, pb, 2, "filtered B=300")
+
+
+def plant_near_max(ci, offsets, rng):
+    """Every row gets a cluster of logits at 16 + offsets (f32 values, or bf16
+    patterns of them), above the rest of the row."""
+    for arr in (ci.target, ci.draft):
+        for idx in np.ndindex(arr.shape[:2]):
+            cols = rng.choice(ci.V, size=len(offsets), replace=False)
+            vals = np.float32(16.0) + np.asarray(offsets, np.float32)
+            if ci.dtype == "bf16":
+                arr[idx][cols] = (vals.view(np.uint32) >> 16).astype(np.uint16)
+            else:
+                arr[idx][cols] = vals
+
+
+def test_small_temperatures_topp_f32():
+    """Temperatures so small that the top first-digit bin spans more than 2^900
+    on the scale of the row maximum (the top-p digit is taken again on that
+    scale), next to ordinary ones in the same batch, with several logits
+    within a few T of the maximum."""
+    ci = synth.chain_inputs(16570, B=8, gamma=3, V=5000, dtype="f32", family="gauss",
+                            draft_sigma=0.3, temperature=1.0)
+    T = np.array([0.002, 0.002, 1.0, 0.002, 0.7, 0.003, 0.001, 0.5], np.float32)
+    ci.temperature = T
+    rng = np.random.default_rng(16571)
+    plant_near_max(ci, [0.001, 0.0, -0.0007, -0.002, -0.004, -0.01], rng)
+    p = np.array([0.5, 0.9, 0.9, 0.99, 0.8, 0.7, 0.95, 0.6], np.float32)
+    ci.draft_tokens = filtered_draft_tokens(ci, None, p, 16572)
+    filtered_parity(ci, None, p, 8, "top-p small T f32")
+    k = np.array([3, 5, 100, 2, 50, 4, 6, 1000], np.int32)
+    ci.draft_tokens = filtered_draft_tokens(ci, k, p, 16573)
+    filtered_parity(ci, k, p, 4, "top-k + top-p small T f32")
+
+
+def test_small_temperatures_topp_bf16_ties():
+    """bf16 rows whose maximum is tied several times, at temperatures where
+    only the ties carry mass (the top bin spans more than 2^900)."""
+    ci = synth.chain_inputs(16580, B=6, gamma=2, V=8192, dtype="bf16", family="gauss",
+                            draft_sigma=0.3, temperature=1.0)
+    ci.temperature = np.array([0.001, 0.002, 0.0005, 1.0, 0.001, 0.8], np.float32)
+    rng = np.random.default_rng(16581)
+    plant_near_max(ci, [0.0, 0.0, 0.0, -0.125, -0.25], rng)
+    p = np.array([0.2, 0.5, 0.9, 0.9, 0.7, 0.95], np.float32)
+    ci.draft_tokens = filtered_draft_tokens(ci, None, p, 16582)
+    filtered_parity(ci, None, p, 6, "top-p small T bf16 ties")
+
+
+@pytest.mark.parametrize("V", [1 << 20, (1 << 20) + 13])
+def test_many_slices_per_row(V):
+    """Rows of more than eight slices (the bf16 search's parts beyond its
+    first round of loads), vector and scalar paths, both filters."""
+    ci = synth.chain_inputs(16590 + V % 7, B=2, gamma=1, V=V, dtype="bf16", family="gauss",
+                            draft_sigma=0.4, temperature=0.8)
+    k = np.array([5000, 300000], np.int32)
+    p = np.array([0.6, 0.95], np.float32)
+    ci.draft_tokens = filtered_draft_tokens(ci, k, p, 16591)
+    filtered_parity(ci, k, p, 3, f"filtered V={V}")
+    ci.draft_tokens = filtered_draft_tokens(ci, None, p, 16592)
+    filtered_parity(ci, None, p, 3, f"top-p V={V}")
