@@ -66,28 +66,42 @@ def small_bytes(ci) -> int:
     return ci.B * (4 * ci.gamma + 4 * (ci.gamma + 1) + 4 + 4 * (ci.gamma + 1) + 4)
 
 
-def source_digest() -> str:
-    """Hash of the chain kernel sources; a stored traffic figure is valid only
-    for the sources it was measured on."""
+# Sources of each kernel whose HBM traffic is stored under profiles/.
+KERNEL_SOURCES = {
+    "chain_verify": ("rejection_sampling_verify_15_amd/csrc/sv_chain.hip",
+                     "rejection_sampling_verify_15_amd/csrc/sv_device.hpp"),
+    "filter_rows": ("rejection_sampling_verify_15_amd/csrc/sv_filter.hip",
+                    "rejection_sampling_verify_15_amd/csrc/sv_device.hpp"),
+}
+# The stored counter summary of each workload.
+TRAFFIC_FILES = {"batched": "traffic_batched_chain.json", "deep": "traffic_deep_chain.json",
+                 "single": "traffic_single_chain.json", "topp": "traffic_topp_filter.json"}
+
+
+def source_digest(kernel: str = "chain_verify") -> str:
+    """Hash of a kernel's sources; a stored traffic figure is valid only for
+    the sources it was measured on."""
     h = hashlib.sha256()
-    for rel in ("rejection_sampling_verify_15_amd/csrc/sv_chain.hip",
-                "rejection_sampling_verify_15_amd/csrc/sv_device.hpp"):
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def stored_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None when it is missing or the kernel changed since."""
-    path = os.path.join(ROOT, "profiles", "traffic_batched_chain.json")
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` in `workload` from the committed
+    rocprofv3 counter summary, or None when it is missing or the kernel's
+    sources changed since."""
+    name = TRAFFIC_FILES.get(workload)
+    if name is None:
+        return None
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     k = rec.get("kernels", {}).get(kernel)
-    if k is None or rec.get("source_sha256") != source_digest():
+    if k is None or k.get("source_sha256") != source_digest(k.get("digest_of", kernel)):
         return None
     return k.get("traffic_bytes_per_launch")
 
@@ -253,7 +267,7 @@ def run_chain(args, torch, synth, sv):
     result.update({
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": stored_traffic(dominant) if args.workload == "batched" else None,
+                     "traffic": stored_traffic(args.workload, dominant),
                      "kernel": dominant, "kernel_us": k_us, "algorithmic_bytes": rd_kernel},
         "kernels_us": {name: kt.mean_us(name) for name in kt.launches},
         "kernels_us_per_call": {name: 1e3 * kt.ms[name] / args.steps for name in kt.launches},
