@@ -77,7 +77,10 @@ class SVError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
+    """The in-tree libspecverify.so, or the build named by SV_LIBRARY (such as
+    the host AddressSanitizer build of asan_build.py)."""
+    return os.environ.get("SV_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                        "libspecverify.so")
 
 
 def lib() -> ctypes.CDLL:
