@@ -328,6 +328,10 @@ def run_tree(args, torch, synth, sv, oracle_sample=True):
             "draft row" if mss else "naive sampling, T=1")
     desc = (f"token-tree verify ({mode}): B=32, N=64 nodes, depth <= 8, branching 1..4, V=128256, "
             f"bf16 logits")
+    all_nodes = getattr(args, "tree_all_nodes", False) and not mss
+    if all_nodes:
+        desc += ("; the all-nodes statistics design (every node's row reduced up front, then the "
+                 "descent; the SV_HOOK_TREE_ALL_NODES control)")
     set_bytes = ti.logits.nbytes * (2 if mss else 1)
     R = max(2, math.ceil(2 * MALL_BYTES / set_bytes) + 1)
 
@@ -373,6 +377,8 @@ def run_tree(args, torch, synth, sv, oracle_sample=True):
             for n in [0] + [int(x) for x in path[b, :nacc[b]]]:
                 rows += int(np.any(ti.parents[b] == n))
     rd = rows * ti.V * es
+    if all_nodes:
+        rd = ti.B * ti.N * ti.V * es   # every node's row, whatever the path
     call_us = 1e3 * total_ms / args.steps
     per_call = {name: kt.ms[name] * 1e3 / args.steps for name in kt.launches}
     dominant = max(per_call, key=per_call.get)  # tree_verify; tree_node_pass in the multi-launch form
@@ -630,6 +636,9 @@ def main():
                     help="batched: call spec_verify_chain without the sampling hint")
     ap.add_argument("--cpu-baseline-only", action="store_true",
                     help="time the oracle on the host only and print its JSON (no GPU use)")
+    ap.add_argument("--tree-all-nodes", action="store_true",
+                    help="tree-greedy / tree-sampling: time the all-nodes statistics design instead of "
+                         "path descent")
     ap.add_argument("--top-p", type=float, default=None,
                     help="topk workload: also filter to this top-p mass after top-k (draft tokens stay top-k draws)")
     args = ap.parse_args()
@@ -653,7 +662,11 @@ def main():
     if args.workload == "tree-mask":
         result = run_mask(args, torch, synth, sv)
     elif args.workload.startswith("tree"):
-        result = run_tree(args, torch, synth, sv)
+        if args.tree_all_nodes and args.workload in ("tree-greedy", "tree-sampling"):
+            with sv.library_control(sv.SV_HOOK_TREE_ALL_NODES, 1):
+                result = run_tree(args, torch, synth, sv)
+        else:
+            result = run_tree(args, torch, synth, sv)
     else:
         result = run_chain(args, torch, synth, sv)
     if baseline is not None:

@@ -524,7 +524,10 @@ typedef enum {
   SV_HOOK_CHAIN_SPLIT = 1,    /* != 0: chain calls use the three-launch form */
   SV_HOOK_TREE_SPLIT = 2,     /* != 0: spec_verify_tree uses its launch-per-step form */
   SV_HOOK_SPIN_LIMIT = 3,     /* > 0: each bounded wait of the chain and tree kernels gives up after this many polls */
-  SV_HOOK_COUNT = 4
+  SV_HOOK_TREE_ALL_NODES = 4, /* != 0: spec_verify_tree reduces every node's row first, then descends (the
+                                 all-nodes design, lecture 17 notes section 4.3, kept to be measured against
+                                 path descent); sv_tree_workspace_bytes then sizes its B*N*chunks partials */
+  SV_HOOK_COUNT = 5
 } sv_hook;
 
 SV_API int sv_set_test_hook(int hook, long long value);

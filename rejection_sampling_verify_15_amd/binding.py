@@ -21,7 +21,7 @@ import torch
 SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_ALIGN, SV_ERR_HIP, SV_ERR_SCRATCH = range(8)
 SV_BF16, SV_F32 = 0, 1
 SV_GAVE_UP = -2   # accepted count of a request whose bounded wait gave up
-SV_HOOK_CHAIN_GRID_CAP, SV_HOOK_CHAIN_SPLIT, SV_HOOK_TREE_SPLIT, SV_HOOK_SPIN_LIMIT = range(4)
+SV_HOOK_CHAIN_GRID_CAP, SV_HOOK_CHAIN_SPLIT, SV_HOOK_TREE_SPLIT, SV_HOOK_SPIN_LIMIT, SV_HOOK_TREE_ALL_NODES = range(5)
 SV_MAX_GAMMA = 32
 SV_HINT_MAX_BATCH = 256
 SV_MAX_TOPK = 128

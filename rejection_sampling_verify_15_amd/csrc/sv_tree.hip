@@ -125,17 +125,10 @@ __global__ __launch_bounds__(kThreads) void tree_init(TreeArgs a) {
   }
 }
 
+// One chunk's partial of a node row: the max and lowest-index argmax
+// (greedy, T == 0) or the max and the fp64 sum of exp((x - max) / T).
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void tree_node_pass(TreeArgs a) {
-  const int b = blockIdx.x / a.nchunk;
-  const int c = blockIdx.x % a.nchunk;
-  const TreeState st = a.state[b];
-  if (!st.active) return;
-  const float T = a.temperature[b];
-  const int c0 = c * kChunk;
-  const int c1 = min(a.V, c0 + kChunk);
-  Slice<DT, VEC> s;
-  s.load(node_row<DT>(a, b, st.node), c0, c1);
+__device__ NodePartial chunk_partial(const Slice<DT, VEC>& s, int c0, int c1, float T) {
   NodePartial out{};
   if (T == 0.0f) {
     ArgMax best{-INFINITY, 0x7fffffff};
@@ -179,6 +172,21 @@ __global__ __launch_bounds__(kThreads) void tree_node_pass(TreeArgs a) {
     out.m = m;
     out.s = acc[0];
   }
+  return out;
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void tree_node_pass(TreeArgs a) {
+  const int b = blockIdx.x / a.nchunk;
+  const int c = blockIdx.x % a.nchunk;
+  const TreeState st = a.state[b];
+  if (!st.active) return;
+  const float T = a.temperature[b];
+  const int c0 = c * kChunk;
+  const int c1 = min(a.V, c0 + kChunk);
+  Slice<DT, VEC> s;
+  s.load(node_row<DT>(a, b, st.node), c0, c1);
+  const NodePartial out = chunk_partial(s, c0, c1, T);
   if (threadIdx.x == 0) a.partials[static_cast<size_t>(b) * a.nchunk + c] = out;
 }
 
@@ -188,24 +196,20 @@ __device__ inline void tree_clear_partials(const TreeArgs& a, int b) {
   for (int c = threadIdx.x; c < a.nchunk; c += kThreads) p[c] = NodePartial{};
 }
 
+// The choice at request b's node st.node from that node's chunk partials p:
+// the token (argmax, or the inverse-CDF draw narrowed to a chunk and scanned
+// there in fp64 with u[b][node]), and the child carrying it.  Writes the
+// request's outputs for this level and returns its next state (inactive once
+// it stops).  With `clear`, p is zeroed once read.  Called by every thread of
+// the workgroup.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void tree_choose(TreeArgs a) {
+__device__ TreeState choose_at(const TreeArgs& a, int b, const TreeState st, NodePartial* p, bool clear) {
   __shared__ int s_chunk, s_hit, s_last, s_child, s_token;
   __shared__ float s_m;
   __shared__ double s_before, s_target;
-  const int b = blockIdx.x;
-  const TreeState st = a.state[b];
-  if (!st.active) {
-    // every thread has read active == 0, so zeroing the state splits no one
-    if (a.last) {
-      tree_clear_partials(a, b);
-      if (threadIdx.x == 0) a.state[b] = TreeState{};
-    }
-    return;
-  }
   const float T = a.temperature[b];
-  const NodePartial* p = a.partials + static_cast<size_t>(b) * a.nchunk;
   const bool greedy = T == 0.0f;
+  __syncthreads();  // a previous choice's readers of the shared words are done
   if (threadIdx.x == 0) {
     s_hit = 0x7fffffff;
     s_last = -1;
@@ -243,7 +247,8 @@ __global__ __launch_bounds__(kThreads) void tree_choose(TreeArgs a) {
     }
   }
   __syncthreads();
-  if (a.last) tree_clear_partials(a, b);  // only thread 0 read them, before the barrier
+  if (clear)  // only thread 0 read them, before the barrier
+    for (int c = threadIdx.x; c < a.nchunk; c += kThreads) p[c] = NodePartial{};
   if (!greedy) {
     const double inv_t = 1.0 / static_cast<double>(T);
     constexpr int kPerThread = kChunk / kThreads;
@@ -286,19 +291,67 @@ __global__ __launch_bounds__(kThreads) void tree_choose(TreeArgs a) {
   for (int j = st.node + 1 + threadIdx.x; j < a.N; j += kThreads)
     if (par[j] == st.node && tok[j] == c_tok) atomicMin(&s_child, j);
   __syncthreads();
+  const int L1 = a.max_depth + 1;
+  const int child = s_child;
   if (threadIdx.x == 0) {
-    const int L1 = a.max_depth + 1;
-    const int child = s_child;
-    if (child != 0x7fffffff) {
-      a.out_tokens[static_cast<size_t>(b) * L1 + st.len] = c_tok;
-      a.out_path[static_cast<size_t>(b) * L1 + st.len] = child;
-      a.state[b] = a.last ? TreeState{} : TreeState{child, st.len + 1, 1, 0};
-    } else {
-      a.out_tokens[static_cast<size_t>(b) * L1 + st.len] = c_tok;
-      a.out_n[b] = st.len;
-      a.state[b] = a.last ? TreeState{} : TreeState{st.node, st.len, 0, 0};
-    }
+    a.out_tokens[static_cast<size_t>(b) * L1 + st.len] = c_tok;
+    if (child != 0x7fffffff) a.out_path[static_cast<size_t>(b) * L1 + st.len] = child;
+    else a.out_n[b] = st.len;
   }
+  return child != 0x7fffffff ? TreeState{child, st.len + 1, 1, 0} : TreeState{st.node, st.len, 0, 0};
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void tree_choose(TreeArgs a) {
+  const int b = blockIdx.x;
+  const TreeState st = a.state[b];
+  NodePartial* p = a.partials + static_cast<size_t>(b) * a.nchunk;
+  if (!st.active) {
+    // every thread has read active == 0, so zeroing the state splits no one
+    if (a.last) {
+      tree_clear_partials(a, b);
+      if (threadIdx.x == 0) a.state[b] = TreeState{};
+    }
+    return;
+  }
+  const TreeState next = choose_at<DT>(a, b, st, p, a.last);
+  if (threadIdx.x == 0) a.state[b] = a.last ? TreeState{} : next;
+}
+
+// ---------------------------------------------------------------------------
+// all-nodes statistics (a test control: the design that reduces every node's
+// row up front, measured against path descent)
+// ---------------------------------------------------------------------------
+// tree_all_pass: one workgroup per (request, node, chunk), the chunk partials
+// of every node of every valid request (all B * N rows read); tree_all_descend:
+// one workgroup per request, the choices level by level from those partials
+// (the draw's crossing chunk read again), then its partials and state back to
+// zero.  Partials: [B][N][nchunk].
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void tree_all_pass(TreeArgs a) {
+  const int c = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.nchunk));
+  const long long bn = blockIdx.x / static_cast<unsigned>(a.nchunk);
+  const int b = static_cast<int>(bn / a.N);
+  const int node = static_cast<int>(bn - static_cast<long long>(b) * a.N);
+  if (!a.state[b].active) return;
+  const float T = a.temperature[b];
+  const int c0 = c * kChunk;
+  const int c1 = min(a.V, c0 + kChunk);
+  Slice<DT, VEC> s;
+  s.load(node_row<DT>(a, b, node), c0, c1);
+  const NodePartial out = chunk_partial(s, c0, c1, T);
+  if (threadIdx.x == 0) a.partials[static_cast<size_t>(bn) * a.nchunk + c] = out;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void tree_all_descend(TreeArgs a) {
+  const int b = blockIdx.x;
+  TreeState st = a.state[b];
+  NodePartial* p = a.partials + static_cast<size_t>(b) * a.N * a.nchunk;
+  while (st.active) st = choose_at<DT>(a, b, st, p + static_cast<size_t>(st.node) * a.nchunk, false);
+  __syncthreads();
+  for (long long i = threadIdx.x; i < static_cast<long long>(a.N) * a.nchunk; i += kThreads) p[i] = NodePartial{};
+  if (threadIdx.x == 0) a.state[b] = TreeState{};
 }
 
 // ---------------------------------------------------------------------------
@@ -686,17 +739,19 @@ __global__ __launch_bounds__(kWave) void tree_verify(TreeFused a) {
 
 struct TreeLayout {
   size_t state, partials, total;                       // multi-launch form
+  size_t a_total;                                      // all-nodes form (partials [B][N][nchunk])
   size_t f_ctl, f_chunks, f_totals, f_lanes;  // single launch (same buffer)
   size_t f_total;
 };
 
 static int tree_fused_chunks(int V) { return (V + kTreeChunk - 1) / kTreeChunk; }
 
-static TreeLayout tree_layout(int B, int V) {
+static TreeLayout tree_layout(int B, int V, int N = 1) {
   TreeLayout L{};
   L.state = 0;
   L.partials = align_up(static_cast<size_t>(B) * sizeof(TreeState));
   L.total = align_up(L.partials + static_cast<size_t>(B) * num_chunks(V) * sizeof(NodePartial));
+  L.a_total = align_up(L.partials + static_cast<size_t>(B) * N * num_chunks(V) * sizeof(NodePartial));
   const size_t nc = static_cast<size_t>(tree_fused_chunks(V));
   size_t off = 0;
   L.f_ctl = off;    off = align_up(off + static_cast<size_t>(B) * kCtlStride * sizeof(uint64_t));
@@ -711,7 +766,7 @@ static TreeLayout tree_layout(int B, int V) {
 // grid within kTreeMaxGrid blocks (and no test hook asking otherwise).
 constexpr long long kTreeMaxGrid = 1 << 20;
 static bool tree_fused_fits(int B, int V) {
-  if (test_hook(SV_HOOK_TREE_SPLIT) != 0) return false;
+  if (test_hook(SV_HOOK_TREE_SPLIT) != 0 || test_hook(SV_HOOK_TREE_ALL_NODES) != 0) return false;
   const long long nc = tree_fused_chunks(V);
   return nc <= kTreeMaxChunks && static_cast<long long>(B) * (nc + 1) <= kTreeMaxGrid;
 }
@@ -722,6 +777,13 @@ static int launch_tree(TreeArgs a, hipStream_t stream) {
   if (n > 0x7fffffffLL) return SV_ERR_SHAPE;
   a.last = 0;
   launch(SV_K_TREE_INIT, tree_init, dim3(a.B), dim3(kThreads), a.N * sizeof(int32_t), stream, a);
+  if (test_hook(SV_HOOK_TREE_ALL_NODES) != 0) {
+    const long long na = n * a.N;
+    if (na > 0x7fffffffLL) return SV_ERR_SHAPE;
+    launch(SV_K_TREE_NODE_PASS, tree_all_pass<DT, VEC>, dim3(static_cast<unsigned>(na)), dim3(kThreads), 0, stream, a);
+    launch(SV_K_TREE_CHOOSE, tree_all_descend<DT>, dim3(a.B), dim3(kThreads), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+  }
   for (int step = 0; step <= a.max_depth; ++step) {
     launch(SV_K_TREE_NODE_PASS, tree_node_pass<DT, VEC>, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, stream, a);
     a.last = step == a.max_depth;
@@ -736,9 +798,9 @@ using namespace sv;
 
 extern "C" size_t sv_tree_workspace_bytes(int B, int N, int V, int dtype) {
   (void)dtype;
-  (void)N;
   if (B < 0 || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > SV_MAX_VOCAB) return 0;
-  const TreeLayout L = tree_layout(B, V);
+  const TreeLayout L = tree_layout(B, V, N);
+  if (test_hook(SV_HOOK_TREE_ALL_NODES) != 0) return L.a_total;
   // either form may run (it depends on max_depth, given at call time)
   return tree_fused_chunks(V) <= kTreeMaxChunks ? std::max(L.total, L.f_total) : L.total;
 }
@@ -759,9 +821,10 @@ extern "C" int spec_verify_tree(const void* target_logits, const int32_t* node_t
     return SV_ERR_NULL;
   const size_t es = dtype == SV_BF16 ? 2 : 4;
   if (!aligned(target_logits, es)) return SV_ERR_ALIGN;
-  const TreeLayout L = tree_layout(B, V);
+  const TreeLayout L = tree_layout(B, V, N);
   const bool fused = tree_fused_fits(B, V);
-  if (workspace_bytes < (fused ? L.f_total : L.total) || !aligned(workspace, 256)) return SV_ERR_WORKSPACE;
+  const size_t need = fused ? L.f_total : (test_hook(SV_HOOK_TREE_ALL_NODES) != 0 ? L.a_total : L.total);
+  if (workspace_bytes < need || !aligned(workspace, 256)) return SV_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const int kv = dtype == SV_BF16 ? Elem<0>::kVec : Elem<1>::kVec;

@@ -154,10 +154,10 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 # test controls and the recovery after a give-up (host logic only)
 # ---------------------------------------------------------------------------
 def test_test_hook_validation(lib):
-    assert lib.sv_set_test_hook(binding.SV_HOOK_SPIN_LIMIT + 1, 1) == sv.SV_ERR_SHAPE
+    assert lib.sv_set_test_hook(binding.SV_HOOK_TREE_ALL_NODES + 1, 1) == sv.SV_ERR_SHAPE
     assert lib.sv_set_test_hook(-1, 1) == sv.SV_ERR_SHAPE
     assert lib.sv_set_test_hook(binding.SV_HOOK_CHAIN_SPLIT, -1) == sv.SV_ERR_SHAPE
-    for h in range(4):
+    for h in range(5):
         assert lib.sv_set_test_hook(h, 0) == sv.SV_OK
 
 

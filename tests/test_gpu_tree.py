@@ -200,3 +200,19 @@ def test_single_launch_returns_workspace_to_zero():
         tally.add(compare_tree(ref, ot.cpu().numpy(), op.cpu().numpy(), on.cpu().numpy()))
     print(f"[tree workspace] {tally}", flush=True)
     tally.check("tree workspace")
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_all_nodes_design_matches(T):
+    """The all-nodes statistics form (SV_HOOK_TREE_ALL_NODES: every node's row
+    reduced up front, then the descent) gives path descent's results: parity
+    with the oracle at the token-tree shape, on small deep trees with mixed
+    modes and an invalid request, and the workspace left zero."""
+    with sv.library_control(sv.SV_HOOK_TREE_ALL_NODES, 1):
+        ti = synth.tree_inputs(temperature=T)
+        tree_parity(ti, 1 if T == 0.0 else 4, f"all-nodes T={T}")
+        small = synth.tree_inputs(seed=311, B=16, N=40, V=3001, max_depth=6, temperature=max(T, 0.7),
+                                  draft_sigma=0.3, dtype="f32", family="gauss")
+        small.temperature[::3] = 0.0
+        small.parents[5, 0] = 0    # an invalid request among valid ones
+        tree_parity(small, 10, f"all-nodes small T={T}")
