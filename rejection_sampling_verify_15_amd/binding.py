@@ -274,6 +274,72 @@ def verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_toke
     return out_tokens, out_num_accepted
 
 
+class PreparedCall:
+    """One entry point with its arguments checked and marshalled once: each
+    call is the C call alone (about the cost of one kernel launch on the
+    host), for loops that verify into the same device buffers step after step.
+    The tensors are held, so their memory stays valid; the stream is the one
+    current when the call was prepared."""
+
+    def __init__(self, fn, name: str, args, outputs, keep):
+        self._fn, self._name, self._args = fn, name, tuple(args)
+        self.outputs = outputs
+        self._keep = keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != SV_OK:
+            raise SVError(st, self._name)
+        return self.outputs
+
+
+def prepare_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: torch.Tensor,
+                  uniforms: torch.Tensor, temperature: torch.Tensor,
+                  out_tokens: Optional[torch.Tensor] = None,
+                  out_num_accepted: Optional[torch.Tensor] = None,
+                  ws: Optional[torch.Tensor] = None, sampling_hint=None) -> PreparedCall:
+    """verify_chain's checks done once: returns a PreparedCall whose every
+    call runs spec_verify_chain (or spec_verify_chain_hinted) on these same
+    tensors, whose contents the caller may change between calls, and returns
+    (out_tokens, out_num_accepted)."""
+    _need_cuda(target, "target")
+    if target.dim() != 3:
+        raise ValueError("target must be [B, gamma+1, V]")
+    B, G1, V = target.shape
+    gamma = G1 - 1
+    dev = target.device
+    dt = _dtype_code(target)
+    if draft is not None:
+        _need_cuda(draft, "draft")
+        if draft.dtype != target.dtype or tuple(draft.shape) != (B, gamma, V):
+            raise ValueError("draft must match target's dtype with shape [B, gamma, V]")
+    for name, t, shape, dtype in (("draft_tokens", draft_tokens, (B, gamma), torch.int32),
+                                  ("uniforms", uniforms, (B, gamma + 1), torch.float32),
+                                  ("temperature", temperature, (B,), torch.float32)):
+        _need_cuda(t, name)
+        if tuple(t.shape) != shape or t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype} with shape {shape}")
+    if out_tokens is None:
+        out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    for name, t, shape in (("out_tokens", out_tokens, (B, gamma + 1)), ("out_num_accepted", out_num_accepted, (B,))):
+        _need_cuda(t, name)
+        if tuple(t.shape) != shape or t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32 with shape {shape}")
+    L = lib()
+    if ws is None:
+        ws = workspace(L.sv_chain_workspace_bytes(B, gamma, V, dt), dev)
+    head = [_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature)]
+    tail = [B, gamma, V, dt, _ptr(out_tokens), _ptr(out_num_accepted), _ptr(ws), ws.numel(), _stream_handle(dev)]
+    keep = (target, draft, draft_tokens, uniforms, temperature, ws)
+    if sampling_hint is not None:
+        hint = sampling_hint_array(sampling_hint, B)
+        return PreparedCall(L.spec_verify_chain_hinted, "spec_verify_chain_hinted", head + [hint] + tail,
+                            (out_tokens, out_num_accepted), keep + (hint,))
+    return PreparedCall(L.spec_verify_chain, "spec_verify_chain", head + tail, (out_tokens, out_num_accepted), keep)
+
+
 def verify_chain_filtered(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: torch.Tensor,
                           uniforms: torch.Tensor, temperature: torch.Tensor,
                           top_k: Optional[torch.Tensor] = None, top_p: Optional[torch.Tensor] = None,

@@ -311,3 +311,26 @@ def test_graph_capture_replays_match_eager():
         other_t, other_n = sv.verify_chain(tgt, drf, tok, to_device(ci.fresh_uniforms(4242 + r)), T, ws=ws)
         torch.cuda.synchronize()
         assert int(other_n.item()) >= 0
+
+
+def test_prepared_call_matches_the_checked_call():
+    """prepare_chain: the same outputs as verify_chain, call after call, with
+    new uniforms written into the same buffer; and the status of a failing
+    call raised."""
+    ci = synth.chain_inputs(16601, B=12, gamma=3, V=20000, dtype="bf16", family="peaked",
+                            draft_sigma=0.6, temperature=0.9, greedy_odd=True)
+    tgt = to_device_logits(ci.target, ci.dtype)
+    drf = to_device_logits(ci.draft, ci.dtype)
+    tok = to_device(ci.draft_tokens.astype(np.int32))
+    T = to_device(ci.temperature.astype(np.float32))
+    u = to_device(ci.uniforms)
+    for hint in (None, ci.temperature > 0):
+        call = sv.prepare_chain(tgt, drf, tok, u, T, sampling_hint=hint)
+        for s in range(4):
+            u.copy_(to_device(ci.fresh_uniforms(16602 + s)))
+            ot, on = call()
+            et, en = sv.verify_chain(tgt, drf, tok, u, T)
+            assert torch.equal(ot, et) and torch.equal(on, en)
+    bad = sv.prepare_chain(tgt, drf, tok, u, T, ws=torch.zeros(256, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(sv.SVError):
+        bad()
