@@ -541,19 +541,26 @@ __device__ inline B16Part b16_part(char* slot, int s) {
 
 // Weights of the 16 values of prefix `bin` relative to value `ref`: the
 // values of one prefix share sign and exponent, so they are evenly spaced
-// and their weights form a geometric sequence, w(s - 1) = w(s) * q from the
-// top value down.  Two fp64 exponentials per prefix; the rest are products.
-// The prefixes of inf and NaN values weigh 0 (only -inf is a valid logit
-// there).
+// and their weights form a geometric sequence, w(s - 1) = w(s) * q, taken
+// from the prefix's highest value present (s_hi) down, so every weight is at
+// most 1 when ref is at least that value (ref = M, or the prefix's top).  Two
+// fp64 exponentials per prefix; the rest are products.  The prefixes of inf
+// and NaN values weigh 0 (only -inf is a valid logit there).
 struct B16Weights {
-  double top, q;  // weight of the prefix's top value, ratio between neighbours
+  double top, q;  // weight of value s_hi, ratio between neighbours
+  int s_hi;       // highest sub-index with a count (-1: none)
 };
 __device__ inline double b16_value(uint32_t k16) { return static_cast<double>(key_value(full_key<0>(k16))); }
-__device__ inline B16Weights b16_weights(int bin, double ref, double l2t) {
+__device__ inline B16Weights b16_weights(const uint32_t (&c)[16], int bin, double ref, double l2t) {
+  int s_hi = -1;
+#pragma unroll
+  for (int sb = 0; sb < 16; ++sb)
+    if (c[sb]) s_hi = sb;
   const double v15 = b16_value(static_cast<uint32_t>(16 * bin + 15));
   const double v14 = b16_value(static_cast<uint32_t>(16 * bin + 14));
-  if (!__builtin_isfinite(v15) || !__builtin_isfinite(v14)) return B16Weights{0.0, 0.0};
-  return B16Weights{exp2_neg(__builtin_fmin((v15 - ref) * l2t, 0.0)), exp2_neg((v14 - v15) * l2t)};
+  if (s_hi < 0 || !__builtin_isfinite(v15) || !__builtin_isfinite(v14)) return B16Weights{0.0, 0.0, s_hi};
+  const double vh = b16_value(static_cast<uint32_t>(16 * bin + s_hi));
+  return B16Weights{exp2_neg(__builtin_fmin((vh - ref) * l2t, 0.0)), exp2_neg((v14 - v15) * l2t), s_hi};
 }
 __device__ inline void b16_unpack(const uint32_t (&w)[8], uint32_t (&c)[16]) {
 #pragma unroll
@@ -570,10 +577,11 @@ __device__ inline void b16_add_quad(uint64_t two, uint32_t* c) {
 }
 // Mass of the prefix's values with key >= floor16 (counts c) relative to ref.
 __device__ inline double b16_mass(const uint32_t (&c)[16], int bin, uint32_t floor16, double ref, double l2t) {
-  const B16Weights w = b16_weights(bin, ref, l2t);
+  const B16Weights w = b16_weights(c, bin, ref, l2t);
   double m = 0.0, x = w.top;
 #pragma unroll
   for (int sb = 15; sb >= 0; --sb) {
+    if (sb > w.s_hi) continue;
     if (c[sb] && static_cast<uint32_t>(16 * bin + sb) >= floor16) m += static_cast<double>(c[sb]) * x;
     x *= w.q;
   }
@@ -585,11 +593,12 @@ __device__ inline double b16_mass(const uint32_t (&c)[16], int bin, uint32_t flo
 // rounding leaves `want` above them all.
 __device__ inline uint32_t b16_walk(const uint32_t (&c)[16], int bin, uint32_t floor16, double acc, double want,
                                     bool mass, double Mv, double l2t) {
-  const B16Weights w = b16_weights(bin, Mv, l2t);
+  const B16Weights w = b16_weights(c, bin, Mv, l2t);
   uint32_t key = 0xffffffffu, low = static_cast<uint32_t>(16 * bin);
   double x = w.top;
 #pragma unroll
   for (int sb = 15; sb >= 0; --sb) {
+    if (sb > w.s_hi) continue;
     const uint32_t k = static_cast<uint32_t>(16 * bin + sb);
     const double ws = x;
     x *= w.q;

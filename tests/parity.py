@@ -243,17 +243,18 @@ def oracle_chain_many(ci, u_sets, requests=None):
 # ---------------------------------------------------------------------------
 # the filtered chain (consistent top-k / top-p over the whole vocabulary)
 # ---------------------------------------------------------------------------
-def oracle_filtered_many(ci, u_sets, top_k=None, top_p=None):
+def oracle_filtered_many(ci, u_sets, top_k=None, top_p=None, requests=None):
     """Oracle results of the filtered chain for each uniform set, computing
-    every request's filtered distributions once.  Each result carries the
-    smallest top-p cut margin of each request."""
+    every request's filtered distributions once (for the requests listed,
+    else all).  Each result carries the smallest top-p cut margin of each
+    request."""
     import oracle
     from oracle import specverify_oracle as so
 
     B, G = ci.B, ci.gamma
     results = [so.FilteredChainResult(np.full((B, G + 1), -1, dtype=np.int32), np.full(B, -1, dtype=np.int32),
                                       [[] for _ in range(B)], np.full(B, np.inf)) for _ in u_sets]
-    for b in range(B):
+    for b in (range(B) if requests is None else requests):
         T = float(np.float32(ci.temperature[b]))
         toks = np.asarray(ci.draft_tokens[b], dtype=np.int64)
         if so._request_invalid(toks, u_sets[0][b], T, ci.V):
@@ -278,13 +279,15 @@ def oracle_filtered_many(ci, u_sets, top_k=None, top_p=None):
     return results
 
 
-def compare_filtered(res, tok_gpu, n_gpu) -> Tally:
-    """compare_chain, where a request whose top-p cut lies within the window
-    of p counts its decisions as in-window: a disagreement there is a
-    boundary mismatch, not a hard failure."""
+def compare_filtered(res, tok_gpu, n_gpu, requests=None) -> Tally:
+    """compare_chain (over the requests listed, else all), where a request
+    whose top-p cut lies within the window of p counts its decisions as
+    in-window: a disagreement there is a boundary mismatch, not a hard
+    failure."""
     tally = Tally()
-    near = [b for b in range(len(n_gpu)) if res.cut_margin[b] < WINDOW]
-    far = [b for b in range(len(n_gpu)) if res.cut_margin[b] >= WINDOW]
+    todo = range(len(n_gpu)) if requests is None else requests
+    near = [b for b in todo if res.cut_margin[b] < WINDOW]
+    far = [b for b in todo if res.cut_margin[b] >= WINDOW]
     tally.add(compare_chain(res, tok_gpu, n_gpu, requests=far))
     for b in near:
         t = compare_chain(res, tok_gpu, n_gpu, requests=[b])

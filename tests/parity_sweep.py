@@ -51,7 +51,43 @@ WORKLOADS = {
     "tree_mss_B32_N64_V128256": (
         "mss", lambda s: synth.tree_inputs(seed=s, temperature=1.0, keep_draft=True),
         [synth.SEED_BASE + 5, 21401, 21402], 250),
+    "topp09_B64_g4_V128256": (
+        "filtered", lambda s: topp_batched(s), [synth.SEED_BASE + 3, 21501, 21502, 21503], 200),
+    "filtered_mixed_B64_g4_V128256": (
+        "filtered", lambda s: mixed_filters(s), [21601, 21602, 21603, 21604], 200),
 }
+
+
+class Filtered:
+    """Chain inputs plus the per-request filter arrays of a filtered call."""
+
+    def __init__(self, ci, top_k, top_p):
+        self.ci, self.top_k, self.top_p = ci, top_k, top_p
+
+    def __getattr__(self, name):
+        return getattr(self.ci, name)
+
+
+def topp_batched(seed):
+    """The batched inputs, every sampling request cut to its top-p 0.9 mass,
+    draft tokens from the cut draft rows."""
+    ci = synth.batched_chain(seed=seed)
+    p = np.full(ci.B, 0.9, np.float32)
+    ci.draft_tokens = synth.topp_draft_tokens(ci, p, seed + 7)
+    return Filtered(ci, None, p)
+
+
+def mixed_filters(seed):
+    """The batched shape with a filter per request: top-k 50 or 1024 or none,
+    then top-p 0.8 or 0.9 or none; draft tokens drawn from the draft rows cut
+    alike (by the oracle's filter, as a draft model decoding with it would)."""
+    from test_gpu_chain_filtered import filtered_draft_tokens
+    ci = synth.batched_chain(seed=seed)
+    rng = np.random.default_rng(seed + 11)
+    k = rng.choice(np.array([50, 1024, ci.V], np.int32), size=ci.B)
+    p = rng.choice(np.array([0.8, 0.9, 1.0], np.float32), size=ci.B)
+    ci.draft_tokens = filtered_draft_tokens(ci, k, p, seed + 13)
+    return Filtered(ci, k, p)
 
 
 def fingerprint(*arrays) -> str:
@@ -69,13 +105,15 @@ def fingerprint(*arrays) -> str:
 def inputs_fingerprint(kind, x) -> str:
     if kind == "chain":
         return fingerprint(x.target, x.draft, x.draft_tokens, x.temperature, x.uniforms)
+    if kind == "filtered":
+        return fingerprint(x.target, x.draft, x.draft_tokens, x.temperature, x.uniforms, x.top_k, x.top_p)
     return fingerprint(x.logits, x.draft_logits, x.node_tokens, x.parents, x.temperature,
                        x.uniforms, x.draw_uniforms)
 
 
 def uniform_sets(kind, x, seed, n_sets):
     """[(u,)] for chain and naive trees, [(u_accept, u_draw)] for MSS."""
-    shape = (x.B, x.gamma + 1) if kind == "chain" else (x.B, x.N)
+    shape = (x.B, x.gamma + 1) if kind in ("chain", "filtered") else (x.B, x.N)
     first = (x.uniforms,) if kind != "mss" else (x.uniforms, x.draw_uniforms)
     out = [first]
     for s in range(1, n_sets):
@@ -107,13 +145,19 @@ def gpu_phase(out_dir, only, sets=None):
             print(f"[gpu] {name} seed={seed} built in {time.time() - t0:.1f}s", flush=True)
             us = uniform_sets(kind, x, seed, n_sets)
             toks, paths, ns = [], [], []
-            if kind == "chain":
+            if kind in ("chain", "filtered"):
                 tgt = to_device_logits(x.target, x.dtype)
                 drf = to_device_logits(x.draft, x.dtype)
                 dt = to_device(x.draft_tokens.astype(np.int32))
                 T = to_device(x.temperature.astype(np.float32))
+                if kind == "filtered":
+                    kd = None if x.top_k is None else to_device(np.asarray(x.top_k, np.int32))
+                    pd = None if x.top_p is None else to_device(np.asarray(x.top_p, np.float32))
                 for (u,) in us:
-                    ot, on = sv.verify_chain(tgt, drf, dt, to_device(u), T)
+                    if kind == "filtered":
+                        ot, on = sv.verify_chain_filtered(tgt, drf, dt, to_device(u), T, kd, pd)
+                    else:
+                        ot, on = sv.verify_chain(tgt, drf, dt, to_device(u), T)
                     toks.append(ot.cpu().numpy())
                     ns.append(on.cpu().numpy())
             else:
@@ -152,10 +196,16 @@ def _compare_part(requests):
     """Oracle results and tally for a subset of requests over every uniform set
     (runs in a forked worker that inherited _STATE)."""
     import oracle
-    from parity import Tally, compare_chain, compare_tree, compare_tree_mss, oracle_chain_many
+    from parity import (Tally, compare_chain, compare_filtered, compare_tree, compare_tree_mss, oracle_chain_many,
+                        oracle_filtered_many)
 
     kind, x, us, gpu = _STATE["kind"], _STATE["x"], _STATE["us"], _STATE["gpu"]
     tally = Tally()
+    if kind == "filtered":
+        refs = oracle_filtered_many(x.ci, [u[0] for u in us], x.top_k, x.top_p, requests=requests)
+        for s, r in enumerate(refs):
+            tally.add(compare_filtered(r, gpu["tokens"][s], gpu["n"][s], requests=requests))
+        return tally
     if kind == "chain":
         refs = oracle_chain_many(x, [u[0] for u in us], requests=requests)
         for s, r in enumerate(refs):

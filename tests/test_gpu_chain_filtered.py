@@ -245,3 +245,22 @@ def test_many_slices_per_row(V):
     filtered_parity(ci, k, p, 3, f"filtered V={V}")
     ci.draft_tokens = filtered_draft_tokens(ci, None, p, 16592)
     filtered_parity(ci, None, p, 3, f"top-p V={V}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_cut_inside_the_top_prefix(dtype):
+    """The maximum's 12-bit prefix holds several values and the cut falls
+    inside it while the prefixes below carry mass too (the weights within the
+    top prefix must be on the scale of the maximum, not of the prefix's top
+    value)."""
+    ci = synth.chain_inputs(16610, B=8, gamma=3, V=6000, dtype=dtype, family="gauss",
+                            draft_sigma=0.3, temperature=0.5)
+    ci.temperature = np.array([0.5, 0.5, 0.8, 0.3, 0.5, 1.0, 0.4, 0.6], np.float32)
+    rng = np.random.default_rng(16611)
+    plant_near_max(ci, [0.5, 0.25, 0.125, 0.0, 0.0, -0.125, -0.25, -0.5, -1.0], rng)
+    p = np.array([0.3, 0.5, 0.7, 0.9, 0.2, 0.6, 0.4, 0.8], np.float32)
+    ci.draft_tokens = filtered_draft_tokens(ci, None, p, 16612)
+    filtered_parity(ci, None, p, 12, f"cut in the top prefix {dtype}")
+    k = np.array([3, 6, 1000, 8, 2, 5000, 4, 7], np.int32)
+    ci.draft_tokens = filtered_draft_tokens(ci, k, p, 16613)
+    filtered_parity(ci, k, p, 8, f"top-k then a cut in the top prefix {dtype}")
