@@ -55,6 +55,10 @@ WORKLOADS = {
         "filtered", lambda s: topp_batched(s), [synth.SEED_BASE + 3, 21501, 21502, 21503], 200),
     "filtered_mixed_B64_g4_V128256": (
         "filtered", lambda s: mixed_filters(s), [21601, 21602, 21603, 21604], 200),
+    "filtered_mixed_f32_B64_g4_V128256": (
+        "filtered", lambda s: mixed_filters(s, dtype="f32"), [21701, 21702, 21703, 21704], 200),
+    "filtered_small_T_B64_g4_V128256": (
+        "filtered", lambda s: mixed_filters(s, small_t=True), [21801, 21802, 21803, 21804], 200),
 }
 
 
@@ -77,13 +81,22 @@ def topp_batched(seed):
     return Filtered(ci, None, p)
 
 
-def mixed_filters(seed):
-    """The batched shape with a filter per request: top-k 50 or 1024 or none,
-    then top-p 0.8 or 0.9 or none; draft tokens drawn from the draft rows cut
-    alike (by the oracle's filter, as a draft model decoding with it would)."""
+def mixed_filters(seed, dtype="bf16", small_t=False):
+    """The batched shape (bf16, or fp32 logits of the same recipe) with a
+    filter per request: top-k 50 or 1024 or none, then top-p 0.8 or 0.9 or
+    none; draft tokens drawn from the draft rows cut alike (by the oracle's
+    filter, as a draft model decoding with it would).  small_t: the sampling
+    requests' temperatures drawn log-uniformly from [0.005, 0.1]."""
     from test_gpu_chain_filtered import filtered_draft_tokens
-    ci = synth.batched_chain(seed=seed)
+    if dtype == "bf16":
+        ci = synth.batched_chain(seed=seed)
+    else:
+        ci = synth.chain_inputs(seed, 64, 4, 128256, dtype=dtype, family="peaked", draft_sigma=(0.3, 2.0),
+                                temperature=0.7, greedy_odd=True, name="batched-f32")
     rng = np.random.default_rng(seed + 11)
+    if small_t:
+        t = np.exp(rng.uniform(np.log(0.005), np.log(0.1), size=ci.B)).astype(np.float32)
+        ci.temperature = np.where(ci.temperature > 0, t, 0.0).astype(np.float32)
     k = rng.choice(np.array([50, 1024, ci.V], np.int32), size=ci.B)
     p = rng.choice(np.array([0.8, 0.9, 1.0], np.float32), size=ci.B)
     ci.draft_tokens = filtered_draft_tokens(ci, k, p, seed + 13)
