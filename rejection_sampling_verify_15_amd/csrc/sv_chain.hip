@@ -44,6 +44,8 @@
 #include <algorithm>
 #include <mutex>
 
+#include <atomic>
+
 #include "sv_device.hpp"
 #include "sv_host.hpp"
 
@@ -1297,33 +1299,33 @@ constexpr long long kUnitPool = 16384;
 // Workgroups of chain_stream that fit on the current device at once.
 template <int DT, bool VEC>
 static long long stream_capacity() {
-  static long long cached[64] = {0};
+  static std::atomic<long long> cached[64];  // per device, filled on first use (any thread)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
+  if (cached[dev].load(std::memory_order_relaxed) == 0) {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_stream<DT, VEC>, kThreads, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 || cus < 1)
       return 1024;
-    cached[dev] = static_cast<long long>(per_cu) * cus;
+    cached[dev].store(static_cast<long long>(per_cu) * cus, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return cached[dev].load(std::memory_order_relaxed);
 }
 
 // Wave slots of chain_verify on the current device (one-wave workgroups).
 template <int DT, bool VEC, int SPAN>
 static long long verify_capacity() {
-  static long long cached[64] = {0};
+  static std::atomic<long long> cached[64];  // per device, filled on first use (any thread)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
+  if (cached[dev].load(std::memory_order_relaxed) == 0) {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_verify<DT, VEC, SPAN>, kWave, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 || cus < 1)
       return 0;
-    cached[dev] = static_cast<long long>(per_cu) * cus;
+    cached[dev].store(static_cast<long long>(per_cu) * cus, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return cached[dev].load(std::memory_order_relaxed);
 }
 
 // The hinted layout's grid (0: the call runs unplanned).  With every request

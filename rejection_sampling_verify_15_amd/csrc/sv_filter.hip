@@ -38,6 +38,8 @@
 // top-k ones, each a pass of the last workgroup.  These masses have fp32
 // precision per element, so an fp32 cut can differ from an fp64 reference
 // only where p lies within about 1e-7 of the mass at the cut.
+#include <atomic>
+
 #include "sv_device.hpp"
 #include "sv_host.hpp"
 
@@ -1051,15 +1053,15 @@ long long filter_group_rows(int V, int dtype) {
 
 // Compute units of the current device (cached per device).
 long long device_cus() {
-  static long long cached[64] = {0};
+  static std::atomic<long long> cached[64];  // per device, filled on first use (any thread)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
+  if (cached[dev].load(std::memory_order_relaxed) == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 256;
-    cached[dev] = cus;
+    cached[dev].store(cus, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return cached[dev].load(std::memory_order_relaxed);
 }
 
 size_t filter_workspace_bytes(int B, int gamma, int V, int dtype) {
