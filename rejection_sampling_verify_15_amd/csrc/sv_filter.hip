@@ -503,65 +503,78 @@ __global__ __launch_bounds__(kFilterThreads) void filter_rows(FilterArgs a) {
 // A bf16 logit has one of 65536 values, so a row is fully described by how
 // many times each value occurs.  A row is cut into S slices of kB16Slice
 // logits; one persistent workgroup per CU takes the (row, slice) items in
-// turn, counts the slice's values in LDS (16-bit counters, two to a word: a
-// slice has fewer than 65536 logits) and writes the slice's part of the row:
-// for every non-empty 12-bit key prefix its count, its mass relative to the
-// prefix's top value and its eight counter words.
-// The row's last item to arrive (nothing waits: the others go on to their
-// next item) sums the S parts and finds both cuts.  The maximum M is the
-// largest value present (in the highest non-empty prefix); a value v weighs count(v) * 2^((v - M) * log2(e) /
-// T) in fp64, and a prefix's mass on that scale is its relative mass times
-// its top value's weight.  Top-k and top-p are scans from the top over the
-// 4096 prefixes, then over the 16 values of the chosen prefix (the only
-// counter words read back).  The last item also clears what the items wrote.
-// No row is read twice.
-constexpr int kB16Threads = 1024;
+// turn and counts the slice's values in LDS (16-bit counters, two to a word:
+// a slice has fewer than 65536 logits).  It then writes the slice's part of
+// the row, by binade (sign and exponent, the top 9 bits of a key: 128
+// evenly spaced values each): for every non-empty binade a record (count,
+// largest key present, fp64 mass relative to that key's value) and its 128
+// counters.  The row's last item to arrive (nothing waits: the others go on
+// to their next item) merges the S records of each binade, one binade per
+// thread: the maximum M is the largest key of the row (each item adds its
+// own with an atomic maximum), a value v weighs count(v) * 2^((v - M) *
+// log2(e) / T) in fp64, and a binade's mass is the sum over the parts of
+// the relative mass times the weight of the part's largest key.  Top-k and
+// top-p are block scans from the top over the 512 binades, then one wave
+// over the 128 values of the chosen binade (the only counters read back).
+// The last item also clears what the items wrote.  No row is read twice.
+constexpr int kB16Threads = 512;                 // two waves per SIMD: 256 VGPRs each, so a slice's loads
+                                                 // stay in registers
 constexpr int kB16Waves = kB16Threads / kWave;
 constexpr int kB16Slice = 65528;                 // a multiple of 8 below 65536: one value's count fits 16 bits
-constexpr int kB16Per = kMaxBins / kB16Threads;  // prefixes per thread (4 consecutive ones)
-constexpr size_t kB16PartBytes = kMaxBins * (4 + 8 + 32);  // counts, masses, counter words
-constexpr size_t kB16Head = 256;                                 // arrival counter
-// Largest log2 weight of the top prefix's top value on the scale of M for
-// which its relative mass is rescaled (beyond it the prefix is weighed value
-// by value: a tiny temperature).
-constexpr double kB16MaxTopLog2 = 900.0;
+constexpr int kB16Batch = (kB16Slice + 8 * kB16Threads - 1) / (8 * kB16Threads);  // 16-byte loads per thread
+constexpr int kB16Binades = 512;                 // top 9 bits of a 16-bit key
+constexpr int kB16PerBinade = 128;               // keys per binade
+static_assert(kB16Binades == kB16Threads, "the finisher holds one binade per thread");
+constexpr size_t kB16RecBytes = kB16Binades * 16;                 // records
+constexpr size_t kB16CountBytes = size_t(1 << 16) * 2;            // 16-bit counters of every key
+constexpr size_t kB16PartBytes = kB16RecBytes + kB16CountBytes;
+constexpr size_t kB16Head = 256;  // arrival counter, then 1 + the row's largest key (atomic maximum)
 
 __host__ __device__ inline size_t b16_slot_bytes(int S) { return kB16Head + static_cast<size_t>(S) * kB16PartBytes; }
 
-// One slice's part, structure of arrays so that consecutive prefixes are
-// consecutive words of every array.
-struct B16Part {
-  uint32_t* cnt12;  // [4096] logits per prefix
-  double* mass;     // [4096] mass relative to the prefix's top value
-  uint64_t* words;  // [4][4096]: counters 4q .. 4q + 3 of prefix b in words[q][b], 16 bits each, lowest first
+// A binade of one part: ck = count | (largest key << 32), m = fp64 mass
+// relative to the largest key's value.  All zero for an empty binade.
+struct B16Rec {
+  uint64_t ck;
+  uint64_t m;
 };
-__device__ inline B16Part b16_part(char* slot, int s) {
-  char* p = slot + kB16Head + static_cast<size_t>(s) * kB16PartBytes;
-  return B16Part{reinterpret_cast<uint32_t*>(p), reinterpret_cast<double*>(p + kMaxBins * 4),
-                 reinterpret_cast<uint64_t*>(p + kMaxBins * 12)};
+__device__ inline B16Rec* b16_recs(char* slot, int s) {
+  return reinterpret_cast<B16Rec*>(slot + kB16Head + static_cast<size_t>(s) * kB16PartBytes);
+}
+// The counters of part s as 64-bit words (four 16-bit counters, lowest key
+// first; binade b is words 32 b .. 32 b + 31).
+__device__ inline uint64_t* b16_words(char* slot, int s) {
+  return reinterpret_cast<uint64_t*>(slot + kB16Head + static_cast<size_t>(s) * kB16PartBytes + kB16RecBytes);
+}
+__device__ inline uint32_t* b16_row_max(char* slot) { return reinterpret_cast<uint32_t*>(slot) + 1; }
+
+__device__ inline double b16_value(uint32_t k16) { return static_cast<double>(key_value(full_key<0>(k16))); }
+// Weight of value v on the scale of M (v <= M); 0 for -inf and the inf / NaN
+// patterns.
+__device__ inline double b16_weight(double v, double M, double l2t) {
+  return (__builtin_isfinite(v) && __builtin_isfinite(M)) ? exp2_neg(__builtin_fmin((v - M) * l2t, 0.0)) : 0.0;
 }
 
-// Weights of the 16 values of prefix `bin` relative to value `ref`: the
-// values of one prefix share sign and exponent, so they are evenly spaced
-// and their weights form a geometric sequence, w(s - 1) = w(s) * q, taken
-// from the prefix's highest value present (s_hi) down, so every weight is at
-// most 1 when ref is at least that value (ref = M, or the prefix's top).  Two
-// fp64 exponentials per prefix; the rest are products.  The prefixes of inf
-// and NaN values weigh 0 (only -inf is a valid logit there).
+// Weights of the 16 values of prefix `pre` (keys 16 pre .. 16 pre + 15)
+// relative to value `ref`: the values of one binade are evenly spaced, so
+// their weights form a geometric sequence, w(s - 1) = w(s) * q, taken from
+// the prefix's highest value present (s_hi) down, every weight at most 1
+// when ref is at least that value.  Two fp64 exponentials per prefix; the
+// rest are products.  The prefixes of inf and NaN values weigh 0 (only -inf
+// is a valid logit there).
 struct B16Weights {
   double top, q;  // weight of value s_hi, ratio between neighbours
   int s_hi;       // highest sub-index with a count (-1: none)
 };
-__device__ inline double b16_value(uint32_t k16) { return static_cast<double>(key_value(full_key<0>(k16))); }
-__device__ inline B16Weights b16_weights(const uint32_t (&c)[16], int bin, double ref, double l2t) {
+__device__ inline B16Weights b16_weights(const uint32_t (&c)[16], int pre, double ref, double l2t) {
   int s_hi = -1;
 #pragma unroll
   for (int sb = 0; sb < 16; ++sb)
     if (c[sb]) s_hi = sb;
-  const double v15 = b16_value(static_cast<uint32_t>(16 * bin + 15));
-  const double v14 = b16_value(static_cast<uint32_t>(16 * bin + 14));
+  const double v15 = b16_value(static_cast<uint32_t>(16 * pre + 15));
+  const double v14 = b16_value(static_cast<uint32_t>(16 * pre + 14));
   if (s_hi < 0 || !__builtin_isfinite(v15) || !__builtin_isfinite(v14)) return B16Weights{0.0, 0.0, s_hi};
-  const double vh = b16_value(static_cast<uint32_t>(16 * bin + s_hi));
+  const double vh = b16_value(static_cast<uint32_t>(16 * pre + s_hi));
   return B16Weights{exp2_neg(__builtin_fmin((vh - ref) * l2t, 0.0)), exp2_neg((v14 - v15) * l2t), s_hi};
 }
 __device__ inline void b16_unpack(const uint32_t (&w)[8], uint32_t (&c)[16]) {
@@ -571,292 +584,234 @@ __device__ inline void b16_unpack(const uint32_t (&w)[8], uint32_t (&c)[16]) {
     c[2 * q + 1] = w[q] >> 16;
   }
 }
-__device__ inline void b16_add_quad(uint64_t two, uint32_t* c) {
-  c[0] += static_cast<uint32_t>(two) & 0xffffu;
-  c[1] += static_cast<uint32_t>(two) >> 16;
-  c[2] += static_cast<uint32_t>(two >> 32) & 0xffffu;
-  c[3] += static_cast<uint32_t>(two >> 48);
-}
-// Mass of the prefix's values with key >= floor16 (counts c) relative to ref.
-__device__ inline double b16_mass(const uint32_t (&c)[16], int bin, uint32_t floor16, double ref, double l2t) {
-  const B16Weights w = b16_weights(c, bin, ref, l2t);
+// Mass of a prefix's values relative to ref.
+__device__ inline double b16_mass(const uint32_t (&c)[16], int pre, double ref, double l2t) {
+  const B16Weights w = b16_weights(c, pre, ref, l2t);
   double m = 0.0, x = w.top;
 #pragma unroll
   for (int sb = 15; sb >= 0; --sb) {
     if (sb > w.s_hi) continue;
-    if (c[sb] && static_cast<uint32_t>(16 * bin + sb) >= floor16) m += static_cast<double>(c[sb]) * x;
+    if (c[sb]) m += static_cast<double>(c[sb]) * x;
     x *= w.q;
   }
   return m;
 }
-// Walks the 16 values of prefix `bin` from the top, in the order and
-// arithmetic of b16_mass: the first key >= floor16 where acc plus its count
-// (or its mass on the scale of Mv) reaches `want`; the lowest such key when
-// rounding leaves `want` above them all.
-__device__ inline uint32_t b16_walk(const uint32_t (&c)[16], int bin, uint32_t floor16, double acc, double want,
-                                    bool mass, double Mv, double l2t) {
-  const B16Weights w = b16_weights(c, bin, Mv, l2t);
-  uint32_t key = 0xffffffffu, low = static_cast<uint32_t>(16 * bin);
-  double x = w.top;
-#pragma unroll
-  for (int sb = 15; sb >= 0; --sb) {
-    if (sb > w.s_hi) continue;
-    const uint32_t k = static_cast<uint32_t>(16 * bin + sb);
-    const double ws = x;
-    x *= w.q;
-    if (!c[sb] || k < floor16) continue;
-    const double add = mass ? static_cast<double>(c[sb]) * ws : static_cast<double>(c[sb]);
-    if (key == 0xffffffffu && acc + add >= want) key = k;
-    acc += add;
-    low = k;
-  }
-  return key != 0xffffffffu ? key : low;
-}
-// The 16 counts of prefix `bin` summed over the S parts of a row.
-__device__ inline void b16_bin_counts(char* slot, int S, int bin, uint32_t (&c)[16]) {
-#pragma unroll
-  for (int sb = 0; sb < 16; ++sb) c[sb] = 0u;
-  for (int s = 0; s < S; ++s) {
-    const B16Part pt = b16_part(slot, s);
-    if (!load_coherent(&pt.cnt12[bin])) continue;
-    uint64_t two[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) two[q] = load_coherent(pt.words + q * kMaxBins + bin);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) b16_add_quad(two[q], c + 4 * q);
-  }
+
+// Reduction over each group of eight lanes (8 g .. 8 g + 7), all of them
+// active; every lane of the group receives the result.
+template <typename T, typename Op>
+__device__ inline T group8_reduce(T v, Op op) {
+  v = op(v, lane_move<kDppQuadSwap1>(v));
+  v = op(v, lane_move<kDppQuadSwap2>(v));
+  return op(v, lane_move<kDppRowHalfMirror>(v));
 }
 
-// Block scan from the top over the kB16Per values each thread holds, thread
-// t holding prefixes 4095 - (kB16Per t + i): the first prefix (from the top)
-// where the running sum reaches `want`, and the sum above it; -1 when none
-// does.
-__device__ inline int b16_find(const double (&v)[kB16Per], double want, double* s_wd, int* s_pos, double* s_above,
-                               double* above_out) {
-  double own = 0.0;
+// Binade b's 128 counters summed over the S parts into s_cnt (threads 0-31,
+// one word of four counters each, eight parts' loads at a time); the
+// caller synchronises.
+__device__ inline void b16_load_binade(char* slot, int S, int b, uint32_t* s_cnt) {
+  if (threadIdx.x >= kB16PerBinade / 4) return;
+  uint32_t c[4] = {0u, 0u, 0u, 0u};
+  constexpr int kPB = 8;
+  for (int s0 = 0; s0 < S; s0 += kPB) {
+    uint64_t w[kPB];
 #pragma unroll
-  for (int i = 0; i < kB16Per; ++i) own += v[i];
-  double inc = own;
-  for (int d = 1; d < kWave; d <<= 1) {
-    const double o = __shfl_up(inc, d, kWave);
-    if (static_cast<int>(threadIdx.x % kWave) >= d) inc += o;
+    for (int u = 0; u < kPB; ++u)
+      w[u] = s0 + u < S ? load_coherent(b16_words(slot, s0 + u) + 32 * b + threadIdx.x) : 0ull;
+#pragma unroll
+    for (int u = 0; u < kPB; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] += static_cast<uint32_t>(w[u] >> (16 * i)) & 0xffffu;
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s_cnt[4 * threadIdx.x + i] = c[i];
+}
+
+// One wave over binade b's values from the top (lane l holds keys
+// 128 b + 127 - 2 l and the one below): the first key >= floor16 where acc
+// plus the counts (or masses on the scale of M) of the keys from the top
+// through it reaches `want`; when rounding leaves `want` above them all, the
+// lowest such key present.  With want <= 0 (mass mode) it is the total of
+// those keys' masses that is asked for: returned through *total.
+__device__ inline uint32_t b16_walk(const uint32_t* s_cnt, int b, uint32_t floor16, double acc, double want,
+                                    bool mass, double M, double l2t, double* total) {
+  const int lane = threadIdx.x % kWave;
+  const int ia = kB16PerBinade - 1 - 2 * lane, ib = ia - 1;
+  const uint32_t ka = static_cast<uint32_t>(kB16PerBinade * b + ia), kb = ka - 1u;
+  const uint32_t ca = s_cnt[ia], cb = s_cnt[ib];
+  const bool ina = ca && ka >= floor16, inb = cb && kb >= floor16;
+  double xa = 0.0, xb = 0.0;
+  if (ina) xa = mass ? static_cast<double>(ca) * b16_weight(b16_value(ka), M, l2t) : static_cast<double>(ca);
+  if (inb) xb = mass ? static_cast<double>(cb) * b16_weight(b16_value(kb), M, l2t) : static_cast<double>(cb);
+  const double own = xa + xb;
+  const double incl = wave_inclusive_sum(own);
+  if (total) *total = read_lane(incl, kWave - 1);
+  const double before = acc + lane_move<kDppWaveShr1>(incl);  // lane 0 receives 0
+  const double after_a = before + xa;
+  const bool ha = ina && after_a >= want, hb = inb && after_a + xb >= want;
+  const uint64_t hit = __ballot(ha || hb);
+  if (hit) {
+    const int l = __builtin_ctzll(hit);
+    return static_cast<uint32_t>(read_lane(static_cast<int>(ha ? ka : kb), l));
+  }
+  const uint64_t any = __ballot(ina || inb);
+  if (!any) return floor16;
+  const int l = 63 - __builtin_clzll(any);
+  return static_cast<uint32_t>(read_lane(static_cast<int>(inb ? kb : ka), l));
+}
+
+// Block scan from the top over one value per thread, thread t holding
+// binade 511 - t: the first binade (from the top) where the running sum
+// reaches want = x (or x times the total of all values, with of_total),
+// and the sum above it; -1 when none does.
+__device__ inline int b16_find(double v, double x, bool of_total, double* s_wd, int* s_pos, double* s_above,
+                               double* above_out, double* want_out) {
+  const double inc = wave_inclusive_sum(v);
   const int w = threadIdx.x / kWave;
   __syncthreads();  // earlier readers of s_wd and s_pos are done
   if (threadIdx.x % kWave == kWave - 1) s_wd[w] = inc;
   if (threadIdx.x == 0) *s_pos = 0x7fffffff;
   __syncthreads();
-  double base = 0.0;
-  for (int i = 0; i < w; ++i) base += s_wd[i];
-  double acc = base + inc - own;
-  int pos = -1;
-  double above = 0.0;
-  if (acc < want) {
-#pragma unroll
-    for (int i = 0; i < kB16Per; ++i) {
-      if (pos < 0 && acc + v[i] >= want) {
-        pos = kB16Per * static_cast<int>(threadIdx.x) + i;
-        above = acc;
-      }
-      acc += v[i];
-    }
+  double base = 0.0, total = 0.0;
+  for (int i = 0; i < kB16Waves; ++i) {
+    if (i < w) base += s_wd[i];
+    total += s_wd[i];
   }
-  if (pos >= 0) atomicMin(s_pos, pos);
+  const double want = of_total ? x * total : x;
+  *want_out = want;
+  const double acc = base + inc - v;
+  const bool hit = acc < want && acc + v >= want;
+  if (hit) atomicMin(s_pos, static_cast<int>(threadIdx.x));
   __syncthreads();
   const int best = *s_pos;
-  if (pos >= 0 && pos == best) *s_above = above;
+  if (hit && static_cast<int>(threadIdx.x) == best) *s_above = acc;
   __syncthreads();
   *above_out = *s_above;
-  return best == 0x7fffffff ? -1 : kMaxBins - 1 - best;
+  return best == 0x7fffffff ? -1 : kB16Binades - 1 - best;
 }
+
+// LDS of the finisher.
+struct B16Shared {
+  double wd[kB16Waves];
+  double above, fm;
+  int pos, lowbin;
+  uint32_t key;
+  uint32_t cnt[kB16PerBinade];  // counters of one binade, summed over the parts
+};
 
 // The last item of a row: both cuts from the S parts, stored in thr, and
 // the parts cleared.
-__device__ __attribute__((noinline)) void b16_finish(const RowJob& j, char* slot, int S, uint32_t* thr, double* s_wd,
-                                                     int* s_wi, int* s_pos, double* s_above, uint32_t* s_key) {
+__device__ __attribute__((always_inline)) inline void b16_finish(const RowJob j, char* slot, int S, uint32_t* thr, B16Shared* sh) {
   const double l2t = kLog2e / static_cast<double>(j.T);
-  // this thread's four prefixes (index i: prefix bin0 + 3 - i, top first),
-  // counts and relative masses summed over the parts, in one round of loads
-  // per four parts; `seen` marks the non-empty (part, prefix) pairs of the
-  // first 8 parts, to clear them
-  const int bin0 = kMaxBins - kB16Per * (static_cast<int>(threadIdx.x) + 1);
-  uint32_t c12[kB16Per] = {0u, 0u, 0u, 0u};
-  double mrel[kB16Per] = {0.0, 0.0, 0.0, 0.0};
-  uint32_t seen = 0u;
+  const int bn = kB16Binades - 1 - static_cast<int>(threadIdx.x);  // this thread's binade, top first
+  uint32_t* row_max = b16_row_max(slot);
+  const uint32_t top1 = load_coherent(row_max);
+  const double M = b16_value(top1 ? top1 - 1u : 0u);
+  // the binade's count and mass over the parts, four parts' records per
+  // round of loads; `seen` marks the parts where it is not empty (the first
+  // 64), to clear them
+  uint32_t cnt = 0u;
+  double mass = 0.0;
+  uint64_t seen = 0u;
   constexpr int kPC = 4;
   for (int s0 = 0; s0 < S; s0 += kPC) {
-    uint64_t cw[kPC][2], mw[kPC][4];
+    uint64_t ck[kPC], mw[kPC];
 #pragma unroll
     for (int u = 0; u < kPC; ++u) {
       const bool in = s0 + u < S;
-      const B16Part pt = b16_part(slot, in ? s0 + u : 0);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) cw[u][h] = in ? load_coherent(reinterpret_cast<const uint64_t*>(pt.cnt12 + bin0) + h) : 0ull;
-#pragma unroll
-      for (int jj = 0; jj < kB16Per; ++jj) mw[u][jj] = in ? load_coherent(reinterpret_cast<const uint64_t*>(pt.mass + bin0 + jj)) : 0ull;
+      B16Rec* r = b16_recs(slot, in ? s0 + u : 0) + bn;
+      ck[u] = in ? load_coherent(&r->ck) : 0ull;
+      mw[u] = in ? load_coherent(&r->m) : 0ull;
     }
 #pragma unroll
     for (int u = 0; u < kPC; ++u) {
-#pragma unroll
-      for (int jj = 0; jj < kB16Per; ++jj) {
-        const uint32_t cj = static_cast<uint32_t>(cw[u][jj / 2] >> (32 * (jj % 2)));
-        c12[kB16Per - 1 - jj] += cj;
-        mrel[kB16Per - 1 - jj] += __longlong_as_double(static_cast<long long>(mw[u][jj]));
-        if (cj && s0 + u < 8) seen |= 1u << (4 * (s0 + u) + jj);
-      }
-    }
-  }
-  // M: the highest non-empty prefix, block-wide, then its highest value
-  int top_bin = -1;
-#pragma unroll
-  for (int i = kB16Per - 1; i >= 0; --i)
-    if (c12[i]) top_bin = bin0 + kB16Per - 1 - i;
-  top_bin = wave_max_int(top_bin);
-  __syncthreads();
-  if (threadIdx.x % kWave == 0) s_wi[threadIdx.x / kWave] = top_bin;
-  __syncthreads();
-  for (int i = 0; i < kB16Waves; ++i) top_bin = max(top_bin, s_wi[i]);
-  top_bin = max(top_bin, 0);
-  if (top_bin >= bin0 && top_bin < bin0 + kB16Per) {
-    uint32_t c[16];
-    b16_bin_counts(slot, S, top_bin, c);
-    uint32_t top = static_cast<uint32_t>(16 * top_bin);
-#pragma unroll
-    for (int sb = 0; sb < 16; ++sb)
-      if (c[sb]) top = static_cast<uint32_t>(16 * top_bin + sb);
-    *s_key = top;
-  }
-  __syncthreads();
-  const double Mv = b16_value(*s_key);
-  __syncthreads();
-
-  // masses on the scale of M: the relative mass times the weight of the
-  // prefix's top value; the top prefix, when that weight passes 2^900, value
-  // by value
-  double m[kB16Per];
-#pragma unroll
-  for (int i = 0; i < kB16Per; ++i) {
-    const int bin = bin0 + kB16Per - 1 - i;
-    m[i] = 0.0;
-    if (!c12[i]) continue;
-    const double v15 = b16_value(static_cast<uint32_t>(16 * bin + 15));
-    const double d = (v15 - Mv) * l2t;
-    if (bin != top_bin) {
-      m[i] = mrel[i] * exp2_neg(__builtin_fmin(d, 0.0));  // below M's prefix: v15 < M
-    } else if (d <= kB16MaxTopLog2) {
-      const double n = __builtin_ceil(__builtin_fmax(d, 0.0));
-      m[i] = mrel[i] * __builtin_ldexp(exp2_neg(__builtin_fmax(d, 0.0) - n), static_cast<int>(n));
-    } else {
-      uint32_t c[16];
-      b16_bin_counts(slot, S, bin, c);
-      m[i] = b16_mass(c, bin, 0u, Mv, l2t);
+      const uint32_t c = static_cast<uint32_t>(ck[u]);
+      if (!c) continue;
+      cnt += c;
+      if (s0 + u < 64) seen |= 1ull << (s0 + u);
+      const double mr = __longlong_as_double(static_cast<long long>(mw[u]));
+      if (mr > 0.0) mass += mr * b16_weight(b16_value(static_cast<uint32_t>(ck[u] >> 32)), M, l2t);
     }
   }
 
   uint32_t floor16 = 0u;
+  int held = -1;  // the binade whose counters sh->cnt holds
   double above = 0.0;
   if (j.cut_k) {
-    double v[kB16Per];
-#pragma unroll
-    for (int i = 0; i < kB16Per; ++i) v[i] = static_cast<double>(c12[i]);  // counts are exact in fp64
-    const int bin = b16_find(v, j.k, s_wd, s_pos, s_above, &above);
-    if (bin < 0 && threadIdx.x == 0) *s_key = 0u;  // cannot happen: k < V
-    if (bin >= bin0 && bin < bin0 + kB16Per) {
-      uint32_t c[16];
-      b16_bin_counts(slot, S, bin, c);
-      *s_key = b16_walk(c, bin, 0u, above, j.k, false, Mv, l2t);
+    double want = 0.0;
+    const int b = b16_find(static_cast<double>(cnt), j.k, false, sh->wd, &sh->pos, &sh->above, &above, &want);  // k < V
+    b16_load_binade(slot, S, b < 0 ? 0 : b, sh->cnt);
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      const uint32_t key = b16_walk(sh->cnt, b < 0 ? 0 : b, 0u, above, j.k, false, M, l2t, nullptr);
+      if (threadIdx.x == 0) sh->key = key;
     }
     __syncthreads();
-    floor16 = *s_key;
-    __syncthreads();
+    floor16 = sh->key;
+    held = b < 0 ? 0 : b;
   }
   uint32_t cut16 = floor16;
   if (j.cut_p) {
-    // masses over the keys >= floor16: the top-k cut's own prefix value by
-    // value, the prefixes below it none
-    const int fbin = static_cast<int>(floor16 >> 4);
-#pragma unroll
-    for (int i = 0; i < kB16Per; ++i) {
-      const int bin = bin0 + kB16Per - 1 - i;
-      if (bin < fbin) {
-        m[i] = 0.0;
-      } else if (bin == fbin && j.cut_k && c12[i]) {
-        uint32_t c[16];
-        b16_bin_counts(slot, S, bin, c);
-        m[i] = b16_mass(c, bin, floor16, Mv, l2t);
+    // masses over the keys >= floor16: the floor's own binade value by value
+    // (its counters are held), the binades below it none
+    const int fb = static_cast<int>(floor16 >> 7);
+    double m = bn < fb ? 0.0 : mass;
+    if (j.cut_k) {
+      if (threadIdx.x < kWave) {
+        double fm = 0.0;
+        b16_walk(sh->cnt, fb, floor16, 0.0, 0.0, true, M, l2t, &fm);
+        if (threadIdx.x == 0) sh->fm = fm;
       }
+      __syncthreads();
+      if (bn == fb) m = sh->fm;
     }
-    double part = 0.0;
-#pragma unroll
-    for (int i = 0; i < kB16Per; ++i) part += m[i];
-    part = wave_sum(part);
-    __syncthreads();
-    if (threadIdx.x % kWave == 0) s_wd[threadIdx.x / kWave] = part;
-    __syncthreads();
-    double Z = 0.0;
-    for (int i = 0; i < kB16Waves; ++i) Z += s_wd[i];
-    const double want = j.p * Z;
-    const int bin = b16_find(m, want, s_wd, s_pos, s_above, &above);
-    if (bin >= 0) {
-      if (bin >= bin0 && bin < bin0 + kB16Per) {
-        uint32_t c[16];
-        b16_bin_counts(slot, S, bin, c);
-        *s_key = b16_walk(c, bin, floor16, above, want, true, Mv, l2t);
-      }
-    } else {
+    double want = 0.0;
+    int b = b16_find(m, j.p, true, sh->wd, &sh->pos, &sh->above, &above, &want);
+    double want_w = want;
+    if (b < 0) {
       // rounding left `want` above the total: the lowest key >= floor16
-      // present (in the lowest non-empty prefix at or above the cut's)
-      int lowbin = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < kB16Per; ++i) {
-        const int b2 = bin0 + kB16Per - 1 - i;
-        if (c12[i] && b2 >= fbin) lowbin = min(lowbin, b2);
-      }
-      lowbin = wave_min(lowbin);
+      // present, in the lowest non-empty binade at or above the floor's
+      if (threadIdx.x == 0) sh->lowbin = 0x7fffffff;
       __syncthreads();
-      if (threadIdx.x % kWave == 0) s_wi[threadIdx.x / kWave] = lowbin;
+      if (cnt && bn >= fb) atomicMin(&sh->lowbin, bn);
       __syncthreads();
-      for (int i = 0; i < kB16Waves; ++i) lowbin = min(lowbin, s_wi[i]);
-      if (lowbin != 0x7fffffff && lowbin >= bin0 && lowbin < bin0 + kB16Per) {
-        uint32_t c[16];
-        b16_bin_counts(slot, S, lowbin, c);
-        uint32_t low = static_cast<uint32_t>(16 * lowbin + 15);
-#pragma unroll
-        for (int sb = 15; sb >= 0; --sb)
-          if (c[sb] && static_cast<uint32_t>(16 * lowbin + sb) >= floor16) low = static_cast<uint32_t>(16 * lowbin + sb);
-        *s_key = low;
-      }
-      if (lowbin == 0x7fffffff && threadIdx.x == 0) *s_key = floor16;
+      b = sh->lowbin == 0x7fffffff ? fb : sh->lowbin;
+      above = 0.0;
+      want_w = __builtin_inf();  // no key reaches it: the walk takes the lowest one
+    }
+    if (b != held) {
+      __syncthreads();  // readers of sh->cnt are done
+      b16_load_binade(slot, S, b, sh->cnt);
+      __syncthreads();
+    }
+    if (threadIdx.x < kWave) {
+      const uint32_t key = b16_walk(sh->cnt, b, floor16, above, want_w, true, M, l2t, nullptr);
+      if (threadIdx.x == 0) sh->key = key;
     }
     __syncthreads();
-    cut16 = *s_key;
+    cut16 = sh->key;
   }
-  if (threadIdx.x == 0) *thr = full_key<0>(cut16) + 1u;
+  if (threadIdx.x == 0) {
+    *thr = full_key<0>(cut16) + 1u;
+    store_coherent(row_max, 0u);
+  }
 
   // clear every word the row's items wrote: the workspace is zero between
   // calls
-  __syncthreads();  // all reads of the parts are done
   for (int s = 0; s < S; ++s) {
-    const B16Part pt = b16_part(slot, s);
-    uint32_t nz = 0u;
-    if (s < 8) {
-      nz = (seen >> (4 * s)) & 0xfu;
-    } else {
-#pragma unroll
-      for (int jj = 0; jj < kB16Per; ++jj)
-        if (load_coherent(&pt.cnt12[bin0 + jj])) nz |= 1u << jj;
-    }
+    B16Rec* r = b16_recs(slot, s) + bn;
+    const bool nz = s < 64 ? ((seen >> s) & 1u) != 0 : static_cast<uint32_t>(load_coherent(&r->ck)) != 0u;
     if (!nz) continue;
-#pragma unroll
-    for (int jj = 0; jj < kB16Per; ++jj) {
-      if (!((nz >> jj) & 1u)) continue;
-      store_coherent(reinterpret_cast<uint64_t*>(pt.mass + bin0 + jj), 0ull);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) store_coherent(pt.words + q * kMaxBins + bin0 + jj, 0ull);
-    }
-    if (nz & 3u) store_coherent(reinterpret_cast<uint64_t*>(pt.cnt12 + bin0), 0ull);
-    if (nz & 12u) store_coherent(reinterpret_cast<uint64_t*>(pt.cnt12 + bin0 + 2), 0ull);
+    store_coherent(&r->ck, 0ull);
+    store_coherent(&r->m, 0ull);
+    uint64_t* wd = b16_words(slot, s) + 32 * bn;
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) store_coherent(wd + q, 0ull);
   }
+}
+
+__device__ inline char* slot_of(const FilterArgs& a, int local) {
+  return static_cast<char*>(a.slots) + static_cast<size_t>(local) * b16_slot_bytes(a.S);
 }
 
 // A row's job as kept in LDS.
@@ -887,25 +842,23 @@ __device__ inline bool b16_item(const FilterArgs& a, const uint16_t* rows, const
 }
 
 // Every workgroup first lists the group's rows that need a cut (one row per
-// thread); the items of those rows are then handed out in order by a counter
-// in the workspace, so no workgroup gets more than its share.  Each
-// workgroup takes its next item while it counts the current one, and on the
-// vector path issues the next slice's loads before it writes the current
-// part.  The last workgroup to leave resets the counter.
+// thread, in passes); the items of those rows are then handed out in order
+// by a counter in the workspace.  A workgroup takes its next item only once
+// it has written its part (and finished the row, when it arrived last), so
+// the rows' finishes do not pile up on the workgroups that took items
+// early; on the vector path it then issues that item's loads at once.  The
+// last workgroup to leave resets the counter.
 template <bool VEC>
 __global__ __launch_bounds__(kB16Threads) void filter_rows_bf16(FilterArgs a) {
   __shared__ uint4 s_pairs[(1 << 16) / 8];  // 65536 16-bit counters
-  __shared__ double s_wd[kB16Waves];
+  __shared__ B16Shared sh;
   __shared__ int s_wi[kB16Waves];
-  __shared__ int s_pos;
-  __shared__ double s_above;
-  __shared__ uint32_t s_key;
   __shared__ int s_last;
   __shared__ uint32_t s_next;
   __shared__ uint16_t s_rows[kFilterSlots];
   __shared__ B16Job s_jobs[kFilterSlots];
   __shared__ int s_nrows;
-  static_assert(kFilterSlots <= kB16Threads, "one row per thread");
+  static_assert(kFilterSlots % kB16Threads == 0, "whole passes over the rows");
   constexpr int kv = Elem<0>::kVec;
   uint32_t* pairs = reinterpret_cast<uint32_t*>(s_pairs);
   uint32_t* head = a.queue;
@@ -913,24 +866,30 @@ __global__ __launch_bounds__(kB16Threads) void filter_rows_bf16(FilterArgs a) {
   for (int i = threadIdx.x; i < (1 << 16) / 8; i += kB16Threads) s_pairs[i] = make_uint4(0u, 0u, 0u, 0u);
   if (threadIdx.x == 0) s_next = __hip_atomic_fetch_add(head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   {
-    // the rows that need a cut, in order
-    RowJob rj;
-    const bool need = static_cast<int>(threadIdx.x) < a.group && row_job(a, a.row0 + threadIdx.x, rj);
-    const uint64_t bal = __ballot(need);
-    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    if (lane == 0) s_wi[w] = __popcll(bal);
-    __syncthreads();
-    int before = 0, all = 0;
-    for (int i = 0; i < kB16Waves; ++i) {
-      if (i < w) before += s_wi[i];
-      all += s_wi[i];
+    // the rows that need a cut, in order: one row per thread in each pass
+    int listed = 0;
+    for (int r0 = 0; r0 < a.group; r0 += kB16Threads) {
+      const int r = r0 + static_cast<int>(threadIdx.x);
+      RowJob rj;
+      const bool need = r < a.group && row_job(a, a.row0 + r, rj);
+      const uint64_t bal = __ballot(need);
+      const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+      if (lane == 0) s_wi[w] = __popcll(bal);
+      __syncthreads();
+      int before = listed, all = listed;
+      for (int i = 0; i < kB16Waves; ++i) {
+        if (i < w) before += s_wi[i];
+        all += s_wi[i];
+      }
+      if (need) {
+        const int q = before + __popcll(bal & ((1ull << lane) - 1ull));
+        s_rows[q] = static_cast<uint16_t>(r);
+        s_jobs[q] = b16_pack(rj);
+      }
+      listed = all;
+      __syncthreads();  // s_wi is read before the next pass writes it
     }
-    if (need) {
-      const int q = before + __popcll(bal & ((1ull << lane) - 1ull));
-      s_rows[q] = static_cast<uint16_t>(threadIdx.x);
-      s_jobs[q] = b16_pack(rj);
-    }
-    if (threadIdx.x == 0) s_nrows = all;
+    if (threadIdx.x == 0) s_nrows = listed;
     __syncthreads();
   }
   const long long items = static_cast<long long>(s_nrows) * a.S;
@@ -939,24 +898,23 @@ __global__ __launch_bounds__(kB16Threads) void filter_rows_bf16(FilterArgs a) {
   const void* base = nullptr;
   int n = 0, row_id = 0, slice = 0, local = 0;
   bool act = item < items && b16_item(a, s_rows, s_jobs, item, j, base, n, row_id, slice, local);
-  uint4 w[kBatch];
+  uint4 w[kB16Batch];
   auto issue = [&](const void* bp, int nn) {
     const int nv = nn / kv;
 #pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
+    for (int q = 0; q < kB16Batch; ++q) {
       const int i = q * kB16Threads + static_cast<int>(threadIdx.x);
       w[q] = Elem<0>::raw(bp, (i < nv ? i : 0) * kv);
     }
   };
   if (VEC && act) issue(base, n);
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave, sp = lane & 7;
   while (item < items) {
-    uint32_t nxt = 0u;
-    if (threadIdx.x == 0) nxt = __hip_atomic_fetch_add(head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (act) {
       if constexpr (VEC) {
-        const int nv = n / kv;  // kBatch * kB16Threads vectors cover a slice
+        const int nv = n / kv;  // kB16Batch * kB16Threads vectors cover a slice
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
+        for (int q = 0; q < kB16Batch; ++q) {
           if (q * kB16Threads + static_cast<int>(threadIdx.x) >= nv) continue;
           float x[kv];
           Elem<0>::unpack(w[q], x);
@@ -973,43 +931,55 @@ __global__ __launch_bounds__(kB16Threads) void filter_rows_bf16(FilterArgs a) {
         });
       }
     }
-    if (threadIdx.x == 0) s_next = nxt;
     __syncthreads();
-    const long long nitem = s_next;
-    RowJob nj{};
-    const void* nbase = nullptr;
-    int nn = 0, nrow = 0, nslice = 0, nlocal = 0;
-    const bool nact = nitem < items && b16_item(a, s_rows, s_jobs, nitem, nj, nbase, nn, nrow, nslice, nlocal);
-    // the next slice's loads go out before this part's stores
-    if (VEC && nact) issue(nbase, nn);
     if (act) {
-      // the slice's part: thread t writes prefixes t + 1024 i (the count,
-      // relative mass and counter words of the non-empty ones), and clears
-      // the LDS counters it read
-      char* slot = static_cast<char*>(a.slots) + static_cast<size_t>(local) * b16_slot_bytes(a.S);
+      // the slice's part, by binade: eight lanes to a binade (sixteen keys
+      // each, consecutive lanes on consecutive LDS words), eight binades to a
+      // wave per step; the LDS counters read are cleared
+      char* slot = slot_of(a, local);
       const double l2t = kLog2e / static_cast<double>(j.T);
-      const B16Part pt = b16_part(slot, slice);
-#pragma unroll 1
-      for (int i = 0; i < kB16Per; ++i) {
-        const int bin = i * kB16Threads + static_cast<int>(threadIdx.x);
-        const uint4 lo = s_pairs[2 * bin], hi = s_pairs[2 * bin + 1];
+      B16Rec* recs = b16_recs(slot, slice);
+      uint64_t* words = b16_words(slot, slice);
+      int kmax = -1;  // the largest key this thread saw
+#pragma unroll 2
+      for (int it = 0; it < kB16Binades / (8 * kB16Waves); ++it) {
+        const int bn = it * (8 * kB16Waves) + wave * 8 + (lane >> 3);
+        const int pre = 8 * bn + sp;  // keys 16 pre .. 16 pre + 15
+        const uint4 lo = s_pairs[2 * pre], hi = s_pairs[2 * pre + 1];
         const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         uint32_t c[16];
         b16_unpack(wd, c);
         uint32_t tot = 0u;
+        int top = -1;
 #pragma unroll
-        for (int sb = 0; sb < 16; ++sb) tot += c[sb];
-        if (!tot) continue;
-        s_pairs[2 * bin] = make_uint4(0u, 0u, 0u, 0u);
-        s_pairs[2 * bin + 1] = make_uint4(0u, 0u, 0u, 0u);
-        store_coherent(pt.cnt12 + bin, tot);
-        store_coherent(reinterpret_cast<uint64_t*>(pt.mass + bin),
-                       static_cast<uint64_t>(__double_as_longlong(b16_mass(c, bin, 0u, b16_value(16 * bin + 15), l2t))));
+        for (int sb = 0; sb < 16; ++sb) {
+          tot += c[sb];
+          if (c[sb]) top = 16 * pre + sb;
+        }
+        if (!__ballot(tot != 0u)) continue;  // eight empty binades
+        const uint32_t bc = static_cast<uint32_t>(group8_reduce(static_cast<int>(tot), [](int x, int y) { return x + y; }));
+        const int bt = group8_reduce(top, [](int x, int y) { return max(x, y); });
+        if (!bc) continue;  // the binade's eight lanes alike
+        if (tot) {
+          s_pairs[2 * pre] = make_uint4(0u, 0u, 0u, 0u);
+          s_pairs[2 * pre + 1] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          store_coherent(pt.words + q * kMaxBins + bin,
-                         static_cast<uint64_t>(wd[2 * q]) | (static_cast<uint64_t>(wd[2 * q + 1]) << 32));
+          for (int q = 0; q < 4; ++q)
+            store_coherent(words + 4 * pre + q,
+                           static_cast<uint64_t>(wd[2 * q]) | (static_cast<uint64_t>(wd[2 * q + 1]) << 32));
+        }
+        const double m = group8_reduce(tot ? b16_mass(c, pre, b16_value(static_cast<uint32_t>(bt)), l2t) : 0.0,
+                                       [](double x, double y) { return x + y; });
+        if (sp == 0) {
+          store_coherent(&recs[bn].ck, static_cast<uint64_t>(bc) | (static_cast<uint64_t>(bt) << 32));
+          store_coherent(&recs[bn].m, static_cast<uint64_t>(__double_as_longlong(m)));
+        }
+        kmax = max(kmax, bt);
       }
+      kmax = wave_max_int(kmax);
+      if (lane == 0 && kmax >= 0)
+        __hip_atomic_fetch_max(b16_row_max(slot), static_cast<uint32_t>(kmax) + 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
       wait_memory();
       __syncthreads();
       uint32_t* arrivals = reinterpret_cast<uint32_t*>(slot);
@@ -1017,10 +987,20 @@ __global__ __launch_bounds__(kB16Threads) void filter_rows_bf16(FilterArgs a) {
       __syncthreads();
       if (s_last) {
         if (threadIdx.x == 0) store_coherent(arrivals, 0u);
-        b16_finish(j, slot, a.S, a.thr + row_id, s_wd, s_wi, &s_pos, &s_above, &s_key);
+        b16_finish(j, slot, a.S, a.thr + row_id, &sh);
       }
     }
+    // the next item is taken only now (a workgroup that finished a row takes
+    // it later than one that did not), and its loads go out
     __syncthreads();
+    if (threadIdx.x == 0) s_next = __hip_atomic_fetch_add(head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const long long nitem = s_next;
+    RowJob nj{};
+    const void* nbase = nullptr;
+    int nn = 0, nrow = 0, nslice = 0, nlocal = 0;
+    const bool nact = nitem < items && b16_item(a, s_rows, s_jobs, nitem, nj, nbase, nn, nrow, nslice, nlocal);
+    if (VEC && nact) issue(nbase, nn);
     item = nitem;
     j = nj;
     base = nbase;
@@ -1037,7 +1017,6 @@ __global__ __launch_bounds__(kB16Threads) void filter_rows_bf16(FilterArgs a) {
     store_coherent(exits, 0u);
   }
 }
-
 }  // namespace
 
 int b16_slices(int V) { return (V + kB16Slice - 1) / kB16Slice; }
