@@ -916,12 +916,15 @@ __global__ __launch_bounds__(kB16Threads) void filter_rows_bf16(FilterArgs a) {
 #pragma unroll
         for (int q = 0; q < kB16Batch; ++q) {
           if (q * kB16Threads + static_cast<int>(threadIdx.x) >= nv) continue;
-          float x[kv];
-          Elem<0>::unpack(w[q], x);
+          const uint32_t wd[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
 #pragma unroll
-          for (int e = 0; e < kv; ++e) {
-            const uint32_t k = order_key(x[e]) >> 16;
-            atomicAdd(&pairs[k >> 1], 1u << ((k & 1u) << 4));
+          for (int e = 0; e < 4; ++e) {
+            // two bf16 patterns to their 16-bit order keys at once (a
+            // negative one inverted, a positive one with its top bit set;
+            // -0 lands on the key below +0, merged after the count)
+            const uint32_t kp = wd[e] ^ (((wd[e] >> 15) & 0x00010001u) * 0x7fffu + 0x80008000u);
+            atomicAdd(&pairs[(kp & 0xffffu) >> 1], (kp & 1u) * 0xffffu + 1u);
+            atomicAdd(&pairs[kp >> 17], ((kp >> 16) & 1u) * 0xffffu + 1u);
           }
         }
       } else {
@@ -933,6 +936,15 @@ __global__ __launch_bounds__(kB16Threads) void filter_rows_bf16(FilterArgs a) {
     }
     __syncthreads();
     if (act) {
+      // -0 counts as +0 (their values are equal): key 0x7fff joins key 0x8000
+      if (threadIdx.x == 0) {
+        const uint32_t neg0 = pairs[0x7fff >> 1] >> 16;
+        if (neg0) {
+          pairs[0x7fff >> 1] &= 0xffffu;
+          pairs[0x8000 >> 1] += neg0;
+        }
+      }
+      __syncthreads();
       // the slice's part, by binade: eight lanes to a binade (sixteen keys
       // each, consecutive lanes on consecutive LDS words), eight binades to a
       // wave per step; the LDS counters read are cleared
@@ -947,16 +959,17 @@ __global__ __launch_bounds__(kB16Threads) void filter_rows_bf16(FilterArgs a) {
         const int pre = 8 * bn + sp;  // keys 16 pre .. 16 pre + 15
         const uint4 lo = s_pairs[2 * pre], hi = s_pairs[2 * pre + 1];
         const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        uint32_t c[16];
-        b16_unpack(wd, c);
-        uint32_t tot = 0u;
-        int top = -1;
+        if (!__ballot((lo.x | lo.y | lo.z | lo.w | hi.x | hi.y | hi.z | hi.w) != 0u)) continue;  // eight empty binades
+        // the 16 counters' total from the words' sum: both halves' sums stay
+        // below 65536 (a slice's counts do), so neither carries
+        uint32_t sum = 0u;
 #pragma unroll
-        for (int sb = 0; sb < 16; ++sb) {
-          tot += c[sb];
-          if (c[sb]) top = 16 * pre + sb;
-        }
-        if (!__ballot(tot != 0u)) continue;  // eight empty binades
+        for (int q = 0; q < 8; ++q) sum += wd[q];
+        const uint32_t tot = (sum & 0xffffu) + (sum >> 16);
+        int top = -1;  // the highest key with a count
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (wd[q]) top = 16 * pre + 2 * q + ((wd[q] >> 16) ? 1 : 0);
         const uint32_t bc = static_cast<uint32_t>(group8_reduce(static_cast<int>(tot), [](int x, int y) { return x + y; }));
         const int bt = group8_reduce(top, [](int x, int y) { return max(x, y); });
         if (!bc) continue;  // the binade's eight lanes alike
@@ -968,8 +981,13 @@ __global__ __launch_bounds__(kB16Threads) void filter_rows_bf16(FilterArgs a) {
             store_coherent(words + 4 * pre + q,
                            static_cast<uint64_t>(wd[2 * q]) | (static_cast<uint64_t>(wd[2 * q + 1]) << 32));
         }
-        const double m = group8_reduce(tot ? b16_mass(c, pre, b16_value(static_cast<uint32_t>(bt)), l2t) : 0.0,
-                                       [](double x, double y) { return x + y; });
+        double mp = 0.0;
+        if (tot) {
+          uint32_t c[16];
+          b16_unpack(wd, c);
+          mp = b16_mass(c, pre, b16_value(static_cast<uint32_t>(bt)), l2t);
+        }
+        const double m = group8_reduce(mp, [](double x, double y) { return x + y; });
         if (sp == 0) {
           store_coherent(&recs[bn].ck, static_cast<uint64_t>(bc) | (static_cast<uint64_t>(bt) << 32));
           store_coherent(&recs[bn].m, static_cast<uint64_t>(__double_as_longlong(m)));

@@ -126,6 +126,28 @@ def test_ties_and_masked_logits():
     filtered_parity(ci, k, p, 10, "filtered ties")
 
 
+@pytest.mark.parametrize("V", [4096, 4093])
+def test_ties_and_signed_zeros_bf16(V):
+    """bf16 rows (the exact-count search, vector and scalar paths) with many
+    equal logits, a fifth of them +0 or -0 (equal values, two bit patterns),
+    and -inf entries; the cuts at and around zero keep both signs."""
+    ci = synth.chain_inputs(16560 + V % 7, B=12, gamma=3, V=V, dtype="bf16", family="gauss",
+                            draft_sigma=0.5, temperature=0.9)
+    rng = np.random.default_rng(16561)
+    for arr in (ci.target, ci.draft):
+        f = (arr.astype(np.uint32) << 16).view(np.float32)
+        f = np.round(f * 2.0) / 2.0                              # few distinct values: ties everywhere
+        bits = (f.view(np.uint32) >> 16).astype(np.uint16)
+        zero = rng.random(bits.shape) < 0.2
+        bits[zero] = np.where(rng.random(int(zero.sum())) < 0.5, 0x0000, 0x8000).astype(np.uint16)
+        bits[:, :, rng.integers(0, V, size=200)] = 0xFF80        # -inf
+        arr[...] = bits
+    k = np.array([1, 5, 50, 500, 1000, 1500, 2000, 2500, 3000, 3500, 100, 10], np.int32)
+    p = np.array([1.0, 0.9, 1.0, 0.95, 1.0, 0.99, 1.0, 0.999, 1.0, 0.5, 0.8, 1.0], np.float32)
+    ci.draft_tokens = filtered_draft_tokens(ci, k, p, 16562)
+    filtered_parity(ci, k, p, 10, f"filtered signed zeros V={V}")
+
+
 def test_invalid_filters_and_greedy():
     ci = synth.chain_inputs(16530, B=10, gamma=2, V=3000, dtype="bf16", family="peaked",
                             draft_sigma=0.5, temperature=1.0)
