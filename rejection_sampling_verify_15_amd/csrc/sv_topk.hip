@@ -11,16 +11,17 @@
 //
 //  1. topk_rows    one 512-thread workgroup per (request, row read), each
 //                  wave owning a contiguous tile of the row.  The row's max
-//                  and lowest-index argmax come first.  For a sampling row the
-//                  k-th largest thread maximum bounds the k-th largest logit
-//                  from below (k threads hold a logit at least that large),
-//                  so only the logits at or above it -- about k of them --
-//                  are collected in LDS with their indices, and the exact
-//                  k-th largest value is found among them by a bit-by-bit
-//                  search over order-preserving keys; each kept logit's rank
-//                  by index places it in the row's kept list.  A
-//                  sampling row is so visited twice, the second time through
-//                  the caches.  Should more than 512 logits pass the bound,
+//                  and lowest-index argmax come first, with each thread's
+//                  maximum per 16-byte step (bf16) or per batch of loads.
+//                  For a sampling row the k-th largest thread maximum bounds
+//                  the k-th largest logit from below (k threads hold a logit
+//                  at least that large), so only the logits at or above it
+//                  -- about k of them -- are collected in LDS with their
+//                  indices, each lane reloading (through the caches) only
+//                  the steps or batches whose maximum reaches the bound; the
+//                  exact k-th largest value is found among them by a
+//                  bit-by-bit search over order-preserving keys; each kept
+//                  logit's rank by index places it in the row's kept list.  Should more than 512 logits pass the bound,
 //                  a bisection over the whole row finds the value and one
 //                  more visit compacts the kept logits in vocabulary order.
 //                  With top-p, the threshold then rises to the largest kept
@@ -108,13 +109,30 @@ struct RowTile {
   const void* row;
   int t0, t1;
 
+  static constexpr int kU = DT == 0 ? kInFlightBf16 : kInFlight;
+  static constexpr int kBatch = kU * kStep;  // logits of a wave's batch of loads in flight
+  __device__ inline int batches() const { return (t1 - t0 + kBatch - 1) / kBatch; }
+
   // f(i0, x, valid) for every step, every lane taking part (valid is false
-  // past the tile), so f may use wave-wide operations.
+  // past the tile), so f may use wave-wide operations; done(batch) after
+  // each batch of kU steps.
   template <typename F>
   __device__ inline void each(F&& f) const {
+    each(f, [](int) {});
+  }
+  template <typename F, typename D>
+  __device__ inline void each(F&& f, D&& done) const {
+    for (int bt = 0; bt < batches(); ++bt) {
+      visit_batch(bt, f);
+      done(bt);
+    }
+  }
+  // The steps of batch bt only.
+  template <typename F>
+  __device__ inline void visit_batch(int bt, F&& f) const {
     const int lane = threadIdx.x % kWave;
-    constexpr int kU = DT == 0 ? kInFlightBf16 : kInFlight;
-    for (int base = t0; base < t1; base += kU * kStep) {
+    {
+      const int base = t0 + bt * kBatch;
       if constexpr (VEC) {
         // the raw groups stay packed until their step is visited
         uint4 w[kU];
@@ -147,25 +165,55 @@ struct RowTile {
   }
 };
 
-// The kk-th largest of one key per thread (0 stands for none): the largest
-// t with at least kk keys >= t, built from the top bit down with one ballot
-// count per bit.  s_buf holds 2 * kRowWaves ints (alternate rounds use
-// alternate halves, so one barrier per bit suffices).
-__device__ inline uint32_t block_kth_key(uint32_t key, int kk, int* s_buf) {
-  const int w = threadIdx.x / kWave;
-  uint32_t ans = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t c = ans | (1u << bit);
-    const int n = __popcll(__ballot(key >= c));
-    int* buf = s_buf + (bit & 1) * kRowWaves;
-    if (threadIdx.x % kWave == 0) buf[w] = n;
-    __syncthreads();
-    int t = 0;
+// bf16 rows on the vector path also keep each step's maximum per thread in
+// LDS (tiles of at most kMaxSteps steps), so the candidate visit reloads
+// only the 16-byte groups that can hold a candidate, all at once.
+constexpr int kMaxSteps = 32;
+static_assert(kMaxSteps % kInFlightBf16 == 0, "a tile of kMaxSteps steps is whole batches");
+
+// Per-thread maxima of the first visit's batches, kMaxSlots of them held
+// in registers: with more batches, consecutive ones share a slot.
+constexpr int kMaxSlots = 8;
+struct BatchMax {
+  float m[kMaxSlots];
+  int per;  // batches per slot
+  __device__ inline int slot(int bt) const { return bt / per; }
+  __device__ inline void add(int bt, float v) {
+    const int s = slot(bt);
 #pragma unroll
-    for (int i = 0; i < kRowWaves; ++i) t += buf[i];
-    if (t >= kk) ans = c;
+    for (int i = 0; i < kMaxSlots; ++i)
+      if (i == s) m[i] = fmaxf(m[i], v);
   }
-  return ans;
+};
+
+// The kk-th largest of one key per thread (0 stands for none): the largest
+// t with at least kk keys >= t.  The keys go through LDS to the first wave,
+// which builds t from the top bit down, eight ballot counts per bit (no
+// barrier per bit), and hands it back.  With low_bit = 16 every key is a
+// bf16 value's: its low 16 bits are 0 for a positive value and all ones for
+// a negative one, so only the top 16 bits are searched and the low ones
+// follow from the sign.
+__device__ inline uint32_t block_kth_key(uint32_t key, int kk, uint32_t* s_keys, uint32_t* s_ans, int low_bit) {
+  s_keys[threadIdx.x] = key;
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    constexpr int kPerLane = kRowThreads / kWave;
+    uint32_t k8[kPerLane];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) k8[i] = s_keys[i * kWave + threadIdx.x];
+    uint32_t ans = 0u;
+    for (int bit = 31; bit >= low_bit; --bit) {
+      const uint32_t c = ans | (1u << bit);
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < kPerLane; ++i) n += __popcll(__ballot(k8[i] >= c));
+      if (n >= kk) ans = c;
+    }
+    if (low_bit > 0 && ans != 0u && !(ans & 0x80000000u)) ans |= (1u << low_bit) - 1u;
+    if (threadIdx.x == 0) *s_ans = ans;
+  }
+  __syncthreads();
+  return *s_ans;
 }
 
 __device__ inline double block_sum_f64(double v, double* s_red) {
@@ -209,7 +257,10 @@ __device__ inline int block_count(int v, int* s_red) {
 // carry none of its work).
 template <int DT, bool VEC, bool TOPP>
 __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
-  __shared__ int s_bits[2 * kRowWaves];
+  __shared__ uint32_t s_keys[kRowThreads];
+  __shared__ uint32_t s_kth;
+  constexpr bool kStepMax = DT == 0 && VEC;
+  __shared__ uint16_t s_smax[kStepMax ? kMaxSteps * kRowThreads : 1];  // bf16: each step's maximum, per thread
   __shared__ float s_kv[kTopkKept];
   __shared__ int s_ki[kTopkKept];
   __shared__ double s_e[kTopkKept];
@@ -255,14 +306,36 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
                           (static_cast<size_t>(b) * G + (k - G - 1)) * static_cast<size_t>(a.V) * Elem<DT>::kBytes;
   tile.t0 = min(a.V, w * a.tile);
   tile.t1 = min(a.V, tile.t0 + a.tile);
-  // 1) max, lowest-index argmax, and this thread's own max
+  // 1) max, lowest-index argmax, this thread's own max, and its maximum per
+  //    batch of loads (so the candidate visit re-reads only the batches
+  //    that can hold a candidate)
   ArgMax best{-INFINITY, kNoIndex};
-  tile.each([&](int i0, const float (&x)[kPer], bool valid) {
-    if (valid)
+  BatchMax bm;
 #pragma unroll
-      for (int e = 0; e < kPer; ++e)
-        if (x[e] > best.v || best.i == kNoIndex) best = ArgMax{x[e], i0 + e};
-  });
+  for (int i = 0; i < kMaxSlots; ++i) bm.m[i] = -INFINITY;
+  bm.per = (tile.batches() + kMaxSlots - 1) / kMaxSlots;
+  if (bm.per < 1) bm.per = 1;
+  float cur = -INFINITY;
+  const bool by_step = kStepMax && tile.t1 - tile.t0 <= kMaxSteps * Tile::kStep;
+  tile.each(
+      [&](int i0, const float (&x)[kPer], bool valid) {
+        float sm = -INFINITY;
+        if (valid)
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) {
+            sm = fmaxf(sm, x[e]);
+            if (x[e] > best.v || best.i == kNoIndex) best = ArgMax{x[e], i0 + e};
+          }
+        cur = fmaxf(cur, sm);
+        if constexpr (kStepMax) {
+          if (by_step) s_smax[((i0 - tile.t0) / Tile::kStep) * kRowThreads + tid] =
+              static_cast<uint16_t>(__float_as_uint(sm) >> 16);
+        }
+      },
+      [&](int bt) {
+        bm.add(bt, cur);
+        cur = -INFINITY;
+      });
   const float own_max = best.v;
   ArgMax wb = wave_argmax(best);
   if (lane == 0) {
@@ -283,7 +356,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
     s_ncand = 0;
     s_nkept = 0;
   }
-  const float lowb = key_float(block_kth_key(order_key(own_max), kk, s_bits));
+  constexpr int kLowBit = DT == 0 ? 16 : 0;  // bf16 keys vary in their top 16 bits only
+  const float lowb = key_float(block_kth_key(order_key(own_max), kk, s_keys, &s_kth, kLowBit));
   // The end of every sampling row: the kept logits sit in s_kv / s_ki (in
   // any order) when there are at most kTopkKept of them.  With top-p the
   // threshold rises to the largest kept value whose mass (the kept logits at
@@ -323,8 +397,10 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
     }
     if (tid == 0) *head = TopkHead{kept, thr, rb.v, rb.i};
   };
-  // 3) the logits at or above it, with their indices
-  tile.each([&](int i0, const float (&x)[kPer], bool valid) {
+  // 3) the logits at or above it, with their indices: only the batches
+  //    whose maximum reaches the bound are read again, each lane its own,
+  //    the lanes' first such batches together, then their second ones
+  auto collect = [&](int i0, const float (&x)[kPer], bool valid) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e)
       if (valid && x[e] >= lowb) {
@@ -334,7 +410,48 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
           s_cidx[slot] = i0 + e;
         }
       }
-  });
+  };
+  uint32_t need = 0u;
+  if constexpr (kStepMax) {
+    // the steps whose maximum reaches the bound, up to four reloaded at once
+    if (by_step)
+      for (int st = 0; st < kMaxSteps; ++st)
+        if (__uint_as_float(static_cast<uint32_t>(s_smax[st * kRowThreads + tid]) << 16) >= lowb) need |= 1u << st;
+    while (__ballot(need != 0u)) {  // empty unless by_step
+      constexpr int kR = 4;
+      int i0s[kR];
+      uint4 wv[kR];
+#pragma unroll
+      for (int j = 0; j < kR; ++j) {
+        i0s[j] = -1;
+        if (need) {
+          i0s[j] = tile.t0 + __builtin_ctz(need) * Tile::kStep + lane * kPer;
+          need &= need - 1u;
+        }
+        wv[j] = (i0s[j] >= 0 && i0s[j] < tile.t1)
+                    ? load_row16_cached(static_cast<const char*>(tile.row) + static_cast<size_t>(i0s[j]) * Elem<DT>::kBytes)
+                    : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int j = 0; j < kR; ++j) {
+        float x[kPer];
+        Elem<DT>::unpack(wv[j], x);
+        collect(i0s[j], x, i0s[j] >= 0 && i0s[j] < tile.t1);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxSlots; ++i)
+    if (!(kStepMax && by_step) && bm.m[i] >= lowb) need |= 1u << i;
+  while (__ballot(need != 0u)) {
+    const int sl = need ? __builtin_ctz(need) : -1;
+    need &= need - 1u;
+    for (int q = 0; q < bm.per; ++q) {
+      const int bt = sl * bm.per + q;
+      if (sl < 0 || bt >= tile.batches()) continue;
+      tile.visit_batch(bt, collect);
+    }
+  }
   __syncthreads();
   const int ncand = s_ncand;
   if (ncand <= kCand) {
@@ -344,7 +461,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
     const bool mine = tid < ncand;
     const float cv = mine ? s_cand[tid] : -INFINITY;
     const int ci = mine ? s_cidx[tid] : kNoIndex;
-    const float thr = key_float(block_kth_key(mine ? order_key(cv) : 0u, kk, s_bits));
+    const float thr = key_float(block_kth_key(mine ? order_key(cv) : 0u, kk, s_keys, &s_kth, kLowBit));
     if (mine && cv >= thr) {
       const int slot = atomicAdd(&s_nkept, 1);
       if (slot < kTopkKept) {
