@@ -78,6 +78,18 @@ def test_topk_batched_shape():
     assert all((r.num_accepted >= 0).all() for r in refs)
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 151936), ("f32", 300000)])
+def test_topk_long_rows(dtype, V):
+    """Rows long enough that the candidate visit reloads by batch of loads:
+    bf16 tiles past 32 steps per thread, and fp32 tiles of more than eight
+    batches (several batches to a slot)."""
+    ci = synth.chain_inputs(15980 + V % 89, B=6, gamma=2, V=V, dtype=dtype, family="gauss",
+                            draft_sigma=(0.2, 1.2), temperature=0.8, greedy_odd=True)
+    k = np.array([1, 7, 50, 128, 3, 100], np.int32)
+    toks = filtered_draft_tokens(ci, k, 15981)
+    topk_parity(ci, k, 6, f"topk long rows {dtype} V={V}", tokens=toks)
+
+
 @pytest.mark.parametrize("dtype,V", [("bf16", 3000), ("f32", 999), ("bf16", 20001)])
 def test_topk_small_many_rounds(dtype, V):
     """k varying per request over [1, 128], close and far drafts, odd
