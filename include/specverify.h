@@ -209,7 +209,7 @@ SV_API int spec_verify_chain_noalloc(const void* target_logits, const void* draf
  * of each search), then the chain launch of spec_verify_chain with the cuts
  * applied wherever a row is read.  Rows are searched in groups of at most
  * 1024 (B times 2 gamma + 1 rows in all); a group of bf16 rows also holds
- * at most 256 MiB of counts (about 288 KiB per row at V = 128256).  The
+ * at most 256 MiB of counts (about 272 KiB per row at V = 128256).  The
  * workspace comes from sv_chain_filtered_workspace_bytes (spec_verify_chain's
  * plus that search area), zero-filled before the first call and left
  * zero-filled by every call.  Returns an sv_status.
