@@ -59,6 +59,10 @@ WORKLOADS = {
         "filtered", lambda s: mixed_filters(s, dtype="f32"), [21701, 21702, 21703, 21704], 200),
     "filtered_small_T_B64_g4_V128256": (
         "filtered", lambda s: mixed_filters(s, small_t=True), [21801, 21802, 21803, 21804], 200),
+    "ragged_B64_g1to4_V128256": (
+        "ragged", lambda s: ragged_batched(s), [synth.SEED_BASE + 3, 21901, 21902, 21903], 210),
+    "topk_mixed_B64_g4_V128256": (
+        "topk", lambda s: topk_mixed(s), [22001, 22002, 22003, 22004], 200),
 }
 
 
@@ -103,6 +107,36 @@ def mixed_filters(seed, dtype="bf16", small_t=False):
     return Filtered(ci, k, p)
 
 
+class Ragged:
+    """Chain inputs plus a draft length per request."""
+
+    def __init__(self, ci, gammas):
+        self.ci, self.gammas = ci, gammas
+
+    def __getattr__(self, name):
+        return getattr(self.ci, name)
+
+
+def ragged_batched(seed):
+    """The batched inputs with request b drafting 1 + b % 4 tokens (the
+    padded arrays of gamma 4)."""
+    ci = synth.batched_chain(seed=seed)
+    return Ragged(ci, (1 + np.arange(ci.B) % 4).astype(np.int32))
+
+
+def topk_mixed(seed):
+    """The batched inputs under the limited top-k entry point: k per request
+    from {1, 5, 50, 128}, then top-p 0.8, 0.9 or none; draft tokens drawn
+    from the draft rows cut alike."""
+    from test_gpu_chain_topk import filtered_draft_tokens
+    ci = synth.batched_chain(seed=seed)
+    rng = np.random.default_rng(seed + 17)
+    k = rng.choice(np.array([1, 5, 50, 128], np.int32), size=ci.B)
+    p = rng.choice(np.array([0.8, 0.9, 1.0], np.float32), size=ci.B)
+    ci.draft_tokens = filtered_draft_tokens(ci, k, seed + 19, top_p=p)
+    return Filtered(ci, k, p)
+
+
 def fingerprint(*arrays) -> str:
     h = hashlib.sha256()
     for a in arrays:
@@ -118,15 +152,17 @@ def fingerprint(*arrays) -> str:
 def inputs_fingerprint(kind, x) -> str:
     if kind == "chain":
         return fingerprint(x.target, x.draft, x.draft_tokens, x.temperature, x.uniforms)
-    if kind == "filtered":
+    if kind in ("filtered", "topk"):
         return fingerprint(x.target, x.draft, x.draft_tokens, x.temperature, x.uniforms, x.top_k, x.top_p)
+    if kind == "ragged":
+        return fingerprint(x.target, x.draft, x.draft_tokens, x.temperature, x.uniforms, x.gammas)
     return fingerprint(x.logits, x.draft_logits, x.node_tokens, x.parents, x.temperature,
                        x.uniforms, x.draw_uniforms)
 
 
 def uniform_sets(kind, x, seed, n_sets):
     """[(u,)] for chain and naive trees, [(u_accept, u_draw)] for MSS."""
-    shape = (x.B, x.gamma + 1) if kind in ("chain", "filtered") else (x.B, x.N)
+    shape = (x.B, x.gamma + 1) if kind in ("chain", "filtered", "ragged", "topk") else (x.B, x.N)
     first = (x.uniforms,) if kind != "mss" else (x.uniforms, x.draw_uniforms)
     out = [first]
     for s in range(1, n_sets):
@@ -158,17 +194,23 @@ def gpu_phase(out_dir, only, sets=None):
             print(f"[gpu] {name} seed={seed} built in {time.time() - t0:.1f}s", flush=True)
             us = uniform_sets(kind, x, seed, n_sets)
             toks, paths, ns = [], [], []
-            if kind in ("chain", "filtered"):
+            if kind in ("chain", "filtered", "ragged", "topk"):
                 tgt = to_device_logits(x.target, x.dtype)
                 drf = to_device_logits(x.draft, x.dtype)
                 dt = to_device(x.draft_tokens.astype(np.int32))
                 T = to_device(x.temperature.astype(np.float32))
-                if kind == "filtered":
+                if kind in ("filtered", "topk"):
                     kd = None if x.top_k is None else to_device(np.asarray(x.top_k, np.int32))
                     pd = None if x.top_p is None else to_device(np.asarray(x.top_p, np.float32))
+                if kind == "ragged":
+                    gd = to_device(np.asarray(x.gammas, np.int32))
                 for (u,) in us:
                     if kind == "filtered":
                         ot, on = sv.verify_chain_filtered(tgt, drf, dt, to_device(u), T, kd, pd)
+                    elif kind == "topk":
+                        ot, on = sv.verify_chain_topk(tgt, drf, dt, to_device(u), T, kd, top_p=pd)
+                    elif kind == "ragged":
+                        ot, on, _ = sv.verify_chain_ragged(tgt, drf, dt, to_device(u), T, gd)
                     else:
                         ot, on = sv.verify_chain(tgt, drf, dt, to_device(u), T)
                     toks.append(ot.cpu().numpy())
@@ -214,6 +256,18 @@ def _compare_part(requests):
 
     kind, x, us, gpu = _STATE["kind"], _STATE["x"], _STATE["us"], _STATE["gpu"]
     tally = Tally()
+    if kind == "ragged":
+        for s, u in enumerate(us):
+            r = oracle.verify_chain_ragged(x.target, x.draft, x.draft_tokens, u[0], x.temperature, x.gammas,
+                                           x.dtype, requests=requests)
+            tally.add(compare_chain(r, gpu["tokens"][s], gpu["n"][s], requests=requests))
+        return tally
+    if kind == "topk":
+        for s, u in enumerate(us):
+            r = oracle.verify_chain_topk(x.target, x.draft, x.draft_tokens, u[0], x.temperature, x.top_k,
+                                         x.dtype, requests=requests, top_p=x.top_p)
+            tally.add(compare_chain(r, gpu["tokens"][s], gpu["n"][s], requests=requests))
+        return tally
     if kind == "filtered":
         refs = oracle_filtered_many(x.ci, [u[0] for u in us], x.top_k, x.top_p, requests=requests)
         for s, r in enumerate(refs):
