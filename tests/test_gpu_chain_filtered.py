@@ -255,10 +255,12 @@ def test_small_temperatures_topp_bf16_ties():
     filtered_parity(ci, None, p, 6, "top-p small T bf16 ties")
 
 
-@pytest.mark.parametrize("V", [1 << 20, (1 << 20) + 13])
+@pytest.mark.parametrize("V", [1 << 20, (1 << 20) + 13, (1 << 22) + 8])
 def test_many_slices_per_row(V):
     """Rows of more than eight slices (the bf16 search's parts beyond its
-    first round of loads), vector and scalar paths, both filters."""
+    first round of loads), vector and scalar paths, both filters; and rows of
+    65 slices (the parts past the 64 whose non-empty binades the row's
+    finish remembers, so it reads their records again to clear them)."""
     ci = synth.chain_inputs(16590 + V % 7, B=2, gamma=1, V=V, dtype="bf16", family="gauss",
                             draft_sigma=0.4, temperature=0.8)
     k = np.array([5000, 300000], np.int32)
