@@ -982,12 +982,12 @@ __global__ __launch_bounds__(kB16Threads) void filter_rows_bf16(FilterArgs a) {
                            static_cast<uint64_t>(wd[2 * q]) | (static_cast<uint64_t>(wd[2 * q + 1]) << 32));
         }
         double mp = 0.0;
-        if (tot) {
+        if (j.cut_p && tot) {  // masses only where a top-p cut needs them
           uint32_t c[16];
           b16_unpack(wd, c);
           mp = b16_mass(c, pre, b16_value(static_cast<uint32_t>(bt)), l2t);
         }
-        const double m = group8_reduce(mp, [](double x, double y) { return x + y; });
+        const double m = j.cut_p ? group8_reduce(mp, [](double x, double y) { return x + y; }) : 0.0;
         if (sp == 0) {
           store_coherent(&recs[bn].ck, static_cast<uint64_t>(bc) | (static_cast<uint64_t>(bt) << 32));
           store_coherent(&recs[bn].m, static_cast<uint64_t>(__double_as_longlong(m)));
