@@ -72,10 +72,13 @@ KERNEL_SOURCES = {
                      "rejection_sampling_verify_15_amd/csrc/sv_device.hpp"),
     "filter_rows": ("rejection_sampling_verify_15_amd/csrc/sv_filter.hip",
                     "rejection_sampling_verify_15_amd/csrc/sv_device.hpp"),
+    "topk_rows": ("rejection_sampling_verify_15_amd/csrc/sv_topk.hip",
+                  "rejection_sampling_verify_15_amd/csrc/sv_device.hpp"),
 }
 # The stored counter summary of each workload.
 TRAFFIC_FILES = {"batched": "traffic_batched_chain.json", "deep": "traffic_deep_chain.json",
-                 "single": "traffic_single_chain.json", "topp": "traffic_topp_filter.json"}
+                 "single": "traffic_single_chain.json", "topp": "traffic_topp_filter.json",
+                 "topk": "traffic_topk_rows.json"}
 
 
 def source_digest(kernel: str = "chain_verify") -> str:
