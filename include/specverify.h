@@ -207,7 +207,9 @@ SV_API int spec_verify_chain_noalloc(const void* target_logits, const void* draf
  * cuts of all rows of the sampling requests (bf16: one read of each row;
  * fp32: one read from HBM, then one pass from the caches per further digit
  * of each search), then the chain launch of spec_verify_chain with the cuts
- * applied wherever a row is read.  Rows are searched in groups of at most
+ * applied wherever a row is read; a bf16 search also leaves each cut row's
+ * maximum and kept mass (fp64), so the chain launch does not read those rows
+ * again except where a draw needs them.  Rows are searched in groups of at most
  * 1024 (B times 2 gamma + 1 rows in all); a group of bf16 rows also holds
  * at most 256 MiB of counts (about 272 KiB per row at V = 128256).  The
  * workspace comes from sv_chain_filtered_workspace_bytes (spec_verify_chain's

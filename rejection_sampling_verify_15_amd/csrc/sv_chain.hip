@@ -137,6 +137,7 @@ struct ChainArgs {
   float* out_tau;        // [B][gamma] tau of each test taken, -1 elsewhere; or NULL
   uint32_t spin;         // poll bound of every wait (kSpinLimit unless a test lowers it)
   const uint32_t* thr;   // [B][2*gamma+1] filter thresholds of a filtered call (key + 1, 0: none), or NULL
+  const RowStat* stats;  // [B][2*gamma+1] maximum and kept mass of every row with a cut, or NULL
   const int32_t* top_k;  // [B] of a filtered call, or NULL
   const float* top_p;    // [B] of a filtered call, or NULL
   ChainPlan plan;        // block layout of a hinted call
@@ -401,6 +402,24 @@ template <int DT, bool VEC>
 __device__ inline void stream_once(const ChainArgs& a, const RowItem& r) {
   StreamItem<DT, VEC, kWave> x;
   if (a.gammas && !row_in_round(a, req_gamma(a, r.b), r.k)) return;  // past the request's length
+  if (a.stats) {
+    // A row the cut search has seen is not read again: its maximum and kept
+    // mass stand in for the chunk results (the first chunk carries them, the
+    // others are empty).  Its decide item clears the cut only once this
+    // item's word is in, so the cut read here is still the search's.
+    const size_t ri = static_cast<size_t>(r.b) * (2 * a.gamma + 1) + r.k;
+    if (a.thr[ri] != 0u) {
+      if (threadIdx.x == 0) {
+        uint64_t w = pack_partial(-INFINITY, 0);
+        if (r.c == 0) {
+          const RowStat st = a.stats[ri];
+          w = pack_partial(st.m, __float_as_int(static_cast<float>(st.z)));
+        }
+        store_coherent(&a.partials[ri * a.nchunk + r.c], w);
+      }
+      return;
+    }
+  }
   if (r.k <= a.gamma) {
     stream_issue<DT, VEC, kWave>(a, r, x);  // target rows: the loads do not wait for the temperature
     if (!temp_ok(x.t)) return;
@@ -654,6 +673,8 @@ __device__ void decide_request(const ChainArgs& a, int b) {
   }
   if (a.thr)
     for (int i = lane; i < R; i += kWave) const_cast<uint32_t*>(a.thr)[static_cast<size_t>(b) * R + i] = 0u;
+  if (a.stats)
+    for (int i = lane; i < R; i += kWave) const_cast<RowStat*>(a.stats)[static_cast<size_t>(b) * R + i] = RowStat{};
   if (kDraws && drawing) {
     // the draw runs beside other requests' units: let this wave issue first
     __builtin_amdgcn_s_setprio(3);
@@ -1268,7 +1289,7 @@ __global__ __launch_bounds__(kWave) void chain_units(ChainArgs a) {
 // host side
 // ---------------------------------------------------------------------------
 struct ChainLayout {
-  size_t partials, pending, units, counters, thr, filt, total;
+  size_t partials, pending, units, counters, thr, stats, filt, total;
 };
 
 static int units_for(int V, int span) { return (V + span - 1) / span; }
@@ -1286,6 +1307,7 @@ static ChainLayout chain_layout(int B, int gamma, int V, bool filtered = false, 
   L.units = off;    off = align_up(off + static_cast<size_t>(B) * nunit * sizeof(UnitRec));
   L.counters = off; off = align_up(off + static_cast<size_t>(B) * kCounterStride * sizeof(uint32_t));
   L.thr = off;      off = align_up(off + static_cast<size_t>(B) * R * sizeof(uint32_t));
+  L.stats = off;    off = align_up(off + (filtered ? static_cast<size_t>(B) * R * sizeof(RowStat) : 0));
   L.filt = off;     off += filtered ? filter_workspace_bytes(B, gamma, V, dtype) : 0;
   L.total = off;
   return L;
@@ -1456,6 +1478,9 @@ static int chain_entry(const void* target_logits, const void* draft_logits, cons
   a.spin = spin_limit(kSpinLimit);
   if (filtered) {
     a.thr = reinterpret_cast<uint32_t*>(ws + L.thr);
+    // bf16 cut searches also leave each cut row's maximum and kept mass, so
+    // the verification does not read those rows again
+    if (dtype == SV_BF16 && (top_k || top_p)) a.stats = reinterpret_cast<RowStat*>(ws + L.stats);
     a.top_k = top_k;
     a.top_p = top_p;
   }
@@ -1471,7 +1496,8 @@ static int chain_entry(const void* target_logits, const void* draft_logits, cons
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   if (filtered) {
     const int st = launch_filter_rows(target_logits, a.draft, temperature, top_k, top_p, B, gamma, V, dtype,
-                                      const_cast<uint32_t*>(a.thr), ws + L.filt, stream);
+                                      const_cast<uint32_t*>(a.thr), const_cast<RowStat*>(a.stats), ws + L.filt,
+                                      stream);
     if (st != SV_OK) return st;
   }
   const int kv = dtype == SV_BF16 ? Elem<0>::kVec : Elem<1>::kVec;

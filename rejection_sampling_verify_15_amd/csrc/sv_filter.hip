@@ -87,6 +87,7 @@ struct FilterArgs {
   void* slots;           // per-row search areas of the group (FilterSlot, or the bf16 parts)
   uint32_t* queue;       // bf16 item counter and exit counter
   uint32_t* thr;         // [B][2 * gamma + 1]: key + 1, 0 = no cut
+  RowStat* stats;        // [B][2 * gamma + 1]: maximum and kept mass of each cut row (bf16), or NULL
 };
 
 __device__ inline bool filter_temp_ok(float t) { return isfinite(t) && t >= 1.17549435e-38f; }
@@ -690,6 +691,17 @@ __device__ inline int b16_find(double v, double x, bool of_total, double* s_wd, 
   return best == 0x7fffffff ? -1 : kB16Binades - 1 - best;
 }
 
+// Sum over the workgroup of one value per thread; every thread receives it.
+__device__ inline double b16_block_sum(double v, double* s_wd) {
+  const double inc = wave_inclusive_sum(v);
+  __syncthreads();  // earlier readers of s_wd are done
+  if (threadIdx.x % kWave == kWave - 1) s_wd[threadIdx.x / kWave] = inc;
+  __syncthreads();
+  double t = 0.0;
+  for (int i = 0; i < kB16Waves; ++i) t += s_wd[i];
+  return t;
+}
+
 // LDS of the finisher.
 struct B16Shared {
   double wd[kB16Waves];
@@ -699,9 +711,11 @@ struct B16Shared {
   uint32_t cnt[kB16PerBinade];  // counters of one binade, summed over the parts
 };
 
-// The last item of a row: both cuts from the S parts, stored in thr, and
-// the parts cleared.
-__device__ __attribute__((always_inline)) inline void b16_finish(const RowJob j, char* slot, int S, uint32_t* thr, B16Shared* sh) {
+// The last item of a row: both cuts from the S parts, stored in thr (with
+// `stat`, also the row's maximum and the mass the cut keeps), and the parts
+// cleared.
+__device__ __attribute__((always_inline)) inline void b16_finish(const RowJob j, char* slot, int S, uint32_t* thr,
+                                                                 RowStat* stat, B16Shared* sh) {
   const double l2t = kLog2e / static_cast<double>(j.T);
   const int bn = kB16Binades - 1 - static_cast<int>(threadIdx.x);  // this thread's binade, top first
   uint32_t* row_max = b16_row_max(slot);
@@ -783,6 +797,7 @@ __device__ __attribute__((always_inline)) inline void b16_finish(const RowJob j,
       __syncthreads();  // readers of sh->cnt are done
       b16_load_binade(slot, S, b, sh->cnt);
       __syncthreads();
+      held = b;
     }
     if (threadIdx.x < kWave) {
       const uint32_t key = b16_walk(sh->cnt, b, floor16, above, want_w, true, M, l2t, nullptr);
@@ -790,6 +805,26 @@ __device__ __attribute__((always_inline)) inline void b16_finish(const RowJob j,
     }
     __syncthreads();
     cut16 = sh->key;
+  }
+  if (stat) {
+    // the kept mass: the binades above the cut's whole, the cut's own binade
+    // value by value from the cut up (its counters are held unless the walk
+    // fell back to a key outside it)
+    const int cb = static_cast<int>(cut16 >> 7);
+    const double up = b16_block_sum(bn > cb ? mass : 0.0, sh->wd);
+    if (cb != held) {
+      __syncthreads();  // readers of sh->cnt are done
+      b16_load_binade(slot, S, cb, sh->cnt);
+      __syncthreads();
+    }
+    if (threadIdx.x < kWave) {
+      double own = 0.0;
+      b16_walk(sh->cnt, cb, cut16, 0.0, 0.0, true, M, l2t, &own);
+      if (threadIdx.x == 0) {
+        stat->z = up + own;
+        stat->m = static_cast<float>(M);
+      }
+    }
   }
   if (threadIdx.x == 0) {
     *thr = full_key<0>(cut16) + 1u;
@@ -981,13 +1016,15 @@ __global__ __launch_bounds__(kB16Threads) void filter_rows_bf16(FilterArgs a) {
             store_coherent(words + 4 * pre + q,
                            static_cast<uint64_t>(wd[2 * q]) | (static_cast<uint64_t>(wd[2 * q + 1]) << 32));
         }
+        // masses only where a top-p cut or the kept mass needs them
+        const bool masses = j.cut_p || a.stats != nullptr;
         double mp = 0.0;
-        if (j.cut_p && tot) {  // masses only where a top-p cut needs them
+        if (masses && tot) {
           uint32_t c[16];
           b16_unpack(wd, c);
           mp = b16_mass(c, pre, b16_value(static_cast<uint32_t>(bt)), l2t);
         }
-        const double m = j.cut_p ? group8_reduce(mp, [](double x, double y) { return x + y; }) : 0.0;
+        const double m = masses ? group8_reduce(mp, [](double x, double y) { return x + y; }) : 0.0;
         if (sp == 0) {
           store_coherent(&recs[bn].ck, static_cast<uint64_t>(bc) | (static_cast<uint64_t>(bt) << 32));
           store_coherent(&recs[bn].m, static_cast<uint64_t>(__double_as_longlong(m)));
@@ -1005,7 +1042,7 @@ __global__ __launch_bounds__(kB16Threads) void filter_rows_bf16(FilterArgs a) {
       __syncthreads();
       if (s_last) {
         if (threadIdx.x == 0) store_coherent(arrivals, 0u);
-        b16_finish(j, slot, a.S, a.thr + row_id, &sh);
+        b16_finish(j, slot, a.S, a.thr + row_id, a.stats ? a.stats + row_id : nullptr, &sh);
       }
     }
     // the next item is taken only now (a workgroup that finished a row takes
@@ -1070,8 +1107,8 @@ size_t filter_workspace_bytes(int B, int gamma, int V, int dtype) {
 }
 
 int launch_filter_rows(const void* target, const void* draft, const float* temperature, const int32_t* top_k,
-                       const float* top_p, int B, int gamma, int V, int dtype, uint32_t* thr, void* slots,
-                       hipStream_t stream) {
+                       const float* top_p, int B, int gamma, int V, int dtype, uint32_t* thr, void* stats,
+                       void* slots, hipStream_t stream) {
   FilterArgs a{};
   a.target = target;
   a.draft = gamma > 0 ? draft : nullptr;
@@ -1085,6 +1122,7 @@ int launch_filter_rows(const void* target, const void* draft, const float* tempe
   a.queue = static_cast<uint32_t*>(slots);
   a.slots = static_cast<char*>(slots) + kQueueBytes;
   a.thr = thr;
+  a.stats = dtype == SV_BF16 ? static_cast<RowStat*>(stats) : nullptr;
   const long long rows = static_cast<long long>(B) * (2 * gamma + 1);
   if (rows == 0 || (!top_k && !top_p)) return SV_OK;
   const int kv = dtype == SV_BF16 ? Elem<0>::kVec : Elem<1>::kVec;

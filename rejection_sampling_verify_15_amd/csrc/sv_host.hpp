@@ -17,15 +17,26 @@ inline bool aligned(const void* p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }
 
+// What a cut search learnt of a row, for the verification after it: m is the
+// row's largest logit and z the sum, over the logits the cut keeps, of
+// exp((x - m) / T) in fp64.  All zero for a row not searched.
+struct RowStat {
+  double z;
+  float m;
+  uint32_t pad;
+};
+static_assert(sizeof(RowStat) == 16, "row stat size");
+
 // The thresholds of a filtered chain call (sv_filter.hip): launches over the
-// rows of the sampling requests, one per digit of each search, writing
-// thr[b][row] = key + 1 of each cut (0: none).  `slots` is the zero-filled
-// search area of filter_workspace_bytes(B, gamma, V, dtype) bytes, left
-// zero-filled.
+// rows of the sampling requests, writing thr[b][row] = key + 1 of each cut
+// (0: none).  `slots` is the zero-filled search area of
+// filter_workspace_bytes(B, gamma, V, dtype) bytes, left zero-filled.  With
+// `stats` (bf16 rows only; 16 bytes per row, zero-filled) every row that gets
+// a cut also gets its largest logit and kept mass there.
 // Returns an sv_status.
 int launch_filter_rows(const void* target, const void* draft, const float* temperature, const int32_t* top_k,
-                       const float* top_p, int B, int gamma, int V, int dtype, uint32_t* thr, void* slots,
-                       hipStream_t stream);
+                       const float* top_p, int B, int gamma, int V, int dtype, uint32_t* thr, void* stats,
+                       void* slots, hipStream_t stream);
 size_t filter_workspace_bytes(int B, int gamma, int V, int dtype);
 
 // Value of a test control (sv_set_test_hook); 0 when unset.
