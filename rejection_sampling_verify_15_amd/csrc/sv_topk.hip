@@ -82,6 +82,7 @@ struct TopkArgs {
   int32_t* out_n;
   TopkHead* heads;   // [B][2*gamma+1]
   TopkEntry* lists;  // [B][2*gamma+1][kTopkKept], vocabulary order
+  double* zs;        // [B][2*gamma+1] fp64 normaliser of each sampling row's kept logits
 };
 
 // T must be 0 (greedy) or a finite positive normal float.
@@ -364,13 +365,12 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
   // or above it, under the temperature softmax over the kept ones) reaches
   // p; then every kept logit is written at its rank by index.
   auto finish = [&](int kept, float thr) {
+    // each staged logit's weight on the scale of the row maximum
+    const double l2t = kLog2e / static_cast<double>(T);
+    double e = 0.0;
+    if (kept <= kTopkKept && tid < s_nkept) e = exp_scaled_t(s_kv[tid], rb.v, l2t);
     if (TOPP && kept <= kTopkKept && pp < 1.0f) {
-      const double l2t = kLog2e / static_cast<double>(T);
-      double e = 0.0;
-      if (tid < kept) {
-        e = exp_scaled_t(s_kv[tid], rb.v, l2t);
-        s_e[tid] = e;
-      }
+      if (tid < kept) s_e[tid] = e;
       const double z = block_sum_f64(e, s_dred);  // its barriers publish s_e
       float cand = -INFINITY;
       if (tid < kept) {
@@ -395,7 +395,12 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(TopkArgs a) {
       }
       a.lists[(static_cast<size_t>(b) * R + k) * kTopkKept + rank] = TopkEntry{my, s_kv[tid]};
     }
-    if (tid == 0) *head = TopkHead{kept, thr, rb.v, rb.i};
+    // the normaliser of the kept logits, for the decision and the draw
+    const double zk = block_sum_f64((kept <= kTopkKept && tid < s_nkept && s_kv[tid] >= thr) ? e : 0.0, s_dred);
+    if (tid == 0) {
+      *head = TopkHead{kept, thr, rb.v, rb.i};
+      a.zs[static_cast<size_t>(b) * R + k] = zk;
+    }
   };
   // 3) the logits at or above it, with their indices: only the batches
   //    whose maximum reaches the bound are read again, each lane its own,
@@ -583,36 +588,8 @@ __global__ __launch_bounds__(kWave) void topk_decide(TopkArgs a) {
   int32_t drawn = -1;
   if (!any_bad) {
     if (sampling) {
-      // fp64 normalisers over the kept lists, the loads of four rows in
-      // flight at once (lane l sums entries l, l + 64, ... of a row)
-      constexpr int kQ = kTopkKept / kWave;
-      constexpr int kRows = 4;
-      for (int r0 = 0; r0 < R; r0 += kRows) {
-        float v[kRows][kQ];
-#pragma unroll
-        for (int rr = 0; rr < kRows; ++rr) {
-          const int r = min(r0 + rr, R - 1);
-          const int c = r0 + rr < R ? s_h[r].count : 0;
-          const TopkEntry* e = lb + static_cast<size_t>(r) * kTopkKept;
-#pragma unroll
-          for (int q = 0; q < kQ; ++q) {
-            const int j = lane + q * kWave;
-            v[rr][q] = j < c ? e[j].val : -INFINITY;
-          }
-        }
-#pragma unroll
-        for (int rr = 0; rr < kRows; ++rr) {
-          const int r = r0 + rr;
-          if (r < R) {
-            double z = 0.0;
-#pragma unroll
-            for (int q = 0; q < kQ; ++q)
-              if (v[rr][q] != -INFINITY) z += exp_scaled_t(v[rr][q], s_h[r].max, l2t);
-            z = wave_sum(z);
-            if (lane == 0) s_z[r] = z;
-          }
-        }
-      }
+      // the fp64 normalisers the row workgroups left
+      for (int r = lane; r < R; r += kWave) s_z[r] = a.zs[static_cast<size_t>(b) * R + r];
       __syncthreads();
     }
     int ok = 1;
@@ -706,10 +683,11 @@ __global__ __launch_bounds__(kWave) void topk_decide(TopkArgs a) {
   }
   uint32_t* hz = reinterpret_cast<uint32_t*>(hb);
   for (int i = lane; i < R * 4; i += kWave) hz[i] = 0u;
+  for (int r = lane; r < R; r += kWave) a.zs[static_cast<size_t>(b) * R + r] = 0.0;
 }
 
 struct TopkLayout {
-  size_t heads, lists, total;
+  size_t heads, lists, zs, total;
 };
 
 TopkLayout topk_layout(int B, int gamma) {
@@ -720,6 +698,8 @@ TopkLayout topk_layout(int B, int gamma) {
   off = align_up(off + static_cast<size_t>(B) * R * sizeof(TopkHead));
   L.lists = off;
   off = align_up(off + static_cast<size_t>(B) * R * kTopkKept * sizeof(TopkEntry));
+  L.zs = off;
+  off = align_up(off + static_cast<size_t>(B) * R * sizeof(double));
   L.total = off;
   return L;
 }
@@ -778,6 +758,7 @@ extern "C" int spec_verify_chain_topk(const void* target_logits, const void* dra
   a.out_n = out_num_accepted;
   a.heads = reinterpret_cast<TopkHead*>(ws + L.heads);
   a.lists = reinterpret_cast<TopkEntry*>(ws + L.lists);
+  a.zs = reinterpret_cast<double*>(ws + L.zs);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const int kv = dtype == SV_BF16 ? Elem<0>::kVec : Elem<1>::kVec;
   const bool vec = (V % kv == 0) && aligned(target_logits, 16) && (!a.draft || aligned(a.draft, 16));
