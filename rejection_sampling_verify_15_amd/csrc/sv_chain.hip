@@ -164,6 +164,13 @@ __device__ inline double exp_row(float x, double ml2t, double l2t) {
   return exp2_neg(__builtin_fma(static_cast<double>(x), l2t, -ml2t));
 }
 
+// Whether any lane of the wave holds a logit above -inf in either value: a
+// -inf logit (masked, or below a filter's cut) weighs exactly 0, so where no
+// lane holds another the exponentials are skipped with no change to any sum.
+__device__ inline bool any_finite(float x, float y) {
+  return __ballot(x != -INFINITY || y != -INFINITY) != 0ull;
+}
+
 // Request classes: 0 samples with its draft rows or has gamma == 0 (it has a
 // final draw), 1 is greedy or cannot sample (target rows only), 2 has an
 // invalid temperature.
@@ -463,7 +470,7 @@ __device__ inline bool poll_words(const uint64_t* p, int c0, int ce, uint64_t (&
   return false;
 }
 
-template <int DT, bool VEC, int SPAN>
+template <int DT, bool VEC, int SPAN, bool kSkip = false>
 __device__ bool draw_token(const ChainArgs& a, int b, const Pending& d, bool zero_wire);
 
 // With kDraws (the single launch), the decide item of a drawing request then
@@ -471,7 +478,7 @@ __device__ bool draw_token(const ChainArgs& a, int b, const Pending& d, bool zer
 // itself.  The count of a drawing request is written by whoever draws (this
 // item, or with counted units the last unit), once the draw has its records:
 // so SV_GAVE_UP from any wait of the request reaches it through one writer.
-template <int DT, bool VEC, int SPAN, bool kDraws>
+template <int DT, bool VEC, int SPAN, bool kDraws, bool kSkip = false>
 __device__ void decide_request(const ChainArgs& a, int b) {
   __shared__ float s_gm[kMaxSlots];
   __shared__ double s_gz[kMaxSlots];
@@ -678,7 +685,7 @@ __device__ void decide_request(const ChainArgs& a, int b) {
   if (kDraws && drawing) {
     // the draw runs beside other requests' units: let this wave issue first
     __builtin_amdgcn_s_setprio(3);
-    const bool whole = draw_token<DT, VEC, SPAN>(a, b, d, true);
+    const bool whole = draw_token<DT, VEC, SPAN, kSkip>(a, b, d, true);
     __builtin_amdgcn_s_setprio(0);
     if (lane == 0) a.out_n[b] = whole ? d.n : SV_GAVE_UP;
   }
@@ -765,7 +772,9 @@ __device__ bool wait_records(const ChainArgs& a, int b, bool cached, double (&f)
 // up or a unit gave up waiting for the decision (its record then holds +inf
 // sums, which no real record can: every exponential is at most 1); the
 // token slot is then left alone.
-template <int DT, bool VEC, int SPAN>
+// kSkip: the calls whose rows carry cuts skip the exponentials where a whole
+// wave holds only cut logits (the unfiltered kernels carry no such test).
+template <int DT, bool VEC, int SPAN, bool kSkip>
 __device__ bool draw_token(const ChainArgs& a, int b, const Pending& d, bool zero_wire) {
   using U = Unit<DT, VEC, SPAN>;
   using Raw = typename U::Raw;
@@ -888,10 +897,13 @@ __device__ bool draw_token(const ChainArgs& a, int b, const Pending& d, bool zer
     if (residual) {
 #pragma unroll
       for (int e = 0; e < Raw::kPer; ++e)
-        wk[e] = fmax(0.0, exp_row(st.at(0, e), mtl, l2t) * rzt - exp_row(sd.at(0, e), mdl, l2t) * rzd);
+        wk[e] = (!kSkip || any_finite(st.at(0, e), sd.at(0, e)))
+                    ? fmax(0.0, exp_row(st.at(0, e), mtl, l2t) * rzt - exp_row(sd.at(0, e), mdl, l2t) * rzd)
+                    : 0.0;
     } else {
 #pragma unroll
-      for (int e = 0; e < Raw::kPer; ++e) wk[e] = exp_row(st.at(0, e), mtl, l2t);
+      for (int e = 0; e < Raw::kPer; ++e)
+        wk[e] = (!kSkip || any_finite(st.at(0, e), st.at(0, e))) ? exp_row(st.at(0, e), mtl, l2t) : 0.0;
     }
     st.shift();
     sd.shift();
@@ -965,7 +977,7 @@ __device__ inline int nth_drawing(const DrawingSet& s, int p) {
 // hands back its share of the final draw as a marked record (zeros when there
 // is no draw, +inf when the wait gave up).  With kCounted it also counts
 // itself in, and the last unit of the request draws and writes the count.
-template <int DT, bool VEC, int SPAN, bool kCounted>
+template <int DT, bool VEC, int SPAN, bool kCounted, bool kSkip = false>
 __device__ void unit_work(const ChainArgs& a, int b, int unit) {
   using U = Unit<DT, VEC, SPAN>;
   using Raw = typename U::Raw;
@@ -997,6 +1009,7 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit) {
       for (int j = 0; j < Raw::kItems; ++j) {
 #pragma unroll
         for (int e = 0; e < Raw::kPer; ++e) {
+          if (kSkip && !any_finite(st.at(0, e), sd.at(0, e))) continue;
           const double et = exp_row(st.at(0, e), mtl, l2t);
           const double ed = exp_row(sd.at(0, e), mdl, l2t);
           all_t += et;
@@ -1013,7 +1026,8 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit) {
 #pragma unroll 1
       for (int j = 0; j < Raw::kItems; ++j) {
 #pragma unroll
-        for (int e = 0; e < Raw::kPer; ++e) all_t += exp_row(st.at(0, e), mtl, l2t);
+        for (int e = 0; e < Raw::kPer; ++e)
+          if (!kSkip || any_finite(st.at(0, e), st.at(0, e))) all_t += exp_row(st.at(0, e), mtl, l2t);
         st.shift();
       }
     }
@@ -1040,7 +1054,7 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit) {
     // the last unit of a request draws while other units may still compute:
     // let its wave issue first on its SIMD
     __builtin_amdgcn_s_setprio(3);
-    const bool whole = draw_token<DT, VEC, SPAN>(a, b, d, false);
+    const bool whole = draw_token<DT, VEC, SPAN, kSkip>(a, b, d, false);
     __builtin_amdgcn_s_setprio(0);
     if (lane == 0) a.out_n[b] = (d.valid != 0 && whole) ? d.n : SV_GAVE_UP;
   }
@@ -1050,7 +1064,7 @@ __device__ void unit_work(const ChainArgs& a, int b, int unit) {
 // tasks (drawing request, unit) in request order, so greedy requests take no
 // workgroups and each task waits only for its own request's decision.
 // Task counts fit in 32 bits (B * nunit < 2^31 within the shape limits).
-template <int DT, bool VEC, int SPAN, bool kCounted>
+template <int DT, bool VEC, int SPAN, bool kCounted, bool kSkip = false>
 __device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count) {
   const uint32_t nunit = static_cast<uint32_t>(a.nunit);
   if (a.B <= kRankMaxBatch) {
@@ -1059,7 +1073,8 @@ __device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count) {
     if (w >= tasks) return;
     for (uint32_t t = w; t < tasks; t += count) {
       const uint32_t p = t / nunit;
-      unit_work<DT, VEC, SPAN, kCounted>(a, nth_drawing(ds, static_cast<int>(p)), static_cast<int>(t - p * nunit));
+      unit_work<DT, VEC, SPAN, kCounted, kSkip>(a, nth_drawing(ds, static_cast<int>(p)),
+                                                static_cast<int>(t - p * nunit));
     }
   } else {
     const uint32_t tasks = static_cast<uint32_t>(a.B) * nunit;
@@ -1067,7 +1082,7 @@ __device__ void unit_pool(const ChainArgs& a, uint32_t w, uint32_t count) {
     for (uint32_t t = w; t < tasks; t += count) {
       const uint32_t b = t / nunit;
       if (request_class(a, a.temperature[b]) == 0)
-        unit_work<DT, VEC, SPAN, kCounted>(a, static_cast<int>(b), static_cast<int>(t - b * nunit));
+        unit_work<DT, VEC, SPAN, kCounted, kSkip>(a, static_cast<int>(b), static_cast<int>(t - b * nunit));
     }
   }
 }
@@ -1189,7 +1204,8 @@ __device__ inline BlockRole planned_role(const ChainArgs& a, uint32_t blk) {
   return r;
 }
 
-template <int DT, bool VEC, int SPAN>
+// SKIP: a filtered call's form (see draw_token).
+template <int DT, bool VEC, int SPAN, bool SKIP = false>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(5))) void chain_verify(ChainArgs a) {
   // 32-bit index arithmetic: this grid has at most kMaxGrid blocks
   const BlockRole r = a.plan.nS >= 0 ? planned_role(a, blockIdx.x) : default_role(a, blockIdx.x);
@@ -1204,11 +1220,11 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(5))) void
       if (it.c < a.nchunk) stream_once<DT, VEC>(a, it);
     }
   } else if (r.kind == BlockRole::kDecide) {
-    if (draws) decide_request<DT, VEC, SPAN, true>(a, r.item.b);
-    else decide_request<DT, VEC, SPAN, false>(a, r.item.b);
+    if (draws) decide_request<DT, VEC, SPAN, true, SKIP>(a, r.item.b);
+    else decide_request<DT, VEC, SPAN, false, SKIP>(a, r.item.b);
   } else if (r.kind == BlockRole::kPool) {
-    if (draws) unit_pool<DT, VEC, SPAN, false>(a, r.w, r.count);
-    else unit_pool<DT, VEC, SPAN, true>(a, r.w, r.count);
+    if (draws) unit_pool<DT, VEC, SPAN, false, SKIP>(a, r.w, r.count);
+    else unit_pool<DT, VEC, SPAN, true, SKIP>(a, r.w, r.count);
   }
 }
 
@@ -1390,8 +1406,13 @@ static int launch_chain(ChainArgs a, hipStream_t stream) {
       else a.plan.nS = -1;
     }
     const dim3 grid(static_cast<unsigned>(n));
-    if (small) launch(SV_K_CHAIN_VERIFY, chain_verify<DT, VEC, kUnitSpanSmall>, grid, dim3(kWave), 0, stream, a);
-    else launch(SV_K_CHAIN_VERIFY, chain_verify<DT, VEC, kUnitSpanLarge>, grid, dim3(kWave), 0, stream, a);
+    if (a.thr) {  // rows with cuts: the form that skips the exponentials of cut logits
+      if (small) launch(SV_K_CHAIN_VERIFY, chain_verify<DT, VEC, kUnitSpanSmall, true>, grid, dim3(kWave), 0, stream, a);
+      else launch(SV_K_CHAIN_VERIFY, chain_verify<DT, VEC, kUnitSpanLarge, true>, grid, dim3(kWave), 0, stream, a);
+    } else {
+      if (small) launch(SV_K_CHAIN_VERIFY, chain_verify<DT, VEC, kUnitSpanSmall>, grid, dim3(kWave), 0, stream, a);
+      else launch(SV_K_CHAIN_VERIFY, chain_verify<DT, VEC, kUnitSpanLarge>, grid, dim3(kWave), 0, stream, a);
+    }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
   }
   a.plan.nS = -1;
