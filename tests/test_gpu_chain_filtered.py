@@ -288,3 +288,22 @@ def test_cut_inside_the_top_prefix(dtype):
     k = np.array([3, 6, 1000, 8, 2, 5000, 4, 7], np.int32)
     ci.draft_tokens = filtered_draft_tokens(ci, k, p, 16613)
     filtered_parity(ci, k, p, 8, f"top-k then a cut in the top prefix {dtype}")
+
+
+@pytest.mark.parametrize("V", [140000, 70003])
+def test_cuts_that_keep_most_of_the_row(V):
+    """Cuts far down the row (k close to V, p close to 1, with masked logits):
+    the cut search's kept mass then sums many binades and the cut's own
+    binade value by value, and the verification takes it in place of the
+    row; several slices per row, vector and scalar paths."""
+    ci = synth.chain_inputs(16620 + V % 11, B=8, gamma=2, V=V, dtype="bf16", family="gauss",
+                            draft_sigma=(0.3, 1.0), temperature=1.0, greedy_odd=False)
+    rng = np.random.default_rng(16621)
+    for arr in (ci.target, ci.draft):
+        masked = rng.integers(0, ci.V, size=ci.V // 50)
+        arr[:, :, masked] = 0xFF80  # -inf
+    ci.temperature = np.array([1.0, 0.7, 2.0, 1.3, 0.9, 1.0, 0.5, 3.0], np.float32)
+    k = np.array([V - 1, V - 500, V // 2, V + 3, V - 1, 20000, V // 3, V - 2], np.int32)
+    p = np.array([1.0, 0.999, 1.0, 0.9999, 0.99, 1.0, 0.995, 0.97], np.float32)
+    ci.draft_tokens = filtered_draft_tokens(ci, k, p, 16622)
+    filtered_parity(ci, k, p, 6, f"cuts keeping most of the row V={V}")
